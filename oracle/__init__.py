@@ -1,0 +1,189 @@
+"""fp64 CPU oracle of the speculative-sampling verify step (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package; the GPU library and
+its Python binding never do.  The arithmetic lives in ``oracle.c`` (plain C,
+fp64, Neumaier sums); this file only marshals numpy arrays.
+
+Parity pins: every exported function is pinned by ``tests/test_oracle_*.py``
+against the pages' equations, closed forms, library routines and brute force
+(see the header of ``oracle.c`` for the pages followed).
+"""
+from __future__ import annotations
+
+import contextlib
+import ctypes
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+FLAG_A, FLAG_B, FLAG_D, FLAG_E = 1, 2, 4, 8
+ACCEPT_BAND, CDF_BAND = 1e-5, 1e-12
+
+_lib = None
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile oracle.c into liboracle.so next to it (gcc, -O2, no fast-math)."""
+    tmp = out + f".tmp{os.getpid()}"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC",
+                           "-shared", "-fno-fast-math", "-o", tmp, src, "-lm"])
+    os.replace(tmp, out)
+    return out
+
+
+@contextlib.contextmanager
+def using_library(path: str):
+    """Route every call through another build of oracle.c for the duration
+    (the mutation tests build copies with planted mistakes this way)."""
+    global _lib
+    saved = _lib
+    _lib = _open(path)
+    try:
+        yield
+    finally:
+        _lib = saved
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        _lib = _open(_LIB)
+    return _lib
+
+
+def _open(path: str):
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    lib.oracle_verify.restype = ctypes.c_int
+    lib.oracle_verify.argtypes = [P, P, i32, i64, i32, P, P, P, P, i32, i32,
+                                  P, P, P, P, P, P, P, P, P, P]
+    lib.oracle_verify_probs.restype = ctypes.c_int
+    lib.oracle_verify_probs.argtypes = [P, P, i64, i32, i32, i32, P, P, P, P, P, P, P]
+    lib.oracle_softmax_rows.restype = ctypes.c_int
+    lib.oracle_softmax_rows.argtypes = [P, i32, i64, i64, ctypes.c_double, P, P, P]
+    lib.oracle_inverse_cdf.restype = i64
+    lib.oracle_inverse_cdf.argtypes = [P, i64, ctypes.c_float, P, P]
+    return lib
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_code(rows: np.ndarray) -> int:
+    if rows.dtype == np.float32:
+        return 0
+    if rows.dtype == np.uint16:
+        return 1
+    raise TypeError(f"stored logits must be float32 or uint16 (bf16 bits), got {rows.dtype}")
+
+
+def verify(w, diag: bool = False, threads: int = 1, seqs: tuple[int, int] | None = None) -> dict:
+    """Run the oracle over a ``workloads.Workload`` (or any object with the
+    same fields).  Returns numpy arrays: tokens [total+B], n [B], flags [B]
+    and, with ``diag``, alpha/px/qx [total], Z/gap [B], row_max/row_sum
+    [2*total+B] (target rows first).  ``seqs`` = (b0, b1) limits the work to
+    those sequences (other outputs stay at their fill values)."""
+    lib = _load()
+    B, V = int(w.B), int(w.V)
+    off = np.ascontiguousarray(w.offsets, np.int32)
+    total = int(off[-1])
+    target = np.ascontiguousarray(w.target)
+    draft = np.ascontiguousarray(w.draft)
+    if draft.size == 0:
+        draft = np.zeros((1, V), target.dtype)
+    dt = _dtype_code(target)
+    tokens = np.ascontiguousarray(w.tokens, np.int32)
+    unif = np.ascontiguousarray(w.uniforms, np.float32)
+    temp = np.ascontiguousarray(w.temperature, np.float32)
+    out = dict(tokens=np.full(total + B, -1, np.int32), n=np.full(B, -2, np.int32),
+               flags=np.zeros(B, np.int32))
+    if diag:
+        out.update(alpha=np.full(total, np.nan), px=np.full(total, np.nan),
+                   qx=np.full(total, np.nan), Z=np.full(B, np.nan), gap=np.full(B, np.nan),
+                   row_max=np.full(2 * total + B, np.nan),
+                   row_sum=np.full(2 * total + B, np.nan))
+    b0, b1 = seqs if seqs is not None else (0, B)
+
+    def run(rng):
+        lo, hi = rng
+        rc = lib.oracle_verify(
+            _ptr(target), _ptr(draft), dt, V, B, _ptr(off), _ptr(tokens), _ptr(unif),
+            _ptr(temp), lo, hi, _ptr(out["tokens"]), _ptr(out["n"]), _ptr(out["flags"]),
+            _ptr(out.get("alpha")), _ptr(out.get("px")), _ptr(out.get("qx")),
+            _ptr(out.get("Z")), _ptr(out.get("gap")), _ptr(out.get("row_max")),
+            _ptr(out.get("row_sum")))
+        if rc != 0:
+            raise RuntimeError(f"oracle_verify failed with code {rc}")
+
+    if threads <= 1 or b1 - b0 <= 1:
+        run((b0, b1))
+    else:
+        edges = np.linspace(b0, b1, min(threads, b1 - b0) + 1).astype(int)
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(run, zip(edges[:-1], edges[1:])))
+    return out
+
+
+def verify_probs(P: np.ndarray, Q: np.ndarray, tokens: np.ndarray, uniforms: np.ndarray,
+                 k: int, shared_rows: bool) -> dict:
+    """Probability-domain verify (no softmax): uniform k over B sequences.
+    shared_rows: P [k+1, V] and Q [k, V] serve every sequence; otherwise
+    P [B*(k+1), V], Q [B*k, V].  tokens [B, k], uniforms [B, k+1]."""
+    lib = _load()
+    P = np.ascontiguousarray(P, np.float64)
+    Q = np.ascontiguousarray(Q, np.float64)
+    V = P.shape[-1]
+    tokens = np.ascontiguousarray(tokens, np.int32).reshape(-1, k) if k else \
+        np.zeros((len(uniforms), 0), np.int32)
+    uniforms = np.ascontiguousarray(uniforms, np.float32).reshape(-1, k + 1)
+    B = uniforms.shape[0]
+    if Q.size == 0:
+        Q = np.zeros((1, V))
+    out = dict(tokens=np.full((B, k + 1), -1, np.int32), n=np.zeros(B, np.int32),
+               flags=np.zeros(B, np.int32), Z=np.zeros(B), gap=np.zeros(B))
+    rc = lib.oracle_verify_probs(_ptr(P), _ptr(Q), V, B, k, int(bool(shared_rows)),
+                                 _ptr(tokens), _ptr(uniforms), _ptr(out["tokens"]),
+                                 _ptr(out["n"]), _ptr(out["flags"]), _ptr(out["Z"]),
+                                 _ptr(out["gap"]))
+    if rc != 0:
+        raise RuntimeError(f"oracle_verify_probs failed with code {rc}")
+    return out
+
+
+def softmax_rows(rows: np.ndarray, T: float):
+    """Tempered softmax of stored rows [n, V] -> (p [n, V], m [n], S [n])."""
+    lib = _load()
+    rows = np.ascontiguousarray(rows)
+    if rows.ndim == 1:
+        rows = rows[None]
+    n, V = rows.shape
+    p = np.empty((n, V))
+    m = np.empty(n)
+    S = np.empty(n)
+    rc = lib.oracle_softmax_rows(_ptr(rows), _dtype_code(rows), n, V, float(T), _ptr(p),
+                                 _ptr(m), _ptr(S))
+    if rc != 0:
+        raise RuntimeError(f"oracle_softmax_rows failed with code {rc}")
+    return p, m, S
+
+
+def inverse_cdf(r: np.ndarray, u: float):
+    """Inverse-CDF draw over a non-negative mass row -> (t, Z, gap)."""
+    lib = _load()
+    r = np.ascontiguousarray(r, np.float64)
+    Z = ctypes.c_double()
+    gap = ctypes.c_double()
+    t = lib.oracle_inverse_cdf(_ptr(r), r.size, ctypes.c_float(np.float32(u)),
+                               ctypes.byref(Z), ctypes.byref(gap))
+    return int(t), Z.value, gap.value

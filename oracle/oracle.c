@@ -1,0 +1,377 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU oracle of the speculative-sampling verify
+ * step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the GPU library, and the GPU library never
+ * calls it.
+ *
+ * Pages this follows (cited by title and section):
+ *   [ifdog] "投机解码", docs.ifdog.com -- sections 投机解码的三步流程 (three-step
+ *           flow), 无损保证：数学推导 (lossless proof, its equations for the
+ *           accept path, the normaliser Z identity, the reject path and the
+ *           output marginal), 动手实践 (worked transformers demo: temperature,
+ *           greedy branch, bonus token).
+ *   [hw]    "大模型推理无损加速:投机采样(Speculative Decoding)数学原理与工业级落地
+ *           实践", bbs.huaweicloud.com -- section 二 (1. acceptance probability
+ *           alpha(x) = min(1, p/q); 2. residual distribution p'(x); 3. marginal
+ *           equivalence) and section 三 (one verify step incl. the bonus).
+ *   [sxl]   "【大模型】- 推测解码", sxl-space.tk -- 基础推测解码器 (target_verify)
+ *           and 批量推测解码 (per-row verify over a batch).
+ *
+ * What is computed, per sequence b (k = k_b drafted tokens x_0..x_{k-1}):
+ *   T = 0 (greedy; [ifdog] 动手实践 greedy branch): a_i = argmax over the raw
+ *     logits of target row i, lowest index on ties.  Accept while x_i == a_i;
+ *     at the first mismatch i emit a_i; if all k match, emit a_k.
+ *   T > 0: p_i = softmax(z_t[i] / T), q_i = softmax(z_d[i] / T) in fp64
+ *     (every row tempered, see the readings below).  Position i is accepted
+ *     iff u_i < alpha_i = min(1, p_i(x_i) / q_i(x_i))  ([ifdog] three-step
+ *     flow step 3; [hw] 二.1).  The first rejection at i = n stops the scan.
+ *     If n < k the emitted token is drawn from r = max(0, p_n - q_n) / Z
+ *     ([ifdog] residual equation; [hw] 二.2); if n = k it is drawn from p_k
+ *     (bonus, [ifdog] three-step flow last bullet; [hw] 三 step 4).  A draw
+ *     with uniform u* = u_k picks t* = min{t : C_t > u* . Z}, C_t = the
+ *     running sum of r over token ids 0..t, Z = C_{V-1}.
+ *
+ * Readings where the pages leave a step open (every one is also listed in
+ * the design notes):
+ *   R1 temperature divides every target and draft row (the lossless proof
+ *      needs the same p in the test and the bonus draw);
+ *   R2 strict u < alpha;
+ *   R3 no epsilon guards (q(x) > 0 holds for finite logits);
+ *   R4 the residual uses the full q_n row;
+ *   R5 the bonus token is always drawn;
+ *   R6 uniform slot k_b drives the draw, slots 0..k_b-1 the accept tests;
+ *   R7 the pages' multinomial draw is an inverse CDF in ascending token id
+ *      with a strict '>' (zero-mass tokens are never picked);
+ *   R8 greedy ties go to the lowest token id;
+ *   R11 if a rejection leaves Z < 1e-9 the draw falls back to p_n (flag D).
+ *
+ * Ambiguity flags (rows where float rounding order may legitimately decide
+ * differently): A = some evaluated accept test has |u - alpha| < 1e-5;
+ * B = u*.Z lies within 1e-12 (absolute) of a CDF boundary C_t; D = degenerate
+ * residual (see R11); E = per-row data error (bad k, T, token).
+ *
+ * Sums are Neumaier-compensated running sums, in ascending token id.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_FLAG_A 1
+#define ORC_FLAG_B 2
+#define ORC_FLAG_D 4
+#define ORC_FLAG_E 8
+
+#define ORC_ACCEPT_BAND 1e-5
+#define ORC_CDF_BAND 1e-12
+#define ORC_DEGENERATE_Z 1e-9
+#define ORC_K_MAX 63
+
+/* ---- small helpers ------------------------------------------------------ */
+
+/* Stored logit -> double.  dtype 0: fp32; dtype 1: bf16 (upper half of an
+ * fp32 bit pattern), decoded exactly. */
+static double orc_decode(const void *rows, int dtype, int64_t idx) {
+    if (dtype == 0) return (double)((const float *)rows)[idx];
+    uint32_t bits = ((uint32_t)((const uint16_t *)rows)[idx]) << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* Neumaier compensated sum. */
+typedef struct { double s, c; } orc_sum;
+
+static void orc_sum_add(orc_sum *a, double x) {
+    double t = a->s + x;
+    if (fabs(a->s) >= fabs(x)) a->c += (a->s - t) + x;
+    else a->c += (x - t) + a->s;
+    a->s = t;
+}
+
+static double orc_sum_value(const orc_sum *a) { return a->s + a->c; }
+
+/* ---- row-level definitions --------------------------------------------- */
+
+/* Largest logit and the lowest token id holding it. */
+static double orc_row_argmax(const void *rows, int dtype, int64_t row, int64_t V,
+                             int64_t *arg) {
+    const int64_t base = row * V;
+    double best = orc_decode(rows, dtype, base);
+    int64_t at = 0;
+    for (int64_t v = 1; v < V; ++v) {
+        double z = orc_decode(rows, dtype, base + v);
+        if (z > best) { best = z; at = v; }
+    }
+    if (arg) *arg = at;
+    return best;
+}
+
+/* Temperature softmax of one row: p_v = exp((z_v - m)/T) / S with
+ * m = max z and S = sum_v exp((z_v - m)/T).  Writes p (length V) and
+ * returns m and S.  [ifdog] 动手实践 applies softmax(logits / T). */
+static void orc_softmax_row(const void *rows, int dtype, int64_t row, int64_t V, double T,
+                            double *p, double *m_out, double *S_out) {
+    const int64_t base = row * V;
+    double m = orc_row_argmax(rows, dtype, row, V, NULL);
+    orc_sum S = {0.0, 0.0};
+    for (int64_t v = 0; v < V; ++v) {
+        double w = exp((orc_decode(rows, dtype, base + v) - m) / T);
+        p[v] = w;
+        orc_sum_add(&S, w);
+    }
+    double s = orc_sum_value(&S);
+    for (int64_t v = 0; v < V; ++v) p[v] /= s;
+    *m_out = m;
+    *S_out = s;
+}
+
+/* ---- the verify step on probability rows ------------------------------- */
+
+/* Mass of token v in the draw: max(0, p_v - q_v) (residual) or p_v (q NULL). */
+static double orc_mass(const double *pr, const double *qr, int64_t v) {
+    return qr ? fmax(0.0, pr[v] - qr[v]) : pr[v];
+}
+
+/* Inverse-CDF draw over token ids in ascending order: Z = sum of all masses,
+ * t* = min{t : C_t > u Z} with C_t the running sum up to t (strict '>', so a
+ * zero-mass token is never picked).  If qr != NULL and Z < 1e-9 the draw
+ * falls back to pr alone (*degenerate = 1): a rejection happens with
+ * probability Z ([ifdog] Z identity), so this only arises from rounding.
+ * Writes Z and the distance from u Z to the nearest C_t. */
+static int64_t orc_draw(const double *pr, const double *qr, int64_t V, float u,
+                        double *Z_out, double *gap_out, int *degenerate) {
+    orc_sum Zs = {0.0, 0.0};
+    for (int64_t v = 0; v < V; ++v) orc_sum_add(&Zs, orc_mass(pr, qr, v));
+    double Z = orc_sum_value(&Zs);
+    *degenerate = 0;
+    if (qr && Z < ORC_DEGENERATE_Z) {
+        *degenerate = 1;
+        qr = NULL;
+        Zs.s = Zs.c = 0.0;
+        for (int64_t v = 0; v < V; ++v) orc_sum_add(&Zs, pr[v]);
+        Z = orc_sum_value(&Zs);
+    }
+    const double target = (double)u * Z;
+    orc_sum C = {0.0, 0.0};
+    double gap = INFINITY;
+    int64_t pick = -1, last_pos = -1;
+    for (int64_t v = 0; v < V; ++v) {
+        double r = orc_mass(pr, qr, v);
+        if (r > 0.0) last_pos = v;
+        orc_sum_add(&C, r);
+        double c = orc_sum_value(&C), d = fabs(target - c);
+        if (d < gap) gap = d;
+        if (pick < 0 && c > target) pick = v;
+    }
+    /* u < 1 makes u Z < Z = C_{V-1}, so a pick always exists; keep a valid
+     * token for the record anyway. */
+    if (pick < 0) pick = last_pos >= 0 ? last_pos : 0;
+    *Z_out = Z;
+    *gap_out = gap;
+    return pick;
+}
+
+
+typedef struct {
+    int32_t n, token, flags;
+    double Z, gap;
+} orc_result;
+
+/* One sequence, sampling path.  P[i] (i = 0..k) are target distributions,
+ * Q[i] (i = 0..k-1) draft distributions, x the drafted tokens, u the k+1
+ * uniforms (u[k] drives the draw). */
+static orc_result orc_verify_probs_seq(const double *const *P, const double *const *Q,
+                                       int64_t V, int k, const int32_t *x, const float *u,
+                                       double *alpha_out, double *px_out, double *qx_out) {
+    orc_result res = {k, -1, 0, 0.0, 0.0};
+
+    /* Accept tests in order; stop at the first rejection ([ifdog] three-step
+     * flow step 3; [hw] 二.1 alpha(x) = min(1, p(x)/q(x))). */
+    for (int i = 0; i < k; ++i) {
+        double px = P[i][x[i]], qx = Q[i][x[i]];
+        double ratio = px / qx;
+        double alpha = ratio < 1.0 ? ratio : 1.0;
+        if (alpha_out) alpha_out[i] = alpha;
+        if (px_out) px_out[i] = px;
+        if (qx_out) qx_out[i] = qx;
+        if (fabs((double)u[i] - alpha) < ORC_ACCEPT_BAND) res.flags |= ORC_FLAG_A;
+        if (!((double)u[i] < alpha)) { res.n = i; break; }
+    }
+    const int n = res.n;
+
+    /* Draw: residual max(0, p_n - q_n) after a rejection ([ifdog] reject-path
+     * equation; [hw] 二.2), else the bonus distribution p_k. */
+    const double *pr = P[n];
+    const double *qr = (n < k) ? Q[n] : NULL;
+    int degenerate = 0;
+    int64_t pick = orc_draw(pr, qr, V, u[k], &res.Z, &res.gap, &degenerate);
+    if (degenerate) res.flags |= ORC_FLAG_D;
+    if (res.gap < ORC_CDF_BAND) res.flags |= ORC_FLAG_B;
+    res.token = (int32_t)pick;
+    return res;
+}
+
+static void orc_write_tokens(int32_t *out, int k, const int32_t *x, int n, int32_t emitted) {
+    for (int i = 0; i <= k; ++i) out[i] = -1;
+    if (n < 0) return;
+    for (int i = 0; i < n; ++i) out[i] = x[i];
+    out[n] = emitted;
+}
+
+/* ---- exported entry points --------------------------------------------- */
+
+/* Probability-domain entry (tests feed p and q directly, bypassing softmax).
+ * Uniform k for all B sequences.  shared_rows != 0: every sequence uses the
+ * same P [k+1, V] and Q [k, V]; otherwise P is [B*(k+1), V] and Q [B*k, V].
+ * tokens [B*k], uniforms [B*(k+1)], out_tokens [B*(k+1)], out_n/out_flags
+ * [B], out_Z/out_gap [B] (may be NULL).  Returns 0, or -1 on bad sizes. */
+int oracle_verify_probs(const double *Pall, const double *Qall, int64_t V, int32_t B,
+                        int32_t k, int32_t shared_rows, const int32_t *tokens,
+                        const float *uniforms, int32_t *out_tokens, int32_t *out_n,
+                        int32_t *out_flags, double *out_Z, double *out_gap) {
+    if (V < 1 || B < 0 || k < 0 || k > ORC_K_MAX) return -1;
+    const double *P[ORC_K_MAX + 1];
+    const double *Q[ORC_K_MAX + 1];
+    for (int32_t b = 0; b < B; ++b) {
+        const int64_t pb = shared_rows ? 0 : (int64_t)b * (k + 1);
+        const int64_t qb = shared_rows ? 0 : (int64_t)b * k;
+        for (int i = 0; i <= k; ++i) P[i] = Pall + (pb + i) * V;
+        for (int i = 0; i < k; ++i) Q[i] = Qall + (qb + i) * V;
+        const int32_t *x = tokens + (int64_t)b * k;
+        int bad = 0;
+        for (int i = 0; i < k; ++i) bad |= (x[i] < 0 || x[i] >= V);
+        orc_result r = {-1, -1, ORC_FLAG_E, 0.0, 0.0};
+        if (!bad)
+            r = orc_verify_probs_seq(P, Q, V, k, x, uniforms + (int64_t)b * (k + 1), NULL,
+                                     NULL, NULL);
+        orc_write_tokens(out_tokens + (int64_t)b * (k + 1), k, x, r.n, r.token);
+        out_n[b] = r.n;
+        if (out_flags) out_flags[b] = r.flags;
+        if (out_Z) out_Z[b] = r.Z;
+        if (out_gap) out_gap[b] = r.gap;
+    }
+    return 0;
+}
+
+/* Logit-domain entry with the same layout as the GPU library:
+ *   target [total+B, V] (sequence b position i at row offsets[b]+b+i),
+ *   draft  [total, V]   (row offsets[b]+i), dtype 0 = fp32, 1 = bf16 bits,
+ *   tokens [total], uniforms [total+B] (slot offsets[b]+b+i),
+ *   temperature [B] (0 = greedy).
+ * Processes sequences b_begin..b_end-1 (so callers may split the batch over
+ * threads).  Outputs: out_tokens [total+B], out_n [B] (-1 = data error),
+ * out_flags [B]; optional (NULL to skip): out_alpha/out_px/out_qx [total]
+ * (position diagnostics), out_Z/out_gap [B], out_row_max/out_row_sum
+ * [2*total+B] (target rows first, then draft rows; NaN where unused).
+ * Returns 0, -1 on bad arguments, -2 on allocation failure. */
+int oracle_verify(const void *target, const void *draft, int32_t dtype, int64_t V,
+                  int32_t B, const int32_t *offsets, const int32_t *tokens,
+                  const float *uniforms, const float *temperature, int32_t b_begin,
+                  int32_t b_end, int32_t *out_tokens, int32_t *out_n, int32_t *out_flags,
+                  double *out_alpha, double *out_px, double *out_qx, double *out_Z,
+                  double *out_gap, double *out_row_max, double *out_row_sum) {
+    if (V < 1 || B < 0 || (dtype != 0 && dtype != 1) || b_begin < 0 || b_end > B ||
+        b_begin > b_end)
+        return -1;
+    const int64_t total = offsets[B];
+    double *buf = (double *)malloc(sizeof(double) * (size_t)V * (2 * ORC_K_MAX + 1));
+    if (!buf) return -2;
+
+    for (int32_t b = b_begin; b < b_end; ++b) {
+        const int64_t o = offsets[b];
+        const int k = (int)(offsets[b + 1] - offsets[b]);
+        const double T = (double)temperature[b];
+        const int64_t trow = o + b;     /* first target row of b */
+        const int64_t drow = o;         /* first draft row of b  */
+        int32_t *out = out_tokens + trow;
+        int bad = (k < 0 || k > ORC_K_MAX || !(T >= 0.0) || isinf(T) || o < 0 ||
+                   offsets[b + 1] > total);
+        const int32_t *x = tokens + drow;
+        for (int i = 0; !bad && i < k; ++i) bad |= (x[i] < 0 || x[i] >= V);
+        if (bad) {
+            for (int i = 0; k >= 0 && i <= k && i <= ORC_K_MAX; ++i) out[i] = -1;
+            out_n[b] = -1;
+            if (out_flags) out_flags[b] = ORC_FLAG_E;
+            continue;
+        }
+        if (out_row_max)
+            for (int i = 0; i <= k; ++i) {
+                out_row_max[trow + i] = NAN;
+                out_row_sum[trow + i] = NAN;
+                if (i < k) {
+                    out_row_max[total + B + drow + i] = NAN;
+                    out_row_sum[total + B + drow + i] = NAN;
+                }
+            }
+
+        if (T == 0.0) {
+            /* Greedy: accept while the draft equals the target argmax. */
+            int n = k;
+            int64_t a = 0;
+            for (int i = 0; i <= k; ++i) {
+                double m = orc_row_argmax(target, dtype, trow + i, V, &a);
+                if (out_row_max) out_row_max[trow + i] = m;
+                if (i == k || x[i] != a) { n = i; break; }
+            }
+            orc_write_tokens(out, k, x, n, (int32_t)a);
+            out_n[b] = n;
+            if (out_flags) out_flags[b] = 0;
+            if (out_Z) out_Z[b] = NAN;
+            if (out_gap) out_gap[b] = NAN;
+            continue;
+        }
+
+        /* Sampling: tempered softmax of every needed row, then the test. */
+        const double *P[ORC_K_MAX + 1];
+        const double *Q[ORC_K_MAX + 1];
+        for (int i = 0; i <= k; ++i) {
+            double *p = buf + (size_t)i * V, m, S;
+            orc_softmax_row(target, dtype, trow + i, V, T, p, &m, &S);
+            P[i] = p;
+            if (out_row_max) { out_row_max[trow + i] = m; out_row_sum[trow + i] = S; }
+        }
+        for (int i = 0; i < k; ++i) {
+            double *q = buf + (size_t)(k + 1 + i) * V, m, S;
+            orc_softmax_row(draft, dtype, drow + i, V, T, q, &m, &S);
+            Q[i] = q;
+            if (out_row_max) {
+                out_row_max[total + B + drow + i] = m;
+                out_row_sum[total + B + drow + i] = S;
+            }
+        }
+        orc_result r = orc_verify_probs_seq(
+            P, Q, V, k, x, uniforms + trow, out_alpha ? out_alpha + drow : NULL,
+            out_px ? out_px + drow : NULL, out_qx ? out_qx + drow : NULL);
+        orc_write_tokens(out, k, x, r.n, r.token);
+        out_n[b] = r.n;
+        if (out_flags) out_flags[b] = r.flags;
+        if (out_Z) out_Z[b] = r.Z;
+        if (out_gap) out_gap[b] = r.gap;
+    }
+    free(buf);
+    return 0;
+}
+
+/* Softmax of stored rows (exposed so tests can pin it against a library
+ * softmax).  Writes p [nrows, V], m [nrows], S [nrows]. */
+int oracle_softmax_rows(const void *rows, int32_t dtype, int64_t nrows, int64_t V, double T,
+                        double *p, double *m, double *S) {
+    if (V < 1 || nrows < 0 || !(T > 0.0) || (dtype != 0 && dtype != 1)) return -1;
+    for (int64_t r = 0; r < nrows; ++r) orc_softmax_row(rows, dtype, r, V, T, p + r * V, &m[r], &S[r]);
+    return 0;
+}
+
+/* Draw only: given one non-negative mass row r [V] and a uniform, return
+ * t* = min{t : C_t > u Z}; writes Z and the boundary gap. */
+int64_t oracle_inverse_cdf(const double *r, int64_t V, float u, double *Z_out, double *gap_out) {
+    double Z, gap;
+    int degenerate;
+    int64_t pick = orc_draw(r, NULL, V, u, &Z, &gap, &degenerate);
+    if (Z_out) *Z_out = Z;
+    if (gap_out) *gap_out = gap;
+    return pick;
+}

@@ -1,0 +1,69 @@
+"""Planted mistakes in copies of the oracle must each fail some pin.
+
+Each mutant is a one-line edit of ``oracle/oracle.c`` of a kind that could
+plausibly slip in (an off-by-one row, '<=' for '<', a swapped residual, a
+dropped temperature, an epsilon guard copied from tutorial code, ...).  The
+copy is compiled with gcc into a temporary directory and the pins of
+``test_oracle_pins`` are run against it; the test passes only if every
+mutant is caught.  Everything runs on the CPU.
+"""
+import os
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "accept_le": ("if (!((double)u[i] < alpha))", "if (!((double)u[i] <= alpha))"),
+    "draw_ge": ("if (pick < 0 && c > target) pick = v;", "if (pick < 0 && c >= target) pick = v;"),
+    "residual_swapped": ("return qr ? fmax(0.0, pr[v] - qr[v]) : pr[v];",
+                         "return qr ? fmax(0.0, qr[v] - pr[v]) : pr[v];"),
+    "no_temperature": ("double w = exp((orc_decode(rows, dtype, base + v) - m) / T);",
+                       "double w = exp((orc_decode(rows, dtype, base + v) - m));"),
+    "draw_uses_first_uniform": ("orc_draw(pr, qr, V, u[k],", "orc_draw(pr, qr, V, u[0],"),
+    "draw_row_off_by_one": ("const double *pr = P[n];", "const double *pr = P[n > 0 ? n - 1 : 0];"),
+    "ratio_transposed": ("double ratio = px / qx;", "double ratio = qx / px;"),
+    "epsilon_guard": ("double ratio = px / qx;", "double ratio = px / (qx + 1e-8);"),
+    "greedy_tie_highest": ("if (z > best) { best = z; at = v; }", "if (z >= best) { best = z; at = v; }"),
+    "greedy_emits_draft": ("orc_write_tokens(out, k, x, n, (int32_t)a);",
+                           "orc_write_tokens(out, k, x, n, n < k ? x[n] : (int32_t)a);"),
+    "uniform_slot_draft_layout": ("uniforms + trow, out_alpha", "uniforms + drow, out_alpha"),
+    "bonus_from_draft_row": ("const double *qr = (n < k) ? Q[n] : NULL;",
+                             "const double *qr = (n < k) ? Q[n] : (k > 0 ? Q[k - 1] : NULL);"),
+}
+
+PINS = [
+    lambda: pins.test_inverse_cdf_hand_case(),
+    lambda: pins.test_softmax_matches_scipy("f32", 0.6),
+    lambda: pins.test_greedy_equals_argmax_with_ties(),
+    lambda: pins.test_alpha_has_no_epsilon_guard(),
+    lambda: pins.test_v2_closed_form(),
+    lambda: pins.test_lossless_exact_enumeration(0),
+    lambda: pins.test_lossless_exact_enumeration(1),
+    lambda: pins.test_lossless_chain_k3(),
+    lambda: pins.test_k_zero_emits_bonus_or_argmax(),
+    lambda: pins.test_oracle_vs_numpy_composition("c3", 6),
+]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation anchor for {name} not unique"
+    mutated = tmp_path / "oracle_mutant.c"
+    mutated.write_text(text.replace(old, new))
+    lib = oracle.build(str(mutated), str(tmp_path / "liboracle_mutant.so"))
+    caught = None
+    with oracle.using_library(lib):
+        for i, pin in enumerate(PINS):
+            try:
+                pin()
+            except AssertionError:
+                caught = i
+                break
+    assert caught is not None, f"mutant {name} survived every pin"
