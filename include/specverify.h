@@ -1,0 +1,148 @@
+/*
+ * specverify.h -- C ABI of libspecverify, the speculative-sampling verify
+ * step on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (pages cited by title and section):
+ *   * "投机解码" (docs.ifdog.com), section 投机解码的三步流程, step 3: each
+ *     drafted token x_i is accepted with probability min(1, p(x_i)/q(x_i));
+ *     at the first rejection a replacement is drawn from the normalised
+ *     max(0, p - q) and later drafts are dropped; if all k are accepted a
+ *     bonus token is drawn from the target distribution at position k+1.
+ *     Its section 动手实践 tempers the distributions with softmax(logits/T)
+ *     and, at T = 0, accepts while the draft equals the target argmax.
+ *   * "大模型推理无损加速:投机采样(Speculative Decoding)数学原理与工业级落地实践"
+ *     (bbs.huaweicloud.com), section 二 (alpha(x), residual p'(x)) and
+ *     section 三 (one verify step over gamma drafts with the bonus draw).
+ *   * "【大模型】- 推测解码" (sxl-space.tk), section 批量推测解码: a batch of
+ *     sequences verified independently.
+ * Readings where the pages leave a step open: every target and draft row is
+ * divided by T; strict u < alpha; no epsilon guards; the residual uses the
+ * full q row; the bonus is always drawn; the uniform of slot k_b drives the
+ * draw; the draw is an inverse CDF over ascending token ids that picks
+ * t* = min{t : sum_{v<=t} r_v > u * sum_v r_v}; greedy ties go to the lowest
+ * token id.
+ *
+ * Conventions shared by every call below:
+ *   * All array arguments are DEVICE pointers (memory of the GPU that is
+ *     current on the calling thread), owned by the caller.  The library keeps
+ *     no pointer after the call returns.
+ *   * Calls only enqueue work on `stream` (0 = the null stream) and never
+ *     synchronise the host; results are valid once the stream has completed.
+ *   * Sequence b (0 <= b < B) has k_b drafted tokens, 0 <= k_b <= SV_K_MAX.
+ *     With `offsets` (int32 [B+1], offsets[0] = 0, non-decreasing,
+ *     offsets[B] = total_draft) k_b = offsets[b+1] - offsets[b]; with
+ *     offsets == NULL every k_b = k_uniform and total_draft = B * k_uniform.
+ *   * Row layout (row-major, V logits per row, dtype fp32 or bf16):
+ *       target_logits [total_draft + B, V]: position i = 0..k_b of sequence b
+ *         is row offsets[b] + b + i (row i scores drafted token i; row k_b is
+ *         the bonus row);
+ *       draft_logits  [total_draft, V]: position i = 0..k_b-1 of b is row
+ *         offsets[b] + i.  Draft rows of greedy (T = 0) sequences are never
+ *         read.
+ *   * draft_tokens int32 [total_draft] (slot offsets[b] + i);
+ *     uniforms fp32 [total_draft + B] in [0, 1) (slot offsets[b] + b + i:
+ *     the accept uniform of position i for i < k_b, the draw uniform for
+ *     i = k_b); temperature fp32 [B] (0 = greedy, > 0 = sampling).
+ *   * Outputs: out_tokens int32 [total_draft + B] (slot offsets[b] + b + i):
+ *     the n_b accepted drafts, then the emitted token, then -1;
+ *     out_n_accepted int32 [B]: n_b in 0..k_b, or -1 for a per-sequence data
+ *     error (k_b out of range, offsets inconsistent, T < 0 or not finite, a
+ *     drafted token outside [0, V), a non-finite row maximum); that
+ *     sequence's token slots are all -1.  NaN/Inf logits are otherwise
+ *     outside the contract.
+ *   * Argument errors are detected on the host before anything is enqueued
+ *     and return a negative sv_status_t with no output written.
+ *   * Pointers must be aligned to their element size; 16-byte aligned logit
+ *     rows (V * element size % 16 == 0 and 16-byte aligned bases) stream
+ *     fastest.
+ *   * workspace == NULL selects a library-owned, grow-only device buffer per
+ *     GPU (allocated with hipMalloc on first use or growth); calls that use it
+ *     must not overlap in time on one GPU.  Callers that run concurrent
+ *     streams pass their own workspace of spec_verify_workspace_size() bytes
+ *     per stream.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SV_K_MAX 63 /* k_b + 1 positions fit one 64-lane wavefront */
+
+typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype_t;
+
+typedef enum {
+    SV_OK = 0,
+    SV_ERR_NULL = -1,      /* a required pointer is NULL */
+    SV_ERR_SHAPE = -2,     /* B, V, k_uniform or total_draft out of range or inconsistent */
+    SV_ERR_DTYPE = -3,     /* dtype is not SV_F32 / SV_BF16 */
+    SV_ERR_ALIGN = -4,     /* a pointer is not aligned to its element size */
+    SV_ERR_WORKSPACE = -5, /* workspace_bytes smaller than spec_verify_workspace_size() */
+    SV_ERR_HIP = -6        /* a HIP call or kernel launch failed */
+} sv_status_t;
+
+/* Bytes of device workspace one call needs for these sizes (0 on bad sizes). */
+size_t spec_verify_workspace_size(int32_t B, int64_t total_draft, int64_t V, sv_dtype_t dtype);
+
+/* The verify step for B sequences (layout above).  Pass 1 streams every needed
+ * logit row once (row maximum, sum of exp((z - max)/T), or the argmax for
+ * greedy rows); one wavefront per sequence then runs the accept tests and
+ * finds the first rejection; a last fp64 pass over the one rejected or bonus
+ * row pair draws the emitted token by inverse CDF. */
+sv_status_t spec_verify(const void *target_logits, const void *draft_logits,
+                        const int32_t *draft_tokens, const int32_t *offsets,
+                        int32_t k_uniform, int64_t total_draft, int32_t B, int64_t V,
+                        sv_dtype_t dtype, const float *uniforms, const float *temperature,
+                        int32_t *out_tokens, int32_t *out_n_accepted, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/* spec_verify plus diagnostics (each may be NULL):
+ *   out_p, out_q fp32 [total_draft]: p_i(x_i), q_i(x_i) of the tempered
+ *     softmax at every drafted position of sampling sequences (NaN for greedy
+ *     sequences);
+ *   out_row_max, out_row_sumexp fp32 [2 * total_draft + B]: per logit row
+ *     (target rows first, then draft rows) the maximum logit and
+ *     sum_v exp((z_v - max)/T); sumexp is NaN for greedy rows and both are NaN
+ *     for rows that are never read. */
+sv_status_t spec_verify_probs(const void *target_logits, const void *draft_logits,
+                              const int32_t *draft_tokens, const int32_t *offsets,
+                              int32_t k_uniform, int64_t total_draft, int32_t B, int64_t V,
+                              sv_dtype_t dtype, const float *uniforms,
+                              const float *temperature, int32_t *out_tokens,
+                              int32_t *out_n_accepted, float *out_p, float *out_q,
+                              float *out_row_max, float *out_row_sumexp, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *spec_verify_status_string(sv_status_t status);
+
+/* Frees the library-owned workspace of every GPU.  Not safe while a call
+ * that uses it is still running. */
+void spec_verify_release(void);
+
+/* Kernel timing for benchmarks.  While enabled (enable != 0), every call
+ * records a hipEvent pair around each kernel it enqueues, on `stream`.
+ * spec_verify_kernel_times() waits for the most recent call's events and
+ * writes up to max_kernels elapsed times in milliseconds (ms[i] belongs to
+ * spec_verify_kernel_name(i)); it returns the number of kernels, or -1 if no
+ * timed call has been made or a HIP call failed. */
+sv_status_t spec_verify_timing(int32_t enable);
+int32_t spec_verify_kernel_times(float *ms, int32_t max_kernels);
+const char *spec_verify_kernel_name(int32_t i);
+
+/* Benchmark tuning: approximate logits per row-pass segment and per draw
+ * chunk (0 restores the defaults, 16384 and 4096).  The workspace size
+ * depends on them, so query spec_verify_workspace_size() after a change.
+ * Returns SV_ERR_SHAPE for negative values. */
+sv_status_t spec_verify_set_geometry(int64_t seg_elems, int64_t chunk_elems);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

