@@ -1,0 +1,202 @@
+#!/usr/bin/env python3
+"""Throughput of the speculative-sampling verify step on one MI355X.
+
+Workload (default): B=256 sequences, k=8 drafted tokens each, V=152064, bf16
+logits, T=1; half the sequences have near-identical drafts (target + N(0,
+0.1^2): mostly all-accept plus a bonus draw), half have independent N(0, 2^2)
+draft logits (mostly an early rejection plus a residual draw).  Inputs are
+seeded synthetic logits generated on the host and copied to HBM before the
+timed region; `--copies` copies are rotated between steps so no step finds
+its rows in the 256 MB last-level cache.
+
+One step = one spec_verify call (row pass, accept scan, fp64 draw) over the
+whole batch.  Output: one JSON line with sequences/s, the achieved HBM
+bandwidth on algorithmic bytes, the roofline of the dominant kernel (the row
+pass) and the fp64 CPU oracle timed on this host as a baseline.
+
+Algorithmic bytes per step: every needed logit row read once (target rows of
+all sequences, draft rows of sampling sequences) plus one extra read of each
+draw row (2 rows for a residual draw, 1 for a bonus draw, 0 for greedy),
+V * element size per row; the small per-sequence arrays are ignored.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "sequences verified/s and achieved HBM GB/s (% of peak), B=256 k=8 V=152064 bf16"
+COUNTERS = os.path.join(ROOT, "profiles", "row_stats_c4_counters.txt")
+K1_SOURCES = ["row_stats.hip", "sv_internal.h"]
+
+
+def k1_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in K1_SOURCES:
+        with open(os.path.join(ROOT, "speculative_decoding_rejection_spec_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic():
+    """HBM bytes per row-pass launch from the committed rocprofv3 counter
+    summary, or None when missing or taken on different kernel sources."""
+    if not os.path.exists(COUNTERS):
+        return None
+    kv = {}
+    for line in open(COUNTERS):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("k1_source_sha256") != k1_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c4", help="c1 c2 c2g c3 c4 c5")
+    ap.add_argument("--copies", type=int, default=2, help="input copies rotated between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-events", action="store_true",
+                    help="time without the per-kernel HIP events (no roofline)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration runs)")
+    ap.add_argument("--seg", type=int, default=0, help="row-pass segment elements (0 = default)")
+    ap.add_argument("--chunk", type=int, default=0, help="draw chunk elements (0 = default)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the verify step runs sequence-parallel on one device and this build has no "
+              "multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import speculative_decoding_rejection_spec_amd as sv
+    import workloads as wl
+
+    if not os.path.exists(sv.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sv.set_geometry(args.seg, args.chunk)
+
+    t_gen = time.perf_counter()
+    w = wl.make_workload(args.workload)
+    t_gen = time.perf_counter() - t_gen
+
+    def logits(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    copies = []
+    for _ in range(max(1, args.copies)):
+        copies.append(dict(target=logits(w.target), draft=logits(w.draft),
+                           tokens=torch.from_numpy(w.tokens).to(dev),
+                           offsets=torch.from_numpy(w.offsets).to(dev),
+                           uniforms=torch.from_numpy(w.uniforms).to(dev),
+                           temperature=torch.from_numpy(w.temperature).to(dev)))
+    out_tok = torch.empty(w.total + w.B, dtype=torch.int32, device=dev)
+    out_n = torch.empty(w.B, dtype=torch.int32, device=dev)
+    ws = torch.empty(sv.spec_verify_workspace_size(w.B, w.total, w.V, sv.SV_BF16 if w.dtype == "bf16"
+                                                   else sv.SV_F32), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        d = copies[i % len(copies)]
+        sv.spec_verify(d["target"], d["draft"], d["tokens"], d["offsets"], d["uniforms"],
+                       d["temperature"], out_tokens=out_tok, out_n_accepted=out_n, workspace=ws)
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    sv.timing(not args.no_kernel_events)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern = sv.kernel_times() if not args.no_kernel_events else {}
+    sv.timing(False)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # Algorithmic bytes from the realised accept counts.
+    n = out_n.cpu().numpy()
+    elt = w.elem_bytes
+    sampling = w.temperature > 0
+    needed_rows = int(np.sum(w.k + 1) + np.sum(w.k[sampling]))
+    draw_rows = int(np.sum(np.where(sampling, np.where(n < w.k, 2, 1), 0)))
+    row_bytes = w.V * elt
+    k1_bytes = needed_rows * row_bytes
+    total_bytes = (needed_rows + draw_rows) * row_bytes
+    seq_per_s = w.B / (ms_per_step / 1e3)
+    hbm_gbs = total_bytes / (ms_per_step / 1e3) / 1e9
+
+    roofline = None
+    if kern:
+        k1_ms = kern["row_stats"]
+        achieved = k1_bytes / (k1_ms / 1e3) / 1e9
+        roofline = {"bound": "hbm", "kernel": "row_stats", "achieved": round(achieved, 1),
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                    "traffic": committed_traffic(), "algorithmic_bytes": k1_bytes,
+                    "mean_ms": round(k1_ms, 5)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = min(16, os.cpu_count() or 1)
+        tc = time.perf_counter()
+        ref = oracle.verify(w, threads=threads)
+        tc = time.perf_counter() - tc
+        agree = int(np.sum(ref["n"] == n))
+        cpu = {"value": round(w.B / tc, 2), "unit": "sequences/s", "cores": threads,
+               "kind": "oracle", "sample": f"the whole batch ({w.B} sequences) once, "
+               f"fp64 C oracle split over {threads} threads; accept counts agree with the "
+               f"GPU on {agree}/{w.B} sequences"}
+
+    res = {
+        "metric": METRIC, "value": round(seq_per_s, 1), "unit": "sequences/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"verify {args.workload}: B={w.B} k={int(w.k.max()) if w.B else 0} "
+                   f"V={w.V} {w.dtype} logits", "B": w.B, "V": w.V, "k_max": int(w.k.max()),
+                   "total_draft": w.total, "logit_dtype": w.dtype,
+                   "temperatures": sorted(set(float(t) for t in w.temperature)),
+                   "input_copies": len(copies)},
+        "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
+        "algorithmic_bytes": total_bytes, "mean_accepted": round(float(n.mean()), 4),
+        "draw_rows": draw_rows, "kernels_ms": {k: round(v, 5) for k, v in kern.items()},
+        "roofline": roofline, "cpu_baseline": cpu, "gen_s": round(t_gen, 2),
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

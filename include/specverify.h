@@ -125,12 +125,15 @@ const char *spec_verify_status_string(sv_status_t status);
  * that uses it is still running. */
 void spec_verify_release(void);
 
-/* Kernel timing for benchmarks.  While enabled (enable != 0), every call
- * records a hipEvent pair around each kernel it enqueues, on `stream`.
- * spec_verify_kernel_times() waits for the most recent call's events and
- * writes up to max_kernels elapsed times in milliseconds (ms[i] belongs to
+/* Kernel timing for benchmarks.  spec_verify_timing(1) turns the probe on
+ * (and clears what it recorded); while it is on, every call records a
+ * hipEvent pair around each kernel it enqueues, on the call's `stream`, for
+ * the last 256 calls.  spec_verify_kernel_times() waits for the most recent
+ * recorded call and writes, for up to max_kernels kernels, the mean elapsed
+ * milliseconds per call over the recorded calls (ms[i] belongs to
  * spec_verify_kernel_name(i)); it returns the number of kernels, or -1 if no
- * timed call has been made or a HIP call failed. */
+ * call was recorded or a HIP call failed.  The probe uses one device: turn it
+ * off and on again after switching devices. */
 sv_status_t spec_verify_timing(int32_t enable);
 int32_t spec_verify_kernel_times(float *ms, int32_t max_kernels);
 const char *spec_verify_kernel_name(int32_t i);

@@ -1,47 +1,60 @@
 // accept.hip -- the accept scan: one wave64 per sequence.
 //
 // Lane i (i <= k_b) owns position i of its sequence.  It merges the segment
-// statistics of target row i (and draft row i) into the row maximum m and the
-// normaliser S = sum_v exp((z_v - m) / T), gathers the logits of the drafted
-// token x_i, and runs the accept test u_i < alpha_i = min(1, p_i(x_i) /
-// q_i(x_i)) (page "投机解码", section 投机解码的三步流程 step 3; page
-// "大模型推理无损加速:投机采样...", section 二.1).  All k tests run at once; a
-// ballot of the rejections and a find-first-set give n, the index of the first
-// rejection (or k), which is exactly the sequential scan that stops at the
-// first rejection.  Greedy sequences (T = 0) accept while x_i equals the target
-// argmax and emit the argmax of row n (section 动手实践, greedy branch).
+// statistics of target row i (and draft row i) into the row maximum and the
+// normaliser, gathers the logits of the drafted token x_i, and runs the
+// accept test u_i < alpha_i = min(1, p_i(x_i) / q_i(x_i)) (page "投机解码",
+// section 投机解码的三步流程 step 3; page "大模型推理无损加速:投机采样...",
+// section 二.1).  All k tests run at once; a ballot of the rejections and a
+// find-first-set give n, the first rejection (or k) -- the same n as a scan
+// that stops at the first rejection.  Greedy sequences (T = 0) accept while
+// x_i equals the target argmax and emit the argmax of row n (section 动手实践,
+// greedy branch).
 //
-// p_i(x_i) and q_i(x_i) are formed in fp64 from the exact logits and row
-// maxima; only S carries the fp32 rounding of the row pass (relative error of
-// order 1e-7, far inside the 1e-5 band in which |u - alpha| counts as a tie).
+// The row pass keeps S_R = sum_v 2^(z_v c - R) with c = log2(e)/T rounded to
+// fp32 and an integer reference R, so p(x) = 2^(z_x c - R) / S_R exactly as
+// the row pass summed it (a softmax at the temperature log2(e)/c, within
+// 6e-8 relative of T); it is formed in fp64.  Worst-case relative error of
+// S_R: about 2e-6 (fp32 partial sums of <= 40 terms, v_exp_f32, the rounded
+// exponent argument); alpha is therefore within 5e-6 of its exact value,
+// inside the 1e-5 band where |u - alpha| counts as a tie.
 //
-// Sampling sequences leave the emitted token to the draw kernels and record a
-// DrawTask: residual draw at row n if n < k, bonus draw at row k otherwise.
+// Sampling sequences leave the emitted token to the draw kernel and record a
+// DrawTask: a residual draw at row n if n < k, a bonus draw at row k
+// otherwise.
 #include "sv_internal.h"
 
 namespace sv {
 namespace {
 
 struct RowStat {
-    float m;
-    int32_t arg;
-    double S;
+    float m;       // row maximum
+    int32_t arg;   // greedy: lowest token id holding m
+    float R;       // sampling: reference exponent
+    double S;      // sampling: sum of 2^(z c - R)
 };
 
-// Merges the nseg segment statistics of one row.  Sampling rows: m = max of
-// the segment maxima, S = sum of segment sums rescaled to m (fp64).  Greedy
-// rows: m and the lowest token id holding it.
-__device__ __forceinline__ RowStat merge_row(const SegStat* seg, int32_t nseg, bool greedy, double T) {
-    RowStat r{-INFINITY, INT32_MAX, 0.0};
-    for (int32_t s = 0; s < nseg; ++s) r.m = fmaxf(r.m, seg[s].m);
+// Merges the nseg segment statistics of one row (exact power-of-two
+// rescaling for sampling rows; lowest id among tied maxima for greedy rows).
+__device__ __forceinline__ RowStat merge_row(const SegStat* seg, int32_t nseg, bool greedy) {
+    RowStat r{-INFINITY, INT32_MAX, -INFINITY, 0.0};
+    for (int32_t s = 0; s < nseg; ++s) {
+        r.m = fmaxf(r.m, seg[s].m);
+        r.R = fmaxf(r.R, seg[s].R);
+    }
     for (int32_t s = 0; s < nseg; ++s) {
         if (greedy) {
             if (seg[s].m == r.m && seg[s].arg < r.arg) r.arg = seg[s].arg;
-        } else if (seg[s].m != -INFINITY) {
-            r.S += seg[s].s * exp((static_cast<double>(seg[s].m) - r.m) / T);
+        } else if (seg[s].R != -INFINITY) {
+            r.S += ldexp(seg[s].s, static_cast<int>(fmaxf(seg[s].R - r.R, -2048.f)));
         }
     }
     return r;
+}
+
+// ln of the normaliser sum_v exp((z_v - m)/T) of a merged sampling row.
+__device__ __forceinline__ double log_norm(const RowStat& r, float c) {
+    return log(r.S) + (static_cast<double>(r.R) - static_cast<double>(r.m) * c) * 0.6931471805599453;
 }
 
 __global__ __launch_bounds__(kThreads) void accept_kernel(Problem p, Plan plan) {
@@ -58,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(Problem p, Plan plan) 
     bool ok = o >= 0 && k64 >= 0 && k64 <= kKMax && o1 <= p.total && temperature_ok(Tf);
     const int k = ok ? static_cast<int>(k64) : 0;
     const bool greedy = (Tf == 0.f);
-    const double T = static_cast<double>(Tf);
+    const float c = greedy ? 0.f : row_scale(Tf);
     const int64_t trow = o + b + lane;             // this lane's target row
     const int64_t drow = o + lane;                 // this lane's draft row
 
@@ -67,12 +80,12 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(Problem p, Plan plan) 
         x = p.tokens[drow];
         if (x < 0 || x >= p.V) ok = false;
     }
-    RowStat rt{0.f, 0, 1.0}, rd{0.f, 0, 1.0};
+    RowStat rt{0.f, 0, 0.f, 1.0}, rd{0.f, 0, 0.f, 1.0};
     if (ok && lane <= k) {
-        rt = merge_row(plan.seg + trow * plan.nseg, plan.nseg, greedy, T);
+        rt = merge_row(plan.seg + trow * plan.nseg, plan.nseg, greedy);
         if (!(fabsf(rt.m) <= 3.4e38f)) ok = false;
         if (!greedy && lane < k) {
-            rd = merge_row(plan.seg + (ntarget + drow) * plan.nseg, plan.nseg, false, T);
+            rd = merge_row(plan.seg + (ntarget + drow) * plan.nseg, plan.nseg, false);
             if (!(fabsf(rd.m) <= 3.4e38f)) ok = false;
         }
     }
@@ -98,8 +111,8 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(Problem p, Plan plan) 
         } else {
             const double zt = load_logit(p.target, p.dtype, trow * p.V + x);
             const double zd = load_logit(p.draft, p.dtype, drow * p.V + x);
-            px = exp((zt - rt.m) / T) / rt.S;
-            qx = exp((zd - rd.m) / T) / rd.S;
+            px = exp2(zt * c - rt.R) / rt.S;
+            qx = exp2(zd * c - rd.R) / rd.S;
             const double alpha = fmin(1.0, px / qx);
             reject = !(static_cast<double>(p.uniforms[trow]) < alpha);
         }
@@ -124,6 +137,7 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(Problem p, Plan plan) 
         t.m_d = n < k ? rd.m : 0.f;
         t.T = Tf;
         t.u = p.uniforms[o + b + k];
+        t.theta = (!greedy && n < k) ? log_norm(rt, c) - log_norm(rd, c) : 0.0;
         plan.task[b] = t;
     }
     if (p.out_p && lane < k) {
@@ -132,10 +146,10 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(Problem p, Plan plan) 
     }
     if (p.out_row_max && lane <= k) {
         p.out_row_max[trow] = rt.m;
-        p.out_row_sum[trow] = greedy ? NAN : static_cast<float>(rt.S);
+        p.out_row_sum[trow] = greedy ? NAN : static_cast<float>(exp(log_norm(rt, c)));
         if (lane < k) {
             p.out_row_max[ntarget + drow] = greedy ? NAN : rd.m;
-            p.out_row_sum[ntarget + drow] = greedy ? NAN : static_cast<float>(rd.S);
+            p.out_row_sum[ntarget + drow] = greedy ? NAN : static_cast<float>(exp(log_norm(rd, c)));
         }
     }
 }

@@ -1,23 +1,27 @@
 // row_stats.hip -- pass 1 of the verify step: one streaming read of every
 // needed logit row.
 //
-// Both acceptance tests and the bonus draw need the tempered softmax
+// The accept tests and the bonus draw need the tempered softmax
 // p = softmax(z / T) of each target row and q of each draft row (page
 // "投机解码", section 动手实践; page "大模型推理无损加速:投机采样...", section 三,
-// which softmaxes all gamma target positions at once).  Only two scalars per
-// row are needed for that: the maximum m and S = sum_v exp((z_v - m) / T);
-// p(x) = exp((z_x - m) / T) / S is then formed for the one drafted token in
-// the accept scan.  Greedy rows (T = 0) need only the argmax (lowest token id
-// on ties, the greedy branch of the same 动手实践 section).
+// which softmaxes all gamma target positions at once).  Two scalars per row
+// suffice: the maximum m and S = sum_v exp((z_v - m) / T); p(x) for the one
+// drafted token is formed later in the accept scan.  Greedy rows (T = 0)
+// need only the argmax, lowest token id on ties (greedy branch of the same
+// 动手实践 section).
 //
 // Work decomposition: the grid is (rows x segments); each 256-thread
-// workgroup streams one contiguous segment of one row with 16-byte
-// non-temporal loads (8 bf16 or 4 fp32 logits per lane, kUnroll loads in
-// flight per lane), keeps an online (max, sum) per lane, and reduces across
-// the workgroup in fp64 at the end.  Per element: one unpack, one max, one
-// subtract, one multiply, one v_exp_f32, one add.  Splitting rows into
-// segments keeps the grid far above the 256 CUs x 8 workgroups the chip can
-// hold, so the last wave of workgroups is short.
+// workgroup streams one contiguous segment of one row.  Each lane owns every
+// 256th 16-byte vector of the segment (8 bf16 or 4 fp32 logits) and keeps a
+// rolling window of kWindow non-temporal loads in flight: the load that
+// replaces a vector is issued before that vector is processed, so memory
+// requests stay outstanding while the lane computes.
+//
+// Per logit: one unpack (shift or mask), half a v_max3, one v_fma
+// (z * c - R), one v_exp_f32, one add.  The running sum is kept relative to an
+// integer-valued reference R = ceil(m * c) (c = log2(e) / T), so rescaling
+// when the maximum grows is an exact v_ldexp; the workgroup-wide merge is in
+// fp64, also by exact powers of two.
 #include "sv_internal.h"
 
 namespace sv {
@@ -25,7 +29,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kUnroll = 4;   // 16-byte loads per lane per batch
+constexpr int kWindow = 8;   // 16-byte loads in flight per lane
 
 __device__ __forceinline__ u32x4 stream_load(const u32x4* p) {
     return __builtin_nontemporal_load(p);
@@ -55,38 +59,44 @@ template <> struct Elem<SV_F32> {
     }
 };
 
-// Online max / sum of exp2((z - m) * c) with c = log2(e) / T, four partial
-// sums to shorten the add dependency chains.
+template <int N>
+__device__ __forceinline__ float max_of(const float* x) {
+    float t = x[0];
+#pragma unroll
+    for (int j = 1; j < N; ++j) t = fmaxf(t, x[j]);
+    return t;
+}
+
+// Online sum of 2^(z*c - R) with R = ceil(m*c) for the running maximum m.
 struct SoftmaxAcc {
-    float m = -INFINITY;
+    float m = -INFINITY;    // running maximum logit
+    float R = -INFINITY;    // reference exponent (integer valued)
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
     float c;
 
+    __device__ __forceinline__ void raise(float tm) {
+        const float Rn = ceilf(tm * c);
+        // exact rescale by 2^(R - Rn); R = -inf only while the sums are 0
+        const int d = static_cast<int>(fmaxf(R - Rn, -512.f));
+        s0 = ldexpf(s0, d); s1 = ldexpf(s1, d); s2 = ldexpf(s2, d); s3 = ldexpf(s3, d);
+        m = tm;
+        R = Rn;
+    }
     template <int N>
-    __device__ __forceinline__ void add(const float* x, const int32_t*) {
-        float tm = x[0];
-#pragma unroll
-        for (int j = 1; j < N; ++j) tm = fmaxf(tm, x[j]);
-        if (tm > m) {
-            const float sc = hw_exp2((m - tm) * c);
-            s0 *= sc; s1 *= sc; s2 *= sc; s3 *= sc;
-            m = tm;
-        }
+    __device__ __forceinline__ void add(const float* x, int32_t) {
+        const float tm = max_of<N>(x);
+        if (tm > m) raise(tm);
 #pragma unroll
         for (int j = 0; j < N; j += 4) {
-            s0 += hw_exp2((x[j] - m) * c);
-            if (j + 1 < N) s1 += hw_exp2((x[j + 1] - m) * c);
-            if (j + 2 < N) s2 += hw_exp2((x[j + 2] - m) * c);
-            if (j + 3 < N) s3 += hw_exp2((x[j + 3] - m) * c);
+            s0 += hw_exp2(fmaf(x[j], c, -R));
+            if (j + 1 < N) s1 += hw_exp2(fmaf(x[j + 1], c, -R));
+            if (j + 2 < N) s2 += hw_exp2(fmaf(x[j + 2], c, -R));
+            if (j + 3 < N) s3 += hw_exp2(fmaf(x[j + 3], c, -R));
         }
     }
     __device__ __forceinline__ void add1(float x, int32_t) {
-        if (x > m) {
-            const float sc = hw_exp2((m - x) * c);
-            s0 *= sc; s1 *= sc; s2 *= sc; s3 *= sc;
-            m = x;
-        }
-        s0 += hw_exp2((x - m) * c);
+        if (x > m) raise(x);
+        s0 += hw_exp2(fmaf(x, c, -R));
     }
 };
 
@@ -97,10 +107,16 @@ struct ArgmaxAcc {
     int32_t a = INT32_MAX;
 
     template <int N>
-    __device__ __forceinline__ void add(const float* x, const int32_t* idx) {
+    __device__ __forceinline__ void add(const float* x, int32_t base) {
+        const float tm = max_of<N>(x);
+        if (tm > m) {
+            int32_t j = 0;
 #pragma unroll
-        for (int j = 0; j < N; ++j)
-            if (x[j] > m) { m = x[j]; a = idx[j]; }
+            for (int e = N - 1; e >= 0; --e)
+                if (x[e] == tm) j = e;
+            m = tm;
+            a = base + j;
+        }
     }
     __device__ __forceinline__ void add1(float x, int32_t i) {
         if (x > m) { m = x; a = i; }
@@ -108,8 +124,8 @@ struct ArgmaxAcc {
 };
 
 // Streams logits [s0, s1) of one row into acc.  Order per lane: the
-// unaligned head element, full batches of kUnroll vectors, the remaining
-// vectors, the tail element -- increasing token ids throughout.
+// unaligned head element, its vectors in increasing order, the tail element
+// -- increasing token ids throughout.
 template <int DT, class Acc>
 __device__ __forceinline__ void stream_segment(const void* row_v, int64_t s0, int64_t s1, Acc& acc) {
     using E = typename Elem<DT>::T;
@@ -120,48 +136,53 @@ __device__ __forceinline__ void stream_segment(const void* row_v, int64_t s0, in
     int64_t head = static_cast<int64_t>(((16u - (addr & 15u)) & 15u) / sizeof(E));
     if (head > s1 - s0) head = s1 - s0;
     const int64_t a0 = s0 + head;
-    const int64_t nvec = (s1 - a0) / N;
-    const int64_t a1 = a0 + nvec * N;
+    const int32_t nvec = static_cast<int32_t>((s1 - a0) / N);
+    const int64_t a1 = a0 + static_cast<int64_t>(nvec) * N;
 
     if (tid < head) acc.add1(load_logit(row_v, DT, s0 + tid), static_cast<int32_t>(s0 + tid));
 
-    const u32x4* vp = reinterpret_cast<const u32x4*>(row + a0);
-    constexpr int64_t kPerBatch = static_cast<int64_t>(kThreads) * kUnroll;
-    const int64_t nbatch = nvec / kPerBatch;
-    for (int64_t bt = 0; bt < nbatch; ++bt) {
-        u32x4 v[kUnroll];
+    // Lane tid owns vectors g = tid + j * 256 < nvec.  The loop runs a
+    // workgroup-uniform ub = ceil(nvec / 256) steps and every load condition
+    // is uniform, so loads stay in flight across steps; a lane whose last
+    // vector does not exist re-reads the segment's last vector (a cache hit)
+    // and skips processing it.
+    if (nvec > 0) {
+        const u32x4* vp = reinterpret_cast<const u32x4*>(row + a0);
+        const int32_t ub = (nvec + kThreads - 1) / kThreads;
+        const int32_t lane_cnt = (nvec - tid + kThreads - 1) / kThreads;
+        auto addr_of = [&](int32_t j) { return vp + min(tid + j * kThreads, nvec - 1); };
+        const int32_t base0 = static_cast<int32_t>(a0) + tid * N;
+        u32x4 buf[kWindow];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) v[u] = stream_load(vp + bt * kPerBatch + u * kThreads + tid);
-        float x[kUnroll * N];
-        int32_t idx[kUnroll * N];
+        for (int u = 0; u < kWindow; ++u)
+            if (u < ub) buf[u] = stream_load(addr_of(u));
+        for (int32_t i = 0; i < ub; i += kWindow) {
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            Elem<DT>::unpack(v[u], x + u * N);
-            const int32_t base = static_cast<int32_t>(a0 + (bt * kPerBatch + u * kThreads + tid) * N);
-#pragma unroll
-            for (int e = 0; e < N; ++e) idx[u * N + e] = base + e;
+            for (int u = 0; u < kWindow; ++u) {
+                if (i + u < ub) {
+                    const u32x4 v = buf[u];
+                    if (i + kWindow + u < ub) buf[u] = stream_load(addr_of(i + kWindow + u));
+                    if (i + u < lane_cnt) {
+                        float x[N];
+                        Elem<DT>::unpack(v, x);
+                        acc.template add<N>(x, base0 + (i + u) * kThreads * N);
+                    }
+                }
+            }
         }
-        acc.template add<kUnroll * N>(x, idx);
-    }
-    for (int64_t j = nbatch * kPerBatch + tid; j < nvec; j += kThreads) {
-        float x[N];
-        int32_t idx[N];
-        Elem<DT>::unpack(stream_load(vp + j), x);
-        const int32_t base = static_cast<int32_t>(a0 + j * N);
-#pragma unroll
-        for (int e = 0; e < N; ++e) idx[e] = base + e;
-        acc.template add<N>(x, idx);
     }
     if (tid < s1 - a1) acc.add1(load_logit(row_v, DT, a1 + tid), static_cast<int32_t>(a1 + tid));
 }
 
-// (m, s) of two partial softmax sums over the same row, in fp64; cd = log2(e)/T.
-__device__ __forceinline__ void merge_softmax(float& m, double& s, float m2, double s2, double cd) {
-    const float mn = fmaxf(m, m2);
-    const double a = (m == -INFINITY) ? 0.0 : s * exp2((static_cast<double>(m) - mn) * cd);
-    const double b = (m2 == -INFINITY) ? 0.0 : s2 * exp2((static_cast<double>(m2) - mn) * cd);
-    m = mn;
-    s = a + b;
+// Two partial sums s * 2^R of the same row, merged exactly in fp64.
+__device__ __forceinline__ void merge_softmax(float& m, float& R, double& s, float m2, float R2, double s2) {
+    m = fmaxf(m, m2);
+    if (R2 == -INFINITY) return;
+    if (R == -INFINITY) { R = R2; s = s2; return; }
+    const float Rn = fmaxf(R, R2);
+    s = ldexp(s, static_cast<int>(fmaxf(R - Rn, -2048.f))) +
+        ldexp(s2, static_cast<int>(fmaxf(R2 - Rn, -2048.f)));
+    R = Rn;
 }
 
 __device__ __forceinline__ void merge_argmax(float& m, int32_t& a, float m2, int32_t a2) {
@@ -187,11 +208,10 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(Problem p, Plan pla
     const int64_t s0 = seg * plan.seg_len;
     const int64_t s1 = min(p.V, s0 + plan.seg_len);
 
-    __shared__ float lds_m[kWaves];
+    __shared__ float lds_m[kWaves], lds_R[kWaves];
     __shared__ double lds_s[kWaves];
     __shared__ int32_t lds_a[kWaves];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    SegStat out;
 
     if (greedy) {
         ArgmaxAcc acc;
@@ -204,25 +224,28 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(Problem p, Plan pla
         __syncthreads();
         if (threadIdx.x == 0) {
             for (int i = 1; i < kWaves; ++i) merge_argmax(m, a, lds_m[i], lds_a[i]);
-            out.m = m; out.arg = a; out.s = 0.0;
+            SegStat out;
+            out.m = m; out.R = 0.f; out.arg = a; out.pad = 0; out.s = 0.0;
+            plan.seg[w] = out;
         }
     } else {
-        const double cd = 1.4426950408889634 / static_cast<double>(T);
         SoftmaxAcc acc;
-        acc.c = static_cast<float>(fmin(cd, 3.0e38));
+        acc.c = row_scale(T);
         stream_segment<DT>(row, s0, s1, acc);
-        float m = acc.m;
+        float m = acc.m, R = acc.R;
         double s = (static_cast<double>(acc.s0) + acc.s1) + (static_cast<double>(acc.s2) + acc.s3);
         for (int off = 32; off > 0; off >>= 1)
-            merge_softmax(m, s, __shfl_xor(m, off, 64), __shfl_xor(s, off, 64), cd);
-        if (lane == 0) { lds_m[wave] = m; lds_s[wave] = s; }
+            merge_softmax(m, R, s, __shfl_xor(m, off, 64), __shfl_xor(R, off, 64),
+                          __shfl_xor(s, off, 64));
+        if (lane == 0) { lds_m[wave] = m; lds_R[wave] = R; lds_s[wave] = s; }
         __syncthreads();
         if (threadIdx.x == 0) {
-            for (int i = 1; i < kWaves; ++i) merge_softmax(m, s, lds_m[i], lds_s[i], cd);
-            out.m = m; out.arg = 0; out.s = s;
+            for (int i = 1; i < kWaves; ++i) merge_softmax(m, R, s, lds_m[i], lds_R[i], lds_s[i]);
+            SegStat out;
+            out.m = m; out.R = R; out.arg = 0; out.pad = 0; out.s = s;
+            plan.seg[w] = out;
         }
     }
-    if (threadIdx.x == 0) plan.seg[w] = out;
 }
 
 }  // namespace

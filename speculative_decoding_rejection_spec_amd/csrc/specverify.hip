@@ -11,12 +11,12 @@ namespace {
 using namespace sv;
 
 constexpr int64_t kDefaultSegElems = 16384;   // row-pass segment length before rounding
-constexpr int64_t kDefaultChunkElems = 4096;  // draw chunk length before rounding
+constexpr int64_t kDefaultChunkElems = 8192;  // draw chunk length before rounding
+constexpr int64_t kMaxChunks = 1024;          // draw chunks per row (the pick keeps them in LDS)
 constexpr int kMaxDevices = 64;
-constexpr int kNumKernels = 5;
+constexpr int kNumKernels = 4;
 
-const char* const kKernelNames[kNumKernels] = {"row_stats", "accept", "draw_sums",
-                                               "draw_residual", "draw_pick"};
+const char* const kKernelNames[kNumKernels] = {"row_stats", "accept", "draw_sums", "draw_pick"};
 
 std::mutex g_mutex;
 int64_t g_seg_elems = kDefaultSegElems;
@@ -26,11 +26,12 @@ int64_t g_chunk_elems = kDefaultChunkElems;
 void* g_ws[kMaxDevices] = {};
 size_t g_ws_bytes[kMaxDevices] = {};
 
-// Timing probe state.
+// Timing probe state: a ring of event pairs for the last kTimedCalls calls.
+constexpr int kTimedCalls = 256;
 bool g_timing = false;
-bool g_timing_valid = false;
+int64_t g_timed_calls = 0;            // calls recorded since the probe was enabled
 int g_timing_device = -1;
-hipEvent_t g_ev[2 * kNumKernels] = {};
+hipEvent_t g_ev[kTimedCalls][2 * kNumKernels] = {};
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -38,22 +39,23 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 struct Geometry {
     int32_t nseg, nchunk;
     int64_t seg_len, chunk_len;
-    size_t off_seg, off_task, off_csum, off_cres, bytes;
+    size_t off_seg, off_task, off_csum, off_band, bytes;
 };
 
-// Splits a row of V logits into n pieces of about `target` elements, each a
-// multiple of 8 elements (16 bytes of bf16) long and none empty.
-void split(int64_t V, int64_t target, int32_t& n, int64_t& len) {
+// Splits a row of V logits into n <= max_pieces pieces of about `target`
+// elements, each a multiple of 8 elements (16 bytes of bf16) long, none empty.
+void split(int64_t V, int64_t target, int64_t max_pieces, int32_t& n, int64_t& len) {
     int64_t pieces = (V + target / 2) / target;
     if (pieces < 1) pieces = 1;
+    if (pieces > max_pieces) pieces = max_pieces;
     len = ceil_div(ceil_div(V, pieces), 8) * 8;
     n = static_cast<int32_t>(ceil_div(V, len));
 }
 
 bool make_geometry(int32_t B, int64_t total, int64_t V, int64_t seg_elems, int64_t chunk_elems,
                    Geometry& g) {
-    split(V, seg_elems, g.nseg, g.seg_len);
-    split(V, chunk_elems, g.nchunk, g.chunk_len);
+    split(V, seg_elems, 1 << 20, g.nseg, g.seg_len);
+    split(V, chunk_elems, kMaxChunks, g.nchunk, g.chunk_len);
     const int64_t rows = 2 * total + B;
     if (rows * g.nseg > 0xFFFFFFFFll || static_cast<int64_t>(B) * g.nchunk > 0xFFFFFFFFll) return false;
     size_t off = 0;
@@ -62,9 +64,9 @@ bool make_geometry(int32_t B, int64_t total, int64_t V, int64_t seg_elems, int64
     g.off_task = off;
     off = align256(off + sizeof(DrawTask) * static_cast<size_t>(B));
     g.off_csum = off;
-    off = align256(off + sizeof(double) * 2 * static_cast<size_t>(B) * g.nchunk);
-    g.off_cres = off;
-    off = align256(off + sizeof(double) * static_cast<size_t>(B) * g.nchunk);
+    off = align256(off + sizeof(ChunkSums) * static_cast<size_t>(B) * g.nchunk);
+    g.off_band = off;
+    off = align256(off + sizeof(int32_t) * kBandSlots * static_cast<size_t>(B) * g.nchunk);
     g.bytes = off;
     return true;
 }
@@ -132,30 +134,36 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     plan.chunk_len = g.chunk_len;
     plan.seg = reinterpret_cast<SegStat*>(ws + g.off_seg);
     plan.task = reinterpret_cast<DrawTask*>(ws + g.off_task);
-    plan.csum = reinterpret_cast<double*>(ws + g.off_csum);
-    plan.cres = reinterpret_cast<double*>(ws + g.off_cres);
+    plan.csum = reinterpret_cast<ChunkSums*>(ws + g.off_csum);
+    plan.band = reinterpret_cast<int32_t*>(ws + g.off_band);
 
+    hipEvent_t* ev = nullptr;
     if (g_timing) {
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess) return SV_ERR_HIP;
         if (g_timing_device != dev) {
-            for (int i = 0; i < 2 * kNumKernels; ++i) {
-                if (g_ev[i]) (void)hipEventDestroy(g_ev[i]);
-                g_ev[i] = nullptr;
-                if (hipEventCreate(&g_ev[i]) != hipSuccess) return SV_ERR_HIP;
-            }
+            for (auto& call : g_ev)
+                for (auto& e : call) {
+                    if (e) (void)hipEventDestroy(e);
+                    e = nullptr;
+                }
+            for (auto& call : g_ev)
+                for (auto& e : call)
+                    if (hipEventCreate(&e) != hipSuccess) return SV_ERR_HIP;
             g_timing_device = dev;
+            g_timed_calls = 0;
         }
+        ev = g_ev[g_timed_calls % kTimedCalls];
     }
     typedef hipError_t (*Launcher)(const Problem&, const Plan&, hipStream_t);
     const Launcher launchers[kNumKernels] = {launch_row_stats, launch_accept, launch_draw_sums,
-                                             launch_draw_residual, launch_draw_pick};
+                                             launch_draw_pick};
     for (int i = 0; i < kNumKernels; ++i) {
-        if (g_timing && hipEventRecord(g_ev[2 * i], stream) != hipSuccess) return SV_ERR_HIP;
+        if (ev && hipEventRecord(ev[2 * i], stream) != hipSuccess) return SV_ERR_HIP;
         if (launchers[i](p, plan, stream) != hipSuccess) return SV_ERR_HIP;
-        if (g_timing && hipEventRecord(g_ev[2 * i + 1], stream) != hipSuccess) return SV_ERR_HIP;
+        if (ev && hipEventRecord(ev[2 * i + 1], stream) != hipSuccess) return SV_ERR_HIP;
     }
-    g_timing_valid = g_timing;
+    if (ev) ++g_timed_calls;
     return SV_OK;
 }
 
@@ -251,17 +259,26 @@ void spec_verify_release(void) {
 sv_status_t spec_verify_timing(int32_t enable) {
     std::lock_guard<std::mutex> lock(g_mutex);
     g_timing = enable != 0;
-    g_timing_valid = false;
+    g_timed_calls = 0;
     return SV_OK;
 }
 
 int32_t spec_verify_kernel_times(float* ms, int32_t max_kernels) {
     std::lock_guard<std::mutex> lock(g_mutex);
-    if (!g_timing_valid || !ms) return -1;
-    if (hipEventSynchronize(g_ev[2 * kNumKernels - 1]) != hipSuccess) return -1;
+    if (g_timed_calls == 0 || !ms) return -1;
+    const int64_t ncalls = g_timed_calls < kTimedCalls ? g_timed_calls : kTimedCalls;
+    const int64_t last = (g_timed_calls - 1) % kTimedCalls;
+    if (hipEventSynchronize(g_ev[last][2 * kNumKernels - 1]) != hipSuccess) return -1;
     const int n = max_kernels < kNumKernels ? max_kernels : kNumKernels;
-    for (int i = 0; i < n; ++i)
-        if (hipEventElapsedTime(&ms[i], g_ev[2 * i], g_ev[2 * i + 1]) != hipSuccess) return -1;
+    for (int i = 0; i < n; ++i) {
+        double sum = 0.0;
+        for (int64_t c = 0; c < ncalls; ++c) {
+            float t = 0.f;
+            if (hipEventElapsedTime(&t, g_ev[c][2 * i], g_ev[c][2 * i + 1]) != hipSuccess) return -1;
+            sum += t;
+        }
+        ms[i] = static_cast<float>(sum / ncalls);
+    }
     return kNumKernels;
 }
 

@@ -1,15 +1,15 @@
 // sv_internal.h -- declarations shared by the HIP sources of libspecverify.
 //
 // Data flow of one call (every kernel is enqueued on the caller's stream):
-//   1. row pass      (row_stats.hip): one workgroup per (logit row, segment)
-//                    streams the segment once and writes a SegStat;
-//   2. accept scan   (accept.hip): one wave64 per sequence combines the
-//                    segments of its rows, runs the k accept tests, finds the
-//                    first rejection and writes the accepted tokens and a
-//                    DrawTask;
-//   3. draw          (draw.hip): fp64 chunk sums over the one rejected or
-//                    bonus row pair, then one workgroup per sequence finds the
-//                    inverse-CDF token inside the chunk that holds u * Z.
+//   1. row pass    (row_stats.hip): one workgroup per (logit row, segment)
+//                  streams the segment once and writes a SegStat;
+//   2. accept scan (accept.hip): one wave64 per sequence merges the segments
+//                  of its rows, runs the k accept tests, finds the first
+//                  rejection, writes the accepted tokens and a DrawTask;
+//   3. draw_sums   (draw.hip): one workgroup per (sequence, chunk) of the one
+//                  rejected or bonus row pair accumulates fp64 chunk sums;
+//   4. draw_pick   (draw.hip): one workgroup per sequence locates the chunk
+//                  that holds u * Z and the token inside it.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -22,24 +22,39 @@ namespace sv {
 constexpr int kThreads = 256;          // workgroup size of every kernel (4 x wave64)
 constexpr int kWaves = kThreads / 64;
 constexpr int kKMax = SV_K_MAX;
+constexpr int kWaveCap = 8;            // band tokens listed per wave of a draw chunk
+constexpr int kBandSlots = kWaves + kWaves * kWaveCap;   // per chunk: counts, then ids
 
-// Statistics of one segment of one logit row.
-struct alignas(16) SegStat {
+// Statistics of one segment of one logit row.  Sampling rows keep their sum
+// as s * 2^R with an integer-valued reference R >= max(z) * c, c = log2(e)/T
+// (row_scale below), so every rescale is an exact power of two.
+struct SegStat {
     float m;       // largest logit in the segment (exact)
+    float R;       // sampling rows: reference exponent (integer valued)
     int32_t arg;   // greedy rows: lowest token id holding m
-    double s;      // sampling rows: sum over the segment of exp((z - m) / T)
+    int32_t pad;
+    double s;      // sampling rows: sum over the segment of 2^(z*c - R)
 };
 
 enum : int32_t { kNone = 0, kResidual = 1, kBonus = 2 };
 
 // The draw one sequence still needs after the accept scan.
-struct alignas(16) DrawTask {
+struct DrawTask {
     int32_t kind;      // kNone (greedy, error), kResidual (n < k) or kBonus (n = k)
     int32_t out_slot;  // index into out_tokens of the emitted token
     int64_t trow;      // target row at position n
     int64_t drow;      // draft row at position n (kResidual only)
     float m_t, m_d;    // exact maxima of those rows
     float T, u;        // temperature and the draw uniform
+    double theta;      // ln(S_p / S_q) from the row pass: p_v > q_v iff d_v > theta
+};
+
+// Per-chunk partial sums of the draw (fp64).
+struct ChunkSums {
+    double sp;   // sum of w_t = exp((z_t - m_t)/T) over the chunk
+    double sq;   // sum of w_d over the chunk (residual)
+    double a;    // sum of w_t over tokens robustly classified p > q
+    double b;    // sum of w_d over the same tokens
 };
 
 // The caller's arguments, passed by value to every kernel.
@@ -71,15 +86,14 @@ struct Plan {
     int64_t chunk_len;   // elements per chunk (multiple of 8)
     SegStat* seg;        // [(2 * total + B) * nseg]; target rows first
     DrawTask* task;      // [B]
-    double* csum;        // [B * nchunk * 2]: per chunk sum of w_t and w_d
-    double* cres;        // [B * nchunk]: per chunk residual mass
+    ChunkSums* csum;     // [B * nchunk]
+    int32_t* band;       // [B * nchunk * kBandSlots]: per-wave counts, then token ids
 };
 
 // Host-side launchers (one per kernel).
 hipError_t launch_row_stats(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_accept(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_draw_sums(const Problem& p, const Plan& plan, hipStream_t s);
-hipError_t launch_draw_residual(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_draw_pick(const Problem& p, const Plan& plan, hipStream_t s);
 
 // ---- device helpers shared by the kernels ---------------------------------
@@ -90,8 +104,10 @@ __device__ __forceinline__ float load_logit(const void* base, int32_t dtype, int
     return static_cast<const float*>(base)[idx];
 }
 
-__device__ __forceinline__ int64_t seq_first_draft(const Problem& p, int32_t b) {
-    return p.offsets ? static_cast<int64_t>(p.offsets[b]) : static_cast<int64_t>(b) * p.k_uniform;
+// c = log2(e) / T as the row pass uses it (the accept scan must form the same
+// float).  Capped at 2^60: beyond that every non-maximal term underflows.
+__device__ __forceinline__ float row_scale(float T) {
+    return static_cast<float>(fmin(1.4426950408889634 / static_cast<double>(T), 0x1p60));
 }
 
 // Sequence owning target row r: the largest b with first_draft(b) + b <= r.
@@ -116,7 +132,7 @@ __device__ __forceinline__ int32_t seq_of_draft_row(const Problem& p, int64_t r)
     return lo;
 }
 
-// Temperature of a sampling row is usable; T == 0 is greedy.
+// Temperature usable: T == 0 is greedy, T > 0 finite is sampling.
 __device__ __forceinline__ bool temperature_ok(float T) { return T >= 0.f && T <= 3.4e38f; }
 
 // Sum of a double over the workgroup; the result is valid in every thread.

@@ -44,6 +44,7 @@ def test_status_strings(lib):
         assert s and s != "unknown status"
     assert lib.spec_verify_status_string(-99).decode() == "unknown status"
     assert lib.spec_verify_kernel_name(0).decode() == "row_stats"
+    assert lib.spec_verify_kernel_name(3).decode() == "draw_pick"
     assert lib.spec_verify_kernel_name(99) is None
 
 
