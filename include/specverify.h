@@ -139,7 +139,7 @@ int32_t spec_verify_kernel_times(float *ms, int32_t max_kernels);
 const char *spec_verify_kernel_name(int32_t i);
 
 /* Benchmark tuning: approximate logits per row-pass segment and per draw
- * chunk (0 restores the defaults, 16384 and 4096).  The workspace size
+ * chunk (0 restores the defaults, 65536 and 8192).  The workspace size
  * depends on them, so query spec_verify_workspace_size() after a change.
  * Returns SV_ERR_SHAPE for negative values. */
 sv_status_t spec_verify_set_geometry(int64_t seg_elems, int64_t chunk_elems);

@@ -12,8 +12,9 @@
 // greedy branch).
 //
 // The row pass keeps S_R = sum_v 2^(z_v c - R) with c = log2(e)/T rounded to
-// fp32 and an integer reference R, so p(x) = 2^(z_x c - R) / S_R exactly as
-// the row pass summed it (a softmax at the temperature log2(e)/c, within
+// fp32 and an integer reference R, and captures z_x, the logit of the
+// drafted token of each row; p(x) = 2^(z_x c - R) / S_R exactly as the row
+// pass summed it (a softmax at the temperature log2(e)/c, within
 // 6e-8 relative of T); it is formed in fp64.  Worst-case relative error of
 // S_R: about 2e-6 (fp32 partial sums of <= 40 terms, v_exp_f32, the rounded
 // exponent argument); alpha is therefore within 5e-6 of its exact value,
@@ -52,9 +53,9 @@ __device__ __forceinline__ RowStat merge_row(const SegStat* seg, int32_t nseg, b
     return r;
 }
 
-// ln of the normaliser sum_v exp((z_v - m)/T) of a merged sampling row.
-__device__ __forceinline__ double log_norm(const RowStat& r, float c) {
-    return log(r.S) + (static_cast<double>(r.R) - static_cast<double>(r.m) * c) * 0.6931471805599453;
+// log2 of the normaliser sum_v 2^((z_v - m) c) of a merged sampling row.
+__device__ __forceinline__ double log2_norm(const RowStat& r, float c) {
+    return log2(r.S) + (static_cast<double>(r.R) - static_cast<double>(r.m) * c);
 }
 
 __global__ __launch_bounds__(kThreads) void accept_kernel(Problem p, Plan plan) {
@@ -109,8 +110,8 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(Problem p, Plan plan) 
         if (greedy) {
             reject = (x != rt.arg);
         } else {
-            const double zt = load_logit(p.target, p.dtype, trow * p.V + x);
-            const double zd = load_logit(p.draft, p.dtype, drow * p.V + x);
+            const double zt = plan.xlogit[trow];             // captured by the row pass
+            const double zd = plan.xlogit[ntarget + drow];
             px = exp2(zt * c - rt.R) / rt.S;
             qx = exp2(zd * c - rd.R) / rd.S;
             const double alpha = fmin(1.0, px / qx);
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(Problem p, Plan plan) 
         t.m_d = n < k ? rd.m : 0.f;
         t.T = Tf;
         t.u = p.uniforms[o + b + k];
-        t.theta = (!greedy && n < k) ? log_norm(rt, c) - log_norm(rd, c) : 0.0;
+        t.theta = (!greedy && n < k) ? log2_norm(rt, c) - log2_norm(rd, c) : 0.0;
         plan.task[b] = t;
     }
     if (p.out_p && lane < k) {
@@ -146,10 +147,10 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(Problem p, Plan plan) 
     }
     if (p.out_row_max && lane <= k) {
         p.out_row_max[trow] = rt.m;
-        p.out_row_sum[trow] = greedy ? NAN : static_cast<float>(exp(log_norm(rt, c)));
+        p.out_row_sum[trow] = greedy ? NAN : static_cast<float>(exp2(log2_norm(rt, c)));
         if (lane < k) {
             p.out_row_max[ntarget + drow] = greedy ? NAN : rd.m;
-            p.out_row_sum[ntarget + drow] = greedy ? NAN : static_cast<float>(exp(log_norm(rd, c)));
+            p.out_row_sum[ntarget + drow] = greedy ? NAN : static_cast<float>(exp2(log2_norm(rd, c)));
         }
     }
 }

@@ -10,28 +10,29 @@
 //
 // Tail tokens of a 10^5-entry distribution carry masses near 1e-10 and sit
 // closer together than fp32 rounding, so the CDF is built in fp64 from
-// w = exp((z - m) / T) of the exact logits and row maxima.
+// w = 2^((z - m) log2(e) / T) of the exact logits and row maxima.
 //
 // draw_sums (grid sequence x chunk) reads the draw rows once:
 //   * bonus draw: per chunk, W_c = sum of w_t;
 //   * residual draw: per chunk, S_p,c = sum w_t and S_q,c = sum w_d (the fp64
 //     normalisers), and A_c, B_c = sums of w_t, w_d over the tokens with
-//     p_v > q_v.  p_v > q_v iff d_v = (z_t - m_t)/T - (z_d - m_d)/T exceeds
-//     theta = ln(S_p / S_q); the accept scan supplies theta from the row
-//     pass's normalisers (within about 5e-6), so tokens with
+//     p_v > q_v.  p_v > q_v iff d_v = log2(w_t / w_d) exceeds
+//     theta = log2(S_p / S_q); the accept scan supplies theta from the row
+//     pass's normalisers (within about 1e-5 in log2 units), so tokens with
 //     |d_v - theta| > kBand are classified exactly, and the few inside the
-//     band are listed (per wave, up to kWaveCap each) and get their exact mass
-//     once S_p and S_q are known.  The residual mass of chunk c is
-//     R_c = A_c / S_p - B_c / S_q + sum over its band tokens of
+//     band are listed per wave (up to kWaveCap each) with their (w_t, w_d),
+//     to get their exact mass once S_p and S_q are known.  The residual mass
+//     of chunk c is R_c = A_c / S_p - B_c / S_q + sum over its band tokens of
 //     max(0, w_t/S_p - w_d/S_q); a chunk whose lists overflowed is rescanned.
 // draw_pick (one workgroup per sequence) forms Z = sum_c R_c, finds the chunk
 // whose cumulative mass crosses u Z, and scans that one chunk with a
 // workgroup-wide fp64 prefix sum over masses held in registers.  The kernel
 // boundary publishes the chunk sums; no device-wide fences are needed.
 //
-// exp in fp64 follows Tang's table-driven method (ACM TOMS 15(2), 1989):
-// y = (64 k + j) ln2/64 + r with |r| <= ln2/128, exp(y) = 2^k 2^(j/64) e^r,
-// e^r - 1 by its degree-5 Taylor polynomial (truncation < 4e-17 relative).
+// 2^y in fp64 follows Tang's table-driven method (ACM TOMS 15(2), 1989) in
+// base 2 with a 256-entry table: y = k + j/256 + r with |r| <= 1/512,
+// 2^y = 2^k 2^(j/256) e^(r ln2), e^(r ln2) - 1 by its degree-4 Taylor
+// polynomial (truncation < 4e-17 relative).  The kernels carry Y = 256 y.
 #include "sv_internal.h"
 
 namespace sv {
@@ -39,46 +40,97 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr double kDegenerateZ = 1e-9;   // residual mass treated as empty
-constexpr double kBand = 2e-5;          // classification band around theta
-constexpr int kMaxPickChunks = 1024;    // chunk masses held in LDS by the pick
+constexpr double kLog2e = 0x1.71547652b82fep+0;
+constexpr double kDegenerateZ = 1e-9;            // residual mass treated as empty
+constexpr double kBand = 3e-5;                   // classification band (log2 units)
+constexpr int kMaxPickChunks = 1024;             // chunk masses held in LDS by the pick
+constexpr int kRun = 16;                         // tokens per lane in the pick's scan
+constexpr int64_t kPiece = kThreads * kRun;      // tokens per scan step of the pick
 
-// 2^(j/64), j = 0..63, correctly rounded.
-__constant__ double kExp2Frac[64] = {
-    0x1.0000000000000p+0, 0x1.02c9a3e778061p+0, 0x1.059b0d3158574p+0, 0x1.0874518759bc8p+0,
-    0x1.0b5586cf9890fp+0, 0x1.0e3ec32d3d1a2p+0, 0x1.11301d0125b51p+0, 0x1.1429aaea92de0p+0,
-    0x1.172b83c7d517bp+0, 0x1.1a35beb6fcb75p+0, 0x1.1d4873168b9aap+0, 0x1.2063b88628cd6p+0,
-    0x1.2387a6e756238p+0, 0x1.26b4565e27cddp+0, 0x1.29e9df51fdee1p+0, 0x1.2d285a6e4030bp+0,
-    0x1.306fe0a31b715p+0, 0x1.33c08b26416ffp+0, 0x1.371a7373aa9cbp+0, 0x1.3a7db34e59ff7p+0,
-    0x1.3dea64c123422p+0, 0x1.4160a21f72e2ap+0, 0x1.44e086061892dp+0, 0x1.486a2b5c13cd0p+0,
-    0x1.4bfdad5362a27p+0, 0x1.4f9b2769d2ca7p+0, 0x1.5342b569d4f82p+0, 0x1.56f4736b527dap+0,
-    0x1.5ab07dd485429p+0, 0x1.5e76f15ad2148p+0, 0x1.6247eb03a5585p+0, 0x1.6623882552225p+0,
-    0x1.6a09e667f3bcdp+0, 0x1.6dfb23c651a2fp+0, 0x1.71f75e8ec5f74p+0, 0x1.75feb564267c9p+0,
-    0x1.7a11473eb0187p+0, 0x1.7e2f336cf4e62p+0, 0x1.82589994cce13p+0, 0x1.868d99b4492edp+0,
-    0x1.8ace5422aa0dbp+0, 0x1.8f1ae99157736p+0, 0x1.93737b0cdc5e5p+0, 0x1.97d829fde4e50p+0,
-    0x1.9c49182a3f090p+0, 0x1.a0c667b5de565p+0, 0x1.a5503b23e255dp+0, 0x1.a9e6b5579fdbfp+0,
-    0x1.ae89f995ad3adp+0, 0x1.b33a2b84f15fbp+0, 0x1.b7f76f2fb5e47p+0, 0x1.bcc1e904bc1d2p+0,
-    0x1.c199bdd85529cp+0, 0x1.c67f12e57d14bp+0, 0x1.cb720dcef9069p+0, 0x1.d072d4a07897cp+0,
-    0x1.d5818dcfba487p+0, 0x1.da9e603db3285p+0, 0x1.dfc97337b9b5fp+0, 0x1.e502ee78b3ff6p+0,
-    0x1.ea4afa2a490dap+0, 0x1.efa1bee615a27p+0, 0x1.f50765b6e4540p+0, 0x1.fa7c1819e90d8p+0,
+// 2^(j/256), j = 0..255, correctly rounded.
+__constant__ double kExp2Frac[256] = {
+    0x1.0000000000000p+0, 0x1.00b1afa5abcbfp+0, 0x1.0163da9fb3335p+0, 0x1.02168143b0281p+0,
+    0x1.02c9a3e778061p+0, 0x1.037d42e11bbccp+0, 0x1.04315e86e7f85p+0, 0x1.04e5f72f654b1p+0,
+    0x1.059b0d3158574p+0, 0x1.0650a0e3c1f89p+0, 0x1.0706b29ddf6dep+0, 0x1.07bd42b72a836p+0,
+    0x1.0874518759bc8p+0, 0x1.092bdf66607e0p+0, 0x1.09e3ecac6f383p+0, 0x1.0a9c79b1f3919p+0,
+    0x1.0b5586cf9890fp+0, 0x1.0c0f145e46c85p+0, 0x1.0cc922b7247f7p+0, 0x1.0d83b23395decp+0,
+    0x1.0e3ec32d3d1a2p+0, 0x1.0efa55fdfa9c5p+0, 0x1.0fb66affed31bp+0, 0x1.1073028d7233ep+0,
+    0x1.11301d0125b51p+0, 0x1.11edbab5e2ab6p+0, 0x1.12abdc06c31ccp+0, 0x1.136a814f204abp+0,
+    0x1.1429aaea92de0p+0, 0x1.14e95934f312ep+0, 0x1.15a98c8a58e51p+0, 0x1.166a45471c3c2p+0,
+    0x1.172b83c7d517bp+0, 0x1.17ed48695bbc0p+0, 0x1.18af9388c8deap+0, 0x1.1972658375d2fp+0,
+    0x1.1a35beb6fcb75p+0, 0x1.1af99f8138a1cp+0, 0x1.1bbe084045cd4p+0, 0x1.1c82f95281c6bp+0,
+    0x1.1d4873168b9aap+0, 0x1.1e0e75eb44027p+0, 0x1.1ed5022fcd91dp+0, 0x1.1f9c18438ce4dp+0,
+    0x1.2063b88628cd6p+0, 0x1.212be3578a819p+0, 0x1.21f49917ddc96p+0, 0x1.22bdda27912d1p+0,
+    0x1.2387a6e756238p+0, 0x1.2451ffb82140ap+0, 0x1.251ce4fb2a63fp+0, 0x1.25e85711ece75p+0,
+    0x1.26b4565e27cddp+0, 0x1.2780e341ddf29p+0, 0x1.284dfe1f56381p+0, 0x1.291ba7591bb70p+0,
+    0x1.29e9df51fdee1p+0, 0x1.2ab8a66d10f13p+0, 0x1.2b87fd0dad990p+0, 0x1.2c57e39771b2fp+0,
+    0x1.2d285a6e4030bp+0, 0x1.2df961f641589p+0, 0x1.2ecafa93e2f56p+0, 0x1.2f9d24abd886bp+0,
+    0x1.306fe0a31b715p+0, 0x1.31432edeeb2fdp+0, 0x1.32170fc4cd831p+0, 0x1.32eb83ba8ea32p+0,
+    0x1.33c08b26416ffp+0, 0x1.3496266e3fa2dp+0, 0x1.356c55f929ff1p+0, 0x1.36431a2de883bp+0,
+    0x1.371a7373aa9cbp+0, 0x1.37f26231e754ap+0, 0x1.38cae6d05d866p+0, 0x1.39a401b7140efp+0,
+    0x1.3a7db34e59ff7p+0, 0x1.3b57fbfec6cf4p+0, 0x1.3c32dc313a8e5p+0, 0x1.3d0e544ede173p+0,
+    0x1.3dea64c123422p+0, 0x1.3ec70df1c5175p+0, 0x1.3fa4504ac801cp+0, 0x1.40822c367a024p+0,
+    0x1.4160a21f72e2ap+0, 0x1.423fb2709468ap+0, 0x1.431f5d950a897p+0, 0x1.43ffa3f84b9d4p+0,
+    0x1.44e086061892dp+0, 0x1.45c2042a7d232p+0, 0x1.46a41ed1d0057p+0, 0x1.4786d668b3237p+0,
+    0x1.486a2b5c13cd0p+0, 0x1.494e1e192aed2p+0, 0x1.4a32af0d7d3dep+0, 0x1.4b17dea6db7d7p+0,
+    0x1.4bfdad5362a27p+0, 0x1.4ce41b817c114p+0, 0x1.4dcb299fddd0dp+0, 0x1.4eb2d81d8abffp+0,
+    0x1.4f9b2769d2ca7p+0, 0x1.508417f4531eep+0, 0x1.516daa2cf6642p+0, 0x1.5257de83f4eefp+0,
+    0x1.5342b569d4f82p+0, 0x1.542e2f4f6ad27p+0, 0x1.551a4ca5d920fp+0, 0x1.56070dde910d2p+0,
+    0x1.56f4736b527dap+0, 0x1.57e27dbe2c4cfp+0, 0x1.58d12d497c7fdp+0, 0x1.59c0827ff07ccp+0,
+    0x1.5ab07dd485429p+0, 0x1.5ba11fba87a03p+0, 0x1.5c9268a5946b7p+0, 0x1.5d84590998b93p+0,
+    0x1.5e76f15ad2148p+0, 0x1.5f6a320dceb71p+0, 0x1.605e1b976dc09p+0, 0x1.6152ae6cdf6f4p+0,
+    0x1.6247eb03a5585p+0, 0x1.633dd1d1929fdp+0, 0x1.6434634ccc320p+0, 0x1.652b9febc8fb7p+0,
+    0x1.6623882552225p+0, 0x1.671c1c70833f6p+0, 0x1.68155d44ca973p+0, 0x1.690f4b19e9538p+0,
+    0x1.6a09e667f3bcdp+0, 0x1.6b052fa75173ep+0, 0x1.6c012750bdabfp+0, 0x1.6cfdcddd47645p+0,
+    0x1.6dfb23c651a2fp+0, 0x1.6ef9298593ae5p+0, 0x1.6ff7df9519484p+0, 0x1.70f7466f42e87p+0,
+    0x1.71f75e8ec5f74p+0, 0x1.72f8286ead08ap+0, 0x1.73f9a48a58174p+0, 0x1.74fbd35d7cbfdp+0,
+    0x1.75feb564267c9p+0, 0x1.77024b1ab6e09p+0, 0x1.780694fde5d3fp+0, 0x1.790b938ac1cf6p+0,
+    0x1.7a11473eb0187p+0, 0x1.7b17b0976cfdbp+0, 0x1.7c1ed0130c132p+0, 0x1.7d26a62ff86f0p+0,
+    0x1.7e2f336cf4e62p+0, 0x1.7f3878491c491p+0, 0x1.80427543e1a12p+0, 0x1.814d2add106d9p+0,
+    0x1.82589994cce13p+0, 0x1.8364c1eb941f7p+0, 0x1.8471a4623c7adp+0, 0x1.857f4179f5b21p+0,
+    0x1.868d99b4492edp+0, 0x1.879cad931a436p+0, 0x1.88ac7d98a6699p+0, 0x1.89bd0a478580fp+0,
+    0x1.8ace5422aa0dbp+0, 0x1.8be05bad61778p+0, 0x1.8cf3216b5448cp+0, 0x1.8e06a5e0866d9p+0,
+    0x1.8f1ae99157736p+0, 0x1.902fed0282c8ap+0, 0x1.9145b0b91ffc6p+0, 0x1.925c353aa2fe2p+0,
+    0x1.93737b0cdc5e5p+0, 0x1.948b82b5f98e5p+0, 0x1.95a44cbc8520fp+0, 0x1.96bdd9a7670b3p+0,
+    0x1.97d829fde4e50p+0, 0x1.98f33e47a22a2p+0, 0x1.9a0f170ca07bap+0, 0x1.9b2bb4d53fe0dp+0,
+    0x1.9c49182a3f090p+0, 0x1.9d674194bb8d5p+0, 0x1.9e86319e32323p+0, 0x1.9fa5e8d07f29ep+0,
+    0x1.a0c667b5de565p+0, 0x1.a1e7aed8eb8bbp+0, 0x1.a309bec4a2d33p+0, 0x1.a42c980460ad8p+0,
+    0x1.a5503b23e255dp+0, 0x1.a674a8af46052p+0, 0x1.a799e1330b358p+0, 0x1.a8bfe53c12e59p+0,
+    0x1.a9e6b5579fdbfp+0, 0x1.ab0e521356ebap+0, 0x1.ac36bbfd3f37ap+0, 0x1.ad5ff3a3c2774p+0,
+    0x1.ae89f995ad3adp+0, 0x1.afb4ce622f2ffp+0, 0x1.b0e07298db666p+0, 0x1.b20ce6c9a8952p+0,
+    0x1.b33a2b84f15fbp+0, 0x1.b468415b749b1p+0, 0x1.b59728de5593ap+0, 0x1.b6c6e29f1c52ap+0,
+    0x1.b7f76f2fb5e47p+0, 0x1.b928cf22749e4p+0, 0x1.ba5b030a1064ap+0, 0x1.bb8e0b79a6f1fp+0,
+    0x1.bcc1e904bc1d2p+0, 0x1.bdf69c3f3a207p+0, 0x1.bf2c25bd71e09p+0, 0x1.c06286141b33dp+0,
+    0x1.c199bdd85529cp+0, 0x1.c2d1cd9fa652cp+0, 0x1.c40ab5fffd07ap+0, 0x1.c544778fafb22p+0,
+    0x1.c67f12e57d14bp+0, 0x1.c7ba88988c933p+0, 0x1.c8f6d9406e7b5p+0, 0x1.ca3405751c4dbp+0,
+    0x1.cb720dcef9069p+0, 0x1.ccb0f2e6d1675p+0, 0x1.cdf0b555dc3fap+0, 0x1.cf3155b5bab74p+0,
+    0x1.d072d4a07897cp+0, 0x1.d1b532b08c968p+0, 0x1.d2f87080d89f2p+0, 0x1.d43c8eacaa1d6p+0,
+    0x1.d5818dcfba487p+0, 0x1.d6c76e862e6d3p+0, 0x1.d80e316c98398p+0, 0x1.d955d71ff6075p+0,
+    0x1.da9e603db3285p+0, 0x1.dbe7cd63a8315p+0, 0x1.dd321f301b460p+0, 0x1.de7d5641c0658p+0,
+    0x1.dfc97337b9b5fp+0, 0x1.e11676b197d17p+0, 0x1.e264614f5a129p+0, 0x1.e3b333b16ee12p+0,
+    0x1.e502ee78b3ff6p+0, 0x1.e653924676d76p+0, 0x1.e7a51fbc74c83p+0, 0x1.e8f7977cdb740p+0,
+    0x1.ea4afa2a490dap+0, 0x1.eb9f4867cca6ep+0, 0x1.ecf482d8e67f1p+0, 0x1.ee4aaa2188510p+0,
+    0x1.efa1bee615a27p+0, 0x1.f0f9c1cb6412ap+0, 0x1.f252b376bba97p+0, 0x1.f3ac948dd7274p+0,
+    0x1.f50765b6e4540p+0, 0x1.f6632798844f8p+0, 0x1.f7bfdad9cbe14p+0, 0x1.f91d802243c89p+0,
+    0x1.fa7c1819e90d8p+0, 0x1.fbdba3692d514p+0, 0x1.fd3c22b8f71f1p+0, 0x1.fe9d96b2a23d9p+0,
 };
 
-// exp(y) in fp64 for y <= ~700 (arguments here are <= 0); tbl = kExp2Frac in LDS.
-// Rounding y * 64/ln2 to an integer n uses the 1.5 * 2^52 shifter: after the
-// add, the low 32 bits of the double hold n in two's complement.
-__device__ __forceinline__ double exp_f64(double y, const double* tbl) {
+// 2^(Y/256) in fp64 for Y <= ~256000 (arguments here are <= 0); tbl = kExp2Frac
+// in LDS.  Y = n + r with n = round(Y) (the 1.5 * 2^52 shifter: after the add
+// the low 32 bits of the double hold n in two's complement) and |r| <= 1/2, so
+// 2^(Y/256) = 2^(n>>8) 2^((n&255)/256) e^x with x = r ln2/256, |x| <= ln2/512;
+// e^x - 1 by its degree-4 Taylor polynomial (truncation < 4e-17 relative).
+__device__ __forceinline__ double exp2_256(double Y, const double* tbl) {
     constexpr double kShift = 0x1.8p52;
-    y = fmax(y, -1000.0);                          // exp(-1000) underflows to 0 anyway
-    const double kd = fma(y, 0x1.71547652b82fep+6, kShift);    // y * 64 / ln2 + shifter
+    Y = fmax(Y, -281600.0);                        // 2^-1100 underflows to 0 anyway
+    const double kd = Y + kShift;
     const int n = static_cast<int>(static_cast<uint32_t>(__double_as_longlong(kd)));
-    const double nd = kd - kShift;
-    const double r = fma(-nd, 0x1.a39ef35793c76p-39, fma(-nd, 0x1.62e42fee00000p-7, y));
-    double q = fma(r, 1.0 / 120.0, 1.0 / 24.0);
-    q = fma(q, r, 1.0 / 6.0);
-    q = fma(q, r, 0.5);
-    q = fma(q, r, 1.0);
-    const double t = tbl[n & 63];
-    return ldexp(fma(t, q * r, t), n >> 6);
+    const double r = Y - (kd - kShift);            // exact
+    double q = fma(r, 0x1.3b2ab6fba4e77p-39, 0x1.c6b08d704a0c0p-29);
+    q = fma(q, r, 0x1.ebfbdff82c58fp-19);
+    q = fma(q, r, 0x1.62e42fefa39efp-9);
+    const double t = tbl[n & 255];
+    return ldexp(fma(t, q * r, t), n >> 8);
 }
 
 template <int DT> struct Vec;
@@ -102,33 +154,41 @@ template <> struct Vec<SV_F32> {
     }
 };
 
-// The one or two rows a draw reads.
+// The one or two rows a draw reads, and Y = 256 (z - m) log2(e) / T as one fma.
 template <int DT>
 struct Rows {
     using E = typename Vec<DT>::E;
     const E* t;          // target row at position n
     const E* d;          // draft row at position n (residual only)
-    double mt, md, invT;
+    double c;            // 256 log2(e) / T
+    double ot, od;       // -m_t * c, -m_d * c
     const double* tbl;
 
-    __device__ __forceinline__ double zt(int64_t v) const { return load_logit(t, DT, v); }
-    __device__ __forceinline__ double zd(int64_t v) const { return load_logit(d, DT, v); }
-    __device__ __forceinline__ double wt(double z) const { return exp_f64((z - mt) * invT, tbl); }
-    __device__ __forceinline__ double wd(double z) const { return exp_f64((z - md) * invT, tbl); }
-    // residual mass max(0, w_t/S_p - w_d/S_q) of token v (iSp = 1/S_p, iSq = 1/S_q)
-    __device__ __forceinline__ double residual(int64_t v, double iSp, double iSq) const {
-        return residual_z(zt(v), zd(v), iSp, iSq);
-    }
-    __device__ __forceinline__ double residual_z(double z_t, double z_d, double iSp, double iSq) const {
-        return fmax(0.0, wt(z_t) * iSp - wd(z_d) * iSq);
-    }
+    __device__ __forceinline__ double Yt(float z) const { return fma(static_cast<double>(z), c, ot); }
+    __device__ __forceinline__ double Yd(float z) const { return fma(static_cast<double>(z), c, od); }
+    __device__ __forceinline__ double wt(float z) const { return exp2_256(Yt(z), tbl); }
+    __device__ __forceinline__ double wd(float z) const { return exp2_256(Yd(z), tbl); }
+    __device__ __forceinline__ float zt(int64_t v) const { return load_logit(t, DT, v); }
+    __device__ __forceinline__ float zd(int64_t v) const { return load_logit(d, DT, v); }
 };
+
+template <int DT>
+__device__ __forceinline__ Rows<DT> rows_of(const Problem& p, const DrawTask& task, const double* tbl) {
+    using E = typename Vec<DT>::E;
+    const double c = 256.0 * kLog2e / static_cast<double>(task.T);
+    return Rows<DT>{static_cast<const E*>(p.target) + task.trow * p.V,
+                    static_cast<const E*>(p.draft) + task.drow * p.V,
+                    c, -static_cast<double>(task.m_t) * c, -static_cast<double>(task.m_d) * c, tbl};
+}
+
+__device__ __forceinline__ void load_table(double* tbl) {
+    for (int i = threadIdx.x; i < 256; i += kThreads) tbl[i] = kExp2Frac[i];
+}
 
 // Calls f(v, z_t, z_d) for this thread's tokens of [v0, v1): 16-byte vector
 // loads (lane-strided vectors) when both rows allow them, scalar otherwise.
 template <int DT, bool kResid, class F>
 __device__ __forceinline__ void for_chunk(const Rows<DT>& rows, int64_t v0, int64_t v1, F&& f) {
-    using E = typename Vec<DT>::E;
     constexpr int N = Vec<DT>::N;
     const bool vec = (reinterpret_cast<uintptr_t>(rows.t + v0) & 15u) == 0 &&
                      (!kResid || (reinterpret_cast<uintptr_t>(rows.d + v0) & 15u) == 0);
@@ -143,17 +203,18 @@ __device__ __forceinline__ void for_chunk(const Rows<DT>& rows, int64_t v0, int6
             float xt[N], xd[N];
             Vec<DT>::unpack(a0, xt);
             if (kResid) Vec<DT>::unpack(b0, xd);
-#pragma unroll 2   // two tokens' fp64 work interleaved: occupancy 6 without spills
-            for (int e = 0; e < N; ++e) f(v0 + j * N + e, xt[e], kResid ? xd[e] : 0.f);
+#pragma unroll
+            for (int e = 0; e < N; ++e) {
+                f(v0 + j * N + e, xt[e], kResid ? xd[e] : 0.f);
+                // interleave at most two tokens' fp64 work: keeps occupancy at 8
+                if (e % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+            }
         }
         vs = v0 + nvec * N;
     }
     for (int64_t v = vs + threadIdx.x; v < v1; v += kThreads)
-        f(v, static_cast<float>(rows.zt(v)), kResid ? static_cast<float>(rows.zd(v)) : 0.f);
+        f(v, rows.zt(v), kResid ? rows.zd(v) : 0.f);
 }
-
-constexpr int kRun = 16;                      // tokens per lane in the pick's scan
-constexpr int64_t kPiece = kThreads * kRun;   // tokens per scan step of the pick
 
 // Sums of four doubles over the workgroup (valid in every thread).
 __device__ __forceinline__ void block_sum4(double& a, double& b, double& c, double& d,
@@ -207,14 +268,6 @@ __device__ __forceinline__ int32_t block_min_max(int32_t x, bool want_min, int32
     return r;
 }
 
-template <int DT>
-__device__ __forceinline__ Rows<DT> rows_of(const Problem& p, const DrawTask& task, const double* tbl) {
-    using E = typename Vec<DT>::E;
-    return Rows<DT>{static_cast<const E*>(p.target) + task.trow * p.V,
-                    static_cast<const E*>(p.draft) + task.drow * p.V,
-                    task.m_t, task.m_d, 1.0 / static_cast<double>(task.T), tbl};
-}
-
 // Chunk pass: grid (sequence x chunk).
 template <int DT>
 __global__ __launch_bounds__(kThreads) void draw_sums_kernel(Problem p, Plan plan) {
@@ -226,11 +279,11 @@ __global__ __launch_bounds__(kThreads) void draw_sums_kernel(Problem p, Plan pla
     const bool resid_task = (task.kind == kResidual);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
-    __shared__ double tbl[64];
+    __shared__ double tbl[256];
     __shared__ double lds4[kWaves][4];
-    __shared__ int32_t wlist[kWaves][kWaveCap];
+    __shared__ double wlist[kWaves][kWaveCap][2];
     __shared__ int32_t wcount[kWaves];
-    if (threadIdx.x < 64) tbl[threadIdx.x] = kExp2Frac[threadIdx.x];
+    load_table(tbl);
     __syncthreads();
     const Rows<DT> rows = rows_of<DT>(p, task, tbl);
 
@@ -239,22 +292,22 @@ __global__ __launch_bounds__(kThreads) void draw_sums_kernel(Problem p, Plan pla
     double sp = 0.0, sq = 0.0, a = 0.0, bq = 0.0;
     int32_t nband = 0;                         // uniform over the lanes still active
     if (resid_task) {
-        const double th_hi = task.theta + kBand, th_lo = task.theta - kBand;
-        for_chunk<DT, true>(rows, v0, v1, [&](int64_t v, float zt, float zd) {
-            const double yt = (static_cast<double>(zt) - rows.mt) * rows.invT;
-            const double yd = (static_cast<double>(zd) - rows.md) * rows.invT;
-            const double wt = exp_f64(yt, tbl), wd = exp_f64(yd, tbl);
+        const double th_hi = 256.0 * (task.theta + kBand), th_lo = 256.0 * (task.theta - kBand);
+        for_chunk<DT, true>(rows, v0, v1, [&](int64_t, float zt, float zd) {
+            const double yt = rows.Yt(zt), yd = rows.Yd(zd);
+            const double wt = exp2_256(yt, tbl), wd = exp2_256(yd, tbl);
             sp += wt;
             sq += wd;
             const double dv = yt - yd;
             const bool hi = dv > th_hi;
-            a += hi ? wt : 0.0;
-            bq += hi ? wd : 0.0;
+            const double h = hi ? 1.0 : 0.0;
+            a = fma(h, wt, a);
+            bq = fma(h, wd, bq);
             const bool in_band = !hi && dv >= th_lo;
             const uint64_t m = __ballot(in_band);
             if (m) {
                 const int pos = nband + __popcll(m & ((1ull << lane) - 1ull));
-                if (in_band && pos < kWaveCap) wlist[wave][pos] = static_cast<int32_t>(v);
+                if (in_band && pos < kWaveCap) { wlist[wave][pos][0] = wt; wlist[wave][pos][1] = wd; }
                 nband += __popcll(m);
             }
         });
@@ -269,11 +322,14 @@ __global__ __launch_bounds__(kThreads) void draw_sums_kernel(Problem p, Plan pla
         plan.csum[w] = cs;
     }
     if (resid_task) {
-        int32_t* band = plan.band + w * kBandSlots;
-        if (threadIdx.x < kWaves) band[threadIdx.x] = wcount[threadIdx.x];
+        if (threadIdx.x < kWaves) plan.band_n[w * kWaves + threadIdx.x] = wcount[threadIdx.x];
         if (threadIdx.x < kWaves * kWaveCap) {
             const int wv = threadIdx.x / kWaveCap, e = threadIdx.x % kWaveCap;
-            if (e < wcount[wv]) band[kWaves + threadIdx.x] = wlist[wv][e];
+            if (e < wcount[wv]) {
+                double* dst = plan.band_w + (w * kWaves * kWaveCap + threadIdx.x) * 2;
+                dst[0] = wlist[wv][e][0];
+                dst[1] = wlist[wv][e][1];
+            }
         }
     }
 }
@@ -282,24 +338,25 @@ __global__ __launch_bounds__(kThreads) void draw_sums_kernel(Problem p, Plan pla
 template <int DT>
 __global__ __launch_bounds__(kThreads) void draw_pick_kernel(Problem p, Plan plan) {
     constexpr int N = Vec<DT>::N;
+    constexpr int kSlots = kWaves * kWaveCap;    // band entries per chunk (32)
     const int32_t b = blockIdx.x;
     const DrawTask task = plan.task[b];
     if (task.kind == kNone) return;
     const bool resid_task = (task.kind == kResidual);
+    const int lane = threadIdx.x & 63;
 
-    __shared__ double tbl[64];
+    __shared__ double tbl[256];
     __shared__ double lds4[kWaves][4];
     __shared__ double lds[kWaves];
     __shared__ int32_t ldsi[kWaves];
     __shared__ double mass[kMaxPickChunks];
     __shared__ double sh_base, sh_target;
     __shared__ int32_t sh_chunk, sh_resid, sh_rescan;
-    if (threadIdx.x < 64) tbl[threadIdx.x] = kExp2Frac[threadIdx.x];
+    load_table(tbl);
     if (threadIdx.x == 0) sh_rescan = 0;
-    __syncthreads();
     const Rows<DT> rows = rows_of<DT>(p, task, tbl);
-    const ChunkSums* cs = plan.csum + static_cast<int64_t>(b) * plan.nchunk;
-    const int32_t* bands = plan.band + static_cast<int64_t>(b) * plan.nchunk * kBandSlots;
+    const int64_t cb = static_cast<int64_t>(b) * plan.nchunk;
+    const ChunkSums* cs = plan.csum + cb;
     const int32_t nchunk = plan.nchunk;
 
     double Sp = 0.0, Sq = 0.0, unused0 = 0.0, unused1 = 0.0;
@@ -307,23 +364,31 @@ __global__ __launch_bounds__(kThreads) void draw_pick_kernel(Problem p, Plan pla
         Sp += cs[j].sp;
         Sq += cs[j].sq;
     }
-    block_sum4(Sp, Sq, unused0, unused1, lds4);
+    block_sum4(Sp, Sq, unused0, unused1, lds4);     // (its barriers also publish tbl)
     const double iSp = 1.0 / Sp, iSq = resid_task ? 1.0 / Sq : 0.0;
 
     if (resid_task) {
-        // per-chunk residual mass: robust part plus band tokens (list order)
-        for (int32_t j = threadIdx.x; j < nchunk; j += kThreads) {
-            const int32_t* bj = bands + static_cast<int64_t>(j) * kBandSlots;
-            double m = cs[j].a * iSp - cs[j].b * iSq;
+        // Band terms: 32 lanes per chunk, one listed token each; a fixed
+        // shuffle tree sums them per chunk (deterministic order).
+        for (int64_t t0 = 0; t0 < static_cast<int64_t>(nchunk) * kSlots; t0 += kThreads) {
+            const int64_t t = t0 + threadIdx.x;
+            const int32_t j = static_cast<int32_t>(t / kSlots), s = static_cast<int32_t>(t % kSlots);
+            double term = 0.0;
             bool over = false;
-            for (int wv = 0; wv < kWaves; ++wv) {
-                const int32_t cnt = bj[wv];
-                over |= cnt > kWaveCap;
-                for (int32_t e = 0; e < cnt && e < kWaveCap; ++e)
-                    m += rows.residual(bj[kWaves + wv * kWaveCap + e], iSp, iSq);
+            if (j < nchunk) {
+                const int32_t cnt = plan.band_n[(cb + j) * kWaves + s / kWaveCap];
+                over = cnt > kWaveCap;
+                if (s % kWaveCap < cnt) {
+                    const double* pw = plan.band_w + ((cb + j) * kSlots + s) * 2;
+                    term = fmax(0.0, pw[0] * iSp - pw[1] * iSq);
+                }
             }
-            mass[j] = over ? NAN : m;
+            for (int off = kSlots / 2; off > 0; off >>= 1) term += __shfl_xor(term, off, 64);
+            if (j < nchunk && s == 0)
+                mass[j] = cs[j].a * iSp - cs[j].b * iSq + term;
             if (over) atomicOr(&sh_rescan, 1);
+            __syncthreads();
+            if (over && s % kWaveCap == 0) mass[j] = NAN;       // this chunk needs a rescan
         }
         __syncthreads();
         if (sh_rescan) {
@@ -333,7 +398,8 @@ __global__ __launch_bounds__(kThreads) void draw_pick_kernel(Problem p, Plan pla
                 const int64_t u0 = static_cast<int64_t>(j) * plan.chunk_len;
                 const int64_t u1 = min(p.V, u0 + plan.chunk_len);
                 double m = 0.0;
-                for (int64_t v = u0 + threadIdx.x; v < u1; v += kThreads) m += rows.residual(v, iSp, iSq);
+                for (int64_t v = u0 + threadIdx.x; v < u1; v += kThreads)
+                    m += fmax(0.0, rows.wt(rows.zt(v)) * iSp - rows.wd(rows.zd(v)) * iSq);
                 m = block_sum(m, lds);
                 if (threadIdx.x == 0) mass[j] = m;
                 __syncthreads();
@@ -392,8 +458,8 @@ __global__ __launch_bounds__(kThreads) void draw_pick_kernel(Problem p, Plan pla
 #pragma unroll
             for (int i = 0; i < kRun; ++i) {
                 const bool in = r0 + i < q1;
-                zt[i] = in ? static_cast<float>(rows.zt(r0 + i)) : 0.f;
-                zd[i] = (in && resid) ? static_cast<float>(rows.zd(r0 + i)) : 0.f;
+                zt[i] = in ? rows.zt(r0 + i) : 0.f;
+                zd[i] = (in && resid) ? rows.zd(r0 + i) : 0.f;
             }
         }
         double m[kRun];
@@ -402,7 +468,8 @@ __global__ __launch_bounds__(kThreads) void draw_pick_kernel(Problem p, Plan pla
 #pragma unroll
         for (int i = 0; i < kRun; ++i) {
             const bool in = r0 + i < q1;
-            m[i] = !in ? 0.0 : (resid ? rows.residual_z(zt[i], zd[i], iSp, iSq) : rows.wt(zt[i]));
+            m[i] = !in ? 0.0
+                       : (resid ? fmax(0.0, rows.wt(zt[i]) * iSp - rows.wd(zd[i]) * iSq) : rows.wt(zt[i]));
             local += m[i];
             if (m[i] > 0.0) lp = static_cast<int32_t>(r0 + i);
         }
@@ -418,6 +485,7 @@ __global__ __launch_bounds__(kThreads) void draw_pick_kernel(Problem p, Plan pla
         last_pos = max(last_pos, block_min_max(lp, false, ldsi));
         base += total;
     }
+    (void)lane;
     // If rounding left no crossing inside the chunk: its last token with mass.
     if (threadIdx.x == 0) {
         if (pick == INT32_MAX) pick = last_pos >= 0 ? last_pos : static_cast<int32_t>(c0);

@@ -13,7 +13,7 @@
 // Work decomposition: the grid is (rows x segments); each 256-thread
 // workgroup streams one contiguous segment of one row.  Each lane owns every
 // 256th 16-byte vector of the segment (8 bf16 or 4 fp32 logits) and keeps a
-// rolling window of kWindow non-temporal loads in flight: the load that
+// rolling window of non-temporal loads in flight (8 for bf16, 4 for fp32): the load that
 // replaces a vector is issued before that vector is processed, so memory
 // requests stay outstanding while the lane computes.
 //
@@ -29,7 +29,6 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWindow = 8;   // 16-byte loads in flight per lane
 
 __device__ __forceinline__ u32x4 stream_load(const u32x4* p) {
     return __builtin_nontemporal_load(p);
@@ -41,7 +40,8 @@ __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2
 template <int DT> struct Elem;
 template <> struct Elem<SV_BF16> {
     using T = uint16_t;
-    static constexpr int N = 8;   // logits per 16-byte vector
+    static constexpr int N = 8;        // logits per 16-byte vector
+    static constexpr int kWindow = 8;  // 16-byte loads in flight per lane
     __device__ static __forceinline__ void unpack(const u32x4 v, float* x) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -53,6 +53,7 @@ template <> struct Elem<SV_BF16> {
 template <> struct Elem<SV_F32> {
     using T = float;
     static constexpr int N = 4;
+    static constexpr int kWindow = 4;  // (8 more than doubles the register footprint here)
     __device__ static __forceinline__ void unpack(const u32x4 v, float* x) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) x[j] = __uint_as_float(v[j]);
@@ -130,6 +131,7 @@ template <int DT, class Acc>
 __device__ __forceinline__ void stream_segment(const void* row_v, int64_t s0, int64_t s1, Acc& acc) {
     using E = typename Elem<DT>::T;
     constexpr int N = Elem<DT>::N;
+    constexpr int kWindow = Elem<DT>::kWindow;
     const E* row = static_cast<const E*>(row_v);
     const int tid = threadIdx.x;
     const uintptr_t addr = reinterpret_cast<uintptr_t>(row + s0);
@@ -141,36 +143,48 @@ __device__ __forceinline__ void stream_segment(const void* row_v, int64_t s0, in
 
     if (tid < head) acc.add1(load_logit(row_v, DT, s0 + tid), static_cast<int32_t>(s0 + tid));
 
-    // Lane tid owns vectors g = tid + j * 256 < nvec.  The loop runs a
-    // workgroup-uniform ub = ceil(nvec / 256) steps and every load condition
-    // is uniform, so loads stay in flight across steps; a lane whose last
-    // vector does not exist re-reads the segment's last vector (a cache hit)
-    // and skips processing it.
-    if (nvec > 0) {
-        const u32x4* vp = reinterpret_cast<const u32x4*>(row + a0);
-        const int32_t ub = (nvec + kThreads - 1) / kThreads;
-        const int32_t lane_cnt = (nvec - tid + kThreads - 1) / kThreads;
-        auto addr_of = [&](int32_t j) { return vp + min(tid + j * kThreads, nvec - 1); };
-        const int32_t base0 = static_cast<int32_t>(a0) + tid * N;
-        u32x4 buf[kWindow];
+    // Full tiles (one 16-byte vector per lane) stream through a rolling
+    // window of kWindow loads.  The tile count is workgroup-uniform, so
+    // every condition below is a scalar branch and each vector is processed
+    // before the load that refills its register is issued.
+    const u32x4* vp = reinterpret_cast<const u32x4*>(row + a0) + tid;
+    const int32_t ntiles = nvec / kThreads;
+    const int32_t base0 = static_cast<int32_t>(a0) + tid * N;
+    auto process = [&](const u32x4 v, int32_t t) {
+        float x[N];
+        Elem<DT>::unpack(v, x);
+        acc.template add<N>(x, base0 + t * kThreads * N);
+    };
+    // The partial tile: lanes tid < rem own one more vector, loaded up front.
+    const int32_t rem = nvec - ntiles * kThreads;
+    u32x4 extra{};
+    if (tid < rem) extra = stream_load(vp + ntiles * kThreads);
+    u32x4 buf[kWindow];
 #pragma unroll
-        for (int u = 0; u < kWindow; ++u)
-            if (u < ub) buf[u] = stream_load(addr_of(u));
-        for (int32_t i = 0; i < ub; i += kWindow) {
+    for (int u = 0; u < kWindow; ++u)
+        if (u < ntiles) buf[u] = stream_load(vp + u * kThreads);
+    int32_t i = 0;
+    // Steady state: every slot is refilled, so the only waits are for the
+    // oldest load in flight.
+    for (; i + 2 * kWindow <= ntiles; i += kWindow) {
 #pragma unroll
-            for (int u = 0; u < kWindow; ++u) {
-                if (i + u < ub) {
-                    const u32x4 v = buf[u];
-                    if (i + kWindow + u < ub) buf[u] = stream_load(addr_of(i + kWindow + u));
-                    if (i + u < lane_cnt) {
-                        float x[N];
-                        Elem<DT>::unpack(v, x);
-                        acc.template add<N>(x, base0 + (i + u) * kThreads * N);
-                    }
-                }
-            }
+        for (int u = 0; u < kWindow; ++u) {
+            process(buf[u], i + u);
+            buf[u] = stream_load(vp + (i + kWindow + u) * kThreads);
         }
     }
+    // Drain: slots i .. i+W-1 (those < ntiles) are loaded, the rest are not.
+#pragma unroll
+    for (int u = 0; u < kWindow; ++u) {
+        if (i + u < ntiles) {
+            process(buf[u], i + u);
+            if (i + kWindow + u < ntiles) buf[u] = stream_load(vp + (i + kWindow + u) * kThreads);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kWindow; ++u)
+        if (i + kWindow + u < ntiles) process(buf[u], i + kWindow + u);
+    if (tid < rem) process(extra, ntiles);
     if (tid < s1 - a1) acc.add1(load_logit(row_v, DT, a1 + tid), static_cast<int32_t>(a1 + tid));
 }
 
@@ -208,6 +222,21 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(Problem p, Plan pla
     const int64_t s0 = seg * plan.seg_len;
     const int64_t s1 = min(p.V, s0 + plan.seg_len);
 
+    // The workgroup whose segment holds this row's drafted token records that
+    // token's logit for the accept scan (loaded now, stored after the stream).
+    bool capture = false;
+    float zx = 0.f;
+    if (!greedy) {
+        const int64_t o = p.offsets ? static_cast<int64_t>(p.offsets[b]) : static_cast<int64_t>(b) * p.k_uniform;
+        const int64_t k = p.offsets ? static_cast<int64_t>(p.offsets[b + 1]) - o : p.k_uniform;
+        const int64_t i = is_target ? r - o - b : r - o;
+        if (i >= 0 && i < k && o >= 0 && o + i < p.total) {
+            const int32_t x = p.tokens[o + i];
+            capture = x >= s0 && x < s1;
+            if (capture && threadIdx.x == 0) zx = load_logit(row, DT, x);
+        }
+    }
+
     __shared__ float lds_m[kWaves], lds_R[kWaves];
     __shared__ double lds_s[kWaves];
     __shared__ int32_t lds_a[kWaves];
@@ -244,6 +273,7 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(Problem p, Plan pla
             SegStat out;
             out.m = m; out.R = R; out.arg = 0; out.pad = 0; out.s = s;
             plan.seg[w] = out;
+            if (capture) plan.xlogit[is_target ? r : ntarget + r] = zx;
         }
     }
 }

@@ -10,7 +10,11 @@
 namespace {
 using namespace sv;
 
-constexpr int64_t kDefaultSegElems = 16384;   // row-pass segment length before rounding
+constexpr int64_t kDefaultSegElems = 65536;   // row-pass segment length before rounding
+// Row-pass segments are whole load windows: 256 lanes x 16 B x the window
+// depth (8 loads for bf16, 4 for fp32), so only a row's last segment can end
+// inside a window.
+int64_t row_unit(sv_dtype_t dtype) { return dtype == SV_BF16 ? 256 * 8 * 8 : 256 * 4 * 4; }
 constexpr int64_t kDefaultChunkElems = 8192;  // draw chunk length before rounding
 constexpr int64_t kMaxChunks = 1024;          // draw chunks per row (the pick keeps them in LDS)
 constexpr int kMaxDevices = 64;
@@ -39,23 +43,24 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 struct Geometry {
     int32_t nseg, nchunk;
     int64_t seg_len, chunk_len;
-    size_t off_seg, off_task, off_csum, off_band, bytes;
+    size_t off_seg, off_task, off_csum, off_band_n, off_band_w, off_xlogit, bytes;
 };
 
 // Splits a row of V logits into n <= max_pieces pieces of about `target`
-// elements, each a multiple of 8 elements (16 bytes of bf16) long, none empty.
-void split(int64_t V, int64_t target, int64_t max_pieces, int32_t& n, int64_t& len) {
+// elements, each a multiple of `unit` elements long, none empty.
+void split(int64_t V, int64_t target, int64_t max_pieces, int64_t unit, int32_t& n, int64_t& len) {
     int64_t pieces = (V + target / 2) / target;
     if (pieces < 1) pieces = 1;
     if (pieces > max_pieces) pieces = max_pieces;
-    len = ceil_div(ceil_div(V, pieces), 8) * 8;
+    len = ceil_div(ceil_div(V, pieces), unit) * unit;
     n = static_cast<int32_t>(ceil_div(V, len));
 }
 
-bool make_geometry(int32_t B, int64_t total, int64_t V, int64_t seg_elems, int64_t chunk_elems,
-                   Geometry& g) {
-    split(V, seg_elems, 1 << 20, g.nseg, g.seg_len);
-    split(V, chunk_elems, kMaxChunks, g.nchunk, g.chunk_len);
+bool make_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dtype, int64_t seg_elems,
+                   int64_t chunk_elems, Geometry& g) {
+    const int64_t unit = row_unit(dtype);
+    split(V, seg_elems, 1 << 20, seg_elems >= unit ? unit : 8, g.nseg, g.seg_len);
+    split(V, chunk_elems, kMaxChunks, 8, g.nchunk, g.chunk_len);
     const int64_t rows = 2 * total + B;
     if (rows * g.nseg > 0xFFFFFFFFll || static_cast<int64_t>(B) * g.nchunk > 0xFFFFFFFFll) return false;
     size_t off = 0;
@@ -65,8 +70,12 @@ bool make_geometry(int32_t B, int64_t total, int64_t V, int64_t seg_elems, int64
     off = align256(off + sizeof(DrawTask) * static_cast<size_t>(B));
     g.off_csum = off;
     off = align256(off + sizeof(ChunkSums) * static_cast<size_t>(B) * g.nchunk);
-    g.off_band = off;
-    off = align256(off + sizeof(int32_t) * kBandSlots * static_cast<size_t>(B) * g.nchunk);
+    g.off_band_n = off;
+    off = align256(off + sizeof(int32_t) * kWaves * static_cast<size_t>(B) * g.nchunk);
+    g.off_band_w = off;
+    off = align256(off + sizeof(double) * 2 * kWaves * kWaveCap * static_cast<size_t>(B) * g.nchunk);
+    g.off_xlogit = off;
+    off = align256(off + sizeof(float) * static_cast<size_t>(rows));
     g.bytes = off;
     return true;
 }
@@ -118,7 +127,8 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     if (p.B == 0) return SV_OK;
     std::lock_guard<std::mutex> lock(g_mutex);
     Geometry g;
-    if (!make_geometry(p.B, p.total, p.V, g_seg_elems, g_chunk_elems, g)) return SV_ERR_SHAPE;
+    if (!make_geometry(p.B, p.total, p.V, static_cast<sv_dtype_t>(p.dtype), g_seg_elems, g_chunk_elems, g))
+        return SV_ERR_SHAPE;
     if (workspace) {
         if (workspace_bytes < g.bytes) return SV_ERR_WORKSPACE;
         if (!aligned(workspace, 16)) return SV_ERR_ALIGN;
@@ -135,7 +145,9 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     plan.seg = reinterpret_cast<SegStat*>(ws + g.off_seg);
     plan.task = reinterpret_cast<DrawTask*>(ws + g.off_task);
     plan.csum = reinterpret_cast<ChunkSums*>(ws + g.off_csum);
-    plan.band = reinterpret_cast<int32_t*>(ws + g.off_band);
+    plan.band_n = reinterpret_cast<int32_t*>(ws + g.off_band_n);
+    plan.band_w = reinterpret_cast<double*>(ws + g.off_band_w);
+    plan.xlogit = reinterpret_cast<float*>(ws + g.off_xlogit);
 
     hipEvent_t* ev = nullptr;
     if (g_timing) {
@@ -176,7 +188,7 @@ size_t spec_verify_workspace_size(int32_t B, int64_t total_draft, int64_t V, sv_
     if (dtype != SV_F32 && dtype != SV_BF16) return 0;
     std::lock_guard<std::mutex> lock(g_mutex);
     Geometry g;
-    if (!make_geometry(B, total_draft, V, g_seg_elems, g_chunk_elems, g)) return 0;
+    if (!make_geometry(B, total_draft, V, dtype, g_seg_elems, g_chunk_elems, g)) return 0;
     return g.bytes;
 }
 

@@ -23,7 +23,6 @@ constexpr int kThreads = 256;          // workgroup size of every kernel (4 x wa
 constexpr int kWaves = kThreads / 64;
 constexpr int kKMax = SV_K_MAX;
 constexpr int kWaveCap = 8;            // band tokens listed per wave of a draw chunk
-constexpr int kBandSlots = kWaves + kWaves * kWaveCap;   // per chunk: counts, then ids
 
 // Statistics of one segment of one logit row.  Sampling rows keep their sum
 // as s * 2^R with an integer-valued reference R >= max(z) * c, c = log2(e)/T
@@ -46,7 +45,7 @@ struct DrawTask {
     int64_t drow;      // draft row at position n (kResidual only)
     float m_t, m_d;    // exact maxima of those rows
     float T, u;        // temperature and the draw uniform
-    double theta;      // ln(S_p / S_q) from the row pass: p_v > q_v iff d_v > theta
+    double theta;      // log2(S_p / S_q) from the row pass: p_v > q_v iff d_v > theta
 };
 
 // Per-chunk partial sums of the draw (fp64).
@@ -87,7 +86,9 @@ struct Plan {
     SegStat* seg;        // [(2 * total + B) * nseg]; target rows first
     DrawTask* task;      // [B]
     ChunkSums* csum;     // [B * nchunk]
-    int32_t* band;       // [B * nchunk * kBandSlots]: per-wave counts, then token ids
+    int32_t* band_n;     // [B * nchunk * kWaves]: band tokens seen per wave of a chunk
+    double* band_w;      // [B * nchunk * kWaves * kWaveCap * 2]: their (w_t, w_d)
+    float* xlogit;       // [2 * total + B]: logit of the drafted token of each row
 };
 
 // Host-side launchers (one per kernel).
