@@ -29,10 +29,13 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Word 3 of a raw buffer descriptor on gfx9-family GPUs (32-bit data format,
+// no swizzle, range checked against num_records).
+constexpr int kBufferDword3 = 0x00020000;
+// Cache policy of the streaming loads: non-temporal.
+constexpr int kLoadNonTemporal = 2;
 
-__device__ __forceinline__ u32x4 stream_load(const u32x4* p) {
-    return __builtin_nontemporal_load(p);
-}
+
 
 // Hardware 2^x (v_exp_f32): 2^-inf = 0.
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -127,11 +130,19 @@ struct ArgmaxAcc {
 // Streams logits [s0, s1) of one row into acc.  Order per lane: the
 // unaligned head element, its vectors in increasing order, the tail element
 // -- increasing token ids throughout.
+//
+// The aligned body is read with raw buffer loads against a descriptor that
+// spans exactly its nvec vectors: a load past the end returns zeros and
+// touches no memory.  Every load is therefore issued on every path, with no
+// branch around it and no clamped re-read, and since the hardware counts
+// outstanding loads in issue order the compiler can wait for exactly the
+// oldest one instead of draining the window.
 template <int DT, class Acc>
 __device__ __forceinline__ void stream_segment(const void* row_v, int64_t s0, int64_t s1, Acc& acc) {
     using E = typename Elem<DT>::T;
     constexpr int N = Elem<DT>::N;
     constexpr int kWindow = Elem<DT>::kWindow;
+    constexpr int32_t kTileBytes = kThreads * 16;
     const E* row = static_cast<const E*>(row_v);
     const int tid = threadIdx.x;
     const uintptr_t addr = reinterpret_cast<uintptr_t>(row + s0);
@@ -140,52 +151,63 @@ __device__ __forceinline__ void stream_segment(const void* row_v, int64_t s0, in
     const int64_t a0 = s0 + head;
     const int32_t nvec = static_cast<int32_t>((s1 - a0) / N);
     const int64_t a1 = a0 + static_cast<int64_t>(nvec) * N;
+    const int64_t ntail = s1 - a1;
 
-    if (tid < head) acc.add1(load_logit(row_v, DT, s0 + tid), static_cast<int32_t>(s0 + tid));
-
-    // Full tiles (one 16-byte vector per lane) stream through a rolling
-    // window of kWindow loads.  The tile count is workgroup-uniform, so
-    // every condition below is a scalar branch and each vector is processed
-    // before the load that refills its register is issued.
-    const u32x4* vp = reinterpret_cast<const u32x4*>(row + a0) + tid;
-    const int32_t ntiles = nvec / kThreads;
+    const int32_t nfull = nvec / kThreads;                       // full tiles
+    const int32_t nt = (nvec + kThreads - 1) / kThreads;         // plus the partial one
+    const int32_t rem = nvec - nfull * kThreads;                 // its lanes: tid < rem
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<E*>(row + a0), 0, nvec * 16, kBufferDword3);
+    const int32_t voff = tid * 16;
+    auto load_tile = [&](int32_t t) {
+        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, t * kTileBytes,
+                                                                               kLoadNonTemporal));
+    };
     const int32_t base0 = static_cast<int32_t>(a0) + tid * N;
     auto process = [&](const u32x4 v, int32_t t) {
         float x[N];
         Elem<DT>::unpack(v, x);
         acc.template add<N>(x, base0 + t * kThreads * N);
     };
-    // The partial tile: lanes tid < rem own one more vector, loaded up front.
-    const int32_t rem = nvec - ntiles * kThreads;
-    u32x4 extra{};
-    if (tid < rem) extra = stream_load(vp + ntiles * kThreads);
+    auto process_last = [&](const u32x4 v, int32_t t) {
+        if (t < nfull || tid < rem) process(v, t);
+    };
+
+    // Head and tail elements (clamped into the segment; used only by the
+    // lanes that own one), then the first window of tiles.  The scheduling
+    // barriers keep this issue order: the loop waits on slot 0 being oldest.
+    const int64_t hi = s0 + min(static_cast<int64_t>(tid), s1 - s0 - 1);
+    const int64_t ti = ntail > 0 ? a1 + min(static_cast<int64_t>(tid), ntail - 1) : hi;
+    const float hv = load_logit(row_v, DT, hi);
+    const float tv = load_logit(row_v, DT, ti);
+    __builtin_amdgcn_sched_barrier(0);
     u32x4 buf[kWindow];
 #pragma unroll
-    for (int u = 0; u < kWindow; ++u)
-        if (u < ntiles) buf[u] = stream_load(vp + u * kThreads);
+    for (int u = 0; u < kWindow; ++u) {
+        buf[u] = load_tile(u);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (tid < head) acc.add1(hv, static_cast<int32_t>(hi));
+
+    // Steady state: tiles i .. i+W-1 are full (i + 2W <= nt <= nfull + 1).
     int32_t i = 0;
-    // Steady state: every slot is refilled, so the only waits are for the
-    // oldest load in flight.
-    for (; i + 2 * kWindow <= ntiles; i += kWindow) {
+    for (; i + 2 * kWindow <= nt; i += kWindow) {
 #pragma unroll
         for (int u = 0; u < kWindow; ++u) {
             process(buf[u], i + u);
-            buf[u] = stream_load(vp + (i + kWindow + u) * kThreads);
+            buf[u] = load_tile(i + kWindow + u);
         }
     }
-    // Drain: slots i .. i+W-1 (those < ntiles) are loaded, the rest are not.
+    // Drain: fewer than 2W tiles remain; loads past the end are free.
 #pragma unroll
     for (int u = 0; u < kWindow; ++u) {
-        if (i + u < ntiles) {
-            process(buf[u], i + u);
-            if (i + kWindow + u < ntiles) buf[u] = stream_load(vp + (i + kWindow + u) * kThreads);
-        }
+        if (i + u < nt) process_last(buf[u], i + u);
+        buf[u] = load_tile(i + kWindow + u);
     }
 #pragma unroll
     for (int u = 0; u < kWindow; ++u)
-        if (i + kWindow + u < ntiles) process(buf[u], i + kWindow + u);
-    if (tid < rem) process(extra, ntiles);
-    if (tid < s1 - a1) acc.add1(load_logit(row_v, DT, a1 + tid), static_cast<int32_t>(a1 + tid));
+        if (i + kWindow + u < nt) process_last(buf[u], i + kWindow + u);
+    if (tid < ntail) acc.add1(tv, static_cast<int32_t>(ti));
 }
 
 // Two partial sums s * 2^R of the same row, merged exactly in fp64.
@@ -223,9 +245,10 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(Problem p, Plan pla
     const int64_t s1 = min(p.V, s0 + plan.seg_len);
 
     // The workgroup whose segment holds this row's drafted token records that
-    // token's logit for the accept scan (loaded now, stored after the stream).
+    // token's logit for the accept scan.  Every workgroup issues the (uniform)
+    // load, at s0 when it captures nothing, so no load sits under a branch.
     bool capture = false;
-    float zx = 0.f;
+    int64_t xc = s0;
     if (!greedy) {
         const int64_t o = p.offsets ? static_cast<int64_t>(p.offsets[b]) : static_cast<int64_t>(b) * p.k_uniform;
         const int64_t k = p.offsets ? static_cast<int64_t>(p.offsets[b + 1]) - o : p.k_uniform;
@@ -233,9 +256,10 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(Problem p, Plan pla
         if (i >= 0 && i < k && o >= 0 && o + i < p.total) {
             const int32_t x = p.tokens[o + i];
             capture = x >= s0 && x < s1;
-            if (capture && threadIdx.x == 0) zx = load_logit(row, DT, x);
+            if (capture) xc = x;
         }
     }
+    const float zx = load_logit(row, DT, xc);
 
     __shared__ float lds_m[kWaves], lds_R[kWaves];
     __shared__ double lds_s[kWaves];
