@@ -24,15 +24,19 @@
 //     to get their exact mass once S_p and S_q are known.  The residual mass
 //     of chunk c is R_c = A_c / S_p - B_c / S_q + sum over its band tokens of
 //     max(0, w_t/S_p - w_d/S_q); a chunk whose lists overflowed is rescanned.
-// draw_pick (one workgroup per sequence) forms Z = sum_c R_c, finds the chunk
-// whose cumulative mass crosses u Z, and scans that one chunk with a
-// workgroup-wide fp64 prefix sum over masses held in registers.  The kernel
-// boundary publishes the chunk sums; no device-wide fences are needed.
+// draw_pick (one 1024-thread workgroup per sequence) forms Z = sum_c R_c,
+// finds the chunk whose cumulative mass crosses u Z with a wave-wide scan,
+// and scans that one chunk with a workgroup-wide fp64 prefix sum over masses
+// held in registers.  The kernel boundary publishes the chunk sums; no
+// device-wide fences are needed.
 //
 // 2^y in fp64 follows Tang's table-driven method (ACM TOMS 15(2), 1989) in
 // base 2 with a 256-entry table: y = k + j/256 + r with |r| <= 1/512,
 // 2^y = 2^k 2^(j/256) e^(r ln2), e^(r ln2) - 1 by its degree-4 Taylor
 // polynomial (truncation < 4e-17 relative).  The kernels carry Y = 256 y.
+// The scaling by 2^k is folded into the table: each entry keeps the high
+// word of 2^(j/256) minus j << 12, so adding round(Y) << 12 to it adds k to
+// the exponent field in one integer add.
 #include "sv_internal.h"
 
 namespace sv {
@@ -43,9 +47,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr double kLog2e = 0x1.71547652b82fep+0;
 constexpr double kDegenerateZ = 1e-9;            // residual mass treated as empty
 constexpr double kBand = 3e-5;                   // classification band (log2 units)
+constexpr double kMinY = -1021.0 * 256.0;        // weights stay normal doubles (>= 2^-1021)
 constexpr int kMaxPickChunks = 1024;             // chunk masses held in LDS by the pick
-constexpr int kRun = 16;                         // tokens per lane in the pick's scan
-constexpr int64_t kPiece = kThreads * kRun;      // tokens per scan step of the pick
+constexpr int kPickThreads = 1024;               // workgroup of the pick
+constexpr int kPickWaves = kPickThreads / 64;
+constexpr int kRun = 8;                          // tokens per lane in the pick's scan
+constexpr int64_t kPiece = kPickThreads * kRun;  // tokens per scan step of the pick
+constexpr int kSlots = kWaves * kWaveCap;        // band entries per chunk (32)
+constexpr int kBufferDword3 = 0x00020000;        // raw buffer descriptor word 3 (gfx9 family)
 
 // 2^(j/256), j = 0..255, correctly rounded.
 __constant__ double kExp2Frac[256] = {
@@ -115,22 +124,37 @@ __constant__ double kExp2Frac[256] = {
     0x1.fa7c1819e90d8p+0, 0x1.fbdba3692d514p+0, 0x1.fd3c22b8f71f1p+0, 0x1.fe9d96b2a23d9p+0,
 };
 
-// 2^(Y/256) in fp64 for Y <= ~256000 (arguments here are <= 0); tbl = kExp2Frac
-// in LDS.  Y = n + r with n = round(Y) (the 1.5 * 2^52 shifter: after the add
-// the low 32 bits of the double hold n in two's complement) and |r| <= 1/2, so
+// One table entry: the low word of 2^(j/256) and its high word minus j << 12.
+struct alignas(8) TabEntry {
+    uint32_t lo, hi;
+};
+
+// Fills the LDS table; call with every thread of the workgroup, then barrier.
+__device__ __forceinline__ void load_table(TabEntry* tbl, int nthreads) {
+    for (int i = threadIdx.x; i < 256; i += nthreads) {
+        const uint64_t bits = static_cast<uint64_t>(__double_as_longlong(kExp2Frac[i]));
+        tbl[i].lo = static_cast<uint32_t>(bits);
+        tbl[i].hi = static_cast<uint32_t>(bits >> 32) - (static_cast<uint32_t>(i) << 12);
+    }
+}
+
+// 2^(Y/256) in fp64 for Y <= 0 (Y is clamped at kMinY).  Y = n + r with
+// n = round(Y) (the 1.5 * 2^52 shifter: after the add the low 32 bits of the
+// double hold n in two's complement) and |r| <= 1/2, so
 // 2^(Y/256) = 2^(n>>8) 2^((n&255)/256) e^x with x = r ln2/256, |x| <= ln2/512;
 // e^x - 1 by its degree-4 Taylor polynomial (truncation < 4e-17 relative).
-__device__ __forceinline__ double exp2_256(double Y, const double* tbl) {
+__device__ __forceinline__ double exp2_256(double Y, const TabEntry* tbl) {
     constexpr double kShift = 0x1.8p52;
-    Y = fmax(Y, -281600.0);                        // 2^-1100 underflows to 0 anyway
+    Y = fmax(Y, kMinY);
     const double kd = Y + kShift;
-    const int n = static_cast<int>(static_cast<uint32_t>(__double_as_longlong(kd)));
+    const uint32_t n = static_cast<uint32_t>(__double_as_longlong(kd));
     const double r = Y - (kd - kShift);            // exact
     double q = fma(r, 0x1.3b2ab6fba4e77p-39, 0x1.c6b08d704a0c0p-29);
     q = fma(q, r, 0x1.ebfbdff82c58fp-19);
     q = fma(q, r, 0x1.62e42fefa39efp-9);
-    const double t = tbl[n & 255];
-    return ldexp(fma(t, q * r, t), n >> 8);
+    const TabEntry e = tbl[n & 255u];
+    const double t = __hiloint2double(static_cast<int>(e.hi + (n << 12)), static_cast<int>(e.lo));
+    return fma(t, q * r, t);
 }
 
 template <int DT> struct Vec;
@@ -162,7 +186,7 @@ struct Rows {
     const E* d;          // draft row at position n (residual only)
     double c;            // 256 log2(e) / T
     double ot, od;       // -m_t * c, -m_d * c
-    const double* tbl;
+    const TabEntry* tbl;
 
     __device__ __forceinline__ double Yt(float z) const { return fma(static_cast<double>(z), c, ot); }
     __device__ __forceinline__ double Yd(float z) const { return fma(static_cast<double>(z), c, od); }
@@ -173,7 +197,7 @@ struct Rows {
 };
 
 template <int DT>
-__device__ __forceinline__ Rows<DT> rows_of(const Problem& p, const DrawTask& task, const double* tbl) {
+__device__ __forceinline__ Rows<DT> rows_of(const Problem& p, const DrawTask& task, const TabEntry* tbl) {
     using E = typename Vec<DT>::E;
     const double c = 256.0 * kLog2e / static_cast<double>(task.T);
     return Rows<DT>{static_cast<const E*>(p.target) + task.trow * p.V,
@@ -181,42 +205,55 @@ __device__ __forceinline__ Rows<DT> rows_of(const Problem& p, const DrawTask& ta
                     c, -static_cast<double>(task.m_t) * c, -static_cast<double>(task.m_d) * c, tbl};
 }
 
-__device__ __forceinline__ void load_table(double* tbl) {
-    for (int i = threadIdx.x; i < 256; i += kThreads) tbl[i] = kExp2Frac[i];
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int32_t byte_off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
-// Calls f(v, z_t, z_d) for this thread's tokens of [v0, v1): 16-byte vector
-// loads (lane-strided vectors) when both rows allow them, scalar otherwise.
+// Calls f(z_t, z_d) for this thread's tokens of [v0, v1), in the order
+// lane-strided 16-byte vectors, then single tokens for a ragged tail.  When
+// both rows start 16-byte aligned the vectors come from raw buffer loads
+// against descriptors that span exactly the chunk's vectors, one iteration
+// ahead of use (a load past the end returns zeros and touches no memory);
+// otherwise every token is loaded on its own.
 template <int DT, bool kResid, class F>
 __device__ __forceinline__ void for_chunk(const Rows<DT>& rows, int64_t v0, int64_t v1, F&& f) {
+    using E = typename Vec<DT>::E;
     constexpr int N = Vec<DT>::N;
     const bool vec = (reinterpret_cast<uintptr_t>(rows.t + v0) & 15u) == 0 &&
                      (!kResid || (reinterpret_cast<uintptr_t>(rows.d + v0) & 15u) == 0);
     int64_t vs = v0;
     if (vec) {
-        const int64_t nvec = (v1 - v0) / N;
-        const u32x4* tp = reinterpret_cast<const u32x4*>(rows.t + v0);
-        const u32x4* dp = reinterpret_cast<const u32x4*>(rows.d + v0);
-        for (int64_t j = threadIdx.x; j < nvec; j += kThreads) {
-            const u32x4 a0 = tp[j];
-            const u32x4 b0 = kResid ? dp[j] : a0;
+        const int32_t nvec = static_cast<int32_t>((v1 - v0) / N);
+        const __amdgpu_buffer_rsrc_t rt =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<E*>(rows.t + v0), 0, nvec * 16, kBufferDword3);
+        const __amdgpu_buffer_rsrc_t rd = kResid
+            ? __builtin_amdgcn_make_buffer_rsrc(const_cast<E*>(rows.d + v0), 0, nvec * 16, kBufferDword3)
+            : rt;
+        int32_t j = threadIdx.x;
+        u32x4 a = buffer_load16(rt, j * 16);
+        u32x4 bb = kResid ? buffer_load16(rd, j * 16) : a;
+        for (; j < nvec; j += kThreads) {
+            const u32x4 an = buffer_load16(rt, (j + kThreads) * 16);
+            const u32x4 bn = kResid ? buffer_load16(rd, (j + kThreads) * 16) : an;
             float xt[N], xd[N];
-            Vec<DT>::unpack(a0, xt);
-            if (kResid) Vec<DT>::unpack(b0, xd);
+            Vec<DT>::unpack(a, xt);
+            if (kResid) Vec<DT>::unpack(bb, xd);
 #pragma unroll
             for (int e = 0; e < N; ++e) {
-                f(v0 + j * N + e, xt[e], kResid ? xd[e] : 0.f);
-                // interleave at most two tokens' fp64 work: keeps occupancy at 8
+                f(xt[e], kResid ? xd[e] : 0.f);
+                // interleave at most two tokens' fp64 work: bounds the register count
                 if (e % 2 == 1) __builtin_amdgcn_sched_barrier(0);
             }
+            a = an;
+            bb = bn;
         }
-        vs = v0 + nvec * N;
+        vs = v0 + static_cast<int64_t>(nvec) * N;
     }
     for (int64_t v = vs + threadIdx.x; v < v1; v += kThreads)
-        f(v, rows.zt(v), kResid ? rows.zd(v) : 0.f);
+        f(rows.zt(v), kResid ? rows.zd(v) : 0.f);
 }
 
-// Sums of four doubles over the workgroup (valid in every thread).
+// Sums of four doubles over a 256-thread workgroup (valid in every thread).
 __device__ __forceinline__ void block_sum4(double& a, double& b, double& c, double& d,
                                            double (*lds)[4]) {
     for (int off = 32; off > 0; off >>= 1) {
@@ -233,8 +270,92 @@ __device__ __forceinline__ void block_sum4(double& a, double& b, double& c, doub
     for (int w = 0; w < kWaves; ++w) { a += lds[w][0]; b += lds[w][1]; c += lds[w][2]; d += lds[w][3]; }
 }
 
-// Exclusive prefix sum over the workgroup in thread order; *total = sum.
-__device__ __forceinline__ double block_scan_excl(double x, double* total, double* lds) {
+// Chunk pass: grid (sequence x chunk), 256 threads.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void draw_sums_kernel(Problem p, Plan plan) {
+    const int64_t w = blockIdx.x;
+    const int32_t b = static_cast<int32_t>(w / plan.nchunk);
+    const int32_t c = static_cast<int32_t>(w - static_cast<int64_t>(b) * plan.nchunk);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+    __shared__ TabEntry tbl[256];
+    __shared__ double lds4[kWaves][4];
+    __shared__ double wlist[kWaves][kWaveCap][2];
+    __shared__ int32_t wcount[kWaves];
+    load_table(tbl, kThreads);                 // overlaps the task load
+    const DrawTask task = plan.task[b];
+    if (task.kind == kNone) return;            // the whole workgroup leaves
+    const bool resid_task = (task.kind == kResidual);
+    __syncthreads();
+    const Rows<DT> rows = rows_of<DT>(p, task, tbl);
+
+    const int64_t v0 = static_cast<int64_t>(c) * plan.chunk_len;
+    const int64_t v1 = min(p.V, v0 + plan.chunk_len);
+    double sp = 0.0, sq = 0.0, a = 0.0, bq = 0.0;
+    int32_t nband = 0;                         // uniform over the lanes still active
+    if (resid_task) {
+        const double th_hi = 256.0 * (task.theta + kBand), th_lo = 256.0 * (task.theta - kBand);
+        for_chunk<DT, true>(rows, v0, v1, [&](float zt, float zd) {
+            const double yt = rows.Yt(zt), yd = rows.Yd(zd);
+            const double wt = exp2_256(yt, tbl), wd = exp2_256(yd, tbl);
+            sp += wt;
+            sq += wd;
+            const double dv = yt - yd;
+            const bool hi = dv > th_hi;
+            const double h = hi ? 1.0 : 0.0;
+            a = fma(h, wt, a);
+            bq = fma(h, wd, bq);
+            // band = lanes with th_lo <= d_v <= th_hi (wave-uniform mask)
+            const uint64_t band = __ballot(dv >= th_lo) & ~__ballot(hi);
+            if (band) {
+                const int pos = nband + __popcll(band & ((1ull << lane) - 1ull));
+                if (((band >> lane) & 1ull) && pos < kWaveCap) {
+                    wlist[wave][pos][0] = wt;
+                    wlist[wave][pos][1] = wd;
+                }
+                nband += __popcll(band);
+            }
+        });
+    } else {
+        for_chunk<DT, false>(rows, v0, v1, [&](float zt, float) { sp += rows.wt(zt); });
+    }
+    if (lane == 0) wcount[wave] = nband;      // lane 0 was active whenever any lane was
+    block_sum4(sp, sq, a, bq, lds4);
+    if (threadIdx.x == 0) {
+        ChunkSums cs;
+        cs.sp = sp; cs.sq = sq; cs.a = a; cs.b = bq;
+        plan.csum[w] = cs;
+    }
+    if (resid_task) {
+        if (threadIdx.x < kWaves) plan.band_n[w * kWaves + threadIdx.x] = wcount[threadIdx.x];
+        if (threadIdx.x < kSlots) {
+            const int wv = threadIdx.x / kWaveCap, e = threadIdx.x % kWaveCap;
+            if (e < wcount[wv]) {
+                double* dst = plan.band_w + (w * kSlots + threadIdx.x) * 2;
+                dst[0] = wlist[wv][e][0];
+                dst[1] = wlist[wv][e][1];
+            }
+        }
+    }
+}
+
+// ---- the pick: one 1024-thread workgroup per sequence ----------------------
+
+// Sum of two doubles over the pick's workgroup (valid in every thread).
+__device__ __forceinline__ void pick_sum2(double& a, double& b, double (*lds)[2]) {
+    for (int off = 32; off > 0; off >>= 1) {
+        a += __shfl_xor(a, off, 64);
+        b += __shfl_xor(b, off, 64);
+    }
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) { lds[threadIdx.x >> 6][0] = a; lds[threadIdx.x >> 6][1] = b; }
+    __syncthreads();
+    a = b = 0.0;
+    for (int w = 0; w < kPickWaves; ++w) { a += lds[w][0]; b += lds[w][1]; }
+}
+
+// Exclusive prefix sum over the pick's workgroup in thread order; *total = sum.
+__device__ __forceinline__ double pick_scan_excl(double x, double* total, double* lds) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     double inc = x;
     for (int off = 1; off < 64; off <<= 1) {
@@ -247,7 +368,7 @@ __device__ __forceinline__ double block_scan_excl(double x, double* total, doubl
     if (lane == 63) lds[wave] = inc;
     __syncthreads();
     double before = 0.0, all = 0.0;
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < kPickWaves; ++w) {
         if (w < wave) before += lds[w];
         all += lds[w];
     }
@@ -255,7 +376,7 @@ __device__ __forceinline__ double block_scan_excl(double x, double* total, doubl
     return before + excl;
 }
 
-__device__ __forceinline__ int32_t block_min_max(int32_t x, bool want_min, int32_t* lds) {
+__device__ __forceinline__ int32_t pick_min_max(int32_t x, bool want_min, int32_t* lds) {
     for (int off = 32; off > 0; off >>= 1) {
         const int32_t y = __shfl_xor(x, off, 64);
         x = want_min ? min(x, y) : max(x, y);
@@ -264,131 +385,139 @@ __device__ __forceinline__ int32_t block_min_max(int32_t x, bool want_min, int32
     if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = x;
     __syncthreads();
     int32_t r = lds[0];
-    for (int w = 1; w < kWaves; ++w) r = want_min ? min(r, lds[w]) : max(r, lds[w]);
+    for (int w = 1; w < kPickWaves; ++w) r = want_min ? min(r, lds[w]) : max(r, lds[w]);
     return r;
 }
 
-// Chunk pass: grid (sequence x chunk).
-template <int DT>
-__global__ __launch_bounds__(kThreads) void draw_sums_kernel(Problem p, Plan plan) {
-    const int64_t w = blockIdx.x;
-    const int32_t b = static_cast<int32_t>(w / plan.nchunk);
-    const int32_t c = static_cast<int32_t>(w - static_cast<int64_t>(b) * plan.nchunk);
-    const DrawTask task = plan.task[b];
-    if (task.kind == kNone) return;
-    const bool resid_task = (task.kind == kResidual);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-
-    __shared__ double tbl[256];
-    __shared__ double lds4[kWaves][4];
-    __shared__ double wlist[kWaves][kWaveCap][2];
-    __shared__ int32_t wcount[kWaves];
-    load_table(tbl);
-    __syncthreads();
-    const Rows<DT> rows = rows_of<DT>(p, task, tbl);
-
-    const int64_t v0 = static_cast<int64_t>(c) * plan.chunk_len;
-    const int64_t v1 = min(p.V, v0 + plan.chunk_len);
-    double sp = 0.0, sq = 0.0, a = 0.0, bq = 0.0;
-    int32_t nband = 0;                         // uniform over the lanes still active
-    if (resid_task) {
-        const double th_hi = 256.0 * (task.theta + kBand), th_lo = 256.0 * (task.theta - kBand);
-        for_chunk<DT, true>(rows, v0, v1, [&](int64_t, float zt, float zd) {
-            const double yt = rows.Yt(zt), yd = rows.Yd(zd);
-            const double wt = exp2_256(yt, tbl), wd = exp2_256(yd, tbl);
-            sp += wt;
-            sq += wd;
-            const double dv = yt - yd;
-            const bool hi = dv > th_hi;
-            const double h = hi ? 1.0 : 0.0;
-            a = fma(h, wt, a);
-            bq = fma(h, wd, bq);
-            const bool in_band = !hi && dv >= th_lo;
-            const uint64_t m = __ballot(in_band);
-            if (m) {
-                const int pos = nband + __popcll(m & ((1ull << lane) - 1ull));
-                if (in_band && pos < kWaveCap) { wlist[wave][pos][0] = wt; wlist[wave][pos][1] = wd; }
-                nband += __popcll(m);
-            }
-        });
-    } else {
-        for_chunk<DT, false>(rows, v0, v1, [&](int64_t, float zt, float) { sp += rows.wt(zt); });
+// Wave-wide search over chunk masses m[0..n) (run by one whole wave): the
+// first chunk whose cumulative mass exceeds target, with the mass before it;
+// when rounding leaves target at or past the total, the last chunk with
+// positive mass.  Returns the total in *Z.
+__device__ __forceinline__ void find_chunk(const double* m, int32_t n, double u, double* Z,
+                                           int32_t* chunk, double* base) {
+    const int lane = threadIdx.x & 63;
+    const int32_t per = (n + 63) / 64;        // chunks per lane, in order
+    const int32_t j0 = min(n, lane * per), j1 = min(n, j0 + per);
+    double mine = 0.0;
+    for (int32_t j = j0; j < j1; ++j) mine += m[j];
+    double inc = mine;
+    for (int off = 1; off < 64; off <<= 1) {
+        const double y = __shfl_up(inc, off, 64);
+        if (lane >= off) inc += y;
     }
-    if (lane == 0) wcount[wave] = nband;      // lane 0 was active whenever any lane was
-    block_sum4(sp, sq, a, bq, lds4);
-    if (threadIdx.x == 0) {
-        ChunkSums cs;
-        cs.sp = sp; cs.sq = sq; cs.a = a; cs.b = bq;
-        plan.csum[w] = cs;
-    }
-    if (resid_task) {
-        if (threadIdx.x < kWaves) plan.band_n[w * kWaves + threadIdx.x] = wcount[threadIdx.x];
-        if (threadIdx.x < kWaves * kWaveCap) {
-            const int wv = threadIdx.x / kWaveCap, e = threadIdx.x % kWaveCap;
-            if (e < wcount[wv]) {
-                double* dst = plan.band_w + (w * kWaves * kWaveCap + threadIdx.x) * 2;
-                dst[0] = wlist[wv][e][0];
-                dst[1] = wlist[wv][e][1];
-            }
+    const double total = __shfl(inc, 63, 64);
+    const double target = u * total;
+    const double excl = inc - mine;
+    // the lane whose range holds the crossing: excl <= target < inc
+    int32_t found = -1;
+    double fb = 0.0;
+    if (excl <= target && target < inc) {
+        double run = excl;
+        for (int32_t j = j0; j < j1; ++j) {
+            if (run + m[j] > target) { found = j; fb = run; break; }
+            run += m[j];
         }
     }
+    // fallback: the last chunk with positive mass
+    int32_t lastj = -1;
+    double lastb = 0.0;
+    {
+        double run = excl;
+        for (int32_t j = j0; j < j1; ++j) {
+            if (m[j] > 0.0) { lastj = j; lastb = run; }
+            run += m[j];
+        }
+    }
+    const uint64_t fm = __ballot(found >= 0);
+    if (fm) {
+        const int src = __ffsll(static_cast<unsigned long long>(fm)) - 1;
+        *chunk = __shfl(found, src, 64);
+        *base = __shfl(fb, src, 64);
+    } else {
+        const uint64_t lm = __ballot(lastj >= 0);
+        const int src = lm ? 63 - __clzll(static_cast<long long>(lm)) : 0;
+        *chunk = lm ? __shfl(lastj, src, 64) : 0;
+        *base = lm ? __shfl(lastb, src, 64) : 0.0;
+    }
+    *Z = total;
 }
 
-// Pick: one workgroup per sequence.
 template <int DT>
-__global__ __launch_bounds__(kThreads) void draw_pick_kernel(Problem p, Plan plan) {
+__global__ __launch_bounds__(kPickThreads) void draw_pick_kernel(Problem p, Plan plan) {
     constexpr int N = Vec<DT>::N;
-    constexpr int kSlots = kWaves * kWaveCap;    // band entries per chunk (32)
     const int32_t b = blockIdx.x;
+    const int tid = threadIdx.x, wave = tid >> 6;
+
+    __shared__ TabEntry tbl[256];
+    __shared__ double red2[kPickWaves][2];
+    __shared__ double scan_lds[kPickWaves];
+    __shared__ int32_t ldsi[kPickWaves];
+    __shared__ double mass[kMaxPickChunks];
+    __shared__ double spc[kMaxPickChunks];
+    __shared__ double sh_base, sh_target;
+    __shared__ int32_t sh_chunk, sh_resid, sh_rescan;
+    load_table(tbl, kPickThreads);
     const DrawTask task = plan.task[b];
     if (task.kind == kNone) return;
     const bool resid_task = (task.kind == kResidual);
-    const int lane = threadIdx.x & 63;
-
-    __shared__ double tbl[256];
-    __shared__ double lds4[kWaves][4];
-    __shared__ double lds[kWaves];
-    __shared__ int32_t ldsi[kWaves];
-    __shared__ double mass[kMaxPickChunks];
-    __shared__ double sh_base, sh_target;
-    __shared__ int32_t sh_chunk, sh_resid, sh_rescan;
-    load_table(tbl);
-    if (threadIdx.x == 0) sh_rescan = 0;
     const Rows<DT> rows = rows_of<DT>(p, task, tbl);
-    const int64_t cb = static_cast<int64_t>(b) * plan.nchunk;
-    const ChunkSums* cs = plan.csum + cb;
     const int32_t nchunk = plan.nchunk;
+    const int64_t cb = static_cast<int64_t>(b) * nchunk;
+    const ChunkSums* cs = plan.csum + cb;
+    if (tid == 0) sh_rescan = 0;
 
-    double Sp = 0.0, Sq = 0.0, unused0 = 0.0, unused1 = 0.0;
-    for (int32_t j = threadIdx.x; j < nchunk; j += kThreads) {
-        Sp += cs[j].sp;
-        Sq += cs[j].sq;
+    // All loads that need only the sequence are issued together: the chunk
+    // sums (one chunk per thread) and the band entries of the first 32
+    // chunks (one slot per thread; an entry past its wave's count is stale
+    // and ignored).
+    double Sp = 0.0, Sq = 0.0, ca = 0.0, cbq = 0.0;
+    for (int32_t j = tid; j < nchunk; j += kPickThreads) {
+        const ChunkSums x = cs[j];
+        Sp += x.sp;
+        Sq += x.sq;
+        spc[j] = x.sp;
+        if (j == tid) { ca = x.a; cbq = x.b; }
     }
-    block_sum4(Sp, Sq, unused0, unused1, lds4);     // (its barriers also publish tbl)
+    const int32_t pj = tid / kSlots, ps = tid % kSlots;
+    int32_t pcnt = 0;
+    double pwt = 0.0, pwd = 0.0;
+    if (resid_task && pj < nchunk) {
+        pcnt = plan.band_n[(cb + pj) * kWaves + ps / kWaveCap];
+        const double* pw = plan.band_w + ((cb + pj) * kSlots + ps) * 2;
+        pwt = pw[0];
+        pwd = pw[1];
+    }
+    pick_sum2(Sp, Sq, red2);                   // (its barriers also publish tbl and spc)
     const double iSp = 1.0 / Sp, iSq = resid_task ? 1.0 / Sq : 0.0;
 
     if (resid_task) {
-        // Band terms: 32 lanes per chunk, one listed token each; a fixed
-        // shuffle tree sums them per chunk (deterministic order).
-        for (int64_t t0 = 0; t0 < static_cast<int64_t>(nchunk) * kSlots; t0 += kThreads) {
-            const int64_t t = t0 + threadIdx.x;
-            const int32_t j = static_cast<int32_t>(t / kSlots), s = static_cast<int32_t>(t % kSlots);
-            double term = 0.0;
-            bool over = false;
-            if (j < nchunk) {
-                const int32_t cnt = plan.band_n[(cb + j) * kWaves + s / kWaveCap];
-                over = cnt > kWaveCap;
-                if (s % kWaveCap < cnt) {
-                    const double* pw = plan.band_w + ((cb + j) * kSlots + s) * 2;
-                    term = fmax(0.0, pw[0] * iSp - pw[1] * iSq);
+        for (int32_t j = tid; j < nchunk; j += kPickThreads) {
+            const double a = (j == tid) ? ca : cs[j].a;
+            const double bq = (j == tid) ? cbq : cs[j].b;
+            mass[j] = a * iSp - bq * iSq;
+        }
+        __syncthreads();
+        // Band terms: 32 lanes per chunk (a half wave), one listed token
+        // each; a fixed shuffle tree sums them (deterministic order).
+        for (int32_t j0 = 0; j0 < nchunk; j0 += kPickThreads / kSlots) {
+            const int32_t j = j0 + pj;
+            int32_t cnt = pcnt;
+            double wt = pwt, wd = pwd;
+            if (j0 > 0) {
+                cnt = 0;
+                if (j < nchunk) {
+                    cnt = plan.band_n[(cb + j) * kWaves + ps / kWaveCap];
+                    const double* pw = plan.band_w + ((cb + j) * kSlots + ps) * 2;
+                    wt = pw[0];
+                    wd = pw[1];
                 }
             }
+            double term = (j < nchunk && ps % kWaveCap < cnt) ? fmax(0.0, wt * iSp - wd * iSq) : 0.0;
             for (int off = kSlots / 2; off > 0; off >>= 1) term += __shfl_xor(term, off, 64);
-            if (j < nchunk && s == 0)
-                mass[j] = cs[j].a * iSp - cs[j].b * iSq + term;
-            if (over) atomicOr(&sh_rescan, 1);
-            __syncthreads();
-            if (over && s % kWaveCap == 0) mass[j] = NAN;       // this chunk needs a rescan
+            const bool over = j < nchunk && cnt > kWaveCap;
+            const bool any_over = (__ballot(over) >> ((tid & 63) & ~(kSlots - 1))) & 0xffffffffull;
+            if (j < nchunk && ps == 0) mass[j] = any_over ? NAN : mass[j] + term;
+            if (over) sh_rescan = 1;           // benign race: every writer stores 1
         }
         __syncthreads();
         if (sh_rescan) {
@@ -397,39 +526,30 @@ __global__ __launch_bounds__(kThreads) void draw_pick_kernel(Problem p, Plan pla
                 if (!isnan(mass[j])) continue;
                 const int64_t u0 = static_cast<int64_t>(j) * plan.chunk_len;
                 const int64_t u1 = min(p.V, u0 + plan.chunk_len);
-                double m = 0.0;
-                for (int64_t v = u0 + threadIdx.x; v < u1; v += kThreads)
+                double m = 0.0, unused = 0.0;
+                for (int64_t v = u0 + tid; v < u1; v += kPickThreads)
                     m += fmax(0.0, rows.wt(rows.zt(v)) * iSp - rows.wd(rows.zd(v)) * iSq);
-                m = block_sum(m, lds);
-                if (threadIdx.x == 0) mass[j] = m;
+                pick_sum2(m, unused, red2);
+                if (tid == 0) mass[j] = m;
                 __syncthreads();
             }
         }
     }
-    if (threadIdx.x == 0) {
+    if (wave == 0) {
         bool resid = resid_task;
-        double Z = 0.0;
+        double Z = 0.0, base = 0.0;
+        int32_t chunk = 0;
         if (resid) {
-            for (int32_t j = 0; j < nchunk; ++j) Z += mass[j];
-            if (Z < kDegenerateZ) resid = false;       // draw from p_n instead
+            find_chunk(mass, nchunk, static_cast<double>(task.u), &Z, &chunk, &base);
+            if (Z < kDegenerateZ) resid = false;   // draw from p_n instead
         }
-        if (!resid) {
-            Z = 0.0;
-            for (int32_t j = 0; j < nchunk; ++j) { mass[j] = cs[j].sp; Z += mass[j]; }
+        if (!resid) find_chunk(spc, nchunk, static_cast<double>(task.u), &Z, &chunk, &base);
+        if (tid == 0) {
+            sh_base = base;
+            sh_target = static_cast<double>(task.u) * Z;
+            sh_chunk = chunk;
+            sh_resid = resid;
         }
-        const double target = static_cast<double>(task.u) * Z;
-        double base = 0.0, last_base = 0.0;
-        int32_t chunk = -1, last = 0;
-        for (int32_t j = 0; j < nchunk; ++j) {
-            if (mass[j] > 0.0) { last = j; last_base = base; }
-            if (base + mass[j] > target) { chunk = j; break; }
-            base += mass[j];
-        }
-        if (chunk < 0) { chunk = last; base = last_base; }   // rounding: u Z at the very end
-        sh_base = base;
-        sh_target = target;
-        sh_chunk = chunk;
-        sh_resid = resid;
     }
     __syncthreads();
     const bool resid = sh_resid;
@@ -443,7 +563,7 @@ __global__ __launch_bounds__(kThreads) void draw_pick_kernel(Problem p, Plan pla
     int32_t pick = INT32_MAX, last_pos = -1;
     for (int64_t q0 = c0; q0 < c1 && pick == INT32_MAX; q0 += kPiece) {
         const int64_t q1 = min(c1, q0 + kPiece);
-        const int64_t r0 = q0 + static_cast<int64_t>(threadIdx.x) * kRun;
+        const int64_t r0 = q0 + static_cast<int64_t>(tid) * kRun;
         float zt[kRun], zd[kRun];
         const bool vec = r0 + kRun <= q1 &&
                          (reinterpret_cast<uintptr_t>(rows.t + r0) & 15u) == 0 &&
@@ -474,20 +594,19 @@ __global__ __launch_bounds__(kThreads) void draw_pick_kernel(Problem p, Plan pla
             if (m[i] > 0.0) lp = static_cast<int32_t>(r0 + i);
         }
         double total;
-        double run = base + block_scan_excl(local, &total, lds);
+        double run = base + pick_scan_excl(local, &total, scan_lds);
         int32_t mine = INT32_MAX;
 #pragma unroll
         for (int i = 0; i < kRun; ++i) {
             run += m[i];
             if (mine == INT32_MAX && run > target) mine = static_cast<int32_t>(r0 + i);
         }
-        pick = block_min_max(mine, true, ldsi);
-        last_pos = max(last_pos, block_min_max(lp, false, ldsi));
+        pick = pick_min_max(mine, true, ldsi);
+        last_pos = max(last_pos, pick_min_max(lp, false, ldsi));
         base += total;
     }
-    (void)lane;
     // If rounding left no crossing inside the chunk: its last token with mass.
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
         if (pick == INT32_MAX) pick = last_pos >= 0 ? last_pos : static_cast<int32_t>(c0);
         p.out_tokens[task.out_slot] = pick;
     }
@@ -506,9 +625,9 @@ hipError_t launch_draw_sums(const Problem& p, const Plan& plan, hipStream_t s) {
 
 hipError_t launch_draw_pick(const Problem& p, const Plan& plan, hipStream_t s) {
     if (p.dtype == SV_BF16)
-        draw_pick_kernel<SV_BF16><<<dim3(static_cast<uint32_t>(p.B)), dim3(kThreads), 0, s>>>(p, plan);
+        draw_pick_kernel<SV_BF16><<<dim3(static_cast<uint32_t>(p.B)), dim3(kPickThreads), 0, s>>>(p, plan);
     else
-        draw_pick_kernel<SV_F32><<<dim3(static_cast<uint32_t>(p.B)), dim3(kThreads), 0, s>>>(p, plan);
+        draw_pick_kernel<SV_F32><<<dim3(static_cast<uint32_t>(p.B)), dim3(kPickThreads), 0, s>>>(p, plan);
     return hipGetLastError();
 }
 
