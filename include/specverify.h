@@ -125,16 +125,23 @@ const char *spec_verify_status_string(sv_status_t status);
  * that uses it is still running. */
 void spec_verify_release(void);
 
-/* Kernel timing for benchmarks.  spec_verify_timing(1) turns the probe on
- * (and clears what it recorded); while it is on, every call records a
- * hipEvent pair around each kernel it enqueues, on the call's `stream`, for
- * the last 256 calls.  spec_verify_kernel_times() waits for the most recent
- * recorded call and writes, for up to max_kernels kernels, the mean elapsed
- * milliseconds per call over the recorded calls (ms[i] belongs to
- * spec_verify_kernel_name(i)); it returns the number of kernels, or -1 if no
- * call was recorded or a HIP call failed.  The probe uses one device: turn it
- * off and on again after switching devices. */
-sv_status_t spec_verify_timing(int32_t enable);
+/* Kernel timing for benchmarks.  spec_verify_timing(kernels, every) turns
+ * the probe on for the kernels whose bits are set in `kernels` (bit i
+ * selects spec_verify_kernel_name(i); 0 turns it off; SV_TIME_ALL selects
+ * every kernel) and clears what it recorded.  While it is on, one call in
+ * `every` (>= 1; the first, then every every-th) records a hipEvent pair
+ * around each selected kernel, on the call's `stream`; the last 256
+ * recorded calls are kept.  Each pair costs a few microseconds of stream
+ * time, which sampling spreads over `every` calls.
+ * spec_verify_kernel_times() waits for the most recent recorded call and
+ * writes, for up to max_kernels kernels, the mean elapsed milliseconds per
+ * call over the recorded calls (ms[i] belongs to spec_verify_kernel_name(i),
+ * NaN for kernels not selected); it returns the number of kernels, or -1 if
+ * the probe is off, no call was recorded or a HIP call failed.
+ * spec_verify_timing returns SV_ERR_SHAPE for every < 1.  The probe uses
+ * one device: turn it off and on again after switching devices. */
+#define SV_TIME_ALL 0xF
+sv_status_t spec_verify_timing(int32_t kernels, int32_t every);
 int32_t spec_verify_kernel_times(float *ms, int32_t max_kernels);
 const char *spec_verify_kernel_name(int32_t i);
 

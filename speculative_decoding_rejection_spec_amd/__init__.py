@@ -10,7 +10,7 @@ from __future__ import annotations
 
 import ctypes
 
-from ._lib import LIB_PATH, SV_BF16, SV_F32, SV_K_MAX, SpecVerifyError, check, lib
+from ._lib import LIB_PATH, SV_BF16, SV_F32, SV_K_MAX, SV_TIME_ALL, SpecVerifyError, check, lib
 
 __all__ = [
     "spec_verify", "spec_verify_probs", "spec_verify_workspace_size", "spec_verify_release",
@@ -143,8 +143,27 @@ def set_geometry(seg_elems: int = 0, chunk_elems: int = 0) -> None:
     check(lib().spec_verify_set_geometry(seg_elems, chunk_elems), "spec_verify_set_geometry")
 
 
-def timing(enable: bool) -> None:
-    check(lib().spec_verify_timing(int(bool(enable))), "spec_verify_timing")
+def timing(enable=True, every: int = 1) -> None:
+    """Turns the kernel timing probe on for every kernel (True), for the named
+    kernels (an iterable of names from kernel_times()), or off (False);
+    one call in `every` is recorded."""
+    if enable is True:
+        mask = SV_TIME_ALL
+    elif not enable:
+        mask = 0
+    else:
+        names = list(enable)
+        mask = 0
+        for i in range(16):
+            nm = lib().spec_verify_kernel_name(i)
+            if nm is None:
+                break
+            if nm.decode() in names:
+                mask |= 1 << i
+                names.remove(nm.decode())
+        if names:
+            raise ValueError(f"unknown kernels {names}")
+    check(lib().spec_verify_timing(mask, int(every)), "spec_verify_timing")
 
 
 def kernel_times() -> dict:
@@ -154,4 +173,5 @@ def kernel_times() -> dict:
     n = lib().spec_verify_kernel_times(buf, 16)
     if n < 0:
         raise RuntimeError("no timed spec_verify call to report")
-    return {lib().spec_verify_kernel_name(i).decode(): float(buf[i]) for i in range(n)}
+    return {lib().spec_verify_kernel_name(i).decode(): float(buf[i]) for i in range(n)
+            if buf[i] == buf[i]}

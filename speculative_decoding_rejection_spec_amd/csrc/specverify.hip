@@ -32,7 +32,9 @@ size_t g_ws_bytes[kMaxDevices] = {};
 
 // Timing probe state: a ring of event pairs for the last kTimedCalls calls.
 constexpr int kTimedCalls = 256;
-bool g_timing = false;
+uint32_t g_timing = 0;                // bit i: time kernel i
+int32_t g_timing_every = 1;           // record one call in this many
+int64_t g_timing_seen = 0;            // calls made since the probe was enabled
 int64_t g_timed_calls = 0;            // calls recorded since the probe was enabled
 int g_timing_device = -1;
 hipEvent_t g_ev[kTimedCalls][2 * kNumKernels] = {};
@@ -150,7 +152,7 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     plan.xlogit = reinterpret_cast<float*>(ws + g.off_xlogit);
 
     hipEvent_t* ev = nullptr;
-    if (g_timing) {
+    if (g_timing && (g_timing_seen++ % g_timing_every) == 0) {
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess) return SV_ERR_HIP;
         if (g_timing_device != dev) {
@@ -171,9 +173,10 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     const Launcher launchers[kNumKernels] = {launch_row_stats, launch_accept, launch_draw_sums,
                                              launch_draw_pick};
     for (int i = 0; i < kNumKernels; ++i) {
-        if (ev && hipEventRecord(ev[2 * i], stream) != hipSuccess) return SV_ERR_HIP;
+        const bool timed = ev && ((g_timing >> i) & 1u);
+        if (timed && hipEventRecord(ev[2 * i], stream) != hipSuccess) return SV_ERR_HIP;
         if (launchers[i](p, plan, stream) != hipSuccess) return SV_ERR_HIP;
-        if (ev && hipEventRecord(ev[2 * i + 1], stream) != hipSuccess) return SV_ERR_HIP;
+        if (timed && hipEventRecord(ev[2 * i + 1], stream) != hipSuccess) return SV_ERR_HIP;
     }
     if (ev) ++g_timed_calls;
     return SV_OK;
@@ -268,21 +271,31 @@ void spec_verify_release(void) {
     if (have_cur) (void)hipSetDevice(cur);
 }
 
-sv_status_t spec_verify_timing(int32_t enable) {
+sv_status_t spec_verify_timing(int32_t kernels, int32_t every) {
     std::lock_guard<std::mutex> lock(g_mutex);
-    g_timing = enable != 0;
+    if (every < 1) return SV_ERR_SHAPE;
+    g_timing = static_cast<uint32_t>(kernels) & ((1u << kNumKernels) - 1u);
+    g_timing_every = every;
+    g_timing_seen = 0;
     g_timed_calls = 0;
     return SV_OK;
 }
 
 int32_t spec_verify_kernel_times(float* ms, int32_t max_kernels) {
     std::lock_guard<std::mutex> lock(g_mutex);
-    if (g_timed_calls == 0 || !ms) return -1;
+    if (g_timed_calls == 0 || !ms || !g_timing) return -1;
     const int64_t ncalls = g_timed_calls < kTimedCalls ? g_timed_calls : kTimedCalls;
     const int64_t last = (g_timed_calls - 1) % kTimedCalls;
-    if (hipEventSynchronize(g_ev[last][2 * kNumKernels - 1]) != hipSuccess) return -1;
+    int last_kernel = 0;
+    for (int i = 0; i < kNumKernels; ++i)
+        if ((g_timing >> i) & 1u) last_kernel = i;
+    if (hipEventSynchronize(g_ev[last][2 * last_kernel + 1]) != hipSuccess) return -1;
     const int n = max_kernels < kNumKernels ? max_kernels : kNumKernels;
     for (int i = 0; i < n; ++i) {
+        if (!((g_timing >> i) & 1u)) {
+            ms[i] = __builtin_nanf("");
+            continue;
+        }
         double sum = 0.0;
         for (int64_t c = 0; c < ncalls; ++c) {
             float t = 0.f;

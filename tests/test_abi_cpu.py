@@ -127,3 +127,12 @@ def test_geometry_knob(lib):
 def test_kernel_times_without_timed_call(lib):
     buf = (ctypes.c_float * 8)()
     assert lib.spec_verify_kernel_times(buf, 8) == -1
+
+
+def test_timing_probe_arguments(lib):
+    assert lib.spec_verify_timing(1, 0) == SHAPE
+    assert lib.spec_verify_timing(0xF, 4) == OK
+    buf = (ctypes.c_float * 8)()
+    assert lib.spec_verify_kernel_times(buf, 8) == -1      # nothing recorded yet
+    assert lib.spec_verify_timing(0, 1) == OK
+    assert lib.spec_verify_kernel_times(buf, 8) == -1
