@@ -11,8 +11,10 @@ its rows in the 256 MB last-level cache.
 
 One step = one spec_verify call (row pass, accept scan, fp64 draw) over the
 whole batch.  Output: one JSON line with sequences/s, the achieved HBM
-bandwidth on algorithmic bytes, the roofline of the dominant kernel (the row
-pass) and the fp64 CPU oracle timed on this host as a baseline.
+bandwidth on algorithmic bytes, the roofline of the dominant kernel and the
+fp64 CPU oracle timed on this host as a baseline.  The dominant kernel is the
+row pass in the default staged form, the persistent kernel (the whole step)
+in the fused form (--mode fused).
 
 Algorithmic bytes per step: every needed logit row read once (target rows of
 all sequences, draft rows of sampling sequences) plus one extra read of each
@@ -32,29 +34,33 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 EVENT_EVERY = 8
 METRIC = "sequences verified/s and achieved HBM GB/s (% of peak), B=256 k=8 V=152064 bf16"
-COUNTERS = os.path.join(ROOT, "profiles", "row_stats_c4_counters.txt")
-K1_SOURCES = ["row_stats.hip", "sv_internal.h"]
+# Counter summaries per roofline kernel, and the sources each kernel is built from.
+COUNTERS = {"row_stats": os.path.join(ROOT, "profiles", "row_stats_c4_counters.txt"),
+            "fused": os.path.join(ROOT, "profiles", "fused_c4_counters.txt")}
+KERNEL_SOURCES = {"row_stats": ["row_stats.hip", "row_pass.h", "sv_internal.h"],
+                  "fused": ["fused.hip", "row_pass.h", "accept_scan.h", "draw_pass.h", "sv_internal.h"]}
 
 
-def k1_source_hash() -> str:
+def source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in K1_SOURCES:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "speculative_decoding_rejection_spec_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def committed_traffic():
-    """HBM bytes per row-pass launch from the committed rocprofv3 counter
+def committed_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary, or None when missing or taken on different kernel sources."""
-    if not os.path.exists(COUNTERS):
+    path = COUNTERS.get(kernel)
+    if not path or not os.path.exists(path):
         return None
     kv = {}
-    for line in open(COUNTERS):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("k1_source_sha256") != k1_source_hash():
+    if kv.get("source_sha256") != source_hash(kernel):
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
@@ -76,6 +82,9 @@ def main():
                     help="also run a plain 1 GiB device copy (counter calibration runs)")
     ap.add_argument("--seg", type=int, default=0, help="row-pass segment elements (0 = default)")
     ap.add_argument("--chunk", type=int, default=0, help="draw chunk elements (0 = default)")
+    ap.add_argument("--mode", choices=["auto", "staged", "fused"], default="auto",
+                    help="launch form (auto = staged)")
+    ap.add_argument("--lag", type=int, default=0, help="fused form: draw lag in sequences (0 = auto)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -97,6 +106,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sv.set_geometry(args.seg, args.chunk)
+    sv.set_mode({"auto": sv.SV_MODE_AUTO, "staged": sv.SV_MODE_STAGED, "fused": sv.SV_MODE_FUSED}[args.mode],
+                args.lag)
 
     t_gen = time.perf_counter()
     w = wl.make_workload(args.workload)
@@ -135,17 +146,24 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    # Which form ran: the probe reports NaN for kernels a call did not launch.
+    sv.timing(True)
+    step(0)
+    torch.cuda.synchronize()
+    form = "fused" if "fused" in sv.kernel_times() else "staged"
+    sv.timing(False)
+    roof_kernel = "fused" if form == "fused" else "row_stats"
 
-    # Timed region: HIP events around the row pass only (the roofline kernel),
-    # on one step in EVENT_EVERY so their cost stays out of the step time.
-    sv.timing(["row_stats"] if not args.no_kernel_events else False, every=EVENT_EVERY)
+    # Timed region: HIP events around the roofline kernel only, on one step
+    # in EVENT_EVERY so their cost stays out of the step time.
+    sv.timing([roof_kernel] if not args.no_kernel_events else False, every=EVENT_EVERY)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    k1_live = sv.kernel_times()["row_stats"] if not args.no_kernel_events else None
+    k1_live = sv.kernel_times()[roof_kernel] if not args.no_kernel_events else None
     sv.timing(False)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     # Per-kernel breakdown: a further untimed pass with events around every kernel.
@@ -172,12 +190,14 @@ def main():
 
     roofline = None
     if k1_live is not None:
-        k1_ms = k1_live
-        achieved = k1_bytes / (k1_ms / 1e3) / 1e9
-        roofline = {"bound": "hbm", "kernel": "row_stats", "achieved": round(achieved, 1),
+        # The row pass reads every needed row once; the fused kernel also
+        # reads the draw rows.
+        kbytes = total_bytes if roof_kernel == "fused" else k1_bytes
+        achieved = kbytes / (k1_live / 1e3) / 1e9
+        roofline = {"bound": "hbm", "kernel": roof_kernel, "achieved": round(achieved, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                    "traffic": committed_traffic(), "algorithmic_bytes": k1_bytes,
-                    "mean_ms": round(k1_ms, 5)}
+                    "traffic": committed_traffic(roof_kernel), "algorithmic_bytes": kbytes,
+                    "mean_ms": round(k1_live, 5)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -201,7 +221,7 @@ def main():
                    f"V={w.V} {w.dtype} logits", "B": w.B, "V": w.V, "k_max": int(w.k.max()),
                    "total_draft": w.total, "logit_dtype": w.dtype,
                    "temperatures": sorted(set(float(t) for t in w.temperature)),
-                   "input_copies": len(copies)},
+                   "input_copies": len(copies), "form": form},
         "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
         "algorithmic_bytes": total_bytes, "mean_accepted": round(float(n.mean()), 4),
         "draw_rows": draw_rows,

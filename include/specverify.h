@@ -93,7 +93,9 @@ size_t spec_verify_workspace_size(int32_t B, int64_t total_draft, int64_t V, sv_
  * logit row once (row maximum, sum of exp((z - max)/T), or the argmax for
  * greedy rows); one wavefront per sequence then runs the accept tests and
  * finds the first rejection; a last fp64 pass over the one rejected or bonus
- * row pair draws the emitted token by inverse CDF. */
+ * row pair draws the emitted token by inverse CDF.  The steps run as four
+ * kernels by default, or as one persistent kernel (spec_verify_set_mode);
+ * the results do not depend on the form. */
 sv_status_t spec_verify(const void *target_logits, const void *draft_logits,
                         const int32_t *draft_tokens, const int32_t *offsets,
                         int32_t k_uniform, int64_t total_draft, int32_t B, int64_t V,
@@ -135,12 +137,14 @@ void spec_verify_release(void);
  * time, which sampling spreads over `every` calls.
  * spec_verify_kernel_times() waits for the most recent recorded call and
  * writes, for up to max_kernels kernels, the mean elapsed milliseconds per
- * call over the recorded calls (ms[i] belongs to spec_verify_kernel_name(i),
- * NaN for kernels not selected); it returns the number of kernels, or -1 if
- * the probe is off, no call was recorded or a HIP call failed.
+ * call over the recorded calls that launched the kernel (ms[i] belongs to
+ * spec_verify_kernel_name(i); NaN for kernels not selected or not launched:
+ * the staged form launches row_stats, accept, draw_sums and draw_pick, the
+ * fused form fused_reset and fused); it returns the number of kernels, or
+ * -1 if the probe is off, no call was recorded or a HIP call failed.
  * spec_verify_timing returns SV_ERR_SHAPE for every < 1.  The probe uses
  * one device: turn it off and on again after switching devices. */
-#define SV_TIME_ALL 0xF
+#define SV_TIME_ALL 0x3F
 sv_status_t spec_verify_timing(int32_t kernels, int32_t every);
 int32_t spec_verify_kernel_times(float *ms, int32_t max_kernels);
 const char *spec_verify_kernel_name(int32_t i);
@@ -150,6 +154,19 @@ const char *spec_verify_kernel_name(int32_t i);
  * depends on them, so query spec_verify_workspace_size() after a change.
  * Returns SV_ERR_SHAPE for negative values. */
 sv_status_t spec_verify_set_geometry(int64_t seg_elems, int64_t chunk_elems);
+
+/* Form of the launch.  SV_MODE_STAGED: four kernels (row pass, accept scan,
+ * draw chunk sums, pick), each step published by a kernel boundary.
+ * SV_MODE_FUSED: one persistent kernel (after a small kernel that clears its
+ * counters) whose workgroups take row segments and draw chunks from a
+ * device-side queue; sequence b's draw chunks are queued fused_lag
+ * sequences after its rows (0 = chosen from the number of resident
+ * workgroups).  It needs B <= 2048 and at most 256 draw chunks per row
+ * (spec_verify returns SV_ERR_SHAPE otherwise); on MI355X it measures
+ * slower than the staged form.  SV_MODE_AUTO (the default): staged.  Both
+ * forms give identical results.  Returns SV_ERR_SHAPE for an unknown mode or fused_lag < 0. */
+enum { SV_MODE_AUTO = 0, SV_MODE_STAGED = 1, SV_MODE_FUSED = 2 };
+sv_status_t spec_verify_set_mode(int32_t mode, int32_t fused_lag);
 
 #ifdef __cplusplus
 }

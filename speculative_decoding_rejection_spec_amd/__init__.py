@@ -10,12 +10,13 @@ from __future__ import annotations
 
 import ctypes
 
-from ._lib import LIB_PATH, SV_BF16, SV_F32, SV_K_MAX, SV_TIME_ALL, SpecVerifyError, check, lib
+from ._lib import (LIB_PATH, SV_BF16, SV_F32, SV_K_MAX, SV_MODE_AUTO, SV_MODE_FUSED, SV_MODE_STAGED,
+                   SV_TIME_ALL, SpecVerifyError, check, lib)
 
 __all__ = [
     "spec_verify", "spec_verify_probs", "spec_verify_workspace_size", "spec_verify_release",
-    "timing", "kernel_times", "set_geometry", "SpecVerifyError", "SV_F32", "SV_BF16",
-    "SV_K_MAX", "LIB_PATH", "lib",
+    "timing", "kernel_times", "set_geometry", "set_mode", "SpecVerifyError", "SV_F32", "SV_BF16",
+    "SV_K_MAX", "SV_MODE_AUTO", "SV_MODE_STAGED", "SV_MODE_FUSED", "LIB_PATH", "lib",
 ]
 
 
@@ -141,6 +142,11 @@ def spec_verify_release() -> None:
 
 def set_geometry(seg_elems: int = 0, chunk_elems: int = 0) -> None:
     check(lib().spec_verify_set_geometry(seg_elems, chunk_elems), "spec_verify_set_geometry")
+
+
+def set_mode(mode: int = SV_MODE_AUTO, fused_lag: int = 0) -> None:
+    """Staged (four kernels), fused (one persistent kernel) or auto."""
+    check(lib().spec_verify_set_mode(int(mode), int(fused_lag)), "spec_verify_set_mode")
 
 
 def timing(enable=True, every: int = 1) -> None:

@@ -1,158 +1,14 @@
-// accept.hip -- the accept scan: one wave64 per sequence.
-//
-// Lane i (i <= k_b) owns position i of its sequence.  It merges the segment
-// statistics of target row i (and draft row i) into the row maximum and the
-// normaliser, gathers the logits of the drafted token x_i, and runs the
-// accept test u_i < alpha_i = min(1, p_i(x_i) / q_i(x_i)) (page "投机解码",
-// section 投机解码的三步流程 step 3; page "大模型推理无损加速:投机采样...",
-// section 二.1).  All k tests run at once; a ballot of the rejections and a
-// find-first-set give n, the first rejection (or k) -- the same n as a scan
-// that stops at the first rejection.  Greedy sequences (T = 0) accept while
-// x_i equals the target argmax and emit the argmax of row n (section 动手实践,
-// greedy branch).
-//
-// The row pass keeps S_R = sum_v 2^(z_v c - R) with c = log2(e)/T rounded to
-// fp32 and an integer reference R, and captures z_x, the logit of the
-// drafted token of each row; p(x) = 2^(z_x c - R) / S_R exactly as the row
-// pass summed it (a softmax at the temperature log2(e)/c, within
-// 6e-8 relative of T); it is formed in fp64.  Worst-case relative error of
-// S_R: about 2e-6 (fp32 partial sums of <= 40 terms, v_exp_f32, the rounded
-// exponent argument); alpha is therefore within 5e-6 of its exact value,
-// inside the 1e-5 band where |u - alpha| counts as a tie.
-//
-// Sampling sequences leave the emitted token to the draw kernel and record a
-// DrawTask: a residual draw at row n if n < k, a bonus draw at row k
-// otherwise.
-#include "sv_internal.h"
+// accept.hip -- the staged accept scan: one wave64 per sequence (the scan
+// itself is in accept_scan.h).
+#include "accept_scan.h"
 
 namespace sv {
 namespace {
 
-struct RowStat {
-    float m;       // row maximum
-    int32_t arg;   // greedy: lowest token id holding m
-    float R;       // sampling: reference exponent
-    double S;      // sampling: sum of 2^(z c - R)
-};
-
-// Merges the nseg segment statistics of one row (exact power-of-two
-// rescaling for sampling rows; lowest id among tied maxima for greedy rows).
-__device__ __forceinline__ RowStat merge_row(const SegStat* seg, int32_t nseg, bool greedy) {
-    RowStat r{-INFINITY, INT32_MAX, -INFINITY, 0.0};
-    for (int32_t s = 0; s < nseg; ++s) {
-        r.m = fmaxf(r.m, seg[s].m);
-        r.R = fmaxf(r.R, seg[s].R);
-    }
-    for (int32_t s = 0; s < nseg; ++s) {
-        if (greedy) {
-            if (seg[s].m == r.m && seg[s].arg < r.arg) r.arg = seg[s].arg;
-        } else if (seg[s].R != -INFINITY) {
-            r.S += ldexp(seg[s].s, static_cast<int>(fmaxf(seg[s].R - r.R, -2048.f)));
-        }
-    }
-    return r;
-}
-
-// log2 of the normaliser sum_v 2^((z_v - m) c) of a merged sampling row.
-__device__ __forceinline__ double log2_norm(const RowStat& r, float c) {
-    return log2(r.S) + (static_cast<double>(r.R) - static_cast<double>(r.m) * c);
-}
-
 __global__ __launch_bounds__(kThreads) void accept_kernel(Problem p, Plan plan) {
-    const int lane = threadIdx.x & 63;
     const int32_t b = blockIdx.x * kWaves + (threadIdx.x >> 6);
     if (b >= p.B) return;                          // whole wave leaves together
-
-    int64_t o, o1;
-    if (p.offsets) { o = p.offsets[b]; o1 = p.offsets[b + 1]; }
-    else { o = static_cast<int64_t>(b) * p.k_uniform; o1 = o + p.k_uniform; }
-    const int64_t k64 = o1 - o;
-    const float Tf = p.temperature[b];
-    const int64_t ntarget = p.total + p.B;
-    bool ok = o >= 0 && k64 >= 0 && k64 <= kKMax && o1 <= p.total && temperature_ok(Tf);
-    const int k = ok ? static_cast<int>(k64) : 0;
-    const bool greedy = (Tf == 0.f);
-    const float c = greedy ? 0.f : row_scale(Tf);
-    const int64_t trow = o + b + lane;             // this lane's target row
-    const int64_t drow = o + lane;                 // this lane's draft row
-
-    int32_t x = -1;
-    if (ok && lane < k) {
-        x = p.tokens[drow];
-        if (x < 0 || x >= p.V) ok = false;
-    }
-    RowStat rt{0.f, 0, 0.f, 1.0}, rd{0.f, 0, 0.f, 1.0};
-    if (ok && lane <= k) {
-        rt = merge_row(plan.seg + trow * plan.nseg, plan.nseg, greedy);
-        if (!(fabsf(rt.m) <= 3.4e38f)) ok = false;
-        if (!greedy && lane < k) {
-            rd = merge_row(plan.seg + (ntarget + drow) * plan.nseg, plan.nseg, false);
-            if (!(fabsf(rd.m) <= 3.4e38f)) ok = false;
-        }
-    }
-    ok = !__any(!ok);                              // one verdict for the whole sequence
-
-    if (!ok) {
-        // Data error: the sequence's own token slots (when its offsets describe
-        // a range inside the batch) are all -1.
-        if (o >= 0 && o1 >= o && o1 <= p.total)
-            for (int64_t i = lane; i <= k64; i += 64) p.out_tokens[o + b + i] = -1;
-        if (lane == 0) {
-            p.out_n[b] = -1;
-            plan.task[b].kind = kNone;
-        }
-        return;
-    }
-
-    bool reject = false;
-    double px = NAN, qx = NAN;
-    if (lane < k) {
-        if (greedy) {
-            reject = (x != rt.arg);
-        } else {
-            const double zt = plan.xlogit[trow];             // captured by the row pass
-            const double zd = plan.xlogit[ntarget + drow];
-            px = exp2(zt * c - rt.R) / rt.S;
-            qx = exp2(zd * c - rd.R) / rd.S;
-            const double alpha = fmin(1.0, px / qx);
-            reject = !(static_cast<double>(p.uniforms[trow]) < alpha);
-        }
-    }
-    const uint64_t mask = __ballot(reject);
-    const int n = mask ? __ffsll(static_cast<unsigned long long>(mask)) - 1 : k;
-
-    if (lane <= k) {
-        int32_t out = -1;
-        if (lane < n) out = x;
-        else if (lane == n && greedy) out = rt.arg;
-        p.out_tokens[trow] = out;
-    }
-    if (lane == n) {
-        p.out_n[b] = n;
-        DrawTask t;
-        t.kind = greedy ? kNone : (n < k ? kResidual : kBonus);
-        t.out_slot = static_cast<int32_t>(trow);
-        t.trow = trow;
-        t.drow = drow;
-        t.m_t = rt.m;
-        t.m_d = n < k ? rd.m : 0.f;
-        t.T = Tf;
-        t.u = p.uniforms[o + b + k];
-        t.theta = (!greedy && n < k) ? log2_norm(rt, c) - log2_norm(rd, c) : 0.0;
-        plan.task[b] = t;
-    }
-    if (p.out_p && lane < k) {
-        p.out_p[drow] = static_cast<float>(px);
-        p.out_q[drow] = static_cast<float>(qx);
-    }
-    if (p.out_row_max && lane <= k) {
-        p.out_row_max[trow] = rt.m;
-        p.out_row_sum[trow] = greedy ? NAN : static_cast<float>(exp2(log2_norm(rt, c)));
-        if (lane < k) {
-            p.out_row_max[ntarget + drow] = greedy ? NAN : rd.m;
-            p.out_row_sum[ntarget + drow] = greedy ? NAN : static_cast<float>(exp2(log2_norm(rd, c)));
-        }
-    }
+    accept_sequence<false>(p, plan, b);
 }
 
 }  // namespace

@@ -1,0 +1,643 @@
+// draw_pass.h -- the emitted token of every sampling sequence, in fp64;
+// shared by the staged draw kernels and the fused kernel.
+//
+// After the first rejection at position n the token is drawn from
+// r = max(0, p_n - q_n) / Z, Z = sum_v max(0, p_n(v) - q_n(v)) (page "投机解码",
+// section 无损保证：数学推导, reject-path equation; page
+// "大模型推理无损加速:投机采样...", section 二.2); if all k drafts were accepted
+// it is drawn from p_k (the bonus token, section 投机解码的三步流程).  The draw
+// is an inverse CDF over ascending token ids with the supplied uniform u:
+// t* = min{t : C_t > u Z}, C_t = sum_{v <= t} r_v.
+//
+// Tail tokens of a 10^5-entry distribution carry masses near 1e-10 and sit
+// closer together than fp32 rounding, so the CDF is built in fp64 from
+// w = 2^((z - m) log2(e) / T) of the exact logits and row maxima.
+//
+// draw_chunk (one workgroup per (sequence, chunk)) reads the draw rows once:
+//   * bonus draw: per chunk, W_c = sum of w_t;
+//   * residual draw: per chunk, S_p,c = sum w_t and S_q,c = sum w_d (the fp64
+//     normalisers), and A_c, B_c = sums of w_t, w_d over the tokens with
+//     p_v > q_v.  p_v > q_v iff d_v = log2(w_t / w_d) exceeds
+//     theta = log2(S_p / S_q); the accept scan supplies theta from the row
+//     pass's normalisers (within about 1e-5 in log2 units), so tokens with
+//     |d_v - theta| > kBand are classified exactly, and the few inside the
+//     band are listed per wave (up to kWaveCap each) with their (w_t, w_d),
+//     to get their exact mass once S_p and S_q are known.  The residual mass
+//     of chunk c is R_c = A_c / S_p - B_c / S_q + sum over its band tokens of
+//     max(0, w_t/S_p - w_d/S_q); a chunk whose lists overflowed is rescanned.
+// pick_sequence (one workgroup per sequence) forms Z = sum_c R_c, finds the
+// chunk whose cumulative mass crosses u Z with a wave-wide scan, and scans
+// that one chunk with a workgroup-wide fp64 prefix sum over masses held in
+// registers.
+//
+// 2^y in fp64 follows Tang's table-driven method (ACM TOMS 15(2), 1989) in
+// base 2 with a 256-entry table: y = k + j/256 + r with |r| <= 1/512,
+// 2^y = 2^k 2^(j/256) e^(r ln2), e^(r ln2) - 1 by its degree-4 Taylor
+// polynomial (truncation < 4e-17 relative).  The kernels carry Y = 256 y.
+// The scaling by 2^k is folded into the table: each entry keeps the high
+// word of 2^(j/256) minus j << 12, so adding round(Y) << 12 to it adds k to
+// the exponent field in one integer add.
+#pragma once
+
+#include "accept_scan.h"
+
+namespace sv {
+namespace drawpass {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr double kLog2e = 0x1.71547652b82fep+0;
+constexpr double kDegenerateZ = 1e-9;            // residual mass treated as empty
+constexpr double kBand = 3e-5;                   // classification band (log2 units)
+constexpr double kMinY = -1021.0 * 256.0;        // weights stay normal doubles (>= 2^-1021)
+constexpr int kRun = 8;                          // tokens per lane in the pick's scan
+constexpr int kSlots = kWaves * kWaveCap;        // band entries per chunk (32)
+constexpr int kBufferDword3 = 0x00020000;        // raw buffer descriptor word 3 (gfx9 family)
+
+// 2^(j/256), j = 0..255, correctly rounded.
+static __constant__ double kExp2Frac[256] = {
+    0x1.0000000000000p+0, 0x1.00b1afa5abcbfp+0, 0x1.0163da9fb3335p+0, 0x1.02168143b0281p+0,
+    0x1.02c9a3e778061p+0, 0x1.037d42e11bbccp+0, 0x1.04315e86e7f85p+0, 0x1.04e5f72f654b1p+0,
+    0x1.059b0d3158574p+0, 0x1.0650a0e3c1f89p+0, 0x1.0706b29ddf6dep+0, 0x1.07bd42b72a836p+0,
+    0x1.0874518759bc8p+0, 0x1.092bdf66607e0p+0, 0x1.09e3ecac6f383p+0, 0x1.0a9c79b1f3919p+0,
+    0x1.0b5586cf9890fp+0, 0x1.0c0f145e46c85p+0, 0x1.0cc922b7247f7p+0, 0x1.0d83b23395decp+0,
+    0x1.0e3ec32d3d1a2p+0, 0x1.0efa55fdfa9c5p+0, 0x1.0fb66affed31bp+0, 0x1.1073028d7233ep+0,
+    0x1.11301d0125b51p+0, 0x1.11edbab5e2ab6p+0, 0x1.12abdc06c31ccp+0, 0x1.136a814f204abp+0,
+    0x1.1429aaea92de0p+0, 0x1.14e95934f312ep+0, 0x1.15a98c8a58e51p+0, 0x1.166a45471c3c2p+0,
+    0x1.172b83c7d517bp+0, 0x1.17ed48695bbc0p+0, 0x1.18af9388c8deap+0, 0x1.1972658375d2fp+0,
+    0x1.1a35beb6fcb75p+0, 0x1.1af99f8138a1cp+0, 0x1.1bbe084045cd4p+0, 0x1.1c82f95281c6bp+0,
+    0x1.1d4873168b9aap+0, 0x1.1e0e75eb44027p+0, 0x1.1ed5022fcd91dp+0, 0x1.1f9c18438ce4dp+0,
+    0x1.2063b88628cd6p+0, 0x1.212be3578a819p+0, 0x1.21f49917ddc96p+0, 0x1.22bdda27912d1p+0,
+    0x1.2387a6e756238p+0, 0x1.2451ffb82140ap+0, 0x1.251ce4fb2a63fp+0, 0x1.25e85711ece75p+0,
+    0x1.26b4565e27cddp+0, 0x1.2780e341ddf29p+0, 0x1.284dfe1f56381p+0, 0x1.291ba7591bb70p+0,
+    0x1.29e9df51fdee1p+0, 0x1.2ab8a66d10f13p+0, 0x1.2b87fd0dad990p+0, 0x1.2c57e39771b2fp+0,
+    0x1.2d285a6e4030bp+0, 0x1.2df961f641589p+0, 0x1.2ecafa93e2f56p+0, 0x1.2f9d24abd886bp+0,
+    0x1.306fe0a31b715p+0, 0x1.31432edeeb2fdp+0, 0x1.32170fc4cd831p+0, 0x1.32eb83ba8ea32p+0,
+    0x1.33c08b26416ffp+0, 0x1.3496266e3fa2dp+0, 0x1.356c55f929ff1p+0, 0x1.36431a2de883bp+0,
+    0x1.371a7373aa9cbp+0, 0x1.37f26231e754ap+0, 0x1.38cae6d05d866p+0, 0x1.39a401b7140efp+0,
+    0x1.3a7db34e59ff7p+0, 0x1.3b57fbfec6cf4p+0, 0x1.3c32dc313a8e5p+0, 0x1.3d0e544ede173p+0,
+    0x1.3dea64c123422p+0, 0x1.3ec70df1c5175p+0, 0x1.3fa4504ac801cp+0, 0x1.40822c367a024p+0,
+    0x1.4160a21f72e2ap+0, 0x1.423fb2709468ap+0, 0x1.431f5d950a897p+0, 0x1.43ffa3f84b9d4p+0,
+    0x1.44e086061892dp+0, 0x1.45c2042a7d232p+0, 0x1.46a41ed1d0057p+0, 0x1.4786d668b3237p+0,
+    0x1.486a2b5c13cd0p+0, 0x1.494e1e192aed2p+0, 0x1.4a32af0d7d3dep+0, 0x1.4b17dea6db7d7p+0,
+    0x1.4bfdad5362a27p+0, 0x1.4ce41b817c114p+0, 0x1.4dcb299fddd0dp+0, 0x1.4eb2d81d8abffp+0,
+    0x1.4f9b2769d2ca7p+0, 0x1.508417f4531eep+0, 0x1.516daa2cf6642p+0, 0x1.5257de83f4eefp+0,
+    0x1.5342b569d4f82p+0, 0x1.542e2f4f6ad27p+0, 0x1.551a4ca5d920fp+0, 0x1.56070dde910d2p+0,
+    0x1.56f4736b527dap+0, 0x1.57e27dbe2c4cfp+0, 0x1.58d12d497c7fdp+0, 0x1.59c0827ff07ccp+0,
+    0x1.5ab07dd485429p+0, 0x1.5ba11fba87a03p+0, 0x1.5c9268a5946b7p+0, 0x1.5d84590998b93p+0,
+    0x1.5e76f15ad2148p+0, 0x1.5f6a320dceb71p+0, 0x1.605e1b976dc09p+0, 0x1.6152ae6cdf6f4p+0,
+    0x1.6247eb03a5585p+0, 0x1.633dd1d1929fdp+0, 0x1.6434634ccc320p+0, 0x1.652b9febc8fb7p+0,
+    0x1.6623882552225p+0, 0x1.671c1c70833f6p+0, 0x1.68155d44ca973p+0, 0x1.690f4b19e9538p+0,
+    0x1.6a09e667f3bcdp+0, 0x1.6b052fa75173ep+0, 0x1.6c012750bdabfp+0, 0x1.6cfdcddd47645p+0,
+    0x1.6dfb23c651a2fp+0, 0x1.6ef9298593ae5p+0, 0x1.6ff7df9519484p+0, 0x1.70f7466f42e87p+0,
+    0x1.71f75e8ec5f74p+0, 0x1.72f8286ead08ap+0, 0x1.73f9a48a58174p+0, 0x1.74fbd35d7cbfdp+0,
+    0x1.75feb564267c9p+0, 0x1.77024b1ab6e09p+0, 0x1.780694fde5d3fp+0, 0x1.790b938ac1cf6p+0,
+    0x1.7a11473eb0187p+0, 0x1.7b17b0976cfdbp+0, 0x1.7c1ed0130c132p+0, 0x1.7d26a62ff86f0p+0,
+    0x1.7e2f336cf4e62p+0, 0x1.7f3878491c491p+0, 0x1.80427543e1a12p+0, 0x1.814d2add106d9p+0,
+    0x1.82589994cce13p+0, 0x1.8364c1eb941f7p+0, 0x1.8471a4623c7adp+0, 0x1.857f4179f5b21p+0,
+    0x1.868d99b4492edp+0, 0x1.879cad931a436p+0, 0x1.88ac7d98a6699p+0, 0x1.89bd0a478580fp+0,
+    0x1.8ace5422aa0dbp+0, 0x1.8be05bad61778p+0, 0x1.8cf3216b5448cp+0, 0x1.8e06a5e0866d9p+0,
+    0x1.8f1ae99157736p+0, 0x1.902fed0282c8ap+0, 0x1.9145b0b91ffc6p+0, 0x1.925c353aa2fe2p+0,
+    0x1.93737b0cdc5e5p+0, 0x1.948b82b5f98e5p+0, 0x1.95a44cbc8520fp+0, 0x1.96bdd9a7670b3p+0,
+    0x1.97d829fde4e50p+0, 0x1.98f33e47a22a2p+0, 0x1.9a0f170ca07bap+0, 0x1.9b2bb4d53fe0dp+0,
+    0x1.9c49182a3f090p+0, 0x1.9d674194bb8d5p+0, 0x1.9e86319e32323p+0, 0x1.9fa5e8d07f29ep+0,
+    0x1.a0c667b5de565p+0, 0x1.a1e7aed8eb8bbp+0, 0x1.a309bec4a2d33p+0, 0x1.a42c980460ad8p+0,
+    0x1.a5503b23e255dp+0, 0x1.a674a8af46052p+0, 0x1.a799e1330b358p+0, 0x1.a8bfe53c12e59p+0,
+    0x1.a9e6b5579fdbfp+0, 0x1.ab0e521356ebap+0, 0x1.ac36bbfd3f37ap+0, 0x1.ad5ff3a3c2774p+0,
+    0x1.ae89f995ad3adp+0, 0x1.afb4ce622f2ffp+0, 0x1.b0e07298db666p+0, 0x1.b20ce6c9a8952p+0,
+    0x1.b33a2b84f15fbp+0, 0x1.b468415b749b1p+0, 0x1.b59728de5593ap+0, 0x1.b6c6e29f1c52ap+0,
+    0x1.b7f76f2fb5e47p+0, 0x1.b928cf22749e4p+0, 0x1.ba5b030a1064ap+0, 0x1.bb8e0b79a6f1fp+0,
+    0x1.bcc1e904bc1d2p+0, 0x1.bdf69c3f3a207p+0, 0x1.bf2c25bd71e09p+0, 0x1.c06286141b33dp+0,
+    0x1.c199bdd85529cp+0, 0x1.c2d1cd9fa652cp+0, 0x1.c40ab5fffd07ap+0, 0x1.c544778fafb22p+0,
+    0x1.c67f12e57d14bp+0, 0x1.c7ba88988c933p+0, 0x1.c8f6d9406e7b5p+0, 0x1.ca3405751c4dbp+0,
+    0x1.cb720dcef9069p+0, 0x1.ccb0f2e6d1675p+0, 0x1.cdf0b555dc3fap+0, 0x1.cf3155b5bab74p+0,
+    0x1.d072d4a07897cp+0, 0x1.d1b532b08c968p+0, 0x1.d2f87080d89f2p+0, 0x1.d43c8eacaa1d6p+0,
+    0x1.d5818dcfba487p+0, 0x1.d6c76e862e6d3p+0, 0x1.d80e316c98398p+0, 0x1.d955d71ff6075p+0,
+    0x1.da9e603db3285p+0, 0x1.dbe7cd63a8315p+0, 0x1.dd321f301b460p+0, 0x1.de7d5641c0658p+0,
+    0x1.dfc97337b9b5fp+0, 0x1.e11676b197d17p+0, 0x1.e264614f5a129p+0, 0x1.e3b333b16ee12p+0,
+    0x1.e502ee78b3ff6p+0, 0x1.e653924676d76p+0, 0x1.e7a51fbc74c83p+0, 0x1.e8f7977cdb740p+0,
+    0x1.ea4afa2a490dap+0, 0x1.eb9f4867cca6ep+0, 0x1.ecf482d8e67f1p+0, 0x1.ee4aaa2188510p+0,
+    0x1.efa1bee615a27p+0, 0x1.f0f9c1cb6412ap+0, 0x1.f252b376bba97p+0, 0x1.f3ac948dd7274p+0,
+    0x1.f50765b6e4540p+0, 0x1.f6632798844f8p+0, 0x1.f7bfdad9cbe14p+0, 0x1.f91d802243c89p+0,
+    0x1.fa7c1819e90d8p+0, 0x1.fbdba3692d514p+0, 0x1.fd3c22b8f71f1p+0, 0x1.fe9d96b2a23d9p+0,
+};
+
+// One table entry: the low word of 2^(j/256) and its high word minus j << 12.
+struct alignas(8) TabEntry {
+    uint32_t lo, hi;
+};
+
+// Fills the LDS table; call with every thread of the workgroup, then barrier.
+__device__ __forceinline__ void load_table(TabEntry* tbl, int nthreads) {
+    for (int i = threadIdx.x; i < 256; i += nthreads) {
+        const uint64_t bits = static_cast<uint64_t>(__double_as_longlong(kExp2Frac[i]));
+        tbl[i].lo = static_cast<uint32_t>(bits);
+        tbl[i].hi = static_cast<uint32_t>(bits >> 32) - (static_cast<uint32_t>(i) << 12);
+    }
+}
+
+// 2^(Y/256) in fp64 for Y <= 0 (Y is clamped at kMinY).  Y = n + r with
+// n = round(Y) (the 1.5 * 2^52 shifter: after the add the low 32 bits of the
+// double hold n in two's complement) and |r| <= 1/2, so
+// 2^(Y/256) = 2^(n>>8) 2^((n&255)/256) e^x with x = r ln2/256, |x| <= ln2/512;
+// e^x - 1 by its degree-4 Taylor polynomial (truncation < 4e-17 relative).
+__device__ __forceinline__ double exp2_256(double Y, const TabEntry* tbl) {
+    constexpr double kShift = 0x1.8p52;
+    Y = fmax(Y, kMinY);
+    const double kd = Y + kShift;
+    const uint32_t n = static_cast<uint32_t>(__double_as_longlong(kd));
+    const double r = Y - (kd - kShift);            // exact
+    double q = fma(r, 0x1.3b2ab6fba4e77p-39, 0x1.c6b08d704a0c0p-29);
+    q = fma(q, r, 0x1.ebfbdff82c58fp-19);
+    q = fma(q, r, 0x1.62e42fefa39efp-9);
+    const TabEntry e = tbl[n & 255u];
+    const double t = __hiloint2double(static_cast<int>(e.hi + (n << 12)), static_cast<int>(e.lo));
+    return fma(t, q * r, t);
+}
+
+template <int DT> struct Vec;
+template <> struct Vec<SV_BF16> {
+    using E = uint16_t;
+    static constexpr int N = 8;
+    __device__ static __forceinline__ void unpack(const u32x4 v, float* x) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[2 * j] = __uint_as_float(v[j] << 16);
+            x[2 * j + 1] = __uint_as_float(v[j] & 0xffff0000u);
+        }
+    }
+};
+template <> struct Vec<SV_F32> {
+    using E = float;
+    static constexpr int N = 4;
+    __device__ static __forceinline__ void unpack(const u32x4 v, float* x) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = __uint_as_float(v[j]);
+    }
+};
+
+// The one or two rows a draw reads, and Y = 256 (z - m) log2(e) / T as one fma.
+template <int DT>
+struct Rows {
+    using E = typename Vec<DT>::E;
+    const E* t;          // target row at position n
+    const E* d;          // draft row at position n (residual only)
+    double c;            // 256 log2(e) / T
+    double ot, od;       // -m_t * c, -m_d * c
+    const TabEntry* tbl;
+
+    __device__ __forceinline__ double Yt(float z) const { return fma(static_cast<double>(z), c, ot); }
+    __device__ __forceinline__ double Yd(float z) const { return fma(static_cast<double>(z), c, od); }
+    __device__ __forceinline__ double wt(float z) const { return exp2_256(Yt(z), tbl); }
+    __device__ __forceinline__ double wd(float z) const { return exp2_256(Yd(z), tbl); }
+    __device__ __forceinline__ float zt(int64_t v) const { return load_logit(t, DT, v); }
+    __device__ __forceinline__ float zd(int64_t v) const { return load_logit(d, DT, v); }
+};
+
+template <int DT>
+__device__ __forceinline__ Rows<DT> rows_of(const Problem& p, const DrawTask& task, const TabEntry* tbl) {
+    using E = typename Vec<DT>::E;
+    const double c = 256.0 * kLog2e / static_cast<double>(task.T);
+    return Rows<DT>{static_cast<const E*>(p.target) + task.trow * p.V,
+                    static_cast<const E*>(p.draft) + task.drow * p.V,
+                    c, -static_cast<double>(task.m_t) * c, -static_cast<double>(task.m_d) * c, tbl};
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int32_t byte_off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+// Calls f(z_t, z_d) for this thread's tokens of [v0, v1), in the order
+// lane-strided 16-byte vectors, then single tokens for a ragged tail.  When
+// both rows start 16-byte aligned the vectors come from raw buffer loads
+// against descriptors that span exactly the chunk's vectors, one iteration
+// ahead of use (a load past the end returns zeros and touches no memory);
+// otherwise every token is loaded on its own.
+template <int DT, bool kResid, class F>
+__device__ __forceinline__ void for_chunk(const Rows<DT>& rows, int64_t v0, int64_t v1, F&& f) {
+    using E = typename Vec<DT>::E;
+    constexpr int N = Vec<DT>::N;
+    const bool vec = (reinterpret_cast<uintptr_t>(rows.t + v0) & 15u) == 0 &&
+                     (!kResid || (reinterpret_cast<uintptr_t>(rows.d + v0) & 15u) == 0);
+    int64_t vs = v0;
+    if (vec) {
+        const int32_t nvec = static_cast<int32_t>((v1 - v0) / N);
+        const __amdgpu_buffer_rsrc_t rt =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<E*>(rows.t + v0), 0, nvec * 16, kBufferDword3);
+        const __amdgpu_buffer_rsrc_t rd = kResid
+            ? __builtin_amdgcn_make_buffer_rsrc(const_cast<E*>(rows.d + v0), 0, nvec * 16, kBufferDword3)
+            : rt;
+        int32_t j = threadIdx.x;
+        u32x4 a = buffer_load16(rt, j * 16);
+        u32x4 bb = kResid ? buffer_load16(rd, j * 16) : a;
+        for (; j < nvec; j += kThreads) {
+            const u32x4 an = buffer_load16(rt, (j + kThreads) * 16);
+            const u32x4 bn = kResid ? buffer_load16(rd, (j + kThreads) * 16) : an;
+            float xt[N], xd[N];
+            Vec<DT>::unpack(a, xt);
+            if (kResid) Vec<DT>::unpack(bb, xd);
+#pragma unroll
+            for (int e = 0; e < N; ++e) {
+                f(xt[e], kResid ? xd[e] : 0.f);
+                // interleave at most two tokens' fp64 work: bounds the register count
+                if (e % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+            }
+            a = an;
+            bb = bn;
+        }
+        vs = v0 + static_cast<int64_t>(nvec) * N;
+    }
+    for (int64_t v = vs + threadIdx.x; v < v1; v += kThreads)
+        f(rows.zt(v), kResid ? rows.zd(v) : 0.f);
+}
+
+// Sums of four doubles over a 256-thread workgroup (valid in every thread).
+__device__ __forceinline__ void block_sum4(double& a, double& b, double& c, double& d,
+                                           double (*lds)[4]) {
+    for (int off = 32; off > 0; off >>= 1) {
+        a += __shfl_xor(a, off, 64);
+        b += __shfl_xor(b, off, 64);
+        c += __shfl_xor(c, off, 64);
+        d += __shfl_xor(d, off, 64);
+    }
+    const int wave = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) { lds[wave][0] = a; lds[wave][1] = b; lds[wave][2] = c; lds[wave][3] = d; }
+    __syncthreads();
+    a = b = c = d = 0.0;
+    for (int w = 0; w < kWaves; ++w) { a += lds[w][0]; b += lds[w][1]; c += lds[w][2]; d += lds[w][3]; }
+}
+
+
+}  // namespace drawpass
+
+// Workgroup scratch of one draw chunk (256 threads).
+struct DrawLds {
+    double red4[kWaves][4];
+    double wlist[kWaves][kWaveCap][2];
+    int32_t wcount[kWaves];
+};
+
+// The exp2 table in LDS: every thread of the workgroup calls this, then the
+// workgroup synchronises before first use.
+__device__ __forceinline__ void load_exp2_table(drawpass::TabEntry* tbl, int nthreads) {
+    drawpass::load_table(tbl, nthreads);
+}
+
+// Chunk c of the draw of sequence b (256 threads): accumulates the chunk's
+// fp64 sums and band lists (see the file comment).  `task` is the
+// sequence's DrawTask (kind != kNone).  kCo: the results go to the pick in
+// another workgroup of the same launch.
+template <int DT, bool kCo>
+__device__ __forceinline__ void draw_chunk(const Problem& p, const Plan& plan, const DrawTask& task,
+                                           int32_t b, int32_t c, const drawpass::TabEntry* tbl,
+                                           DrawLds& lds) {
+    using namespace drawpass;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t w = static_cast<int64_t>(b) * plan.nchunk + c;
+    const bool resid_task = (task.kind == kResidual);
+    const Rows<DT> rows = rows_of<DT>(p, task, tbl);
+
+    const int64_t v0 = static_cast<int64_t>(c) * plan.chunk_len;
+    const int64_t v1 = min(p.V, v0 + plan.chunk_len);
+    double sp = 0.0, sq = 0.0, a = 0.0, bq = 0.0;
+    int32_t nband = 0;                         // uniform over the lanes still active
+    if (resid_task) {
+        const double th_hi = 256.0 * (task.theta + kBand), th_lo = 256.0 * (task.theta - kBand);
+        for_chunk<DT, true>(rows, v0, v1, [&](float zt, float zd) {
+            const double yt = rows.Yt(zt), yd = rows.Yd(zd);
+            const double wt = exp2_256(yt, tbl), wd = exp2_256(yd, tbl);
+            sp += wt;
+            sq += wd;
+            const double dv = yt - yd;
+            const bool hi = dv > th_hi;
+            const double h = hi ? 1.0 : 0.0;
+            a = fma(h, wt, a);
+            bq = fma(h, wd, bq);
+            // band = lanes with th_lo <= d_v <= th_hi (wave-uniform mask)
+            const uint64_t band = __ballot(dv >= th_lo) & ~__ballot(hi);
+            if (band) {
+                const int pos = nband + __popcll(band & ((1ull << lane) - 1ull));
+                if (((band >> lane) & 1ull) && pos < kWaveCap) {
+                    lds.wlist[wave][pos][0] = wt;
+                    lds.wlist[wave][pos][1] = wd;
+                }
+                nband += __popcll(band);
+            }
+        });
+    } else {
+        for_chunk<DT, false>(rows, v0, v1, [&](float zt, float) { sp += rows.wt(zt); });
+    }
+    if (lane == 0) lds.wcount[wave] = nband;  // lane 0 was active whenever any lane was
+    block_sum4(sp, sq, a, bq, lds.red4);
+    if (threadIdx.x == 0) {
+        ChunkSums* cs = plan.csum + w;
+        st_co<kCo>(&cs->sp, sp);
+        st_co<kCo>(&cs->sq, sq);
+        st_co<kCo>(&cs->a, a);
+        st_co<kCo>(&cs->b, bq);
+    }
+    if (resid_task) {
+        if (threadIdx.x < kWaves) st_co<kCo>(&plan.band_n[w * kWaves + threadIdx.x], lds.wcount[threadIdx.x]);
+        if (threadIdx.x < kSlots) {
+            const int wv = threadIdx.x / kWaveCap, e = threadIdx.x % kWaveCap;
+            if (e < lds.wcount[wv]) {
+                double* dst = plan.band_w + (w * kSlots + threadIdx.x) * 2;
+                st_co<kCo>(&dst[0], lds.wlist[wv][e][0]);
+                st_co<kCo>(&dst[1], lds.wlist[wv][e][1]);
+            }
+        }
+    }
+}
+
+// ---- the pick: one NT-thread workgroup per sequence -----------------------
+
+constexpr int kMaxPickChunks = 1024;          // chunk masses held in LDS by the pick
+
+template <int NT, int MAXC = kMaxPickChunks>
+struct PickLds {
+    static constexpr int kW = NT / 64;
+    double red2[kW][2];
+    double scan[kW];
+    int32_t ldsi[kW];
+    double mass[MAXC];
+    double spc[MAXC];
+    double base, target;
+    int32_t chunk, resid, rescan;
+};
+
+namespace drawpass {
+
+// Sum of two doubles over an NT-thread workgroup (valid in every thread).
+template <int NT>
+__device__ __forceinline__ void pick_sum2(double& a, double& b, double (*lds)[2]) {
+    for (int off = 32; off > 0; off >>= 1) {
+        a += __shfl_xor(a, off, 64);
+        b += __shfl_xor(b, off, 64);
+    }
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) { lds[threadIdx.x >> 6][0] = a; lds[threadIdx.x >> 6][1] = b; }
+    __syncthreads();
+    a = b = 0.0;
+    for (int w = 0; w < NT / 64; ++w) { a += lds[w][0]; b += lds[w][1]; }
+}
+
+// Exclusive prefix sum over an NT-thread workgroup in thread order; *total = sum.
+template <int NT>
+__device__ __forceinline__ double pick_scan_excl(double x, double* total, double* lds) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    double inc = x;
+    for (int off = 1; off < 64; off <<= 1) {
+        const double y = __shfl_up(inc, off, 64);
+        if (lane >= off) inc += y;
+    }
+    double excl = __shfl_up(inc, 1, 64);
+    if (lane == 0) excl = 0.0;
+    __syncthreads();
+    if (lane == 63) lds[wave] = inc;
+    __syncthreads();
+    double before = 0.0, all = 0.0;
+    for (int w = 0; w < NT / 64; ++w) {
+        if (w < wave) before += lds[w];
+        all += lds[w];
+    }
+    *total = all;
+    return before + excl;
+}
+
+template <int NT>
+__device__ __forceinline__ int32_t pick_min_max(int32_t x, bool want_min, int32_t* lds) {
+    for (int off = 32; off > 0; off >>= 1) {
+        const int32_t y = __shfl_xor(x, off, 64);
+        x = want_min ? min(x, y) : max(x, y);
+    }
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = x;
+    __syncthreads();
+    int32_t r = lds[0];
+    for (int w = 1; w < NT / 64; ++w) r = want_min ? min(r, lds[w]) : max(r, lds[w]);
+    return r;
+}
+
+// Wave-wide search over chunk masses m[0..n) (run by one whole wave): the
+// first chunk whose cumulative mass exceeds target, with the mass before it;
+// when rounding leaves target at or past the total, the last chunk with
+// positive mass.  Returns the total in *Z.
+__device__ __forceinline__ void find_chunk(const double* m, int32_t n, double u, double* Z,
+                                           int32_t* chunk, double* base) {
+    const int lane = threadIdx.x & 63;
+    const int32_t per = (n + 63) / 64;        // chunks per lane, in order
+    const int32_t j0 = min(n, lane * per), j1 = min(n, j0 + per);
+    double mine = 0.0;
+    for (int32_t j = j0; j < j1; ++j) mine += m[j];
+    double inc = mine;
+    for (int off = 1; off < 64; off <<= 1) {
+        const double y = __shfl_up(inc, off, 64);
+        if (lane >= off) inc += y;
+    }
+    const double total = __shfl(inc, 63, 64);
+    const double target = u * total;
+    const double excl = inc - mine;
+    // the lane whose range holds the crossing: excl <= target < inc
+    int32_t found = -1;
+    double fb = 0.0;
+    if (excl <= target && target < inc) {
+        double run = excl;
+        for (int32_t j = j0; j < j1; ++j) {
+            if (run + m[j] > target) { found = j; fb = run; break; }
+            run += m[j];
+        }
+    }
+    // fallback: the last chunk with positive mass
+    int32_t lastj = -1;
+    double lastb = 0.0;
+    {
+        double run = excl;
+        for (int32_t j = j0; j < j1; ++j) {
+            if (m[j] > 0.0) { lastj = j; lastb = run; }
+            run += m[j];
+        }
+    }
+    const uint64_t fm = __ballot(found >= 0);
+    if (fm) {
+        const int src = __ffsll(static_cast<unsigned long long>(fm)) - 1;
+        *chunk = __shfl(found, src, 64);
+        *base = __shfl(fb, src, 64);
+    } else {
+        const uint64_t lm = __ballot(lastj >= 0);
+        const int src = lm ? 63 - __clzll(static_cast<long long>(lm)) : 0;
+        *chunk = lm ? __shfl(lastj, src, 64) : 0;
+        *base = lm ? __shfl(lastb, src, 64) : 0.0;
+    }
+    *Z = total;
+}
+
+}  // namespace drawpass
+
+// The pick of sequence b (NT threads, NT a multiple of 256): from the chunk
+// sums of every chunk of its draw, the emitted token.  `task` is the
+// sequence's DrawTask (kind != kNone); plan.nchunk <= MAXC.  kCo: the chunk
+// sums come from other workgroups of the same launch.
+template <int DT, int NT, bool kCo, int MAXC = kMaxPickChunks>
+__device__ __forceinline__ void pick_sequence(const Problem& p, const Plan& plan, const DrawTask& task,
+                                              int32_t b, const drawpass::TabEntry* tbl,
+                                              PickLds<NT, MAXC>& L) {
+    using namespace drawpass;
+    static_assert(NT % 256 == 0 && NT <= 1024, "pick workgroup size");
+    constexpr int N = Vec<DT>::N;
+    constexpr int64_t kPiece = NT * kRun;    // tokens per scan step
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const bool resid_task = (task.kind == kResidual);
+    const Rows<DT> rows = rows_of<DT>(p, task, tbl);
+    const int32_t nchunk = plan.nchunk;
+    const int64_t cb = static_cast<int64_t>(b) * nchunk;
+    const ChunkSums* cs = plan.csum + cb;
+    if (tid == 0) L.rescan = 0;
+
+    // All loads that need only the sequence are issued together: the chunk
+    // sums (one chunk per thread) and the band entries of the first NT/32
+    // chunks (one slot per thread; an entry past its wave's count is stale
+    // and ignored).
+    double Sp = 0.0, Sq = 0.0, ca = 0.0, cbq = 0.0;
+    for (int32_t j = tid; j < nchunk; j += NT) {
+        const double xsp = ld_co<kCo>(&cs[j].sp);
+        Sp += xsp;
+        Sq += ld_co<kCo>(&cs[j].sq);
+        L.spc[j] = xsp;
+        if (j == tid) { ca = ld_co<kCo>(&cs[j].a); cbq = ld_co<kCo>(&cs[j].b); }
+    }
+    const int32_t pj = tid / kSlots, ps = tid % kSlots;
+    int32_t pcnt = 0;
+    double pwt = 0.0, pwd = 0.0;
+    if (resid_task && pj < nchunk) {
+        pcnt = ld_co<kCo>(&plan.band_n[(cb + pj) * kWaves + ps / kWaveCap]);
+        const double* pw = plan.band_w + ((cb + pj) * kSlots + ps) * 2;
+        pwt = ld_co<kCo>(&pw[0]);
+        pwd = ld_co<kCo>(&pw[1]);
+    }
+    pick_sum2<NT>(Sp, Sq, L.red2);              // (its barriers also publish spc)
+    const double iSp = 1.0 / Sp, iSq = resid_task ? 1.0 / Sq : 0.0;
+
+    if (resid_task) {
+        for (int32_t j = tid; j < nchunk; j += NT) {
+            const double a = (j == tid) ? ca : ld_co<kCo>(&cs[j].a);
+            const double bq = (j == tid) ? cbq : ld_co<kCo>(&cs[j].b);
+            L.mass[j] = a * iSp - bq * iSq;
+        }
+        __syncthreads();
+        // Band terms: 32 lanes per chunk (a half wave), one listed token
+        // each; a fixed shuffle tree sums them (deterministic order).
+        for (int32_t j0 = 0; j0 < nchunk; j0 += NT / kSlots) {
+            const int32_t j = j0 + pj;
+            int32_t cnt = pcnt;
+            double wt = pwt, wd = pwd;
+            if (j0 > 0) {
+                cnt = 0;
+                if (j < nchunk) {
+                    cnt = ld_co<kCo>(&plan.band_n[(cb + j) * kWaves + ps / kWaveCap]);
+                    const double* pw = plan.band_w + ((cb + j) * kSlots + ps) * 2;
+                    wt = ld_co<kCo>(&pw[0]);
+                    wd = ld_co<kCo>(&pw[1]);
+                }
+            }
+            double term = (j < nchunk && ps % kWaveCap < cnt) ? fmax(0.0, wt * iSp - wd * iSq) : 0.0;
+            for (int off = kSlots / 2; off > 0; off >>= 1) term += __shfl_xor(term, off, 64);
+            const bool over = j < nchunk && cnt > kWaveCap;
+            const bool any_over = (__ballot(over) >> ((tid & 63) & ~(kSlots - 1))) & 0xffffffffull;
+            if (j < nchunk && ps == 0) L.mass[j] = any_over ? NAN : L.mass[j] + term;
+            if (over) L.rescan = 1;            // benign race: every writer stores 1
+        }
+        __syncthreads();
+        if (L.rescan) {
+            // chunks whose band lists overflowed: exact rescan (rare)
+            for (int32_t j = 0; j < nchunk; ++j) {
+                if (!isnan(L.mass[j])) continue;
+                const int64_t u0 = static_cast<int64_t>(j) * plan.chunk_len;
+                const int64_t u1 = min(p.V, u0 + plan.chunk_len);
+                double m = 0.0, unused = 0.0;
+                for (int64_t v = u0 + tid; v < u1; v += NT)
+                    m += fmax(0.0, rows.wt(rows.zt(v)) * iSp - rows.wd(rows.zd(v)) * iSq);
+                pick_sum2<NT>(m, unused, L.red2);
+                if (tid == 0) L.mass[j] = m;
+                __syncthreads();
+            }
+        }
+    }
+    if (wave == 0) {
+        bool resid = resid_task;
+        double Z = 0.0, base = 0.0;
+        int32_t chunk = 0;
+        if (resid) {
+            find_chunk(L.mass, nchunk, static_cast<double>(task.u), &Z, &chunk, &base);
+            if (Z < kDegenerateZ) resid = false;   // draw from p_n instead
+        }
+        if (!resid) find_chunk(L.spc, nchunk, static_cast<double>(task.u), &Z, &chunk, &base);
+        if (tid == 0) {
+            L.base = base;
+            L.target = static_cast<double>(task.u) * Z;
+            L.chunk = chunk;
+            L.resid = resid;
+        }
+    }
+    __syncthreads();
+    const bool resid = L.resid;
+    const double target = L.target;
+    double base = L.base;
+    const int64_t c0 = static_cast<int64_t>(L.chunk) * plan.chunk_len;
+    const int64_t c1 = min(p.V, c0 + plan.chunk_len);
+
+    // Scan the chunk in pieces of kPiece tokens: lane tid owns kRun consecutive
+    // tokens of the piece, loaded together, masses kept in registers.
+    int32_t pick = INT32_MAX, last_pos = -1;
+    for (int64_t q0 = c0; q0 < c1 && pick == INT32_MAX; q0 += kPiece) {
+        const int64_t q1 = min(c1, q0 + kPiece);
+        const int64_t r0 = q0 + static_cast<int64_t>(tid) * kRun;
+        float zt[kRun], zd[kRun];
+        const bool vec = r0 + kRun <= q1 &&
+                         (reinterpret_cast<uintptr_t>(rows.t + r0) & 15u) == 0 &&
+                         (!resid || (reinterpret_cast<uintptr_t>(rows.d + r0) & 15u) == 0);
+        if (vec) {
+#pragma unroll
+            for (int i = 0; i < kRun / N; ++i) {
+                Vec<DT>::unpack(reinterpret_cast<const u32x4*>(rows.t + r0)[i], zt + i * N);
+                if (resid) Vec<DT>::unpack(reinterpret_cast<const u32x4*>(rows.d + r0)[i], zd + i * N);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kRun; ++i) {
+                const bool in = r0 + i < q1;
+                zt[i] = in ? rows.zt(r0 + i) : 0.f;
+                zd[i] = (in && resid) ? rows.zd(r0 + i) : 0.f;
+            }
+        }
+        double m[kRun];
+        double local = 0.0;
+        int32_t lp = -1;
+#pragma unroll
+        for (int i = 0; i < kRun; ++i) {
+            const bool in = r0 + i < q1;
+            m[i] = !in ? 0.0
+                       : (resid ? fmax(0.0, rows.wt(zt[i]) * iSp - rows.wd(zd[i]) * iSq) : rows.wt(zt[i]));
+            local += m[i];
+            if (m[i] > 0.0) lp = static_cast<int32_t>(r0 + i);
+        }
+        double total;
+        double run = base + pick_scan_excl<NT>(local, &total, L.scan);
+        int32_t mine = INT32_MAX;
+#pragma unroll
+        for (int i = 0; i < kRun; ++i) {
+            run += m[i];
+            if (mine == INT32_MAX && run > target) mine = static_cast<int32_t>(r0 + i);
+        }
+        pick = pick_min_max<NT>(mine, true, L.ldsi);
+        last_pos = max(last_pos, pick_min_max<NT>(lp, false, L.ldsi));
+        base += total;
+    }
+    // If rounding left no crossing inside the chunk: its last token with mass.
+    if (tid == 0) {
+        if (pick == INT32_MAX) pick = last_pos >= 0 ? last_pos : static_cast<int32_t>(c0);
+        p.out_tokens[task.out_slot] = pick;
+    }
+}
+
+}  // namespace sv

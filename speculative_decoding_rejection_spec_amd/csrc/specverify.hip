@@ -18,13 +18,18 @@ int64_t row_unit(sv_dtype_t dtype) { return dtype == SV_BF16 ? 256 * 8 * 8 : 256
 constexpr int64_t kDefaultChunkElems = 8192;  // draw chunk length before rounding
 constexpr int64_t kMaxChunks = 1024;          // draw chunks per row (the pick keeps them in LDS)
 constexpr int kMaxDevices = 64;
-constexpr int kNumKernels = 4;
+constexpr int kNumKernels = 6;
+enum { kKRowStats, kKAccept, kKDrawSums, kKDrawPick, kKFusedReset, kKFused };
 
-const char* const kKernelNames[kNumKernels] = {"row_stats", "accept", "draw_sums", "draw_pick"};
+const char* const kKernelNames[kNumKernels] = {"row_stats", "accept", "draw_sums", "draw_pick",
+                                               "fused_reset", "fused"};
 
 std::mutex g_mutex;
 int64_t g_seg_elems = kDefaultSegElems;
 int64_t g_chunk_elems = kDefaultChunkElems;
+int32_t g_mode = SV_MODE_AUTO;
+int32_t g_fused_lag = 0;                     // 0: chosen from the resident grid
+constexpr double kLagFactor = 1.5;           // resident grids of items between rows and draw
 
 // Library-owned workspace, one grow-only buffer per device.
 void* g_ws[kMaxDevices] = {};
@@ -38,6 +43,7 @@ int64_t g_timing_seen = 0;            // calls made since the probe was enabled
 int64_t g_timed_calls = 0;            // calls recorded since the probe was enabled
 int g_timing_device = -1;
 hipEvent_t g_ev[kTimedCalls][2 * kNumKernels] = {};
+uint32_t g_ev_mask[kTimedCalls] = {};        // kernels recorded in each call
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -45,7 +51,7 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 struct Geometry {
     int32_t nseg, nchunk;
     int64_t seg_len, chunk_len;
-    size_t off_seg, off_task, off_csum, off_band_n, off_band_w, off_xlogit, bytes;
+    size_t off_seg, off_task, off_csum, off_band_n, off_band_w, off_xlogit, off_ctr, bytes;
 };
 
 // Splits a row of V logits into n <= max_pieces pieces of about `target`
@@ -78,6 +84,8 @@ bool make_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dtype, int64_
     off = align256(off + sizeof(double) * 2 * kWaves * kWaveCap * static_cast<size_t>(B) * g.nchunk);
     g.off_xlogit = off;
     off = align256(off + sizeof(float) * static_cast<size_t>(rows));
+    g.off_ctr = off;
+    off = align256(off + sizeof(uint32_t) * static_cast<size_t>(fused_counter_words(B)));
     g.bytes = off;
     return true;
 }
@@ -150,6 +158,29 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     plan.band_n = reinterpret_cast<int32_t*>(ws + g.off_band_n);
     plan.band_w = reinterpret_cast<double*>(ws + g.off_band_w);
     plan.xlogit = reinterpret_cast<float*>(ws + g.off_xlogit);
+    plan.ctr = reinterpret_cast<uint32_t*>(ws + g.off_ctr);
+
+    // The fused form needs the schedule prefix and the pick's chunk masses
+    // in LDS, and an item count below 2^31.
+    const int64_t max_items = (2 * p.total + p.B) * static_cast<int64_t>(g.nseg) +
+                              static_cast<int64_t>(p.B) * g.nchunk;
+    const bool fused_fits = p.B <= kFusedMaxB && g.nchunk <= kFusedMaxChunks && max_items < (1ll << 31);
+    // The fused form measured slower than the staged one on MI355X (see
+    // fused.hip), so it runs only when asked for.
+    const bool fused = g_mode == SV_MODE_FUSED;
+    if (fused && !fused_fits) return SV_ERR_SHAPE;
+    Fused f{};
+    if (fused) {
+        if (fused_grid(p.dtype, &f.blocks) != hipSuccess) return SV_ERR_HIP;
+        if (g_fused_lag > 0) {
+            f.lag = g_fused_lag;
+        } else {
+            const double per_step = g.nseg * (2.0 * p.total / p.B + 1.0) + g.nchunk;
+            f.lag = static_cast<int32_t>(kLagFactor * f.blocks / per_step + 1.0);
+        }
+        if (f.lag > p.B) f.lag = p.B;
+        if (f.lag < 1) f.lag = 1;
+    }
 
     hipEvent_t* ev = nullptr;
     if (g_timing && (g_timing_seen++ % g_timing_every) == 0) {
@@ -169,17 +200,30 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
         }
         ev = g_ev[g_timed_calls % kTimedCalls];
     }
-    typedef hipError_t (*Launcher)(const Problem&, const Plan&, hipStream_t);
-    const Launcher launchers[kNumKernels] = {launch_row_stats, launch_accept, launch_draw_sums,
-                                             launch_draw_pick};
-    for (int i = 0; i < kNumKernels; ++i) {
+    uint32_t recorded = 0;
+    auto launch = [&](int i, auto&& fn) -> bool {
         const bool timed = ev && ((g_timing >> i) & 1u);
-        if (timed && hipEventRecord(ev[2 * i], stream) != hipSuccess) return SV_ERR_HIP;
-        if (launchers[i](p, plan, stream) != hipSuccess) return SV_ERR_HIP;
-        if (timed && hipEventRecord(ev[2 * i + 1], stream) != hipSuccess) return SV_ERR_HIP;
+        if (timed && hipEventRecord(ev[2 * i], stream) != hipSuccess) return false;
+        if (fn() != hipSuccess) return false;
+        if (timed && hipEventRecord(ev[2 * i + 1], stream) != hipSuccess) return false;
+        if (timed) recorded |= 1u << i;
+        return true;
+    };
+    bool ok;
+    if (fused) {
+        ok = launch(kKFusedReset, [&] { return launch_fused_reset(p, plan, stream); }) &&
+             launch(kKFused, [&] { return launch_fused(p, plan, f, stream); });
+    } else {
+        ok = launch(kKRowStats, [&] { return launch_row_stats(p, plan, stream); }) &&
+             launch(kKAccept, [&] { return launch_accept(p, plan, stream); }) &&
+             launch(kKDrawSums, [&] { return launch_draw_sums(p, plan, stream); }) &&
+             launch(kKDrawPick, [&] { return launch_draw_pick(p, plan, stream); });
     }
-    if (ev) ++g_timed_calls;
-    return SV_OK;
+    if (ev) {
+        g_ev_mask[g_timed_calls % kTimedCalls] = recorded;
+        ++g_timed_calls;
+    }
+    return ok ? SV_OK : SV_ERR_HIP;
 }
 
 }  // namespace
@@ -286,29 +330,36 @@ int32_t spec_verify_kernel_times(float* ms, int32_t max_kernels) {
     if (g_timed_calls == 0 || !ms || !g_timing) return -1;
     const int64_t ncalls = g_timed_calls < kTimedCalls ? g_timed_calls : kTimedCalls;
     const int64_t last = (g_timed_calls - 1) % kTimedCalls;
-    int last_kernel = 0;
-    for (int i = 0; i < kNumKernels; ++i)
-        if ((g_timing >> i) & 1u) last_kernel = i;
+    const uint32_t last_mask = g_ev_mask[last];
+    if (last_mask == 0) return -1;
+    const int last_kernel = 31 - __builtin_clz(last_mask);
     if (hipEventSynchronize(g_ev[last][2 * last_kernel + 1]) != hipSuccess) return -1;
     const int n = max_kernels < kNumKernels ? max_kernels : kNumKernels;
     for (int i = 0; i < n; ++i) {
-        if (!((g_timing >> i) & 1u)) {
-            ms[i] = __builtin_nanf("");
-            continue;
-        }
         double sum = 0.0;
+        int64_t cnt = 0;
         for (int64_t c = 0; c < ncalls; ++c) {
+            if (!((g_ev_mask[c] >> i) & 1u)) continue;
             float t = 0.f;
             if (hipEventElapsedTime(&t, g_ev[c][2 * i], g_ev[c][2 * i + 1]) != hipSuccess) return -1;
             sum += t;
+            ++cnt;
         }
-        ms[i] = static_cast<float>(sum / ncalls);
+        ms[i] = cnt ? static_cast<float>(sum / cnt) : __builtin_nanf("");
     }
     return kNumKernels;
 }
 
 const char* spec_verify_kernel_name(int32_t i) {
     return (i >= 0 && i < kNumKernels) ? kKernelNames[i] : nullptr;
+}
+
+sv_status_t spec_verify_set_mode(int32_t mode, int32_t fused_lag) {
+    if (mode < SV_MODE_AUTO || mode > SV_MODE_FUSED || fused_lag < 0) return SV_ERR_SHAPE;
+    std::lock_guard<std::mutex> lock(g_mutex);
+    g_mode = mode;
+    g_fused_lag = fused_lag;
+    return SV_OK;
 }
 
 sv_status_t spec_verify_set_geometry(int64_t seg_elems, int64_t chunk_elems) {

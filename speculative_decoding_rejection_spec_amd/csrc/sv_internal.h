@@ -1,15 +1,23 @@
 // sv_internal.h -- declarations shared by the HIP sources of libspecverify.
 //
-// Data flow of one call (every kernel is enqueued on the caller's stream):
-//   1. row pass    (row_stats.hip): one workgroup per (logit row, segment)
-//                  streams the segment once and writes a SegStat;
-//   2. accept scan (accept.hip): one wave64 per sequence merges the segments
-//                  of its rows, runs the k accept tests, finds the first
-//                  rejection, writes the accepted tokens and a DrawTask;
-//   3. draw_sums   (draw.hip): one workgroup per (sequence, chunk) of the one
-//                  rejected or bonus row pair accumulates fp64 chunk sums;
-//   4. draw_pick   (draw.hip): one workgroup per sequence locates the chunk
-//                  that holds u * Z and the token inside it.
+// Data flow of one call, staged form (every kernel is enqueued on the
+// caller's stream; kernel boundaries publish each step's results):
+//   1. row pass    (row_stats.hip, row_pass.h): one workgroup per (logit row,
+//                  segment) streams the segment once and writes a SegStat;
+//   2. accept scan (accept.hip, accept_scan.h): one wave64 per sequence
+//                  merges the segments of its rows, runs the k accept tests,
+//                  finds the first rejection, writes the accepted tokens and
+//                  a DrawTask;
+//   3. draw_sums   (draw.hip, draw_pass.h): one workgroup per (sequence,
+//                  chunk) of the one rejected or bonus row pair accumulates
+//                  fp64 chunk sums;
+//   4. draw_pick   (draw.hip, draw_pass.h): one workgroup per sequence
+//                  locates the chunk that holds u * Z and the token inside it.
+// Fused form (fused.hip): one persistent launch runs the same four steps as
+// work items taken from a device-side queue; the last workgroup to finish a
+// sequence's rows runs its accept scan and the last to finish its chunks
+// runs its pick, so the draws of early sequences overlap the streaming of
+// later ones.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -89,6 +97,22 @@ struct Plan {
     int32_t* band_n;     // [B * nchunk * kWaves]: band tokens seen per wave of a chunk
     double* band_w;      // [B * nchunk * kWaves * kWaveCap * 2]: their (w_t, w_d)
     float* xlogit;       // [2 * total + B]: logit of the drafted token of each row
+    uint32_t* ctr;       // fused form only: kCtrHeader words, then rows_done[B], ready[B], chunks_done[B]
+};
+
+// Layout of Plan::ctr (fused form), zeroed before every launch.  The queue
+// word also carries the abandon bit kQueueAbandoned.
+enum : int32_t { kCtrQueue = 0, kCtrHeader = 4 };
+constexpr uint32_t kQueueAbandoned = 0x80000000u;
+
+// Limits of the fused form (larger calls use the staged form).
+constexpr int kFusedMaxB = 2048;        // sequences (the schedule prefix lives in LDS)
+constexpr int kFusedMaxChunks = 256;    // draw chunks per row (the pick's LDS)
+
+// Launch parameters of the fused form.
+struct Fused {
+    int32_t lag;       // super-steps between a sequence's rows and its draw chunks
+    int32_t blocks;    // resident workgroups
 };
 
 // Host-side launchers (one per kernel).
@@ -96,6 +120,10 @@ hipError_t launch_row_stats(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_accept(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_draw_sums(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_draw_pick(const Problem& p, const Plan& plan, hipStream_t s);
+hipError_t launch_fused_reset(const Problem& p, const Plan& plan, hipStream_t s);
+hipError_t launch_fused(const Problem& p, const Plan& plan, const Fused& f, hipStream_t s);
+hipError_t fused_grid(int32_t dtype, int32_t* blocks);   // resident workgroups on this device
+int64_t fused_counter_words(int32_t B);
 
 // ---- device helpers shared by the kernels ---------------------------------
 
@@ -103,6 +131,36 @@ __device__ __forceinline__ float load_logit(const void* base, int32_t dtype, int
     if (dtype == SV_BF16)
         return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(base)[idx]) << 16);
     return static_cast<const float*>(base)[idx];
+}
+
+// Data handed between workgroups of ONE launch (the fused form).  The L2 of
+// each XCD is not coherent with the others for ordinary accesses, so such
+// data is stored and loaded with agent-scope relaxed atomics (global_store /
+// global_load with sc1: written through to, and read from, the point where
+// all XCDs agree).  kCo = false gives ordinary accesses for the staged form,
+// where kernel boundaries publish everything.
+template <bool kCo, class T>
+__device__ __forceinline__ T ld_co(const T* ptr) {
+    if constexpr (kCo) return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else return *ptr;
+}
+template <bool kCo, class T>
+__device__ __forceinline__ void st_co(T* ptr, T v) {
+    if constexpr (kCo) __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *ptr = v;
+}
+
+// Waits until every global store this thread has issued has completed
+// (s_waitcnt vmcnt(0): on gfx9-family GPUs vmcnt also counts stores, and a
+// write-through store completes once it is visible at agent scope).  The
+// signal fences keep the compiler from moving memory operations across it.
+// Used before a counter increment that hands the stored data to another
+// workgroup; cheaper than an agent-scope release fence, which would also
+// write back the whole L2.
+__device__ __forceinline__ void wait_stores() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt unchanged
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // c = log2(e) / T as the row pass uses it (the accept scan must form the same

@@ -22,8 +22,14 @@ pytestmark = pytest.mark.gpu
 AMBIGUOUS = oracle.FLAG_A | oracle.FLAG_B | oracle.FLAG_D
 
 
-@pytest.fixture(scope="module")
-def sv(cuda):
+MODES = ["staged", "fused"]
+CURRENT = {"mode": None}
+
+
+@pytest.fixture(scope="module", params=MODES)
+def sv(cuda, request):
+    """The library, set to the staged (four kernels) or the fused (one
+    persistent kernel) form; every test below runs in both."""
     import os
 
     import speculative_decoding_rejection_spec_amd as sv
@@ -31,7 +37,11 @@ def sv(cuda):
         import __graft_entry__
         __graft_entry__.build()
     sv.set_geometry(0, 0)
-    return sv
+    sv.set_mode(sv.SV_MODE_FUSED if request.param == "fused" else sv.SV_MODE_STAGED)
+    CURRENT["mode"] = request.param
+    print(f"[mode {request.param}]", flush=True)
+    yield sv
+    sv.set_mode(sv.SV_MODE_AUTO)
 
 
 def to_device(w, dev):
@@ -190,11 +200,15 @@ def test_ragged_vocab(sv, cuda, dtype, V):
 
 def test_tiny_geometry_many_segments(sv, cuda):
     """Force many row segments and draw chunks: exercises the segment merge
-    and the chunk search across hundreds of pieces."""
+    and the chunk search across hundreds of pieces (the fused form holds at
+    most 256 chunks per row)."""
     w = workload("c5", 0, 48)
     ref = oracle.verify(w)
+    geoms = ((64, 8), (1000, 200), (1 << 20, 1 << 20))
+    if CURRENT["mode"] == "fused":
+        geoms = ((64, 600), (1000, 512), (1 << 20, 1 << 20))
     try:
-        for seg, chunk in ((64, 8), (1000, 200), (1 << 20, 1 << 20)):
+        for seg, chunk in geoms:
             sv.set_geometry(seg, chunk)
             compare(w, run_gpu(sv, w, cuda), ref, f"geometry {seg}/{chunk}")
     finally:
@@ -251,3 +265,65 @@ def test_data_errors_are_per_sequence(sv, cuda):
         elif not ref["flags"][b] & AMBIGUOUS:
             assert gpu["n"][b] == ref["n"][b]
             assert np.array_equal(gpu["tokens"][sl], ref["tokens"][sl])
+
+
+def test_fused_lag_extremes(sv, cuda):
+    """The fused schedule with the draw chunks right behind their rows
+    (lag 1: draw items wait for their sequence) and after all rows (lag B)."""
+    if CURRENT["mode"] != "fused":
+        pytest.skip("fused form only")
+    w = workload("c5", 0, 64)
+    ref = oracle.verify(w)
+    try:
+        for lag in (1, 2, 64):
+            sv.set_mode(sv.SV_MODE_FUSED, lag)
+            compare(w, run_gpu(sv, w, cuda), ref, f"lag {lag}")
+    finally:
+        sv.set_mode(sv.SV_MODE_FUSED)
+
+
+def test_batch_limits(sv, cuda):
+    """B = 2048 (the fused form's largest batch, every prefix entry used) and
+    B = 2049 (auto falls back to the staged form; forcing fused is refused)."""
+    g = np.random.default_rng(2048)
+    V = 520
+    for B in (2048, 2049):
+        k = g.integers(0, 5, size=B)
+        off = np.concatenate([[0], np.cumsum(k)])
+        zt = (g.standard_normal((int(off[-1]) + B, V)) * 2).astype(np.float32)
+        t_of_d = np.array([off[b] + b + i for b in range(B) for i in range(k[b])], dtype=np.int64)
+        zd = zt[t_of_d] + g.standard_normal((len(t_of_d), V)).astype(np.float32)
+        temps = np.where(np.arange(B) % 3 == 0, 0.0, 0.8).astype(np.float32)
+        w = wl.assemble(zt, zd, g.integers(0, V, size=len(t_of_d)),
+                        g.random(len(t_of_d) + B, dtype=np.float32), temps, k, dtype="bf16")
+        ref = oracle.verify(w, threads=16)
+        if B > 2048 and CURRENT["mode"] == "fused":
+            with pytest.raises(sv.SpecVerifyError):
+                run_gpu(sv, w, cuda)
+            sv.set_mode(sv.SV_MODE_AUTO)
+            try:
+                compare(w, run_gpu(sv, w, cuda), ref, f"B={B} auto")
+            finally:
+                sv.set_mode(sv.SV_MODE_FUSED)
+        else:
+            compare(w, run_gpu(sv, w, cuda), ref, f"B={B}")
+
+
+def test_fused_matches_staged_bitwise(sv, cuda):
+    """Both forms run the same row pass, accept scan and chunk sums, so the
+    counts and diagnostics are identical on the full C4 batch; the pick scans
+    its chunk in pieces of a different size, which could change a token only
+    within about 1e-15 of a CDF boundary (no C4 sequence is that close)."""
+    if CURRENT["mode"] != "fused":
+        pytest.skip("run once")
+    w = workload("c4")
+    out = {}
+    try:
+        for mode in (sv.SV_MODE_STAGED, sv.SV_MODE_FUSED):
+            sv.set_mode(mode)
+            out[mode] = run_gpu(sv, w, cuda, probs=True)
+    finally:
+        sv.set_mode(sv.SV_MODE_FUSED)
+    a, b = out[sv.SV_MODE_STAGED], out[sv.SV_MODE_FUSED]
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
