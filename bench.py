@@ -16,10 +16,15 @@ fp64 CPU oracle timed on this host as a baseline.  The dominant kernel is the
 row pass in the default staged form, the persistent kernel (the whole step)
 in the fused form (--mode fused).
 
-Algorithmic bytes per step: every needed logit row read once (target rows of
-all sequences, draft rows of sampling sequences) plus one extra read of each
-draw row (2 rows for a residual draw, 1 for a bonus draw, 0 for greedy),
-V * element size per row; the small per-sequence arrays are ignored.
+Algorithmic bytes per step: the logit rows the step reads, once each, plus
+one extra read of each draw row (2 rows for a residual draw, 1 for a bonus
+draw, 0 for greedy), V * element size per row; the small per-sequence arrays
+are ignored.  Rows read: with early exit (the default, --lead 1) the
+leading positions of every sequence and the remaining positions of the
+sequences they leave undecided; in one full pass (--lead 0) or the fused
+form, every target row and the draft rows of sampling sequences.  Both
+figures, and the minimum (the rows up to each sequence's first rejection),
+are in the output line.
 """
 import argparse
 import hashlib
@@ -36,8 +41,10 @@ EVENT_EVERY = 8
 METRIC = "sequences verified/s and achieved HBM GB/s (% of peak), B=256 k=8 V=152064 bf16"
 # Counter summaries per roofline kernel, and the sources each kernel is built from.
 COUNTERS = {"row_stats": os.path.join(ROOT, "profiles", "row_stats_c4_counters.txt"),
+            "row_lead+row_stats": os.path.join(ROOT, "profiles", "row_pass_early_exit_c4_counters.txt"),
             "fused": os.path.join(ROOT, "profiles", "fused_c4_counters.txt")}
 KERNEL_SOURCES = {"row_stats": ["row_stats.hip", "row_pass.h", "sv_internal.h"],
+                  "row_lead+row_stats": ["row_stats.hip", "row_pass.h", "sv_internal.h"],
                   "fused": ["fused.hip", "row_pass.h", "accept_scan.h", "draw_pass.h", "sv_internal.h"]}
 
 
@@ -85,6 +92,8 @@ def main():
     ap.add_argument("--mode", choices=["auto", "staged", "fused"], default="auto",
                     help="launch form (auto = staged)")
     ap.add_argument("--lag", type=int, default=0, help="fused form: draw lag in sequences (0 = auto)")
+    ap.add_argument("--lead", type=int, default=1,
+                    help="early exit: leading positions read by every sequence (0 = one full pass)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -108,6 +117,7 @@ def main():
     sv.set_geometry(args.seg, args.chunk)
     sv.set_mode({"auto": sv.SV_MODE_AUTO, "staged": sv.SV_MODE_STAGED, "fused": sv.SV_MODE_FUSED}[args.mode],
                 args.lag)
+    sv.set_early_exit(args.lead)
 
     t_gen = time.perf_counter()
     w = wl.make_workload(args.workload)
@@ -150,20 +160,28 @@ def main():
     sv.timing(True)
     step(0)
     torch.cuda.synchronize()
-    form = "fused" if "fused" in sv.kernel_times() else "staged"
+    launched = sv.kernel_times()
+    form = "fused" if "fused" in launched else "staged"
+    early = "row_lead" in launched
     sv.timing(False)
-    roof_kernel = "fused" if form == "fused" else "row_stats"
+    # The roofline kernel: the row pass (its two launches with early exit) or
+    # the fused kernel.
+    roof = ["fused"] if form == "fused" else (["row_lead", "row_stats"] if early else ["row_stats"])
+    roof_kernel = "+".join(roof)
 
-    # Timed region: HIP events around the roofline kernel only, on one step
-    # in EVENT_EVERY so their cost stays out of the step time.
-    sv.timing([roof_kernel] if not args.no_kernel_events else False, every=EVENT_EVERY)
+    # Timed region: HIP events around the roofline kernel(s) only, on one
+    # step in EVENT_EVERY so their cost stays out of the step time.
+    sv.timing(roof if not args.no_kernel_events else False, every=EVENT_EVERY)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    k1_live = sv.kernel_times()[roof_kernel] if not args.no_kernel_events else None
+    k1_live = None
+    if not args.no_kernel_events:
+        kt = sv.kernel_times()
+        k1_live = sum(kt[k] for k in roof)
     sv.timing(False)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     # Per-kernel breakdown: a further untimed pass with events around every kernel.
@@ -180,11 +198,21 @@ def main():
     n = out_n.cpu().numpy()
     elt = w.elem_bytes
     sampling = w.temperature > 0
-    needed_rows = int(np.sum(w.k + 1) + np.sum(w.k[sampling]))
-    draw_rows = int(np.sum(np.where(sampling, np.where(n < w.k, 2, 1), 0)))
+    k = w.k.astype(np.int64)
+    full_rows = int(np.sum(k + 1) + np.sum(k[sampling]))          # every needed row, one pass
+    min_rows = int(np.sum(n + 1) + np.sum(np.minimum(n + 1, k)[sampling]))   # up to the first rejection
+    if early:
+        L = args.lead
+        lead_rows = np.minimum(k, L - 1) + 1 + np.where(sampling, np.minimum(k, L), 0)
+        decided = (n < L) | (k < L)
+        rest_rows = np.where(decided, 0, (k - L + 1) + np.where(sampling, k - L, 0))
+        read_rows = int(np.sum(lead_rows + rest_rows))
+    else:
+        read_rows = full_rows
+    draw_rows = int(np.sum(np.where(sampling, np.where(n < k, 2, 1), 0)))
     row_bytes = w.V * elt
-    k1_bytes = needed_rows * row_bytes
-    total_bytes = (needed_rows + draw_rows) * row_bytes
+    k1_bytes = read_rows * row_bytes
+    total_bytes = (read_rows + draw_rows) * row_bytes
     seq_per_s = w.B / (ms_per_step / 1e3)
     hbm_gbs = total_bytes / (ms_per_step / 1e3) / 1e9
 
@@ -221,9 +249,11 @@ def main():
                    f"V={w.V} {w.dtype} logits", "B": w.B, "V": w.V, "k_max": int(w.k.max()),
                    "total_draft": w.total, "logit_dtype": w.dtype,
                    "temperatures": sorted(set(float(t) for t in w.temperature)),
-                   "input_copies": len(copies), "form": form},
+                   "input_copies": len(copies), "form": form,
+                   "early_exit_lead": args.lead if early else 0},
         "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
         "algorithmic_bytes": total_bytes, "mean_accepted": round(float(n.mean()), 4),
+        "rows_read": read_rows, "rows_full_pass": full_rows, "rows_minimum": min_rows,
         "draw_rows": draw_rows,
         "kernels_ms": {k: round(v, 5) for k, v in kern.items()},   # separate pass, all kernels evented
         "roofline": roofline, "cpu_baseline": cpu, "gen_s": round(t_gen, 2),

@@ -139,12 +139,13 @@ void spec_verify_release(void);
  * writes, for up to max_kernels kernels, the mean elapsed milliseconds per
  * call over the recorded calls that launched the kernel (ms[i] belongs to
  * spec_verify_kernel_name(i); NaN for kernels not selected or not launched:
- * the staged form launches row_stats, accept, draw_sums and draw_pick, the
- * fused form fused_reset and fused); it returns the number of kernels, or
- * -1 if the probe is off, no call was recorded or a HIP call failed.
+ * the staged form launches row_lead and accept_lead (early exit only),
+ * row_stats, accept, draw_sums and draw_pick, the fused form fused_reset
+ * and fused); it returns the number of kernels, or -1 if the probe is off,
+ * no call was recorded or a HIP call failed.
  * spec_verify_timing returns SV_ERR_SHAPE for every < 1.  The probe uses
  * one device: turn it off and on again after switching devices. */
-#define SV_TIME_ALL 0x3F
+#define SV_TIME_ALL 0xFF
 sv_status_t spec_verify_timing(int32_t kernels, int32_t every);
 int32_t spec_verify_kernel_times(float *ms, int32_t max_kernels);
 const char *spec_verify_kernel_name(int32_t i);
@@ -167,6 +168,18 @@ sv_status_t spec_verify_set_geometry(int64_t seg_elems, int64_t chunk_elems);
  * forms give identical results.  Returns SV_ERR_SHAPE for an unknown mode or fused_lag < 0. */
 enum { SV_MODE_AUTO = 0, SV_MODE_STAGED = 1, SV_MODE_FUSED = 2 };
 sv_status_t spec_verify_set_mode(int32_t mode, int32_t fused_lag);
+
+/* Early exit (staged form).  The pages' verify loop tests one position at a
+ * time and stops at the first rejection, so the rows after it are never
+ * needed.  With lead_positions = L > 0 (default 1) the row pass first reads
+ * positions 0..L-1 of every sequence and runs their accept tests; sequences
+ * with a rejection there (or with k_b < L) are settled, and only the other
+ * sequences' remaining rows are read.  L = 0 reads every row in one pass.
+ * The outputs do not depend on L, except that the out_p/out_q and row
+ * diagnostics of spec_verify_probs are NaN for rows that were not read
+ * (and data errors in unread rows, such as a non-finite row, go unseen).
+ * Returns SV_ERR_SHAPE unless 0 <= L <= SV_K_MAX + 1. */
+sv_status_t spec_verify_set_early_exit(int32_t lead_positions);
 
 #ifdef __cplusplus
 }

@@ -15,7 +15,7 @@ from ._lib import (LIB_PATH, SV_BF16, SV_F32, SV_K_MAX, SV_MODE_AUTO, SV_MODE_FU
 
 __all__ = [
     "spec_verify", "spec_verify_probs", "spec_verify_workspace_size", "spec_verify_release",
-    "timing", "kernel_times", "set_geometry", "set_mode", "SpecVerifyError", "SV_F32", "SV_BF16",
+    "timing", "kernel_times", "set_geometry", "set_mode", "set_early_exit", "SpecVerifyError", "SV_F32", "SV_BF16",
     "SV_K_MAX", "SV_MODE_AUTO", "SV_MODE_STAGED", "SV_MODE_FUSED", "LIB_PATH", "lib",
 ]
 
@@ -142,6 +142,11 @@ def spec_verify_release() -> None:
 
 def set_geometry(seg_elems: int = 0, chunk_elems: int = 0) -> None:
     check(lib().spec_verify_set_geometry(seg_elems, chunk_elems), "spec_verify_set_geometry")
+
+
+def set_early_exit(lead_positions: int = 1) -> None:
+    """Leading positions every sequence reads before the rest (0 = off)."""
+    check(lib().spec_verify_set_early_exit(int(lead_positions)), "spec_verify_set_early_exit")
 
 
 def set_mode(mode: int = SV_MODE_AUTO, fused_lag: int = 0) -> None:

@@ -67,8 +67,19 @@ __device__ __forceinline__ double log2_norm(const RowStat& r, float c) {
 // Accept scan of sequence b (0 <= b < B), run by every lane of one wave.
 // kCo: the SegStats and captured logits come from other workgroups of the
 // same launch, and the DrawTask goes to others.
+//
+// Early exit: only the rows of positions < limit have been read.  If their
+// tests already decide the outcome (a rejection among them, or every
+// position including the bonus row read) the scan writes everything and
+// sets *done = 1; otherwise (the first rejection, if any, lies at or past
+// limit) it writes nothing but *done = 0, and runs again once the remaining
+// rows are read; it then appends those rows' segments to plan.rest.  The
+// scan stops at the first rejection, like the pages'
+// loop over positions, so rows after it never influence the result.
+// Diagnostics of rows that were not read are NaN.
 template <bool kCo>
-__device__ __forceinline__ void accept_sequence(const Problem& p, const Plan& plan, int32_t b) {
+__device__ __forceinline__ void accept_sequence(const Problem& p, const Plan& plan, int32_t b,
+                                                int32_t limit = kKMax + 1, int32_t* done = nullptr) {
     const int lane = threadIdx.x & 63;
     int64_t o, o1;
     if (p.offsets) { o = p.offsets[b]; o1 = p.offsets[b + 1]; }
@@ -89,7 +100,8 @@ __device__ __forceinline__ void accept_sequence(const Problem& p, const Plan& pl
         if (x < 0 || x >= p.V) ok = false;
     }
     RowStat rt{0.f, 0, 0.f, 1.0}, rd{0.f, 0, 0.f, 1.0};
-    if (ok && lane <= k) {
+    const bool read = lane < limit;                // this position's rows have been read
+    if (ok && lane <= k && read) {
         rt = merge_row<kCo>(plan.seg + trow * plan.nseg, plan.nseg, greedy);
         if (!(fabsf(rt.m) <= 3.4e38f)) ok = false;
         if (!greedy && lane < k) {
@@ -107,13 +119,14 @@ __device__ __forceinline__ void accept_sequence(const Problem& p, const Plan& pl
         if (lane == 0) {
             p.out_n[b] = -1;
             st_co<kCo>(&plan.task[b].kind, static_cast<int32_t>(kNone));
+            if (done) *done = 1;
         }
         return;
     }
 
     bool reject = false;
     double px = NAN, qx = NAN;
-    if (lane < k) {
+    if (lane < k && read) {
         if (greedy) {
             reject = (x != rt.arg);
         } else {
@@ -126,7 +139,30 @@ __device__ __forceinline__ void accept_sequence(const Problem& p, const Plan& pl
         }
     }
     const uint64_t mask = __ballot(reject);
+    if (!mask && k >= limit) {                     // undecided: rows past limit are needed
+        if (done) {
+            if (lane == 0) *done = 0;
+            // List the remaining row segments: target rows limit..k, then
+            // (sampling) draft rows limit..k-1, each in nseg segments.
+            const int32_t nt = k - limit + 1, nd = greedy ? 0 : k - limit;
+            const int32_t cnt = (nt + nd) * plan.nseg;
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(plan.rest_n, static_cast<uint32_t>(cnt));
+            base = __shfl(base, 0, 64);
+            for (int32_t e = lane; e < cnt; e += 64) {
+                const int32_t j = e / plan.nseg, sg = e - j * plan.nseg;
+                RestItem it;
+                it.b = b;
+                it.is_target = j < nt;
+                it.row = static_cast<int32_t>(j < nt ? o + b + limit + j : o + limit + (j - nt));
+                it.seg = sg;
+                plan.rest[base + e] = it;
+            }
+        }
+        return;
+    }
     const int n = mask ? __ffsll(static_cast<unsigned long long>(mask)) - 1 : k;
+    if (done && lane == 0) *done = 1;
 
     // Slot n of a sampling sequence is written by the draw alone: in the
     // fused form the draw runs in another workgroup, possibly on another XCD,
@@ -151,11 +187,11 @@ __device__ __forceinline__ void accept_sequence(const Problem& p, const Plan& pl
         p.out_q[drow] = static_cast<float>(qx);
     }
     if (p.out_row_max && lane <= k) {
-        p.out_row_max[trow] = rt.m;
-        p.out_row_sum[trow] = greedy ? NAN : static_cast<float>(exp2(log2_norm(rt, c)));
+        p.out_row_max[trow] = read ? rt.m : NAN;
+        p.out_row_sum[trow] = (greedy || !read) ? NAN : static_cast<float>(exp2(log2_norm(rt, c)));
         if (lane < k) {
-            p.out_row_max[ntarget + drow] = greedy ? NAN : rd.m;
-            p.out_row_sum[ntarget + drow] = greedy ? NAN : static_cast<float>(exp2(log2_norm(rd, c)));
+            p.out_row_max[ntarget + drow] = (greedy || !read) ? NAN : rd.m;
+            p.out_row_sum[ntarget + drow] = (greedy || !read) ? NAN : static_cast<float>(exp2(log2_norm(rd, c)));
         }
     }
 }

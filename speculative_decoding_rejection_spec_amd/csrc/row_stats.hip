@@ -5,22 +5,65 @@
 // draft rows; each 256-thread workgroup streams one contiguous segment of
 // one row and writes its SegStat.  The kernel boundary publishes the
 // statistics to the accept scan.
+//
+// Early exit: the pages verify one position at a time and stop at the first
+// rejection, so rows after it are never needed (page "投机解码", section
+// 投机解码的三步流程, step 3; page "大模型推理无损加速:投机采样...", section 三).
+// row_lead reads the leading positions of every sequence; after their accept
+// scan, row_stats reads the rest only for sequences still undecided.
 #include "row_pass.h"
 
 namespace sv {
 namespace {
 
+// First drafted slot of sequence b.
+__device__ __forceinline__ int64_t first_slot(const Problem& p, int32_t b) {
+    return p.offsets ? static_cast<int64_t>(p.offsets[b]) : static_cast<int64_t>(b) * p.k_uniform;
+}
+
+// All rows, or with early exit the row segments the leading positions left
+// to read (listed by the lead accept scan; workgroups past the end of the
+// list return at once).
 template <int DT>
 __global__ __launch_bounds__(kThreads) void row_stats_kernel(Problem p, Plan plan) {
     const int64_t w = blockIdx.x;
+    __shared__ RowLds lds;
+    if (plan.lead > 0) {
+        if (w >= *plan.rest_n) return;
+        const RestItem it = plan.rest[w];
+        row_segment<DT, false>(p, plan, it.b, it.is_target != 0, it.row, it.seg, lds);
+        return;
+    }
     const int64_t row_all = w / plan.nseg;
     const int64_t seg = w - row_all * plan.nseg;
     const int64_t ntarget = p.total + p.B;
     const bool is_target = row_all < ntarget;
     const int64_t r = is_target ? row_all : row_all - ntarget;
     const int32_t b = is_target ? seq_of_target_row(p, r) : seq_of_draft_row(p, r);
-    __shared__ RowLds lds;
     row_segment<DT, false>(p, plan, b, is_target, r, seg, lds);
+}
+
+// Early exit, first round: the rows of positions < lead of every sequence.
+// Grid (sequence, position, target/draft, segment); a workgroup whose row
+// does not exist (position past k_b, or a sequence whose offsets describe
+// no usable range) returns at once.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void row_lead_kernel(Problem p, Plan plan) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) *plan.rest_n = 0;   // the lead accept scan fills the list
+    int64_t q = blockIdx.x;
+    const int64_t seg = q % plan.nseg;
+    q /= plan.nseg;
+    const bool is_target = (q & 1) == 0;
+    q >>= 1;
+    const int32_t i = static_cast<int32_t>(q % plan.lead);
+    const int32_t b = static_cast<int32_t>(q / plan.lead);
+    const int64_t o = first_slot(p, b);
+    const int64_t o1 = p.offsets ? static_cast<int64_t>(p.offsets[b + 1]) : o + p.k_uniform;
+    if (!(o >= 0 && o1 >= o && o1 - o <= kKMax && o1 <= p.total)) return;
+    const int64_t k = o1 - o;
+    if (is_target ? i > k : i >= k) return;
+    __shared__ RowLds lds;
+    row_segment<DT, false>(p, plan, b, is_target, is_target ? o + b + i : o + i, seg, lds);
 }
 
 }  // namespace
@@ -32,6 +75,16 @@ hipError_t launch_row_stats(const Problem& p, const Plan& plan, hipStream_t s) {
         row_stats_kernel<SV_BF16><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s>>>(p, plan);
     else
         row_stats_kernel<SV_F32><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s>>>(p, plan);
+    return hipGetLastError();
+}
+
+hipError_t launch_row_lead(const Problem& p, const Plan& plan, hipStream_t s) {
+    const int64_t blocks = static_cast<int64_t>(p.B) * plan.lead * 2 * plan.nseg;
+    if (blocks == 0) return hipSuccess;
+    if (p.dtype == SV_BF16)
+        row_lead_kernel<SV_BF16><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s>>>(p, plan);
+    else
+        row_lead_kernel<SV_F32><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s>>>(p, plan);
     return hipGetLastError();
 }
 

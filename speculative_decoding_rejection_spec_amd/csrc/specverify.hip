@@ -16,19 +16,21 @@ constexpr int64_t kDefaultSegElems = 65536;   // row-pass segment length before 
 // inside a window.
 int64_t row_unit(sv_dtype_t dtype) { return dtype == SV_BF16 ? 256 * 8 * 8 : 256 * 4 * 4; }
 constexpr int64_t kDefaultChunkElems = 8192;  // draw chunk length before rounding
+constexpr int32_t kDefaultLead = 1;           // early exit after the first position
 constexpr int64_t kMaxChunks = 1024;          // draw chunks per row (the pick keeps them in LDS)
 constexpr int kMaxDevices = 64;
-constexpr int kNumKernels = 6;
-enum { kKRowStats, kKAccept, kKDrawSums, kKDrawPick, kKFusedReset, kKFused };
+constexpr int kNumKernels = 8;
+enum { kKRowStats, kKAccept, kKDrawSums, kKDrawPick, kKFusedReset, kKFused, kKRowLead, kKAcceptLead };
 
 const char* const kKernelNames[kNumKernels] = {"row_stats", "accept", "draw_sums", "draw_pick",
-                                               "fused_reset", "fused"};
+                                               "fused_reset", "fused", "row_lead", "accept_lead"};
 
 std::mutex g_mutex;
 int64_t g_seg_elems = kDefaultSegElems;
 int64_t g_chunk_elems = kDefaultChunkElems;
 int32_t g_mode = SV_MODE_AUTO;
 int32_t g_fused_lag = 0;                     // 0: chosen from the resident grid
+int32_t g_lead = kDefaultLead;               // early exit: leading positions read first (0: off)
 constexpr double kLagFactor = 1.5;           // resident grids of items between rows and draw
 
 // Library-owned workspace, one grow-only buffer per device.
@@ -51,7 +53,8 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 struct Geometry {
     int32_t nseg, nchunk;
     int64_t seg_len, chunk_len;
-    size_t off_seg, off_task, off_csum, off_band_n, off_band_w, off_xlogit, off_ctr, bytes;
+    size_t off_seg, off_task, off_csum, off_band_n, off_band_w, off_xlogit, off_ctr, off_done, off_rest,
+        off_rest_n, bytes;
 };
 
 // Splits a row of V logits into n <= max_pieces pieces of about `target`
@@ -70,7 +73,7 @@ bool make_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dtype, int64_
     split(V, seg_elems, 1 << 20, seg_elems >= unit ? unit : 8, g.nseg, g.seg_len);
     split(V, chunk_elems, kMaxChunks, 8, g.nchunk, g.chunk_len);
     const int64_t rows = 2 * total + B;
-    if (rows * g.nseg > 0xFFFFFFFFll || static_cast<int64_t>(B) * g.nchunk > 0xFFFFFFFFll) return false;
+    if (rows * g.nseg > 0x7FFFFFFFll || static_cast<int64_t>(B) * g.nchunk > 0x7FFFFFFFll) return false;
     size_t off = 0;
     g.off_seg = off;
     off = align256(off + sizeof(SegStat) * static_cast<size_t>(rows) * g.nseg);
@@ -86,6 +89,12 @@ bool make_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dtype, int64_
     off = align256(off + sizeof(float) * static_cast<size_t>(rows));
     g.off_ctr = off;
     off = align256(off + sizeof(uint32_t) * static_cast<size_t>(fused_counter_words(B)));
+    g.off_done = off;
+    off = align256(off + sizeof(int32_t) * static_cast<size_t>(B));
+    g.off_rest = off;
+    off = align256(off + sizeof(RestItem) * static_cast<size_t>(rows) * g.nseg);
+    g.off_rest_n = off;
+    off = align256(off + sizeof(uint32_t));
     g.bytes = off;
     return true;
 }
@@ -159,6 +168,9 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     plan.band_w = reinterpret_cast<double*>(ws + g.off_band_w);
     plan.xlogit = reinterpret_cast<float*>(ws + g.off_xlogit);
     plan.ctr = reinterpret_cast<uint32_t*>(ws + g.off_ctr);
+    plan.done = reinterpret_cast<int32_t*>(ws + g.off_done);
+    plan.rest = reinterpret_cast<RestItem*>(ws + g.off_rest);
+    plan.rest_n = reinterpret_cast<uint32_t*>(ws + g.off_rest_n);
 
     // The fused form needs the schedule prefix and the pick's chunk masses
     // in LDS, and an item count below 2^31.
@@ -169,6 +181,7 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     // fused.hip), so it runs only when asked for.
     const bool fused = g_mode == SV_MODE_FUSED;
     if (fused && !fused_fits) return SV_ERR_SHAPE;
+    plan.lead = fused ? 0 : g_lead;           // the fused form reads every row
     Fused f{};
     if (fused) {
         if (fused_grid(p.dtype, &f.blocks) != hipSuccess) return SV_ERR_HIP;
@@ -214,7 +227,9 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
         ok = launch(kKFusedReset, [&] { return launch_fused_reset(p, plan, stream); }) &&
              launch(kKFused, [&] { return launch_fused(p, plan, f, stream); });
     } else {
-        ok = launch(kKRowStats, [&] { return launch_row_stats(p, plan, stream); }) &&
+        ok = (plan.lead == 0 || (launch(kKRowLead, [&] { return launch_row_lead(p, plan, stream); }) &&
+                                 launch(kKAcceptLead, [&] { return launch_accept_lead(p, plan, stream); }))) &&
+             launch(kKRowStats, [&] { return launch_row_stats(p, plan, stream); }) &&
              launch(kKAccept, [&] { return launch_accept(p, plan, stream); }) &&
              launch(kKDrawSums, [&] { return launch_draw_sums(p, plan, stream); }) &&
              launch(kKDrawPick, [&] { return launch_draw_pick(p, plan, stream); });
@@ -359,6 +374,13 @@ sv_status_t spec_verify_set_mode(int32_t mode, int32_t fused_lag) {
     std::lock_guard<std::mutex> lock(g_mutex);
     g_mode = mode;
     g_fused_lag = fused_lag;
+    return SV_OK;
+}
+
+sv_status_t spec_verify_set_early_exit(int32_t lead_positions) {
+    if (lead_positions < 0 || lead_positions > SV_K_MAX + 1) return SV_ERR_SHAPE;
+    std::lock_guard<std::mutex> lock(g_mutex);
+    g_lead = lead_positions;
     return SV_OK;
 }
 

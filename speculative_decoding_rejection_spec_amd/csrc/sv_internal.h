@@ -1,7 +1,11 @@
 // sv_internal.h -- declarations shared by the HIP sources of libspecverify.
 //
 // Data flow of one call, staged form (every kernel is enqueued on the
-// caller's stream; kernel boundaries publish each step's results):
+// caller's stream; kernel boundaries publish each step's results).  With
+// early exit (Plan::lead > 0) steps 1 and 2 first run over the leading
+// positions of every sequence (row_lead, accept_lead); sequences whose
+// outcome those decide are done, and steps 1 and 2 then run over the
+// remaining rows of the others only:
 //   1. row pass    (row_stats.hip, row_pass.h): one workgroup per (logit row,
 //                  segment) streams the segment once and writes a SegStat;
 //   2. accept scan (accept.hip, accept_scan.h): one wave64 per sequence
@@ -64,6 +68,14 @@ struct ChunkSums {
     double b;    // sum of w_d over the same tokens
 };
 
+// One row segment of the second early-exit round.
+struct RestItem {
+    int32_t b;           // sequence
+    int32_t is_target;   // target row (1) or draft row (0)
+    int32_t row;         // row index in its array
+    int32_t seg;         // segment
+};
+
 // The caller's arguments, passed by value to every kernel.
 struct Problem {
     const void* target;
@@ -98,6 +110,10 @@ struct Plan {
     double* band_w;      // [B * nchunk * kWaves * kWaveCap * 2]: their (w_t, w_d)
     float* xlogit;       // [2 * total + B]: logit of the drafted token of each row
     uint32_t* ctr;       // fused form only: kCtrHeader words, then rows_done[B], ready[B], chunks_done[B]
+    int32_t lead;        // early exit: positions every sequence reads first (0: one pass over all rows)
+    int32_t* done;       // early exit: [B], 1 once a sequence's outcome is known from its leading positions
+    RestItem* rest;      // early exit: [(2 * total + B) * nseg], the row segments still to read
+    uint32_t* rest_n;    // early exit: number of entries in rest
 };
 
 // Layout of Plan::ctr (fused form), zeroed before every launch.  The queue
@@ -117,7 +133,9 @@ struct Fused {
 
 // Host-side launchers (one per kernel).
 hipError_t launch_row_stats(const Problem& p, const Plan& plan, hipStream_t s);
+hipError_t launch_row_lead(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_accept(const Problem& p, const Plan& plan, hipStream_t s);
+hipError_t launch_accept_lead(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_draw_sums(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_draw_pick(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_fused_reset(const Problem& p, const Plan& plan, hipStream_t s);

@@ -22,14 +22,20 @@ pytestmark = pytest.mark.gpu
 AMBIGUOUS = oracle.FLAG_A | oracle.FLAG_B | oracle.FLAG_D
 
 
-MODES = ["staged", "fused"]
+# Launch forms: staged with early exit after the first position (the
+# default), staged reading every row in one pass, and the fused persistent
+# kernel.  Every test below runs in each.
+MODES = ["early", "full", "fused"]
 CURRENT = {"mode": None}
+
+
+def set_form(sv, form):
+    sv.set_mode(sv.SV_MODE_FUSED if form == "fused" else sv.SV_MODE_STAGED)
+    sv.set_early_exit(1 if form == "early" else 0)
 
 
 @pytest.fixture(scope="module", params=MODES)
 def sv(cuda, request):
-    """The library, set to the staged (four kernels) or the fused (one
-    persistent kernel) form; every test below runs in both."""
     import os
 
     import speculative_decoding_rejection_spec_amd as sv
@@ -37,11 +43,12 @@ def sv(cuda, request):
         import __graft_entry__
         __graft_entry__.build()
     sv.set_geometry(0, 0)
-    sv.set_mode(sv.SV_MODE_FUSED if request.param == "fused" else sv.SV_MODE_STAGED)
+    set_form(sv, request.param)
     CURRENT["mode"] = request.param
-    print(f"[mode {request.param}]", flush=True)
+    print(f"[form {request.param}]", flush=True)
     yield sv
     sv.set_mode(sv.SV_MODE_AUTO)
+    sv.set_early_exit(1)
 
 
 def to_device(w, dev):
@@ -143,6 +150,23 @@ def test_many_sequences_flag_rate(sv, cuda):
     assert amb <= 0.001 * tot
 
 
+def needed_rows(w, n):
+    """Boolean masks over target rows and draft rows: the rows of positions
+    up to the first rejection n_b (the draft row only below k_b, and only
+    for sampling sequences) -- what any verify must read."""
+    tgt = np.zeros(w.total + w.B, bool)
+    dft = np.zeros(w.total, bool)
+    for b in range(w.B):
+        nb = int(n[b])
+        if nb < 0:
+            continue
+        tgt[w.target_row(b, 0):w.target_row(b, nb) + 1] = True
+        if w.temperature[b] > 0:
+            o = int(w.offsets[b])
+            dft[o:o + min(nb + 1, int(w.k[b]))] = True
+    return tgt, dft
+
+
 def test_probabilities_and_row_stats(sv, cuda):
     for name, B in (("c1", 32), ("c3", 16), ("c5", 64)):
         w = workload(name, 0, B)
@@ -153,8 +177,14 @@ def test_probabilities_and_row_stats(sv, cuda):
         assert np.max(np.abs(g["p"][have] - ref["px"][have])) < 1e-5, name
         assert np.max(np.abs(g["q"][have] - ref["qx"][have])) < 1e-5, name
         used = ~np.isnan(ref["row_max"])
+        if CURRENT["mode"] == "early":
+            # rows after the first rejection may be unread (NaN); every needed row is read
+            tgt, dft = needed_rows(w, ref["n"])
+            need = np.concatenate([tgt, dft]) & used
+            assert not np.isnan(g["row_max"][need]).any(), name
+            used &= ~np.isnan(g["row_max"])
         np.testing.assert_array_equal(g["row_max"][used], ref["row_max"][used].astype(np.float32))
-        s_used = ~np.isnan(ref["row_sum"])
+        s_used = ~np.isnan(ref["row_sum"]) & ~np.isnan(g["row_sumexp"])
         rel = np.abs(g["row_sumexp"][s_used] - ref["row_sum"][s_used]) / ref["row_sum"][s_used]
         assert rel.max() < 1e-5, (name, rel.max())
 
@@ -309,6 +339,26 @@ def test_batch_limits(sv, cuda):
             compare(w, run_gpu(sv, w, cuda), ref, f"B={B}")
 
 
+def test_early_exit_leads(sv, cuda):
+    """Early exit after 1, 2, 3 and 64 leading positions (64: everything is
+    read in the first round) gives the same outputs as one full pass."""
+    if CURRENT["mode"] != "early":
+        pytest.skip("early-exit form only")
+    w = workload("c5", 0, 96)
+    ref = oracle.verify(w, threads=16)
+    base = None
+    try:
+        for lead in (1, 2, 3, 64):
+            sv.set_early_exit(lead)
+            out = run_gpu(sv, w, cuda)
+            compare(w, out, ref, f"lead {lead}")
+            if base is None:
+                base = out
+            assert np.array_equal(out["tokens"], base["tokens"]) and np.array_equal(out["n"], base["n"])
+    finally:
+        sv.set_early_exit(1)
+
+
 def test_fused_matches_staged_bitwise(sv, cuda):
     """Both forms run the same row pass, accept scan and chunk sums, so the
     counts and diagnostics are identical on the full C4 batch; the pick scans
@@ -321,9 +371,10 @@ def test_fused_matches_staged_bitwise(sv, cuda):
     try:
         for mode in (sv.SV_MODE_STAGED, sv.SV_MODE_FUSED):
             sv.set_mode(mode)
+            sv.set_early_exit(0)
             out[mode] = run_gpu(sv, w, cuda, probs=True)
     finally:
-        sv.set_mode(sv.SV_MODE_FUSED)
+        set_form(sv, "fused")
     a, b = out[sv.SV_MODE_STAGED], out[sv.SV_MODE_FUSED]
     for key in a:
         np.testing.assert_array_equal(a[key], b[key], err_msg=key)
