@@ -19,7 +19,7 @@ in the fused form (--mode fused).
 Algorithmic bytes per step: the logit rows the step reads, once each, plus
 one extra read of each draw row (2 rows for a residual draw, 1 for a bonus
 draw, 0 for greedy), V * element size per row; the small per-sequence arrays
-are ignored.  Rows read: with early exit (the default, --lead 1) the
+are ignored.  Rows read: with early exit (--lead 1; the default for C4) the
 leading positions of every sequence and the remaining positions of the
 sequences they leave undecided; in one full pass (--lead 0) or the fused
 form, every target row and the draft rows of sampling sequences.  Both
@@ -92,8 +92,9 @@ def main():
     ap.add_argument("--mode", choices=["auto", "staged", "fused"], default="auto",
                     help="launch form (auto = staged)")
     ap.add_argument("--lag", type=int, default=0, help="fused form: draw lag in sequences (0 = auto)")
-    ap.add_argument("--lead", type=int, default=1,
-                    help="early exit: leading positions read by every sequence (0 = one full pass)")
+    ap.add_argument("--lead", type=int, default=-1,
+                    help="early exit: leading positions read by every sequence (0 = one full pass, "
+                         "-1 = the library's choice by batch size)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -202,7 +203,7 @@ def main():
     full_rows = int(np.sum(k + 1) + np.sum(k[sampling]))          # every needed row, one pass
     min_rows = int(np.sum(n + 1) + np.sum(np.minimum(n + 1, k)[sampling]))   # up to the first rejection
     if early:
-        L = args.lead
+        L = args.lead if args.lead > 0 else 1
         lead_rows = np.minimum(k, L - 1) + 1 + np.where(sampling, np.minimum(k, L), 0)
         decided = (n < L) | (k < L)
         rest_rows = np.where(decided, 0, (k - L + 1) + np.where(sampling, k - L, 0))
@@ -250,7 +251,7 @@ def main():
                    "total_draft": w.total, "logit_dtype": w.dtype,
                    "temperatures": sorted(set(float(t) for t in w.temperature)),
                    "input_copies": len(copies), "form": form,
-                   "early_exit_lead": args.lead if early else 0},
+                   "early_exit_lead": (args.lead if args.lead > 0 else 1) if early else 0},
         "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
         "algorithmic_bytes": total_bytes, "mean_accepted": round(float(n.mean()), 4),
         "rows_read": read_rows, "rows_full_pass": full_rows, "rows_minimum": min_rows,

@@ -171,14 +171,17 @@ sv_status_t spec_verify_set_mode(int32_t mode, int32_t fused_lag);
 
 /* Early exit (staged form).  The pages' verify loop tests one position at a
  * time and stops at the first rejection, so the rows after it are never
- * needed.  With lead_positions = L > 0 (default 1) the row pass first reads
- * positions 0..L-1 of every sequence and runs their accept tests; sequences
- * with a rejection there (or with k_b < L) are settled, and only the other
+ * needed.  With lead_positions = L > 0 the row pass first reads positions
+ * 0..L-1 of every sequence and runs their accept tests; sequences with a
+ * rejection there (or with k_b < L) are settled, and only the other
  * sequences' remaining rows are read.  L = 0 reads every row in one pass.
- * The outputs do not depend on L, except that the out_p/out_q and row
- * diagnostics of spec_verify_probs are NaN for rows that were not read
- * (and data errors in unread rows, such as a non-finite row, go unseen).
- * Returns SV_ERR_SHAPE unless 0 <= L <= SV_K_MAX + 1. */
+ * L = -1 (the default) chooses: L = 1 when all logit rows of the call
+ * together hold at least 512 MiB, else 0 (the two extra launches cost more
+ * than small batches can save).  The outputs do not depend on L, except
+ * that the out_p/out_q and row diagnostics of spec_verify_probs are NaN for
+ * rows that were not read (and data errors in unread rows, such as a
+ * non-finite row, go unseen).  Returns SV_ERR_SHAPE unless
+ * -1 <= L <= SV_K_MAX + 1. */
 sv_status_t spec_verify_set_early_exit(int32_t lead_positions);
 
 #ifdef __cplusplus

@@ -144,8 +144,9 @@ def set_geometry(seg_elems: int = 0, chunk_elems: int = 0) -> None:
     check(lib().spec_verify_set_geometry(seg_elems, chunk_elems), "spec_verify_set_geometry")
 
 
-def set_early_exit(lead_positions: int = 1) -> None:
-    """Leading positions every sequence reads before the rest (0 = off)."""
+def set_early_exit(lead_positions: int = -1) -> None:
+    """Leading positions every sequence reads before the rest (0 = off,
+    -1 = automatic by batch size)."""
     check(lib().spec_verify_set_early_exit(int(lead_positions)), "spec_verify_set_early_exit")
 
 

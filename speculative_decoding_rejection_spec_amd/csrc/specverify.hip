@@ -16,7 +16,12 @@ constexpr int64_t kDefaultSegElems = 65536;   // row-pass segment length before 
 // inside a window.
 int64_t row_unit(sv_dtype_t dtype) { return dtype == SV_BF16 ? 256 * 8 * 8 : 256 * 4 * 4; }
 constexpr int64_t kDefaultChunkElems = 8192;  // draw chunk length before rounding
-constexpr int32_t kDefaultLead = 1;           // early exit after the first position
+// Early exit is worth its two extra launches (~15 us) only when the rows
+// it may skip take longer than that to stream: automatic mode (lead -1)
+// uses one leading position when all rows together hold at least
+// kAutoLeadBytes, and one full pass otherwise.
+constexpr int32_t kAutoLead = -1;
+constexpr int64_t kAutoLeadBytes = 512ll << 20;
 constexpr int64_t kMaxChunks = 1024;          // draw chunks per row (the pick keeps them in LDS)
 constexpr int kMaxDevices = 64;
 constexpr int kNumKernels = 8;
@@ -30,7 +35,14 @@ int64_t g_seg_elems = kDefaultSegElems;
 int64_t g_chunk_elems = kDefaultChunkElems;
 int32_t g_mode = SV_MODE_AUTO;
 int32_t g_fused_lag = 0;                     // 0: chosen from the resident grid
-int32_t g_lead = kDefaultLead;               // early exit: leading positions read first (0: off)
+int32_t g_lead = kAutoLead;                  // early exit: leading positions read first (0: off)
+
+int32_t effective_lead(int64_t B, int64_t total, int64_t V, sv_dtype_t dtype) {
+    if (g_mode == SV_MODE_FUSED) return 0;      // the fused form reads every row
+    if (g_lead != kAutoLead) return g_lead;
+    const int64_t bytes = (2 * total + B) * V * (dtype == SV_BF16 ? 2 : 4);
+    return bytes >= kAutoLeadBytes ? 1 : 0;
+}
 constexpr double kLagFactor = 1.5;           // resident grids of items between rows and draw
 
 // Library-owned workspace, one grow-only buffer per device.
@@ -181,7 +193,7 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     // fused.hip), so it runs only when asked for.
     const bool fused = g_mode == SV_MODE_FUSED;
     if (fused && !fused_fits) return SV_ERR_SHAPE;
-    plan.lead = fused ? 0 : g_lead;           // the fused form reads every row
+    plan.lead = fused ? 0 : effective_lead(p.B, p.total, p.V, static_cast<sv_dtype_t>(p.dtype));
     Fused f{};
     if (fused) {
         if (fused_grid(p.dtype, &f.blocks) != hipSuccess) return SV_ERR_HIP;
@@ -378,7 +390,7 @@ sv_status_t spec_verify_set_mode(int32_t mode, int32_t fused_lag) {
 }
 
 sv_status_t spec_verify_set_early_exit(int32_t lead_positions) {
-    if (lead_positions < 0 || lead_positions > SV_K_MAX + 1) return SV_ERR_SHAPE;
+    if (lead_positions < kAutoLead || lead_positions > SV_K_MAX + 1) return SV_ERR_SHAPE;
     std::lock_guard<std::mutex> lock(g_mutex);
     g_lead = lead_positions;
     return SV_OK;

@@ -23,8 +23,8 @@ AMBIGUOUS = oracle.FLAG_A | oracle.FLAG_B | oracle.FLAG_D
 
 
 # Launch forms: staged with early exit after the first position (the
-# default), staged reading every row in one pass, and the fused persistent
-# kernel.  Every test below runs in each.
+# default for large batches), staged reading every row in one pass, and the
+# fused persistent kernel.  Every test below runs in each.
 MODES = ["early", "full", "fused"]
 CURRENT = {"mode": None}
 
@@ -48,7 +48,7 @@ def sv(cuda, request):
     print(f"[form {request.param}]", flush=True)
     yield sv
     sv.set_mode(sv.SV_MODE_AUTO)
-    sv.set_early_exit(1)
+    sv.set_early_exit(-1)
 
 
 def to_device(w, dev):
