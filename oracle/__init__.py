@@ -73,6 +73,11 @@ def _open(path: str):
     lib.oracle_softmax_rows.argtypes = [P, i32, i64, i64, ctypes.c_double, P, P, P]
     lib.oracle_inverse_cdf.restype = i64
     lib.oracle_inverse_cdf.argtypes = [P, i64, ctypes.c_float, P, P]
+    lib.oracle_verify_gathered.restype = ctypes.c_int
+    lib.oracle_verify_gathered.argtypes = [P, P, i32, i64, i32, P, P, P, P, P, i32, i32,
+                                           P, P, P, P, P, P, P, P]
+    lib.oracle_draft_sample.restype = ctypes.c_int
+    lib.oracle_draft_sample.argtypes = [P, i32, i64, i32, P, P, i32, i32, P, P, P, P]
     return lib
 
 
@@ -88,12 +93,16 @@ def _dtype_code(rows: np.ndarray) -> int:
     raise TypeError(f"stored logits must be float32 or uint16 (bf16 bits), got {rows.dtype}")
 
 
-def verify(w, diag: bool = False, threads: int = 1, seqs: tuple[int, int] | None = None) -> dict:
+def verify(w, diag: bool = False, threads: int = 1, seqs: tuple[int, int] | None = None,
+           draft_probs: np.ndarray | None = None) -> dict:
     """Run the oracle over a ``workloads.Workload`` (or any object with the
     same fields).  Returns numpy arrays: tokens [total+B], n [B], flags [B]
     and, with ``diag``, alpha/px/qx [total], Z/gap [B], row_max/row_sum
-    [2*total+B] (target rows first).  ``seqs`` = (b0, b1) limits the work to
-    those sequences (other outputs stay at their fill values)."""
+    [2*total+B] (target rows first; not for the gathered form).  ``seqs`` =
+    (b0, b1) limits the work to those sequences (other outputs stay at their
+    fill values).  ``draft_probs`` [total] (fp32): the drafter's gathered
+    q_i(x_i), used in the accept tests instead of the draft rows' softmax
+    (oracle_verify_gathered)."""
     lib = _load()
     B, V = int(w.B), int(w.V)
     off = np.ascontiguousarray(w.offsets, np.int32)
@@ -115,14 +124,29 @@ def verify(w, diag: bool = False, threads: int = 1, seqs: tuple[int, int] | None
                    row_sum=np.full(2 * total + B, np.nan))
     b0, b1 = seqs if seqs is not None else (0, B)
 
+    qg = None
+    if draft_probs is not None:
+        qg = np.ascontiguousarray(draft_probs, np.float32)
+        if qg.size == 0:
+            qg = np.zeros(1, np.float32)
+        out.pop("row_max", None)
+        out.pop("row_sum", None)
+
     def run(rng):
         lo, hi = rng
-        rc = lib.oracle_verify(
-            _ptr(target), _ptr(draft), dt, V, B, _ptr(off), _ptr(tokens), _ptr(unif),
-            _ptr(temp), lo, hi, _ptr(out["tokens"]), _ptr(out["n"]), _ptr(out["flags"]),
-            _ptr(out.get("alpha")), _ptr(out.get("px")), _ptr(out.get("qx")),
-            _ptr(out.get("Z")), _ptr(out.get("gap")), _ptr(out.get("row_max")),
-            _ptr(out.get("row_sum")))
+        if qg is None:
+            rc = lib.oracle_verify(
+                _ptr(target), _ptr(draft), dt, V, B, _ptr(off), _ptr(tokens), _ptr(unif),
+                _ptr(temp), lo, hi, _ptr(out["tokens"]), _ptr(out["n"]), _ptr(out["flags"]),
+                _ptr(out.get("alpha")), _ptr(out.get("px")), _ptr(out.get("qx")),
+                _ptr(out.get("Z")), _ptr(out.get("gap")), _ptr(out.get("row_max")),
+                _ptr(out.get("row_sum")))
+        else:
+            rc = lib.oracle_verify_gathered(
+                _ptr(target), _ptr(draft), dt, V, B, _ptr(off), _ptr(tokens), _ptr(qg),
+                _ptr(unif), _ptr(temp), lo, hi, _ptr(out["tokens"]), _ptr(out["n"]),
+                _ptr(out["flags"]), _ptr(out.get("alpha")), _ptr(out.get("px")),
+                _ptr(out.get("qx")), _ptr(out.get("Z")), _ptr(out.get("gap")))
         if rc != 0:
             raise RuntimeError(f"oracle_verify failed with code {rc}")
 
@@ -187,3 +211,35 @@ def inverse_cdf(r: np.ndarray, u: float):
     t = lib.oracle_inverse_cdf(_ptr(r), r.size, ctypes.c_float(np.float32(u)),
                                ctypes.byref(Z), ctypes.byref(gap))
     return int(t), Z.value, gap.value
+
+
+def draft_sample(logits: np.ndarray, temperature, uniforms, threads: int = 1) -> dict:
+    """Draft sampler over stored rows [rows, V] (fp32 or bf16 bits): per row
+    the drawn token, its probability q(x) (fp64; 1 for greedy rows), flags
+    (B: u Z within 1e-12 of a CDF boundary; E: bad temperature) and the
+    boundary gap."""
+    lib = _load()
+    logits = np.ascontiguousarray(logits)
+    if logits.ndim == 1:
+        logits = logits[None]
+    rows, V = logits.shape
+    temp = np.ascontiguousarray(np.broadcast_to(np.asarray(temperature, np.float32), (rows,)))
+    unif = np.ascontiguousarray(np.asarray(uniforms, np.float32).reshape(rows))
+    out = dict(tokens=np.full(rows, -1, np.int32), probs=np.full(rows, np.nan),
+               flags=np.zeros(rows, np.int32), gap=np.full(rows, np.nan))
+
+    def run(rng):
+        lo, hi = rng
+        rc = lib.oracle_draft_sample(_ptr(logits), _dtype_code(logits), V, rows, _ptr(temp),
+                                     _ptr(unif), lo, hi, _ptr(out["tokens"]), _ptr(out["probs"]),
+                                     _ptr(out["flags"]), _ptr(out["gap"]))
+        if rc != 0:
+            raise RuntimeError(f"oracle_draft_sample failed with code {rc}")
+
+    if threads <= 1 or rows <= 1:
+        run((0, rows))
+    else:
+        edges = np.linspace(0, rows, min(threads, rows) + 1).astype(int)
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(run, zip(edges[:-1], edges[1:])))
+    return out

@@ -48,6 +48,12 @@
  *   R8 greedy ties go to the lowest token id;
  *   R11 if a rejection leaves Z < 1e-9 the draw falls back to p_n (flag D).
  *
+ * Two more entry points follow the same pages: oracle_verify_gathered (the
+ * accept tests divide by the drafter's gathered q_i(x_i) instead of the draft
+ * row's softmax; the full draft row enters only the residual) and
+ * oracle_draft_sample (the drafter's own step: x ~ softmax(z / T) by the same
+ * inverse CDF, or the argmax at T = 0, with q(x) reported).
+ *
  * Ambiguity flags (rows where float rounding order may legitimately decide
  * differently): A = some evaluated accept test has |u - alpha| < 1e-5;
  * B = u*.Z lies within 1e-12 (absolute) of a CDF boundary C_t; D = degenerate
@@ -186,13 +192,17 @@ typedef struct {
  * uniforms (u[k] drives the draw). */
 static orc_result orc_verify_probs_seq(const double *const *P, const double *const *Q,
                                        int64_t V, int k, const int32_t *x, const float *u,
-                                       double *alpha_out, double *px_out, double *qx_out) {
+                                       const float *qg, double *alpha_out, double *px_out,
+                                       double *qx_out) {
     orc_result res = {k, -1, 0, 0.0, 0.0};
 
     /* Accept tests in order; stop at the first rejection ([ifdog] three-step
-     * flow step 3; [hw] 二.1 alpha(x) = min(1, p(x)/q(x))). */
+     * flow step 3; [hw] 二.1 alpha(x) = min(1, p(x)/q(x))).  qg != NULL: the
+     * drafter's own q_i(x_i), gathered when it sampled x_i ([hw] 三 drafting
+     * step, [sxl] 基础推测解码器 draft_probs), replaces Q[i][x_i]; the full q
+     * row is then used only for the residual at the rejection. */
     for (int i = 0; i < k; ++i) {
-        double px = P[i][x[i]], qx = Q[i][x[i]];
+        double px = P[i][x[i]], qx = qg ? (double)qg[i] : Q[i][x[i]];
         double ratio = px / qx;
         double alpha = ratio < 1.0 ? ratio : 1.0;
         if (alpha_out) alpha_out[i] = alpha;
@@ -246,7 +256,7 @@ int oracle_verify_probs(const double *Pall, const double *Qall, int64_t V, int32
         for (int i = 0; i < k; ++i) bad |= (x[i] < 0 || x[i] >= V);
         orc_result r = {-1, -1, ORC_FLAG_E, 0.0, 0.0};
         if (!bad)
-            r = orc_verify_probs_seq(P, Q, V, k, x, uniforms + (int64_t)b * (k + 1), NULL,
+            r = orc_verify_probs_seq(P, Q, V, k, x, uniforms + (int64_t)b * (k + 1), NULL, NULL,
                                      NULL, NULL);
         orc_write_tokens(out_tokens + (int64_t)b * (k + 1), k, x, r.n, r.token);
         out_n[b] = r.n;
@@ -268,12 +278,13 @@ int oracle_verify_probs(const double *Pall, const double *Qall, int64_t V, int32
  * (position diagnostics), out_Z/out_gap [B], out_row_max/out_row_sum
  * [2*total+B] (target rows first, then draft rows; NaN where unused).
  * Returns 0, -1 on bad arguments, -2 on allocation failure. */
-int oracle_verify(const void *target, const void *draft, int32_t dtype, int64_t V,
-                  int32_t B, const int32_t *offsets, const int32_t *tokens,
-                  const float *uniforms, const float *temperature, int32_t b_begin,
-                  int32_t b_end, int32_t *out_tokens, int32_t *out_n, int32_t *out_flags,
-                  double *out_alpha, double *out_px, double *out_qx, double *out_Z,
-                  double *out_gap, double *out_row_max, double *out_row_sum) {
+static int orc_verify_range(const void *target, const void *draft, int32_t dtype, int64_t V,
+                            int32_t B, const int32_t *offsets, const int32_t *tokens,
+                            const float *draft_probs, const float *uniforms,
+                            const float *temperature, int32_t b_begin, int32_t b_end,
+                            int32_t *out_tokens, int32_t *out_n, int32_t *out_flags,
+                            double *out_alpha, double *out_px, double *out_qx, double *out_Z,
+                            double *out_gap, double *out_row_max, double *out_row_sum) {
     if (V < 1 || B < 0 || (dtype != 0 && dtype != 1) || b_begin < 0 || b_end > B ||
         b_begin > b_end)
         return -1;
@@ -292,6 +303,11 @@ int oracle_verify(const void *target, const void *draft, int32_t dtype, int64_t 
                    offsets[b + 1] > total);
         const int32_t *x = tokens + drow;
         for (int i = 0; !bad && i < k; ++i) bad |= (x[i] < 0 || x[i] >= V);
+        /* A gathered q(x) must be a probability the drafter could have drawn
+         * x with: finite and > 0 (sampling sequences only). */
+        const float *qg = draft_probs ? draft_probs + drow : NULL;
+        for (int i = 0; !bad && qg && T > 0.0 && i < k; ++i)
+            bad |= !(qg[i] > 0.0f && qg[i] <= 1.0f);
         if (bad) {
             for (int i = 0; k >= 0 && i <= k && i <= ORC_K_MAX; ++i) out[i] = -1;
             out_n[b] = -1;
@@ -344,7 +360,7 @@ int oracle_verify(const void *target, const void *draft, int32_t dtype, int64_t 
             }
         }
         orc_result r = orc_verify_probs_seq(
-            P, Q, V, k, x, uniforms + trow, out_alpha ? out_alpha + drow : NULL,
+            P, Q, V, k, x, uniforms + trow, qg, out_alpha ? out_alpha + drow : NULL,
             out_px ? out_px + drow : NULL, out_qx ? out_qx + drow : NULL);
         orc_write_tokens(out, k, x, r.n, r.token);
         out_n[b] = r.n;
@@ -353,6 +369,91 @@ int oracle_verify(const void *target, const void *draft, int32_t dtype, int64_t 
         if (out_gap) out_gap[b] = r.gap;
     }
     free(buf);
+    return 0;
+}
+
+int oracle_verify(const void *target, const void *draft, int32_t dtype, int64_t V,
+                  int32_t B, const int32_t *offsets, const int32_t *tokens,
+                  const float *uniforms, const float *temperature, int32_t b_begin,
+                  int32_t b_end, int32_t *out_tokens, int32_t *out_n, int32_t *out_flags,
+                  double *out_alpha, double *out_px, double *out_qx, double *out_Z,
+                  double *out_gap, double *out_row_max, double *out_row_sum) {
+    return orc_verify_range(target, draft, dtype, V, B, offsets, tokens, NULL, uniforms,
+                            temperature, b_begin, b_end, out_tokens, out_n, out_flags, out_alpha,
+                            out_px, out_qx, out_Z, out_gap, out_row_max, out_row_sum);
+}
+
+/* The same verify step with the drafter's gathered probabilities:
+ * draft_probs [total] holds q_i(x_i) as the drafter computed it when it
+ * sampled x_i ([hw] 三 drafting step: q_prob.gather; [sxl] 基础推测解码器:
+ * draft_generate returns the gathered probabilities and target_verify divides
+ * by them).  The accept test uses it in place of the draft row's softmax;
+ * the full draft row is needed only at the rejected position, for the
+ * residual ([hw] 三 recomputes q there).  A sampling sequence whose gathered
+ * value is not in (0, 1] is a data error (out_n = -1). */
+int oracle_verify_gathered(const void *target, const void *draft, int32_t dtype, int64_t V,
+                           int32_t B, const int32_t *offsets, const int32_t *tokens,
+                           const float *draft_probs, const float *uniforms,
+                           const float *temperature, int32_t b_begin, int32_t b_end,
+                           int32_t *out_tokens, int32_t *out_n, int32_t *out_flags,
+                           double *out_alpha, double *out_px, double *out_qx, double *out_Z,
+                           double *out_gap) {
+    if (!draft_probs) return -1;
+    return orc_verify_range(target, draft, dtype, V, B, offsets, tokens, draft_probs, uniforms,
+                            temperature, b_begin, b_end, out_tokens, out_n, out_flags, out_alpha,
+                            out_px, out_qx, out_Z, out_gap, NULL, NULL);
+}
+
+/* Draft sampler: the drafter's step that produces each drafted token.  Row
+ * r holds the draft model's logits; T = temperature[r].
+ *   T = 0: x = argmax over the raw logits, lowest id on ties ([ifdog] 动手实践,
+ *          greedy drafting); its probability is reported as 1 (the T -> 0
+ *          limit of softmax(z / T) is a point mass on that id).
+ *   T > 0: q = softmax(z / T) ([ifdog] 动手实践; [hw] 三 and [sxl] use T = 1),
+ *          and x is drawn from q by the same inverse CDF as the verify draws
+ *          (reading R7: x = min{t : C_t > u Z} with u = uniforms[r]); its
+ *          probability q(x) is what the drafter gathers for the verify.
+ *   T < 0 or not finite: data error, x = -1, probability NaN, flag E.
+ * Rows r_begin..r_end-1.  Outputs: out_tokens/out_probs/out_flags [rows];
+ * out_gap [rows] (may be NULL): distance from u Z to the nearest C_t (flag B
+ * below 1e-12).  Returns 0, -1 on bad arguments, -2 on allocation failure. */
+int oracle_draft_sample(const void *logits, int32_t dtype, int64_t V, int32_t rows,
+                        const float *temperature, const float *uniforms, int32_t r_begin,
+                        int32_t r_end, int32_t *out_tokens, double *out_probs,
+                        int32_t *out_flags, double *out_gap) {
+    if (V < 1 || rows < 0 || (dtype != 0 && dtype != 1) || r_begin < 0 || r_end > rows ||
+        r_begin > r_end)
+        return -1;
+    double *q = (double *)malloc(sizeof(double) * (size_t)V);
+    if (!q) return -2;
+    for (int32_t r = r_begin; r < r_end; ++r) {
+        const double T = (double)temperature[r];
+        if (!(T >= 0.0) || isinf(T)) {
+            out_tokens[r] = -1;
+            out_probs[r] = NAN;
+            out_flags[r] = ORC_FLAG_E;
+            if (out_gap) out_gap[r] = NAN;
+            continue;
+        }
+        if (T == 0.0) {
+            int64_t a = 0;
+            orc_row_argmax(logits, dtype, r, V, &a);
+            out_tokens[r] = (int32_t)a;
+            out_probs[r] = 1.0;
+            out_flags[r] = 0;
+            if (out_gap) out_gap[r] = NAN;
+            continue;
+        }
+        double m, S, Z, gap;
+        int degenerate;
+        orc_softmax_row(logits, dtype, r, V, T, q, &m, &S);
+        int64_t t = orc_draw(q, NULL, V, uniforms[r], &Z, &gap, &degenerate);
+        out_tokens[r] = (int32_t)t;
+        out_probs[r] = q[t];
+        out_flags[r] = gap < ORC_CDF_BAND ? ORC_FLAG_B : 0;
+        if (out_gap) out_gap[r] = gap;
+    }
+    free(q);
     return 0;
 }
 

@@ -12,6 +12,7 @@ import os
 import pytest
 
 import oracle
+import test_oracle_draft as dpins
 import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
@@ -30,9 +31,18 @@ MUTANTS = {
     "greedy_tie_highest": ("if (z > best) { best = z; at = v; }", "if (z >= best) { best = z; at = v; }"),
     "greedy_emits_draft": ("orc_write_tokens(out, k, x, n, (int32_t)a);",
                            "orc_write_tokens(out, k, x, n, n < k ? x[n] : (int32_t)a);"),
-    "uniform_slot_draft_layout": ("uniforms + trow, out_alpha", "uniforms + drow, out_alpha"),
+    "uniform_slot_draft_layout": ("uniforms + trow, qg, out_alpha", "uniforms + drow, qg, out_alpha"),
     "bonus_from_draft_row": ("const double *qr = (n < k) ? Q[n] : NULL;",
                              "const double *qr = (n < k) ? Q[n] : (k > 0 ? Q[k - 1] : NULL);"),
+    # drafter-side entry points
+    "gathered_q_ignored": ("double px = P[i][x[i]], qx = qg ? (double)qg[i] : Q[i][x[i]];",
+                           "double px = P[i][x[i]], qx = Q[i][x[i]];"),
+    "gathered_not_checked": ("bad |= !(qg[i] > 0.0f && qg[i] <= 1.0f);", "bad |= 0;"),
+    "draft_prob_of_neighbour": ("out_probs[r] = q[t];", "out_probs[r] = q[t > 0 ? t - 1 : t + 1];"),
+    "draft_untempered": ("orc_softmax_row(logits, dtype, r, V, T, q, &m, &S);",
+                         "orc_softmax_row(logits, dtype, r, V, 1.0, q, &m, &S);"),
+    "draft_greedy_highest_tie": ("orc_row_argmax(logits, dtype, r, V, &a);\n            out_tokens[r] = (int32_t)a;",
+                                 "orc_row_argmax(logits, dtype, r, V, &a);\n            out_tokens[r] = (int32_t)(V - 1 - a);"),
 }
 
 PINS = [
@@ -46,6 +56,10 @@ PINS = [
     lambda: pins.test_lossless_chain_k3(),
     lambda: pins.test_k_zero_emits_bonus_or_argmax(),
     lambda: pins.test_oracle_vs_numpy_composition("c3", 6),
+    lambda: dpins.test_draft_sample_matches_scipy_searchsorted("f32"),
+    lambda: dpins.test_draft_sample_greedy_and_errors(),
+    lambda: dpins.test_gathered_reads_only_the_rejected_draft_row(),
+    lambda: dpins.test_gathered_bad_values_are_data_errors(),
 ]
 
 
