@@ -120,6 +120,49 @@ sv_status_t spec_verify_probs(const void *target_logits, const void *draft_logit
                               float *out_row_max, float *out_row_sumexp, void *workspace,
                               size_t workspace_bytes, hipStream_t stream);
 
+/* The verify step with the drafter's gathered probabilities (page
+ * "大模型推理无损加速:投机采样..." section 三: the draft stage keeps
+ * q_prob.gather(next_token), the accept test divides by it, and the full
+ * draft distribution is rebuilt only at the rejected position; page
+ * "【大模型】- 推测解码" section 基础推测解码器: target_verify(input_ids,
+ * draft_tokens, draft_probs)).
+ *   draft_probs fp32 [total_draft] (slot offsets[b] + i): q_i(x_i) as the
+ *     drafter computed it when it sampled x_i; for sampling sequences it
+ *     must lie in (0, 1], otherwise the sequence is a data error (-1).
+ *     Ignored for greedy sequences.
+ *   out_emit_prob fp32 [B] (may be NULL): the probability of the emitted
+ *     token under the distribution it was drawn from (the residual
+ *     max(0, p_n - q_n)/Z, or p_k for a bonus; 1 for greedy sequences; NaN
+ *     for data errors).
+ * Every other argument and output is as for spec_verify.  Only target rows
+ * and, for each sequence that rejects at position n < k_b, draft row n are
+ * read; early exit (spec_verify_set_early_exit) applies to the target rows.
+ * Always runs in the staged form. */
+sv_status_t spec_verify_gathered(const void *target_logits, const void *draft_logits,
+                                 const int32_t *draft_tokens, const float *draft_probs,
+                                 const int32_t *offsets, int32_t k_uniform, int64_t total_draft,
+                                 int32_t B, int64_t V, sv_dtype_t dtype, const float *uniforms,
+                                 const float *temperature, int32_t *out_tokens,
+                                 int32_t *out_n_accepted, float *out_emit_prob, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/* The drafter's sampling step (page "投机解码", section 动手实践: the draft
+ * model's next token is drawn from softmax(logits / T), or is the argmax at
+ * T = 0; page "大模型推理无损加速:投机采样..." section 三: the drawn token's
+ * probability is gathered for the verify).
+ *   logits [rows, V] (fp32 or bf16, one draft-model row per sequence);
+ *   temperature fp32 [rows] (0 = greedy); uniforms fp32 [rows] in [0, 1).
+ *   out_tokens int32 [rows]: x = min{t : sum_{v<=t} q_v > u} (the same fp64
+ *     inverse CDF over ascending ids as the verify's draws), the lowest-id
+ *     argmax at T = 0, -1 for an unusable temperature;
+ *   out_probs fp32 [rows] (may be NULL): q(x) (1 at T = 0, NaN on error) --
+ *     the draft_probs of spec_verify_gathered.
+ * Workspace as for spec_verify with B = rows and total_draft = 0. */
+sv_status_t spec_draft_sample(const void *logits, int32_t rows, int64_t V, sv_dtype_t dtype,
+                              const float *temperature, const float *uniforms,
+                              int32_t *out_tokens, float *out_probs, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *spec_verify_status_string(sv_status_t status);
 
@@ -140,12 +183,13 @@ void spec_verify_release(void);
  * call over the recorded calls that launched the kernel (ms[i] belongs to
  * spec_verify_kernel_name(i); NaN for kernels not selected or not launched:
  * the staged form launches row_lead and accept_lead (early exit only),
- * row_stats, accept, draw_sums and draw_pick, the fused form fused_reset
- * and fused); it returns the number of kernels, or -1 if the probe is off,
- * no call was recorded or a HIP call failed.
+ * row_stats, accept, row_draft (gathered form only), draw_sums and
+ * draw_pick, the fused form fused_reset and fused); it returns the number
+ * of kernels, or -1 if the probe is off, no call was recorded or a HIP call
+ * failed.
  * spec_verify_timing returns SV_ERR_SHAPE for every < 1.  The probe uses
  * one device: turn it off and on again after switching devices. */
-#define SV_TIME_ALL 0xFF
+#define SV_TIME_ALL 0x1FF
 sv_status_t spec_verify_timing(int32_t kernels, int32_t every);
 int32_t spec_verify_kernel_times(float *ms, int32_t max_kernels);
 const char *spec_verify_kernel_name(int32_t i);

@@ -14,7 +14,8 @@ from ._lib import (LIB_PATH, SV_BF16, SV_F32, SV_K_MAX, SV_MODE_AUTO, SV_MODE_FU
                    SV_TIME_ALL, SpecVerifyError, check, lib)
 
 __all__ = [
-    "spec_verify", "spec_verify_probs", "spec_verify_workspace_size", "spec_verify_release",
+    "spec_verify", "spec_verify_probs", "spec_verify_gathered", "spec_draft_sample",
+    "spec_verify_workspace_size", "spec_verify_release",
     "timing", "kernel_times", "set_geometry", "set_mode", "set_early_exit", "SpecVerifyError", "SV_F32", "SV_BF16",
     "SV_K_MAX", "SV_MODE_AUTO", "SV_MODE_STAGED", "SV_MODE_FUSED", "LIB_PATH", "lib",
 ]
@@ -129,6 +130,63 @@ def spec_verify_probs(target_logits, draft_logits, draft_tokens, offsets, unifor
         ws_bytes, _stream(dev, stream))
     check(st, "spec_verify_probs")
     return dict(tokens=out_tokens, n=out_n, p=out_p, q=out_q, row_max=row_max, row_sumexp=row_sum)
+
+
+def spec_verify_gathered(target_logits, draft_logits, draft_tokens, draft_probs, offsets, uniforms,
+                         temperature, *, k_uniform: int = 0, out_tokens=None, out_n_accepted=None,
+                         out_emit_prob=None, workspace=None, stream=None):
+    """spec_verify with the drafter's gathered q_i(x_i) (``draft_probs``,
+    float32 [total]); returns (out_tokens, out_n_accepted, out_emit_prob [B]
+    float32: the emitted token's probability under its draw)."""
+    import torch
+    dev, V, B, total, out_tokens, out_n_accepted = _prepare(
+        target_logits, draft_logits, draft_tokens, offsets, uniforms, temperature, k_uniform,
+        out_tokens, out_n_accepted)
+    _need(draft_probs, "draft_probs", torch.float32, dev)
+    if draft_probs.numel() != total:
+        raise ValueError(f"draft_probs must have {total} entries")
+    if out_emit_prob is None:
+        out_emit_prob = torch.empty(B, dtype=torch.float32, device=dev)
+    _need(out_emit_prob, "out_emit_prob", torch.float32, dev)
+    if out_emit_prob.numel() != B:
+        raise ValueError(f"out_emit_prob must have {B} entries")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().spec_verify_gathered(
+        _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(draft_probs),
+        _ptr(offsets), int(k_uniform), total, B, V, _dtype_code(target_logits.dtype),
+        _ptr(uniforms), _ptr(temperature), _ptr(out_tokens), _ptr(out_n_accepted),
+        _ptr(out_emit_prob), _ptr(workspace), ws_bytes, _stream(dev, stream))
+    check(st, "spec_verify_gathered")
+    return out_tokens, out_n_accepted, out_emit_prob
+
+
+def spec_draft_sample(logits, temperature, uniforms, *, out_tokens=None, out_probs=None,
+                      workspace=None, stream=None):
+    """The drafter's sampling step over ``logits`` [rows, V] (float32 or
+    bfloat16): returns (tokens [rows] int32, probs [rows] float32 = q(x))."""
+    import torch
+    dev = logits.device
+    if dev.type != "cuda" or logits.dim() != 2 or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous [rows, V] GPU tensor")
+    rows, V = int(logits.shape[0]), int(logits.shape[1])
+    _need(temperature, "temperature", torch.float32, dev)
+    _need(uniforms, "uniforms", torch.float32, dev)
+    if temperature.numel() != rows or uniforms.numel() != rows:
+        raise ValueError(f"temperature and uniforms must have {rows} entries")
+    if out_tokens is None:
+        out_tokens = torch.empty(rows, dtype=torch.int32, device=dev)
+    if out_probs is None:
+        out_probs = torch.empty(rows, dtype=torch.float32, device=dev)
+    _need(out_tokens, "out_tokens", torch.int32, dev)
+    _need(out_probs, "out_probs", torch.float32, dev)
+    if out_tokens.numel() != rows or out_probs.numel() != rows:
+        raise ValueError("out_tokens / out_probs have the wrong size")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().spec_draft_sample(_ptr(logits), rows, V, _dtype_code(logits.dtype), _ptr(temperature),
+                                 _ptr(uniforms), _ptr(out_tokens), _ptr(out_probs), _ptr(workspace),
+                                 ws_bytes, _stream(dev, stream))
+    check(st, "spec_draft_sample")
+    return out_tokens, out_probs
 
 
 def spec_verify_workspace_size(B: int, total_draft: int, V: int, dtype) -> int:

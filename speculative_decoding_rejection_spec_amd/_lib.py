@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 
 SV_F32, SV_BF16 = 0, 1
 SV_K_MAX = 63
-SV_TIME_ALL = 0xFF
+SV_TIME_ALL = 0x1FF
 SV_MODE_AUTO, SV_MODE_STAGED, SV_MODE_FUSED = 0, 1, 2
 STATUS = {0: "SV_OK", -1: "SV_ERR_NULL", -2: "SV_ERR_SHAPE", -3: "SV_ERR_DTYPE",
           -4: "SV_ERR_ALIGN", -5: "SV_ERR_WORKSPACE", -6: "SV_ERR_HIP"}
@@ -28,6 +28,9 @@ SIGNATURES = {
                            _P, _SZ, _P]),
     "spec_verify_probs": (_I32, [_P, _P, _P, _P, _I32, _I64, _I32, _I64, _I32, _P, _P, _P,
                                  _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "spec_verify_gathered": (_I32, [_P, _P, _P, _P, _P, _I32, _I64, _I32, _I64, _I32, _P, _P, _P,
+                                    _P, _P, _P, _SZ, _P]),
+    "spec_draft_sample": (_I32, [_P, _I32, _I64, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "spec_verify_status_string": (ctypes.c_char_p, [_I32]),
     "spec_verify_release": (None, []),
     "spec_verify_timing": (_I32, [_I32, _I32]),

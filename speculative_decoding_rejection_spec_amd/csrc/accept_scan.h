@@ -90,21 +90,27 @@ __device__ __forceinline__ void accept_sequence(const Problem& p, const Plan& pl
     bool ok = o >= 0 && k64 >= 0 && k64 <= kKMax && o1 <= p.total && temperature_ok(Tf);
     const int k = ok ? static_cast<int>(k64) : 0;
     const bool greedy = (Tf == 0.f);
+    const bool gathered = p.draft_probs != nullptr;   // q_i(x_i) from the drafter
     const float c = greedy ? 0.f : row_scale(Tf);
     const int64_t trow = o + b + lane;             // this lane's target row
     const int64_t drow = o + lane;                 // this lane's draft row
 
     int32_t x = -1;
+    float qg = NAN;
     if (ok && lane < k) {
         x = p.tokens[drow];
         if (x < 0 || x >= p.V) ok = false;
+        if (gathered && !greedy) {
+            qg = p.draft_probs[drow];
+            if (!(qg > 0.f && qg <= 1.f)) ok = false;   // not a probability x could be drawn with
+        }
     }
     RowStat rt{0.f, 0, 0.f, 1.0}, rd{0.f, 0, 0.f, 1.0};
     const bool read = lane < limit;                // this position's rows have been read
     if (ok && lane <= k && read) {
         rt = merge_row<kCo>(plan.seg + trow * plan.nseg, plan.nseg, greedy);
         if (!(fabsf(rt.m) <= 3.4e38f)) ok = false;
-        if (!greedy && lane < k) {
+        if (!greedy && !gathered && lane < k) {
             rd = merge_row<kCo>(plan.seg + (ntarget + drow) * plan.nseg, plan.nseg, false);
             if (!(fabsf(rd.m) <= 3.4e38f)) ok = false;
         }
@@ -118,6 +124,7 @@ __device__ __forceinline__ void accept_sequence(const Problem& p, const Plan& pl
             for (int64_t i = lane; i <= k64; i += 64) p.out_tokens[o + b + i] = -1;
         if (lane == 0) {
             p.out_n[b] = -1;
+            if (p.out_emit_prob) p.out_emit_prob[b] = NAN;
             st_co<kCo>(&plan.task[b].kind, static_cast<int32_t>(kNone));
             if (done) *done = 1;
         }
@@ -131,9 +138,13 @@ __device__ __forceinline__ void accept_sequence(const Problem& p, const Plan& pl
             reject = (x != rt.arg);
         } else {
             const double zt = ld_co<kCo>(&plan.xlogit[trow]);       // captured by the row pass
-            const double zd = ld_co<kCo>(&plan.xlogit[ntarget + drow]);
             px = exp2(zt * c - rt.R) / rt.S;
-            qx = exp2(zd * c - rd.R) / rd.S;
+            if (gathered) {
+                qx = qg;
+            } else {
+                const double zd = ld_co<kCo>(&plan.xlogit[ntarget + drow]);
+                qx = exp2(zd * c - rd.R) / rd.S;
+            }
             const double alpha = fmin(1.0, px / qx);
             reject = !(static_cast<double>(p.uniforms[trow]) < alpha);
         }
@@ -144,7 +155,7 @@ __device__ __forceinline__ void accept_sequence(const Problem& p, const Plan& pl
             if (lane == 0) *done = 0;
             // List the remaining row segments: target rows limit..k, then
             // (sampling) draft rows limit..k-1, each in nseg segments.
-            const int32_t nt = k - limit + 1, nd = greedy ? 0 : k - limit;
+            const int32_t nt = k - limit + 1, nd = (greedy || gathered) ? 0 : k - limit;
             const int32_t cnt = (nt + nd) * plan.nseg;
             uint32_t base = 0;
             if (lane == 0) base = atomicAdd(plan.rest_n, static_cast<uint32_t>(cnt));
@@ -171,8 +182,24 @@ __device__ __forceinline__ void accept_sequence(const Problem& p, const Plan& pl
     if (lane <= k && (lane != n || greedy)) p.out_tokens[trow] = lane < n ? x : (lane == n ? rt.arg : -1);
     if (lane == n) {
         p.out_n[b] = n;
+        if (greedy && p.out_emit_prob) p.out_emit_prob[b] = 1.f;   // the T -> 0 limit: a point mass
+        // Gathered form: draft row n has not been read; list it, and leave
+        // log2 S_p in theta until its statistics resolve the task.
+        const bool pending = gathered && !greedy && n < k;
+        if (pending) {
+            const uint32_t base = atomicAdd(plan.dlist_n, static_cast<uint32_t>(plan.nseg));
+            for (int32_t sg = 0; sg < plan.nseg; ++sg) {
+                RestItem it;
+                it.b = b;
+                it.is_target = 0;
+                it.row = static_cast<int32_t>(drow);
+                it.seg = sg;
+                plan.dlist[base + sg] = it;
+            }
+        }
         DrawTask* t = plan.task + b;
-        st_co<kCo>(&t->kind, static_cast<int32_t>(greedy ? kNone : (n < k ? kResidual : kBonus)));
+        st_co<kCo>(&t->kind, static_cast<int32_t>(greedy ? kNone : (n < k ? (pending ? kResidualPending : kResidual)
+                                                                          : kBonus)));
         st_co<kCo>(&t->out_slot, static_cast<int32_t>(trow));
         st_co<kCo>(&t->trow, trow);
         st_co<kCo>(&t->drow, drow);
@@ -180,25 +207,28 @@ __device__ __forceinline__ void accept_sequence(const Problem& p, const Plan& pl
         st_co<kCo>(&t->m_d, n < k ? rd.m : 0.f);
         st_co<kCo>(&t->T, Tf);
         st_co<kCo>(&t->u, p.uniforms[o + b + k]);
-        st_co<kCo>(&t->theta, (!greedy && n < k) ? log2_norm(rt, c) - log2_norm(rd, c) : 0.0);
+        st_co<kCo>(&t->theta, (!greedy && n < k) ? log2_norm(rt, c) - (pending ? 0.0 : log2_norm(rd, c)) : 0.0);
     }
     if (p.out_p && lane < k) {
         p.out_p[drow] = static_cast<float>(px);
         p.out_q[drow] = static_cast<float>(qx);
     }
     if (p.out_row_max && lane <= k) {
+        const bool dread = read && !greedy && !gathered;
         p.out_row_max[trow] = read ? rt.m : NAN;
         p.out_row_sum[trow] = (greedy || !read) ? NAN : static_cast<float>(exp2(log2_norm(rt, c)));
         if (lane < k) {
-            p.out_row_max[ntarget + drow] = (greedy || !read) ? NAN : rd.m;
-            p.out_row_sum[ntarget + drow] = (greedy || !read) ? NAN : static_cast<float>(exp2(log2_norm(rd, c)));
+            p.out_row_max[ntarget + drow] = dread ? rd.m : NAN;
+            p.out_row_sum[ntarget + drow] = dread ? static_cast<float>(exp2(log2_norm(rd, c))) : NAN;
         }
     }
 }
 
-// The DrawTask of sequence b as written by accept_sequence.
+// The DrawTask of sequence b as written by accept_sequence; a pending
+// residual of the gathered form is completed from its draft row's SegStats
+// (read after the accept scan): its maximum, and theta = log2 S_p - log2 S_q.
 template <bool kCo>
-__device__ __forceinline__ DrawTask load_task(const Plan& plan, int32_t b) {
+__device__ __forceinline__ DrawTask load_task(const Problem& p, const Plan& plan, int32_t b) {
     const DrawTask* t = plan.task + b;
     DrawTask r;
     r.kind = ld_co<kCo>(&t->kind);
@@ -210,6 +240,12 @@ __device__ __forceinline__ DrawTask load_task(const Plan& plan, int32_t b) {
     r.T = ld_co<kCo>(&t->T);
     r.u = ld_co<kCo>(&t->u);
     r.theta = ld_co<kCo>(&t->theta);
+    if (r.kind == kResidualPending) {
+        const RowStat rd = merge_row<kCo>(plan.seg + (p.total + p.B + r.drow) * plan.nseg, plan.nseg, false);
+        r.m_d = rd.m;
+        r.theta -= log2_norm(rd, row_scale(r.T));
+        r.kind = kResidual;
+    }
     return r;
 }
 

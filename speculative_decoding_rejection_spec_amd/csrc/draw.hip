@@ -17,7 +17,7 @@ __global__ __launch_bounds__(kThreads) void draw_sums_kernel(Problem p, Plan pla
     __shared__ drawpass::TabEntry tbl[256];
     __shared__ DrawLds lds;
     load_exp2_table(tbl, kThreads);            // overlaps the task load
-    const DrawTask task = load_task<false>(plan, b);
+    const DrawTask task = load_task<false>(p, plan, b);
     if (task.kind == kNone) return;            // the whole workgroup leaves
     __syncthreads();
     draw_chunk<DT, false>(p, plan, task, b, c, tbl, lds);
@@ -29,7 +29,7 @@ __global__ __launch_bounds__(kPickThreads) void draw_pick_kernel(Problem p, Plan
     __shared__ drawpass::TabEntry tbl[256];
     __shared__ PickLds<kPickThreads> lds;
     load_exp2_table(tbl, kPickThreads);
-    const DrawTask task = load_task<false>(plan, b);
+    const DrawTask task = load_task<false>(p, plan, b);
     if (task.kind == kNone) return;
     __syncthreads();
     pick_sequence<DT, kPickThreads, false>(p, plan, task, b, tbl, lds);

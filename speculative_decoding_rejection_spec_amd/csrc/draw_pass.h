@@ -362,7 +362,7 @@ struct PickLds {
     int32_t ldsi[kW];
     double mass[MAXC];
     double spc[MAXC];
-    double base, target;
+    double base, target, Z;
     int32_t chunk, resid, rescan;
 };
 
@@ -574,6 +574,7 @@ __device__ __forceinline__ void pick_sequence(const Problem& p, const Plan& plan
         if (!resid) find_chunk(L.spc, nchunk, static_cast<double>(task.u), &Z, &chunk, &base);
         if (tid == 0) {
             L.base = base;
+            L.Z = Z;
             L.target = static_cast<double>(task.u) * Z;
             L.chunk = chunk;
             L.resid = resid;
@@ -637,6 +638,12 @@ __device__ __forceinline__ void pick_sequence(const Problem& p, const Plan& plan
     if (tid == 0) {
         if (pick == INT32_MAX) pick = last_pos >= 0 ? last_pos : static_cast<int32_t>(c0);
         p.out_tokens[task.out_slot] = pick;
+        if (p.out_emit_prob) {
+            // its probability under the distribution it was drawn from
+            const double wt = rows.wt(rows.zt(pick));
+            const double mass = resid ? fmax(0.0, wt * iSp - rows.wd(rows.zd(pick)) * iSq) : wt;
+            p.out_emit_prob[b] = static_cast<float>(mass / L.Z);
+        }
     }
 }
 

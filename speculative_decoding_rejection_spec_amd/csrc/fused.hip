@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kThreads, kFusedWavesPerEU) void fused_kernel(Probl
             }
             __syncthreads();
             if (!L.flag) continue;
-            const DrawTask task = load_task<true>(plan, b);
+            const DrawTask task = load_task<true>(p, plan, b);
             if (task.kind == kNone) continue;
             do_chunk<DT>(p, plan, task, b, c, L.tbl, L.u.draw);
             wait_stores();

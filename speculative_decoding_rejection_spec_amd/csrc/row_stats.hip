@@ -10,7 +10,12 @@
 // rejection, so rows after it are never needed (page "投机解码", section
 // 投机解码的三步流程, step 3; page "大模型推理无损加速:投机采样...", section 三).
 // row_lead reads the leading positions of every sequence; after their accept
-// scan, row_stats reads the rest only for sequences still undecided.
+// scan, row_list reads the rest only for sequences still undecided.
+//
+// Gathered form (the drafter hands over q_i(x_i), page
+// "大模型推理无损加速:投机采样..." section 三): the accept tests need no draft
+// rows, so the passes above read target rows only, and row_list then reads
+// the one draft row at each rejection, for the residual.
 #include "row_pass.h"
 
 namespace sv {
@@ -21,26 +26,34 @@ __device__ __forceinline__ int64_t first_slot(const Problem& p, int32_t b) {
     return p.offsets ? static_cast<int64_t>(p.offsets[b]) : static_cast<int64_t>(b) * p.k_uniform;
 }
 
-// All rows, or with early exit the row segments the leading positions left
-// to read (listed by the lead accept scan; workgroups past the end of the
-// list return at once).
+// Every needed row in one pass (draft rows only when the accept tests need
+// their softmax, i.e. not in the gathered form).
 template <int DT>
 __global__ __launch_bounds__(kThreads) void row_stats_kernel(Problem p, Plan plan) {
     const int64_t w = blockIdx.x;
+    if (w == 0 && threadIdx.x == 0) *plan.dlist_n = 0;   // the accept scan fills the draft list
     __shared__ RowLds lds;
-    if (plan.lead > 0) {
-        if (w >= *plan.rest_n) return;
-        const RestItem it = plan.rest[w];
-        row_segment<DT, false>(p, plan, it.b, it.is_target != 0, it.row, it.seg, lds);
-        return;
-    }
     const int64_t row_all = w / plan.nseg;
     const int64_t seg = w - row_all * plan.nseg;
     const int64_t ntarget = p.total + p.B;
     const bool is_target = row_all < ntarget;
     const int64_t r = is_target ? row_all : row_all - ntarget;
+    if (!is_target && p.draft_probs) return;
     const int32_t b = is_target ? seq_of_target_row(p, r) : seq_of_draft_row(p, r);
     row_segment<DT, false>(p, plan, b, is_target, r, seg, lds);
+}
+
+// The row segments of a list built by an accept scan: with early exit the
+// rows the leading positions left to read, in the gathered form the draft
+// rows at rejections.  Workgroups past the end of the list return at once.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void row_list_kernel(Problem p, Plan plan, const RestItem* list,
+                                                            const uint32_t* count) {
+    const int64_t w = blockIdx.x;
+    if (w >= *count) return;
+    const RestItem it = list[w];
+    __shared__ RowLds lds;
+    row_segment<DT, false>(p, plan, it.b, it.is_target != 0, it.row, it.seg, lds);
 }
 
 // Early exit, first round: the rows of positions < lead of every sequence.
@@ -49,7 +62,10 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(Problem p, Plan pla
 // no usable range) returns at once.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void row_lead_kernel(Problem p, Plan plan) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) *plan.rest_n = 0;   // the lead accept scan fills the list
+    if (blockIdx.x == 0 && threadIdx.x == 0) {                   // the accept scans fill the lists
+        *plan.rest_n = 0;
+        *plan.dlist_n = 0;
+    }
     int64_t q = blockIdx.x;
     const int64_t seg = q % plan.nseg;
     q /= plan.nseg;
@@ -61,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void row_lead_kernel(Problem p, Plan plan
     const int64_t o1 = p.offsets ? static_cast<int64_t>(p.offsets[b + 1]) : o + p.k_uniform;
     if (!(o >= 0 && o1 >= o && o1 - o <= kKMax && o1 <= p.total)) return;
     const int64_t k = o1 - o;
-    if (is_target ? i > k : i >= k) return;
+    if (is_target ? i > k : (i >= k || p.draft_probs)) return;
     __shared__ RowLds lds;
     row_segment<DT, false>(p, plan, b, is_target, is_target ? o + b + i : o + i, seg, lds);
 }
@@ -75,6 +91,16 @@ hipError_t launch_row_stats(const Problem& p, const Plan& plan, hipStream_t s) {
         row_stats_kernel<SV_BF16><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s>>>(p, plan);
     else
         row_stats_kernel<SV_F32><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s>>>(p, plan);
+    return hipGetLastError();
+}
+
+hipError_t launch_row_list(const Problem& p, const Plan& plan, const RestItem* list, const uint32_t* count,
+                           int64_t max_items, hipStream_t s) {
+    if (max_items == 0) return hipSuccess;
+    if (p.dtype == SV_BF16)
+        row_list_kernel<SV_BF16><<<dim3(static_cast<uint32_t>(max_items)), dim3(kThreads), 0, s>>>(p, plan, list, count);
+    else
+        row_list_kernel<SV_F32><<<dim3(static_cast<uint32_t>(max_items)), dim3(kThreads), 0, s>>>(p, plan, list, count);
     return hipGetLastError();
 }
 

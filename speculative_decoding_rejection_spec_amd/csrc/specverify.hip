@@ -24,11 +24,13 @@ constexpr int32_t kAutoLead = -1;
 constexpr int64_t kAutoLeadBytes = 512ll << 20;
 constexpr int64_t kMaxChunks = 1024;          // draw chunks per row (the pick keeps them in LDS)
 constexpr int kMaxDevices = 64;
-constexpr int kNumKernels = 8;
-enum { kKRowStats, kKAccept, kKDrawSums, kKDrawPick, kKFusedReset, kKFused, kKRowLead, kKAcceptLead };
+constexpr int kNumKernels = 9;
+enum { kKRowStats, kKAccept, kKDrawSums, kKDrawPick, kKFusedReset, kKFused, kKRowLead, kKAcceptLead,
+       kKRowDraft };
 
-const char* const kKernelNames[kNumKernels] = {"row_stats", "accept", "draw_sums", "draw_pick",
-                                               "fused_reset", "fused", "row_lead", "accept_lead"};
+const char* const kKernelNames[kNumKernels] = {"row_stats", "accept",      "draw_sums",
+                                               "draw_pick", "fused_reset", "fused",
+                                               "row_lead",  "accept_lead", "row_draft"};
 
 std::mutex g_mutex;
 int64_t g_seg_elems = kDefaultSegElems;
@@ -40,6 +42,7 @@ int32_t g_lead = kAutoLead;                  // early exit: leading positions re
 int32_t effective_lead(int64_t B, int64_t total, int64_t V, sv_dtype_t dtype) {
     if (g_mode == SV_MODE_FUSED) return 0;      // the fused form reads every row
     if (g_lead != kAutoLead) return g_lead;
+    if (total == 0) return 0;                    // only bonus rows: nothing to skip
     const int64_t bytes = (2 * total + B) * V * (dtype == SV_BF16 ? 2 : 4);
     return bytes >= kAutoLeadBytes ? 1 : 0;
 }
@@ -66,7 +69,7 @@ struct Geometry {
     int32_t nseg, nchunk;
     int64_t seg_len, chunk_len;
     size_t off_seg, off_task, off_csum, off_band_n, off_band_w, off_xlogit, off_ctr, off_done, off_rest,
-        off_rest_n, bytes;
+        off_rest_n, off_dlist, off_dlist_n, off_nbuf, bytes;
 };
 
 // Splits a row of V logits into n <= max_pieces pieces of about `target`
@@ -107,6 +110,12 @@ bool make_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dtype, int64_
     off = align256(off + sizeof(RestItem) * static_cast<size_t>(rows) * g.nseg);
     g.off_rest_n = off;
     off = align256(off + sizeof(uint32_t));
+    g.off_dlist = off;
+    off = align256(off + sizeof(RestItem) * static_cast<size_t>(B) * g.nseg);
+    g.off_dlist_n = off;
+    off = align256(off + sizeof(uint32_t));
+    g.off_nbuf = off;                                   // accept counts of spec_draft_sample
+    off = align256(off + sizeof(int32_t) * static_cast<size_t>(B));
     g.bytes = off;
     return true;
 }
@@ -183,6 +192,10 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     plan.done = reinterpret_cast<int32_t*>(ws + g.off_done);
     plan.rest = reinterpret_cast<RestItem*>(ws + g.off_rest);
     plan.rest_n = reinterpret_cast<uint32_t*>(ws + g.off_rest_n);
+    plan.dlist = reinterpret_cast<RestItem*>(ws + g.off_dlist);
+    plan.dlist_n = reinterpret_cast<uint32_t*>(ws + g.off_dlist_n);
+    Problem pr = p;
+    if (!pr.out_n) pr.out_n = reinterpret_cast<int32_t*>(ws + g.off_nbuf);
 
     // The fused form needs the schedule prefix and the pick's chunk masses
     // in LDS, and an item count below 2^31.
@@ -191,7 +204,9 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     const bool fused_fits = p.B <= kFusedMaxB && g.nchunk <= kFusedMaxChunks && max_items < (1ll << 31);
     // The fused form measured slower than the staged one on MI355X (see
     // fused.hip), so it runs only when asked for.
-    const bool fused = g_mode == SV_MODE_FUSED;
+    // The gathered form reads draft rows after the accept scans, which only
+    // the staged form does.
+    const bool fused = g_mode == SV_MODE_FUSED && !p.draft_probs;
     if (fused && !fused_fits) return SV_ERR_SHAPE;
     plan.lead = fused ? 0 : effective_lead(p.B, p.total, p.V, static_cast<sv_dtype_t>(p.dtype));
     Fused f{};
@@ -234,17 +249,28 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
         if (timed) recorded |= 1u << i;
         return true;
     };
+    const int64_t all_items = (2 * p.total + p.B) * static_cast<int64_t>(g.nseg);
     bool ok;
     if (fused) {
-        ok = launch(kKFusedReset, [&] { return launch_fused_reset(p, plan, stream); }) &&
-             launch(kKFused, [&] { return launch_fused(p, plan, f, stream); });
+        ok = launch(kKFusedReset, [&] { return launch_fused_reset(pr, plan, stream); }) &&
+             launch(kKFused, [&] { return launch_fused(pr, plan, f, stream); });
     } else {
-        ok = (plan.lead == 0 || (launch(kKRowLead, [&] { return launch_row_lead(p, plan, stream); }) &&
-                                 launch(kKAcceptLead, [&] { return launch_accept_lead(p, plan, stream); }))) &&
-             launch(kKRowStats, [&] { return launch_row_stats(p, plan, stream); }) &&
-             launch(kKAccept, [&] { return launch_accept(p, plan, stream); }) &&
-             launch(kKDrawSums, [&] { return launch_draw_sums(p, plan, stream); }) &&
-             launch(kKDrawPick, [&] { return launch_draw_pick(p, plan, stream); });
+        // Row pass: one pass over every needed row, or (early exit) the
+        // leading positions, their accept scan, then the listed remainder.
+        if (plan.lead > 0)
+            ok = launch(kKRowLead, [&] { return launch_row_lead(pr, plan, stream); }) &&
+                 launch(kKAcceptLead, [&] { return launch_accept_lead(pr, plan, stream); }) &&
+                 launch(kKRowStats, [&] { return launch_row_list(pr, plan, plan.rest, plan.rest_n, all_items, stream); });
+        else
+            ok = launch(kKRowStats, [&] { return launch_row_stats(pr, plan, stream); });
+        ok = ok && launch(kKAccept, [&] { return launch_accept(pr, plan, stream); });
+        // Gathered form: the draft rows at the rejections.
+        if (ok && pr.draft_probs)
+            ok = launch(kKRowDraft, [&] {
+                return launch_row_list(pr, plan, plan.dlist, plan.dlist_n, static_cast<int64_t>(p.B) * g.nseg, stream);
+            });
+        ok = ok && launch(kKDrawSums, [&] { return launch_draw_sums(pr, plan, stream); }) &&
+             launch(kKDrawPick, [&] { return launch_draw_pick(pr, plan, stream); });
     }
     if (ev) {
         g_ev_mask[g_timed_calls % kTimedCalls] = recorded;
@@ -296,6 +322,8 @@ sv_status_t spec_verify_probs(const void* target_logits, const void* draft_logit
     p.out_q = out_q;
     p.out_row_max = out_row_max;
     p.out_row_sum = out_row_sumexp;
+    p.draft_probs = nullptr;
+    p.out_emit_prob = nullptr;
     p.V = V;
     p.total = total_draft;
     p.B = B;
@@ -314,6 +342,68 @@ sv_status_t spec_verify(const void* target_logits, const void* draft_logits,
                              total_draft, B, V, dtype, uniforms, temperature, out_tokens,
                              out_n_accepted, nullptr, nullptr, nullptr, nullptr, workspace,
                              workspace_bytes, stream);
+}
+
+sv_status_t spec_verify_gathered(const void* target_logits, const void* draft_logits,
+                                 const int32_t* draft_tokens, const float* draft_probs,
+                                 const int32_t* offsets, int32_t k_uniform, int64_t total_draft,
+                                 int32_t B, int64_t V, sv_dtype_t dtype, const float* uniforms,
+                                 const float* temperature, int32_t* out_tokens,
+                                 int32_t* out_n_accepted, float* out_emit_prob, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+    sv_status_t st = check_args(target_logits, draft_logits, draft_tokens, offsets, k_uniform,
+                                total_draft, B, V, dtype, uniforms, temperature, out_tokens,
+                                out_n_accepted);
+    if (st != SV_OK) return st;
+    if (total_draft > 0 && !draft_probs) return SV_ERR_NULL;
+    if (!aligned(draft_probs, 4) || !aligned(out_emit_prob, 4)) return SV_ERR_ALIGN;
+    Problem p{};
+    p.target = target_logits;
+    p.draft = draft_logits;
+    p.tokens = draft_tokens;
+    p.offsets = offsets;
+    p.uniforms = uniforms;
+    p.temperature = temperature;
+    p.out_tokens = out_tokens;
+    p.out_n = out_n_accepted;
+    p.draft_probs = total_draft > 0 ? draft_probs : nullptr;
+    p.out_emit_prob = out_emit_prob;
+    p.V = V;
+    p.total = total_draft;
+    p.B = B;
+    p.k_uniform = offsets ? 0 : k_uniform;
+    p.dtype = dtype;
+    return run(p, workspace, workspace_bytes, stream);
+}
+
+sv_status_t spec_draft_sample(const void* logits, int32_t rows, int64_t V, sv_dtype_t dtype,
+                              const float* temperature, const float* uniforms, int32_t* out_tokens,
+                              float* out_probs, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+    // A verify of `rows` sequences with no drafted tokens: each row is the
+    // bonus row of its sequence, so its token is drawn from softmax(z / T)
+    // by the verify's inverse CDF (or is the argmax at T = 0).
+    if (rows < 0) return SV_ERR_SHAPE;
+    if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
+    if (!logits || !temperature || !uniforms || !out_tokens) return SV_ERR_NULL;
+    if (V < 1 || V > 0x7FFFFFFFll) return SV_ERR_SHAPE;
+    const size_t elt = dtype == SV_BF16 ? 2 : 4;
+    if (!aligned(logits, elt) || !aligned(temperature, 4) || !aligned(uniforms, 4) ||
+        !aligned(out_tokens, 4) || !aligned(out_probs, 4))
+        return SV_ERR_ALIGN;
+    Problem p{};
+    p.target = logits;
+    p.uniforms = uniforms;
+    p.temperature = temperature;
+    p.out_tokens = out_tokens;
+    p.out_n = nullptr;                           // the workspace holds the (zero) counts
+    p.out_emit_prob = out_probs;
+    p.V = V;
+    p.total = 0;
+    p.B = rows;
+    p.k_uniform = 0;
+    p.dtype = dtype;
+    return run(p, workspace, workspace_bytes, stream);
 }
 
 const char* spec_verify_status_string(sv_status_t status) {

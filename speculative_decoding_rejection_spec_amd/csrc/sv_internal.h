@@ -47,7 +47,10 @@ struct SegStat {
     double s;      // sampling rows: sum over the segment of 2^(z*c - R)
 };
 
-enum : int32_t { kNone = 0, kResidual = 1, kBonus = 2 };
+// kResidualPending: a residual draw of the gathered form, whose draft row n
+// is read after the accept scan (its maximum and normaliser come from that
+// row's SegStats; DrawTask::theta holds log2 S_p until then).
+enum : int32_t { kNone = 0, kResidual = 1, kBonus = 2, kResidualPending = 3 };
 
 // The draw one sequence still needs after the accept scan.
 struct DrawTask {
@@ -90,6 +93,8 @@ struct Problem {
     float* out_q;
     float* out_row_max;
     float* out_row_sum;
+    const float* draft_probs; // gathered form: [total] q_i(x_i) from the drafter (nullptr otherwise)
+    float* out_emit_prob;     // [B] probability of the emitted token under its draw, may be nullptr
     int64_t V;
     int64_t total;            // total drafted tokens = offsets[B]
     int32_t B;
@@ -114,6 +119,8 @@ struct Plan {
     int32_t* done;       // early exit: [B], 1 once a sequence's outcome is known from its leading positions
     RestItem* rest;      // early exit: [(2 * total + B) * nseg], the row segments still to read
     uint32_t* rest_n;    // early exit: number of entries in rest
+    RestItem* dlist;     // gathered form: [B * nseg], segments of the draft rows at rejections
+    uint32_t* dlist_n;   // gathered form: number of entries in dlist
 };
 
 // Layout of Plan::ctr (fused form), zeroed before every launch.  The queue
@@ -133,6 +140,8 @@ struct Fused {
 
 // Host-side launchers (one per kernel).
 hipError_t launch_row_stats(const Problem& p, const Plan& plan, hipStream_t s);
+hipError_t launch_row_list(const Problem& p, const Plan& plan, const RestItem* list, const uint32_t* count,
+                           int64_t max_items, hipStream_t s);
 hipError_t launch_row_lead(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_accept(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_accept_lead(const Problem& p, const Plan& plan, hipStream_t s);

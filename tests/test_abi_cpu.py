@@ -27,7 +27,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(spec_verify\w*)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(spec_(?:verify|draft)\w*)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported(lib):
