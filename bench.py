@@ -92,6 +92,10 @@ def main():
     ap.add_argument("--mode", choices=["auto", "staged", "fused"], default="auto",
                     help="launch form (auto = staged)")
     ap.add_argument("--lag", type=int, default=0, help="fused form: draw lag in sequences (0 = auto)")
+    ap.add_argument("--entry", choices=["verify", "gathered", "draft"], default="verify",
+                    help="verify: spec_verify; gathered: spec_verify_gathered with the drafts' q(x) "
+                         "(the accept tests need no draft rows); draft: spec_draft_sample over one "
+                         "draft-model row per sequence")
     ap.add_argument("--lead", type=int, default=-1,
                     help="early exit: leading positions read by every sequence (0 = one full pass, "
                          "-1 = the library's choice by batch size)")
@@ -141,10 +145,39 @@ def main():
     ws = torch.empty(sv.spec_verify_workspace_size(w.B, w.total, w.V, sv.SV_BF16 if w.dtype == "bf16"
                                                    else sv.SV_F32), dtype=torch.uint8, device=dev)
 
+    if args.entry == "gathered":
+        # the drafter's gathered q_i(x_i), formed on the device from the draft
+        # rows (input preparation, outside the timed region)
+        for d in copies:
+            tq = d["temperature"].repeat_interleave((d["offsets"][1:] - d["offsets"][:-1]).long())
+            probs = torch.softmax(d["draft"].float() / tq.clamp_min(1e-30)[:, None], dim=-1)
+            d["qg"] = probs.gather(1, d["tokens"].long()[:, None]).squeeze(1).contiguous()
+            del probs
+        emit = torch.empty(w.B, dtype=torch.float32, device=dev)
+    if args.entry == "draft":
+        # one draft-model row per sequence (its first draft row), its T, and
+        # the sequence's first uniform
+        for d in copies:
+            first = d["offsets"][:-1].long()
+            d["drow"] = d["draft"][first].contiguous()
+            d["du"] = d["uniforms"][first + torch.arange(w.B, device=dev)].contiguous()
+        dtok = torch.empty(w.B, dtype=torch.int32, device=dev)
+        dprob = torch.empty(w.B, dtype=torch.float32, device=dev)
+        ws = torch.empty(sv.spec_verify_workspace_size(w.B, 0, w.V, sv.SV_BF16 if w.dtype == "bf16"
+                                                       else sv.SV_F32), dtype=torch.uint8, device=dev)
+
     def step(i):
         d = copies[i % len(copies)]
-        sv.spec_verify(d["target"], d["draft"], d["tokens"], d["offsets"], d["uniforms"],
-                       d["temperature"], out_tokens=out_tok, out_n_accepted=out_n, workspace=ws)
+        if args.entry == "gathered":
+            sv.spec_verify_gathered(d["target"], d["draft"], d["tokens"], d["qg"], d["offsets"],
+                                    d["uniforms"], d["temperature"], out_tokens=out_tok,
+                                    out_n_accepted=out_n, out_emit_prob=emit, workspace=ws)
+        elif args.entry == "draft":
+            sv.spec_draft_sample(d["drow"], d["temperature"], d["du"], out_tokens=dtok, out_probs=dprob,
+                                 workspace=ws)
+        else:
+            sv.spec_verify(d["target"], d["draft"], d["tokens"], d["offsets"], d["uniforms"],
+                           d["temperature"], out_tokens=out_tok, out_n_accepted=out_n, workspace=ws)
 
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -168,6 +201,8 @@ def main():
     # The roofline kernel: the row pass (its two launches with early exit) or
     # the fused kernel.
     roof = ["fused"] if form == "fused" else (["row_lead", "row_stats"] if early else ["row_stats"])
+    if "row_draft" in launched:
+        roof.append("row_draft")
     roof_kernel = "+".join(roof)
 
     # Timed region: HIP events around the roofline kernel(s) only, on one
@@ -196,20 +231,32 @@ def main():
         sv.timing(False)
 
     # Algorithmic bytes from the realised accept counts.
-    n = out_n.cpu().numpy()
     elt = w.elem_bytes
     sampling = w.temperature > 0
-    k = w.k.astype(np.int64)
-    full_rows = int(np.sum(k + 1) + np.sum(k[sampling]))          # every needed row, one pass
-    min_rows = int(np.sum(n + 1) + np.sum(np.minimum(n + 1, k)[sampling]))   # up to the first rejection
+    if args.entry == "draft":
+        # one row per sequence read once, plus its bonus-style draw row
+        k = np.zeros(w.B, np.int64)
+        n = np.zeros(w.B, np.int64)
+    else:
+        k = w.k.astype(np.int64)
+        n = out_n.cpu().numpy().astype(np.int64)
+    gathered = args.entry == "gathered"
+    dsamp = sampling & (not gathered)          # sequences whose accept tests read draft rows
+    full_rows = int(np.sum(k + 1) + np.sum(k[dsamp]))                     # every needed row, one pass
+    min_rows = int(np.sum(n + 1) + np.sum(np.minimum(n + 1, k)[dsamp]))  # up to the first rejection
     if early:
         L = args.lead if args.lead > 0 else 1
-        lead_rows = np.minimum(k, L - 1) + 1 + np.where(sampling, np.minimum(k, L), 0)
+        lead_rows = np.minimum(k, L - 1) + 1 + np.where(dsamp, np.minimum(k, L), 0)
         decided = (n < L) | (k < L)
-        rest_rows = np.where(decided, 0, (k - L + 1) + np.where(sampling, k - L, 0))
+        rest_rows = np.where(decided, 0, (k - L + 1) + np.where(dsamp, k - L, 0))
         read_rows = int(np.sum(lead_rows + rest_rows))
     else:
         read_rows = full_rows
+    if gathered:                                 # the draft row at each rejection
+        extra = int(np.sum(sampling & (n < k)))
+        read_rows += extra
+        min_rows += extra
+        full_rows += extra
     draw_rows = int(np.sum(np.where(sampling, np.where(n < k, 2, 1), 0)))
     row_bytes = w.V * elt
     k1_bytes = read_rows * row_bytes
@@ -232,17 +279,33 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         threads = min(16, os.cpu_count() or 1)
-        tc = time.perf_counter()
-        ref = oracle.verify(w, threads=threads)
-        tc = time.perf_counter() - tc
-        agree = int(np.sum(ref["n"] == n))
-        cpu = {"value": round(w.B / tc, 2), "unit": "sequences/s", "cores": threads,
-               "kind": "oracle", "sample": f"the whole batch ({w.B} sequences) once, "
-               f"fp64 C oracle split over {threads} threads; accept counts agree with the "
+        if args.entry == "draft":
+            first = w.offsets[:-1].astype(np.int64)
+            rows_in = np.ascontiguousarray(w.draft[first])
+            du = copies[0]["du"].cpu().numpy()
+            tc = time.perf_counter()
+            ref = oracle.draft_sample(rows_in, w.temperature, du, threads=threads)
+            tc = time.perf_counter() - tc
+            agree = int(np.sum(ref["tokens"] == dtok.cpu().numpy()))
+            what = "tokens"
+        else:
+            qg = copies[0]["qg"].cpu().numpy() if gathered else None
+            tc = time.perf_counter()
+            ref = oracle.verify(w, threads=threads, draft_probs=qg)
+            tc = time.perf_counter() - tc
+            agree = int(np.sum(ref["n"] == n))
+            what = "accept counts"
+        cpu = {"value": round(w.B / tc, 2), "unit": "rows/s" if args.entry == "draft" else "sequences/s",
+               "cores": threads, "kind": "oracle", "sample": f"the whole batch ({w.B} sequences) once, "
+               f"fp64 C oracle split over {threads} threads; {what} agree with the "
                f"GPU on {agree}/{w.B} sequences"}
 
+    metric = {"verify": METRIC,
+              "gathered": METRIC + " (verify with the drafts' gathered q(x))",
+              "draft": "draft rows sampled/s (spec_draft_sample), one row per sequence"}[args.entry]
     res = {
-        "metric": METRIC, "value": round(seq_per_s, 1), "unit": "sequences/s", "n_gpus": 1,
+        "metric": metric, "value": round(seq_per_s, 1),
+        "unit": "rows/s" if args.entry == "draft" else "sequences/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
@@ -250,7 +313,7 @@ def main():
                    f"V={w.V} {w.dtype} logits", "B": w.B, "V": w.V, "k_max": int(w.k.max()),
                    "total_draft": w.total, "logit_dtype": w.dtype,
                    "temperatures": sorted(set(float(t) for t in w.temperature)),
-                   "input_copies": len(copies), "form": form,
+                   "input_copies": len(copies), "form": form, "entry": args.entry,
                    "early_exit_lead": (args.lead if args.lead > 0 else 1) if early else 0},
         "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
         "algorithmic_bytes": total_bytes, "mean_accepted": round(float(n.mean()), 4),
