@@ -44,7 +44,8 @@ COUNTERS = {"row_stats": os.path.join(ROOT, "profiles", "row_stats_c4_counters.t
             "row_lead+row_stats": os.path.join(ROOT, "profiles", "row_pass_early_exit_c4_counters.txt"),
             "fused": os.path.join(ROOT, "profiles", "fused_c4_counters.txt")}
 KERNEL_SOURCES = {"row_stats": ["row_stats.hip", "row_pass.h", "sv_internal.h"],
-                  "row_lead+row_stats": ["row_stats.hip", "row_pass.h", "sv_internal.h"],
+                  "row_lead+row_stats": ["row_stats.hip", "rest_draw.hip", "row_pass.h", "draw_pass.h",
+                                         "sv_internal.h"],
                   "fused": ["fused.hip", "row_pass.h", "accept_scan.h", "draw_pass.h", "sv_internal.h"]}
 
 
@@ -258,8 +259,14 @@ def main():
         min_rows += extra
         full_rows += extra
     draw_rows = int(np.sum(np.where(sampling, np.where(n < k, 2, 1), 0)))
+    # With early exit the second round's launch also draws the sequences the
+    # leading positions settled (their draw rows count towards that launch).
+    early_draw_rows = 0
+    if early:
+        settled = ((n < L) | (k < L)) & sampling & ~(gathered & (n < k))
+        early_draw_rows = int(np.sum(np.where(settled, np.where(n < k, 2, 1), 0)))
     row_bytes = w.V * elt
-    k1_bytes = read_rows * row_bytes
+    k1_bytes = (read_rows + early_draw_rows) * row_bytes
     total_bytes = (read_rows + draw_rows) * row_bytes
     seq_per_s = w.B / (ms_per_step / 1e3)
     hbm_gbs = total_bytes / (ms_per_step / 1e3) / 1e9
@@ -318,7 +325,7 @@ def main():
         "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
         "algorithmic_bytes": total_bytes, "mean_accepted": round(float(n.mean()), 4),
         "rows_read": read_rows, "rows_full_pass": full_rows, "rows_minimum": min_rows,
-        "draw_rows": draw_rows,
+        "draw_rows": draw_rows, "early_draw_rows": early_draw_rows,
         "kernels_ms": {k: round(v, 5) for k, v in kern.items()},   # separate pass, all kernels evented
         "roofline": roofline, "cpu_baseline": cpu, "gen_s": round(t_gen, 2),
     }

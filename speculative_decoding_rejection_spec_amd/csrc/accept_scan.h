@@ -71,8 +71,10 @@ __device__ __forceinline__ double log2_norm(const RowStat& r, float c) {
 // Early exit: only the rows of positions < limit have been read.  If their
 // tests already decide the outcome (a rejection among them, or every
 // position including the bonus row read) the scan writes everything and
-// sets *done = 1; otherwise (the first rejection, if any, lies at or past
-// limit) it writes nothing but *done = 0, and runs again once the remaining
+// sets *done to kDecided, or to kDecidedEarlyDraw (listing b in plan.early)
+// when the draw rows have been read too; otherwise (the first rejection, if
+// any, lies at or past limit) it writes nothing but *done = kUndecided, and
+// runs again once the remaining
 // rows are read; it then appends those rows' segments to plan.rest.  The
 // scan stops at the first rejection, like the pages'
 // loop over positions, so rows after it never influence the result.
@@ -126,7 +128,7 @@ __device__ __forceinline__ void accept_sequence(const Problem& p, const Plan& pl
             p.out_n[b] = -1;
             if (p.out_emit_prob) p.out_emit_prob[b] = NAN;
             st_co<kCo>(&plan.task[b].kind, static_cast<int32_t>(kNone));
-            if (done) *done = 1;
+            if (done) *done = kDecided;
         }
         return;
     }
@@ -152,7 +154,7 @@ __device__ __forceinline__ void accept_sequence(const Problem& p, const Plan& pl
     const uint64_t mask = __ballot(reject);
     if (!mask && k >= limit) {                     // undecided: rows past limit are needed
         if (done) {
-            if (lane == 0) *done = 0;
+            if (lane == 0) *done = kUndecided;
             // List the remaining row segments: target rows limit..k, then
             // (sampling) draft rows limit..k-1, each in nseg segments.
             const int32_t nt = k - limit + 1, nd = (greedy || gathered) ? 0 : k - limit;
@@ -173,7 +175,13 @@ __device__ __forceinline__ void accept_sequence(const Problem& p, const Plan& pl
         return;
     }
     const int n = mask ? __ffsll(static_cast<unsigned long long>(mask)) - 1 : k;
-    if (done && lane == 0) *done = 1;
+    if (done && lane == n) {
+        // Settled by its leading positions: a sampling sequence whose draw
+        // rows have been read can draw beside the remaining row pass.
+        const bool early_draw = !greedy && !(gathered && n < k);
+        *done = early_draw ? kDecidedEarlyDraw : kDecided;
+        if (early_draw) plan.early[atomicAdd(plan.early_n, 1u)] = b;
+    }
 
     // Slot n of a sampling sequence is written by the draw alone: in the
     // fused form the draw runs in another workgroup, possibly on another XCD,

@@ -17,6 +17,7 @@ __global__ __launch_bounds__(kThreads) void draw_sums_kernel(Problem p, Plan pla
     __shared__ drawpass::TabEntry tbl[256];
     __shared__ DrawLds lds;
     load_exp2_table(tbl, kThreads);            // overlaps the task load
+    if (plan.lead > 0 && plan.done[b] == kDecidedEarlyDraw) return;   // drawn beside the row pass
     const DrawTask task = load_task<false>(p, plan, b);
     if (task.kind == kNone) return;            // the whole workgroup leaves
     __syncthreads();

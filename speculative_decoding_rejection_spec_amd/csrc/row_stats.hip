@@ -65,6 +65,7 @@ __global__ __launch_bounds__(kThreads) void row_lead_kernel(Problem p, Plan plan
     if (blockIdx.x == 0 && threadIdx.x == 0) {                   // the accept scans fill the lists
         *plan.rest_n = 0;
         *plan.dlist_n = 0;
+        *plan.early_n = 0;
     }
     int64_t q = blockIdx.x;
     const int64_t seg = q % plan.nseg;

@@ -69,7 +69,7 @@ struct Geometry {
     int32_t nseg, nchunk;
     int64_t seg_len, chunk_len;
     size_t off_seg, off_task, off_csum, off_band_n, off_band_w, off_xlogit, off_ctr, off_done, off_rest,
-        off_rest_n, off_dlist, off_dlist_n, off_nbuf, bytes;
+        off_rest_n, off_dlist, off_dlist_n, off_nbuf, off_early, off_early_n, bytes;
 };
 
 // Splits a row of V logits into n <= max_pieces pieces of about `target`
@@ -116,6 +116,10 @@ bool make_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dtype, int64_
     off = align256(off + sizeof(uint32_t));
     g.off_nbuf = off;                                   // accept counts of spec_draft_sample
     off = align256(off + sizeof(int32_t) * static_cast<size_t>(B));
+    g.off_early = off;
+    off = align256(off + sizeof(int32_t) * static_cast<size_t>(B));
+    g.off_early_n = off;
+    off = align256(off + sizeof(uint32_t));
     g.bytes = off;
     return true;
 }
@@ -194,6 +198,8 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     plan.rest_n = reinterpret_cast<uint32_t*>(ws + g.off_rest_n);
     plan.dlist = reinterpret_cast<RestItem*>(ws + g.off_dlist);
     plan.dlist_n = reinterpret_cast<uint32_t*>(ws + g.off_dlist_n);
+    plan.early = reinterpret_cast<int32_t*>(ws + g.off_early);
+    plan.early_n = reinterpret_cast<uint32_t*>(ws + g.off_early_n);
     Problem pr = p;
     if (!pr.out_n) pr.out_n = reinterpret_cast<int32_t*>(ws + g.off_nbuf);
 
@@ -249,7 +255,6 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
         if (timed) recorded |= 1u << i;
         return true;
     };
-    const int64_t all_items = (2 * p.total + p.B) * static_cast<int64_t>(g.nseg);
     bool ok;
     if (fused) {
         ok = launch(kKFusedReset, [&] { return launch_fused_reset(pr, plan, stream); }) &&
@@ -260,7 +265,14 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
         if (plan.lead > 0)
             ok = launch(kKRowLead, [&] { return launch_row_lead(pr, plan, stream); }) &&
                  launch(kKAcceptLead, [&] { return launch_accept_lead(pr, plan, stream); }) &&
-                 launch(kKRowStats, [&] { return launch_row_list(pr, plan, plan.rest, plan.rest_n, all_items, stream); });
+                 launch(kKRowStats, [&] {
+                     // (a settled sequence of the gathered form has not read its draft row yet,
+                     // so it has no early draw: the plain list pass suffices)
+                     return pr.draft_probs
+                                ? launch_row_list(pr, plan, plan.rest, plan.rest_n,
+                                                  (2 * p.total + p.B) * static_cast<int64_t>(g.nseg), stream)
+                                : launch_rest_and_early_draws(pr, plan, stream);
+                 });
         else
             ok = launch(kKRowStats, [&] { return launch_row_stats(pr, plan, stream); });
         ok = ok && launch(kKAccept, [&] { return launch_accept(pr, plan, stream); });

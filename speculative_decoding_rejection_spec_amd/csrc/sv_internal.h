@@ -121,7 +121,12 @@ struct Plan {
     uint32_t* rest_n;    // early exit: number of entries in rest
     RestItem* dlist;     // gathered form: [B * nseg], segments of the draft rows at rejections
     uint32_t* dlist_n;   // gathered form: number of entries in dlist
+    int32_t* early;      // early exit: [B], sequences whose draw runs beside the remaining rows
+    uint32_t* early_n;   // early exit: number of entries in early
 };
+
+// Plan::done values (early exit).
+enum : int32_t { kUndecided = 0, kDecided = 1, kDecidedEarlyDraw = 2 };
 
 // Layout of Plan::ctr (fused form), zeroed before every launch.  The queue
 // word also carries the abandon bit kQueueAbandoned.
@@ -142,6 +147,7 @@ struct Fused {
 hipError_t launch_row_stats(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_row_list(const Problem& p, const Plan& plan, const RestItem* list, const uint32_t* count,
                            int64_t max_items, hipStream_t s);
+hipError_t launch_rest_and_early_draws(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_row_lead(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_accept(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_accept_lead(const Problem& p, const Plan& plan, hipStream_t s);
