@@ -78,6 +78,12 @@ def _open(path: str):
                                            P, P, P, P, P, P, P, P]
     lib.oracle_draft_sample.restype = ctypes.c_int
     lib.oracle_draft_sample.argtypes = [P, i32, i64, i32, P, P, i32, i32, P, P, P, P]
+    lib.oracle_commit.restype = ctypes.c_int
+    lib.oracle_commit.argtypes = [P, P, P, i32, P, P, i32, P, P]
+    lib.oracle_adapt_k.restype = ctypes.c_int
+    lib.oracle_adapt_k.argtypes = [P, P, i32, i32, i32, P, P, P]
+    lib.oracle_ngram_draft.restype = ctypes.c_int
+    lib.oracle_ngram_draft.argtypes = [P, P, i32, i32, i32, i32, i32, P, P]
     return lib
 
 
@@ -243,3 +249,58 @@ def draft_sample(logits: np.ndarray, temperature, uniforms, threads: int = 1) ->
         with ThreadPoolExecutor(threads) as ex:
             list(ex.map(run, zip(edges[:-1], edges[1:])))
     return out
+
+
+def commit(out_tokens, out_n, offsets, seq_tokens, seq_len):
+    """One round's commit: returns (seq_tokens', seq_len', committed,
+    committed_offsets); the inputs are not modified."""
+    lib = _load()
+    out_tokens = np.ascontiguousarray(out_tokens, np.int32)
+    out_n = np.ascontiguousarray(out_n, np.int32)
+    offsets = np.ascontiguousarray(offsets, np.int32)
+    seq = np.array(seq_tokens, np.int32, copy=True, order="C")
+    L = np.array(seq_len, np.int32, copy=True)
+    B, max_len = seq.shape
+    committed = np.full(max(1, int(offsets[-1]) + B), -1, np.int32)
+    coff = np.zeros(B + 1, np.int32)
+    rc = lib.oracle_commit(_ptr(out_tokens), _ptr(out_n), _ptr(offsets), B, _ptr(seq), _ptr(L),
+                           max_len, _ptr(committed), _ptr(coff))
+    if rc != 0:
+        raise RuntimeError(f"oracle_commit failed with code {rc}")
+    return seq, L, committed[:coff[-1]], coff
+
+
+class AdaptK:
+    """Adaptive draft length over rounds (oracle_adapt_k); holds the
+    oracle's own per-sequence history."""
+
+    def __init__(self, B: int, min_k: int = 1, max_k: int = 10, k0=None):
+        self.B, self.min_k, self.max_k = B, min_k, max_k
+        self.k = np.full(B, (min_k + max_k) // 2 if k0 is None else k0, np.int32)
+        self.hist = np.zeros((B, 100))
+        self.count = np.zeros(B, np.int32)
+
+    def update(self, out_n, k_used) -> np.ndarray:
+        lib = _load()
+        out_n = np.ascontiguousarray(out_n, np.int32)
+        k_used = np.ascontiguousarray(k_used, np.int32)
+        rc = lib.oracle_adapt_k(_ptr(out_n), _ptr(k_used), self.B, self.min_k, self.max_k,
+                                _ptr(self.hist), _ptr(self.count), _ptr(self.k))
+        if rc != 0:
+            raise RuntimeError(f"oracle_adapt_k failed with code {rc}")
+        return self.k.copy()
+
+
+def ngram_draft(seq_tokens, seq_len, ngram_max: int, ngram_min: int, k_max: int):
+    """n-gram drafts: returns (draft_tokens packed, draft_offsets [B+1])."""
+    lib = _load()
+    seq = np.ascontiguousarray(seq_tokens, np.int32)
+    L = np.ascontiguousarray(seq_len, np.int32)
+    B, max_len = seq.shape
+    toks = np.full(max(1, B * k_max), -1, np.int32)
+    off = np.zeros(B + 1, np.int32)
+    rc = lib.oracle_ngram_draft(_ptr(seq), _ptr(L), B, max_len, ngram_max, ngram_min, k_max,
+                                _ptr(toks), _ptr(off))
+    if rc != 0:
+        raise RuntimeError(f"oracle_ngram_draft failed with code {rc}")
+    return toks[:off[-1]], off

@@ -52,7 +52,10 @@
  * accept tests divide by the drafter's gathered q_i(x_i) instead of the draft
  * row's softmax; the full draft row enters only the residual) and
  * oracle_draft_sample (the drafter's own step: x ~ softmax(z / T) by the same
- * inverse CDF, or the argmax at T = 0, with q(x) reported).
+ * inverse CDF, or the argmax at T = 0, with q(x) reported).  The round's
+ * bookkeeping follows: oracle_commit (append the committed tokens),
+ * oracle_adapt_k (adaptive draft length) and oracle_ngram_draft
+ * (prompt-lookup drafting without a draft model).
  *
  * Ambiguity flags (rows where float rounding order may legitimately decide
  * differently): A = some evaluated accept test has |u - alpha| < 1e-5;
@@ -454,6 +457,110 @@ int oracle_draft_sample(const void *logits, int32_t dtype, int64_t V, int32_t ro
         if (out_gap) out_gap[r] = gap;
     }
     free(q);
+    return 0;
+}
+
+/* ---- post-verify bookkeeping and the n-gram drafter --------------------- */
+
+/* Commit one verify round to each sequence ([sxl] 基础推测解码器 generate, step
+ * 3 更新生成序列, and 批量推测解码 update_generated: the verified tokens are
+ * appended to the generated sequence; [ifdog] 动手实践 and [hw] 三 append the
+ * accepted drafts AND the replacement or bonus token -- [sxl]'s own loop
+ * drops the replacement when some drafts were accepted, which reads as a
+ * bug).  Sequence b (n = out_n[b]) commits out_tokens[o_b+b .. o_b+b+n],
+ * n + 1 tokens, cut to the room left in its row of seq_tokens [B, max_len];
+ * a data-error sequence (n < 0) commits nothing.  Updates seq_len; writes
+ * committed_offsets [B+1] (prefix sums of the committed counts) and the
+ * committed tokens packed in that order into committed [total+B]. */
+int oracle_commit(const int32_t *out_tokens, const int32_t *out_n, const int32_t *offsets,
+                  int32_t B, int32_t *seq_tokens, int32_t *seq_len, int32_t max_len,
+                  int32_t *committed, int32_t *committed_offsets) {
+    if (B < 0 || max_len < 0) return -1;
+    committed_offsets[0] = 0;
+    for (int32_t b = 0; b < B; ++b) {
+        const int64_t slot = (int64_t)offsets[b] + b;
+        int32_t c = out_n[b] >= 0 ? out_n[b] + 1 : 0;
+        const int32_t room = seq_len[b] < max_len ? max_len - seq_len[b] : 0;
+        if (c > room) c = room;
+        for (int32_t i = 0; i < c; ++i) {
+            seq_tokens[(int64_t)b * max_len + seq_len[b] + i] = out_tokens[slot + i];
+            committed[committed_offsets[b] + i] = out_tokens[slot + i];
+        }
+        seq_len[b] += c;
+        committed_offsets[b + 1] = committed_offsets[b] + c;
+    }
+    return 0;
+}
+
+/* Adaptive draft length, one round ([sxl] 自适应推测解码 adapt_k; [hw] 四
+ * adaptive gamma): sequence b appends its acceptance rate n/k (n accepted of
+ * the k it drafted; 0 when none were accepted, as [sxl] records 0 when
+ * target_verify returns no accepted tokens) to a history of at most 100;
+ * once it holds at least 10 rates, the mean of the last 10 (summed in order,
+ * oldest first, in fp64) above 0.8 raises k by one (at most max_k), below
+ * 0.5 lowers it by one (at least min_k).  k_used [B] is the k of this round;
+ * k [B] is updated in place.  history [B, 100] and hist_count [B] are the
+ * oracle's own state (initially zero).  Sequences with n < 0 (data errors) or
+ * k_used < 1 are left unchanged. */
+int oracle_adapt_k(const int32_t *out_n, const int32_t *k_used, int32_t B, int32_t min_k,
+                   int32_t max_k, double *history, int32_t *hist_count, int32_t *k) {
+    if (B < 0 || min_k < 1 || max_k < min_k) return -1;
+    for (int32_t b = 0; b < B; ++b) {
+        if (out_n[b] < 0 || k_used[b] < 1) continue;
+        double *h = history + (int64_t)b * 100;
+        const double rate = out_n[b] > 0 ? (double)out_n[b] / (double)k_used[b] : 0.0;
+        if (hist_count[b] == 100) {            /* drop the oldest */
+            memmove(h, h + 1, sizeof(double) * 99);
+            hist_count[b] = 99;
+        }
+        h[hist_count[b]++] = rate;
+        if (hist_count[b] >= 10) {
+            double sum = 0.0;
+            for (int32_t i = hist_count[b] - 10; i < hist_count[b]; ++i) sum += h[i];
+            const double avg = sum / 10.0;
+            if (avg > 0.8) k[b] = k[b] + 1 < max_k ? k[b] + 1 : max_k;
+            else if (avg < 0.5) k[b] = k[b] - 1 > min_k ? k[b] - 1 : min_k;
+        }
+    }
+    return 0;
+}
+
+/* n-gram (prompt-lookup) drafting ([ifdog] Lookahead 与 n-gram 投机; [hw] 四,
+ * Prompt Lookup Decoding): no draft model -- the drafts are copied from the
+ * sequence itself, after an earlier occurrence of its last n tokens.
+ * Readings: n runs from ngram_max down to ngram_min and the first n with a
+ * match wins; the match is the most recent one, i.e. the largest start j
+ * with tokens[j .. j+n-1] equal to the last n tokens and j + n < L (at least
+ * one token follows it, so the suffix itself never matches); the drafts are
+ * the up to k_max tokens that follow the match, cut at the end of the
+ * sequence; no match gives no drafts.  seq_tokens [B, max_len] with L =
+ * seq_len[b].  Writes draft_offsets [B+1] (prefix sums of the counts) and the
+ * drafts packed in that order into draft_tokens [B * k_max]. */
+int oracle_ngram_draft(const int32_t *seq_tokens, const int32_t *seq_len, int32_t B,
+                       int32_t max_len, int32_t ngram_max, int32_t ngram_min, int32_t k_max,
+                       int32_t *draft_tokens, int32_t *draft_offsets) {
+    if (B < 0 || ngram_min < 1 || ngram_max < ngram_min || k_max < 0) return -1;
+    draft_offsets[0] = 0;
+    for (int32_t b = 0; b < B; ++b) {
+        const int32_t *t = seq_tokens + (int64_t)b * max_len;
+        const int32_t L = seq_len[b] < max_len ? seq_len[b] : max_len;
+        int32_t start = -1, n_used = 0;
+        for (int32_t n = ngram_max; n >= ngram_min && start < 0; --n) {
+            if (L < n + 1) continue;
+            for (int32_t j = L - n - 1; j >= 0; --j) {
+                int32_t eq = 1;
+                for (int32_t i = 0; i < n && eq; ++i) eq = (t[j + i] == t[L - n + i]);
+                if (eq) { start = j; n_used = n; break; }
+            }
+        }
+        int32_t c = 0;
+        if (start >= 0) {
+            c = L - (start + n_used);
+            if (c > k_max) c = k_max;
+            for (int32_t i = 0; i < c; ++i) draft_tokens[draft_offsets[b] + i] = t[start + n_used + i];
+        }
+        draft_offsets[b + 1] = draft_offsets[b] + c;
+    }
     return 0;
 }
 

@@ -12,6 +12,7 @@ import os
 import pytest
 
 import oracle
+import test_oracle_bookkeeping as bpins
 import test_oracle_draft as dpins
 import test_oracle_pins as pins
 
@@ -41,6 +42,15 @@ MUTANTS = {
     "draft_prob_of_neighbour": ("out_probs[r] = q[t];", "out_probs[r] = q[t > 0 ? t - 1 : t + 1];"),
     "draft_untempered": ("orc_softmax_row(logits, dtype, r, V, T, q, &m, &S);",
                          "orc_softmax_row(logits, dtype, r, V, 1.0, q, &m, &S);"),
+    # post-verify bookkeeping and the n-gram drafter
+    "commit_drops_emitted": ("int32_t c = out_n[b] >= 0 ? out_n[b] + 1 : 0;",
+                             "int32_t c = out_n[b] >= 0 ? out_n[b] : 0;"),
+    "adapt_ge": ("if (avg > 0.8)", "if (avg >= 0.8)"),
+    "adapt_window_9": ("for (int32_t i = hist_count[b] - 10; i < hist_count[b]; ++i) sum += h[i];",
+                       "for (int32_t i = hist_count[b] - 9; i < hist_count[b]; ++i) sum += h[i] * (10.0 / 9.0);"),
+    "adapt_rate_k_plus_1": ("(double)out_n[b] / (double)k_used[b]", "(double)out_n[b] / (double)(k_used[b] + 1)"),
+    "ngram_first_match": ("for (int32_t j = L - n - 1; j >= 0; --j) {", "for (int32_t j = 0; j <= L - n - 1; ++j) {"),
+    "ngram_suffix_matches_itself": ("for (int32_t j = L - n - 1; j >= 0; --j) {", "for (int32_t j = L - n; j >= 0; --j) {"),
     "draft_greedy_highest_tie": ("orc_row_argmax(logits, dtype, r, V, &a);\n            out_tokens[r] = (int32_t)a;",
                                  "orc_row_argmax(logits, dtype, r, V, &a);\n            out_tokens[r] = (int32_t)(V - 1 - a);"),
 }
@@ -60,6 +70,11 @@ PINS = [
     lambda: dpins.test_draft_sample_greedy_and_errors(),
     lambda: dpins.test_gathered_reads_only_the_rejected_draft_row(),
     lambda: dpins.test_gathered_bad_values_are_data_errors(),
+    lambda: bpins.test_commit_hand_case(),
+    lambda: bpins.test_adapt_k_boundaries_are_strict(),
+    lambda: bpins.test_adapt_k_window_is_the_last_ten(),
+    lambda: bpins.test_adapt_k_rate_uses_the_rounds_own_k(),
+    lambda: bpins.test_ngram_hand_cases(),
 ]
 
 
