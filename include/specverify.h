@@ -163,6 +163,56 @@ sv_status_t spec_draft_sample(const void *logits, int32_t rows, int64_t V, sv_dt
                               int32_t *out_tokens, float *out_probs, void *workspace,
                               size_t workspace_bytes, hipStream_t stream);
 
+/* ---- after the verify: bookkeeping and n-gram drafting -------------------
+ * (page "【大模型】- 推测解码", sections 基础推测解码器, 批量推测解码 and
+ * 自适应推测解码; page "投机解码", sections 动手实践 and Lookahead 与 n-gram 投机;
+ * page "大模型推理无损加速:投机采样...", section 四).  Same conventions as above:
+ * device pointers, enqueue-only on `stream`, argument errors returned before
+ * anything is enqueued. */
+
+/* Commits one verify round: sequence b appends its n_b accepted drafts and
+ * its emitted token (out_tokens slots offsets[b]+b .. offsets[b]+b+n_b, as
+ * spec_verify wrote them; offsets == NULL means k_uniform drafts each) to row
+ * b of seq_tokens [B, max_len] after its seq_len[b] tokens (0 <= seq_len[b]
+ * <= max_len), cut to the room left; a data-error sequence (n_b < 0) appends
+ * nothing.  seq_len is updated.  committed_offsets int32 [B+1] receives the
+ * prefix sums of the appended counts and committed (int32, room for every
+ * appended token: total_draft + B suffices; may be NULL) the appended tokens
+ * in sequence order. */
+sv_status_t spec_commit(const int32_t *out_tokens, const int32_t *out_n_accepted,
+                        const int32_t *offsets, int32_t k_uniform, int32_t B,
+                        int32_t *seq_tokens, int32_t *seq_len, int32_t max_len,
+                        int32_t *committed, int32_t *committed_offsets, hipStream_t stream);
+
+/* Adaptive draft length, one round (the adapt_k rule of section 自适应推测解码):
+ * sequence b records its acceptance rate n_b / k_b (0 when n_b = 0; k_b from
+ * offsets or k_uniform); once it holds 10 rates, the mean of the last 10
+ * (summed oldest first in fp64) above 0.8 raises k[b] by one, below 0.5 lowers
+ * it by one, within [min_k, max_k] (1 <= min_k <= max_k <= SV_K_MAX).  State:
+ * history fp64 [B, 10] (a ring of the last rates) and rounds int32 [B] (rates
+ * recorded), both zero before the first round; k int32 [B] is read and
+ * updated (the pages start at (min_k + max_k) / 2).  Sequences with n_b < 0
+ * or k_b = 0 are left unchanged. */
+sv_status_t spec_adapt_k(const int32_t *out_n_accepted, const int32_t *offsets, int32_t k_uniform,
+                         int32_t B, int32_t min_k, int32_t max_k, double *history,
+                         int32_t *rounds, int32_t *k, hipStream_t stream);
+
+/* n-gram (prompt-lookup) drafting, no draft model: for each sequence (row b
+ * of seq_tokens [B, max_len], its first seq_len[b] tokens), the drafts are
+ * the up to k_max (<= SV_K_MAX) tokens that follow the most recent earlier
+ * occurrence of its last n tokens, trying n = ngram_max down to ngram_min
+ * (>= 1) and taking the first n that matches; an occurrence must be followed
+ * by at least one token, and the continuation stops at the end of the
+ * sequence; no match gives no drafts.  Output in spec_verify's layout:
+ * draft_offsets int32 [B+1] (prefix sums of the counts) and draft_tokens
+ * int32 [B * k_max] (packed).  workspace: spec_ngram_workspace_size(B) bytes,
+ * or NULL for the library-owned buffer (shared with spec_verify's). */
+size_t spec_ngram_workspace_size(int32_t B);
+sv_status_t spec_ngram_draft(const int32_t *seq_tokens, const int32_t *seq_len, int32_t B,
+                             int32_t max_len, int32_t ngram_max, int32_t ngram_min, int32_t k_max,
+                             int32_t *draft_tokens, int32_t *draft_offsets, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *spec_verify_status_string(sv_status_t status);
 

@@ -15,6 +15,7 @@ from ._lib import (LIB_PATH, SV_BF16, SV_F32, SV_K_MAX, SV_MODE_AUTO, SV_MODE_FU
 
 __all__ = [
     "spec_verify", "spec_verify_probs", "spec_verify_gathered", "spec_draft_sample",
+    "spec_commit", "spec_adapt_k", "spec_ngram_draft",
     "spec_verify_workspace_size", "spec_verify_release",
     "timing", "kernel_times", "set_geometry", "set_mode", "set_early_exit", "SpecVerifyError", "SV_F32", "SV_BF16",
     "SV_K_MAX", "SV_MODE_AUTO", "SV_MODE_STAGED", "SV_MODE_FUSED", "LIB_PATH", "lib",
@@ -187,6 +188,89 @@ def spec_draft_sample(logits, temperature, uniforms, *, out_tokens=None, out_pro
                                  ws_bytes, _stream(dev, stream))
     check(st, "spec_draft_sample")
     return out_tokens, out_probs
+
+
+def spec_commit(out_tokens, out_n_accepted, offsets, seq_tokens, seq_len, *, k_uniform: int = 0,
+                committed=None, committed_offsets=None, stream=None):
+    """Appends each sequence's accepted drafts and emitted token to its row
+    of ``seq_tokens`` [B, max_len] (int32; ``seq_len`` [B] updated in place);
+    returns (committed tokens packed, committed_offsets [B+1])."""
+    import torch
+    dev = seq_tokens.device
+    B, max_len = int(seq_tokens.shape[0]), int(seq_tokens.shape[1])
+    for t, nm in ((out_tokens, "out_tokens"), (out_n_accepted, "out_n_accepted"), (seq_tokens, "seq_tokens"),
+                  (seq_len, "seq_len")):
+        _need(t, nm, torch.int32, dev)
+    if offsets is not None:
+        _need(offsets, "offsets", torch.int32, dev)
+        if offsets.numel() != B + 1:
+            raise ValueError(f"offsets must have {B + 1} entries")
+    total = out_tokens.numel() - B
+    if out_n_accepted.numel() != B or seq_len.numel() != B or total < 0:
+        raise ValueError("out_n_accepted / seq_len / out_tokens sizes do not match B")
+    if offsets is None and total != B * int(k_uniform):
+        raise ValueError("without offsets, out_tokens must hold B * (k_uniform + 1) entries")
+    if committed is None:
+        committed = torch.empty(max(1, total + B), dtype=torch.int32, device=dev)
+    if committed_offsets is None:
+        committed_offsets = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    _need(committed, "committed", torch.int32, dev)
+    _need(committed_offsets, "committed_offsets", torch.int32, dev)
+    if committed.numel() < total + B or committed_offsets.numel() != B + 1:
+        raise ValueError("committed needs total + B entries and committed_offsets B + 1")
+    check(lib().spec_commit(_ptr(out_tokens), _ptr(out_n_accepted), _ptr(offsets), int(k_uniform), B,
+                            _ptr(seq_tokens), _ptr(seq_len), max_len, _ptr(committed),
+                            _ptr(committed_offsets), _stream(dev, stream)), "spec_commit")
+    return committed, committed_offsets
+
+
+def spec_adapt_k(out_n_accepted, offsets, history, rounds, k, *, k_uniform: int = 0, min_k: int = 1,
+                 max_k: int = 10, stream=None):
+    """One round of the adaptive draft length; ``history`` float64 [B, 10],
+    ``rounds`` int32 [B] (zero at the start) and ``k`` int32 [B] are updated
+    in place."""
+    import torch
+    dev = k.device
+    B = int(k.numel())
+    _need(out_n_accepted, "out_n_accepted", torch.int32, dev)
+    _need(history, "history", torch.float64, dev)
+    _need(rounds, "rounds", torch.int32, dev)
+    _need(k, "k", torch.int32, dev)
+    if offsets is not None:
+        _need(offsets, "offsets", torch.int32, dev)
+        if offsets.numel() != B + 1:
+            raise ValueError(f"offsets must have {B + 1} entries")
+    if out_n_accepted.numel() != B or rounds.numel() != B or tuple(history.shape) != (B, 10):
+        raise ValueError("out_n_accepted [B], rounds [B] and history [B, 10] expected")
+    check(lib().spec_adapt_k(_ptr(out_n_accepted), _ptr(offsets), int(k_uniform), B, int(min_k), int(max_k),
+                             _ptr(history), _ptr(rounds), _ptr(k), _stream(dev, stream)), "spec_adapt_k")
+    return k
+
+
+def spec_ngram_draft(seq_tokens, seq_len, *, ngram_max: int = 3, ngram_min: int = 1, k_max: int = 8,
+                     draft_tokens=None, draft_offsets=None, workspace=None, stream=None):
+    """n-gram drafts of each sequence: returns (draft_tokens packed
+    [B * k_max], draft_offsets [B+1])."""
+    import torch
+    dev = seq_tokens.device
+    B, max_len = int(seq_tokens.shape[0]), int(seq_tokens.shape[1])
+    _need(seq_tokens, "seq_tokens", torch.int32, dev)
+    _need(seq_len, "seq_len", torch.int32, dev)
+    if seq_len.numel() != B:
+        raise ValueError(f"seq_len must have {B} entries")
+    if draft_tokens is None:
+        draft_tokens = torch.empty(max(1, B * k_max), dtype=torch.int32, device=dev)
+    if draft_offsets is None:
+        draft_offsets = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    _need(draft_tokens, "draft_tokens", torch.int32, dev)
+    _need(draft_offsets, "draft_offsets", torch.int32, dev)
+    if draft_tokens.numel() < B * k_max or draft_offsets.numel() != B + 1:
+        raise ValueError("draft_tokens needs B * k_max entries and draft_offsets B + 1")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().spec_ngram_draft(_ptr(seq_tokens), _ptr(seq_len), B, max_len, int(ngram_max), int(ngram_min),
+                                 int(k_max), _ptr(draft_tokens), _ptr(draft_offsets), _ptr(workspace), ws_bytes,
+                                 _stream(dev, stream)), "spec_ngram_draft")
+    return draft_tokens, draft_offsets
 
 
 def spec_verify_workspace_size(B: int, total_draft: int, V: int, dtype) -> int:

@@ -31,6 +31,10 @@ SIGNATURES = {
     "spec_verify_gathered": (_I32, [_P, _P, _P, _P, _P, _I32, _I64, _I32, _I64, _I32, _P, _P, _P,
                                     _P, _P, _P, _SZ, _P]),
     "spec_draft_sample": (_I32, [_P, _I32, _I64, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
+    "spec_commit": (_I32, [_P, _P, _P, _I32, _I32, _P, _P, _I32, _P, _P, _P]),
+    "spec_adapt_k": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P]),
+    "spec_ngram_workspace_size": (_SZ, [_I32]),
+    "spec_ngram_draft": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "spec_verify_status_string": (ctypes.c_char_p, [_I32]),
     "spec_verify_release": (None, []),
     "spec_verify_timing": (_I32, [_I32, _I32]),

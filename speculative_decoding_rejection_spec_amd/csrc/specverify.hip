@@ -418,6 +418,62 @@ sv_status_t spec_draft_sample(const void* logits, int32_t rows, int64_t V, sv_dt
     return run(p, workspace, workspace_bytes, stream);
 }
 
+sv_status_t spec_commit(const int32_t* out_tokens, const int32_t* out_n_accepted, const int32_t* offsets,
+                        int32_t k_uniform, int32_t B, int32_t* seq_tokens, int32_t* seq_len, int32_t max_len,
+                        int32_t* committed, int32_t* committed_offsets, hipStream_t stream) {
+    if (B < 0 || max_len < 0 || (!offsets && (k_uniform < 0 || k_uniform > SV_K_MAX))) return SV_ERR_SHAPE;
+    if (!out_tokens || !out_n_accepted || !seq_tokens || !seq_len || !committed_offsets) return SV_ERR_NULL;
+    if (!aligned(out_tokens, 4) || !aligned(out_n_accepted, 4) || !aligned(offsets, 4) ||
+        !aligned(seq_tokens, 4) || !aligned(seq_len, 4) || !aligned(committed, 4) ||
+        !aligned(committed_offsets, 4))
+        return SV_ERR_ALIGN;
+    return launch_commit(out_tokens, out_n_accepted, offsets, k_uniform, B, seq_tokens, seq_len, max_len,
+                         committed, committed_offsets, stream) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+sv_status_t spec_adapt_k(const int32_t* out_n_accepted, const int32_t* offsets, int32_t k_uniform, int32_t B,
+                         int32_t min_k, int32_t max_k, double* history, int32_t* rounds, int32_t* k,
+                         hipStream_t stream) {
+    if (B < 0 || min_k < 1 || max_k < min_k || max_k > SV_K_MAX ||
+        (!offsets && (k_uniform < 0 || k_uniform > SV_K_MAX)))
+        return SV_ERR_SHAPE;
+    if (B > 0 && (!out_n_accepted || !history || !rounds || !k)) return SV_ERR_NULL;
+    if (!aligned(out_n_accepted, 4) || !aligned(offsets, 4) || !aligned(history, 8) || !aligned(rounds, 4) ||
+        !aligned(k, 4))
+        return SV_ERR_ALIGN;
+    return launch_adapt_k(out_n_accepted, offsets, k_uniform, B, min_k, max_k, history, rounds, k, stream) ==
+                   hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+size_t spec_ngram_workspace_size(int32_t B) {
+    return B < 0 ? 0 : align256(sizeof(int32_t) * (static_cast<size_t>(B) + 1));
+}
+
+sv_status_t spec_ngram_draft(const int32_t* seq_tokens, const int32_t* seq_len, int32_t B, int32_t max_len,
+                             int32_t ngram_max, int32_t ngram_min, int32_t k_max, int32_t* draft_tokens,
+                             int32_t* draft_offsets, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+    if (B < 0 || max_len < 0 || ngram_min < 1 || ngram_max < ngram_min || k_max < 0 || k_max > SV_K_MAX)
+        return SV_ERR_SHAPE;
+    if (!draft_offsets || (B > 0 && (!seq_tokens || !seq_len || (k_max > 0 && !draft_tokens))))
+        return SV_ERR_NULL;
+    if (!aligned(seq_tokens, 4) || !aligned(seq_len, 4) || !aligned(draft_tokens, 4) ||
+        !aligned(draft_offsets, 4))
+        return SV_ERR_ALIGN;
+    const size_t need = spec_ngram_workspace_size(B);
+    if (workspace) {
+        if (workspace_bytes < need) return SV_ERR_WORKSPACE;
+        if (!aligned(workspace, 4)) return SV_ERR_ALIGN;
+    } else {
+        std::lock_guard<std::mutex> lock(g_mutex);
+        const sv_status_t st = owned_workspace(need, &workspace);
+        if (st != SV_OK) return st;
+    }
+    return launch_ngram_draft(seq_tokens, seq_len, B, max_len, ngram_max, ngram_min, k_max,
+                              static_cast<int32_t*>(workspace), draft_tokens, draft_offsets, stream) ==
+                   hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
 const char* spec_verify_status_string(sv_status_t status) {
     switch (status) {
         case SV_OK: return "ok";

@@ -156,6 +156,15 @@ hipError_t launch_draw_pick(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_fused_reset(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_fused(const Problem& p, const Plan& plan, const Fused& f, hipStream_t s);
 hipError_t fused_grid(int32_t dtype, int32_t* blocks);   // resident workgroups on this device
+hipError_t launch_commit(const int32_t* out_tokens, const int32_t* out_n, const int32_t* offsets,
+                         int32_t k_uniform, int32_t B, int32_t* seq_tokens, int32_t* seq_len,
+                         int32_t max_len, int32_t* committed, int32_t* committed_offsets, hipStream_t s);
+hipError_t launch_adapt_k(const int32_t* out_n, const int32_t* offsets, int32_t k_uniform, int32_t B,
+                          int32_t min_k, int32_t max_k, double* history, int32_t* rounds, int32_t* k,
+                          hipStream_t s);
+hipError_t launch_ngram_draft(const int32_t* seq_tokens, const int32_t* seq_len, int32_t B, int32_t max_len,
+                              int32_t ngram_max, int32_t ngram_min, int32_t k_max, int32_t* cont_start,
+                              int32_t* draft_tokens, int32_t* draft_offsets, hipStream_t s);
 int64_t fused_counter_words(int32_t B);
 
 // ---- device helpers shared by the kernels ---------------------------------

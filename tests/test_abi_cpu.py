@@ -27,7 +27,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(spec_(?:verify|draft)\w*)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(spec_\w+)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -136,3 +136,26 @@ def test_timing_probe_arguments(lib):
     assert lib.spec_verify_kernel_times(buf, 8) == -1      # nothing recorded yet
     assert lib.spec_verify_timing(0, 1) == OK
     assert lib.spec_verify_kernel_times(buf, 8) == -1
+
+
+def test_bookkeeping_argument_errors(lib):
+    """Host-side validation of the bookkeeping and n-gram entry points (every
+    call fails before any HIP call)."""
+    p = ctypes.c_void_p(16)                     # never dereferenced: validation fails first
+    assert lib.spec_commit(p, p, None, 0, -1, p, p, 8, p, p, None) == SHAPE
+    assert lib.spec_commit(p, p, None, 64, 1, p, p, 8, p, p, None) == SHAPE
+    assert lib.spec_commit(None, p, None, 1, 1, p, p, 8, p, p, None) == NULL
+    assert lib.spec_commit(p, p, None, 1, 1, p, p, 8, p, None, None) == NULL
+    assert lib.spec_commit(ctypes.c_void_p(18), p, None, 1, 1, p, p, 8, p, p, None) == ALIGN
+    assert lib.spec_adapt_k(p, None, 4, 1, 0, 10, p, p, p, None) == SHAPE
+    assert lib.spec_adapt_k(p, None, 4, 1, 5, 4, p, p, p, None) == SHAPE
+    assert lib.spec_adapt_k(p, None, 4, 1, 1, 64, p, p, p, None) == SHAPE
+    assert lib.spec_adapt_k(None, None, 4, 1, 1, 10, p, p, p, None) == NULL
+    assert lib.spec_adapt_k(p, None, 4, 1, 1, 10, ctypes.c_void_p(20), p, p, None) == ALIGN
+    assert lib.spec_ngram_draft(p, p, 2, 16, 3, 0, 4, p, p, None, 0, None) == SHAPE
+    assert lib.spec_ngram_draft(p, p, 2, 16, 2, 3, 4, p, p, None, 0, None) == SHAPE
+    assert lib.spec_ngram_draft(p, p, 2, 16, 3, 1, 64, p, p, None, 0, None) == SHAPE
+    assert lib.spec_ngram_draft(p, p, 2, 16, 3, 1, 4, p, None, None, 0, None) == NULL
+    assert lib.spec_ngram_draft(p, p, 2, 16, 3, 1, 4, p, p, p, 1, None) == WORKSPACE
+    assert lib.spec_ngram_workspace_size(-1) == 0
+    assert lib.spec_ngram_workspace_size(1000) >= 4 * 1001
