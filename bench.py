@@ -93,10 +93,11 @@ def main():
     ap.add_argument("--mode", choices=["auto", "staged", "fused"], default="auto",
                     help="launch form (auto = staged)")
     ap.add_argument("--lag", type=int, default=0, help="fused form: draw lag in sequences (0 = auto)")
-    ap.add_argument("--entry", choices=["verify", "gathered", "draft"], default="verify",
+    ap.add_argument("--entry", choices=["verify", "gathered", "draft", "ngram", "commit"], default="verify",
                     help="verify: spec_verify; gathered: spec_verify_gathered with the drafts' q(x) "
                          "(the accept tests need no draft rows); draft: spec_draft_sample over one "
-                         "draft-model row per sequence")
+                         "draft-model row per sequence; ngram: spec_ngram_draft over B=512 token streams "
+                         "of 4096; commit: spec_commit + spec_adapt_k of the workload's verify outputs")
     ap.add_argument("--lead", type=int, default=-1,
                     help="early exit: leading positions read by every sequence (0 = one full pass, "
                          "-1 = the library's choice by batch size)")
@@ -125,9 +126,14 @@ def main():
                 args.lag)
     sv.set_early_exit(args.lead)
 
+    if args.entry == "ngram":
+        return bench_ngram(args, sv, torch, np)
+
     t_gen = time.perf_counter()
     w = wl.make_workload(args.workload)
     t_gen = time.perf_counter() - t_gen
+    if args.entry == "commit":
+        return bench_commit(args, sv, torch, np, w)
 
     def logits(a):
         if a.dtype == np.uint16:
@@ -307,8 +313,10 @@ def main():
                f"fp64 C oracle split over {threads} threads; {what} agree with the "
                f"GPU on {agree}/{w.B} sequences"}
 
-    metric = {"verify": METRIC,
-              "gathered": METRIC + " (verify with the drafts' gathered q(x))",
+    kdesc = f"k={int(w.k.max())}" if int(w.k.min()) == int(w.k.max()) else f"k={int(w.k.min())}..{int(w.k.max())}"
+    base = f"sequences verified/s and achieved HBM GB/s (% of peak), B={w.B} {kdesc} V={w.V} {w.dtype}"
+    metric = {"verify": base,
+              "gathered": base + " (verify with the drafts' gathered q(x))",
               "draft": "draft rows sampled/s (spec_draft_sample), one row per sequence"}[args.entry]
     res = {
         "metric": metric, "value": round(seq_per_s, 1),
@@ -330,6 +338,92 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "gen_s": round(t_gen, 2),
     }
     print(json.dumps(res), flush=True)
+
+
+def _timed(torch, fn, steps, warmup):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def _line(args, metric, value, unit, ms, config, extra):
+    res = {"metric": metric, "value": round(value, 1), "unit": unit, "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "int32", "data": "synthetic", "config": config, **extra}
+    print(json.dumps(res), flush=True)
+
+
+def bench_ngram(args, sv, torch, np):
+    """n-gram drafting over B=512 synthetic token streams of up to 4096 tokens
+    (a 200-token alphabet with copied motifs, so suffixes recur)."""
+    dev = torch.device("cuda:0")
+    g = np.random.default_rng(2024)
+    B, max_len, kmax = 512, 4096, 8
+    seq = g.integers(0, 200, size=(B, max_len)).astype(np.int32)
+    for b in range(B):
+        for _ in range(16):
+            m = int(g.integers(4, 32))
+            src, dst = g.integers(0, max_len - m, size=2)
+            seq[b, dst:dst + m] = seq[b, src:src + m]
+    L = g.integers(max_len // 2, max_len + 1, size=B).astype(np.int32)
+    dseq, dL = torch.from_numpy(seq).to(dev), torch.from_numpy(L).to(dev)
+    tok = torch.empty(B * kmax, dtype=torch.int32, device=dev)
+    off = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    ws = torch.empty(sv.lib().spec_ngram_workspace_size(B), dtype=torch.uint8, device=dev)
+    ms = _timed(torch, lambda i: sv.spec_ngram_draft(dseq, dL, ngram_max=3, ngram_min=1, k_max=kmax,
+                                                     draft_tokens=tok, draft_offsets=off, workspace=ws),
+                args.steps, args.warmup)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        tc = time.perf_counter()
+        ref_t, ref_o = oracle.ngram_draft(seq, L, 3, 1, kmax)
+        tc = time.perf_counter() - tc
+        same = bool(np.array_equal(ref_o, off.cpu().numpy()))
+        cpu = {"value": round(B / tc, 2), "unit": "sequences/s", "cores": 1, "kind": "oracle",
+               "sample": f"the whole batch once, C oracle on one thread; offsets agree with the GPU: {same}"}
+    drafted = int(off[-1].item())
+    _line(args, "sequences n-gram-drafted/s (spec_ngram_draft, n = 3..1, k_max = 8)", B / (ms / 1e3),
+          "sequences/s", ms, {"workload": f"ngram: B={B} token streams, lengths {max_len // 2}..{max_len}",
+                              "B": B, "max_len": max_len, "k_max": kmax},
+          {"drafts_per_sequence": round(drafted / B, 3), "token_bytes": int(L.sum()) * 4,
+           "token_gbs": round(int(L.sum()) * 4 / (ms / 1e3) / 1e9, 1), "cpu_baseline": cpu})
+
+
+def bench_commit(args, sv, torch, np, w):
+    """spec_commit + spec_adapt_k on the outputs of one verify of the workload
+    (each step appends one round to rows of 4096 tokens)."""
+    dev = torch.device("cuda:0")
+    def logits(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+    off = torch.from_numpy(w.offsets).to(dev)
+    tok, n = sv.spec_verify(logits(w.target), logits(w.draft), torch.from_numpy(w.tokens).to(dev), off,
+                            torch.from_numpy(w.uniforms).to(dev), torch.from_numpy(w.temperature).to(dev))
+    max_len = 4096
+    steps = min(args.steps, 250)
+    seq = torch.zeros((w.B, max_len), dtype=torch.int32, device=dev)
+    L = torch.full((w.B,), 512, dtype=torch.int32, device=dev)
+    com = torch.empty(w.total + w.B, dtype=torch.int32, device=dev)
+    coff = torch.empty(w.B + 1, dtype=torch.int32, device=dev)
+    hist = torch.zeros((w.B, 10), dtype=torch.float64, device=dev)
+    rounds = torch.zeros(w.B, dtype=torch.int32, device=dev)
+    k = torch.full((w.B,), 5, dtype=torch.int32, device=dev)
+
+    def step(i):
+        sv.spec_commit(tok, n, off, seq, L, committed=com, committed_offsets=coff)
+        sv.spec_adapt_k(n, off, hist, rounds, k, min_k=1, max_k=10)
+    args.steps = steps
+    ms = _timed(torch, step, steps, min(args.warmup, 10))
+    _line(args, "verify rounds committed/s (spec_commit + spec_adapt_k)", 1e3 / ms, "rounds/s", ms,
+          {"workload": f"commit {args.workload}: B={w.B}", "B": w.B, "max_len": max_len},
+          {"sequences_per_s": round(w.B / (ms / 1e3), 1)})
 
 
 if __name__ == "__main__":

@@ -245,9 +245,11 @@ int32_t spec_verify_kernel_times(float *ms, int32_t max_kernels);
 const char *spec_verify_kernel_name(int32_t i);
 
 /* Benchmark tuning: approximate logits per row-pass segment and per draw
- * chunk (0 restores the defaults, 65536 and 8192).  The workspace size
- * depends on them, so query spec_verify_workspace_size() after a change.
- * Returns SV_ERR_SHAPE for negative values. */
+ * chunk (0 restores the automatic choice: 65536 and 8192 for batches that
+ * fill the GPU, shorter -- down to 4096 and 1024 -- for small calls, so that
+ * their passes still spread over the CUs).  The workspace size depends on
+ * them, so query spec_verify_workspace_size() after a change.  Returns
+ * SV_ERR_SHAPE for negative values. */
 sv_status_t spec_verify_set_geometry(int64_t seg_elems, int64_t chunk_elems);
 
 /* Form of the launch.  SV_MODE_STAGED: four kernels (row pass, accept scan,

@@ -37,23 +37,40 @@ struct RowStat {
     double S;      // sampling: sum of 2^(z c - R)
 };
 
-// Merges the nseg segment statistics of one row (exact power-of-two
-// rescaling for sampling rows; lowest id among tied maxima for greedy rows).
+// Merges the nseg segment statistics of one row in segment order: sampling
+// rows by exact power-of-two rescaling to the largest reference exponent
+// seen so far (the same sum as rescaling every term to the final one);
+// greedy rows keep the lowest id among tied maxima.  Statistics are loaded
+// four segments at a time so their round trips overlap.
 template <bool kCo>
 __device__ __forceinline__ RowStat merge_row(const SegStat* seg, int32_t nseg, bool greedy) {
+    constexpr int kBatch = 4;
     RowStat r{-INFINITY, INT32_MAX, -INFINITY, 0.0};
-    for (int32_t s = 0; s < nseg; ++s) {
-        r.m = fmaxf(r.m, ld_co<kCo>(&seg[s].m));
-        if (!greedy) r.R = fmaxf(r.R, ld_co<kCo>(&seg[s].R));
-    }
-    for (int32_t s = 0; s < nseg; ++s) {
-        if (greedy) {
-            const int32_t a = ld_co<kCo>(&seg[s].arg);
-            if (ld_co<kCo>(&seg[s].m) == r.m && a < r.arg) r.arg = a;
-        } else {
-            const float Rs = ld_co<kCo>(&seg[s].R);
-            if (Rs != -INFINITY)
-                r.S += ldexp(ld_co<kCo>(&seg[s].s), static_cast<int>(fmaxf(Rs - r.R, -2048.f)));
+    for (int32_t s0 = 0; s0 < nseg; s0 += kBatch) {
+        float m[kBatch], R[kBatch];
+        int32_t a[kBatch];
+        double v[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            const int32_t s = s0 + i < nseg ? s0 + i : nseg - 1;   // clamped; used only when in range
+            m[i] = ld_co<kCo>(&seg[s].m);
+            if (greedy) a[i] = ld_co<kCo>(&seg[s].arg);
+            else { R[i] = ld_co<kCo>(&seg[s].R); v[i] = ld_co<kCo>(&seg[s].s); }
+        }
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            if (s0 + i >= nseg) break;
+            if (greedy) {
+                if (m[i] > r.m || (m[i] == r.m && a[i] < r.arg)) { r.m = m[i]; r.arg = a[i]; }
+                continue;
+            }
+            r.m = fmaxf(r.m, m[i]);
+            if (R[i] == -INFINITY) continue;                        // an empty segment
+            if (R[i] > r.R) {
+                if (r.R != -INFINITY) r.S = ldexp(r.S, static_cast<int>(fmaxf(r.R - R[i], -2048.f)));
+                r.R = R[i];
+            }
+            r.S += ldexp(v[i], static_cast<int>(fmaxf(R[i] - r.R, -2048.f)));
         }
     }
     return r;

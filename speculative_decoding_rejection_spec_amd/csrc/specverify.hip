@@ -33,8 +33,24 @@ const char* const kKernelNames[kNumKernels] = {"row_stats", "accept",      "draw
                                                "row_lead",  "accept_lead", "row_draft"};
 
 std::mutex g_mutex;
-int64_t g_seg_elems = kDefaultSegElems;
-int64_t g_chunk_elems = kDefaultChunkElems;
+int64_t g_seg_elems = 0;                     // 0: automatic (auto_lengths)
+int64_t g_chunk_elems = 0;
+
+// Automatic segment and chunk lengths: the defaults suit batches that fill
+// the GPU many times over (C4: 8704 row workgroups, 4864 draw workgroups);
+// a small call is cut finer so its row pass still has about kRowBlocks
+// workgroups and its draw about kDrawBlocks (no finer than kMinSeg /
+// kMinChunk logits).
+constexpr int64_t kRowBlocks = 2048, kDrawBlocks = 1024;
+constexpr int64_t kMinSeg = 8192, kMinChunk = 1024;
+void auto_lengths(int32_t B, int64_t total, int64_t V, int64_t* seg, int64_t* chunk) {
+    const int64_t rows = 2 * total + B;
+    int64_t s = rows * V / kRowBlocks, c = static_cast<int64_t>(B) * V / kDrawBlocks;
+    s = s < kMinSeg ? kMinSeg : (s > kDefaultSegElems ? kDefaultSegElems : s);
+    c = c < kMinChunk ? kMinChunk : (c > kDefaultChunkElems ? kDefaultChunkElems : c);
+    *seg = g_seg_elems ? g_seg_elems : s;
+    *chunk = g_chunk_elems ? g_chunk_elems : c;
+}
 int32_t g_mode = SV_MODE_AUTO;
 int32_t g_fused_lag = 0;                     // 0: chosen from the resident grid
 int32_t g_lead = kAutoLead;                  // early exit: leading positions read first (0: off)
@@ -171,7 +187,9 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     if (p.B == 0) return SV_OK;
     std::lock_guard<std::mutex> lock(g_mutex);
     Geometry g;
-    if (!make_geometry(p.B, p.total, p.V, static_cast<sv_dtype_t>(p.dtype), g_seg_elems, g_chunk_elems, g))
+    int64_t seg_elems, chunk_elems;
+    auto_lengths(p.B, p.total, p.V, &seg_elems, &chunk_elems);
+    if (!make_geometry(p.B, p.total, p.V, static_cast<sv_dtype_t>(p.dtype), seg_elems, chunk_elems, g))
         return SV_ERR_SHAPE;
     if (workspace) {
         if (workspace_bytes < g.bytes) return SV_ERR_WORKSPACE;
@@ -300,7 +318,9 @@ size_t spec_verify_workspace_size(int32_t B, int64_t total_draft, int64_t V, sv_
     if (dtype != SV_F32 && dtype != SV_BF16) return 0;
     std::lock_guard<std::mutex> lock(g_mutex);
     Geometry g;
-    if (!make_geometry(B, total_draft, V, dtype, g_seg_elems, g_chunk_elems, g)) return 0;
+    int64_t seg_elems, chunk_elems;
+    auto_lengths(B, total_draft, V, &seg_elems, &chunk_elems);
+    if (!make_geometry(B, total_draft, V, dtype, seg_elems, chunk_elems, g)) return 0;
     return g.bytes;
 }
 
@@ -557,8 +577,8 @@ sv_status_t spec_verify_set_early_exit(int32_t lead_positions) {
 sv_status_t spec_verify_set_geometry(int64_t seg_elems, int64_t chunk_elems) {
     if (seg_elems < 0 || chunk_elems < 0) return SV_ERR_SHAPE;
     std::lock_guard<std::mutex> lock(g_mutex);
-    g_seg_elems = seg_elems ? seg_elems : kDefaultSegElems;
-    g_chunk_elems = chunk_elems ? chunk_elems : kDefaultChunkElems;
+    g_seg_elems = seg_elems;
+    g_chunk_elems = chunk_elems;
     return SV_OK;
 }
 
