@@ -42,11 +42,14 @@ METRIC = "sequences verified/s and achieved HBM GB/s (% of peak), B=256 k=8 V=15
 # Counter summaries per roofline kernel, and the sources each kernel is built from.
 COUNTERS = {"row_stats": os.path.join(ROOT, "profiles", "row_stats_c4_counters.txt"),
             "row_lead+row_stats": os.path.join(ROOT, "profiles", "row_pass_early_exit_c4_counters.txt"),
-            "fused": os.path.join(ROOT, "profiles", "fused_c4_counters.txt")}
+            "fused": os.path.join(ROOT, "profiles", "fused_c4_counters.txt"),
+            "row_lead+rest+draw_pick": os.path.join(ROOT, "profiles", "verify_c4_queued_counters.txt")}
 KERNEL_SOURCES = {"row_stats": ["row_stats.hip", "row_pass.h", "sv_internal.h"],
                   "row_lead+row_stats": ["row_stats.hip", "rest_draw.hip", "row_pass.h", "draw_pass.h",
                                          "sv_internal.h"],
-                  "fused": ["fused.hip", "row_pass.h", "accept_scan.h", "draw_pass.h", "sv_internal.h"]}
+                  "fused": ["fused.hip", "row_pass.h", "accept_scan.h", "draw_pass.h", "sv_internal.h"],
+                  "row_lead+rest+draw_pick": ["row_stats.hip", "rest_queue.hip", "draw.hip", "row_pass.h",
+                                              "accept_scan.h", "draw_pass.h", "sv_internal.h"]}
 
 
 def source_hash(kernel: str) -> str:
@@ -98,6 +101,10 @@ def main():
                          "(the accept tests need no draft rows); draft: spec_draft_sample over one "
                          "draft-model row per sequence; ngram: spec_ngram_draft over B=512 token streams "
                          "of 4096; commit: spec_commit + spec_adapt_k of the workload's verify outputs")
+    ap.add_argument("--queue", type=int, default=0,
+                    help="early exit: draws beside the rows (0) or all in the final launch (1)")
+    ap.add_argument("--queue-lag", type=int, nargs=2, default=[0, 0], metavar=("ACCEPT", "DRAW"),
+                    help="early exit: lags of the accept and draw items in sequences (0 0 = automatic)")
     ap.add_argument("--lead", type=int, default=-1,
                     help="early exit: leading positions read by every sequence (0 = one full pass, "
                          "-1 = the library's choice by batch size)")
@@ -125,6 +132,7 @@ def main():
     sv.set_mode({"auto": sv.SV_MODE_AUTO, "staged": sv.SV_MODE_STAGED, "fused": sv.SV_MODE_FUSED}[args.mode],
                 args.lag)
     sv.set_early_exit(args.lead)
+    sv.set_queue(args.queue, *args.queue_lag)
 
     if args.entry == "ngram":
         return bench_ngram(args, sv, torch, np)
@@ -205,9 +213,17 @@ def main():
     form = "fused" if "fused" in launched else "staged"
     early = "row_lead" in launched
     sv.timing(False)
-    # The roofline kernel: the row pass (its two launches with early exit) or
-    # the fused kernel.
-    roof = ["fused"] if form == "fused" else (["row_lead", "row_stats"] if early else ["row_stats"])
+    # The roofline kernel: the row pass (one launch, or the two launches of
+    # early exit in the gathered form), the fused kernel, or -- early exit
+    # with queued draws -- the three launches that stream every row and draw
+    # row (the draws run inside the second round and the final launch).
+    queued = "rest" in launched
+    if form == "fused":
+        roof = ["fused"]
+    elif queued:
+        roof = ["row_lead", "rest", "draw_pick"]
+    else:
+        roof = ["row_lead", "row_stats"] if early else ["row_stats"]
     if "row_draft" in launched:
         roof.append("row_draft")
     roof_kernel = "+".join(roof)
@@ -265,14 +281,8 @@ def main():
         min_rows += extra
         full_rows += extra
     draw_rows = int(np.sum(np.where(sampling, np.where(n < k, 2, 1), 0)))
-    # With early exit the second round's launch also draws the sequences the
-    # leading positions settled (their draw rows count towards that launch).
-    early_draw_rows = 0
-    if early:
-        settled = ((n < L) | (k < L)) & sampling & ~(gathered & (n < k))
-        early_draw_rows = int(np.sum(np.where(settled, np.where(n < k, 2, 1), 0)))
     row_bytes = w.V * elt
-    k1_bytes = (read_rows + early_draw_rows) * row_bytes
+    k1_bytes = read_rows * row_bytes
     total_bytes = (read_rows + draw_rows) * row_bytes
     seq_per_s = w.B / (ms_per_step / 1e3)
     hbm_gbs = total_bytes / (ms_per_step / 1e3) / 1e9
@@ -281,7 +291,7 @@ def main():
     if k1_live is not None:
         # The row pass reads every needed row once; the fused kernel also
         # reads the draw rows.
-        kbytes = total_bytes if roof_kernel == "fused" else k1_bytes
+        kbytes = total_bytes if (roof_kernel == "fused" or queued) else k1_bytes
         achieved = kbytes / (k1_live / 1e3) / 1e9
         roofline = {"bound": "hbm", "kernel": roof_kernel, "achieved": round(achieved, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
@@ -333,7 +343,7 @@ def main():
         "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
         "algorithmic_bytes": total_bytes, "mean_accepted": round(float(n.mean()), 4),
         "rows_read": read_rows, "rows_full_pass": full_rows, "rows_minimum": min_rows,
-        "draw_rows": draw_rows, "early_draw_rows": early_draw_rows,
+        "draw_rows": draw_rows,
         "kernels_ms": {k: round(v, 5) for k, v in kern.items()},   # separate pass, all kernels evented
         "roofline": roofline, "cpu_baseline": cpu, "gen_s": round(t_gen, 2),
     }

@@ -232,14 +232,16 @@ void spec_verify_release(void);
  * writes, for up to max_kernels kernels, the mean elapsed milliseconds per
  * call over the recorded calls that launched the kernel (ms[i] belongs to
  * spec_verify_kernel_name(i); NaN for kernels not selected or not launched:
- * the staged form launches row_lead and accept_lead (early exit only),
- * row_stats, accept, row_draft (gathered form only), draw_sums and
- * draw_pick, the fused form fused_reset and fused); it returns the number
+ * the staged form launches row_stats, accept, draw_sums and draw_pick in
+ * one pass; with early exit row_lead, accept_lead, rest and draw_pick,
+ * or in the gathered form row_lead, accept_lead, row_stats, accept,
+ * row_draft, draw_sums and draw_pick; the fused form fused_reset and
+ * fused); it returns the number
  * of kernels, or -1 if the probe is off, no call was recorded or a HIP call
  * failed.
  * spec_verify_timing returns SV_ERR_SHAPE for every < 1.  The probe uses
  * one device: turn it off and on again after switching devices. */
-#define SV_TIME_ALL 0x1FF
+#define SV_TIME_ALL 0x3FF
 sv_status_t spec_verify_timing(int32_t kernels, int32_t every);
 int32_t spec_verify_kernel_times(float *ms, int32_t max_kernels);
 const char *spec_verify_kernel_name(int32_t i);
@@ -279,6 +281,24 @@ sv_status_t spec_verify_set_mode(int32_t mode, int32_t fused_lag);
  * non-finite row, go unseen).  Returns SV_ERR_SHAPE unless
  * -1 <= L <= SV_K_MAX + 1. */
 sv_status_t spec_verify_set_early_exit(int32_t lead_positions);
+
+/* Early exit outside the gathered form ends in two launches.  "rest"
+ * streams the remaining rows and, beside them, makes the draws: the chunks
+ * of the sequences the leading positions settled are interleaved with the
+ * rows; each undecided sequence's accept scan runs lag_accept sequences
+ * (blocks of rows) after its own rows, and its draw chunks lag_draw blocks
+ * after them, each waiting (boundedly) until what it needs is written.
+ * "draw_pick" redoes whatever a wait that ran out left (usually nothing)
+ * and picks every emitted token.  Where a chunk is summed does not change
+ * any output.  mode SV_QUEUE_OVERLAP (the default): as described;
+ * SV_QUEUE_FINAL: every accept scan and chunk of that round in draw_pick;
+ * SV_QUEUE_HANDOFF: the undecided sequences take the path of a wait that
+ * runs out (they are redone in draw_pick; for tests).
+ * lag_accept, lag_draw = 0 choose them from the number of resident
+ * workgroups and the expected rows per sequence.  Returns SV_ERR_SHAPE for
+ * an unknown mode or a negative lag. */
+enum { SV_QUEUE_OVERLAP = 0, SV_QUEUE_FINAL = 1, SV_QUEUE_HANDOFF = 2 };
+sv_status_t spec_verify_set_queue(int32_t mode, int32_t lag_accept, int32_t lag_draw);
 
 #ifdef __cplusplus
 }

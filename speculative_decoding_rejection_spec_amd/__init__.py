@@ -11,14 +11,15 @@ from __future__ import annotations
 import ctypes
 
 from ._lib import (LIB_PATH, SV_BF16, SV_F32, SV_K_MAX, SV_MODE_AUTO, SV_MODE_FUSED, SV_MODE_STAGED,
-                   SV_TIME_ALL, SpecVerifyError, check, lib)
+                   SV_QUEUE_FINAL, SV_QUEUE_HANDOFF, SV_QUEUE_OVERLAP, SV_TIME_ALL, SpecVerifyError, check, lib)
 
 __all__ = [
     "spec_verify", "spec_verify_probs", "spec_verify_gathered", "spec_draft_sample",
     "spec_commit", "spec_adapt_k", "spec_ngram_draft",
     "spec_verify_workspace_size", "spec_verify_release",
-    "timing", "kernel_times", "set_geometry", "set_mode", "set_early_exit", "SpecVerifyError", "SV_F32", "SV_BF16",
-    "SV_K_MAX", "SV_MODE_AUTO", "SV_MODE_STAGED", "SV_MODE_FUSED", "LIB_PATH", "lib",
+    "timing", "kernel_times", "set_geometry", "set_mode", "set_early_exit", "set_queue", "SpecVerifyError",
+    "SV_F32", "SV_BF16", "SV_K_MAX", "SV_MODE_AUTO", "SV_MODE_STAGED", "SV_MODE_FUSED", "SV_QUEUE_OVERLAP",
+    "SV_QUEUE_FINAL", "SV_QUEUE_HANDOFF", "LIB_PATH", "lib",
 ]
 
 
@@ -290,6 +291,12 @@ def set_early_exit(lead_positions: int = -1) -> None:
     """Leading positions every sequence reads before the rest (0 = off,
     -1 = automatic by batch size)."""
     check(lib().spec_verify_set_early_exit(int(lead_positions)), "spec_verify_set_early_exit")
+
+
+def set_queue(mode: int = SV_QUEUE_OVERLAP, lag_accept: int = 0, lag_draw: int = 0) -> None:
+    """Where early exit's second-round accept scans and draw chunks run, and
+    their lags in sequences (0 = automatic); outputs do not change."""
+    check(lib().spec_verify_set_queue(int(mode), int(lag_accept), int(lag_draw)), "spec_verify_set_queue")
 
 
 def set_mode(mode: int = SV_MODE_AUTO, fused_lag: int = 0) -> None:

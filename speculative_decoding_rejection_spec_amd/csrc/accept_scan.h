@@ -53,9 +53,11 @@ __device__ __forceinline__ RowStat merge_row(const SegStat* seg, int32_t nseg, b
 #pragma unroll
         for (int i = 0; i < kBatch; ++i) {
             const int32_t s = s0 + i < nseg ? s0 + i : nseg - 1;   // clamped; used only when in range
-            m[i] = ld_co<kCo>(&seg[s].m);
-            if (greedy) a[i] = ld_co<kCo>(&seg[s].arg);
-            else { R[i] = ld_co<kCo>(&seg[s].R); v[i] = ld_co<kCo>(&seg[s].s); }
+            const uint64_t h = ld_co<kCo>(&seg[s].head);
+            m[i] = head_m(h);
+            a[i] = static_cast<int32_t>(head_hi(h));
+            R[i] = __uint_as_float(head_hi(h));
+            if (!greedy) v[i] = ld_co<kCo>(&seg[s].s);
         }
 #pragma unroll
         for (int i = 0; i < kBatch; ++i) {
@@ -81,6 +83,54 @@ __device__ __forceinline__ double log2_norm(const RowStat& r, float c) {
     return log2(r.S) + (static_cast<double>(r.R) - static_cast<double>(r.m) * c);
 }
 
+// Early exit: lists the rows sequence b still needs (target rows limit..k,
+// then draft rows limit..k-1 unless no_draft), nseg segments each, as block
+// i of the second round's schedule, and marks their statistics and
+// captured logits unset.  The schedule is block after block in listing
+// order; after block i come the accept item of block i - lag_a and the
+// nchunk draw items of block i - lag_c (those of the last blocks follow the
+// whole schedule, where the second round finds them by arithmetic), so an
+// item is dispatched about lag blocks after the rows it needs.  The task
+// of a sampling sequence is marked unset until that accept item writes it.
+__device__ __forceinline__ void list_rest(const Problem& p, const Plan& plan, int32_t b, int64_t o, int32_t k,
+                                          int32_t limit, bool no_draft, bool greedy) {
+    const int lane = threadIdx.x & 63;
+    const int64_t ntarget = p.total + p.B;
+    const int32_t nseg = plan.nseg;
+    const int32_t nt = k - limit + 1, nd = no_draft ? 0 : k - limit;
+    const int32_t cnt = (nt + nd) * nseg;
+    uint64_t pos = 0;
+    if (lane == 0) pos = atomicAdd(reinterpret_cast<unsigned long long*>(plan.blk_ctr),
+                                   (1ull << 32) | static_cast<uint64_t>(cnt));
+    pos = __shfl(pos, 0, 64);
+    const int64_t i = static_cast<int64_t>(pos >> 32), base = static_cast<int64_t>(pos & 0xffffffffu);
+    const int64_t nchunk = plan.nchunk;
+    const int64_t at = base + max(static_cast<int64_t>(0), i - plan.lag_a) +
+                       nchunk * max(static_cast<int64_t>(0), i - plan.lag_c);
+    for (int32_t e = lane; e < cnt; e += 64) {
+        const int32_t j = e / nseg, sg = e - j * nseg;
+        const bool tgt = j < nt;
+        const int64_t row = tgt ? o + b + limit + j : o + limit + (j - nt);
+        plan.sched[at + e] = RestItem{b, tgt ? kItemTarget : kItemDraft, static_cast<int32_t>(row), sg};
+        SegStat* st = plan.seg + (tgt ? row : ntarget + row) * nseg + sg;
+        st->head = kUnset64;
+        st->s = __longlong_as_double(static_cast<long long>(kUnset64));
+        if (sg == 0 && !greedy) plan.xlogit[tgt ? row : ntarget + row] = __uint_as_float(kUnset32);
+    }
+    int64_t q = at + cnt;
+    if (i >= plan.lag_a) {
+        if (lane == 0) plan.sched[q] = RestItem{-1, kItemAccept, static_cast<int32_t>(i - plan.lag_a), 0};
+        ++q;
+    }
+    if (i >= plan.lag_c)
+        for (int32_t c = lane; c < nchunk; c += 64)
+            plan.sched[q + c] = RestItem{-1, kItemChunk, static_cast<int32_t>(i - plan.lag_c), c};
+    if (lane == 0) {
+        plan.blk_seq[i] = b;
+        if (!greedy) plan.task[b].kind = kTaskUnset;
+    }
+}
+
 // Accept scan of sequence b (0 <= b < B), run by every lane of one wave.
 // kCo: the SegStats and captured logits come from other workgroups of the
 // same launch, and the DrawTask goes to others.
@@ -92,12 +142,14 @@ __device__ __forceinline__ double log2_norm(const RowStat& r, float c) {
 // when the draw rows have been read too; otherwise (the first rejection, if
 // any, lies at or past limit) it writes nothing but *done = kUndecided, and
 // runs again once the remaining
-// rows are read; it then appends those rows' segments to plan.rest.  The
+// rows are read; it then lists those rows' segments (list_rest).  The
 // scan stops at the first rejection, like the pages'
 // loop over positions, so rows after it never influence the result.
-// Diagnostics of rows that were not read are NaN.
+// Diagnostics of rows that were not read are NaN.  Returns (the same in
+// every lane) whether the scan settled the sequence with a draw still to
+// make, i.e. wrote a DrawTask other than kNone.
 template <bool kCo>
-__device__ __forceinline__ void accept_sequence(const Problem& p, const Plan& plan, int32_t b,
+__device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& plan, int32_t b,
                                                 int32_t limit = kKMax + 1, int32_t* done = nullptr) {
     const int lane = threadIdx.x & 63;
     int64_t o, o1;
@@ -147,7 +199,7 @@ __device__ __forceinline__ void accept_sequence(const Problem& p, const Plan& pl
             st_co<kCo>(&plan.task[b].kind, static_cast<int32_t>(kNone));
             if (done) *done = kDecided;
         }
-        return;
+        return false;
     }
 
     bool reject = false;
@@ -172,30 +224,16 @@ __device__ __forceinline__ void accept_sequence(const Problem& p, const Plan& pl
     if (!mask && k >= limit) {                     // undecided: rows past limit are needed
         if (done) {
             if (lane == 0) *done = kUndecided;
-            // List the remaining row segments: target rows limit..k, then
-            // (sampling) draft rows limit..k-1, each in nseg segments.
-            const int32_t nt = k - limit + 1, nd = (greedy || gathered) ? 0 : k - limit;
-            const int32_t cnt = (nt + nd) * plan.nseg;
-            uint32_t base = 0;
-            if (lane == 0) base = atomicAdd(plan.rest_n, static_cast<uint32_t>(cnt));
-            base = __shfl(base, 0, 64);
-            for (int32_t e = lane; e < cnt; e += 64) {
-                const int32_t j = e / plan.nseg, sg = e - j * plan.nseg;
-                RestItem it;
-                it.b = b;
-                it.is_target = j < nt;
-                it.row = static_cast<int32_t>(j < nt ? o + b + limit + j : o + limit + (j - nt));
-                it.seg = sg;
-                plan.rest[base + e] = it;
-            }
+            list_rest(p, plan, b, o, k, limit, greedy || gathered, greedy);
         }
-        return;
+        return false;
     }
     const int n = mask ? __ffsll(static_cast<unsigned long long>(mask)) - 1 : k;
     if (done && lane == n) {
         // Settled by its leading positions: a sampling sequence whose draw
         // rows have been read can draw beside the remaining row pass.
-        const bool early_draw = !greedy && !(gathered && n < k);
+        // (not in the gathered form, whose second round only streams rows)
+        const bool early_draw = !greedy && !gathered;
         *done = early_draw ? kDecidedEarlyDraw : kDecided;
         if (early_draw) plan.early[atomicAdd(plan.early_n, 1u)] = b;
     }
@@ -214,17 +252,10 @@ __device__ __forceinline__ void accept_sequence(const Problem& p, const Plan& pl
         if (pending) {
             const uint32_t base = atomicAdd(plan.dlist_n, static_cast<uint32_t>(plan.nseg));
             for (int32_t sg = 0; sg < plan.nseg; ++sg) {
-                RestItem it;
-                it.b = b;
-                it.is_target = 0;
-                it.row = static_cast<int32_t>(drow);
-                it.seg = sg;
-                plan.dlist[base + sg] = it;
+                plan.dlist[base + sg] = RestItem{b, kItemDraft, static_cast<int32_t>(drow), sg};
             }
         }
         DrawTask* t = plan.task + b;
-        st_co<kCo>(&t->kind, static_cast<int32_t>(greedy ? kNone : (n < k ? (pending ? kResidualPending : kResidual)
-                                                                          : kBonus)));
         st_co<kCo>(&t->out_slot, static_cast<int32_t>(trow));
         st_co<kCo>(&t->trow, trow);
         st_co<kCo>(&t->drow, drow);
@@ -233,6 +264,9 @@ __device__ __forceinline__ void accept_sequence(const Problem& p, const Plan& pl
         st_co<kCo>(&t->T, Tf);
         st_co<kCo>(&t->u, p.uniforms[o + b + k]);
         st_co<kCo>(&t->theta, (!greedy && n < k) ? log2_norm(rt, c) - (pending ? 0.0 : log2_norm(rd, c)) : 0.0);
+        if constexpr (kCo) wait_stores();          // the kind, written last, says the rest is visible
+        st_co<kCo>(&t->kind, static_cast<int32_t>(greedy ? kNone : (n < k ? (pending ? kResidualPending : kResidual)
+                                                                          : kBonus)));
     }
     if (p.out_p && lane < k) {
         p.out_p[drow] = static_cast<float>(px);
@@ -247,6 +281,7 @@ __device__ __forceinline__ void accept_sequence(const Problem& p, const Plan& pl
             p.out_row_sum[ntarget + drow] = dread ? static_cast<float>(exp2(log2_norm(rd, c))) : NAN;
         }
     }
+    return !greedy;
 }
 
 // The DrawTask of sequence b as written by accept_sequence; a pending

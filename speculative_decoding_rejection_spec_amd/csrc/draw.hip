@@ -24,16 +24,40 @@ __global__ __launch_bounds__(kThreads) void draw_sums_kernel(Problem p, Plan pla
     draw_chunk<DT, false>(p, plan, task, b, c, tbl, lds);
 }
 
+// Early exit with the draws beside the rows (plan.queued): a sequence whose
+// wait in the second round ran out (or every sequence, SV_QUEUE_FINAL) is
+// redone here first -- its accept scan if its leading positions left it
+// undecided, then every chunk -- with the chunk pass of a 256-thread
+// workgroup (the other threads only take part in its barriers).
 template <int DT>
 __global__ __launch_bounds__(kPickThreads) void draw_pick_kernel(Problem p, Plan plan) {
     const int32_t b = blockIdx.x;
     __shared__ drawpass::TabEntry tbl[256];
-    __shared__ PickLds<kPickThreads> lds;
+    __shared__ union {
+        PickLds<kPickThreads> pick;
+        DrawLds draw;
+    } lds;
     load_exp2_table(tbl, kPickThreads);
+    const bool redo = plan.queued && (plan.queue_mode == SV_QUEUE_FINAL || plan.aband[b] != 0);
+    if (redo) {
+        if (plan.done[b] == kUndecided) {
+            if (threadIdx.x < 64) accept_sequence<true>(p, plan, b);
+            wait_stores();
+        }
+        __syncthreads();
+        const DrawTask task = load_task<true>(p, plan, b);
+        if (task.kind == kNone) return;
+        for (int32_t c = 0; c < plan.nchunk; ++c)
+            draw_chunk<DT, true, kPickThreads>(p, plan, task, b, c, tbl, lds.draw);
+        wait_stores();
+        __syncthreads();
+        pick_sequence<DT, kPickThreads, true>(p, plan, task, b, tbl, lds.pick);
+        return;
+    }
     const DrawTask task = load_task<false>(p, plan, b);
     if (task.kind == kNone) return;
     __syncthreads();
-    pick_sequence<DT, kPickThreads, false>(p, plan, task, b, tbl, lds);
+    pick_sequence<DT, kPickThreads, false>(p, plan, task, b, tbl, lds.pick);
 }
 
 }  // namespace

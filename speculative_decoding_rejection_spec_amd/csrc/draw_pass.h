@@ -262,7 +262,9 @@ __device__ __forceinline__ void block_sum4(double& a, double& b, double& c, doub
     }
     const int wave = threadIdx.x >> 6;
     __syncthreads();
-    if ((threadIdx.x & 63) == 0) { lds[wave][0] = a; lds[wave][1] = b; lds[wave][2] = c; lds[wave][3] = d; }
+    if ((threadIdx.x & 63) == 0 && wave < kWaves) {   // (waves past kWaves only take part in the barriers)
+        lds[wave][0] = a; lds[wave][1] = b; lds[wave][2] = c; lds[wave][3] = d;
+    }
     __syncthreads();
     a = b = c = d = 0.0;
     for (int w = 0; w < kWaves; ++w) { a += lds[w][0]; b += lds[w][1]; c += lds[w][2]; d += lds[w][3]; }
@@ -287,8 +289,10 @@ __device__ __forceinline__ void load_exp2_table(drawpass::TabEntry* tbl, int nth
 // Chunk c of the draw of sequence b (256 threads): accumulates the chunk's
 // fp64 sums and band lists (see the file comment).  `task` is the
 // sequence's DrawTask (kind != kNone).  kCo: the results go to the pick in
-// another workgroup of the same launch.
-template <int DT, bool kCo>
+// another workgroup of the same launch.  NT: the workgroup size; threads
+// past the first 256 do no work but take part in the barriers, so the
+// results are those of a 256-thread workgroup, bit for bit.
+template <int DT, bool kCo, int NT = kThreads>
 __device__ __forceinline__ void draw_chunk(const Problem& p, const Plan& plan, const DrawTask& task,
                                            int32_t b, int32_t c, const drawpass::TabEntry* tbl,
                                            DrawLds& lds) {
@@ -302,7 +306,9 @@ __device__ __forceinline__ void draw_chunk(const Problem& p, const Plan& plan, c
     const int64_t v1 = min(p.V, v0 + plan.chunk_len);
     double sp = 0.0, sq = 0.0, a = 0.0, bq = 0.0;
     int32_t nband = 0;                         // uniform over the lanes still active
-    if (resid_task) {
+    const bool active = NT == kThreads || threadIdx.x < kThreads;
+    if (!active) {
+    } else if (resid_task) {
         const double th_hi = 256.0 * (task.theta + kBand), th_lo = 256.0 * (task.theta - kBand);
         for_chunk<DT, true>(rows, v0, v1, [&](float zt, float zd) {
             const double yt = rows.Yt(zt), yd = rows.Yd(zd);
@@ -328,7 +334,7 @@ __device__ __forceinline__ void draw_chunk(const Problem& p, const Plan& plan, c
     } else {
         for_chunk<DT, false>(rows, v0, v1, [&](float zt, float) { sp += rows.wt(zt); });
     }
-    if (lane == 0) lds.wcount[wave] = nband;  // lane 0 was active whenever any lane was
+    if (lane == 0 && wave < kWaves) lds.wcount[wave] = nband;  // lane 0 was active whenever any lane was
     block_sum4(sp, sq, a, bq, lds.red4);
     if (threadIdx.x == 0) {
         ChunkSums* cs = plan.csum + w;

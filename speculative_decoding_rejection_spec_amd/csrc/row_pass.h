@@ -287,9 +287,7 @@ __device__ __forceinline__ void row_segment(const Problem& p, const Plan& plan, 
         __syncthreads();
         if (threadIdx.x == 0) {
             for (int i = 1; i < kWaves; ++i) merge_argmax(m, a, lds.m[i], lds.a[i]);
-            st_co<kCo>(&plan.seg[w].m, m);
-            st_co<kCo>(&plan.seg[w].R, 0.f);
-            st_co<kCo>(&plan.seg[w].arg, a);
+            st_co<kCo>(&plan.seg[w].head, seg_head(m, static_cast<uint32_t>(a)));
             st_co<kCo>(&plan.seg[w].s, 0.0);
         }
     } else {
@@ -305,9 +303,7 @@ __device__ __forceinline__ void row_segment(const Problem& p, const Plan& plan, 
         __syncthreads();
         if (threadIdx.x == 0) {
             for (int i = 1; i < kWaves; ++i) merge_softmax(m, R, s, lds.m[i], lds.R[i], lds.s[i]);
-            st_co<kCo>(&plan.seg[w].m, m);
-            st_co<kCo>(&plan.seg[w].R, R);
-            st_co<kCo>(&plan.seg[w].arg, 0);
+            st_co<kCo>(&plan.seg[w].head, seg_head(m, __float_as_uint(R)));
             st_co<kCo>(&plan.seg[w].s, s);
             if (capture) st_co<kCo>(&plan.xlogit[is_target ? r : ntarget + r], zx);
         }

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void row_list_kernel(Problem p, Plan plan
     if (w >= *count) return;
     const RestItem it = list[w];
     __shared__ RowLds lds;
-    row_segment<DT, false>(p, plan, it.b, it.is_target != 0, it.row, it.seg, lds);
+    row_segment<DT, false>(p, plan, it.b, it.kind == kItemTarget, it.row, it.seg, lds);
 }
 
 // Early exit, first round: the rows of positions < lead of every sequence.
@@ -63,10 +63,12 @@ __global__ __launch_bounds__(kThreads) void row_list_kernel(Problem p, Plan plan
 template <int DT>
 __global__ __launch_bounds__(kThreads) void row_lead_kernel(Problem p, Plan plan) {
     if (blockIdx.x == 0 && threadIdx.x == 0) {                   // the accept scans fill the lists
-        *plan.rest_n = 0;
+        *plan.blk_ctr = 0;
         *plan.dlist_n = 0;
         *plan.early_n = 0;
     }
+    if (blockIdx.x < static_cast<uint32_t>(p.B) && threadIdx.x == 0)   // (the grid has at least 2B blocks)
+        plan.aband[blockIdx.x] = 0;
     int64_t q = blockIdx.x;
     const int64_t seg = q % plan.nseg;
     q /= plan.nseg;

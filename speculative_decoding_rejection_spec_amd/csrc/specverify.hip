@@ -24,13 +24,13 @@ constexpr int32_t kAutoLead = -1;
 constexpr int64_t kAutoLeadBytes = 512ll << 20;
 constexpr int64_t kMaxChunks = 1024;          // draw chunks per row (the pick keeps them in LDS)
 constexpr int kMaxDevices = 64;
-constexpr int kNumKernels = 9;
+constexpr int kNumKernels = 10;
 enum { kKRowStats, kKAccept, kKDrawSums, kKDrawPick, kKFusedReset, kKFused, kKRowLead, kKAcceptLead,
-       kKRowDraft };
+       kKRowDraft, kKRest };
 
-const char* const kKernelNames[kNumKernels] = {"row_stats", "accept",      "draw_sums",
-                                               "draw_pick", "fused_reset", "fused",
-                                               "row_lead",  "accept_lead", "row_draft"};
+const char* const kKernelNames[kNumKernels] = {"row_stats", "accept",      "draw_sums", "draw_pick",
+                                               "fused_reset", "fused",     "row_lead",  "accept_lead",
+                                               "row_draft", "rest"};
 
 std::mutex g_mutex;
 int64_t g_seg_elems = 0;                     // 0: automatic (auto_lengths)
@@ -54,6 +54,23 @@ void auto_lengths(int32_t B, int64_t total, int64_t V, int64_t* seg, int64_t* ch
 int32_t g_mode = SV_MODE_AUTO;
 int32_t g_fused_lag = 0;                     // 0: chosen from the resident grid
 int32_t g_lead = kAutoLead;                  // early exit: leading positions read first (0: off)
+int32_t g_queue_mode = SV_QUEUE_OVERLAP;
+int32_t g_lag_a = 0, g_lag_c = 0;            // 0: chosen from the resident grid
+constexpr int kRestWgsPerCu = 5;             // resident second-round workgroups per CU (its register count)
+
+hipError_t device_cus(int* cus) {
+    static int cached[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    if (!cached[dev]) {
+        e = hipDeviceGetAttribute(&cached[dev], hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+    }
+    *cus = cached[dev];
+    return hipSuccess;
+}
 
 int32_t effective_lead(int64_t B, int64_t total, int64_t V, sv_dtype_t dtype) {
     if (g_mode == SV_MODE_FUSED) return 0;      // the fused form reads every row
@@ -84,8 +101,8 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 struct Geometry {
     int32_t nseg, nchunk;
     int64_t seg_len, chunk_len;
-    size_t off_seg, off_task, off_csum, off_band_n, off_band_w, off_xlogit, off_ctr, off_done, off_rest,
-        off_rest_n, off_dlist, off_dlist_n, off_nbuf, off_early, off_early_n, bytes;
+    size_t off_seg, off_task, off_csum, off_band_n, off_band_w, off_xlogit, off_ctr, off_done, off_sched,
+        off_blk_ctr, off_blk_seq, off_dlist, off_dlist_n, off_nbuf, off_early, off_early_n, off_aband, bytes;
 };
 
 // Splits a row of V logits into n <= max_pieces pieces of about `target`
@@ -104,7 +121,8 @@ bool make_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dtype, int64_
     split(V, seg_elems, 1 << 20, seg_elems >= unit ? unit : 8, g.nseg, g.seg_len);
     split(V, chunk_elems, kMaxChunks, 8, g.nchunk, g.chunk_len);
     const int64_t rows = 2 * total + B;
-    if (rows * g.nseg > 0x7FFFFFFFll || static_cast<int64_t>(B) * g.nchunk > 0x7FFFFFFFll) return false;
+    // (the second round's grid holds every row segment and every draw chunk)
+    if (rows * g.nseg + static_cast<int64_t>(B) * (1 + g.nchunk) > 0x7FFFFFFFll) return false;
     size_t off = 0;
     g.off_seg = off;
     off = align256(off + sizeof(SegStat) * static_cast<size_t>(rows) * g.nseg);
@@ -122,10 +140,13 @@ bool make_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dtype, int64_
     off = align256(off + sizeof(uint32_t) * static_cast<size_t>(fused_counter_words(B)));
     g.off_done = off;
     off = align256(off + sizeof(int32_t) * static_cast<size_t>(B));
-    g.off_rest = off;
-    off = align256(off + sizeof(RestItem) * static_cast<size_t>(rows) * g.nseg);
-    g.off_rest_n = off;
-    off = align256(off + sizeof(uint32_t));
+    g.off_sched = off;
+    off = align256(off + sizeof(RestItem) * (static_cast<size_t>(rows) * g.nseg +
+                                             static_cast<size_t>(B) * (1 + g.nchunk)));
+    g.off_blk_ctr = off;
+    off = align256(off + sizeof(uint64_t));
+    g.off_blk_seq = off;
+    off = align256(off + sizeof(int32_t) * static_cast<size_t>(B));
     g.off_dlist = off;
     off = align256(off + sizeof(RestItem) * static_cast<size_t>(B) * g.nseg);
     g.off_dlist_n = off;
@@ -136,6 +157,8 @@ bool make_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dtype, int64_
     off = align256(off + sizeof(int32_t) * static_cast<size_t>(B));
     g.off_early_n = off;
     off = align256(off + sizeof(uint32_t));
+    g.off_aband = off;
+    off = align256(off + sizeof(int32_t) * static_cast<size_t>(B));
     g.bytes = off;
     return true;
 }
@@ -212,12 +235,15 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     plan.xlogit = reinterpret_cast<float*>(ws + g.off_xlogit);
     plan.ctr = reinterpret_cast<uint32_t*>(ws + g.off_ctr);
     plan.done = reinterpret_cast<int32_t*>(ws + g.off_done);
-    plan.rest = reinterpret_cast<RestItem*>(ws + g.off_rest);
-    plan.rest_n = reinterpret_cast<uint32_t*>(ws + g.off_rest_n);
+    plan.sched = reinterpret_cast<RestItem*>(ws + g.off_sched);
+    plan.blk_ctr = reinterpret_cast<uint64_t*>(ws + g.off_blk_ctr);
+    plan.blk_seq = reinterpret_cast<int32_t*>(ws + g.off_blk_seq);
     plan.dlist = reinterpret_cast<RestItem*>(ws + g.off_dlist);
     plan.dlist_n = reinterpret_cast<uint32_t*>(ws + g.off_dlist_n);
     plan.early = reinterpret_cast<int32_t*>(ws + g.off_early);
     plan.early_n = reinterpret_cast<uint32_t*>(ws + g.off_early_n);
+    plan.aband = reinterpret_cast<int32_t*>(ws + g.off_aband);
+    plan.queue_mode = g_queue_mode;
     Problem pr = p;
     if (!pr.out_n) pr.out_n = reinterpret_cast<int32_t*>(ws + g.off_nbuf);
 
@@ -233,6 +259,26 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     const bool fused = g_mode == SV_MODE_FUSED && !p.draft_probs;
     if (fused && !fused_fits) return SV_ERR_SHAPE;
     plan.lead = fused ? 0 : effective_lead(p.B, p.total, p.V, static_cast<sv_dtype_t>(p.dtype));
+    plan.lag_a = plan.lag_c = 1 << 30;             // no accept or draw items in the schedule
+    plan.queued = plan.lead > 0 && !p.draft_probs;
+    if (plan.queued) {
+        if (g_lag_a > 0) {
+            plan.lag_a = g_lag_a;
+            plan.lag_c = g_lag_c > g_lag_a ? g_lag_c : g_lag_a;
+        } else {
+            // An item waiting for what it needs holds its CU slot, so items
+            // start well after their rows: the accept item about 1.4 resident
+            // grids of row segments later, the draw items about 2.3 (measured
+            // on MI355X; shorter lags wait more than they overlap).
+            int cus = 0;
+            if (device_cus(&cus) != hipSuccess) return SV_ERR_HIP;
+            const double window = static_cast<double>(cus) * kRestWgsPerCu;
+            double per_block = (2.0 * static_cast<double>(p.total) / p.B - 2.0 * plan.lead + 1.0) * g.nseg;
+            if (per_block < g.nseg) per_block = g.nseg;
+            plan.lag_a = static_cast<int32_t>(1.4 * window / per_block) + 1;
+            plan.lag_c = static_cast<int32_t>(2.3 * window / per_block) + 2;
+        }
+    }
     Fused f{};
     if (fused) {
         if (fused_grid(p.dtype, &f.blocks) != hipSuccess) return SV_ERR_HIP;
@@ -280,19 +326,29 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     } else {
         // Row pass: one pass over every needed row, or (early exit) the
         // leading positions, their accept scan, then the listed remainder.
+        // Early exit outside the gathered form ends in two launches: the
+        // remaining rows with the draws beside them, and the picks (with the
+        // redo of anything that round left over, usually nothing).
+        const bool queued = plan.queued != 0;
         if (plan.lead > 0)
             ok = launch(kKRowLead, [&] { return launch_row_lead(pr, plan, stream); }) &&
-                 launch(kKAcceptLead, [&] { return launch_accept_lead(pr, plan, stream); }) &&
-                 launch(kKRowStats, [&] {
-                     // (a settled sequence of the gathered form has not read its draft row yet,
-                     // so it has no early draw: the plain list pass suffices)
-                     return pr.draft_probs
-                                ? launch_row_list(pr, plan, plan.rest, plan.rest_n,
-                                                  (2 * p.total + p.B) * static_cast<int64_t>(g.nseg), stream)
-                                : launch_rest_and_early_draws(pr, plan, stream);
-                 });
+                 launch(kKAcceptLead, [&] { return launch_accept_lead(pr, plan, stream); });
         else
             ok = launch(kKRowStats, [&] { return launch_row_stats(pr, plan, stream); });
+        if (queued) {
+            ok = ok && launch(kKRest, [&] { return launch_rest_draws(pr, plan, stream); }) &&
+                 launch(kKDrawPick, [&] { return launch_draw_pick(pr, plan, stream); });
+            if (ev) {
+                g_ev_mask[g_timed_calls % kTimedCalls] = recorded;
+                ++g_timed_calls;
+            }
+            return ok ? SV_OK : SV_ERR_HIP;
+        }
+        if (plan.lead > 0)   // gathered form: a settled sequence has no early draw
+            ok = ok && launch(kKRowStats, [&] {
+                return launch_row_list(pr, plan, plan.sched, reinterpret_cast<const uint32_t*>(plan.blk_ctr),
+                                       (2 * p.total + p.B) * static_cast<int64_t>(g.nseg), stream);
+            });
         ok = ok && launch(kKAccept, [&] { return launch_accept(pr, plan, stream); });
         // Gathered form: the draft rows at the rejections.
         if (ok && pr.draft_probs)
@@ -571,6 +627,15 @@ sv_status_t spec_verify_set_early_exit(int32_t lead_positions) {
     if (lead_positions < kAutoLead || lead_positions > SV_K_MAX + 1) return SV_ERR_SHAPE;
     std::lock_guard<std::mutex> lock(g_mutex);
     g_lead = lead_positions;
+    return SV_OK;
+}
+
+sv_status_t spec_verify_set_queue(int32_t mode, int32_t lag_accept, int32_t lag_draw) {
+    if (mode < SV_QUEUE_OVERLAP || mode > SV_QUEUE_HANDOFF || lag_accept < 0 || lag_draw < 0) return SV_ERR_SHAPE;
+    std::lock_guard<std::mutex> lock(g_mutex);
+    g_queue_mode = mode;
+    g_lag_a = lag_accept;
+    g_lag_c = lag_draw;
     return SV_OK;
 }
 

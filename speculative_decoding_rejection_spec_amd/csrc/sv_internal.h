@@ -36,21 +36,33 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kKMax = SV_K_MAX;
 constexpr int kWaveCap = 8;            // band tokens listed per wave of a draw chunk
 
-// Statistics of one segment of one logit row.  Sampling rows keep their sum
-// as s * 2^R with an integer-valued reference R >= max(z) * c, c = log2(e)/T
-// (row_scale below), so every rescale is an exact power of two.
+// Statistics of one segment of one logit row, as two 64-bit words, each
+// written and read whole.  `head` packs the largest logit m of the segment
+// (exact; low 32 bits, fp32) with, for sampling rows, the integer-valued
+// reference exponent R >= max(z) * c, c = log2(e)/T (row_scale below; fp32
+// bits), and for greedy rows the lowest token id holding m.  `s` is, for
+// sampling rows, the sum over the segment of 2^(z*c - R) (0 for greedy
+// rows), so every rescale is an exact power of two.  kUnset64 in a word
+// marks it not yet written; a captured logit not yet written is kUnset32.
 struct SegStat {
-    float m;       // largest logit in the segment (exact)
-    float R;       // sampling rows: reference exponent (integer valued)
-    int32_t arg;   // greedy rows: lowest token id holding m
-    int32_t pad;
-    double s;      // sampling rows: sum over the segment of 2^(z*c - R)
+    uint64_t head;
+    double s;
 };
+constexpr uint64_t kUnset64 = ~0ull;
+constexpr uint32_t kUnset32 = ~0u;
+
+__device__ __forceinline__ uint64_t seg_head(float m, uint32_t hi) {
+    return static_cast<uint64_t>(__float_as_uint(m)) | (static_cast<uint64_t>(hi) << 32);
+}
+__device__ __forceinline__ float head_m(uint64_t h) { return __uint_as_float(static_cast<uint32_t>(h)); }
+__device__ __forceinline__ uint32_t head_hi(uint64_t h) { return static_cast<uint32_t>(h >> 32); }
 
 // kResidualPending: a residual draw of the gathered form, whose draft row n
 // is read after the accept scan (its maximum and normaliser come from that
 // row's SegStats; DrawTask::theta holds log2 S_p until then).
-enum : int32_t { kNone = 0, kResidual = 1, kBonus = 2, kResidualPending = 3 };
+// kTaskUnset: early exit's second round has not yet written the task (its
+// kind is written last, after the other fields are visible).
+enum : int32_t { kTaskUnset = -1, kNone = 0, kResidual = 1, kBonus = 2, kResidualPending = 3 };
 
 // The draw one sequence still needs after the accept scan.
 struct DrawTask {
@@ -71,12 +83,17 @@ struct ChunkSums {
     double b;    // sum of w_d over the same tokens
 };
 
-// One row segment of the second early-exit round.
+// One work item of the second early-exit round: a row segment (kind
+// kItemDraft / kItemTarget: row index in its array, segment), the accept
+// scan of an undecided sequence (kItemAccept: row = its block, i.e. the
+// order in which the lead accept scan listed it), or one draw chunk of such
+// a sequence (kItemChunk: row = block, seg = chunk).
+enum : int32_t { kItemDraft = 0, kItemTarget = 1, kItemAccept = 2, kItemChunk = 3 };
 struct RestItem {
-    int32_t b;           // sequence
-    int32_t is_target;   // target row (1) or draft row (0)
-    int32_t row;         // row index in its array
-    int32_t seg;         // segment
+    int32_t b;           // sequence (row items)
+    int32_t kind;        // kItem*
+    int32_t row;
+    int32_t seg;
 };
 
 // The caller's arguments, passed by value to every kernel.
@@ -117,12 +134,18 @@ struct Plan {
     uint32_t* ctr;       // fused form only: kCtrHeader words, then rows_done[B], ready[B], chunks_done[B]
     int32_t lead;        // early exit: positions every sequence reads first (0: one pass over all rows)
     int32_t* done;       // early exit: [B], 1 once a sequence's outcome is known from its leading positions
-    RestItem* rest;      // early exit: [(2 * total + B) * nseg], the row segments still to read
-    uint32_t* rest_n;    // early exit: number of entries in rest
+    RestItem* sched;     // early exit: [(2 * total + B) * nseg + B * (1 + nchunk)], the second round's items
+    uint64_t* blk_ctr;   // early exit: (undecided sequences listed) << 32 | (row segments listed)
     RestItem* dlist;     // gathered form: [B * nseg], segments of the draft rows at rejections
     uint32_t* dlist_n;   // gathered form: number of entries in dlist
-    int32_t* early;      // early exit: [B], sequences whose draw runs beside the remaining rows
+    int32_t* early;      // early exit: [B], sampling sequences the leading positions settled
     uint32_t* early_n;   // early exit: number of entries in early
+    int32_t* blk_seq;    // early exit: [B] the sequence listed as block i
+    int32_t lag_a, lag_c;// early exit: the accept item of block j follows block j + lag_a, its chunks
+                         // follow block j + lag_c (huge: none inserted, the gathered form)
+    int32_t* aband;      // [B] 1: sequence b is left to the pick launch
+    int32_t queued;      // early exit with the draws beside the rows (not the gathered form)
+    int32_t queue_mode;  // SV_QUEUE_*: where the second round's draw chunks are summed
 };
 
 // Plan::done values (early exit).
@@ -148,6 +171,7 @@ hipError_t launch_row_stats(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_row_list(const Problem& p, const Plan& plan, const RestItem* list, const uint32_t* count,
                            int64_t max_items, hipStream_t s);
 hipError_t launch_rest_and_early_draws(const Problem& p, const Plan& plan, hipStream_t s);
+hipError_t launch_rest_draws(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_row_lead(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_accept(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_accept_lead(const Problem& p, const Plan& plan, hipStream_t s);

@@ -124,6 +124,15 @@ def test_geometry_knob(lib):
     assert lib.spec_verify_workspace_size(64, 256, 128256, 1) == base
 
 
+def test_queue_knob(lib):
+    assert lib.spec_verify_set_queue(3, 0, 0) == SHAPE
+    assert lib.spec_verify_set_queue(-1, 0, 0) == SHAPE
+    assert lib.spec_verify_set_queue(0, -1, 0) == SHAPE
+    assert lib.spec_verify_set_queue(0, 0, -1) == SHAPE
+    for mode in (2, 1, 0):
+        assert lib.spec_verify_set_queue(mode, 0, 0) == OK
+
+
 def test_kernel_times_without_timed_call(lib):
     buf = (ctypes.c_float * 8)()
     assert lib.spec_verify_kernel_times(buf, 8) == -1

@@ -19,6 +19,7 @@ from test_oracle_draft import gathered_q
 pytestmark = pytest.mark.gpu
 
 FORMS = ["early", "full", "fused"]
+FORM = {"name": None}
 
 
 @pytest.fixture(scope="module", params=FORMS)
@@ -32,6 +33,7 @@ def sv(cuda, request):
     sv.set_geometry(0, 0)
     sv.set_mode(sv.SV_MODE_FUSED if request.param == "fused" else sv.SV_MODE_STAGED)
     sv.set_early_exit(1 if request.param == "early" else 0)
+    FORM["name"] = request.param
     print(f"[form {request.param}]", flush=True)
     yield sv
     sv.set_mode(sv.SV_MODE_AUTO)
@@ -157,6 +159,23 @@ def test_gathered_ignores_other_draft_rows(sv, cuda):
     w2 = wl.Workload(**{**w.__dict__, "draft": wl.bf16_round(draft)})
     got = run_gathered(sv, w2, qg, cuda)
     assert np.array_equal(got["tokens"], base["tokens"]) and np.array_equal(got["n"], base["n"])
+
+
+def test_gathered_leads_past_short_sequences(sv, cuda):
+    """Leading positions 2 and 3 on C5 (k_b from 1): sequences with k_b below
+    the lead settle in the first round with their bonus draw still to make."""
+    if FORM["name"] != "early":
+        pytest.skip("early-exit form only")
+    w = wl.make_workload("c5", trial=6, B=128)
+    assert np.any(w.k < 3)
+    qg = gathered_q(w)
+    ref = oracle.verify(w, threads=16, draft_probs=qg)
+    try:
+        for lead in (2, 3):
+            sv.set_early_exit(lead)
+            compare(w, run_gathered(sv, w, qg, cuda), ref, f"gathered lead {lead}")
+    finally:
+        sv.set_early_exit(1)
 
 
 def test_gathered_data_errors(sv, cuda):

@@ -359,6 +359,39 @@ def test_early_exit_leads(sv, cuda):
         sv.set_early_exit(1)
 
 
+def test_queue_modes_bitwise(sv, cuda):
+    """Early exit's second round with its accept scans and draw chunks beside
+    the rows (automatic lags, lags of 1 and 2 sequences so items wait for
+    rows still streaming, lags past the end so every item follows all rows),
+    with all of them in the final launch, or with every undecided sequence
+    taking the path of a wait that runs out: the same chunk sums and picks, so
+    bit-identical outputs, and parity with the oracle (full C4 and C5
+    batches; C5 also with leads 2 and 64, where sequences with k_b < lead
+    settle in the first round)."""
+    if CURRENT["mode"] != "early":
+        pytest.skip("early-exit form only")
+    cases = [("c4", None, 1), ("c5", None, 1), ("c5", None, 2), ("c5", 96, 64)]
+    settings = [(sv.SV_QUEUE_OVERLAP, 0, 0), (sv.SV_QUEUE_OVERLAP, 1, 1), (sv.SV_QUEUE_OVERLAP, 1, 2),
+                (sv.SV_QUEUE_OVERLAP, 5000, 5000), (sv.SV_QUEUE_FINAL, 0, 0), (sv.SV_QUEUE_HANDOFF, 0, 0)]
+    try:
+        for name, B, lead in cases:
+            w = workload(name, 0, B)
+            ref = oracle.verify(w, threads=16)
+            sv.set_early_exit(lead)
+            outs = []
+            for mode, la, lc in settings:
+                print(f"  {name} lead {lead} queue {mode} lags {la} {lc}", flush=True)
+                sv.set_queue(mode, la, lc)
+                outs.append(run_gpu(sv, w, cuda, probs=True))
+            for o, st in zip(outs[1:], settings[1:]):
+                for key in outs[0]:
+                    np.testing.assert_array_equal(o[key], outs[0][key], err_msg=f"{name} lead {lead} {st} {key}")
+            compare(w, outs[0], ref, f"{name} lead {lead} queued")
+    finally:
+        sv.set_queue(sv.SV_QUEUE_OVERLAP)
+        sv.set_early_exit(1)
+
+
 def test_fused_matches_staged_bitwise(sv, cuda):
     """Both forms run the same row pass, accept scan and chunk sums, so the
     counts and diagnostics are identical on the full C4 batch; the pick scans
