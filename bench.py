@@ -41,15 +41,11 @@ EVENT_EVERY = 8
 METRIC = "sequences verified/s and achieved HBM GB/s (% of peak), B=256 k=8 V=152064 bf16"
 # Counter summaries per roofline kernel, and the sources each kernel is built from.
 COUNTERS = {"row_stats": os.path.join(ROOT, "profiles", "row_stats_c4_counters.txt"),
-            "row_lead+row_stats": os.path.join(ROOT, "profiles", "row_pass_early_exit_c4_counters.txt"),
             "fused": os.path.join(ROOT, "profiles", "fused_c4_counters.txt"),
-            "row_lead+rest+draw_pick": os.path.join(ROOT, "profiles", "verify_c4_queued_counters.txt")}
+            "rest": os.path.join(ROOT, "profiles", "second_round_c4_counters.txt")}
 KERNEL_SOURCES = {"row_stats": ["row_stats.hip", "row_pass.h", "sv_internal.h"],
-                  "row_lead+row_stats": ["row_stats.hip", "rest_draw.hip", "row_pass.h", "draw_pass.h",
-                                         "sv_internal.h"],
                   "fused": ["fused.hip", "row_pass.h", "accept_scan.h", "draw_pass.h", "sv_internal.h"],
-                  "row_lead+rest+draw_pick": ["row_stats.hip", "rest_queue.hip", "draw.hip", "row_pass.h",
-                                              "accept_scan.h", "draw_pass.h", "sv_internal.h"]}
+                  "rest": ["second_round.hip", "row_pass.h", "accept_scan.h", "draw_pass.h", "sv_internal.h"]}
 
 
 def source_hash(kernel: str) -> str:
@@ -214,14 +210,14 @@ def main():
     early = "row_lead" in launched
     sv.timing(False)
     # The roofline kernel: the row pass (one launch, or the two launches of
-    # early exit in the gathered form), the fused kernel, or -- early exit
-    # with queued draws -- the three launches that stream every row and draw
-    # row (the draws run inside the second round and the final launch).
+    # early exit in the gathered form), the fused kernel, or -- early exit --
+    # the second round, the dominant launch, which streams the remaining rows
+    # and every draw row.
     queued = "rest" in launched
     if form == "fused":
         roof = ["fused"]
     elif queued:
-        roof = ["row_lead", "rest", "draw_pick"]
+        roof = ["rest"]
     else:
         roof = ["row_lead", "row_stats"] if early else ["row_stats"]
     if "row_draft" in launched:
@@ -273,6 +269,7 @@ def main():
         decided = (n < L) | (k < L)
         rest_rows = np.where(decided, 0, (k - L + 1) + np.where(dsamp, k - L, 0))
         read_rows = int(np.sum(lead_rows + rest_rows))
+        second_rows = int(np.sum(rest_rows))
     else:
         read_rows = full_rows
     if gathered:                                 # the draft row at each rejection
@@ -291,7 +288,8 @@ def main():
     if k1_live is not None:
         # The row pass reads every needed row once; the fused kernel also
         # reads the draw rows.
-        kbytes = total_bytes if (roof_kernel == "fused" or queued) else k1_bytes
+        kbytes = total_bytes if roof_kernel == "fused" else (
+            (second_rows + draw_rows) * row_bytes if queued else k1_bytes)
         achieved = kbytes / (k1_live / 1e3) / 1e9
         roofline = {"bound": "hbm", "kernel": roof_kernel, "achieved": round(achieved, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),

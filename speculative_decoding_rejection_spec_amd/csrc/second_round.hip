@@ -1,4 +1,4 @@
-// rest_queue.hip -- early exit outside the gathered form: the second round,
+// second_round.hip -- early exit outside the gathered form: the second round,
 // which streams the remaining rows and makes the draws beside them.
 //
 // Second round (rest_draws_kernel).  The lead accept scan listed, for each

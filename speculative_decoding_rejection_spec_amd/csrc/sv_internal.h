@@ -1,11 +1,8 @@
 // sv_internal.h -- declarations shared by the HIP sources of libspecverify.
 //
 // Data flow of one call, staged form (every kernel is enqueued on the
-// caller's stream; kernel boundaries publish each step's results).  With
-// early exit (Plan::lead > 0) steps 1 and 2 first run over the leading
-// positions of every sequence (row_lead, accept_lead); sequences whose
-// outcome those decide are done, and steps 1 and 2 then run over the
-// remaining rows of the others only:
+// caller's stream; kernel boundaries publish each step's results).  One pass
+// (Plan::lead == 0):
 //   1. row pass    (row_stats.hip, row_pass.h): one workgroup per (logit row,
 //                  segment) streams the segment once and writes a SegStat;
 //   2. accept scan (accept.hip, accept_scan.h): one wave64 per sequence
@@ -17,11 +14,17 @@
 //                  fp64 chunk sums;
 //   4. draw_pick   (draw.hip, draw_pass.h): one workgroup per sequence
 //                  locates the chunk that holds u * Z and the token inside it.
-// Fused form (fused.hip): one persistent launch runs the same four steps as
-// work items taken from a device-side queue; the last workgroup to finish a
+// Early exit (Plan::lead > 0): steps 1 and 2 run over the leading positions
+// of every sequence (row_lead, accept_lead), which settles some sequences and
+// lists the remaining rows of the others; then one launch
+// (second_round.hip) streams those rows, runs the undecided sequences'
+// accept scans and every draw chunk beside them, and draw_pick picks.  The
+// gathered form instead streams the listed rows (row_list), then runs steps
+// 2-4 with the draft rows at rejections read in between.
+// Fused form (fused.hip): one persistent launch runs the four steps as work
+// items taken from a device-side queue; the last workgroup to finish a
 // sequence's rows runs its accept scan and the last to finish its chunks
-// runs its pick, so the draws of early sequences overlap the streaming of
-// later ones.
+// runs its pick.
 #pragma once
 
 #include <hip/hip_runtime.h>
