@@ -289,7 +289,7 @@ def main():
         # The row pass reads every needed row once; the fused kernel also
         # reads the draw rows.
         kbytes = total_bytes if roof_kernel == "fused" else (
-            (second_rows + draw_rows) * row_bytes if queued else k1_bytes)
+            (second_rows + (draw_rows if args.queue == 0 else 0)) * row_bytes if queued else k1_bytes)
         achieved = kbytes / (k1_live / 1e3) / 1e9
         roofline = {"bound": "hbm", "kernel": roof_kernel, "achieved": round(achieved, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),

@@ -110,8 +110,10 @@ __device__ __forceinline__ void list_rest(const Problem& p, const Plan& plan, in
     for (int32_t e = lane; e < cnt; e += 64) {
         const int32_t j = e / nseg, sg = e - j * nseg;
         const bool tgt = j < nt;
-        const int64_t row = tgt ? o + b + limit + j : o + limit + (j - nt);
-        plan.sched[at + e] = RestItem{b, tgt ? kItemTarget : kItemDraft, static_cast<int32_t>(row), sg};
+        const int32_t pos = limit + (tgt ? j : j - nt);          // position in the sequence
+        const int64_t row = tgt ? o + b + pos : o + pos;
+        const int32_t x = (!greedy && pos < k) ? p.tokens[o + pos] : -1;   // (validated by the scan)
+        plan.sched[at + e] = rest_item(b, static_cast<int32_t>(row), tgt ? kItemTarget : kItemDraft, sg, x);
         SegStat* st = plan.seg + (tgt ? row : ntarget + row) * nseg + sg;
         st->head = kUnset64;
         st->s = __longlong_as_double(static_cast<long long>(kUnset64));
@@ -119,12 +121,12 @@ __device__ __forceinline__ void list_rest(const Problem& p, const Plan& plan, in
     }
     int64_t q = at + cnt;
     if (i >= plan.lag_a) {
-        if (lane == 0) plan.sched[q] = RestItem{-1, kItemAccept, static_cast<int32_t>(i - plan.lag_a), 0};
+        if (lane == 0) plan.sched[q] = rest_item(static_cast<int32_t>(i - plan.lag_a), 0, kItemAccept, 0, -1);
         ++q;
     }
     if (i >= plan.lag_c)
         for (int32_t c = lane; c < nchunk; c += 64)
-            plan.sched[q + c] = RestItem{-1, kItemChunk, static_cast<int32_t>(i - plan.lag_c), c};
+            plan.sched[q + c] = rest_item(static_cast<int32_t>(i - plan.lag_c), 0, kItemChunk, c, -1);
     if (lane == 0) {
         plan.blk_seq[i] = b;
         if (!greedy) plan.task[b].kind = kTaskUnset;
@@ -252,7 +254,7 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
         if (pending) {
             const uint32_t base = atomicAdd(plan.dlist_n, static_cast<uint32_t>(plan.nseg));
             for (int32_t sg = 0; sg < plan.nseg; ++sg) {
-                plan.dlist[base + sg] = RestItem{b, kItemDraft, static_cast<int32_t>(drow), sg};
+                plan.dlist[base + sg] = rest_item(b, static_cast<int32_t>(drow), kItemDraft, sg, -1);
             }
         }
         DrawTask* t = plan.task + b;

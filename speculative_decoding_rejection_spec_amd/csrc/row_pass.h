@@ -19,9 +19,15 @@
 //
 // Per logit: one unpack (shift or mask), half a v_max3, one v_fma
 // (z * c - R), one v_exp_f32, one add.  The running sum is kept relative to
-// an integer-valued reference R = ceil(m * c) (c = log2(e) / T), so
-// rescaling when the maximum grows is an exact v_ldexp; the workgroup-wide
-// merge is in fp64, also by exact powers of two.
+// an integer-valued reference R (c = log2(e) / T), so rescaling when the
+// maximum grows is an exact v_ldexp; the workgroup-wide merge is in fp64,
+// also by exact powers of two.  R starts at ceil(m0 * c) for the largest
+// logit m0 of the wave's first tile and is raised to ceil(m * c) only when
+// a logit m exceeds it by more than kSlack (in log2 units): with every lane
+// raising at its own new maxima, some lane of a wave raised on nearly every
+// tile; seeded from the wave and given that slack, a raise is rare, and the
+// exponent argument z * c - R stays below kSlack + 1, where its fp32
+// rounding (at most 2^-23) adds under 1e-7 relative to a term.
 #pragma once
 
 #include "sv_internal.h"
@@ -71,25 +77,32 @@ __device__ __forceinline__ float max_of(const float* x) {
     return t;
 }
 
-// Online sum of 2^(z*c - R) with R = ceil(m*c) for the running maximum m.
+// Online sum of 2^(z*c - R) with an integer-valued reference R >= m*c - kSlack
+// for the running maximum m.
 struct SoftmaxAcc {
+    static constexpr float kSlack = 2.f;
     float m = -INFINITY;    // running maximum logit
     float R = -INFINITY;    // reference exponent (integer valued)
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
     float c;
 
+    // The first reference, from the largest logit of the wave's first tile
+    // (-inf: none; the first logit seen sets it).  Called before any add.
+    __device__ __forceinline__ void prime(float wm) {
+        if (wm > -INFINITY) R = ceilf(wm * c);
+    }
     __device__ __forceinline__ void raise(float tm) {
         const float Rn = ceilf(tm * c);
         // exact rescale by 2^(R - Rn); R = -inf only while the sums are 0
         const int d = static_cast<int>(fmaxf(R - Rn, -512.f));
         s0 = ldexpf(s0, d); s1 = ldexpf(s1, d); s2 = ldexpf(s2, d); s3 = ldexpf(s3, d);
-        m = tm;
         R = Rn;
     }
     template <int N>
     __device__ __forceinline__ void add(const float* x, int32_t) {
         const float tm = max_of<N>(x);
-        if (tm > m) raise(tm);
+        m = fmaxf(m, tm);
+        if (tm * c > R + kSlack) raise(tm);
 #pragma unroll
         for (int j = 0; j < N; j += 4) {
             s0 += hw_exp2(fmaf(x[j], c, -R));
@@ -99,7 +112,8 @@ struct SoftmaxAcc {
         }
     }
     __device__ __forceinline__ void add1(float x, int32_t) {
-        if (x > m) raise(x);
+        m = fmaxf(m, x);
+        if (x * c > R + kSlack) raise(x);
         s0 += hw_exp2(fmaf(x, c, -R));
     }
 };
@@ -109,6 +123,8 @@ struct SoftmaxAcc {
 struct ArgmaxAcc {
     float m = -INFINITY;
     int32_t a = INT32_MAX;
+
+    __device__ __forceinline__ void prime(float) {}
 
     template <int N>
     __device__ __forceinline__ void add(const float* x, int32_t base) {
@@ -186,6 +202,16 @@ __device__ __forceinline__ void stream_segment(const void* row_v, int64_t s0, in
         buf[u] = load_tile(u);
         __builtin_amdgcn_sched_barrier(0);
     }
+    {
+        // The wave's largest logit in its first tile (and head elements)
+        // seeds the accumulator's reference.
+        float x[N];
+        Elem<DT>::unpack(buf[0], x);
+        float lm = (0 < nfull || tid < rem) ? max_of<N>(x) : -INFINITY;
+        if (tid < head) lm = fmaxf(lm, hv);
+        for (int off = 32; off > 0; off >>= 1) lm = fmaxf(lm, __shfl_xor(lm, off, 64));
+        acc.prime(lm);
+    }
     if (tid < head) acc.add1(hv, static_cast<int32_t>(hi));
 
     // Steady state: tiles i .. i+W-1 are full (i + 2W <= nt <= nfull + 1).
@@ -240,10 +266,14 @@ struct RowLds {
 // (sequences with an unusable temperature, draft rows of greedy sequences)
 // are skipped.  kCo selects stores that other workgroups of the same launch
 // may read (see st_co).  kWindow: 16-byte loads in flight per lane (0: the
-// dtype's default, sized for full occupancy).
+// dtype's default, sized for full occupancy).  x_hint: the drafted token of
+// this row (-1: none), when the caller knows it, else kXFromOffsets.
+constexpr int32_t kXFromOffsets = -2;   // row_segment's x_hint: look the drafted token up
+
 template <int DT, bool kCo, int kWindowArg = 0>
 __device__ __forceinline__ void row_segment(const Problem& p, const Plan& plan, int32_t b, bool is_target,
-                                            int64_t r, int64_t seg, RowLds& lds) {
+                                            int64_t r, int64_t seg, RowLds& lds,
+                                            int32_t x_hint = kXFromOffsets) {
     using namespace rowpass;
     constexpr int kWindow = kWindowArg > 0 ? kWindowArg : Elem<DT>::kWindow;
     const float T = p.temperature[b];
@@ -263,7 +293,10 @@ __device__ __forceinline__ void row_segment(const Problem& p, const Plan& plan, 
     // load, at s0 when it captures nothing, so no load sits under a branch.
     bool capture = false;
     int64_t xc = s0;
-    if (!greedy) {
+    if (!greedy && x_hint != kXFromOffsets) {
+        capture = x_hint >= s0 && x_hint < s1;
+        if (capture) xc = x_hint;
+    } else if (!greedy) {
         const int64_t o = p.offsets ? static_cast<int64_t>(p.offsets[b]) : static_cast<int64_t>(b) * p.k_uniform;
         const int64_t k = p.offsets ? static_cast<int64_t>(p.offsets[b + 1]) - o : p.k_uniform;
         const int64_t i = is_target ? r - o - b : r - o;

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void row_list_kernel(Problem p, Plan plan
     if (w >= *count) return;
     const RestItem it = list[w];
     __shared__ RowLds lds;
-    row_segment<DT, false>(p, plan, it.b, it.kind == kItemTarget, it.row, it.seg, lds);
+    row_segment<DT, false>(p, plan, it.b, item_kind(it) == kItemTarget, it.row, item_seg(it), lds, it.x);
 }
 
 // Early exit, first round: the rows of positions < lead of every sequence.

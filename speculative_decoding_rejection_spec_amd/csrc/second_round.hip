@@ -97,20 +97,21 @@ __global__ __launch_bounds__(kThreads) void rest_draws_kernel(Problem p, Plan pl
             int64_t t = v - vend;
             const int64_t na = min(nblk, la);
             if (t < na) {
-                it = RestItem{-1, kItemAccept, static_cast<int32_t>(nblk - na + t), 0};
+                it = rest_item(static_cast<int32_t>(nblk - na + t), 0, kItemAccept, 0, -1);
             } else {
                 t -= na;
-                it = RestItem{-1, kItemChunk, static_cast<int32_t>(nblk - min(nblk, lc) + t / nchunk),
-                              static_cast<int32_t>(t % nchunk)};
+                it = rest_item(static_cast<int32_t>(nblk - min(nblk, lc) + t / nchunk), 0, kItemChunk,
+                               static_cast<int32_t>(t % nchunk), -1);
             }
         }
-        if (it.kind == kItemTarget || it.kind == kItemDraft) {
-            row_segment<DT, true>(p, plan, it.b, it.kind == kItemTarget, it.row, it.seg, lds.row);
+        const int32_t kind = item_kind(it);
+        if (kind == kItemTarget || kind == kItemDraft) {
+            row_segment<DT, true>(p, plan, it.b, kind == kItemTarget, it.row, item_seg(it), lds.row, it.x);
             return;
         }
-        b = plan.blk_seq[it.row];
+        b = plan.blk_seq[it.b];
         if (plan.queue_mode == SV_QUEUE_FINAL) return;
-        if (it.kind == kItemAccept) {
+        if (kind == kItemAccept) {
             if (tid >= 64) return;                     // one wave runs it
             bool ready = plan.queue_mode != SV_QUEUE_HANDOFF;
             for (uint32_t polls = 0; ready; ++polls) {
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void rest_draws_kernel(Problem p, Plan pl
         }
         // a draw chunk of an undecided sequence
         if (p.temperature[b] == 0.f) return;       // greedy: nothing to draw
-        c = it.seg;
+        c = item_seg(it);
         if (tid == 0) {
             bool ready = false;
             if (plan.queue_mode != SV_QUEUE_HANDOFF)

@@ -42,8 +42,8 @@ constexpr int kWaveCap = 8;            // band tokens listed per wave of a draw 
 // Statistics of one segment of one logit row, as two 64-bit words, each
 // written and read whole.  `head` packs the largest logit m of the segment
 // (exact; low 32 bits, fp32) with, for sampling rows, the integer-valued
-// reference exponent R >= max(z) * c, c = log2(e)/T (row_scale below; fp32
-// bits), and for greedy rows the lowest token id holding m.  `s` is, for
+// reference exponent R >= max(z) * c - 2, c = log2(e)/T (row_scale below;
+// fp32 bits), and for greedy rows the lowest token id holding m.  `s` is, for
 // sampling rows, the sum over the segment of 2^(z*c - R) (0 for greedy
 // rows), so every rescale is an exact power of two.  kUnset64 in a word
 // marks it not yet written; a captured logit not yet written is kUnset32.
@@ -87,17 +87,21 @@ struct ChunkSums {
 };
 
 // One work item of the second early-exit round: a row segment (kind
-// kItemDraft / kItemTarget: row index in its array, segment), the accept
-// scan of an undecided sequence (kItemAccept: row = its block, i.e. the
-// order in which the lead accept scan listed it), or one draw chunk of such
-// a sequence (kItemChunk: row = block, seg = chunk).
+// kItemDraft / kItemTarget), the accept scan of an undecided sequence
+// (kItemAccept), or one draw chunk of such a sequence (kItemChunk).  The
+// gathered form's row lists use the row-segment kinds.
 enum : int32_t { kItemDraft = 0, kItemTarget = 1, kItemAccept = 2, kItemChunk = 3 };
 struct RestItem {
-    int32_t b;           // sequence (row items)
-    int32_t kind;        // kItem*
-    int32_t row;
-    int32_t seg;
+    int32_t b;      // row segments: the sequence; accept and draw items: its block (listing order)
+    int32_t row;    // row segments: row index in its array
+    int32_t kseg;   // kind << 28 | segment (row segments) or chunk (draw items)
+    int32_t x;      // row segments: the drafted token whose logit the row's segments capture, or -1
 };
+__device__ __forceinline__ RestItem rest_item(int32_t b, int32_t row, int32_t kind, int32_t seg, int32_t x) {
+    return RestItem{b, row, (kind << 28) | seg, x};
+}
+__device__ __forceinline__ int32_t item_kind(const RestItem& it) { return it.kseg >> 28; }
+__device__ __forceinline__ int32_t item_seg(const RestItem& it) { return it.kseg & 0x0FFFFFFF; }
 
 // The caller's arguments, passed by value to every kernel.
 struct Problem {
