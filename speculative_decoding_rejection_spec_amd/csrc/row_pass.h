@@ -78,12 +78,18 @@ __device__ __forceinline__ float max_of(const float* x) {
 }
 
 // Online sum of 2^(z*c - R) with an integer-valued reference R >= m*c - kSlack
-// for the running maximum m.
+// for the running maximum m, in 4 fp32 partial sums: sum j takes logit j of
+// each vector (fp32, 4 per vector) or the pair j, j + 4 added first (bf16, 8
+// per vector), and a head or tail element goes to sum 3.  With at most
+// max_seg_elems(dtype) logits per segment a sum is built from at most 40
+// vectors' terms and 2 single ones, so its rounding stays below 42 * 2^-24
+// relative.
+constexpr int kSums = 4;
 struct SoftmaxAcc {
     static constexpr float kSlack = 2.f;
     float m = -INFINITY;    // running maximum logit
     float R = -INFINITY;    // reference exponent (integer valued)
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    float s[kSums] = {};
     float c;
 
     // The first reference, from the largest logit of the wave's first tile
@@ -95,26 +101,35 @@ struct SoftmaxAcc {
         const float Rn = ceilf(tm * c);
         // exact rescale by 2^(R - Rn); R = -inf only while the sums are 0
         const int d = static_cast<int>(fmaxf(R - Rn, -512.f));
-        s0 = ldexpf(s0, d); s1 = ldexpf(s1, d); s2 = ldexpf(s2, d); s3 = ldexpf(s3, d);
+#pragma unroll
+        for (int j = 0; j < kSums; ++j) s[j] = ldexpf(s[j], d);
         R = Rn;
     }
     template <int N>
     __device__ __forceinline__ void add(const float* x, int32_t) {
+        static_assert(N == kSums || N == 2 * kSums, "partial sums per vector");
         const float tm = max_of<N>(x);
         m = fmaxf(m, tm);
         if (tm * c > R + kSlack) raise(tm);
 #pragma unroll
-        for (int j = 0; j < N; j += 4) {
-            s0 += hw_exp2(fmaf(x[j], c, -R));
-            if (j + 1 < N) s1 += hw_exp2(fmaf(x[j + 1], c, -R));
-            if (j + 2 < N) s2 += hw_exp2(fmaf(x[j + 2], c, -R));
-            if (j + 3 < N) s3 += hw_exp2(fmaf(x[j + 3], c, -R));
+        for (int j = 0; j < kSums; ++j) {
+            if constexpr (N == 2 * kSums)
+                s[j] += hw_exp2(fmaf(x[j], c, -R)) + hw_exp2(fmaf(x[j + kSums], c, -R));
+            else
+                s[j] += hw_exp2(fmaf(x[j], c, -R));
         }
     }
+    // A single logit (a segment's unaligned head or tail): its own sum.
     __device__ __forceinline__ void add1(float x, int32_t) {
         m = fmaxf(m, x);
         if (x * c > R + kSlack) raise(x);
-        s0 += hw_exp2(fmaf(x, c, -R));
+        s[kSums - 1] += hw_exp2(fmaf(x, c, -R));
+    }
+    __device__ __forceinline__ double total() const {
+        double t = 0.0;
+#pragma unroll
+        for (int j = 0; j < kSums; ++j) t += static_cast<double>(s[j]);
+        return t;
     }
 };
 
@@ -328,7 +343,7 @@ __device__ __forceinline__ void row_segment(const Problem& p, const Plan& plan, 
         acc.c = row_scale(T);
         stream_segment<DT, kWindow>(row, s0, s1, acc);
         float m = acc.m, R = acc.R;
-        double s = (static_cast<double>(acc.s0) + acc.s1) + (static_cast<double>(acc.s2) + acc.s3);
+        double s = acc.total();
         for (int off = 32; off > 0; off >>= 1)
             merge_softmax(m, R, s, __shfl_xor(m, off, 64), __shfl_xor(R, off, 64),
                           __shfl_xor(s, off, 64));

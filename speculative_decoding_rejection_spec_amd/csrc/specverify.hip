@@ -106,9 +106,12 @@ struct Geometry {
 };
 
 // Splits a row of V logits into n <= max_pieces pieces of about `target`
-// elements, each a multiple of `unit` elements long, none empty.
-void split(int64_t V, int64_t target, int64_t max_pieces, int64_t unit, int32_t& n, int64_t& len) {
+// elements (at most max_len when that fits max_pieces; max_len a multiple of
+// unit), each a multiple of `unit` elements long, none empty.
+void split(int64_t V, int64_t target, int64_t max_pieces, int64_t unit, int64_t max_len, int32_t& n,
+           int64_t& len) {
     int64_t pieces = (V + target / 2) / target;
+    if (pieces < ceil_div(V, max_len)) pieces = ceil_div(V, max_len);
     if (pieces < 1) pieces = 1;
     if (pieces > max_pieces) pieces = max_pieces;
     len = ceil_div(ceil_div(V, pieces), unit) * unit;
@@ -118,8 +121,8 @@ void split(int64_t V, int64_t target, int64_t max_pieces, int64_t unit, int32_t&
 bool make_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dtype, int64_t seg_elems,
                    int64_t chunk_elems, Geometry& g) {
     const int64_t unit = row_unit(dtype);
-    split(V, seg_elems, 1 << 20, seg_elems >= unit ? unit : 8, g.nseg, g.seg_len);
-    split(V, chunk_elems, kMaxChunks, 8, g.nchunk, g.chunk_len);
+    split(V, seg_elems, 1 << 20, seg_elems >= unit ? unit : 8, max_seg_elems(dtype), g.nseg, g.seg_len);
+    split(V, chunk_elems, kMaxChunks, 8, V, g.nchunk, g.chunk_len);
     const int64_t rows = 2 * total + B;
     // (the second round's grid holds every row segment and every draw chunk)
     if (rows * g.nseg + static_cast<int64_t>(B) * (1 + g.nchunk) > 0x7FFFFFFFll) return false;

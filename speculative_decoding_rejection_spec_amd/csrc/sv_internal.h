@@ -38,6 +38,11 @@ constexpr int kThreads = 256;          // workgroup size of every kernel (4 x wa
 constexpr int kWaves = kThreads / 64;
 constexpr int kKMax = SV_K_MAX;
 constexpr int kWaveCap = 8;            // band tokens listed per wave of a draw chunk
+// Row pass: the longest segment, so that each lane's fp32 partial sums
+// take at most 40 vectors (16 bytes: 8 bf16 or 4 fp32 logits) each.
+__host__ __device__ constexpr int64_t max_seg_elems(int32_t dtype) {
+    return 40 * kThreads * (dtype == SV_BF16 ? 8 : 4);
+}
 
 // Statistics of one segment of one logit row, as two 64-bit words, each
 // written and read whole.  `head` packs the largest logit m of the segment
