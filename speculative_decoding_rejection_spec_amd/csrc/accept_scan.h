@@ -17,9 +17,10 @@
 // drafted token of each row; p(x) = 2^(z_x c - R) / S_R exactly as the row
 // pass summed it (a softmax at the temperature log2(e)/c, within
 // 6e-8 relative of T); it is formed in fp64.  Worst-case relative error of
-// S_R: about 2e-6 (fp32 partial sums of <= 40 terms, v_exp_f32, the rounded
-// exponent argument); alpha is therefore within 5e-6 of its exact value,
-// inside the 1e-5 band where |u - alpha| counts as a tie.
+// S_R: under 3e-6 (fp32 partial sums of at most 42 terms: 2.5e-6; v_exp_f32
+// and the rounded exponent argument, below 3 in magnitude: 3e-7; the merges
+// are in fp64); alpha is therefore within 6e-6 of its exact value, inside
+// the 1e-5 band where |u - alpha| counts as a tie.
 //
 // Sampling sequences leave the emitted token to the draw and record a
 // DrawTask: a residual draw at row n if n < k, a bonus draw at row k
