@@ -46,7 +46,9 @@
  *   R7 the pages' multinomial draw is an inverse CDF in ascending token id
  *      with a strict '>' (zero-mass tokens are never picked);
  *   R8 greedy ties go to the lowest token id;
- *   R11 if a rejection leaves Z < 1e-9 the draw falls back to p_n (flag D).
+ *   R11 if a rejection leaves Z < 1e-9 the draw falls back to p_n (flag D);
+ *   R26 a logit row the scan reaches (positions up to the first rejection)
+ *      whose maximum is not finite makes the sequence a data error (flag E).
  *
  * Two more entry points follow the same pages: oracle_verify_gathered (the
  * accept tests divide by the drafter's gathered q_i(x_i) instead of the draft
@@ -117,6 +119,14 @@ static double orc_row_argmax(const void *rows, int dtype, int64_t row, int64_t V
     }
     if (arg) *arg = at;
     return best;
+}
+
+/* A sequence whose scan reaches a logit row with a non-finite maximum:
+ * every token slot -1, n = -1, flag E (reading R26). */
+static void orc_row_error(int32_t *out, int k, int32_t *out_n, int32_t *out_flag) {
+    for (int i = 0; i <= k; ++i) out[i] = -1;
+    *out_n = -1;
+    if (out_flag) *out_flag = ORC_FLAG_E;
 }
 
 /* Temperature softmax of one row: p_v = exp((z_v - m)/T) / S with
@@ -329,12 +339,17 @@ static int orc_verify_range(const void *target, const void *draft, int32_t dtype
 
         if (T == 0.0) {
             /* Greedy: accept while the draft equals the target argmax. */
-            int n = k;
+            int n = k, row_bad = 0;
             int64_t a = 0;
             for (int i = 0; i <= k; ++i) {
                 double m = orc_row_argmax(target, dtype, trow + i, V, &a);
                 if (out_row_max) out_row_max[trow + i] = m;
+                if (!isfinite(m)) { row_bad = 1; break; }      /* reading R26 */
                 if (i == k || x[i] != a) { n = i; break; }
+            }
+            if (row_bad) {
+                orc_row_error(out, k, out_n + b, out_flags ? out_flags + b : NULL);
+                continue;
             }
             orc_write_tokens(out, k, x, n, (int32_t)a);
             out_n[b] = n;
@@ -347,24 +362,38 @@ static int orc_verify_range(const void *target, const void *draft, int32_t dtype
         /* Sampling: tempered softmax of every needed row, then the test. */
         const double *P[ORC_K_MAX + 1];
         const double *Q[ORC_K_MAX + 1];
+        double mt[ORC_K_MAX + 1], md[ORC_K_MAX + 1];
         for (int i = 0; i <= k; ++i) {
-            double *p = buf + (size_t)i * V, m, S;
-            orc_softmax_row(target, dtype, trow + i, V, T, p, &m, &S);
+            double *p = buf + (size_t)i * V, S;
+            orc_softmax_row(target, dtype, trow + i, V, T, p, &mt[i], &S);
             P[i] = p;
-            if (out_row_max) { out_row_max[trow + i] = m; out_row_sum[trow + i] = S; }
+            if (out_row_max) { out_row_max[trow + i] = mt[i]; out_row_sum[trow + i] = S; }
         }
         for (int i = 0; i < k; ++i) {
-            double *q = buf + (size_t)(k + 1 + i) * V, m, S;
-            orc_softmax_row(draft, dtype, drow + i, V, T, q, &m, &S);
+            double *q = buf + (size_t)(k + 1 + i) * V, S;
+            orc_softmax_row(draft, dtype, drow + i, V, T, q, &md[i], &S);
             Q[i] = q;
             if (out_row_max) {
-                out_row_max[total + B + drow + i] = m;
+                out_row_max[total + B + drow + i] = md[i];
                 out_row_sum[total + B + drow + i] = S;
             }
         }
         orc_result r = orc_verify_probs_seq(
             P, Q, V, k, x, uniforms + trow, qg, out_alpha ? out_alpha + drow : NULL,
             out_px ? out_px + drow : NULL, out_qx ? out_qx + drow : NULL);
+        /* Reading R26: a row the scan reaches whose maximum is not finite
+         * makes the sequence a data error -- target rows 0..n and draft rows
+         * 0..n (the gathered form reads only draft row n, for the residual);
+         * rows after the first rejection are never read. */
+        int row_bad = 0;
+        for (int i = 0; i <= r.n && !row_bad; ++i)
+            row_bad = !isfinite(mt[i]) || (i < k && (!qg || i == r.n) && !isfinite(md[i]));
+        if (row_bad) {
+            orc_row_error(out, k, out_n + b, out_flags ? out_flags + b : NULL);
+            if (out_Z) out_Z[b] = NAN;
+            if (out_gap) out_gap[b] = NAN;
+            continue;
+        }
         orc_write_tokens(out, k, x, r.n, r.token);
         out_n[b] = r.n;
         if (out_flags) out_flags[b] = r.flags;

@@ -15,6 +15,7 @@ import oracle
 import test_oracle_bookkeeping as bpins
 import test_oracle_draft as dpins
 import test_oracle_pins as pins
+import test_oracle_rows as rpins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -51,6 +52,8 @@ MUTANTS = {
     "adapt_rate_k_plus_1": ("(double)out_n[b] / (double)k_used[b]", "(double)out_n[b] / (double)(k_used[b] + 1)"),
     "ngram_first_match": ("for (int32_t j = L - n - 1; j >= 0; --j) {", "for (int32_t j = 0; j <= L - n - 1; ++j) {"),
     "ngram_suffix_matches_itself": ("for (int32_t j = L - n - 1; j >= 0; --j) {", "for (int32_t j = L - n; j >= 0; --j) {"),
+    "rows_past_rejection_read": ("for (int i = 0; i <= r.n && !row_bad; ++i)", "for (int i = 0; i <= k && !row_bad; ++i)"),
+    "greedy_nonfinite_row_ignored": ("if (!isfinite(m)) { row_bad = 1; break; }", "if (0) { row_bad = 1; break; }"),
     "draft_greedy_highest_tie": ("orc_row_argmax(logits, dtype, r, V, &a);\n            out_tokens[r] = (int32_t)a;",
                                  "orc_row_argmax(logits, dtype, r, V, &a);\n            out_tokens[r] = (int32_t)(V - 1 - a);"),
 }
@@ -75,6 +78,9 @@ PINS = [
     lambda: bpins.test_adapt_k_window_is_the_last_ten(),
     lambda: bpins.test_adapt_k_rate_uses_the_rounds_own_k(),
     lambda: bpins.test_ngram_hand_cases(),
+    lambda: rpins.test_nonfinite_rows_the_scan_reaches(),
+    lambda: rpins.test_nonfinite_past_the_rejection_changes_nothing(),
+    lambda: rpins.test_greedy_reaches_rows_up_to_the_first_mismatch(),
 ]
 
 
