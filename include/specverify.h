@@ -47,9 +47,11 @@
  *     the n_b accepted drafts, then the emitted token, then -1;
  *     out_n_accepted int32 [B]: n_b in 0..k_b, or -1 for a per-sequence data
  *     error (k_b out of range, offsets inconsistent, T < 0 or not finite, a
- *     drafted token outside [0, V), a non-finite row maximum); that
- *     sequence's token slots are all -1.  NaN/Inf logits are otherwise
- *     outside the contract.
+ *     drafted token outside [0, V), or a logit row with a non-finite
+ *     maximum that the scan reaches: target and draft rows up to and
+ *     including the first rejection -- rows past it are never looked at,
+ *     whichever form reads them); that sequence's token slots are all -1.
+ *     NaN logits are otherwise outside the contract.
  *   * Argument errors are detected on the host before anything is enqueued
  *     and return a negative sv_status_t with no output written.
  *   * Pointers must be aligned to their element size; 16-byte aligned logit
@@ -277,8 +279,7 @@ sv_status_t spec_verify_set_mode(int32_t mode, int32_t fused_lag);
  * together hold at least 512 MiB, else 0 (the two extra launches cost more
  * than small batches can save).  The outputs do not depend on L, except
  * that the out_p/out_q and row diagnostics of spec_verify_probs are NaN for
- * rows that were not read (and data errors in unread rows, such as a
- * non-finite row, go unseen).  Returns SV_ERR_SHAPE unless
+ * rows that were not read.  Returns SV_ERR_SHAPE unless
  * -1 <= L <= SV_K_MAX + 1. */
 sv_status_t spec_verify_set_early_exit(int32_t lead_positions);
 

@@ -181,19 +181,20 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
     }
     RowStat rt{0.f, 0, 0.f, 1.0}, rd{0.f, 0, 0.f, 1.0};
     const bool read = lane < limit;                // this position's rows have been read
+    bool row_bad = false;                          // a row of this position has a non-finite maximum
     if (ok && lane <= k && read) {
         rt = merge_row<kCo>(plan.seg + trow * plan.nseg, plan.nseg, greedy);
-        if (!(fabsf(rt.m) <= 3.4e38f)) ok = false;
+        row_bad = !(fabsf(rt.m) <= 3.4e38f);
         if (!greedy && !gathered && lane < k) {
             rd = merge_row<kCo>(plan.seg + (ntarget + drow) * plan.nseg, plan.nseg, false);
-            if (!(fabsf(rd.m) <= 3.4e38f)) ok = false;
+            row_bad = row_bad || !(fabsf(rd.m) <= 3.4e38f);
         }
     }
     ok = !__any(!ok);                              // one verdict for the whole sequence
 
-    if (!ok) {
-        // Data error: the sequence's own token slots (when its offsets describe
-        // a range inside the batch) are all -1.
+    // Data error: the sequence's own token slots (when its offsets describe
+    // a range inside the batch) are all -1.
+    auto data_error = [&]() {
         if (o >= 0 && o1 >= o && o1 <= p.total)
             for (int64_t i = lane; i <= k64; i += 64) p.out_tokens[o + b + i] = -1;
         if (lane == 0) {
@@ -202,6 +203,9 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
             st_co<kCo>(&plan.task[b].kind, static_cast<int32_t>(kNone));
             if (done) *done = kDecided;
         }
+    };
+    if (!ok) {
+        data_error();
         return false;
     }
 
@@ -223,7 +227,11 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
             reject = !(static_cast<double>(p.uniforms[trow]) < alpha);
         }
     }
-    const uint64_t mask = __ballot(reject);
+    // A row with a non-finite maximum ends the scan where it stands, like a
+    // rejection, and makes the sequence a data error if the scan gets there
+    // (rows past the first rejection are never looked at).
+    const uint64_t bad = __ballot(row_bad);
+    const uint64_t mask = __ballot(reject) | bad;
     if (!mask && k >= limit) {                     // undecided: rows past limit are needed
         if (done) {
             if (lane == 0) *done = kUndecided;
@@ -232,6 +240,10 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
         return false;
     }
     const int n = mask ? __ffsll(static_cast<unsigned long long>(mask)) - 1 : k;
+    if ((bad >> n) & 1ull) {
+        data_error();
+        return false;
+    }
     if (done && lane == n) {
         // Settled by its leading positions: a sampling sequence whose draw
         // rows have been read can draw beside the remaining row pass.

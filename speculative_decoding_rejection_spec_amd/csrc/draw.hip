@@ -56,6 +56,18 @@ __global__ __launch_bounds__(kPickThreads) void draw_pick_kernel(Problem p, Plan
     }
     const DrawTask task = load_task<false>(p, plan, b);
     if (task.kind == kNone) return;
+    if (task.kind == kResidual && !(fabsf(task.m_d) <= 3.4e38f)) {
+        // The gathered form reads the rejected position's draft row only
+        // now: a non-finite maximum there makes the sequence a data error.
+        const int64_t o = p.offsets ? static_cast<int64_t>(p.offsets[b]) : static_cast<int64_t>(b) * p.k_uniform;
+        const int64_t k = p.offsets ? static_cast<int64_t>(p.offsets[b + 1]) - o : p.k_uniform;
+        for (int64_t i = threadIdx.x; i <= k; i += kPickThreads) p.out_tokens[o + b + i] = -1;
+        if (threadIdx.x == 0) {
+            p.out_n[b] = -1;
+            if (p.out_emit_prob) p.out_emit_prob[b] = NAN;
+        }
+        return;
+    }
     __syncthreads();
     pick_sequence<DT, kPickThreads, false>(p, plan, task, b, tbl, lds.pick);
 }

@@ -178,6 +178,27 @@ def test_gathered_leads_past_short_sequences(sv, cuda):
         sv.set_early_exit(1)
 
 
+def test_gathered_nonfinite_draft_rows(sv, cuda):
+    """The gathered form reads a draft row only at the rejection: a
+    non-finite maximum there is a data error, elsewhere it changes nothing
+    (reading R26)."""
+    w = wl.make_workload("c4", trial=2, B=32, V=4096)
+    qg = gathered_q(w)
+    base = oracle.verify(w, draft_probs=qg)
+    draft = wl.logits_as_f32(w.draft).copy()
+    for b in range(w.B):
+        n = int(base["n"][b])
+        if n < 0:
+            continue
+        pos = n if b % 2 == 0 else (n + 1 if n + 1 < int(w.k[b]) else -1)
+        if pos >= 0 and pos < int(w.k[b]):
+            draft[int(w.offsets[b]) + pos, 11] = np.inf
+    w2 = wl.Workload(**{**w.__dict__, "draft": wl.bf16_round(draft)})
+    ref = oracle.verify(w2, draft_probs=qg)
+    assert (ref["n"] == -1).sum() >= 5
+    compare(w2, run_gathered(sv, w2, qg, cuda), ref, "gathered non-finite draft rows")
+
+
 def test_gathered_data_errors(sv, cuda):
     w = wl.make_workload("c3", trial=4, B=12, V=3000)
     qg = gathered_q(w)

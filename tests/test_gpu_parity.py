@@ -280,6 +280,69 @@ def test_special_cases(sv, cuda):
         sv.set_geometry(0, 0)
 
 
+def nonfinite_workload(V=4096, dtype="bf16"):
+    """Sequences whose scans reach, or stop short of, a row with a
+    non-finite maximum (reading R26; the cases of tests/test_oracle_rows.py
+    at V = 4096, one per sequence, next to clean ones)."""
+    K = 4
+    g = np.random.default_rng(31)
+    T_rows, D_rows, X, U, T = [], [], [], [], []
+
+    def add(t, d, x, u, temp):
+        T_rows.append(t); D_rows.append(d); X.append(x); U.append(u); T.append(temp)
+
+    def base():
+        return ((g.standard_normal((K + 1, V)) * 2).astype(np.float32),
+                (g.standard_normal((K, V)) * 2).astype(np.float32), g.integers(0, V, size=K))
+
+    def reject_at(t, d, x, i):
+        d[i] = -30.0
+        d[i, x[i]] = 30.0
+        t[i, x[i]] = -30.0
+        u = np.zeros(K + 1, np.float32)
+        u[i] = 0.5
+        return u
+
+    zeros = np.zeros(K + 1, np.float32)
+    for pos in range(K + 1):                      # target row reached: +inf, or all -inf
+        t, d, x = base(); t[pos, 17] = np.inf; add(t, d, x, zeros, 1.0)
+        t, d, x = base(); t[pos] = -np.inf; add(t, d, x, zeros, 1.0)
+    for pos in range(K):                          # draft row reached
+        t, d, x = base(); d[pos, 5] = np.inf; add(t, d, x, zeros, 1.0)
+    for j in range(K):                            # rejection at j, +inf at j or later
+        for pos in range(j, K + 1):
+            t, d, x = base(); u = reject_at(t, d, x, j); t[pos, 9] = np.inf; add(t, d, x, u, 1.0)
+    for _ in range(4):                            # clean
+        t, d, x = base(); add(t, d, x, zeros, 1.0)
+    for bad_pos in (1, 4):                        # greedy: mismatch at 3, +inf at the accepted argmax 1 or past it
+        t, _, _ = base(); d = np.zeros((K, V), np.float32)
+        x = np.argmax(t[:K], axis=1); x[3] = (x[3] + 1) % V
+        t[bad_pos, x[bad_pos] if bad_pos < K else 0] = np.inf
+        add(t, d, x, zeros, 0.0)
+    B = len(T)
+    return wl.assemble(np.concatenate(T_rows), np.concatenate(D_rows), np.concatenate(X),
+                       np.concatenate(U), np.array(T, np.float32), [K] * B, dtype=dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_nonfinite_rows_reading(sv, cuda, dtype):
+    """A row with a non-finite maximum is a data error exactly when the scan
+    reaches it, in every form (one pass reads rows past the rejection, early
+    exit does not, the fused form reads everything)."""
+    w = nonfinite_workload(dtype=dtype)
+    ref = oracle.verify(w)
+    assert (ref["n"] == -1).sum() > 10 and (ref["n"] >= 0).sum() > 10
+    leads = (1, 2, 5) if CURRENT["mode"] == "early" else (None,)
+    try:
+        for lead in leads:
+            if lead is not None:
+                sv.set_early_exit(lead)
+            compare(w, run_gpu(sv, w, cuda), ref, f"non-finite rows, lead {lead}")
+    finally:
+        if CURRENT["mode"] == "early":
+            sv.set_early_exit(1)
+
+
 def test_data_errors_are_per_sequence(sv, cuda):
     w = workload("c3", 0, 16)
     bad = dataclasses.replace(w, tokens=w.tokens.copy(), temperature=w.temperature.copy())
