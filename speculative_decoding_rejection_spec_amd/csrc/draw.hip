@@ -7,7 +7,6 @@
 namespace sv {
 namespace {
 
-constexpr int kPickThreads = 1024;
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void draw_sums_kernel(Problem p, Plan plan) {
@@ -29,7 +28,7 @@ __global__ __launch_bounds__(kThreads) void draw_sums_kernel(Problem p, Plan pla
 // redone here first -- its accept scan if its leading positions left it
 // undecided, then every chunk -- with the chunk pass of a 256-thread
 // workgroup (the other threads only take part in its barriers).
-template <int DT>
+template <int DT, int kPickThreads>
 __global__ __launch_bounds__(kPickThreads) void draw_pick_kernel(Problem p, Plan plan) {
     const int32_t b = blockIdx.x;
     __shared__ drawpass::TabEntry tbl[256];
@@ -83,11 +82,18 @@ hipError_t launch_draw_sums(const Problem& p, const Plan& plan, hipStream_t s) {
     return hipGetLastError();
 }
 
+// One workgroup per sequence: 1024 threads while the sequences fit one per
+// CU, else 512 (two per CU, so the picks still run in one round).
 hipError_t launch_draw_pick(const Problem& p, const Plan& plan, hipStream_t s) {
-    if (p.dtype == SV_BF16)
-        draw_pick_kernel<SV_BF16><<<dim3(static_cast<uint32_t>(p.B)), dim3(kPickThreads), 0, s>>>(p, plan);
-    else
-        draw_pick_kernel<SV_F32><<<dim3(static_cast<uint32_t>(p.B)), dim3(kPickThreads), 0, s>>>(p, plan);
+    const dim3 grid(static_cast<uint32_t>(p.B));
+    const bool wide = p.B <= plan.cus;
+    if (p.dtype == SV_BF16) {
+        if (wide) draw_pick_kernel<SV_BF16, 1024><<<grid, dim3(1024), 0, s>>>(p, plan);
+        else draw_pick_kernel<SV_BF16, 512><<<grid, dim3(512), 0, s>>>(p, plan);
+    } else {
+        if (wide) draw_pick_kernel<SV_F32, 1024><<<grid, dim3(1024), 0, s>>>(p, plan);
+        else draw_pick_kernel<SV_F32, 512><<<grid, dim3(512), 0, s>>>(p, plan);
+    }
     return hipGetLastError();
 }
 

@@ -262,6 +262,7 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     const bool fused = g_mode == SV_MODE_FUSED && !p.draft_probs;
     if (fused && !fused_fits) return SV_ERR_SHAPE;
     plan.lead = fused ? 0 : effective_lead(p.B, p.total, p.V, static_cast<sv_dtype_t>(p.dtype));
+    if (device_cus(&plan.cus) != hipSuccess) return SV_ERR_HIP;
     plan.lag_a = plan.lag_c = 1 << 30;             // no accept or draw items in the schedule
     plan.queued = plan.lead > 0 && !p.draft_probs;
     if (plan.queued) {
@@ -273,9 +274,7 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
             // start well after their rows: the accept item about 1.4 resident
             // grids of row segments later, the draw items about 2.3 (measured
             // on MI355X; shorter lags wait more than they overlap).
-            int cus = 0;
-            if (device_cus(&cus) != hipSuccess) return SV_ERR_HIP;
-            const double window = static_cast<double>(cus) * kRestWgsPerCu;
+            const double window = static_cast<double>(plan.cus) * kRestWgsPerCu;
             double per_block = (2.0 * static_cast<double>(p.total) / p.B - 2.0 * plan.lead + 1.0) * g.nseg;
             if (per_block < g.nseg) per_block = g.nseg;
             plan.lag_a = static_cast<int32_t>(1.4 * window / per_block) + 1;

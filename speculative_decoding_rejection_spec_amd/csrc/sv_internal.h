@@ -157,6 +157,7 @@ struct Plan {
                          // follow block j + lag_c (huge: none inserted, the gathered form)
     int32_t* aband;      // [B] 1: sequence b is left to the pick launch
     int32_t queued;      // early exit with the draws beside the rows (not the gathered form)
+    int32_t cus;         // compute units of the device
     int32_t queue_mode;  // SV_QUEUE_*: where the second round's draw chunks are summed
 };
 
