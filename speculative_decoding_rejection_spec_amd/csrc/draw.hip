@@ -36,9 +36,9 @@ __global__ __launch_bounds__(kPickThreads) void draw_pick_kernel(Problem p, Plan
         PickLds<kPickThreads> pick;
         DrawLds draw;
     } lds;
-    load_exp2_table(tbl, kPickThreads);
     const bool redo = plan.queued && (plan.queue_mode == SV_QUEUE_FINAL || plan.aband[b] != 0);
     if (redo) {
+        load_exp2_table(tbl, kPickThreads);
         if (plan.done[b] == kUndecided) {
             if (threadIdx.x < 64) accept_sequence<true>(p, plan, b);
             wait_stores();
@@ -53,7 +53,8 @@ __global__ __launch_bounds__(kPickThreads) void draw_pick_kernel(Problem p, Plan
         pick_sequence<DT, kPickThreads, true>(p, plan, task, b, tbl, lds.pick);
         return;
     }
-    const DrawTask task = load_task<false>(p, plan, b);
+    const DrawTask task = load_task<false>(p, plan, b);   // (issued before the table's loads)
+    load_exp2_table(tbl, kPickThreads);
     if (task.kind == kNone) return;
     if (task.kind == kResidual && !(fabsf(task.m_d) <= 3.4e38f)) {
         // The gathered form reads the rejected position's draft row only

@@ -365,7 +365,7 @@ struct PickLds {
     static constexpr int kW = NT / 64;
     double red2[kW][2];
     double scan[kW];
-    int32_t ldsi[kW];
+    int32_t ldsi[2 * kW];
     double mass[MAXC];
     double spc[MAXC];
     double base, target, Z;
@@ -411,18 +411,20 @@ __device__ __forceinline__ double pick_scan_excl(double x, double* total, double
     return before + excl;
 }
 
+// The minimum of x and the maximum of y over an NT-thread workgroup, in one
+// exchange through LDS (lds: 2 * NT / 64 ints).
 template <int NT>
-__device__ __forceinline__ int32_t pick_min_max(int32_t x, bool want_min, int32_t* lds) {
+__device__ __forceinline__ void pick_min_and_max(int32_t& x, int32_t& y, int32_t* lds) {
     for (int off = 32; off > 0; off >>= 1) {
-        const int32_t y = __shfl_xor(x, off, 64);
-        x = want_min ? min(x, y) : max(x, y);
+        x = min(x, __shfl_xor(x, off, 64));
+        y = max(y, __shfl_xor(y, off, 64));
     }
     __syncthreads();
-    if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = x;
+    if ((threadIdx.x & 63) == 0) { lds[2 * (threadIdx.x >> 6)] = x; lds[2 * (threadIdx.x >> 6) + 1] = y; }
     __syncthreads();
-    int32_t r = lds[0];
-    for (int w = 1; w < NT / 64; ++w) r = want_min ? min(r, lds[w]) : max(r, lds[w]);
-    return r;
+    x = lds[0];
+    y = lds[1];
+    for (int w = 1; w < NT / 64; ++w) { x = min(x, lds[2 * w]); y = max(y, lds[2 * w + 1]); }
 }
 
 // Wave-wide search over chunk masses m[0..n) (run by one whole wave): the
@@ -595,7 +597,8 @@ __device__ __forceinline__ void pick_sequence(const Problem& p, const Plan& plan
 
     // Scan the chunk in pieces of kPiece tokens: lane tid owns kRun consecutive
     // tokens of the piece, loaded together, masses kept in registers.
-    int32_t pick = INT32_MAX, last_pos = -1;
+    int32_t pick = INT32_MAX, last_pos = -1, mine = INT32_MAX;
+    double mine_mass = 0.0;
     for (int64_t q0 = c0; q0 < c1 && pick == INT32_MAX; q0 += kPiece) {
         const int64_t q1 = min(c1, q0 + kPiece);
         const int64_t r0 = q0 + static_cast<int64_t>(tid) * kRun;
@@ -630,19 +633,27 @@ __device__ __forceinline__ void pick_sequence(const Problem& p, const Plan& plan
         }
         double total;
         double run = base + pick_scan_excl<NT>(local, &total, L.scan);
-        int32_t mine = INT32_MAX;
+        mine = INT32_MAX;
 #pragma unroll
         for (int i = 0; i < kRun; ++i) {
             run += m[i];
-            if (mine == INT32_MAX && run > target) mine = static_cast<int32_t>(r0 + i);
+            if (mine == INT32_MAX && run > target) { mine = static_cast<int32_t>(r0 + i); mine_mass = m[i]; }
         }
-        pick = pick_min_max<NT>(mine, true, L.ldsi);
-        last_pos = max(last_pos, pick_min_max<NT>(lp, false, L.ldsi));
+        int32_t first = mine;
+        pick_min_and_max<NT>(first, lp, L.ldsi);
+        pick = first;
+        last_pos = max(last_pos, lp);
         base += total;
     }
-    // If rounding left no crossing inside the chunk: its last token with mass.
-    if (tid == 0) {
-        if (pick == INT32_MAX) pick = last_pos >= 0 ? last_pos : static_cast<int32_t>(c0);
+    if (pick != INT32_MAX) {
+        // the thread that found the crossing holds the token's mass
+        if (mine == pick) {
+            p.out_tokens[task.out_slot] = pick;
+            if (p.out_emit_prob) p.out_emit_prob[b] = static_cast<float>(mine_mass / L.Z);
+        }
+    } else if (tid == 0) {
+        // rounding left no crossing inside the chunk: its last token with mass
+        pick = last_pos >= 0 ? last_pos : static_cast<int32_t>(c0);
         p.out_tokens[task.out_slot] = pick;
         if (p.out_emit_prob) {
             // its probability under the distribution it was drawn from
