@@ -81,7 +81,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c4", help="c1 c2 c2g c3 c4 c5")
-    ap.add_argument("--copies", type=int, default=2, help="input copies rotated between steps")
+    ap.add_argument("--copies", type=int, default=4, help="input copies rotated between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time without the per-kernel HIP events (no roofline)")
@@ -92,11 +92,13 @@ def main():
     ap.add_argument("--mode", choices=["auto", "staged", "fused"], default="auto",
                     help="launch form (auto = staged)")
     ap.add_argument("--lag", type=int, default=0, help="fused form: draw lag in sequences (0 = auto)")
-    ap.add_argument("--entry", choices=["verify", "gathered", "draft", "ngram", "commit"], default="verify",
+    ap.add_argument("--entry", choices=["verify", "gathered", "draft", "ngram", "commit", "stream"],
+                    default="verify",
                     help="verify: spec_verify; gathered: spec_verify_gathered with the drafts' q(x) "
                          "(the accept tests need no draft rows); draft: spec_draft_sample over one "
                          "draft-model row per sequence; ngram: spec_ngram_draft over B=512 token streams "
-                         "of 4096; commit: spec_commit + spec_adapt_k of the workload's verify outputs")
+                         "of 4096; commit: spec_commit + spec_adapt_k of the workload's verify outputs; "
+                         "stream: the bare read-reduce reference over the workload's logit bytes")
     ap.add_argument("--queue", type=int, default=0,
                     help="early exit: draws beside the rows (0) or all in the final launch (1)")
     ap.add_argument("--queue-lag", type=int, nargs=2, default=[0, 0], metavar=("ACCEPT", "DRAW"),
@@ -132,6 +134,8 @@ def main():
 
     if args.entry == "ngram":
         return bench_ngram(args, sv, torch, np)
+    if args.entry == "stream":
+        return bench_stream(args, sv, torch, np)
 
     t_gen = time.perf_counter()
     w = wl.make_workload(args.workload)
@@ -239,6 +243,15 @@ def main():
         k1_live = sum(kt[k] for k in roof)
     sv.timing(False)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # Per-step distribution: a further pass with an event pair around each step.
+    step_ms = []
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(64)]
+    for i, (e0, e1) in enumerate(evs):
+        e0.record()
+        step(i)
+        e1.record()
+    torch.cuda.synchronize()
+    step_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
     # Per-kernel breakdown: a further untimed pass with events around every kernel.
     kern = {}
     if not args.no_kernel_events:
@@ -319,7 +332,13 @@ def main():
         cpu = {"value": round(w.B / tc, 2), "unit": "rows/s" if args.entry == "draft" else "sequences/s",
                "cores": threads, "kind": "oracle", "sample": f"the whole batch ({w.B} sequences) once, "
                f"fp64 C oracle split over {threads} threads; {what} agree with the "
-               f"GPU on {agree}/{w.B} sequences"}
+               f"GPU on {agree}/{w.B} sequences", "cpu_model": cpu_model()}
+        if args.entry != "draft":
+            n1 = min(w.B, 32)
+            t1 = time.perf_counter()
+            oracle.verify(w, threads=1, seqs=(0, n1), draft_probs=qg)
+            t1 = time.perf_counter() - t1
+            cpu["single_thread"] = {"value": round(n1 / t1, 2), "sample": f"sequences 0..{n1 - 1}, one thread"}
 
     kdesc = f"k={int(w.k.max())}" if int(w.k.min()) == int(w.k.max()) else f"k={int(w.k.min())}..{int(w.k.max())}"
     base = f"sequences verified/s and achieved HBM GB/s (% of peak), B={w.B} {kdesc} V={w.V} {w.dtype}"
@@ -344,6 +363,8 @@ def main():
         "draw_rows": draw_rows,
         "kernels_ms": {k: round(v, 5) for k, v in kern.items()},   # separate pass, all kernels evented
         "roofline": roofline, "cpu_baseline": cpu, "gen_s": round(t_gen, 2),
+        "step_ms_events": {"median": round(step_ms[len(step_ms) // 2], 5), "p10": round(step_ms[6], 5),
+                           "p90": round(step_ms[57], 5), "steps": len(step_ms)},
     }
     print(json.dumps(res), flush=True)
 
@@ -359,11 +380,51 @@ def _timed(torch, fn, steps, warmup):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
-def _line(args, metric, value, unit, ms, config, extra):
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _line(args, metric, value, unit, ms, config, extra, dtype="int32"):
     res = {"metric": metric, "value": round(value, 1), "unit": unit, "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "int32", "data": "synthetic", "config": config, **extra}
+           "vs_baseline": None, "dtype": dtype, "data": "synthetic", "config": config, **extra}
     print(json.dumps(res), flush=True)
+
+
+def bench_stream(args, sv, torch, np):
+    """The bare read-reduce reference: the C4 logit arrays' bytes (1.32 GB)
+    streamed by spec_stream_probe in the row pass's segment size, copies
+    rotated like the verify bench."""
+    dev = torch.device("cuda:0")
+    nbytes = (2304 + 2048) * 152064 * 2
+    bufs = [torch.randint(0, 1 << 15, (nbytes // 2,), dtype=torch.int16, device=dev)
+            for _ in range(max(2, args.copies))]
+    out = torch.empty((nbytes + 163839) // 163840, dtype=torch.int32, device=dev)
+    for i in range(args.warmup):
+        sv.stream_probe(bufs[i % len(bufs)], out=out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        sv.stream_probe(bufs[i % len(bufs)], out=out)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for i in range(args.steps):
+        sv.stream_probe(bufs[i % len(bufs)], out=out)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms_ev = ev[0].elapsed_time(ev[1]) / args.steps
+    gbs = nbytes / (ms / 1e3) / 1e9
+    _line(args, "bare read-reduce GB/s (spec_stream_probe over 1.32 GB, 163840-byte segments)", gbs,
+          "GB/s", ms, {"workload": "stream 1.32 GB (the C4 logit arrays' bytes)", "bytes": nbytes},
+          {"hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "ms_per_call_events": round(ms_ev, 5)}, dtype="u32")
 
 
 def bench_ngram(args, sv, torch, np):

@@ -222,6 +222,17 @@ const char *spec_verify_status_string(sv_status_t status);
  * that uses it is still running. */
 void spec_verify_release(void);
 
+/* Benchmark reference: a bare read-reduce over `bytes` of device memory at
+ * `data` (16-byte aligned), one 256-thread workgroup per `seg_bytes`
+ * (a multiple of 16, 4096 .. 2^30) reading it the way the row pass reads a
+ * segment (16-byte raw buffer loads, 8 in flight per lane, non-temporal)
+ * and writing the XOR of its whole 16-byte words to out[i] (uint32,
+ * ceil(bytes / seg_bytes) entries, caller-owned).  Its bandwidth is the
+ * practical ceiling for the row pass.  Enqueue-only on `stream`.  Returns
+ * SV_ERR_SHAPE / SV_ERR_NULL / SV_ERR_ALIGN for bad arguments. */
+sv_status_t spec_stream_probe(const void *data, int64_t bytes, int64_t seg_bytes, uint32_t *out,
+                              hipStream_t stream);
+
 /* Kernel timing for benchmarks.  spec_verify_timing(kernels, every) turns
  * the probe on for the kernels whose bits are set in `kernels` (bit i
  * selects spec_verify_kernel_name(i); 0 turns it off; SV_TIME_ALL selects

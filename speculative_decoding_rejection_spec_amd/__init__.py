@@ -17,7 +17,7 @@ __all__ = [
     "spec_verify", "spec_verify_probs", "spec_verify_gathered", "spec_draft_sample",
     "spec_commit", "spec_adapt_k", "spec_ngram_draft",
     "spec_verify_workspace_size", "spec_verify_release",
-    "timing", "kernel_times", "set_geometry", "set_mode", "set_early_exit", "set_queue", "SpecVerifyError",
+    "stream_probe", "timing", "kernel_times", "set_geometry", "set_mode", "set_early_exit", "set_queue", "SpecVerifyError",
     "SV_F32", "SV_BF16", "SV_K_MAX", "SV_MODE_AUTO", "SV_MODE_STAGED", "SV_MODE_FUSED", "SV_QUEUE_OVERLAP",
     "SV_QUEUE_FINAL", "SV_QUEUE_HANDOFF", "LIB_PATH", "lib",
 ]
@@ -302,6 +302,23 @@ def set_queue(mode: int = SV_QUEUE_OVERLAP, lag_accept: int = 0, lag_draw: int =
 def set_mode(mode: int = SV_MODE_AUTO, fused_lag: int = 0) -> None:
     """Staged (four kernels), fused (one persistent kernel) or auto."""
     check(lib().spec_verify_set_mode(int(mode), int(fused_lag)), "spec_verify_set_mode")
+
+
+def stream_probe(data, seg_bytes: int = 163840, out=None, stream=None):
+    """Bare read-reduce over a contiguous device tensor (benchmark reference
+    for the row pass's bandwidth); returns the per-workgroup XOR words."""
+    import torch
+    if data.device.type != "cuda" or not data.is_contiguous():
+        raise ValueError("data must be a contiguous GPU tensor")
+    nbytes = data.numel() * data.element_size()
+    n = (nbytes + seg_bytes - 1) // seg_bytes
+    if out is None:
+        out = torch.empty(max(1, n), dtype=torch.int32, device=data.device)
+    elif out.numel() < n or out.dtype != torch.int32 or out.device != data.device:
+        raise ValueError(f"out must be int32 on {data.device} with at least {n} entries")
+    check(lib().spec_stream_probe(_ptr(data), nbytes, seg_bytes, _ptr(out), _stream(data.device, stream)),
+          "spec_stream_probe")
+    return out
 
 
 def timing(enable=True, every: int = 1) -> None:

@@ -43,6 +43,7 @@ SIGNATURES = {
     "spec_verify_kernel_name": (ctypes.c_char_p, [_I32]),
     "spec_verify_set_geometry": (_I32, [_I64, _I64]),
     "spec_verify_set_queue": (_I32, [_I32, _I32, _I32]),
+    "spec_stream_probe": (_I32, [_P, _I64, _I64, _P, _P]),
     "spec_verify_set_mode": (_I32, [_I32, _I32]),
     "spec_verify_set_early_exit": (_I32, [_I32]),
 }

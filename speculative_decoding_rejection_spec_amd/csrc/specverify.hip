@@ -523,6 +523,15 @@ sv_status_t spec_adapt_k(const int32_t* out_n_accepted, const int32_t* offsets, 
                    hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
+sv_status_t spec_stream_probe(const void* data, int64_t bytes, int64_t seg_bytes, uint32_t* out,
+                              hipStream_t stream) {
+    if (bytes < 0 || seg_bytes < 4096 || seg_bytes % 16 != 0 || seg_bytes > (1ll << 30)) return SV_ERR_SHAPE;
+    if ((bytes + seg_bytes - 1) / seg_bytes > 0x7FFFFFFFll) return SV_ERR_SHAPE;
+    if (bytes > 0 && (!data || !out)) return SV_ERR_NULL;
+    if (!aligned(data, 16) || !aligned(out, 4)) return SV_ERR_ALIGN;
+    return launch_stream_probe(data, bytes, seg_bytes, out, stream) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
 size_t spec_ngram_workspace_size(int32_t B) {
     return B < 0 ? 0 : align256(sizeof(int32_t) * (static_cast<size_t>(B) + 1));
 }

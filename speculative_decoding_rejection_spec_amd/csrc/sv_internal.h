@@ -203,6 +203,8 @@ hipError_t launch_ngram_draft(const int32_t* seq_tokens, const int32_t* seq_len,
                               int32_t ngram_max, int32_t ngram_min, int32_t k_max, int32_t* cont_start,
                               int32_t* draft_tokens, int32_t* draft_offsets, hipStream_t s);
 int64_t fused_counter_words(int32_t B);
+hipError_t launch_stream_probe(const void* data, int64_t bytes, int64_t seg_bytes, uint32_t* out,
+                               hipStream_t s);
 
 // ---- device helpers shared by the kernels ---------------------------------
 

@@ -124,6 +124,15 @@ def test_geometry_knob(lib):
     assert lib.spec_verify_workspace_size(64, 256, 128256, 1) == base
 
 
+def test_stream_probe_argument_errors(lib):
+    p = ctypes.c_void_p(0x100000)
+    assert lib.spec_stream_probe(p, 1 << 20, 1024, p, None) == SHAPE        # segment too short
+    assert lib.spec_stream_probe(p, 1 << 20, 4100, p, None) == SHAPE        # not a multiple of 16
+    assert lib.spec_stream_probe(p, -1, 4096, p, None) == SHAPE
+    assert lib.spec_stream_probe(None, 1 << 20, 4096, p, None) == NULL
+    assert lib.spec_stream_probe(ctypes.c_void_p(0x100008), 1 << 20, 4096, p, None) == ALIGN
+
+
 def test_queue_knob(lib):
     assert lib.spec_verify_set_queue(3, 0, 0) == SHAPE
     assert lib.spec_verify_set_queue(-1, 0, 0) == SHAPE
