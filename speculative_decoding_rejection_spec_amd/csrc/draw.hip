@@ -1,12 +1,11 @@
 // draw.hip -- the staged draw: draw_sums (grid sequence x chunk, 256
-// threads) and draw_pick (one 1024-thread workgroup per sequence).  The
-// kernel boundary publishes the chunk sums; the work itself is in
+// threads) and draw_pick (one 1024- or 512-thread workgroup per sequence).
+// The kernel boundary publishes the chunk sums; the work itself is in
 // draw_pass.h.
 #include "draw_pass.h"
 
 namespace sv {
 namespace {
-
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void draw_sums_kernel(Problem p, Plan plan) {
@@ -16,7 +15,6 @@ __global__ __launch_bounds__(kThreads) void draw_sums_kernel(Problem p, Plan pla
     __shared__ drawpass::TabEntry tbl[256];
     __shared__ DrawLds lds;
     load_exp2_table(tbl, kThreads);            // overlaps the task load
-    if (plan.lead > 0 && plan.done[b] == kDecidedEarlyDraw) return;   // drawn beside the row pass
     const DrawTask task = load_task<false>(p, plan, b);
     if (task.kind == kNone) return;            // the whole workgroup leaves
     __syncthreads();

@@ -145,7 +145,7 @@ struct Plan {
     float* xlogit;       // [2 * total + B]: logit of the drafted token of each row
     uint32_t* ctr;       // fused form only: kCtrHeader words, then rows_done[B], ready[B], chunks_done[B]
     int32_t lead;        // early exit: positions every sequence reads first (0: one pass over all rows)
-    int32_t* done;       // early exit: [B], 1 once a sequence's outcome is known from its leading positions
+    int32_t* done;       // early exit: [B], kUndecided / kDecided / kDecidedEarlyDraw after the lead scan
     RestItem* sched;     // early exit: [(2 * total + B) * nseg + B * (1 + nchunk)], the second round's items
     uint64_t* blk_ctr;   // early exit: (undecided sequences listed) << 32 | (row segments listed)
     RestItem* dlist;     // gathered form: [B * nseg], segments of the draft rows at rejections
@@ -183,7 +183,6 @@ struct Fused {
 hipError_t launch_row_stats(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_row_list(const Problem& p, const Plan& plan, const RestItem* list, const uint32_t* count,
                            int64_t max_items, hipStream_t s);
-hipError_t launch_rest_and_early_draws(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_rest_draws(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_row_lead(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_accept(const Problem& p, const Plan& plan, hipStream_t s);
