@@ -89,13 +89,20 @@ struct SoftmaxAcc {
     static constexpr float kSlack = 2.f;
     float m = -INFINITY;    // running maximum logit
     float R = -INFINITY;    // reference exponent (integer valued)
+    float nR = 0.f;         // -R, or 0 while R = -inf (every logit so far -inf: its terms are then 0)
+    float thr = -INFINITY;  // R + kSlack: a logit z with z * c above it raises R
     float s[kSums] = {};
     float c;
 
+    __device__ __forceinline__ void set_ref(float Rn) {
+        R = Rn;
+        nR = -Rn;
+        thr = Rn + kSlack;
+    }
     // The first reference, from the largest logit of the wave's first tile
-    // (-inf: none; the first logit seen sets it).  Called before any add.
+    // (-inf: none; the first finite logit seen sets it).  Called before any add.
     __device__ __forceinline__ void prime(float wm) {
-        if (wm > -INFINITY) R = ceilf(wm * c);
+        if (wm > -INFINITY) set_ref(ceilf(wm * c));
     }
     __device__ __forceinline__ void raise(float tm) {
         const float Rn = ceilf(tm * c);
@@ -103,27 +110,33 @@ struct SoftmaxAcc {
         const int d = static_cast<int>(fmaxf(R - Rn, -512.f));
 #pragma unroll
         for (int j = 0; j < kSums; ++j) s[j] = ldexpf(s[j], d);
-        R = Rn;
+        set_ref(Rn);
     }
+    // The vector's logits are folded into the running maximum one by one
+    // (v_max3, with no canonicalising moves: the chain starts from a
+    // maximum), and since m * c <= thr holds after every add, testing the
+    // new maximum tests the vector's.
     template <int N>
     __device__ __forceinline__ void add(const float* x, int32_t) {
         static_assert(N == kSums || N == 2 * kSums, "partial sums per vector");
-        const float tm = max_of<N>(x);
-        m = fmaxf(m, tm);
-        if (tm * c > R + kSlack) raise(tm);
+        float mm = m;
+#pragma unroll
+        for (int j = 0; j < N; ++j) mm = fmaxf(mm, x[j]);
+        m = mm;
+        if (mm * c > thr) raise(mm);
 #pragma unroll
         for (int j = 0; j < kSums; ++j) {
             if constexpr (N == 2 * kSums)
-                s[j] += hw_exp2(fmaf(x[j], c, -R)) + hw_exp2(fmaf(x[j + kSums], c, -R));
+                s[j] += hw_exp2(fmaf(x[j], c, nR)) + hw_exp2(fmaf(x[j + kSums], c, nR));
             else
-                s[j] += hw_exp2(fmaf(x[j], c, -R));
+                s[j] += hw_exp2(fmaf(x[j], c, nR));
         }
     }
     // A single logit (a segment's unaligned head or tail): its own sum.
     __device__ __forceinline__ void add1(float x, int32_t) {
         m = fmaxf(m, x);
-        if (x * c > R + kSlack) raise(x);
-        s[kSums - 1] += hw_exp2(fmaf(x, c, -R));
+        if (m * c > thr) raise(m);
+        s[kSums - 1] += hw_exp2(fmaf(x, c, nR));
     }
     __device__ __forceinline__ double total() const {
         double t = 0.0;

@@ -343,6 +343,66 @@ def test_nonfinite_rows_reading(sv, cuda, dtype):
             sv.set_early_exit(1)
 
 
+def masked_workload(dtype, V=40000):
+    """Rows with masked vocabulary entries (-inf logits: probability zero):
+    a masked prefix longer than a workgroup's first tile of loads, a masked
+    padded tail, a masked block across segment boundaries, and scattered
+    masked entries, at T = 1, 0.7 and 0.  Drafted tokens are sampled from
+    the draft rows, so a drafted token is never masked; half the sequences
+    have near-identical draft rows, so bonus draws from masked rows occur."""
+    K = 4
+    g = np.random.default_rng(47)
+    masks = [np.arange(V) < 2600, np.arange(V) >= V - 464,
+             (np.arange(V) >= 7000) & (np.arange(V) < 18000), None]
+    T_rows, D_rows, X, U, T = [], [], [], [], []
+    for b in range(24):
+        t = (g.standard_normal((K + 1, V)) * 2).astype(np.float32)
+        near = b % 2 == 0
+        d = (t[:K] + g.standard_normal((K, V)) * 0.1).astype(np.float32) if near else \
+            (g.standard_normal((K, V)) * 2).astype(np.float32)
+        m = masks[b % 4]
+        if m is None:
+            m = g.random((K + 1, V)) < 0.3
+            t[m] = -np.inf
+            d[m[:K]] = -np.inf
+        else:
+            t[:, m] = -np.inf
+            d[:, m] = -np.inf
+        temp = (1.0, 0.7, 0.0)[b % 3]
+        x = np.empty(K, np.int64)
+        for i in range(K):
+            if temp == 0.0:
+                x[i] = int(np.argmax(d[i]))
+            else:
+                z = d[i].astype(np.float64) / temp
+                q = np.exp(z - z.max())
+                x[i] = int(g.choice(V, p=q / q.sum()))
+        T_rows.append(t); D_rows.append(d); X.append(x); T.append(temp)
+        U.append((g.integers(0, 1 << 24, size=K + 1) / float(1 << 24)).astype(np.float32))
+    return wl.assemble(np.concatenate(T_rows), np.concatenate(D_rows), np.concatenate(X),
+                       np.concatenate(U), np.array(T, np.float32), [K] * len(T), dtype=dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_masked_vocabulary(sv, cuda, dtype):
+    """Masked (-inf) logits carry no probability: tokens, accept counts,
+    probabilities and row statistics match the oracle."""
+    w = masked_workload(dtype)
+    ref = oracle.verify(w, diag=True)
+    assert (ref["n"] >= 0).all()
+    compare(w, run_gpu(sv, w, cuda), ref, "masked vocabulary")
+    g = run_gpu(sv, w, cuda, probs=True)
+    have = ~np.isnan(ref["px"])
+    assert np.max(np.abs(g["p"][have] - ref["px"][have])) < 1e-5
+    assert np.max(np.abs(g["q"][have] - ref["qx"][have])) < 1e-5
+    used = ~np.isnan(ref["row_max"]) & ~np.isnan(g["row_max"])
+    np.testing.assert_array_equal(g["row_max"][used], ref["row_max"][used].astype(np.float32))
+    s_used = ~np.isnan(ref["row_sum"]) & ~np.isnan(g["row_sumexp"])
+    assert s_used.sum() > 24
+    rel = np.abs(g["row_sumexp"][s_used] - ref["row_sum"][s_used]) / ref["row_sum"][s_used]
+    assert rel.max() < 1e-5, rel.max()
+
+
 def test_data_errors_are_per_sequence(sv, cuda):
     w = workload("c3", 0, 16)
     bad = dataclasses.replace(w, tokens=w.tokens.copy(), temperature=w.temperature.copy())
