@@ -82,6 +82,33 @@ def test_draft_sample_parity(sv, cuda, dtype, V, rows):
     np.testing.assert_array_equal(prob[greedy], 1.0)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_draft_sample_masked_vocabulary(sv, cuda, dtype):
+    """Masked (-inf) logits carry no probability: a masked prefix longer
+    than a workgroup's first tile of loads, a padded tail, a block across
+    segment boundaries, scattered entries."""
+    V, rows = 40000, 96
+    g = np.random.default_rng(53)
+    z = (g.standard_normal((rows, V)) * 2).astype(np.float32)
+    idx = np.arange(V)
+    for r in range(rows):
+        kind = r % 4
+        if kind == 0:
+            z[r, idx < 2600] = -np.inf
+        elif kind == 1:
+            z[r, idx >= V - 464] = -np.inf
+        elif kind == 2:
+            z[r, (idx >= 7000) & (idx < 18000)] = -np.inf
+        else:
+            z[r, g.random(V) < 0.3] = -np.inf
+    stored = wl.bf16_round(z) if dtype == "bf16" else z
+    T = g.choice(np.array([0.0, 0.6, 1.0], np.float32), size=rows)
+    u = (g.integers(0, 1 << 24, size=rows) / float(1 << 24)).astype(np.float32)
+    tok, prob = run_sample(sv, stored, T, u, cuda)
+    check_sample(stored, T, u, tok, prob, f"masked {dtype}")
+    assert np.all(np.isfinite(z[np.arange(rows), tok]))
+
+
 def test_draft_sample_zipf_rows(sv, cuda):
     """Zipf-shaped rows like the workloads' target logits, bf16, V = 128256."""
     w = wl.make_workload("c3", trial=5, B=96)
