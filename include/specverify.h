@@ -246,7 +246,8 @@ sv_status_t spec_stream_probe(const void *data, int64_t bytes, int64_t seg_bytes
  * call over the recorded calls that launched the kernel (ms[i] belongs to
  * spec_verify_kernel_name(i); NaN for kernels not selected or not launched:
  * the staged form launches row_stats, accept, draw_sums and draw_pick in
- * one pass; with early exit row_lead, accept_lead, rest and draw_pick,
+ * one pass, or row_stats and draw_all (spec_verify_set_draw); with early
+ * exit row_lead, accept_lead, rest and draw_pick,
  * or in the gathered form row_lead, accept_lead, row_stats, accept,
  * row_draft, draw_sums and draw_pick; the fused form fused_reset and
  * fused); it returns the number
@@ -254,7 +255,7 @@ sv_status_t spec_stream_probe(const void *data, int64_t bytes, int64_t seg_bytes
  * failed.
  * spec_verify_timing returns SV_ERR_SHAPE for every < 1.  The probe uses
  * one device: turn it off and on again after switching devices. */
-#define SV_TIME_ALL 0x3FF
+#define SV_TIME_ALL 0x7FF
 sv_status_t spec_verify_timing(int32_t kernels, int32_t every);
 int32_t spec_verify_kernel_times(float *ms, int32_t max_kernels);
 const char *spec_verify_kernel_name(int32_t i);
@@ -267,8 +268,9 @@ const char *spec_verify_kernel_name(int32_t i);
  * SV_ERR_SHAPE for negative values. */
 sv_status_t spec_verify_set_geometry(int64_t seg_elems, int64_t chunk_elems);
 
-/* Form of the launch.  SV_MODE_STAGED: four kernels (row pass, accept scan,
- * draw chunk sums, pick), each step published by a kernel boundary.
+/* Form of the launch.  SV_MODE_STAGED: a kernel per step (row pass, accept
+ * scan, draw chunk sums, pick; small one-pass calls join the last three,
+ * see spec_verify_set_draw), each step published by a kernel boundary.
  * SV_MODE_FUSED: one persistent kernel (after a small kernel that clears its
  * counters) whose workgroups take row segments and draw chunks from a
  * device-side queue; sequence b's draw chunks are queued fused_lag
@@ -311,6 +313,18 @@ sv_status_t spec_verify_set_early_exit(int32_t lead_positions);
  * an unknown mode or a negative lag. */
 enum { SV_QUEUE_OVERLAP = 0, SV_QUEUE_FINAL = 1, SV_QUEUE_HANDOFF = 2 };
 sv_status_t spec_verify_set_queue(int32_t mode, int32_t lag_accept, int32_t lag_draw);
+
+/* The draw of a one-pass call outside the gathered form (no early exit):
+ * SV_DRAW_ONE: one launch, "draw_all" (sequences x chunks), in which every
+ * workgroup runs its sequence's accept scan (only one of them writes its
+ * outputs), sums its chunk, and the workgroup that sums a sequence's last
+ * chunk picks the token; SV_DRAW_THREE: three launches, "accept",
+ * "draw_sums" and "draw_pick".  SV_DRAW_AUTO (the default): one launch
+ * while the draw's workgroups fit one round on the CUs (B * chunks <= 4 per
+ * CU), else three.  Both give identical outputs.  Returns SV_ERR_SHAPE for
+ * an unknown mode. */
+enum { SV_DRAW_AUTO = 0, SV_DRAW_ONE = 1, SV_DRAW_THREE = 2 };
+sv_status_t spec_verify_set_draw(int32_t mode);
 
 #ifdef __cplusplus
 }

@@ -10,16 +10,17 @@ from __future__ import annotations
 
 import ctypes
 
-from ._lib import (LIB_PATH, SV_BF16, SV_F32, SV_K_MAX, SV_MODE_AUTO, SV_MODE_FUSED, SV_MODE_STAGED,
-                   SV_QUEUE_FINAL, SV_QUEUE_HANDOFF, SV_QUEUE_OVERLAP, SV_TIME_ALL, SpecVerifyError, check, lib)
+from ._lib import (LIB_PATH, SV_BF16, SV_DRAW_AUTO, SV_DRAW_ONE, SV_DRAW_THREE, SV_F32, SV_K_MAX, SV_MODE_AUTO,
+                   SV_MODE_FUSED, SV_MODE_STAGED, SV_QUEUE_FINAL, SV_QUEUE_HANDOFF, SV_QUEUE_OVERLAP, SV_TIME_ALL,
+                   SpecVerifyError, check, lib)
 
 __all__ = [
     "spec_verify", "spec_verify_probs", "spec_verify_gathered", "spec_draft_sample",
     "spec_commit", "spec_adapt_k", "spec_ngram_draft",
     "spec_verify_workspace_size", "spec_verify_release",
-    "stream_probe", "timing", "kernel_times", "set_geometry", "set_mode", "set_early_exit", "set_queue", "SpecVerifyError",
+    "stream_probe", "timing", "kernel_times", "set_geometry", "set_mode", "set_early_exit", "set_queue", "set_draw", "SpecVerifyError",
     "SV_F32", "SV_BF16", "SV_K_MAX", "SV_MODE_AUTO", "SV_MODE_STAGED", "SV_MODE_FUSED", "SV_QUEUE_OVERLAP",
-    "SV_QUEUE_FINAL", "SV_QUEUE_HANDOFF", "LIB_PATH", "lib",
+    "SV_QUEUE_FINAL", "SV_QUEUE_HANDOFF", "SV_DRAW_AUTO", "SV_DRAW_ONE", "SV_DRAW_THREE", "LIB_PATH", "lib",
 ]
 
 
@@ -297,6 +298,12 @@ def set_queue(mode: int = SV_QUEUE_OVERLAP, lag_accept: int = 0, lag_draw: int =
     """Where early exit's second-round accept scans and draw chunks run, and
     their lags in sequences (0 = automatic); outputs do not change."""
     check(lib().spec_verify_set_queue(int(mode), int(lag_accept), int(lag_draw)), "spec_verify_set_queue")
+
+
+def set_draw(mode: int = SV_DRAW_AUTO) -> None:
+    """One-pass draw as one launch (SV_DRAW_ONE), three (SV_DRAW_THREE) or
+    chosen by size (SV_DRAW_AUTO); outputs do not change."""
+    check(lib().spec_verify_set_draw(int(mode)), "spec_verify_set_draw")
 
 
 def set_mode(mode: int = SV_MODE_AUTO, fused_lag: int = 0) -> None:

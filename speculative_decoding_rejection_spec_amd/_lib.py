@@ -15,9 +15,10 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 
 SV_F32, SV_BF16 = 0, 1
 SV_K_MAX = 63
-SV_TIME_ALL = 0x3FF
+SV_TIME_ALL = 0x7FF
 SV_MODE_AUTO, SV_MODE_STAGED, SV_MODE_FUSED = 0, 1, 2
 SV_QUEUE_OVERLAP, SV_QUEUE_FINAL, SV_QUEUE_HANDOFF = 0, 1, 2
+SV_DRAW_AUTO, SV_DRAW_ONE, SV_DRAW_THREE = 0, 1, 2
 STATUS = {0: "SV_OK", -1: "SV_ERR_NULL", -2: "SV_ERR_SHAPE", -3: "SV_ERR_DTYPE",
           -4: "SV_ERR_ALIGN", -5: "SV_ERR_WORKSPACE", -6: "SV_ERR_HIP"}
 
@@ -43,6 +44,7 @@ SIGNATURES = {
     "spec_verify_kernel_name": (ctypes.c_char_p, [_I32]),
     "spec_verify_set_geometry": (_I32, [_I64, _I64]),
     "spec_verify_set_queue": (_I32, [_I32, _I32, _I32]),
+    "spec_verify_set_draw": (_I32, [_I32]),
     "spec_stream_probe": (_I32, [_P, _I64, _I64, _P, _P]),
     "spec_verify_set_mode": (_I32, [_I32, _I32]),
     "spec_verify_set_early_exit": (_I32, [_I32]),

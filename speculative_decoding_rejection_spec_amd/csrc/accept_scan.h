@@ -151,9 +151,16 @@ __device__ __forceinline__ void list_rest(const Problem& p, const Plan& plan, in
 // Diagnostics of rows that were not read are NaN.  Returns (the same in
 // every lane) whether the scan settled the sequence with a draw still to
 // make, i.e. wrote a DrawTask other than kNone.
+//
+// task_out (one pass only): also returns the DrawTask in every lane (kind
+// kNone when there is nothing to draw).  emit = false: the scan writes
+// nothing at all -- for workgroups that need the task of a sequence whose
+// outputs another workgroup writes (the same scan over the same inputs
+// gives the same task).
 template <bool kCo>
 __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& plan, int32_t b,
-                                                int32_t limit = kKMax + 1, int32_t* done = nullptr) {
+                                                int32_t limit = kKMax + 1, int32_t* done = nullptr,
+                                                DrawTask* task_out = nullptr, bool emit = true) {
     const int lane = threadIdx.x & 63;
     int64_t o, o1;
     if (p.offsets) { o = p.offsets[b]; o1 = p.offsets[b + 1]; }
@@ -195,6 +202,8 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
     // Data error: the sequence's own token slots (when its offsets describe
     // a range inside the batch) are all -1.
     auto data_error = [&]() {
+        if (task_out) task_out->kind = kNone;
+        if (!emit) return;
         if (o >= 0 && o1 >= o && o1 <= p.total)
             for (int64_t i = lane; i <= k64; i += 64) p.out_tokens[o + b + i] = -1;
         if (lane == 0) {
@@ -252,6 +261,23 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
         *done = early_draw ? kDecidedEarlyDraw : kDecided;
         if (early_draw) plan.early[atomicAdd(plan.early_n, 1u)] = b;
     }
+
+    const int32_t kind = greedy ? kNone : (n < k ? kResidual : kBonus);
+    if (task_out) {
+        // (gathered form excluded: its residual needs the draft row read later)
+        DrawTask& t = *task_out;
+        t.kind = kind;
+        t.out_slot = static_cast<int32_t>(o + b + n);
+        t.trow = o + b + n;
+        t.drow = o + n;
+        t.m_t = __shfl(rt.m, n, 64);
+        t.m_d = n < k ? __shfl(rd.m, n, 64) : 0.f;
+        t.T = Tf;
+        t.u = p.uniforms[o + b + k];
+        const double th = (!greedy && n < k) ? log2_norm(rt, c) - log2_norm(rd, c) : 0.0;
+        t.theta = __shfl(th, n, 64);
+    }
+    if (!emit) return !greedy;
 
     // Slot n of a sampling sequence is written by the draw alone: in the
     // fused form the draw runs in another workgroup, possibly on another XCD,

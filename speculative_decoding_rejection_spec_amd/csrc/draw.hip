@@ -1,6 +1,8 @@
 // draw.hip -- the staged draw: draw_sums (grid sequence x chunk, 256
-// threads) and draw_pick (one 1024- or 512-thread workgroup per sequence).
-// The kernel boundary publishes the chunk sums; the work itself is in
+// threads) and draw_pick (one 1024- or 512-thread workgroup per sequence),
+// where the kernel boundary publishes the chunk sums; or, for one-pass calls
+// whose draw fits one round of workgroups, draw_all, which also runs the
+// accept scans and the picks.  The work itself is in accept_scan.h and
 // draw_pass.h.
 #include "draw_pass.h"
 
@@ -70,7 +72,53 @@ __global__ __launch_bounds__(kPickThreads) void draw_pick_kernel(Problem p, Plan
     pick_sequence<DT, kPickThreads, false>(p, plan, task, b, tbl, lds.pick);
 }
 
+// One pass, small calls: the accept scan, the chunk sums and the pick in
+// one launch (grid sequence x chunk, 256 threads).  Every workgroup of
+// sequence b runs b's accept scan to learn its draw task (workgroup 0 of
+// the sequence writes the scan's outputs, the others write nothing); the
+// workgroup that completes the sequence's count of summed chunks (the
+// sums written through before the count) picks the token.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void draw_all_kernel(Problem p, Plan plan) {
+    const int64_t w = blockIdx.x;
+    const int32_t b = static_cast<int32_t>(w / plan.nchunk);
+    const int32_t c = static_cast<int32_t>(w - static_cast<int64_t>(b) * plan.nchunk);
+    __shared__ drawpass::TabEntry tbl[256];
+    __shared__ union {
+        DrawLds draw;
+        PickLds<kThreads> pick;
+    } lds;
+    __shared__ DrawTask s_task;
+    __shared__ int32_t s_last;
+    load_exp2_table(tbl, kThreads);
+    if (threadIdx.x < 64) {
+        DrawTask t;
+        accept_sequence<false>(p, plan, b, kKMax + 1, nullptr, &t, c == 0);
+        if (threadIdx.x == 0) s_task = t;
+    }
+    __syncthreads();
+    const DrawTask task = s_task;
+    if (task.kind == kNone) return;            // greedy or a data error: nothing to draw
+    draw_chunk<DT, true>(p, plan, task, b, c, tbl, lds.draw);
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0)
+        s_last = __hip_atomic_fetch_add(plan.picked + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u ==
+                 static_cast<uint32_t>(plan.nchunk);
+    __syncthreads();
+    if (s_last) pick_sequence<DT, kThreads, true>(p, plan, task, b, tbl, lds.pick);
+}
+
 }  // namespace
+
+hipError_t launch_draw_all(const Problem& p, const Plan& plan, hipStream_t s) {
+    const int64_t blocks = static_cast<int64_t>(p.B) * plan.nchunk;
+    if (p.dtype == SV_BF16)
+        draw_all_kernel<SV_BF16><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s>>>(p, plan);
+    else
+        draw_all_kernel<SV_F32><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s>>>(p, plan);
+    return hipGetLastError();
+}
 
 hipError_t launch_draw_sums(const Problem& p, const Plan& plan, hipStream_t s) {
     const int64_t blocks = static_cast<int64_t>(p.B) * plan.nchunk;

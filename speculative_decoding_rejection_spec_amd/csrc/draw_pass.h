@@ -503,56 +503,61 @@ __device__ __forceinline__ void pick_sequence(const Problem& p, const Plan& plan
     if (tid == 0) L.rescan = 0;
 
     // All loads that need only the sequence are issued together: the chunk
-    // sums (one chunk per thread) and the band entries of the first NT/32
-    // chunks (one slot per thread; an entry past its wave's count is stale
-    // and ignored).
+    // sums and the band counts of chunk tid (a row with more chunks than the
+    // workgroup has threads loads the others' in the loops below).
     double Sp = 0.0, Sq = 0.0, ca = 0.0, cbq = 0.0;
+    int32_t cnt0[kWaves] = {};
     for (int32_t j = tid; j < nchunk; j += NT) {
         const double xsp = ld_co<kCo>(&cs[j].sp);
         Sp += xsp;
         Sq += ld_co<kCo>(&cs[j].sq);
         L.spc[j] = xsp;
-        if (j == tid) { ca = ld_co<kCo>(&cs[j].a); cbq = ld_co<kCo>(&cs[j].b); }
-    }
-    const int32_t pj = tid / kSlots, ps = tid % kSlots;
-    int32_t pcnt = 0;
-    double pwt = 0.0, pwd = 0.0;
-    if (resid_task && pj < nchunk) {
-        pcnt = ld_co<kCo>(&plan.band_n[(cb + pj) * kWaves + ps / kWaveCap]);
-        const double* pw = plan.band_w + ((cb + pj) * kSlots + ps) * 2;
-        pwt = ld_co<kCo>(&pw[0]);
-        pwd = ld_co<kCo>(&pw[1]);
+        if (j == tid) {
+            ca = ld_co<kCo>(&cs[j].a);
+            cbq = ld_co<kCo>(&cs[j].b);
+            if (resid_task)
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) cnt0[w] = ld_co<kCo>(&plan.band_n[(cb + j) * kWaves + w]);
+        }
     }
     pick_sum2<NT>(Sp, Sq, L.red2);              // (its barriers also publish spc)
     const double iSp = 1.0 / Sp, iSq = resid_task ? 1.0 / Sq : 0.0;
 
     if (resid_task) {
+        // Chunk j's residual mass, by thread j: A_j / S_p - B_j / S_q plus
+        // max(0, w_t / S_p - w_d / S_q) of its listed band tokens in list
+        // order; NaN marks a chunk whose lists overflowed (rescanned below).
         for (int32_t j = tid; j < nchunk; j += NT) {
-            const double a = (j == tid) ? ca : ld_co<kCo>(&cs[j].a);
-            const double bq = (j == tid) ? cbq : ld_co<kCo>(&cs[j].b);
-            L.mass[j] = a * iSp - bq * iSq;
-        }
-        __syncthreads();
-        // Band terms: 32 lanes per chunk (a half wave), one listed token
-        // each; a fixed shuffle tree sums them (deterministic order).
-        for (int32_t j0 = 0; j0 < nchunk; j0 += NT / kSlots) {
-            const int32_t j = j0 + pj;
-            int32_t cnt = pcnt;
-            double wt = pwt, wd = pwd;
-            if (j0 > 0) {
-                cnt = 0;
-                if (j < nchunk) {
-                    cnt = ld_co<kCo>(&plan.band_n[(cb + j) * kWaves + ps / kWaveCap]);
-                    const double* pw = plan.band_w + ((cb + j) * kSlots + ps) * 2;
-                    wt = ld_co<kCo>(&pw[0]);
-                    wd = ld_co<kCo>(&pw[1]);
+            double a = ca, bq = cbq;
+            int32_t cnt[kWaves];
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) cnt[w] = cnt0[w];
+            if (j != tid) {
+                a = ld_co<kCo>(&cs[j].a);
+                bq = ld_co<kCo>(&cs[j].b);
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) cnt[w] = ld_co<kCo>(&plan.band_n[(cb + j) * kWaves + w]);
+            }
+            double m = a * iSp - bq * iSq;
+            bool over = false;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                over = over || cnt[w] > kWaveCap;
+                const int32_t nw = min(cnt[w], kWaveCap);
+                if (nw > 0) {
+                    const double* pw = plan.band_w + ((cb + j) * kSlots + w * kWaveCap) * 2;
+                    double wt[kWaveCap], wd[kWaveCap];
+#pragma unroll
+                    for (int e = 0; e < kWaveCap; ++e) {
+                        wt[e] = e < nw ? ld_co<kCo>(&pw[2 * e]) : 0.0;
+                        wd[e] = e < nw ? ld_co<kCo>(&pw[2 * e + 1]) : 0.0;
+                    }
+#pragma unroll
+                    for (int e = 0; e < kWaveCap; ++e)
+                        if (e < nw) m += fmax(0.0, wt[e] * iSp - wd[e] * iSq);
                 }
             }
-            double term = (j < nchunk && ps % kWaveCap < cnt) ? fmax(0.0, wt * iSp - wd * iSq) : 0.0;
-            for (int off = kSlots / 2; off > 0; off >>= 1) term += __shfl_xor(term, off, 64);
-            const bool over = j < nchunk && cnt > kWaveCap;
-            const bool any_over = (__ballot(over) >> ((tid & 63) & ~(kSlots - 1))) & 0xffffffffull;
-            if (j < nchunk && ps == 0) L.mass[j] = any_over ? NAN : L.mass[j] + term;
+            L.mass[j] = over ? NAN : m;
             if (over) L.rescan = 1;            // benign race: every writer stores 1
         }
         __syncthreads();
@@ -595,14 +600,13 @@ __device__ __forceinline__ void pick_sequence(const Problem& p, const Plan& plan
     const int64_t c0 = static_cast<int64_t>(L.chunk) * plan.chunk_len;
     const int64_t c1 = min(p.V, c0 + plan.chunk_len);
 
-    // Scan the chunk in pieces of kPiece tokens: lane tid owns kRun consecutive
-    // tokens of the piece, loaded together, masses kept in registers.
-    int32_t pick = INT32_MAX, last_pos = -1, mine = INT32_MAX;
-    double mine_mass = 0.0;
-    for (int64_t q0 = c0; q0 < c1 && pick == INT32_MAX; q0 += kPiece) {
+    // Scan the chunk in pieces of kPiece tokens: lane tid owns kRun
+    // consecutive tokens of the piece, loaded together, masses kept in
+    // registers.  The next piece's loads are issued before this piece's
+    // arithmetic.
+    auto load_piece = [&](int64_t q0, float* zt, float* zd) {
         const int64_t q1 = min(c1, q0 + kPiece);
         const int64_t r0 = q0 + static_cast<int64_t>(tid) * kRun;
-        float zt[kRun], zd[kRun];
         const bool vec = r0 + kRun <= q1 &&
                          (reinterpret_cast<uintptr_t>(rows.t + r0) & 15u) == 0 &&
                          (!resid || (reinterpret_cast<uintptr_t>(rows.d + r0) & 15u) == 0);
@@ -620,6 +624,20 @@ __device__ __forceinline__ void pick_sequence(const Problem& p, const Plan& plan
                 zd[i] = (in && resid) ? rows.zd(r0 + i) : 0.f;
             }
         }
+    };
+    int32_t pick = INT32_MAX, last_pos = -1, mine = INT32_MAX;
+    double mine_mass = 0.0;
+    float zt[kRun], zd[kRun];
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) zd[i] = 0.f;
+    load_piece(c0, zt, zd);
+    for (int64_t q0 = c0; q0 < c1 && pick == INT32_MAX; q0 += kPiece) {
+        const int64_t q1 = min(c1, q0 + kPiece);
+        const int64_t r0 = q0 + static_cast<int64_t>(tid) * kRun;
+        float nzt[kRun], nzd[kRun];
+#pragma unroll
+        for (int i = 0; i < kRun; ++i) { nzt[i] = 0.f; nzd[i] = 0.f; }
+        if (q1 < c1) load_piece(q1, nzt, nzd);
         double m[kRun];
         double local = 0.0;
         int32_t lp = -1;
@@ -644,6 +662,8 @@ __device__ __forceinline__ void pick_sequence(const Problem& p, const Plan& plan
         pick = first;
         last_pos = max(last_pos, lp);
         base += total;
+#pragma unroll
+        for (int i = 0; i < kRun; ++i) { zt[i] = nzt[i]; zd[i] = nzd[i]; }
     }
     if (pick != INT32_MAX) {
         // the thread that found the crossing holds the token's mass

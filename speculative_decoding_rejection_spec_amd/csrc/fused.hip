@@ -1,6 +1,6 @@
 // fused.hip -- the whole verify step in one persistent launch.
 //
-// The staged form runs four kernels back to back; the draw (fp64, bound by
+// The staged form runs a kernel per step back to back; the draw (fp64, bound by
 // vector ALU) then waits for the end of the row pass (bound by HBM), and
 // each kernel boundary drains the GPU.  Here one grid of resident
 // workgroups takes work items from a device-side queue in a fixed order:

@@ -32,6 +32,7 @@ template <int DT>
 __global__ __launch_bounds__(kThreads) void row_stats_kernel(Problem p, Plan plan) {
     const int64_t w = blockIdx.x;
     if (w == 0 && threadIdx.x == 0) *plan.dlist_n = 0;   // the accept scan fills the draft list
+    if (w < p.B && threadIdx.x == 0) plan.picked[w] = 0u;   // (the grid has at least B blocks)
     __shared__ RowLds lds;
     const int64_t row_all = w / plan.nseg;
     const int64_t seg = w - row_all * plan.nseg;

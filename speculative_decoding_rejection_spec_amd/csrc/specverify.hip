@@ -24,13 +24,13 @@ constexpr int32_t kAutoLead = -1;
 constexpr int64_t kAutoLeadBytes = 512ll << 20;
 constexpr int64_t kMaxChunks = 1024;          // draw chunks per row (the pick keeps them in LDS)
 constexpr int kMaxDevices = 64;
-constexpr int kNumKernels = 10;
+constexpr int kNumKernels = 11;
 enum { kKRowStats, kKAccept, kKDrawSums, kKDrawPick, kKFusedReset, kKFused, kKRowLead, kKAcceptLead,
-       kKRowDraft, kKRest };
+       kKRowDraft, kKRest, kKDrawAll };
 
 const char* const kKernelNames[kNumKernels] = {"row_stats", "accept",      "draw_sums", "draw_pick",
                                                "fused_reset", "fused",     "row_lead",  "accept_lead",
-                                               "row_draft", "rest"};
+                                               "row_draft", "rest",        "draw_all"};
 
 std::mutex g_mutex;
 int64_t g_seg_elems = 0;                     // 0: automatic (auto_lengths)
@@ -56,6 +56,14 @@ int32_t g_fused_lag = 0;                     // 0: chosen from the resident grid
 int32_t g_lead = kAutoLead;                  // early exit: leading positions read first (0: off)
 int32_t g_queue_mode = SV_QUEUE_OVERLAP;
 int32_t g_lag_a = 0, g_lag_c = 0;            // 0: chosen from the resident grid
+int32_t g_draw_mode = SV_DRAW_AUTO;
+// One pass: the draw runs as one launch (draw_all) while its workgroups
+// (sequences x chunks) fit one round on the CUs, counted at this many per
+// CU; a larger draw takes three launches (accept, draw_sums, draw_pick),
+// since the pick's count of summed chunks makes the workgroup that finishes
+// a sequence last do its pick, and with several rounds in flight those
+// land on whichever XCD already lags, which then lags further.
+constexpr int kDrawAllWgsPerCu = 4;
 constexpr int kRestWgsPerCu = 5;             // resident second-round workgroups per CU (its register count)
 
 hipError_t device_cus(int* cus) {
@@ -102,7 +110,7 @@ struct Geometry {
     int32_t nseg, nchunk;
     int64_t seg_len, chunk_len;
     size_t off_seg, off_task, off_csum, off_band_n, off_band_w, off_xlogit, off_ctr, off_done, off_sched,
-        off_blk_ctr, off_blk_seq, off_dlist, off_dlist_n, off_nbuf, off_early, off_early_n, off_aband, bytes;
+        off_blk_ctr, off_blk_seq, off_dlist, off_dlist_n, off_nbuf, off_early, off_early_n, off_aband, off_picked, bytes;
 };
 
 // Splits a row of V logits into n <= max_pieces pieces of about `target`
@@ -162,6 +170,8 @@ bool make_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dtype, int64_
     off = align256(off + sizeof(uint32_t));
     g.off_aband = off;
     off = align256(off + sizeof(int32_t) * static_cast<size_t>(B));
+    g.off_picked = off;
+    off = align256(off + sizeof(uint32_t) * static_cast<size_t>(B));
     g.bytes = off;
     return true;
 }
@@ -246,6 +256,7 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     plan.early = reinterpret_cast<int32_t*>(ws + g.off_early);
     plan.early_n = reinterpret_cast<uint32_t*>(ws + g.off_early_n);
     plan.aband = reinterpret_cast<int32_t*>(ws + g.off_aband);
+    plan.picked = reinterpret_cast<uint32_t*>(ws + g.off_picked);
     plan.queue_mode = g_queue_mode;
     Problem pr = p;
     if (!pr.out_n) pr.out_n = reinterpret_cast<int32_t*>(ws + g.off_nbuf);
@@ -351,6 +362,20 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
                 return launch_row_list(pr, plan, plan.sched, reinterpret_cast<const uint32_t*>(plan.blk_ctr),
                                        (2 * p.total + p.B) * static_cast<int64_t>(g.nseg), stream);
             });
+        // One pass, outside the gathered form: a draw that fits one round of
+        // workgroups runs as one launch with the accept scans and the picks.
+        const bool draw_all = !pr.draft_probs && plan.lead == 0 &&
+                              (g_draw_mode == SV_DRAW_ONE ||
+                               (g_draw_mode == SV_DRAW_AUTO &&
+                                static_cast<int64_t>(p.B) * g.nchunk <= static_cast<int64_t>(kDrawAllWgsPerCu) * plan.cus));
+        if (draw_all) {
+            ok = ok && launch(kKDrawAll, [&] { return launch_draw_all(pr, plan, stream); });
+            if (ev) {
+                g_ev_mask[g_timed_calls % kTimedCalls] = recorded;
+                ++g_timed_calls;
+            }
+            return ok ? SV_OK : SV_ERR_HIP;
+        }
         ok = ok && launch(kKAccept, [&] { return launch_accept(pr, plan, stream); });
         // Gathered form: the draft rows at the rejections.
         if (ok && pr.draft_probs)
@@ -647,6 +672,13 @@ sv_status_t spec_verify_set_queue(int32_t mode, int32_t lag_accept, int32_t lag_
     g_queue_mode = mode;
     g_lag_a = lag_accept;
     g_lag_c = lag_draw;
+    return SV_OK;
+}
+
+sv_status_t spec_verify_set_draw(int32_t mode) {
+    if (mode < SV_DRAW_AUTO || mode > SV_DRAW_THREE) return SV_ERR_SHAPE;
+    std::lock_guard<std::mutex> lock(g_mutex);
+    g_draw_mode = mode;
     return SV_OK;
 }
 

@@ -156,6 +156,7 @@ struct Plan {
     int32_t lag_a, lag_c;// early exit: the accept item of block j follows block j + lag_a, its chunks
                          // follow block j + lag_c (huge: none inserted, the gathered form)
     int32_t* aband;      // [B] 1: sequence b is left to the pick launch
+    uint32_t* picked;    // one pass, single draw launch: [B] chunks of sequence b summed so far
     int32_t queued;      // early exit with the draws beside the rows (not the gathered form)
     int32_t cus;         // compute units of the device
     int32_t queue_mode;  // SV_QUEUE_*: where the second round's draw chunks are summed
@@ -189,6 +190,7 @@ hipError_t launch_accept(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_accept_lead(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_draw_sums(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_draw_pick(const Problem& p, const Plan& plan, hipStream_t s);
+hipError_t launch_draw_all(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_fused_reset(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_fused(const Problem& p, const Plan& plan, const Fused& f, hipStream_t s);
 hipError_t fused_grid(int32_t dtype, int32_t* blocks);   // resident workgroups on this device

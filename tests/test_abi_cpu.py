@@ -142,6 +142,13 @@ def test_queue_knob(lib):
         assert lib.spec_verify_set_queue(mode, 0, 0) == OK
 
 
+def test_draw_knob(lib):
+    assert lib.spec_verify_set_draw(3) == SHAPE
+    assert lib.spec_verify_set_draw(-1) == SHAPE
+    for mode in (2, 1, 0):
+        assert lib.spec_verify_set_draw(mode) == OK
+
+
 def test_kernel_times_without_timed_call(lib):
     buf = (ctypes.c_float * 8)()
     assert lib.spec_verify_kernel_times(buf, 8) == -1

@@ -23,15 +23,17 @@ AMBIGUOUS = oracle.FLAG_A | oracle.FLAG_B | oracle.FLAG_D
 
 
 # Launch forms: staged with early exit after the first position (the
-# default for large batches), staged reading every row in one pass, and the
-# fused persistent kernel.  Every test below runs in each.
-MODES = ["early", "full", "fused"]
+# default for large batches), staged reading every row in one pass with the
+# draw as one launch ("full") or as three ("full3"), and the fused
+# persistent kernel.  Every test below runs in each.
+MODES = ["early", "full", "full3", "fused"]
 CURRENT = {"mode": None}
 
 
 def set_form(sv, form):
     sv.set_mode(sv.SV_MODE_FUSED if form == "fused" else sv.SV_MODE_STAGED)
     sv.set_early_exit(1 if form == "early" else 0)
+    sv.set_draw(sv.SV_DRAW_THREE if form == "full3" else sv.SV_DRAW_ONE if form == "full" else sv.SV_DRAW_AUTO)
 
 
 @pytest.fixture(scope="module", params=MODES)
@@ -49,6 +51,7 @@ def sv(cuda, request):
     yield sv
     sv.set_mode(sv.SV_MODE_AUTO)
     sv.set_early_exit(-1)
+    sv.set_draw(sv.SV_DRAW_AUTO)
 
 
 def to_device(w, dev):
