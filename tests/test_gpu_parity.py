@@ -406,6 +406,21 @@ def test_masked_vocabulary(sv, cuda, dtype):
     assert rel.max() < 1e-5, rel.max()
 
 
+def test_hand_worked_cases(sv, cuda):
+    """The verify steps worked by hand in tests/golden/hand_cases.json give
+    the hand-computed accept counts and tokens on the GPU too."""
+    from test_oracle_golden import CASES, workload_of
+    for case in CASES:
+        for dtype in ("f32", "bf16"):
+            w = workload_of(case)
+            if dtype == "bf16":
+                w = wl.assemble(wl.bf16_to_f32(wl.bf16_round(w.target)), wl.bf16_to_f32(wl.bf16_round(w.draft)),
+                                w.tokens, w.uniforms, w.temperature, w.k, dtype="bf16")
+            gpu = run_gpu(sv, w, cuda)
+            assert int(gpu["n"][0]) == case["n"], (case["name"], dtype)
+            assert gpu["tokens"].tolist() == case["out"], (case["name"], dtype)
+
+
 def test_data_errors_are_per_sequence(sv, cuda):
     w = workload("c3", 0, 16)
     bad = dataclasses.replace(w, tokens=w.tokens.copy(), temperature=w.temperature.copy())
