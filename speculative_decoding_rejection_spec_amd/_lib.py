@@ -67,6 +67,11 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
                               f"python -m speculative_decoding_rejection_spec_amd.build")
+        # torch first: it brings its own HIP runtime (soname libamdhip64.so.7),
+        # which the library's dependency then resolves to.  Loaded the other
+        # way round, the process would hold two HIP runtimes and the library
+        # would launch onto streams its runtime does not know.
+        import torch  # noqa: F401
         handle = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(handle, name)

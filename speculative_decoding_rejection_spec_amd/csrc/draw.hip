@@ -28,15 +28,21 @@ __global__ __launch_bounds__(kThreads) void draw_sums_kernel(Problem p, Plan pla
 // redone here first -- its accept scan if its leading positions left it
 // undecided, then every chunk -- with the chunk pass of a 256-thread
 // workgroup (the other threads only take part in its barriers).
+// (At 4 waves per SIMD two 512-thread workgroups share a CU: at most 128 VGPRs.)
 template <int DT, int kPickThreads>
-__global__ __launch_bounds__(kPickThreads) void draw_pick_kernel(Problem p, Plan plan) {
+__global__ __launch_bounds__(kPickThreads, 4) void draw_pick_kernel(Problem p, Plan plan) {
     const int32_t b = blockIdx.x;
     __shared__ drawpass::TabEntry tbl[256];
     __shared__ union {
         PickLds<kPickThreads> pick;
         DrawLds draw;
     } lds;
-    const bool redo = plan.queued && (plan.queue_mode == SV_QUEUE_FINAL || plan.aband[b] != 0);
+    // The loads of the common path are issued together, before anything
+    // depends on them: the redo flag, the task, chunk threadIdx.x's sums.
+    const int32_t ab = plan.queued ? plan.aband[b] : 0;
+    const DrawTask task0 = load_task<false>(p, plan, b);
+    const PickPrefetch pf = pick_prefetch<false>(plan, b);
+    const bool redo = plan.queued && (plan.queue_mode == SV_QUEUE_FINAL || ab != 0);
     if (redo) {
         load_exp2_table(tbl, kPickThreads);
         if (plan.done[b] == kUndecided) {
@@ -50,10 +56,10 @@ __global__ __launch_bounds__(kPickThreads) void draw_pick_kernel(Problem p, Plan
             draw_chunk<DT, true, kPickThreads>(p, plan, task, b, c, tbl, lds.draw);
         wait_stores();
         __syncthreads();
-        pick_sequence<DT, kPickThreads, true>(p, plan, task, b, tbl, lds.pick);
+        pick_sequence<DT, kPickThreads, true>(p, plan, task, b, tbl, lds.pick, pick_prefetch<true>(plan, b));
         return;
     }
-    const DrawTask task = load_task<false>(p, plan, b);   // (issued before the table's loads)
+    const DrawTask task = task0;
     load_exp2_table(tbl, kPickThreads);
     if (task.kind == kNone) return;
     if (task.kind == kResidual && !(fabsf(task.m_d) <= 3.4e38f)) {
@@ -69,7 +75,7 @@ __global__ __launch_bounds__(kPickThreads) void draw_pick_kernel(Problem p, Plan
         return;
     }
     __syncthreads();
-    pick_sequence<DT, kPickThreads, false>(p, plan, task, b, tbl, lds.pick);
+    pick_sequence<DT, kPickThreads, false>(p, plan, task, b, tbl, lds.pick, pf);
 }
 
 // One pass, small calls: the accept scan, the chunk sums and the pick in
@@ -106,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void draw_all_kernel(Problem p, Plan plan
         s_last = __hip_atomic_fetch_add(plan.picked + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u ==
                  static_cast<uint32_t>(plan.nchunk);
     __syncthreads();
-    if (s_last) pick_sequence<DT, kThreads, true>(p, plan, task, b, tbl, lds.pick);
+    if (s_last) pick_sequence<DT, kThreads, true>(p, plan, task, b, tbl, lds.pick, pick_prefetch<true>(plan, b));
 }
 
 }  // namespace

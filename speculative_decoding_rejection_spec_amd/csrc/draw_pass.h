@@ -482,14 +482,39 @@ __device__ __forceinline__ void find_chunk(const double* m, int32_t n, double u,
 
 }  // namespace drawpass
 
+// The loads of a pick that need only the sequence, for chunk threadIdx.x:
+// its sums and band counts (so they can be issued before the task is known;
+// for a bonus draw all but sp are unused).
+struct PickPrefetch {
+    double sp = 0.0, sq = 0.0, a = 0.0, b = 0.0;
+    int32_t cnt[kWaves] = {};
+};
+template <bool kCo>
+__device__ __forceinline__ PickPrefetch pick_prefetch(const Plan& plan, int32_t b) {
+    PickPrefetch f;
+    const int32_t j = threadIdx.x;
+    if (j < plan.nchunk) {
+        const int64_t cj = static_cast<int64_t>(b) * plan.nchunk + j;
+        const ChunkSums* c = plan.csum + cj;
+        f.sp = ld_co<kCo>(&c->sp);
+        f.sq = ld_co<kCo>(&c->sq);
+        f.a = ld_co<kCo>(&c->a);
+        f.b = ld_co<kCo>(&c->b);
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) f.cnt[w] = ld_co<kCo>(&plan.band_n[cj * kWaves + w]);
+    }
+    return f;
+}
+
 // The pick of sequence b (NT threads, NT a multiple of 256): from the chunk
 // sums of every chunk of its draw, the emitted token.  `task` is the
-// sequence's DrawTask (kind != kNone); plan.nchunk <= MAXC.  kCo: the chunk
-// sums come from other workgroups of the same launch.
+// sequence's DrawTask (kind != kNone); plan.nchunk <= MAXC; pf is
+// pick_prefetch<kCo>(plan, b).  kCo: the chunk sums come from other
+// workgroups of the same launch.
 template <int DT, int NT, bool kCo, int MAXC = kMaxPickChunks>
 __device__ __forceinline__ void pick_sequence(const Problem& p, const Plan& plan, const DrawTask& task,
                                               int32_t b, const drawpass::TabEntry* tbl,
-                                              PickLds<NT, MAXC>& L) {
+                                              PickLds<NT, MAXC>& L, const PickPrefetch& pf) {
     using namespace drawpass;
     static_assert(NT % 256 == 0 && NT <= 1024, "pick workgroup size");
     constexpr int N = Vec<DT>::N;
@@ -502,23 +527,24 @@ __device__ __forceinline__ void pick_sequence(const Problem& p, const Plan& plan
     const ChunkSums* cs = plan.csum + cb;
     if (tid == 0) L.rescan = 0;
 
-    // All loads that need only the sequence are issued together: the chunk
-    // sums and the band counts of chunk tid (a row with more chunks than the
-    // workgroup has threads loads the others' in the loops below).
-    double Sp = 0.0, Sq = 0.0, ca = 0.0, cbq = 0.0;
-    int32_t cnt0[kWaves] = {};
-    for (int32_t j = tid; j < nchunk; j += NT) {
+    // Chunk tid's sums and band counts come prefetched (a row with more
+    // chunks than the workgroup has threads loads the others' here and in
+    // the loop below).
+    double Sp = 0.0, Sq = 0.0;
+    const double ca = pf.a, cbq = pf.b;
+    int32_t cnt0[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) cnt0[w] = pf.cnt[w];
+    if (tid < nchunk) {
+        Sp = pf.sp;
+        Sq = pf.sq;
+        L.spc[tid] = pf.sp;
+    }
+    for (int32_t j = tid + NT; j < nchunk; j += NT) {
         const double xsp = ld_co<kCo>(&cs[j].sp);
         Sp += xsp;
         Sq += ld_co<kCo>(&cs[j].sq);
         L.spc[j] = xsp;
-        if (j == tid) {
-            ca = ld_co<kCo>(&cs[j].a);
-            cbq = ld_co<kCo>(&cs[j].b);
-            if (resid_task)
-#pragma unroll
-                for (int w = 0; w < kWaves; ++w) cnt0[w] = ld_co<kCo>(&plan.band_n[(cb + j) * kWaves + w]);
-        }
     }
     pick_sum2<NT>(Sp, Sq, L.red2);              // (its barriers also publish spc)
     const double iSp = 1.0 / Sp, iSq = resid_task ? 1.0 / Sq : 0.0;

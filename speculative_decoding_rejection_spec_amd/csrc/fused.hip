@@ -108,7 +108,7 @@ __device__ __noinline__ void do_chunk(const Problem& p, const Plan& plan, const 
 template <int DT>
 __device__ __noinline__ void do_pick(const Problem& p, const Plan& plan, const DrawTask& task, int32_t b,
                                      const drawpass::TabEntry* tbl, PickLds<kThreads, kFusedMaxChunks>& lds) {
-    pick_sequence<DT, kThreads, true, kFusedMaxChunks>(p, plan, task, b, tbl, lds);
+    pick_sequence<DT, kThreads, true, kFusedMaxChunks>(p, plan, task, b, tbl, lds, pick_prefetch<true>(plan, b));
 }
 
 template <int DT>

@@ -552,3 +552,28 @@ def test_fused_matches_staged_bitwise(sv, cuda):
     a, b = out[sv.SV_MODE_STAGED], out[sv.SV_MODE_FUSED]
     for key in a:
         np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+
+
+def test_library_loaded_before_torch(cuda):
+    """Touching the library before torch is imported still leaves one HIP
+    runtime in the process (the binding imports torch before loading it):
+    a verify launched on torch's stream then succeeds."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import speculative_decoding_rejection_spec_amd as sv\n"
+        "sv.set_geometry(0, 0)\n"
+        "import numpy as np, torch, workloads as wl\n"
+        "w = wl.make_workload('c1', trial=0, B=4)\n"
+        "d = torch.device('cuda:0')\n"
+        "t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(d)\n"
+        "tok, n = sv.spec_verify(t(w.target), t(w.draft), t(w.tokens), t(w.offsets), t(w.uniforms),\n"
+        "                        t(w.temperature))\n"
+        "torch.cuda.synchronize()\n"
+        "print('ok', n.cpu().numpy().tolist())\n" % root)
+    print("[subprocess: library before torch]", flush=True)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=110)
+    assert r.returncode == 0 and "ok" in r.stdout, r.stderr[-2000:]
