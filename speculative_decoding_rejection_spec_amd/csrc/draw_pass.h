@@ -13,22 +13,25 @@
 // closer together than fp32 rounding, so the CDF is built in fp64 from
 // w = 2^((z - m) log2(e) / T) of the exact logits and row maxima.
 //
-// draw_chunk (one workgroup per (sequence, chunk)) reads the draw rows once:
-//   * bonus draw: per chunk, W_c = sum of w_t;
-//   * residual draw: per chunk, S_p,c = sum w_t and S_q,c = sum w_d (the fp64
-//     normalisers), and A_c, B_c = sums of w_t, w_d over the tokens with
+// draw_chunk (one workgroup per (sequence, chunk)) reads the draw rows once;
+// wave w of it covers sub-chunk w, a contiguous quarter of the chunk, and
+// keeps its sums on its own:
+//   * bonus draw: per sub-chunk, W_s = sum of w_t;
+//   * residual draw: per sub-chunk, S_p,s = sum w_t and S_q,s = sum w_d (the
+//     fp64 normalisers), and A_s, B_s = sums of w_t, w_d over the tokens with
 //     p_v > q_v.  p_v > q_v iff d_v = log2(w_t / w_d) exceeds
 //     theta = log2(S_p / S_q); the accept scan supplies theta from the row
 //     pass's normalisers (within about 1e-5 in log2 units), so tokens with
 //     |d_v - theta| > kBand are classified exactly, and the few inside the
-//     band are listed per wave (up to kWaveCap each) with their (w_t, w_d),
+//     band are listed per sub-chunk (up to kWaveCap) with their (w_t, w_d),
 //     to get their exact mass once S_p and S_q are known.  The residual mass
-//     of chunk c is R_c = A_c / S_p - B_c / S_q + sum over its band tokens of
-//     max(0, w_t/S_p - w_d/S_q); a chunk whose lists overflowed is rescanned.
-// pick_sequence (one workgroup per sequence) forms Z = sum_c R_c, finds the
-// chunk whose cumulative mass crosses u Z with a wave-wide scan, and scans
-// that one chunk with a workgroup-wide fp64 prefix sum over masses held in
-// registers.
+//     of sub-chunk s is R_s = A_s / S_p - B_s / S_q + sum over its band
+//     tokens of max(0, w_t/S_p - w_d/S_q); a sub-chunk whose list overflowed
+//     is rescanned.
+// pick_sequence (one workgroup per sequence) forms Z = sum_s R_s, finds the
+// sub-chunk whose cumulative mass crosses u Z with a wave-wide scan, and
+// scans that one sub-chunk with a workgroup-wide fp64 prefix sum over masses
+// held in registers.
 //
 // 2^y in fp64 follows Tang's table-driven method (ACM TOMS 15(2), 1989) in
 // base 2 with a 256-entry table: y = k + j/256 + r with |r| <= 1/512,
@@ -50,7 +53,6 @@ constexpr double kLog2e = 0x1.71547652b82fep+0;
 constexpr double kDegenerateZ = 1e-9;            // residual mass treated as empty
 constexpr double kBand = 3e-5;                   // classification band (log2 units)
 constexpr double kMinY = -1021.0 * 256.0;        // weights stay normal doubles (>= 2^-1021)
-constexpr int kRun = 8;                          // tokens per lane in the pick's scan
 constexpr int kSlots = kWaves * kWaveCap;        // band entries per chunk (32)
 constexpr int kBufferDword3 = 0x00020000;        // raw buffer descriptor word 3 (gfx9 family)
 
@@ -176,6 +178,47 @@ template <> struct Vec<SV_F32> {
     }
 };
 
+// kR consecutive logits of one row, loaded by one lane in as few loads as
+// their alignment allows (aligned(): to their size, at most 16 bytes).
+template <int DT, int kR>
+struct Run {
+    using E = typename Vec<DT>::E;
+    static constexpr int kBytes = kR * static_cast<int>(sizeof(E));
+    static constexpr int kWords = kBytes / 4;
+    static constexpr uintptr_t kAlign = kBytes < 16 ? kBytes : 16;
+    __device__ static __forceinline__ bool aligned(const E* ptr) {
+        return (reinterpret_cast<uintptr_t>(ptr) & (kAlign - 1)) == 0;
+    }
+    __device__ static __forceinline__ void load(const E* ptr, float* z) {
+        uint32_t w[kWords];
+        if constexpr (kBytes >= 16) {
+#pragma unroll
+            for (int i = 0; i < kBytes / 16; ++i) {
+                const u32x4 v = reinterpret_cast<const u32x4*>(ptr)[i];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) w[4 * i + j] = v[j];
+            }
+        } else if constexpr (kBytes == 8) {
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 v = *reinterpret_cast<const u32x2*>(ptr);
+            w[0] = v[0];
+            w[1] = v[1];
+        } else {
+            static_assert(kBytes == 4, "run size");
+            w[0] = *reinterpret_cast<const uint32_t*>(ptr);
+        }
+#pragma unroll
+        for (int i = 0; i < kWords; ++i) {
+            if constexpr (DT == SV_BF16) {
+                z[2 * i] = __uint_as_float(w[i] << 16);
+                z[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+            } else {
+                z[i] = __uint_as_float(w[i]);
+            }
+        }
+    }
+};
+
 // The one or two rows a draw reads, and Y = 256 (z - m) log2(e) / T as one fma.
 template <int DT>
 struct Rows {
@@ -207,16 +250,17 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int32_t
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
-// Calls f(z_t, z_d) for this thread's tokens of [v0, v1), in the order
-// lane-strided 16-byte vectors, then single tokens for a ragged tail.  When
-// both rows start 16-byte aligned the vectors come from raw buffer loads
-// against descriptors that span exactly the chunk's vectors, one iteration
-// ahead of use (a load past the end returns zeros and touches no memory);
-// otherwise every token is loaded on its own.
+// Calls f(z_t, z_d) for this lane's tokens of [v0, v1), run by one whole
+// wave: lane-strided 16-byte vectors, then single tokens for a ragged tail.
+// When both rows are 16-byte aligned at v0 the vectors come from raw buffer
+// loads against descriptors that span exactly the range's vectors, one
+// iteration ahead of use (a load past the end returns zeros and touches no
+// memory); otherwise every token is loaded on its own.
 template <int DT, bool kResid, class F>
-__device__ __forceinline__ void for_chunk(const Rows<DT>& rows, int64_t v0, int64_t v1, F&& f) {
+__device__ __forceinline__ void for_range(const Rows<DT>& rows, int64_t v0, int64_t v1, F&& f) {
     using E = typename Vec<DT>::E;
     constexpr int N = Vec<DT>::N;
+    const int lane = threadIdx.x & 63;
     const bool vec = (reinterpret_cast<uintptr_t>(rows.t + v0) & 15u) == 0 &&
                      (!kResid || (reinterpret_cast<uintptr_t>(rows.d + v0) & 15u) == 0);
     int64_t vs = v0;
@@ -227,12 +271,12 @@ __device__ __forceinline__ void for_chunk(const Rows<DT>& rows, int64_t v0, int6
         const __amdgpu_buffer_rsrc_t rd = kResid
             ? __builtin_amdgcn_make_buffer_rsrc(const_cast<E*>(rows.d + v0), 0, nvec * 16, kBufferDword3)
             : rt;
-        int32_t j = threadIdx.x;
+        int32_t j = lane;
         u32x4 a = buffer_load16(rt, j * 16);
         u32x4 bb = kResid ? buffer_load16(rd, j * 16) : a;
-        for (; j < nvec; j += kThreads) {
-            const u32x4 an = buffer_load16(rt, (j + kThreads) * 16);
-            const u32x4 bn = kResid ? buffer_load16(rd, (j + kThreads) * 16) : an;
+        for (; j < nvec; j += 64) {
+            const u32x4 an = buffer_load16(rt, (j + 64) * 16);
+            const u32x4 bn = kResid ? buffer_load16(rd, (j + 64) * 16) : an;
             float xt[N], xd[N];
             Vec<DT>::unpack(a, xt);
             if (kResid) Vec<DT>::unpack(bb, xd);
@@ -247,35 +291,40 @@ __device__ __forceinline__ void for_chunk(const Rows<DT>& rows, int64_t v0, int6
         }
         vs = v0 + static_cast<int64_t>(nvec) * N;
     }
-    for (int64_t v = vs + threadIdx.x; v < v1; v += kThreads)
+    for (int64_t v = vs + lane; v < v1; v += 64)
         f(rows.zt(v), kResid ? rows.zd(v) : 0.f);
 }
 
-// Sums of four doubles over a 256-thread workgroup (valid in every thread).
-__device__ __forceinline__ void block_sum4(double& a, double& b, double& c, double& d,
-                                           double (*lds)[4]) {
+// Sums of four doubles over one wave (valid in every lane; a fixed
+// butterfly, so every lane holds the same bits).
+__device__ __forceinline__ void wave_sum4(double& a, double& b, double& c, double& d) {
     for (int off = 32; off > 0; off >>= 1) {
         a += __shfl_xor(a, off, 64);
         b += __shfl_xor(b, off, 64);
         c += __shfl_xor(c, off, 64);
         d += __shfl_xor(d, off, 64);
     }
-    const int wave = threadIdx.x >> 6;
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0 && wave < kWaves) {   // (waves past kWaves only take part in the barriers)
-        lds[wave][0] = a; lds[wave][1] = b; lds[wave][2] = c; lds[wave][3] = d;
-    }
-    __syncthreads();
-    a = b = c = d = 0.0;
-    for (int w = 0; w < kWaves; ++w) { a += lds[w][0]; b += lds[w][1]; c += lds[w][2]; d += lds[w][3]; }
 }
-
 
 }  // namespace drawpass
 
-// Workgroup scratch of one draw chunk (256 threads).
+// Sub-chunk w (0 <= w < kWaves) of chunk c: the chunk cut into kWaves
+// contiguous pieces of a whole number of 16-byte vectors (the last one
+// shorter, possibly empty), one per wave of the chunk's workgroup.  The
+// pick keeps the masses of sub-chunks, so its final scan covers a quarter
+// of a chunk.  [*s0, *s1) in token ids.
+template <int DT>
+__device__ __forceinline__ void sub_range(const Problem& p, const Plan& plan, int64_t c, int w, int64_t* s0,
+                                          int64_t* s1) {
+    constexpr int64_t N = drawpass::Vec<DT>::N;
+    const int64_t q = ((plan.chunk_len + kWaves - 1) / kWaves + N - 1) / N * N;
+    const int64_t c0 = c * plan.chunk_len, c1 = min(p.V, c0 + plan.chunk_len);
+    *s0 = min(c1, c0 + w * q);
+    *s1 = min(c1, c0 + (w + 1) * q);
+}
+
+// Workgroup scratch of one draw chunk (256 threads): each wave's band list.
 struct DrawLds {
-    double red4[kWaves][4];
     double wlist[kWaves][kWaveCap][2];
     int32_t wcount[kWaves];
 };
@@ -286,31 +335,33 @@ __device__ __forceinline__ void load_exp2_table(drawpass::TabEntry* tbl, int nth
     drawpass::load_table(tbl, nthreads);
 }
 
-// Chunk c of the draw of sequence b (256 threads): accumulates the chunk's
-// fp64 sums and band lists (see the file comment).  `task` is the
-// sequence's DrawTask (kind != kNone).  kCo: the results go to the pick in
-// another workgroup of the same launch.  NT: the workgroup size; threads
-// past the first 256 do no work but take part in the barriers, so the
+// Chunk c of the draw of sequence b (256 threads): wave w accumulates the
+// fp64 sums and band list of sub-chunk w (see the file comment).  `task` is
+// the sequence's DrawTask (kind != kNone).  kCo: the results go to the pick
+// in another workgroup of the same launch.  NT: the workgroup size; threads
+// past the first 256 do no work but take part in the barrier, so the
 // results are those of a 256-thread workgroup, bit for bit.
 template <int DT, bool kCo, int NT = kThreads>
 __device__ __forceinline__ void draw_chunk(const Problem& p, const Plan& plan, const DrawTask& task,
                                            int32_t b, int32_t c, const drawpass::TabEntry* tbl,
                                            DrawLds& lds) {
     using namespace drawpass;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t w = static_cast<int64_t>(b) * plan.nchunk + c;
+    // (the wave index through readfirstlane: the compiler then keeps the
+    // sub-chunk's bounds and buffer descriptors in scalar registers)
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t sub = (static_cast<int64_t>(b) * plan.nchunk + c) * kWaves;   // sub-chunk 0 of the chunk
     const bool resid_task = (task.kind == kResidual);
     const Rows<DT> rows = rows_of<DT>(p, task, tbl);
+    const bool active = NT == kThreads || threadIdx.x < kThreads;
+    int64_t v0 = 0, v1 = 0;
+    if (active) sub_range<DT>(p, plan, c, wave, &v0, &v1);
 
-    const int64_t v0 = static_cast<int64_t>(c) * plan.chunk_len;
-    const int64_t v1 = min(p.V, v0 + plan.chunk_len);
     double sp = 0.0, sq = 0.0, a = 0.0, bq = 0.0;
     int32_t nband = 0;                         // uniform over the lanes still active
-    const bool active = NT == kThreads || threadIdx.x < kThreads;
     if (!active) {
     } else if (resid_task) {
         const double th_hi = 256.0 * (task.theta + kBand), th_lo = 256.0 * (task.theta - kBand);
-        for_chunk<DT, true>(rows, v0, v1, [&](float zt, float zd) {
+        for_range<DT, true>(rows, v0, v1, [&](float zt, float zd) {
             const double yt = rows.Yt(zt), yd = rows.Yd(zd);
             const double wt = exp2_256(yt, tbl), wd = exp2_256(yd, tbl);
             sp += wt;
@@ -332,23 +383,26 @@ __device__ __forceinline__ void draw_chunk(const Problem& p, const Plan& plan, c
             }
         });
     } else {
-        for_chunk<DT, false>(rows, v0, v1, [&](float zt, float) { sp += rows.wt(zt); });
+        for_range<DT, false>(rows, v0, v1, [&](float zt, float) { sp += rows.wt(zt); });
     }
-    if (lane == 0 && wave < kWaves) lds.wcount[wave] = nband;  // lane 0 was active whenever any lane was
-    block_sum4(sp, sq, a, bq, lds.red4);
-    if (threadIdx.x == 0) {
-        ChunkSums* cs = plan.csum + w;
-        st_co<kCo>(&cs->sp, sp);
-        st_co<kCo>(&cs->sq, sq);
-        st_co<kCo>(&cs->a, a);
-        st_co<kCo>(&cs->b, bq);
+    if (active) {
+        wave_sum4(sp, sq, a, bq);
+        if (lane == 0) {                       // lane 0 was active whenever any lane was
+            lds.wcount[wave] = nband;
+            ChunkSums* cs = plan.csum + sub + wave;
+            st_co<kCo>(&cs->sp, sp);
+            st_co<kCo>(&cs->sq, sq);
+            st_co<kCo>(&cs->a, a);
+            st_co<kCo>(&cs->b, bq);
+            if (resid_task) st_co<kCo>(&plan.band_n[sub + wave], nband);
+        }
     }
     if (resid_task) {
-        if (threadIdx.x < kWaves) st_co<kCo>(&plan.band_n[w * kWaves + threadIdx.x], lds.wcount[threadIdx.x]);
+        __syncthreads();
         if (threadIdx.x < kSlots) {
             const int wv = threadIdx.x / kWaveCap, e = threadIdx.x % kWaveCap;
             if (e < lds.wcount[wv]) {
-                double* dst = plan.band_w + (w * kSlots + threadIdx.x) * 2;
+                double* dst = plan.band_w + (sub * kWaveCap + threadIdx.x) * 2;
                 st_co<kCo>(&dst[0], lds.wlist[wv][e][0]);
                 st_co<kCo>(&dst[1], lds.wlist[wv][e][1]);
             }
@@ -358,16 +412,17 @@ __device__ __forceinline__ void draw_chunk(const Problem& p, const Plan& plan, c
 
 // ---- the pick: one NT-thread workgroup per sequence -----------------------
 
-constexpr int kMaxPickChunks = 1024;          // chunk masses held in LDS by the pick
+constexpr int kMaxPickSubs = kMaxChunks * kWaves;   // sub-chunk masses held in LDS by the pick
+constexpr int64_t kPiece = 2048;                     // tokens per step of the pick's final scan
 
-template <int NT, int MAXC = kMaxPickChunks>
+template <int NT, int MAXS = kMaxPickSubs>
 struct PickLds {
     static constexpr int kW = NT / 64;
     double red2[kW][2];
     double scan[kW];
     int32_t ldsi[2 * kW];
-    double mass[MAXC];
-    double spc[MAXC];
+    double mass[MAXS];
+    double spc[MAXS];
     double base, target, Z;
     int32_t chunk, resid, rescan;
 };
@@ -482,65 +537,59 @@ __device__ __forceinline__ void find_chunk(const double* m, int32_t n, double u,
 
 }  // namespace drawpass
 
-// The loads of a pick that need only the sequence, for chunk threadIdx.x:
-// its sums and band counts (so they can be issued before the task is known;
-// for a bonus draw all but sp are unused).
+// The loads of a pick that need only the sequence, for sub-chunk
+// threadIdx.x: its sums and band count (so they can be issued before the
+// task is known; for a bonus draw all but sp are unused).
 struct PickPrefetch {
     double sp = 0.0, sq = 0.0, a = 0.0, b = 0.0;
-    int32_t cnt[kWaves] = {};
+    int32_t cnt = 0;
 };
 template <bool kCo>
 __device__ __forceinline__ PickPrefetch pick_prefetch(const Plan& plan, int32_t b) {
     PickPrefetch f;
     const int32_t j = threadIdx.x;
-    if (j < plan.nchunk) {
-        const int64_t cj = static_cast<int64_t>(b) * plan.nchunk + j;
-        const ChunkSums* c = plan.csum + cj;
+    if (j < plan.nchunk * kWaves) {
+        const int64_t sj = static_cast<int64_t>(b) * plan.nchunk * kWaves + j;
+        const ChunkSums* c = plan.csum + sj;
         f.sp = ld_co<kCo>(&c->sp);
         f.sq = ld_co<kCo>(&c->sq);
         f.a = ld_co<kCo>(&c->a);
         f.b = ld_co<kCo>(&c->b);
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) f.cnt[w] = ld_co<kCo>(&plan.band_n[cj * kWaves + w]);
+        f.cnt = ld_co<kCo>(&plan.band_n[sj]);
     }
     return f;
 }
 
-// The pick of sequence b (NT threads, NT a multiple of 256): from the chunk
-// sums of every chunk of its draw, the emitted token.  `task` is the
-// sequence's DrawTask (kind != kNone); plan.nchunk <= MAXC; pf is
-// pick_prefetch<kCo>(plan, b).  kCo: the chunk sums come from other
-// workgroups of the same launch.
-template <int DT, int NT, bool kCo, int MAXC = kMaxPickChunks>
+// The pick of sequence b (NT threads, NT a multiple of 256): from the sums
+// of every sub-chunk of its draw, the emitted token.  `task` is the
+// sequence's DrawTask (kind != kNone); plan.nchunk * kWaves <= MAXS; pf is
+// pick_prefetch<kCo>(plan, b).  kCo: the sums come from other workgroups of
+// the same launch.
+template <int DT, int NT, bool kCo, int MAXS = kMaxPickSubs>
 __device__ __forceinline__ void pick_sequence(const Problem& p, const Plan& plan, const DrawTask& task,
                                               int32_t b, const drawpass::TabEntry* tbl,
-                                              PickLds<NT, MAXC>& L, const PickPrefetch& pf) {
+                                              PickLds<NT, MAXS>& L, const PickPrefetch& pf) {
     using namespace drawpass;
     static_assert(NT % 256 == 0 && NT <= 1024, "pick workgroup size");
-    constexpr int N = Vec<DT>::N;
-    constexpr int64_t kPiece = NT * kRun;    // tokens per scan step
+    constexpr int kRun = kPiece / NT;        // tokens per lane per scan step
     const int tid = threadIdx.x, wave = tid >> 6;
     const bool resid_task = (task.kind == kResidual);
     const Rows<DT> rows = rows_of<DT>(p, task, tbl);
-    const int32_t nchunk = plan.nchunk;
-    const int64_t cb = static_cast<int64_t>(b) * nchunk;
-    const ChunkSums* cs = plan.csum + cb;
+    const int32_t nsub = plan.nchunk * kWaves;
+    const int64_t sb = static_cast<int64_t>(b) * nsub;
+    const ChunkSums* cs = plan.csum + sb;
     if (tid == 0) L.rescan = 0;
 
-    // Chunk tid's sums and band counts come prefetched (a row with more
-    // chunks than the workgroup has threads loads the others' here and in
-    // the loop below).
+    // Sub-chunk tid's sums and band count come prefetched (a row with more
+    // sub-chunks than the workgroup has threads loads the others' here and
+    // in the loop below).
     double Sp = 0.0, Sq = 0.0;
-    const double ca = pf.a, cbq = pf.b;
-    int32_t cnt0[kWaves];
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) cnt0[w] = pf.cnt[w];
-    if (tid < nchunk) {
+    if (tid < nsub) {
         Sp = pf.sp;
         Sq = pf.sq;
         L.spc[tid] = pf.sp;
     }
-    for (int32_t j = tid + NT; j < nchunk; j += NT) {
+    for (int32_t j = tid + NT; j < nsub; j += NT) {
         const double xsp = ld_co<kCo>(&cs[j].sp);
         Sp += xsp;
         Sq += ld_co<kCo>(&cs[j].sq);
@@ -550,49 +599,41 @@ __device__ __forceinline__ void pick_sequence(const Problem& p, const Plan& plan
     const double iSp = 1.0 / Sp, iSq = resid_task ? 1.0 / Sq : 0.0;
 
     if (resid_task) {
-        // Chunk j's residual mass, by thread j: A_j / S_p - B_j / S_q plus
+        // Sub-chunk j's residual mass, by thread j: A_j / S_p - B_j / S_q plus
         // max(0, w_t / S_p - w_d / S_q) of its listed band tokens in list
-        // order; NaN marks a chunk whose lists overflowed (rescanned below).
-        for (int32_t j = tid; j < nchunk; j += NT) {
-            double a = ca, bq = cbq;
-            int32_t cnt[kWaves];
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) cnt[w] = cnt0[w];
+        // order; NaN marks a sub-chunk whose list overflowed (rescanned below).
+        for (int32_t j = tid; j < nsub; j += NT) {
+            double a = pf.a, bq = pf.b;
+            int32_t cnt = pf.cnt;
             if (j != tid) {
                 a = ld_co<kCo>(&cs[j].a);
                 bq = ld_co<kCo>(&cs[j].b);
-#pragma unroll
-                for (int w = 0; w < kWaves; ++w) cnt[w] = ld_co<kCo>(&plan.band_n[(cb + j) * kWaves + w]);
+                cnt = ld_co<kCo>(&plan.band_n[sb + j]);
             }
             double m = a * iSp - bq * iSq;
-            bool over = false;
+            const int32_t nw = min(cnt, kWaveCap);
+            if (nw > 0) {
+                const double* pw = plan.band_w + (sb + j) * kWaveCap * 2;
+                double wt[kWaveCap], wd[kWaveCap];
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                over = over || cnt[w] > kWaveCap;
-                const int32_t nw = min(cnt[w], kWaveCap);
-                if (nw > 0) {
-                    const double* pw = plan.band_w + ((cb + j) * kSlots + w * kWaveCap) * 2;
-                    double wt[kWaveCap], wd[kWaveCap];
-#pragma unroll
-                    for (int e = 0; e < kWaveCap; ++e) {
-                        wt[e] = e < nw ? ld_co<kCo>(&pw[2 * e]) : 0.0;
-                        wd[e] = e < nw ? ld_co<kCo>(&pw[2 * e + 1]) : 0.0;
-                    }
-#pragma unroll
-                    for (int e = 0; e < kWaveCap; ++e)
-                        if (e < nw) m += fmax(0.0, wt[e] * iSp - wd[e] * iSq);
+                for (int e = 0; e < kWaveCap; ++e) {
+                    wt[e] = e < nw ? ld_co<kCo>(&pw[2 * e]) : 0.0;
+                    wd[e] = e < nw ? ld_co<kCo>(&pw[2 * e + 1]) : 0.0;
                 }
+#pragma unroll
+                for (int e = 0; e < kWaveCap; ++e)
+                    if (e < nw) m += fmax(0.0, wt[e] * iSp - wd[e] * iSq);
             }
-            L.mass[j] = over ? NAN : m;
-            if (over) L.rescan = 1;            // benign race: every writer stores 1
+            L.mass[j] = cnt > kWaveCap ? NAN : m;
+            if (cnt > kWaveCap) L.rescan = 1;  // benign race: every writer stores 1
         }
         __syncthreads();
         if (L.rescan) {
-            // chunks whose band lists overflowed: exact rescan (rare)
-            for (int32_t j = 0; j < nchunk; ++j) {
+            // sub-chunks whose band list overflowed: exact rescan (rare)
+            for (int32_t j = 0; j < nsub; ++j) {
                 if (!isnan(L.mass[j])) continue;
-                const int64_t u0 = static_cast<int64_t>(j) * plan.chunk_len;
-                const int64_t u1 = min(p.V, u0 + plan.chunk_len);
+                int64_t u0, u1;
+                sub_range<DT>(p, plan, j / kWaves, j % kWaves, &u0, &u1);
                 double m = 0.0, unused = 0.0;
                 for (int64_t v = u0 + tid; v < u1; v += NT)
                     m += fmax(0.0, rows.wt(rows.zt(v)) * iSp - rows.wd(rows.zd(v)) * iSq);
@@ -607,10 +648,10 @@ __device__ __forceinline__ void pick_sequence(const Problem& p, const Plan& plan
         double Z = 0.0, base = 0.0;
         int32_t chunk = 0;
         if (resid) {
-            find_chunk(L.mass, nchunk, static_cast<double>(task.u), &Z, &chunk, &base);
+            find_chunk(L.mass, nsub, static_cast<double>(task.u), &Z, &chunk, &base);
             if (Z < kDegenerateZ) resid = false;   // draw from p_n instead
         }
-        if (!resid) find_chunk(L.spc, nchunk, static_cast<double>(task.u), &Z, &chunk, &base);
+        if (!resid) find_chunk(L.spc, nsub, static_cast<double>(task.u), &Z, &chunk, &base);
         if (tid == 0) {
             L.base = base;
             L.Z = Z;
@@ -623,25 +664,24 @@ __device__ __forceinline__ void pick_sequence(const Problem& p, const Plan& plan
     const bool resid = L.resid;
     const double target = L.target;
     double base = L.base;
-    const int64_t c0 = static_cast<int64_t>(L.chunk) * plan.chunk_len;
-    const int64_t c1 = min(p.V, c0 + plan.chunk_len);
+    int64_t c0, c1;
+    sub_range<DT>(p, plan, L.chunk / kWaves, L.chunk % kWaves, &c0, &c1);
 
-    // Scan the chunk in pieces of kPiece tokens: lane tid owns kRun
+    // Scan the sub-chunk in pieces of kPiece tokens: lane tid owns kRun
     // consecutive tokens of the piece, loaded together, masses kept in
     // registers.  The next piece's loads are issued before this piece's
     // arithmetic.
-    auto load_piece = [&](int64_t q0, float* zt, float* zd) {
+    auto load_piece = [&](int64_t q0, float (&zt)[kRun], float (&zd)[kRun]) {
         const int64_t q1 = min(c1, q0 + kPiece);
         const int64_t r0 = q0 + static_cast<int64_t>(tid) * kRun;
-        const bool vec = r0 + kRun <= q1 &&
-                         (reinterpret_cast<uintptr_t>(rows.t + r0) & 15u) == 0 &&
-                         (!resid || (reinterpret_cast<uintptr_t>(rows.d + r0) & 15u) == 0);
-        if (vec) {
-#pragma unroll
-            for (int i = 0; i < kRun / N; ++i) {
-                Vec<DT>::unpack(reinterpret_cast<const u32x4*>(rows.t + r0)[i], zt + i * N);
-                if (resid) Vec<DT>::unpack(reinterpret_cast<const u32x4*>(rows.d + r0)[i], zd + i * N);
-            }
+        // (fp32 runs shorter than 16 bytes take the per-token path: two
+        // dword loads cost no more, and the two-path form put zt/zd in
+        // scratch memory)
+        constexpr bool kVec = DT == SV_BF16 || kRun * 4 >= 16;
+        if (kVec && r0 + kRun <= q1 && Run<DT, kRun>::aligned(rows.t + r0) &&
+            (!resid || Run<DT, kRun>::aligned(rows.d + r0))) {
+            Run<DT, kRun>::load(rows.t + r0, zt);
+            if (resid) Run<DT, kRun>::load(rows.d + r0, zd);
         } else {
 #pragma unroll
             for (int i = 0; i < kRun; ++i) {

@@ -57,7 +57,7 @@ struct FusedLds {
     union {
         RowLds row;
         DrawLds draw;
-        PickLds<kThreads, kFusedMaxChunks> pick;
+        PickLds<kThreads, kFusedMaxChunks * kWaves> pick;
     } u;
     int32_t scan[kWaves];
     uint32_t item;
@@ -107,8 +107,8 @@ __device__ __noinline__ void do_chunk(const Problem& p, const Plan& plan, const 
 }
 template <int DT>
 __device__ __noinline__ void do_pick(const Problem& p, const Plan& plan, const DrawTask& task, int32_t b,
-                                     const drawpass::TabEntry* tbl, PickLds<kThreads, kFusedMaxChunks>& lds) {
-    pick_sequence<DT, kThreads, true, kFusedMaxChunks>(p, plan, task, b, tbl, lds, pick_prefetch<true>(plan, b));
+                                     const drawpass::TabEntry* tbl, PickLds<kThreads, kFusedMaxChunks * kWaves>& lds) {
+    pick_sequence<DT, kThreads, true, kFusedMaxChunks * kWaves>(p, plan, task, b, tbl, lds, pick_prefetch<true>(plan, b));
 }
 
 template <int DT>

@@ -22,7 +22,6 @@ constexpr int64_t kDefaultChunkElems = 8192;  // draw chunk length before roundi
 // kAutoLeadBytes, and one full pass otherwise.
 constexpr int32_t kAutoLead = -1;
 constexpr int64_t kAutoLeadBytes = 512ll << 20;
-constexpr int64_t kMaxChunks = 1024;          // draw chunks per row (the pick keeps them in LDS)
 constexpr int kMaxDevices = 64;
 constexpr int kNumKernels = 11;
 enum { kKRowStats, kKAccept, kKDrawSums, kKDrawPick, kKFusedReset, kKFused, kKRowLead, kKAcceptLead,
@@ -140,7 +139,7 @@ bool make_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dtype, int64_
     g.off_task = off;
     off = align256(off + sizeof(DrawTask) * static_cast<size_t>(B));
     g.off_csum = off;
-    off = align256(off + sizeof(ChunkSums) * static_cast<size_t>(B) * g.nchunk);
+    off = align256(off + sizeof(ChunkSums) * kWaves * static_cast<size_t>(B) * g.nchunk);
     g.off_band_n = off;
     off = align256(off + sizeof(int32_t) * kWaves * static_cast<size_t>(B) * g.nchunk);
     g.off_band_w = off;

@@ -38,6 +38,7 @@ constexpr int kThreads = 256;          // workgroup size of every kernel (4 x wa
 constexpr int kWaves = kThreads / 64;
 constexpr int kKMax = SV_K_MAX;
 constexpr int kWaveCap = 8;            // band tokens listed per wave of a draw chunk
+constexpr int kMaxChunks = 256;        // draw chunks per row (the pick keeps a mass per sub-chunk in LDS)
 // Row pass: the longest segment, so that each lane's fp32 partial sums
 // take at most 40 vectors (16 bytes: 8 bf16 or 4 fp32 logits) each.
 __host__ __device__ constexpr int64_t max_seg_elems(int32_t dtype) {
@@ -83,7 +84,7 @@ struct DrawTask {
     double theta;      // log2(S_p / S_q) from the row pass: p_v > q_v iff d_v > theta
 };
 
-// Per-chunk partial sums of the draw (fp64).
+// Partial sums of the draw over one sub-chunk (fp64).
 struct ChunkSums {
     double sp;   // sum of w_t = exp((z_t - m_t)/T) over the chunk
     double sq;   // sum of w_d over the chunk (residual)
@@ -139,8 +140,8 @@ struct Plan {
     int64_t chunk_len;   // elements per chunk (multiple of 8)
     SegStat* seg;        // [(2 * total + B) * nseg]; target rows first
     DrawTask* task;      // [B]
-    ChunkSums* csum;     // [B * nchunk]
-    int32_t* band_n;     // [B * nchunk * kWaves]: band tokens seen per wave of a chunk
+    ChunkSums* csum;     // [B * nchunk * kWaves]: one per sub-chunk (wave) of each chunk
+    int32_t* band_n;     // [B * nchunk * kWaves]: band tokens seen per sub-chunk (wave) of a chunk
     double* band_w;      // [B * nchunk * kWaves * kWaveCap * 2]: their (w_t, w_d)
     float* xlogit;       // [2 * total + B]: logit of the drafted token of each row
     uint32_t* ctr;       // fused form only: kCtrHeader words, then rows_done[B], ready[B], chunks_done[B]
