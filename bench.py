@@ -218,7 +218,9 @@ def main():
     # the second round, the dominant launch, which streams the remaining rows
     # and every draw row.
     queued = "rest" in launched
-    if form == "fused":
+    if "sample_sums" in launched:                # the draft sampler: one read of each row
+        roof = ["sample_sums"]
+    elif form == "fused":
         roof = ["fused"]
     elif queued:
         roof = ["rest"]
@@ -290,7 +292,9 @@ def main():
         read_rows += extra
         min_rows += extra
         full_rows += extra
-    draw_rows = int(np.sum(np.where(sampling, np.where(n < k, 2, 1), 0)))
+    # (the draft sampler reads each row once: its sums pass re-reads a
+    # sub-chunk from cache, its pick one sub-chunk)
+    draw_rows = 0 if args.entry == "draft" else int(np.sum(np.where(sampling, np.where(n < k, 2, 1), 0)))
     row_bytes = w.V * elt
     k1_bytes = read_rows * row_bytes
     total_bytes = (read_rows + draw_rows) * row_bytes

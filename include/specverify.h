@@ -156,9 +156,11 @@ sv_status_t spec_verify_gathered(const void *target_logits, const void *draft_lo
  *   temperature fp32 [rows] (0 = greedy); uniforms fp32 [rows] in [0, 1).
  *   out_tokens int32 [rows]: x = min{t : sum_{v<=t} q_v > u} (the same fp64
  *     inverse CDF over ascending ids as the verify's draws), the lowest-id
- *     argmax at T = 0, -1 for an unusable temperature;
+ *     argmax at T = 0, -1 for an unusable temperature or a row whose maximum
+ *     is not finite;
  *   out_probs fp32 [rows] (may be NULL): q(x) (1 at T = 0, NaN on error) --
  *     the draft_probs of spec_verify_gathered.
+ * Two launches ("sample_sums", "sample_pick"), one read of each row.
  * Workspace as for spec_verify with B = rows and total_draft = 0. */
 sv_status_t spec_draft_sample(const void *logits, int32_t rows, int64_t V, sv_dtype_t dtype,
                               const float *temperature, const float *uniforms,
@@ -250,12 +252,12 @@ sv_status_t spec_stream_probe(const void *data, int64_t bytes, int64_t seg_bytes
  * exit row_lead, accept_lead, rest and draw_pick,
  * or in the gathered form row_lead, accept_lead, row_stats, accept,
  * row_draft, draw_sums and draw_pick; the fused form fused_reset and
- * fused); it returns the number
+ * fused; spec_draft_sample sample_sums and sample_pick); it returns the number
  * of kernels, or -1 if the probe is off, no call was recorded or a HIP call
  * failed.
  * spec_verify_timing returns SV_ERR_SHAPE for every < 1.  The probe uses
  * one device: turn it off and on again after switching devices. */
-#define SV_TIME_ALL 0x7FF
+#define SV_TIME_ALL 0x1FFF
 sv_status_t spec_verify_timing(int32_t kernels, int32_t every);
 int32_t spec_verify_kernel_times(float *ms, int32_t max_kernels);
 const char *spec_verify_kernel_name(int32_t i);

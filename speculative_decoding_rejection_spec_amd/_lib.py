@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 
 SV_F32, SV_BF16 = 0, 1
 SV_K_MAX = 63
-SV_TIME_ALL = 0x7FF
+SV_TIME_ALL = 0x1FFF
 SV_MODE_AUTO, SV_MODE_STAGED, SV_MODE_FUSED = 0, 1, 2
 SV_QUEUE_OVERLAP, SV_QUEUE_FINAL, SV_QUEUE_HANDOFF = 0, 1, 2
 SV_DRAW_AUTO, SV_DRAW_ONE, SV_DRAW_THREE = 0, 1, 2

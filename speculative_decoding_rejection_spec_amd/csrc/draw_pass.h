@@ -537,6 +537,106 @@ __device__ __forceinline__ void find_chunk(const double* m, int32_t n, double u,
 
 }  // namespace drawpass
 
+// The final step of a pick (every thread of the NT-thread workgroup): scans
+// sub-chunk L.chunk from the cumulative mass L.base for the first token whose
+// cumulative mass exceeds L.target, and writes it to out_tokens[out_slot]
+// (and its probability, mass / L.Z, to out_emit_prob[b]).  Masses are
+// max(0, w_t iSp - w_d iSq) for a residual draw, w_t otherwise.
+template <int DT, int NT, int MAXS>
+__device__ __forceinline__ void pick_scan(const Problem& p, const Plan& plan, const drawpass::Rows<DT>& rows,
+                                          bool resid, double iSp, double iSq, int64_t out_slot, int32_t b,
+                                          PickLds<NT, MAXS>& L) {
+    using namespace drawpass;
+    constexpr int kRun = kPiece / NT;        // tokens per lane per scan step
+    const int tid = threadIdx.x;
+    const double target = L.target;
+    double base = L.base;
+    int64_t c0, c1;
+    sub_range<DT>(p, plan, L.chunk / kWaves, L.chunk % kWaves, &c0, &c1);
+
+    // Scan the sub-chunk in pieces of kPiece tokens: lane tid owns kRun
+    // consecutive tokens of the piece, loaded together, masses kept in
+    // registers.  The next piece's loads are issued before this piece's
+    // arithmetic.
+    auto load_piece = [&](int64_t q0, float (&zt)[kRun], float (&zd)[kRun]) {
+        const int64_t q1 = min(c1, q0 + kPiece);
+        const int64_t r0 = q0 + static_cast<int64_t>(tid) * kRun;
+        // (fp32 runs shorter than 16 bytes take the per-token path: two
+        // dword loads cost no more, and the two-path form put zt/zd in
+        // scratch memory)
+        constexpr bool kVec = DT == SV_BF16 || kRun * 4 >= 16;
+        if (kVec && r0 + kRun <= q1 && Run<DT, kRun>::aligned(rows.t + r0) &&
+            (!resid || Run<DT, kRun>::aligned(rows.d + r0))) {
+            Run<DT, kRun>::load(rows.t + r0, zt);
+            if (resid) Run<DT, kRun>::load(rows.d + r0, zd);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kRun; ++i) {
+                const bool in = r0 + i < q1;
+                zt[i] = in ? rows.zt(r0 + i) : 0.f;
+                zd[i] = (in && resid) ? rows.zd(r0 + i) : 0.f;
+            }
+        }
+    };
+    int32_t pick = INT32_MAX, last_pos = -1, mine = INT32_MAX;
+    double mine_mass = 0.0;
+    float zt[kRun], zd[kRun];
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) zd[i] = 0.f;
+    load_piece(c0, zt, zd);
+    for (int64_t q0 = c0; q0 < c1 && pick == INT32_MAX; q0 += kPiece) {
+        const int64_t q1 = min(c1, q0 + kPiece);
+        const int64_t r0 = q0 + static_cast<int64_t>(tid) * kRun;
+        float nzt[kRun], nzd[kRun];
+#pragma unroll
+        for (int i = 0; i < kRun; ++i) { nzt[i] = 0.f; nzd[i] = 0.f; }
+        if (q1 < c1) load_piece(q1, nzt, nzd);
+        double m[kRun];
+        double local = 0.0;
+        int32_t lp = -1;
+#pragma unroll
+        for (int i = 0; i < kRun; ++i) {
+            const bool in = r0 + i < q1;
+            m[i] = !in ? 0.0
+                       : (resid ? fmax(0.0, rows.wt(zt[i]) * iSp - rows.wd(zd[i]) * iSq) : rows.wt(zt[i]));
+            local += m[i];
+            if (m[i] > 0.0) lp = static_cast<int32_t>(r0 + i);
+        }
+        double total;
+        double run = base + pick_scan_excl<NT>(local, &total, L.scan);
+        mine = INT32_MAX;
+#pragma unroll
+        for (int i = 0; i < kRun; ++i) {
+            run += m[i];
+            if (mine == INT32_MAX && run > target) { mine = static_cast<int32_t>(r0 + i); mine_mass = m[i]; }
+        }
+        int32_t first = mine;
+        pick_min_and_max<NT>(first, lp, L.ldsi);
+        pick = first;
+        last_pos = max(last_pos, lp);
+        base += total;
+#pragma unroll
+        for (int i = 0; i < kRun; ++i) { zt[i] = nzt[i]; zd[i] = nzd[i]; }
+    }
+    if (pick != INT32_MAX) {
+        // the thread that found the crossing holds the token's mass
+        if (mine == pick) {
+            p.out_tokens[out_slot] = pick;
+            if (p.out_emit_prob) p.out_emit_prob[b] = static_cast<float>(mine_mass / L.Z);
+        }
+    } else if (tid == 0) {
+        // rounding left no crossing inside the chunk: its last token with mass
+        pick = last_pos >= 0 ? last_pos : static_cast<int32_t>(c0);
+        p.out_tokens[out_slot] = pick;
+        if (p.out_emit_prob) {
+            // its probability under the distribution it was drawn from
+            const double wt = rows.wt(rows.zt(pick));
+            const double mass = resid ? fmax(0.0, wt * iSp - rows.wd(rows.zd(pick)) * iSq) : wt;
+            p.out_emit_prob[b] = static_cast<float>(mass / L.Z);
+        }
+    }
+}
+
 // The loads of a pick that need only the sequence, for sub-chunk
 // threadIdx.x: its sums and band count (so they can be issued before the
 // task is known; for a bonus draw all but sp are unused).
@@ -571,7 +671,6 @@ __device__ __forceinline__ void pick_sequence(const Problem& p, const Plan& plan
                                               PickLds<NT, MAXS>& L, const PickPrefetch& pf) {
     using namespace drawpass;
     static_assert(NT % 256 == 0 && NT <= 1024, "pick workgroup size");
-    constexpr int kRun = kPiece / NT;        // tokens per lane per scan step
     const int tid = threadIdx.x, wave = tid >> 6;
     const bool resid_task = (task.kind == kResidual);
     const Rows<DT> rows = rows_of<DT>(p, task, tbl);
@@ -661,93 +760,7 @@ __device__ __forceinline__ void pick_sequence(const Problem& p, const Plan& plan
         }
     }
     __syncthreads();
-    const bool resid = L.resid;
-    const double target = L.target;
-    double base = L.base;
-    int64_t c0, c1;
-    sub_range<DT>(p, plan, L.chunk / kWaves, L.chunk % kWaves, &c0, &c1);
-
-    // Scan the sub-chunk in pieces of kPiece tokens: lane tid owns kRun
-    // consecutive tokens of the piece, loaded together, masses kept in
-    // registers.  The next piece's loads are issued before this piece's
-    // arithmetic.
-    auto load_piece = [&](int64_t q0, float (&zt)[kRun], float (&zd)[kRun]) {
-        const int64_t q1 = min(c1, q0 + kPiece);
-        const int64_t r0 = q0 + static_cast<int64_t>(tid) * kRun;
-        // (fp32 runs shorter than 16 bytes take the per-token path: two
-        // dword loads cost no more, and the two-path form put zt/zd in
-        // scratch memory)
-        constexpr bool kVec = DT == SV_BF16 || kRun * 4 >= 16;
-        if (kVec && r0 + kRun <= q1 && Run<DT, kRun>::aligned(rows.t + r0) &&
-            (!resid || Run<DT, kRun>::aligned(rows.d + r0))) {
-            Run<DT, kRun>::load(rows.t + r0, zt);
-            if (resid) Run<DT, kRun>::load(rows.d + r0, zd);
-        } else {
-#pragma unroll
-            for (int i = 0; i < kRun; ++i) {
-                const bool in = r0 + i < q1;
-                zt[i] = in ? rows.zt(r0 + i) : 0.f;
-                zd[i] = (in && resid) ? rows.zd(r0 + i) : 0.f;
-            }
-        }
-    };
-    int32_t pick = INT32_MAX, last_pos = -1, mine = INT32_MAX;
-    double mine_mass = 0.0;
-    float zt[kRun], zd[kRun];
-#pragma unroll
-    for (int i = 0; i < kRun; ++i) zd[i] = 0.f;
-    load_piece(c0, zt, zd);
-    for (int64_t q0 = c0; q0 < c1 && pick == INT32_MAX; q0 += kPiece) {
-        const int64_t q1 = min(c1, q0 + kPiece);
-        const int64_t r0 = q0 + static_cast<int64_t>(tid) * kRun;
-        float nzt[kRun], nzd[kRun];
-#pragma unroll
-        for (int i = 0; i < kRun; ++i) { nzt[i] = 0.f; nzd[i] = 0.f; }
-        if (q1 < c1) load_piece(q1, nzt, nzd);
-        double m[kRun];
-        double local = 0.0;
-        int32_t lp = -1;
-#pragma unroll
-        for (int i = 0; i < kRun; ++i) {
-            const bool in = r0 + i < q1;
-            m[i] = !in ? 0.0
-                       : (resid ? fmax(0.0, rows.wt(zt[i]) * iSp - rows.wd(zd[i]) * iSq) : rows.wt(zt[i]));
-            local += m[i];
-            if (m[i] > 0.0) lp = static_cast<int32_t>(r0 + i);
-        }
-        double total;
-        double run = base + pick_scan_excl<NT>(local, &total, L.scan);
-        mine = INT32_MAX;
-#pragma unroll
-        for (int i = 0; i < kRun; ++i) {
-            run += m[i];
-            if (mine == INT32_MAX && run > target) { mine = static_cast<int32_t>(r0 + i); mine_mass = m[i]; }
-        }
-        int32_t first = mine;
-        pick_min_and_max<NT>(first, lp, L.ldsi);
-        pick = first;
-        last_pos = max(last_pos, lp);
-        base += total;
-#pragma unroll
-        for (int i = 0; i < kRun; ++i) { zt[i] = nzt[i]; zd[i] = nzd[i]; }
-    }
-    if (pick != INT32_MAX) {
-        // the thread that found the crossing holds the token's mass
-        if (mine == pick) {
-            p.out_tokens[task.out_slot] = pick;
-            if (p.out_emit_prob) p.out_emit_prob[b] = static_cast<float>(mine_mass / L.Z);
-        }
-    } else if (tid == 0) {
-        // rounding left no crossing inside the chunk: its last token with mass
-        pick = last_pos >= 0 ? last_pos : static_cast<int32_t>(c0);
-        p.out_tokens[task.out_slot] = pick;
-        if (p.out_emit_prob) {
-            // its probability under the distribution it was drawn from
-            const double wt = rows.wt(rows.zt(pick));
-            const double mass = resid ? fmax(0.0, wt * iSp - rows.wd(rows.zd(pick)) * iSq) : wt;
-            p.out_emit_prob[b] = static_cast<float>(mass / L.Z);
-        }
-    }
+    pick_scan<DT, NT, MAXS>(p, plan, rows, L.resid, iSp, iSq, task.out_slot, b, L);
 }
 
 }  // namespace sv

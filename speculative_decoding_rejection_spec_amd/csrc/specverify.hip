@@ -23,13 +23,14 @@ constexpr int64_t kDefaultChunkElems = 8192;  // draw chunk length before roundi
 constexpr int32_t kAutoLead = -1;
 constexpr int64_t kAutoLeadBytes = 512ll << 20;
 constexpr int kMaxDevices = 64;
-constexpr int kNumKernels = 11;
+constexpr int kNumKernels = 13;
 enum { kKRowStats, kKAccept, kKDrawSums, kKDrawPick, kKFusedReset, kKFused, kKRowLead, kKAcceptLead,
-       kKRowDraft, kKRest, kKDrawAll };
+       kKRowDraft, kKRest, kKDrawAll, kKSampleSums, kKSamplePick };
 
-const char* const kKernelNames[kNumKernels] = {"row_stats", "accept",      "draw_sums", "draw_pick",
-                                               "fused_reset", "fused",     "row_lead",  "accept_lead",
-                                               "row_draft", "rest",        "draw_all"};
+const char* const kKernelNames[kNumKernels] = {"row_stats", "accept",      "draw_sums",   "draw_pick",
+                                               "fused_reset", "fused",     "row_lead",    "accept_lead",
+                                               "row_draft", "rest",        "draw_all",    "sample_sums",
+                                               "sample_pick"};
 
 std::mutex g_mutex;
 int64_t g_seg_elems = 0;                     // 0: automatic (auto_lengths)
@@ -218,7 +219,10 @@ sv_status_t owned_workspace(size_t bytes, void** out) {
     return SV_OK;
 }
 
-sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// sample: the drafter's sampling step (spec_draft_sample), k = 0 for every
+// row: two launches of its own (sample.hip) instead of the verify's.
+sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                bool sample = false) {
     if (p.B == 0) return SV_OK;
     std::lock_guard<std::mutex> lock(g_mutex);
     Geometry g;
@@ -269,7 +273,7 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     // fused.hip), so it runs only when asked for.
     // The gathered form reads draft rows after the accept scans, which only
     // the staged form does.
-    const bool fused = g_mode == SV_MODE_FUSED && !p.draft_probs;
+    const bool fused = g_mode == SV_MODE_FUSED && !p.draft_probs && !sample;
     if (fused && !fused_fits) return SV_ERR_SHAPE;
     plan.lead = fused ? 0 : effective_lead(p.B, p.total, p.V, static_cast<sv_dtype_t>(p.dtype));
     if (device_cus(&plan.cus) != hipSuccess) return SV_ERR_HIP;
@@ -332,7 +336,10 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
         return true;
     };
     bool ok;
-    if (fused) {
+    if (sample) {
+        ok = launch(kKSampleSums, [&] { return launch_sample_sums(pr, plan, stream); }) &&
+             launch(kKSamplePick, [&] { return launch_sample_pick(pr, plan, stream); });
+    } else if (fused) {
         ok = launch(kKFusedReset, [&] { return launch_fused_reset(pr, plan, stream); }) &&
              launch(kKFused, [&] { return launch_fused(pr, plan, f, stream); });
     } else {
@@ -517,7 +524,7 @@ sv_status_t spec_draft_sample(const void* logits, int32_t rows, int64_t V, sv_dt
     p.B = rows;
     p.k_uniform = 0;
     p.dtype = dtype;
-    return run(p, workspace, workspace_bytes, stream);
+    return run(p, workspace, workspace_bytes, stream, /*sample=*/true);
 }
 
 sv_status_t spec_commit(const int32_t* out_tokens, const int32_t* out_n_accepted, const int32_t* offsets,

@@ -192,6 +192,8 @@ hipError_t launch_accept_lead(const Problem& p, const Plan& plan, hipStream_t s)
 hipError_t launch_draw_sums(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_draw_pick(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_draw_all(const Problem& p, const Plan& plan, hipStream_t s);
+hipError_t launch_sample_sums(const Problem& p, const Plan& plan, hipStream_t s);
+hipError_t launch_sample_pick(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_fused_reset(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_fused(const Problem& p, const Plan& plan, const Fused& f, hipStream_t s);
 hipError_t fused_grid(int32_t dtype, int32_t* blocks);   // resident workgroups on this device

@@ -109,6 +109,30 @@ def test_draft_sample_masked_vocabulary(sv, cuda, dtype):
     assert np.all(np.isfinite(z[np.arange(rows), tok]))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_draft_sample_nonfinite_rows(sv, cuda, dtype):
+    """A row whose maximum is not finite (+inf, or every entry -inf) gives
+    -1 and NaN, as a data error does in the verify (reading R26); the other
+    rows are unaffected."""
+    V, rows = 20000, 12
+    g = np.random.default_rng(59)
+    z = (g.standard_normal((rows, V)) * 2).astype(np.float32)
+    z[1, 777] = np.inf
+    z[4] = -np.inf
+    z[7, 19999] = np.inf                            # in the row's last sub-chunk
+    z[5] = -np.inf                                  # a greedy row with no finite logit
+    T = np.array([1.0, 1.0, 0.0, 0.7, 1.0, 0.0, 1.0, 0.0, 1.0, 1.0, 0.7, 1.0], np.float32)
+    stored = wl.bf16_round(z) if dtype == "bf16" else z
+    u = (g.integers(0, 1 << 24, size=rows) / float(1 << 24)).astype(np.float32)
+    tok, prob = run_sample(sv, stored, T, u, cuda)
+    bad = [1, 4, 5, 7]
+    assert np.all(tok[bad] == -1) and np.all(np.isnan(prob[bad]))
+    good = [r for r in range(rows) if r not in bad]
+    ref = oracle.draft_sample(stored[good], T[good], u[good])
+    ok = (ref["flags"] & oracle.FLAG_B) == 0
+    assert np.array_equal(tok[good][ok], ref["tokens"][ok])
+
+
 def test_draft_sample_zipf_rows(sv, cuda):
     """Zipf-shaped rows like the workloads' target logits, bf16, V = 128256."""
     w = wl.make_workload("c3", trial=5, B=96)
