@@ -5,12 +5,12 @@
 // each row:
 //
 //   sample_sums (grid rows x chunks, 256 threads): wave w of a chunk's
-//     workgroup covers sub-chunk w.  Sampling rows: its largest logit z_max,
-//     the reference Y_s = 256 ceil(z_max log2(e) / T) (a whole number of
-//     octaves, so rescaling between references is exact), and the fp64 sum
-//     of 2^((256 z log2(e) / T - Y_s) / 256) over the sub-chunk (a second
-//     read of the sub-chunk, from cache).  Greedy rows: its largest logit
-//     and the lowest id holding it.
+//     workgroup covers sub-chunk w.  Sampling rows: its largest logit, a
+//     reference Y_s that is a whole number of octaves (256 per octave in the
+//     draw's Y = 256 z log2(e) / T units; rescaling between such references
+//     is exact) at most 32 octaves below the largest Y, and the fp64 sum of
+//     2^((Y - Y_s) / 256) over the sub-chunk, in one read.  Greedy rows: its
+//     largest logit and the lowest id holding it.
 //   sample_pick (one workgroup per row): the row's maximum over the
 //     sub-chunks (a non-finite one is a data error, as in the verify), the
 //     common reference Y_0 = max Y_s, the sub-chunk masses rescaled to it,
@@ -63,20 +63,36 @@ __global__ __launch_bounds__(kThreads) void sample_sums_kernel(Problem p, Plan p
     load_exp2_table(tbl, kThreads);
     __syncthreads();
     const double C = 256.0 * kLog2e / static_cast<double>(T);
-    Rows<DT> rows{row, row, C, 0.0, 0.0, tbl};
+    const Rows<DT> rows{row, row, C, 0.0, 0.0, tbl};
+    // One read: each lane sums its weights relative to its own reference R
+    // (a multiple of 256 in Y units), raised -- with an exact rescale of the
+    // sum -- only when a logit exceeds it by more than kSlackY; the lanes'
+    // sums are then rescaled to the wave's largest reference.
+    constexpr double kSlackY = 256.0 * 32.0;
     float mx = -INFINITY;
-    for_range<DT, false>(rows, s0, s1, [&](float z, float) { mx = fmaxf(mx, z); });
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-    double s = 0.0, Y = -INFINITY;
-    if (fabsf(mx) <= 3.4e38f) {                           // finite: else the pick reports the row
-        Y = 256.0 * ceil(static_cast<double>(mx) * (C / 256.0));
-        rows.ot = -Y;
-        for_range<DT, false>(rows, s0, s1, [&](float z, float) { s += rows.wt(z); });
-        for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+    double R = -INFINITY, s = 0.0;
+    for_range<DT, false>(rows, s0, s1, [&](float z, float) {
+        mx = fmaxf(mx, z);
+        double Y = fma(static_cast<double>(z), C, -R);
+        if (Y > kSlackY) {                                // (the first finite logit: Y = +inf)
+            const double Rn = 256.0 * ceil(static_cast<double>(z) * (C / 256.0));
+            s = ldexp(s, static_cast<int>(fmax((R - Rn) / 256.0, -2048.0)));
+            R = Rn;
+            Y = fma(static_cast<double>(z), C, -R);
+        }
+        s += exp2_256(Y, tbl);
+    });
+    double Rw = R;
+    for (int off = 32; off > 0; off >>= 1) {
+        mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+        Rw = fmax(Rw, __shfl_xor(Rw, off, 64));
     }
+    s = (R == -INFINITY || !(fabsf(mx) <= 3.4e38f)) ? 0.0 : ldexp(s, static_cast<int>(fmax((R - Rw) / 256.0, -2048.0)));
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
     if (lane == 0) {
-        out->sp = s;
-        out->sq = Y;
+        const bool finite = fabsf(mx) <= 3.4e38f;         // else the pick reports the row
+        out->sp = finite ? s : 0.0;
+        out->sq = finite ? Rw : -INFINITY;
         out->a = mx;
     }
 }
