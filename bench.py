@@ -281,8 +281,10 @@ def main():
     if early:
         L = args.lead if args.lead > 0 else 1
         lead_rows = np.minimum(k, L - 1) + 1 + np.where(dsamp, np.minimum(k, L), 0)
-        decided = (n < L) | (k < L)
-        rest_rows = np.where(decided, 0, (k - L + 1) + np.where(dsamp, k - L, 0))
+        # (a sampling sequence's bonus row is read by its draw alone: the
+        # sequence is settled once its k drafted positions are)
+        decided = (n < L) | (k < L) | (dsamp & (k <= L))
+        rest_rows = np.where(decided, 0, (k - L + 1) - dsamp + np.where(dsamp, k - L, 0))
         read_rows = int(np.sum(lead_rows + rest_rows))
         second_rows = int(np.sum(rest_rows))
     else:

@@ -289,7 +289,11 @@ sv_status_t spec_verify_set_mode(int32_t mode, int32_t fused_lag);
  * needed.  With lead_positions = L > 0 the row pass first reads positions
  * 0..L-1 of every sequence and runs their accept tests; sequences with a
  * rejection there (or with k_b < L) are settled, and only the other
- * sequences' remaining rows are read.  L = 0 reads every row in one pass.
+ * sequences' remaining rows are read.  Outside the gathered form the bonus
+ * row (position k_b) of a sampling sequence is read by its draw alone, when
+ * all k_b drafts are accepted: its row diagnostics are NaN, and a sampling
+ * sequence is settled once its k_b drafted positions are.
+ * L = 0 reads every row in one pass.
  * L = -1 (the default) chooses: L = 1 when all logit rows of the call
  * together hold at least 512 MiB, else 0 (the two extra launches cost more
  * than small batches can save).  The outputs do not depend on L, except

@@ -94,11 +94,11 @@ __device__ __forceinline__ double log2_norm(const RowStat& r, float c) {
 // item is dispatched about lag blocks after the rows it needs.  The task
 // of a sampling sequence is marked unset until that accept item writes it.
 __device__ __forceinline__ void list_rest(const Problem& p, const Plan& plan, int32_t b, int64_t o, int32_t k,
-                                          int32_t limit, bool no_draft, bool greedy) {
+                                          int32_t limit, bool no_draft, bool greedy, bool skip_bonus_row) {
     const int lane = threadIdx.x & 63;
     const int64_t ntarget = p.total + p.B;
     const int32_t nseg = plan.nseg;
-    const int32_t nt = k - limit + 1, nd = no_draft ? 0 : k - limit;
+    const int32_t nt = k - limit + (skip_bonus_row ? 0 : 1), nd = no_draft ? 0 : k - limit;
     const int32_t cnt = (nt + nd) * nseg;
     uint64_t pos = 0;
     if (lane == 0) pos = atomicAdd(reinterpret_cast<unsigned long long*>(plan.blk_ctr),
@@ -173,6 +173,9 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
     const bool greedy = (Tf == 0.f);
     const bool gathered = p.draft_probs != nullptr;   // q_i(x_i) from the drafter
     const float c = greedy ? 0.f : row_scale(Tf);
+    // Early exit beside the draws: the bonus row of a sampling sequence is
+    // read by its draw alone, only when the bonus is drawn (kBonusSelf).
+    const bool bonus_unread = plan.queued && !greedy && !gathered;
     const int64_t trow = o + b + lane;             // this lane's target row
     const int64_t drow = o + lane;                 // this lane's draft row
 
@@ -188,8 +191,9 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
     }
     RowStat rt{0.f, 0, 0.f, 1.0}, rd{0.f, 0, 0.f, 1.0};
     const bool read = lane < limit;                // this position's rows have been read
+    const bool tread = read && !(bonus_unread && lane == k);   // ... and its target row
     bool row_bad = false;                          // a row of this position has a non-finite maximum
-    if (ok && lane <= k && read) {
+    if (ok && lane <= k && tread) {
         rt = merge_row<kCo>(plan.seg + trow * plan.nseg, plan.nseg, greedy);
         row_bad = !(fabsf(rt.m) <= 3.4e38f);
         if (!greedy && !gathered && lane < k) {
@@ -241,10 +245,10 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
     // (rows past the first rejection are never looked at).
     const uint64_t bad = __ballot(row_bad);
     const uint64_t mask = __ballot(reject) | bad;
-    if (!mask && k >= limit) {                     // undecided: rows past limit are needed
+    if (!mask && (bonus_unread ? k > limit : k >= limit)) {   // undecided: rows past limit are needed
         if (done) {
             if (lane == 0) *done = kUndecided;
-            list_rest(p, plan, b, o, k, limit, greedy || gathered, greedy);
+            list_rest(p, plan, b, o, k, limit, greedy || gathered, greedy, bonus_unread);
         }
         return false;
     }
@@ -262,7 +266,7 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
         if (early_draw) plan.early[atomicAdd(plan.early_n, 1u)] = b;
     }
 
-    const int32_t kind = greedy ? kNone : (n < k ? kResidual : kBonus);
+    const int32_t kind = greedy ? kNone : (n < k ? kResidual : (bonus_unread ? kBonusSelf : kBonus));
     if (task_out) {
         // (gathered form excluded: its residual needs the draft row read later)
         DrawTask& t = *task_out;
@@ -307,7 +311,7 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
         st_co<kCo>(&t->theta, (!greedy && n < k) ? log2_norm(rt, c) - (pending ? 0.0 : log2_norm(rd, c)) : 0.0);
         if constexpr (kCo) wait_stores();          // the kind, written last, says the rest is visible
         st_co<kCo>(&t->kind, static_cast<int32_t>(greedy ? kNone : (n < k ? (pending ? kResidualPending : kResidual)
-                                                                          : kBonus)));
+                                                                          : kind)));
     }
     if (p.out_p && lane < k) {
         p.out_p[drow] = static_cast<float>(px);
@@ -315,8 +319,8 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
     }
     if (p.out_row_max && lane <= k) {
         const bool dread = read && !greedy && !gathered;
-        p.out_row_max[trow] = read ? rt.m : NAN;
-        p.out_row_sum[trow] = (greedy || !read) ? NAN : static_cast<float>(exp2(log2_norm(rt, c)));
+        p.out_row_max[trow] = tread ? rt.m : NAN;
+        p.out_row_sum[trow] = (greedy || !tread) ? NAN : static_cast<float>(exp2(log2_norm(rt, c)));
         if (lane < k) {
             p.out_row_max[ntarget + drow] = dread ? rd.m : NAN;
             p.out_row_sum[ntarget + drow] = dread ? static_cast<float>(exp2(log2_norm(rd, c))) : NAN;

@@ -323,6 +323,47 @@ __device__ __forceinline__ void sub_range(const Problem& p, const Plan& plan, in
     *s1 = min(c1, c0 + (w + 1) * q);
 }
 
+// Sum over [v0, v1) (one whole wave) of w = 2^((Y - R) / 256),
+// Y = fma(z, rows.c, 0) = 256 z log2(e) / T, relative to a reference R of
+// the range's own: a whole number of octaves (a multiple of 256) at most
+// kSlackOct octaves below the largest Y.  Each lane raises its reference,
+// with an exact power-of-two rescale of its sum, only when a logit passes
+// it by that much; the lanes' sums are then rescaled to the wave's largest
+// reference.  Weights relative to any common reference give the same
+// distribution.  In every lane: *s, *R (-inf: no finite logit) and the
+// range's largest logit *mx (a non-finite one: *s = 0, *R = -inf).
+template <int DT>
+__device__ __forceinline__ void self_ref_sum(const drawpass::Rows<DT>& rows, int64_t v0, int64_t v1, double* s_out,
+                                             double* R_out, float* mx_out) {
+    using namespace drawpass;
+    constexpr double kSlackY = 256.0 * 32.0;     // kSlackOct = 32 octaves
+    const double C = rows.c;
+    float mx = -INFINITY;
+    double R = -INFINITY, s = 0.0;
+    for_range<DT, false>(rows, v0, v1, [&](float z, float) {
+        mx = fmaxf(mx, z);
+        double Y = fma(static_cast<double>(z), C, -R);
+        if (Y > kSlackY) {                        // (the first finite logit: Y = +inf)
+            const double Rn = 256.0 * ceil(static_cast<double>(z) * (C / 256.0));
+            s = ldexp(s, static_cast<int>(fmax((R - Rn) / 256.0, -2048.0)));
+            R = Rn;
+            Y = fma(static_cast<double>(z), C, -R);
+        }
+        s += exp2_256(Y, rows.tbl);
+    });
+    double Rw = R;
+    for (int off = 32; off > 0; off >>= 1) {
+        mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+        Rw = fmax(Rw, __shfl_xor(Rw, off, 64));
+    }
+    const bool finite = fabsf(mx) <= 3.4e38f;
+    s = (R == -INFINITY || !finite) ? 0.0 : ldexp(s, static_cast<int>(fmax((R - Rw) / 256.0, -2048.0)));
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+    *s_out = finite ? s : 0.0;
+    *R_out = finite ? Rw : -INFINITY;
+    *mx_out = mx;
+}
+
 // Workgroup scratch of one draw chunk (256 threads): each wave's band list.
 struct DrawLds {
     double wlist[kWaves][kWaveCap][2];
@@ -382,11 +423,15 @@ __device__ __forceinline__ void draw_chunk(const Problem& p, const Plan& plan, c
                 nband += __popcll(band);
             }
         });
+    } else if (task.kind == kBonusSelf) {
+        float mx;
+        self_ref_sum<DT>(rows, v0, v1, &sp, &sq, &mx);   // (already summed over the wave)
+        a = mx;
     } else {
         for_range<DT, false>(rows, v0, v1, [&](float zt, float) { sp += rows.wt(zt); });
     }
     if (active) {
-        wave_sum4(sp, sq, a, bq);
+        if (task.kind != kBonusSelf) wave_sum4(sp, sq, a, bq);
         if (lane == 0) {                       // lane 0 was active whenever any lane was
             lds.wcount[wave] = nband;
             ChunkSums* cs = plan.csum + sub + wave;
@@ -441,6 +486,22 @@ __device__ __forceinline__ void pick_sum2(double& a, double& b, double (*lds)[2]
     __syncthreads();
     a = b = 0.0;
     for (int w = 0; w < NT / 64; ++w) { a += lds[w][0]; b += lds[w][1]; }
+}
+
+// The maxima of a float and a double over an NT-thread workgroup (valid in
+// every thread).
+template <int NT>
+__device__ __forceinline__ void pick_max2(float& x, double& y, double (*lds)[2]) {
+    for (int off = 32; off > 0; off >>= 1) {
+        x = fmaxf(x, __shfl_xor(x, off, 64));
+        y = fmax(y, __shfl_xor(y, off, 64));
+    }
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) { lds[threadIdx.x >> 6][0] = x; lds[threadIdx.x >> 6][1] = y; }
+    __syncthreads();
+    x = static_cast<float>(lds[0][0]);
+    y = lds[0][1];
+    for (int w = 1; w < NT / 64; ++w) { x = fmaxf(x, static_cast<float>(lds[w][0])); y = fmax(y, lds[w][1]); }
 }
 
 // Exclusive prefix sum over an NT-thread workgroup in thread order; *total = sum.
@@ -673,25 +734,50 @@ __device__ __forceinline__ void pick_sequence(const Problem& p, const Plan& plan
     static_assert(NT % 256 == 0 && NT <= 1024, "pick workgroup size");
     const int tid = threadIdx.x, wave = tid >> 6;
     const bool resid_task = (task.kind == kResidual);
-    const Rows<DT> rows = rows_of<DT>(p, task, tbl);
+    Rows<DT> rows = rows_of<DT>(p, task, tbl);
     const int32_t nsub = plan.nchunk * kWaves;
     const int64_t sb = static_cast<int64_t>(b) * nsub;
     const ChunkSums* cs = plan.csum + sb;
     if (tid == 0) L.rescan = 0;
 
+    // A bonus draw of a row the row pass did not read: its maximum decides
+    // whether the sequence is a data error (R26), and the sub-chunk sums are
+    // rescaled exactly to their largest reference Y0, which the scan's
+    // weights are then taken relative to.
+    const bool self_ref = task.kind == kBonusSelf;
+    double Y0 = 0.0;
+    if (self_ref) {
+        float mx = -INFINITY;
+        double Ym = -INFINITY;
+        for (int32_t j = tid; j < nsub; j += NT) {
+            Ym = fmax(Ym, j == tid ? pf.sq : ld_co<kCo>(&cs[j].sq));
+            mx = fmaxf(mx, static_cast<float>(j == tid ? pf.a : ld_co<kCo>(&cs[j].a)));
+        }
+        pick_max2<NT>(mx, Ym, L.red2);
+        if (!(fabsf(mx) <= 3.4e38f)) {
+            const int64_t o = p.offsets ? static_cast<int64_t>(p.offsets[b]) : static_cast<int64_t>(b) * p.k_uniform;
+            const int64_t k = p.offsets ? static_cast<int64_t>(p.offsets[b + 1]) - o : p.k_uniform;
+            for (int64_t i = tid; i <= k; i += NT) p.out_tokens[o + b + i] = -1;
+            if (tid == 0) {
+                p.out_n[b] = -1;
+                if (p.out_emit_prob) p.out_emit_prob[b] = NAN;
+            }
+            return;
+        }
+        Y0 = Ym;
+        rows.ot = -Y0;
+    }
+
     // Sub-chunk tid's sums and band count come prefetched (a row with more
     // sub-chunks than the workgroup has threads loads the others' here and
     // in the loop below).
     double Sp = 0.0, Sq = 0.0;
-    if (tid < nsub) {
-        Sp = pf.sp;
-        Sq = pf.sq;
-        L.spc[tid] = pf.sp;
-    }
-    for (int32_t j = tid + NT; j < nsub; j += NT) {
-        const double xsp = ld_co<kCo>(&cs[j].sp);
+    for (int32_t j = tid; j < nsub; j += NT) {
+        double xsp = j == tid ? pf.sp : ld_co<kCo>(&cs[j].sp);
+        const double y = j == tid ? pf.sq : ld_co<kCo>(&cs[j].sq);
+        if (self_ref) xsp = y == -INFINITY ? 0.0 : ldexp(xsp, static_cast<int>(fmax((y - Y0) / 256.0, -2048.0)));
+        else Sq += y;
         Sp += xsp;
-        Sq += ld_co<kCo>(&cs[j].sq);
         L.spc[j] = xsp;
     }
     pick_sum2<NT>(Sp, Sq, L.red2);              // (its barriers also publish spc)

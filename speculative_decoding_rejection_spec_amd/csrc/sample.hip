@@ -64,35 +64,12 @@ __global__ __launch_bounds__(kThreads) void sample_sums_kernel(Problem p, Plan p
     __syncthreads();
     const double C = 256.0 * kLog2e / static_cast<double>(T);
     const Rows<DT> rows{row, row, C, 0.0, 0.0, tbl};
-    // One read: each lane sums its weights relative to its own reference R
-    // (a multiple of 256 in Y units), raised -- with an exact rescale of the
-    // sum -- only when a logit exceeds it by more than kSlackY; the lanes'
-    // sums are then rescaled to the wave's largest reference.
-    constexpr double kSlackY = 256.0 * 32.0;
-    float mx = -INFINITY;
-    double R = -INFINITY, s = 0.0;
-    for_range<DT, false>(rows, s0, s1, [&](float z, float) {
-        mx = fmaxf(mx, z);
-        double Y = fma(static_cast<double>(z), C, -R);
-        if (Y > kSlackY) {                                // (the first finite logit: Y = +inf)
-            const double Rn = 256.0 * ceil(static_cast<double>(z) * (C / 256.0));
-            s = ldexp(s, static_cast<int>(fmax((R - Rn) / 256.0, -2048.0)));
-            R = Rn;
-            Y = fma(static_cast<double>(z), C, -R);
-        }
-        s += exp2_256(Y, tbl);
-    });
-    double Rw = R;
-    for (int off = 32; off > 0; off >>= 1) {
-        mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-        Rw = fmax(Rw, __shfl_xor(Rw, off, 64));
-    }
-    s = (R == -INFINITY || !(fabsf(mx) <= 3.4e38f)) ? 0.0 : ldexp(s, static_cast<int>(fmax((R - Rw) / 256.0, -2048.0)));
-    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+    double sum, R;
+    float mx;
+    self_ref_sum<DT>(rows, s0, s1, &sum, &R, &mx);
     if (lane == 0) {
-        const bool finite = fabsf(mx) <= 3.4e38f;         // else the pick reports the row
-        out->sp = finite ? s : 0.0;
-        out->sq = finite ? Rw : -INFINITY;
+        out->sp = sum;
+        out->sq = R;
         out->a = mx;
     }
 }
@@ -114,20 +91,6 @@ __device__ __forceinline__ void block_argmax(float& m, int32_t& a, double (*red)
         const float m2 = static_cast<float>(red[w][0]);
         if (m2 > m || (m2 == m && ldsi[w] < a)) { m = m2; a = ldsi[w]; }
     }
-}
-
-template <int NT>
-__device__ __forceinline__ void block_max2(float& x, double& y, double (*red)[2]) {
-    for (int off = 32; off > 0; off >>= 1) {
-        x = fmaxf(x, __shfl_xor(x, off, 64));
-        y = fmax(y, __shfl_xor(y, off, 64));
-    }
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) { red[threadIdx.x >> 6][0] = x; red[threadIdx.x >> 6][1] = y; }
-    __syncthreads();
-    x = static_cast<float>(red[0][0]);
-    y = red[0][1];
-    for (int w = 1; w < NT / 64; ++w) { x = fmaxf(x, static_cast<float>(red[w][0])); y = fmax(y, red[w][1]); }
 }
 
 template <int DT, int NT>
@@ -176,7 +139,7 @@ __global__ __launch_bounds__(NT, 4) void sample_pick_kernel(Problem p, Plan plan
         mx = fmaxf(mx, static_cast<float>(cs[j].a));
         Y0 = fmax(Y0, y);
     }
-    block_max2<NT>(mx, Y0, L.red2);                       // (its barriers also publish spc, mass)
+    pick_max2<NT>(mx, Y0, L.red2);                       // (its barriers also publish spc, mass)
     if (!(fabsf(mx) <= 3.4e38f)) { data_error(); return; }
     for (int32_t j = tid; j < nsub; j += NT) {
         const double y = L.mass[j];

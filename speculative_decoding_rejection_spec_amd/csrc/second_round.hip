@@ -44,8 +44,9 @@ __device__ __forceinline__ bool rows_written(const Problem& p, const Plan& plan,
         const int64_t trow = o + b + lane, drow = ntarget + o + lane;
         for (int32_t sg = 0; sg < plan.nseg; ++sg) {
             const SegStat* t = plan.seg + trow * plan.nseg + sg;
-            ok = ok && ld_co<true>(&t->head) != kUnset64 &&
-                 __double_as_longlong(ld_co<true>(&t->s)) != static_cast<long long>(kUnset64);
+            if (greedy || lane < k)                // (a sampling sequence's bonus row is not listed)
+                ok = ok && ld_co<true>(&t->head) != kUnset64 &&
+                     __double_as_longlong(ld_co<true>(&t->s)) != static_cast<long long>(kUnset64);
             if (!greedy && lane < k) {
                 const SegStat* d = plan.seg + drow * plan.nseg + sg;
                 ok = ok && ld_co<true>(&d->head) != kUnset64 &&

@@ -71,11 +71,14 @@ __device__ __forceinline__ uint32_t head_hi(uint64_t h) { return static_cast<uin
 // row's SegStats; DrawTask::theta holds log2 S_p until then).
 // kTaskUnset: early exit's second round has not yet written the task (its
 // kind is written last, after the other fields are visible).
-enum : int32_t { kTaskUnset = -1, kNone = 0, kResidual = 1, kBonus = 2, kResidualPending = 3 };
+// kBonusSelf: a bonus draw whose row the row pass did not read (early exit
+// beside the draws): the draw takes the weights relative to references of
+// its own, and the pick checks the row's maximum (R26 there).
+enum : int32_t { kTaskUnset = -1, kNone = 0, kResidual = 1, kBonus = 2, kResidualPending = 3, kBonusSelf = 4 };
 
 // The draw one sequence still needs after the accept scan.
 struct DrawTask {
-    int32_t kind;      // kNone (greedy, error), kResidual (n < k) or kBonus (n = k)
+    int32_t kind;      // kNone (greedy, error), kResidual (n < k), kBonus or kBonusSelf (n = k)
     int32_t out_slot;  // index into out_tokens of the emitted token
     int64_t trow;      // target row at position n
     int64_t drow;      // draft row at position n (kResidual only)

@@ -156,7 +156,9 @@ def test_many_sequences_flag_rate(sv, cuda):
 def needed_rows(w, n):
     """Boolean masks over target rows and draft rows: the rows of positions
     up to the first rejection n_b (the draft row only below k_b, and only
-    for sampling sequences) -- what any verify must read."""
+    for sampling sequences) whose statistics the early-exit row pass
+    reports.  A sampling sequence's bonus row (position k_b) is read by its
+    draw alone, so it reports none."""
     tgt = np.zeros(w.total + w.B, bool)
     dft = np.zeros(w.total, bool)
     for b in range(w.B):
@@ -164,6 +166,8 @@ def needed_rows(w, n):
         if nb < 0:
             continue
         tgt[w.target_row(b, 0):w.target_row(b, nb) + 1] = True
+        if w.temperature[b] > 0 and nb == int(w.k[b]):
+            tgt[w.target_row(b, nb)] = False
         if w.temperature[b] > 0:
             o = int(w.offsets[b])
             dft[o:o + min(nb + 1, int(w.k[b]))] = True
