@@ -1,8 +1,10 @@
-"""Long parity runs: 10^4 sequences per small configuration (C1, C2, C3), in
-batches of fresh seeds, through the default launch form; tokens and accept
-counts bit-exact on every sequence the oracle does not flag, flagged
-sequences valid, and the flagged share under 0.1%.  Generating the
-synthetic rows dominates the time (about a minute for all three on a
+"""Long parity runs: 10^4 sequences per small configuration (C1, C2, C3) and
+about 1800 at the full sizes (three C4 batches of 256, two C5 batches of
+512, both in the default early-exit form), in batches of fresh seeds,
+through the default launch form; tokens and accept counts bit-exact on
+every sequence the oracle does not flag, flagged sequences valid, and the
+flagged share under 0.1%.  Generating the synthetic rows dominates the time
+(about a minute for C1-C3 and ten seconds per full-size batch on a
 16-thread host)."""
 import pytest
 
@@ -13,7 +15,8 @@ from test_gpu_parity import compare, run_gpu
 pytestmark = pytest.mark.gpu
 
 BATCHES = [("c1", 2500, t) for t in range(100, 104)] + [("c2", 2000, t) for t in range(100, 105)] + \
-          [("c3", 2000, t) for t in range(100, 105)]
+          [("c3", 2000, t) for t in range(100, 105)] + [("c4", 256, t) for t in range(100, 103)] + \
+          [("c5", 512, t) for t in range(100, 102)]
 TOTALS = {}
 
 
