@@ -740,10 +740,10 @@ __device__ __forceinline__ void pick_sequence(const Problem& p, const Plan& plan
     const ChunkSums* cs = plan.csum + sb;
     if (tid == 0) L.rescan = 0;
 
-    // A bonus draw of a row the row pass did not read: its maximum decides
-    // whether the sequence is a data error (R26), and the sub-chunk sums are
-    // rescaled exactly to their largest reference Y0, which the scan's
-    // weights are then taken relative to.
+    // A bonus draw of a row the row pass did not read: a non-finite maximum
+    // of the row makes the sequence a data error; otherwise the sub-chunk
+    // sums are rescaled exactly to their largest reference Y0, which the
+    // scan's weights are then taken relative to.
     const bool self_ref = task.kind == kBonusSelf;
     double Y0 = 0.0;
     if (self_ref) {

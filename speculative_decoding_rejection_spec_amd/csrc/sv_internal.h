@@ -73,7 +73,8 @@ __device__ __forceinline__ uint32_t head_hi(uint64_t h) { return static_cast<uin
 // kind is written last, after the other fields are visible).
 // kBonusSelf: a bonus draw whose row the row pass did not read (early exit
 // beside the draws): the draw takes the weights relative to references of
-// its own, and the pick checks the row's maximum (R26 there).
+// its own, and the pick checks the row's maximum (a non-finite one makes the
+// sequence a data error).
 enum : int32_t { kTaskUnset = -1, kNone = 0, kResidual = 1, kBonus = 2, kResidualPending = 3, kBonusSelf = 4 };
 
 // The draw one sequence still needs after the accept scan.
