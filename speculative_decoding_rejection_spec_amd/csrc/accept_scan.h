@@ -43,41 +43,56 @@ struct RowStat {
 // seen so far (the same sum as rescaling every term to the final one);
 // greedy rows keep the lowest id among tied maxima.  Statistics are loaded
 // four segments at a time so their round trips overlap.
+// Merges the statistics (h = SegStat::head, v = SegStat::s) of the next
+// segment of a row into r, segments in order.
+__device__ __forceinline__ void merge_seg(RowStat& r, uint64_t h, double v, bool greedy) {
+    const float m = head_m(h);
+    if (greedy) {
+        const int32_t a = static_cast<int32_t>(head_hi(h));
+        if (m > r.m || (m == r.m && a < r.arg)) { r.m = m; r.arg = a; }
+        return;
+    }
+    const float R = __uint_as_float(head_hi(h));
+    r.m = fmaxf(r.m, m);
+    if (R == -INFINITY) return;                                  // an empty segment
+    if (R > r.R) {
+        if (r.R != -INFINITY) r.S = ldexp(r.S, static_cast<int>(fmaxf(r.R - R, -2048.f)));
+        r.R = R;
+    }
+    r.S += ldexp(v, static_cast<int>(fmaxf(R - r.R, -2048.f)));
+}
+
 template <bool kCo>
 __device__ __forceinline__ RowStat merge_row(const SegStat* seg, int32_t nseg, bool greedy) {
     constexpr int kBatch = 4;
     RowStat r{-INFINITY, INT32_MAX, -INFINITY, 0.0};
     for (int32_t s0 = 0; s0 < nseg; s0 += kBatch) {
-        float m[kBatch], R[kBatch];
-        int32_t a[kBatch];
+        uint64_t h[kBatch];
         double v[kBatch];
 #pragma unroll
         for (int i = 0; i < kBatch; ++i) {
             const int32_t s = s0 + i < nseg ? s0 + i : nseg - 1;   // clamped; used only when in range
-            const uint64_t h = ld_co<kCo>(&seg[s].head);
-            m[i] = head_m(h);
-            a[i] = static_cast<int32_t>(head_hi(h));
-            R[i] = __uint_as_float(head_hi(h));
-            if (!greedy) v[i] = ld_co<kCo>(&seg[s].s);
+            h[i] = ld_co<kCo>(&seg[s].head);
+            v[i] = greedy ? 0.0 : ld_co<kCo>(&seg[s].s);
         }
 #pragma unroll
         for (int i = 0; i < kBatch; ++i) {
             if (s0 + i >= nseg) break;
-            if (greedy) {
-                if (m[i] > r.m || (m[i] == r.m && a[i] < r.arg)) { r.m = m[i]; r.arg = a[i]; }
-                continue;
-            }
-            r.m = fmaxf(r.m, m[i]);
-            if (R[i] == -INFINITY) continue;                        // an empty segment
-            if (R[i] > r.R) {
-                if (r.R != -INFINITY) r.S = ldexp(r.S, static_cast<int>(fmaxf(r.R - R[i], -2048.f)));
-                r.R = R[i];
-            }
-            r.S += ldexp(v[i], static_cast<int>(fmaxf(R[i] - r.R, -2048.f)));
+            merge_seg(r, h[i], v[i], greedy);
         }
     }
     return r;
 }
+
+// The statistics a sampling sequence's accept scan reads, loaded by the wave
+// that polled for them (rows of at most kPolledSegs segments): lane i holds
+// position i's target and draft row segments and captured logits.
+constexpr int kPolledSegs = 2;
+struct Polled {
+    uint64_t th[kPolledSegs], dh[kPolledSegs];
+    double ts[kPolledSegs], ds[kPolledSegs];
+    float xt, xd;
+};
 
 // log2 of the normaliser sum_v 2^((z_v - m) c) of a merged sampling row.
 __device__ __forceinline__ double log2_norm(const RowStat& r, float c) {
@@ -156,11 +171,14 @@ __device__ __forceinline__ void list_rest(const Problem& p, const Plan& plan, in
 // kNone when there is nothing to draw).  emit = false: the scan writes
 // nothing at all -- for workgroups that need the task of a sequence whose
 // outputs another workgroup writes (the same scan over the same inputs
-// gives the same task).
+// gives the same task).  pre (sampling sequences outside the gathered form,
+// rows of at most kPolledSegs segments, every position read): the rows'
+// statistics already loaded, used instead of loading them again.
 template <bool kCo>
 __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& plan, int32_t b,
                                                 int32_t limit = kKMax + 1, int32_t* done = nullptr,
-                                                DrawTask* task_out = nullptr, bool emit = true) {
+                                                DrawTask* task_out = nullptr, bool emit = true,
+                                                const Polled* pre = nullptr) {
     const int lane = threadIdx.x & 63;
     int64_t o, o1;
     if (p.offsets) { o = p.offsets[b]; o1 = p.offsets[b + 1]; }
@@ -194,10 +212,24 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
     const bool tread = read && !(bonus_unread && lane == k);   // ... and its target row
     bool row_bad = false;                          // a row of this position has a non-finite maximum
     if (ok && lane <= k && tread) {
-        rt = merge_row<kCo>(plan.seg + trow * plan.nseg, plan.nseg, greedy);
+        if (pre) {
+            rt = RowStat{-INFINITY, INT32_MAX, -INFINITY, 0.0};
+#pragma unroll
+            for (int sg = 0; sg < kPolledSegs; ++sg)
+                if (sg < plan.nseg) merge_seg(rt, pre->th[sg], pre->ts[sg], false);
+        } else {
+            rt = merge_row<kCo>(plan.seg + trow * plan.nseg, plan.nseg, greedy);
+        }
         row_bad = !(fabsf(rt.m) <= 3.4e38f);
         if (!greedy && !gathered && lane < k) {
-            rd = merge_row<kCo>(plan.seg + (ntarget + drow) * plan.nseg, plan.nseg, false);
+            if (pre) {
+                rd = RowStat{-INFINITY, INT32_MAX, -INFINITY, 0.0};
+#pragma unroll
+                for (int sg = 0; sg < kPolledSegs; ++sg)
+                    if (sg < plan.nseg) merge_seg(rd, pre->dh[sg], pre->ds[sg], false);
+            } else {
+                rd = merge_row<kCo>(plan.seg + (ntarget + drow) * plan.nseg, plan.nseg, false);
+            }
             row_bad = row_bad || !(fabsf(rd.m) <= 3.4e38f);
         }
     }
@@ -228,12 +260,12 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
         if (greedy) {
             reject = (x != rt.arg);
         } else {
-            const double zt = ld_co<kCo>(&plan.xlogit[trow]);       // captured by the row pass
+            const double zt = pre ? pre->xt : ld_co<kCo>(&plan.xlogit[trow]);   // captured by the row pass
             px = exp2(zt * c - rt.R) / rt.S;
             if (gathered) {
                 qx = qg;
             } else {
-                const double zd = ld_co<kCo>(&plan.xlogit[ntarget + drow]);
+                const double zd = pre ? pre->xd : ld_co<kCo>(&plan.xlogit[ntarget + drow]);
                 qx = exp2(zd * c - rd.R) / rd.S;
             }
             const double alpha = fmin(1.0, px / qx);

@@ -60,6 +60,40 @@ __device__ __forceinline__ bool rows_written(const Problem& p, const Plan& plan,
     return !__any(!ok);
 }
 
+// The same for a sampling sequence whose rows have at most kPolledSegs
+// segments, keeping what it loads: lane i < k loads position i's target and
+// draft segment statistics and captured logits (also those of the leading
+// positions, written by an earlier launch) into *pre, which the accept scan
+// then uses without loading them again.
+__device__ __forceinline__ bool rows_written_polled(const Problem& p, const Plan& plan, int32_t b, Polled* pre) {
+    const int lane = threadIdx.x & 63;
+    const int64_t o = p.offsets ? static_cast<int64_t>(p.offsets[b]) : static_cast<int64_t>(b) * p.k_uniform;
+    const int64_t k = p.offsets ? static_cast<int64_t>(p.offsets[b + 1]) - o : p.k_uniform;
+    const int64_t ntarget = p.total + p.B;
+    bool ok = true;
+    if (lane < k) {
+        const int64_t trow = o + b + lane, drow = ntarget + o + lane;
+#pragma unroll
+        for (int sg = 0; sg < kPolledSegs; ++sg) {
+            if (sg < plan.nseg) {
+                const SegStat* t = plan.seg + trow * plan.nseg + sg;
+                const SegStat* d = plan.seg + drow * plan.nseg + sg;
+                pre->th[sg] = ld_co<true>(&t->head);
+                pre->ts[sg] = ld_co<true>(&t->s);
+                pre->dh[sg] = ld_co<true>(&d->head);
+                pre->ds[sg] = ld_co<true>(&d->s);
+                ok = ok && pre->th[sg] != kUnset64 && pre->dh[sg] != kUnset64 &&
+                     __double_as_longlong(pre->ts[sg]) != static_cast<long long>(kUnset64) &&
+                     __double_as_longlong(pre->ds[sg]) != static_cast<long long>(kUnset64);
+            }
+        }
+        pre->xt = ld_co<true>(&plan.xlogit[trow]);
+        pre->xd = ld_co<true>(&plan.xlogit[drow]);
+        ok = ok && __float_as_uint(pre->xt) != kUnset32 && __float_as_uint(pre->xd) != kUnset32;
+    }
+    return !__any(!ok);
+}
+
 template <int DT>
 __global__ __launch_bounds__(kThreads) void rest_draws_kernel(Problem p, Plan plan) {
     __shared__ union {
@@ -115,12 +149,19 @@ __global__ __launch_bounds__(kThreads) void rest_draws_kernel(Problem p, Plan pl
         if (kind == kItemAccept) {
             if (tid >= 64) return;                     // one wave runs it
             bool ready = plan.queue_mode != SV_QUEUE_HANDOFF;
+            // (a sampling sequence with short segment lists keeps what its
+            // last poll loaded, saving the scan a round trip to memory)
+            const bool keep = p.temperature[b] != 0.f && plan.nseg <= kPolledSegs;
+            Polled pre;
             for (uint32_t polls = 0; ready; ++polls) {
-                if (rows_written(p, plan, b)) break;
+                if (keep ? rows_written_polled(p, plan, b, &pre) : rows_written(p, plan, b)) break;
                 if (polls == kPolls) ready = false;
                 __builtin_amdgcn_s_sleep(8);
             }
-            if (ready) accept_sequence<true>(p, plan, b);
+            if (ready) {
+                if (keep) accept_sequence<true>(p, plan, b, kKMax + 1, nullptr, nullptr, true, &pre);
+                else accept_sequence<true>(p, plan, b);
+            }
             else if (tid == 0) plan.aband[b] = 1;    // the pick launch redoes the sequence
             return;
         }
