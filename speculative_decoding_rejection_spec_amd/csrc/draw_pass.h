@@ -742,18 +742,22 @@ __device__ __forceinline__ void pick_sequence(const Problem& p, const Plan& plan
 
     // A bonus draw of a row the row pass did not read: a non-finite maximum
     // of the row makes the sequence a data error; otherwise the sub-chunk
-    // sums are rescaled exactly to their largest reference Y0, which the
-    // scan's weights are then taken relative to.
+    // sums are rescaled exactly to their largest reference Y0 (by wave 0,
+    // which then searches them), and the scan's weights are taken relative
+    // to Y0.  A bonus draw needs no S_p: the search forms Z itself.
     const bool self_ref = task.kind == kBonusSelf;
-    double Y0 = 0.0;
+    double Sp = 1.0, Sq = 1.0;
     if (self_ref) {
         float mx = -INFINITY;
         double Ym = -INFINITY;
         for (int32_t j = tid; j < nsub; j += NT) {
-            Ym = fmax(Ym, j == tid ? pf.sq : ld_co<kCo>(&cs[j].sq));
+            const double y = j == tid ? pf.sq : ld_co<kCo>(&cs[j].sq);
+            L.spc[j] = j == tid ? pf.sp : ld_co<kCo>(&cs[j].sp);
+            L.mass[j] = y;
+            Ym = fmax(Ym, y);
             mx = fmaxf(mx, static_cast<float>(j == tid ? pf.a : ld_co<kCo>(&cs[j].a)));
         }
-        pick_max2<NT>(mx, Ym, L.red2);
+        pick_max2<NT>(mx, Ym, L.red2);          // (its barriers also publish spc and mass)
         if (!(fabsf(mx) <= 3.4e38f)) {
             const int64_t o = p.offsets ? static_cast<int64_t>(p.offsets[b]) : static_cast<int64_t>(b) * p.k_uniform;
             const int64_t k = p.offsets ? static_cast<int64_t>(p.offsets[b + 1]) - o : p.k_uniform;
@@ -764,23 +768,28 @@ __device__ __forceinline__ void pick_sequence(const Problem& p, const Plan& plan
             }
             return;
         }
-        Y0 = Ym;
-        rows.ot = -Y0;
+        rows.ot = -Ym;
+        if (wave == 0) {
+            for (int32_t j = tid; j < nsub; j += 64) {
+                const double y = L.mass[j];
+                L.spc[j] = y == -INFINITY ? 0.0 : ldexp(L.spc[j], static_cast<int>(fmax((y - Ym) / 256.0, -2048.0)));
+            }
+            __builtin_amdgcn_wave_barrier();    // (LDS accesses of one wave complete in order)
+        }
+    } else {
+        // Sub-chunk tid's sums and band count come prefetched (a row with
+        // more sub-chunks than the workgroup has threads loads the others'
+        // here and in the loop below).
+        Sp = 0.0;
+        Sq = 0.0;
+        for (int32_t j = tid; j < nsub; j += NT) {
+            const double xsp = j == tid ? pf.sp : ld_co<kCo>(&cs[j].sp);
+            Sq += j == tid ? pf.sq : ld_co<kCo>(&cs[j].sq);
+            Sp += xsp;
+            L.spc[j] = xsp;
+        }
+        pick_sum2<NT>(Sp, Sq, L.red2);          // (its barriers also publish spc)
     }
-
-    // Sub-chunk tid's sums and band count come prefetched (a row with more
-    // sub-chunks than the workgroup has threads loads the others' here and
-    // in the loop below).
-    double Sp = 0.0, Sq = 0.0;
-    for (int32_t j = tid; j < nsub; j += NT) {
-        double xsp = j == tid ? pf.sp : ld_co<kCo>(&cs[j].sp);
-        const double y = j == tid ? pf.sq : ld_co<kCo>(&cs[j].sq);
-        if (self_ref) xsp = y == -INFINITY ? 0.0 : ldexp(xsp, static_cast<int>(fmax((y - Y0) / 256.0, -2048.0)));
-        else Sq += y;
-        Sp += xsp;
-        L.spc[j] = xsp;
-    }
-    pick_sum2<NT>(Sp, Sq, L.red2);              // (its barriers also publish spc)
     const double iSp = 1.0 / Sp, iSq = resid_task ? 1.0 / Sq : 0.0;
 
     if (resid_task) {
