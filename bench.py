@@ -314,6 +314,11 @@ def main():
     hbm_gbs = total_bytes / (ms_per_step / 1e3) / 1e9
 
     roofline = None
+    # The committed counter summaries were taken on the C4 verify in the
+    # default geometry: their traffic applies to no other workload or shape.
+    counters_apply = (args.workload == "c4" and args.entry == "verify" and args.seg == 0 and args.chunk == 0 and
+                      args.lead in (-1, 0, 1) and args.queue == 0 and list(args.queue_lag) == [0, 0] and
+                      args.mode == "auto")
     if k1_live is not None:
         # The row pass reads every needed row once; the fused kernel also
         # reads the draw rows.
@@ -322,7 +327,8 @@ def main():
         achieved = kbytes / (k1_live / 1e3) / 1e9
         roofline = {"bound": "hbm", "kernel": roof_kernel, "achieved": round(achieved, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                    "traffic": committed_traffic(roof_kernel), "algorithmic_bytes": kbytes,
+                    "traffic": committed_traffic(roof_kernel) if counters_apply else None,
+                    "algorithmic_bytes": kbytes,
                     "mean_ms": round(k1_live, 5)}
 
     cpu = None
