@@ -6,31 +6,29 @@
 namespace sv {
 namespace {
 
-__global__ __launch_bounds__(kThreads) void accept_kernel(Problem p, Plan plan) {
-    const int32_t b = blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (b >= p.B) return;                          // whole wave leaves together
+// One wave per workgroup: the scans spread over B compute units (C4's lead
+// scan: 9.7 -> 8.6 us against four waves per workgroup).
+__global__ __launch_bounds__(64) void accept_kernel(Problem p, Plan plan) {
+    const int32_t b = blockIdx.x;
     if (plan.lead > 0 && plan.done[b]) return;     // decided by its leading positions
     accept_sequence<false>(p, plan, b);
 }
 
 // Early exit: the accept scan over the leading positions only.
-__global__ __launch_bounds__(kThreads) void accept_lead_kernel(Problem p, Plan plan) {
-    const int32_t b = blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (b >= p.B) return;
+__global__ __launch_bounds__(64) void accept_lead_kernel(Problem p, Plan plan) {
+    const int32_t b = blockIdx.x;
     accept_sequence<false>(p, plan, b, plan.lead, plan.done + b);
 }
 
 }  // namespace
 
 hipError_t launch_accept(const Problem& p, const Plan& plan, hipStream_t s) {
-    const int64_t blocks = (static_cast<int64_t>(p.B) + kWaves - 1) / kWaves;
-    accept_kernel<<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s>>>(p, plan);
+    accept_kernel<<<dim3(static_cast<uint32_t>(p.B)), dim3(64), 0, s>>>(p, plan);
     return hipGetLastError();
 }
 
 hipError_t launch_accept_lead(const Problem& p, const Plan& plan, hipStream_t s) {
-    const int64_t blocks = (static_cast<int64_t>(p.B) + kWaves - 1) / kWaves;
-    accept_lead_kernel<<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s>>>(p, plan);
+    accept_lead_kernel<<<dim3(static_cast<uint32_t>(p.B)), dim3(64), 0, s>>>(p, plan);
     return hipGetLastError();
 }
 
