@@ -1,5 +1,5 @@
 // draw.hip -- the staged draw: draw_sums (grid sequence x chunk, 256
-// threads) and draw_pick (one 1024- or 512-thread workgroup per sequence),
+// threads) and draw_pick (one 512-thread workgroup per sequence),
 // where the kernel boundary publishes the chunk sums; or, for one-pass calls
 // whose draw fits one round of workgroups, draw_all, which also runs the
 // accept scans and the picks.  The work itself is in accept_scan.h and
@@ -135,18 +135,16 @@ hipError_t launch_draw_sums(const Problem& p, const Plan& plan, hipStream_t s) {
     return hipGetLastError();
 }
 
-// One workgroup per sequence: 1024 threads while the sequences fit one per
-// CU, else 512 (two per CU, so the picks still run in one round).
+// One 512-thread workgroup per sequence (two share a CU once the sequences
+// outnumber the CUs).  1024-thread picks, one per CU, were slower for 256
+// sequences of V = 152064 (13.3 against 11.5 us): twice the waves in every
+// barrier for half the tokens per lane.
 hipError_t launch_draw_pick(const Problem& p, const Plan& plan, hipStream_t s) {
     const dim3 grid(static_cast<uint32_t>(p.B));
-    const bool wide = p.B <= plan.cus;
-    if (p.dtype == SV_BF16) {
-        if (wide) draw_pick_kernel<SV_BF16, 1024><<<grid, dim3(1024), 0, s>>>(p, plan);
-        else draw_pick_kernel<SV_BF16, 512><<<grid, dim3(512), 0, s>>>(p, plan);
-    } else {
-        if (wide) draw_pick_kernel<SV_F32, 1024><<<grid, dim3(1024), 0, s>>>(p, plan);
-        else draw_pick_kernel<SV_F32, 512><<<grid, dim3(512), 0, s>>>(p, plan);
-    }
+    if (p.dtype == SV_BF16)
+        draw_pick_kernel<SV_BF16, 512><<<grid, dim3(512), 0, s>>>(p, plan);
+    else
+        draw_pick_kernel<SV_F32, 512><<<grid, dim3(512), 0, s>>>(p, plan);
     return hipGetLastError();
 }
 

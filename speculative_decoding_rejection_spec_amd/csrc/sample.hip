@@ -176,18 +176,13 @@ hipError_t launch_sample_sums(const Problem& p, const Plan& plan, hipStream_t s)
     return hipGetLastError();
 }
 
-// One workgroup per row: 1024 threads while the rows fit one per CU, else
-// 512 (two per CU).
+// One 512-thread workgroup per row (as the verify's pick).
 hipError_t launch_sample_pick(const Problem& p, const Plan& plan, hipStream_t s) {
     const dim3 grid(static_cast<uint32_t>(p.B));
-    const bool wide = p.B <= plan.cus;
-    if (p.dtype == SV_BF16) {
-        if (wide) sample_pick_kernel<SV_BF16, 1024><<<grid, dim3(1024), 0, s>>>(p, plan);
-        else sample_pick_kernel<SV_BF16, 512><<<grid, dim3(512), 0, s>>>(p, plan);
-    } else {
-        if (wide) sample_pick_kernel<SV_F32, 1024><<<grid, dim3(1024), 0, s>>>(p, plan);
-        else sample_pick_kernel<SV_F32, 512><<<grid, dim3(512), 0, s>>>(p, plan);
-    }
+    if (p.dtype == SV_BF16)
+        sample_pick_kernel<SV_BF16, 512><<<grid, dim3(512), 0, s>>>(p, plan);
+    else
+        sample_pick_kernel<SV_F32, 512><<<grid, dim3(512), 0, s>>>(p, plan);
     return hipGetLastError();
 }
 

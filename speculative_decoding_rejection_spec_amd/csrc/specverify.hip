@@ -37,7 +37,8 @@ int64_t g_seg_elems = 0;                     // 0: automatic (auto_lengths)
 int64_t g_chunk_elems = 0;
 
 // Automatic segment and chunk lengths: the defaults suit batches that fill
-// the GPU many times over (C4: 8704 row workgroups, 4864 draw workgroups);
+// the GPU many times over (256 sequences of k = 8, V = 152064: 8704 row
+// workgroups, 4864 draw workgroups);
 // a small call is cut finer so its row pass still has about kRowBlocks
 // workgroups and its draw about kDrawBlocks (no finer than kMinSeg /
 // kMinChunk logits).
