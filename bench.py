@@ -12,17 +12,17 @@ its rows in the 256 MB last-level cache.
 One step = one spec_verify call (row pass, accept scan, fp64 draw) over the
 whole batch.  Output: one JSON line with sequences/s, the achieved HBM
 bandwidth on algorithmic bytes, the roofline of the dominant kernel and the
-fp64 CPU oracle timed on this host as a baseline.  The dominant kernel is the
-row pass in the default staged form, the persistent kernel (the whole step)
-in the fused form (--mode fused).
+fp64 CPU oracle timed on this host as a baseline.  The dominant kernel is
+early exit's second round (the remaining rows and every draw row) for C4 and
+C5, the one-pass row pass for smaller calls.
 
 Algorithmic bytes per step: the logit rows the step reads, once each, plus
 one extra read of each draw row (2 rows for a residual draw, 1 for a bonus
 draw, 0 for greedy), V * element size per row; the small per-sequence arrays
 are ignored.  Rows read: with early exit (--lead 1; the default for C4) the
 leading positions of every sequence and the remaining positions of the
-sequences they leave undecided; in one full pass (--lead 0) or the fused
-form, every target row and the draft rows of sampling sequences.  Both
+sequences they leave undecided; in one full pass (--lead 0), every target
+row and the draft rows of sampling sequences.  Both
 figures, and the minimum (the rows up to each sequence's first rejection),
 are in the output line.
 """
@@ -42,10 +42,8 @@ EVENT_EVERY = 8
 METRIC = "sequences verified/s and achieved HBM GB/s (% of peak), B=256 k=8 V=152064 bf16"
 # Counter summaries per roofline kernel, and the sources each kernel is built from.
 COUNTERS = {"row_stats": os.path.join(ROOT, "profiles", "row_stats_c4_counters.txt"),
-            "fused": os.path.join(ROOT, "profiles", "fused_c4_counters.txt"),
             "rest": os.path.join(ROOT, "profiles", "second_round_c4_counters.txt")}
 KERNEL_SOURCES = {"row_stats": ["row_stats.hip", "row_pass.h", "sv_internal.h"],
-                  "fused": ["fused.hip", "row_pass.h", "accept_scan.h", "draw_pass.h", "sv_internal.h"],
                   "rest": ["second_round.hip", "row_pass.h", "accept_scan.h", "draw_pass.h", "sv_internal.h"]}
 
 
@@ -99,9 +97,6 @@ def main():
                     help="also run a plain 1 GiB device copy (counter calibration runs)")
     ap.add_argument("--seg", type=int, default=0, help="row-pass segment elements (0 = default)")
     ap.add_argument("--chunk", type=int, default=0, help="draw chunk elements (0 = default)")
-    ap.add_argument("--mode", choices=["auto", "staged", "fused"], default="auto",
-                    help="launch form (auto = staged)")
-    ap.add_argument("--lag", type=int, default=0, help="fused form: draw lag in sequences (0 = auto)")
     ap.add_argument("--entry", choices=["verify", "gathered", "draft", "ngram", "commit", "stream"],
                     default="verify",
                     help="verify: spec_verify; gathered: spec_verify_gathered with the drafts' q(x) "
@@ -137,8 +132,6 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sv.set_geometry(args.seg, args.chunk)
-    sv.set_mode({"auto": sv.SV_MODE_AUTO, "staged": sv.SV_MODE_STAGED, "fused": sv.SV_MODE_FUSED}[args.mode],
-                args.lag)
     sv.set_early_exit(args.lead)
     sv.set_queue(args.queue, *args.queue_lag)
 
@@ -215,23 +208,19 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # Which form ran: the probe reports NaN for kernels a call did not launch.
+    # Which kernels a call launches (kernel_times() lists only those).
     sv.timing(True)
     step(0)
     torch.cuda.synchronize()
     launched = sv.kernel_times()
-    form = "fused" if "fused" in launched else "staged"
     early = "row_lead" in launched
     sv.timing(False)
     # The roofline kernel: the row pass (one launch, or the two launches of
-    # early exit in the gathered form), the fused kernel, or -- early exit --
-    # the second round, the dominant launch, which streams the remaining rows
-    # and every draw row.
+    # early exit in the gathered form), or -- early exit -- the second round,
+    # the dominant launch, which streams the remaining rows and every draw row.
     queued = "rest" in launched
     if "sample_sums" in launched:                # the draft sampler: one read of each row
         roof = ["sample_sums"]
-    elif form == "fused":
-        roof = ["fused"]
     elif queued:
         roof = ["rest"]
     else:
@@ -317,13 +306,11 @@ def main():
     # The committed counter summaries were taken on the C4 verify in the
     # default geometry: their traffic applies to no other workload or shape.
     counters_apply = (args.workload == "c4" and args.entry == "verify" and args.seg == 0 and args.chunk == 0 and
-                      args.lead in (-1, 0, 1) and args.queue == 0 and list(args.queue_lag) == [0, 0] and
-                      args.mode == "auto")
+                      args.lead in (-1, 0, 1) and args.queue == 0 and list(args.queue_lag) == [0, 0])
     if k1_live is not None:
-        # The row pass reads every needed row once; the fused kernel also
-        # reads the draw rows.
-        kbytes = total_bytes if roof_kernel == "fused" else (
-            (second_rows + (draw_rows if args.queue == 0 else 0)) * row_bytes if queued else k1_bytes)
+        # The row pass reads every needed row once; the second round also
+        # reads the draw rows (unless they are all left to the pick launch).
+        kbytes = (second_rows + (draw_rows if args.queue == 0 else 0)) * row_bytes if queued else k1_bytes
         achieved = kbytes / (k1_live / 1e3) / 1e9
         roofline = {"bound": "hbm", "kernel": roof_kernel, "achieved": round(achieved, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
@@ -377,7 +364,7 @@ def main():
                    f"V={w.V} {w.dtype} logits", "B": w.B, "V": w.V, "k_max": int(w.k.max()),
                    "total_draft": w.total, "logit_dtype": w.dtype,
                    "temperatures": sorted(set(float(t) for t in w.temperature)),
-                   "input_copies": len(copies), "form": form, "entry": args.entry,
+                   "input_copies": len(copies), "entry": args.entry,
                    "early_exit_lead": (args.lead if args.lead > 0 else 1) if early else 0},
         "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
         "algorithmic_bytes": total_bytes, "mean_accepted": round(float(n.mean()), 4),

@@ -95,9 +95,11 @@ size_t spec_verify_workspace_size(int32_t B, int64_t total_draft, int64_t V, sv_
  * logit row once (row maximum, sum of exp((z - max)/T), or the argmax for
  * greedy rows); one wavefront per sequence then runs the accept tests and
  * finds the first rejection; a last fp64 pass over the one rejected or bonus
- * row pair draws the emitted token by inverse CDF.  The steps run as four
- * kernels by default, or as one persistent kernel (spec_verify_set_mode);
- * the results do not depend on the form. */
+ * row pair draws the emitted token by inverse CDF.  Calls whose logit rows
+ * hold at least 512 MiB read the rows in position order and stop at each
+ * sequence's first rejection (early exit, four launches); smaller calls read
+ * every needed row in one pass (two to four launches).  The outputs do not
+ * depend on the form. */
 sv_status_t spec_verify(const void *target_logits, const void *draft_logits,
                         const int32_t *draft_tokens, const int32_t *offsets,
                         int32_t k_uniform, int64_t total_draft, int32_t B, int64_t V,
@@ -112,7 +114,9 @@ sv_status_t spec_verify(const void *target_logits, const void *draft_logits,
  *   out_row_max, out_row_sumexp fp32 [2 * total_draft + B]: per logit row
  *     (target rows first, then draft rows) the maximum logit and
  *     sum_v exp((z_v - max)/T); sumexp is NaN for greedy rows and both are NaN
- *     for rows that are never read. */
+ *     for rows that are never read (with early exit: rows past a sequence's
+ *     first rejection, and the bonus row of a sampling sequence, which its
+ *     draw alone reads). */
 sv_status_t spec_verify_probs(const void *target_logits, const void *draft_logits,
                               const int32_t *draft_tokens, const int32_t *offsets,
                               int32_t k_uniform, int64_t total_draft, int32_t B, int64_t V,
@@ -138,8 +142,7 @@ sv_status_t spec_verify_probs(const void *target_logits, const void *draft_logit
  *     for data errors).
  * Every other argument and output is as for spec_verify.  Only target rows
  * and, for each sequence that rejects at position n < k_b, draft row n are
- * read; early exit (spec_verify_set_early_exit) applies to the target rows.
- * Always runs in the staged form. */
+ * read; early exit applies to the target rows. */
 sv_status_t spec_verify_gathered(const void *target_logits, const void *draft_logits,
                                  const int32_t *draft_tokens, const float *draft_probs,
                                  const int32_t *offsets, int32_t k_uniform, int64_t total_draft,
@@ -223,114 +226,6 @@ const char *spec_verify_status_string(sv_status_t status);
 /* Frees the library-owned workspace of every GPU.  Not safe while a call
  * that uses it is still running. */
 void spec_verify_release(void);
-
-/* Benchmark reference: a bare read-reduce over `bytes` of device memory at
- * `data` (16-byte aligned), one 256-thread workgroup per `seg_bytes`
- * (a multiple of 16, 4096 .. 2^30) reading it the way the row pass reads a
- * segment (16-byte raw buffer loads, 8 in flight per lane, non-temporal)
- * and writing the XOR of its whole 16-byte words to out[i] (uint32,
- * ceil(bytes / seg_bytes) entries, caller-owned).  Its bandwidth is the
- * practical ceiling for the row pass.  Enqueue-only on `stream`.  Returns
- * SV_ERR_SHAPE / SV_ERR_NULL / SV_ERR_ALIGN for bad arguments. */
-sv_status_t spec_stream_probe(const void *data, int64_t bytes, int64_t seg_bytes, uint32_t *out,
-                              hipStream_t stream);
-
-/* Kernel timing for benchmarks.  spec_verify_timing(kernels, every) turns
- * the probe on for the kernels whose bits are set in `kernels` (bit i
- * selects spec_verify_kernel_name(i); 0 turns it off; SV_TIME_ALL selects
- * every kernel) and clears what it recorded.  While it is on, one call in
- * `every` (>= 1; the first, then every every-th) records a hipEvent pair
- * around each selected kernel, on the call's `stream`; the last 256
- * recorded calls are kept.  Each pair costs a few microseconds of stream
- * time, which sampling spreads over `every` calls.
- * spec_verify_kernel_times() waits for the most recent recorded call and
- * writes, for up to max_kernels kernels, the mean elapsed milliseconds per
- * call over the recorded calls that launched the kernel (ms[i] belongs to
- * spec_verify_kernel_name(i); NaN for kernels not selected or not launched:
- * the staged form launches row_stats, accept, draw_sums and draw_pick in
- * one pass, or row_stats and draw_all (spec_verify_set_draw); with early
- * exit row_lead, accept_lead, rest and draw_pick,
- * or in the gathered form row_lead, accept_lead, row_stats, accept,
- * row_draft, draw_sums and draw_pick; the fused form fused_reset and
- * fused; spec_draft_sample sample_sums and sample_pick); it returns the number
- * of kernels, or -1 if the probe is off, no call was recorded or a HIP call
- * failed.
- * spec_verify_timing returns SV_ERR_SHAPE for every < 1.  The probe uses
- * one device: turn it off and on again after switching devices. */
-#define SV_TIME_ALL 0x1FFF
-sv_status_t spec_verify_timing(int32_t kernels, int32_t every);
-int32_t spec_verify_kernel_times(float *ms, int32_t max_kernels);
-const char *spec_verify_kernel_name(int32_t i);
-
-/* Benchmark tuning: approximate logits per row-pass segment and per draw
- * chunk (0 restores the automatic choice: 65536 and 8192 for batches that
- * fill the GPU, shorter -- down to 4096 and 1024 -- for small calls, so that
- * their passes still spread over the CUs).  The workspace size depends on
- * them, so query spec_verify_workspace_size() after a change.  Returns
- * SV_ERR_SHAPE for negative values. */
-sv_status_t spec_verify_set_geometry(int64_t seg_elems, int64_t chunk_elems);
-
-/* Form of the launch.  SV_MODE_STAGED: a kernel per step (row pass, accept
- * scan, draw chunk sums, pick; small one-pass calls join the last three,
- * see spec_verify_set_draw), each step published by a kernel boundary.
- * SV_MODE_FUSED: one persistent kernel (after a small kernel that clears its
- * counters) whose workgroups take row segments and draw chunks from a
- * device-side queue; sequence b's draw chunks are queued fused_lag
- * sequences after its rows (0 = chosen from the number of resident
- * workgroups).  It needs B <= 2048 and at most 256 draw chunks per row
- * (spec_verify returns SV_ERR_SHAPE otherwise); on MI355X it measures
- * slower than the staged form.  SV_MODE_AUTO (the default): staged.  Both
- * forms give identical results.  Returns SV_ERR_SHAPE for an unknown mode or fused_lag < 0. */
-enum { SV_MODE_AUTO = 0, SV_MODE_STAGED = 1, SV_MODE_FUSED = 2 };
-sv_status_t spec_verify_set_mode(int32_t mode, int32_t fused_lag);
-
-/* Early exit (staged form).  The pages' verify loop tests one position at a
- * time and stops at the first rejection, so the rows after it are never
- * needed.  With lead_positions = L > 0 the row pass first reads positions
- * 0..L-1 of every sequence and runs their accept tests; sequences with a
- * rejection there (or with k_b < L) are settled, and only the other
- * sequences' remaining rows are read.  Outside the gathered form the bonus
- * row (position k_b) of a sampling sequence is read by its draw alone, when
- * all k_b drafts are accepted: its row diagnostics are NaN, and a sampling
- * sequence is settled once its k_b drafted positions are.
- * L = 0 reads every row in one pass.
- * L = -1 (the default) chooses: L = 1 when all logit rows of the call
- * together hold at least 512 MiB, else 0 (the two extra launches cost more
- * than small batches can save).  The outputs do not depend on L, except
- * that the out_p/out_q and row diagnostics of spec_verify_probs are NaN for
- * rows that were not read.  Returns SV_ERR_SHAPE unless
- * -1 <= L <= SV_K_MAX + 1. */
-sv_status_t spec_verify_set_early_exit(int32_t lead_positions);
-
-/* Early exit outside the gathered form ends in two launches.  "rest"
- * streams the remaining rows and, beside them, makes the draws: the chunks
- * of the sequences the leading positions settled are interleaved with the
- * rows; each undecided sequence's accept scan runs lag_accept sequences
- * (blocks of rows) after its own rows, and its draw chunks lag_draw blocks
- * after them, each waiting (boundedly) until what it needs is written.
- * "draw_pick" redoes whatever a wait that ran out left (usually nothing)
- * and picks every emitted token.  Where a chunk is summed does not change
- * any output.  mode SV_QUEUE_OVERLAP (the default): as described;
- * SV_QUEUE_FINAL: every accept scan and chunk of that round in draw_pick;
- * SV_QUEUE_HANDOFF: the undecided sequences take the path of a wait that
- * runs out (they are redone in draw_pick; for tests).
- * lag_accept, lag_draw = 0 choose them from the number of resident
- * workgroups and the expected rows per sequence.  Returns SV_ERR_SHAPE for
- * an unknown mode or a negative lag. */
-enum { SV_QUEUE_OVERLAP = 0, SV_QUEUE_FINAL = 1, SV_QUEUE_HANDOFF = 2 };
-sv_status_t spec_verify_set_queue(int32_t mode, int32_t lag_accept, int32_t lag_draw);
-
-/* The draw of a one-pass call outside the gathered form (no early exit):
- * SV_DRAW_ONE: one launch, "draw_all" (sequences x chunks), in which every
- * workgroup runs its sequence's accept scan (only one of them writes its
- * outputs), sums its chunk, and the workgroup that sums a sequence's last
- * chunk picks the token; SV_DRAW_THREE: three launches, "accept",
- * "draw_sums" and "draw_pick".  SV_DRAW_AUTO (the default): one launch
- * while the draw's workgroups fit one round on the CUs (B * chunks <= 4 per
- * CU), else three.  Both give identical outputs.  Returns SV_ERR_SHAPE for
- * an unknown mode. */
-enum { SV_DRAW_AUTO = 0, SV_DRAW_ONE = 1, SV_DRAW_THREE = 2 };
-sv_status_t spec_verify_set_draw(int32_t mode);
 
 #ifdef __cplusplus
 }

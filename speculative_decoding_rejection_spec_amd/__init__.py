@@ -5,23 +5,75 @@ below take torch tensors that already live on one GPU, check that they have
 the layout the C call documents, and pass their pointers and the current HIP
 stream to the library.  All arithmetic of the verify step runs in the HIP
 kernels; torch is used for device memory and streams only.
+
+set_geometry / set_early_exit / set_queue / set_draw and timing() are test
+and benchmark options of this binding (csrc/sv_tuning.h): they are kept in
+the calling Python process and passed to the library with each call, which
+holds no such state itself.
 """
 from __future__ import annotations
 
 import ctypes
 
-from ._lib import (LIB_PATH, SV_BF16, SV_DRAW_AUTO, SV_DRAW_ONE, SV_DRAW_THREE, SV_F32, SV_K_MAX, SV_MODE_AUTO,
-                   SV_MODE_FUSED, SV_MODE_STAGED, SV_QUEUE_FINAL, SV_QUEUE_HANDOFF, SV_QUEUE_OVERLAP, SV_TIME_ALL,
-                   SpecVerifyError, check, lib)
+from ._lib import (LIB_PATH, SV_BF16, SV_DRAW_AUTO, SV_DRAW_ONE, SV_DRAW_THREE, SV_F32, SV_K_MAX, SV_NUM_KERNELS,
+                   SV_QUEUE_FINAL, SV_QUEUE_HANDOFF, SV_QUEUE_OVERLAP, SpecVerifyError, Tuning, check, lib)
 
 __all__ = [
     "spec_verify", "spec_verify_probs", "spec_verify_gathered", "spec_draft_sample",
     "spec_commit", "spec_adapt_k", "spec_ngram_draft",
     "spec_verify_workspace_size", "spec_verify_release",
-    "stream_probe", "timing", "kernel_times", "set_geometry", "set_mode", "set_early_exit", "set_queue", "set_draw", "SpecVerifyError",
-    "SV_F32", "SV_BF16", "SV_K_MAX", "SV_MODE_AUTO", "SV_MODE_STAGED", "SV_MODE_FUSED", "SV_QUEUE_OVERLAP",
+    "stream_probe", "timing", "kernel_times", "set_geometry", "set_early_exit", "set_queue", "set_draw",
+    "reset_options", "SpecVerifyError", "SV_F32", "SV_BF16", "SV_K_MAX", "SV_QUEUE_OVERLAP",
     "SV_QUEUE_FINAL", "SV_QUEUE_HANDOFF", "SV_DRAW_AUTO", "SV_DRAW_ONE", "SV_DRAW_THREE", "LIB_PATH", "lib",
 ]
+
+# ---- per-call options (csrc/sv_tuning.h), held by this binding ------------
+_DEFAULTS = dict(seg_elems=0, chunk_elems=0, lead=-1, queue_mode=SV_QUEUE_OVERLAP, lag_accept=0, lag_draw=0,
+                 draw_mode=SV_DRAW_AUTO)
+_OPTS = dict(_DEFAULTS)
+_TIMING = {"mask": 0, "every": 1, "seen": 0, "records": [], "free": []}
+_MAX_RECORDS = 256
+
+
+def _options_set() -> bool:
+    return _OPTS != _DEFAULTS
+
+
+def _tuning(record: bool):
+    """The sv_tuning_t for the next call (None: defaults, no timing), and the
+    timing record it fills, if any."""
+    rec = None
+    if record and _TIMING["mask"]:
+        if _TIMING["seen"] % _TIMING["every"] == 0:
+            rec = _timing_record()
+        _TIMING["seen"] += 1
+    if rec is None and not _options_set():
+        return None, None
+    t = Tuning(**_OPTS)
+    if rec is not None:
+        t.timed = _TIMING["mask"]
+        t.events = ctypes.cast(rec["events"], ctypes.c_void_p)
+        t.launched = ctypes.cast(ctypes.pointer(rec["launched"]), ctypes.c_void_p)
+    return t, rec
+
+
+def _timing_record():
+    ev = _TIMING["free"].pop() if _TIMING["free"] else None
+    if ev is None:
+        ev = (ctypes.c_void_p * (2 * SV_NUM_KERNELS))()
+        check(lib().spec_timing_events_create(2 * SV_NUM_KERNELS, ev), "spec_timing_events_create")
+    rec = {"events": ev, "launched": ctypes.c_uint32(0), "mask": _TIMING["mask"]}
+    recs = _TIMING["records"]
+    recs.append(rec)
+    if len(recs) > _MAX_RECORDS:
+        _TIMING["free"].append(recs.pop(0)["events"])
+    return rec
+
+
+def reset_options() -> None:
+    """Every per-call option back to the library's defaults (timing off)."""
+    _OPTS.update(_DEFAULTS)
+    timing(False)
 
 
 def _dtype_code(dtype) -> int:
@@ -103,11 +155,15 @@ def spec_verify(target_logits, draft_logits, draft_tokens, offsets, uniforms, te
         target_logits, draft_logits, draft_tokens, offsets, uniforms, temperature, k_uniform,
         out_tokens, out_n_accepted)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().spec_verify(
-        _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(offsets),
-        int(k_uniform), total, B, V, _dtype_code(target_logits.dtype), _ptr(uniforms),
-        _ptr(temperature), _ptr(out_tokens), _ptr(out_n_accepted), _ptr(workspace), ws_bytes,
-        _stream(dev, stream))
+    args = (_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(offsets),
+            int(k_uniform), total, B, V, _dtype_code(target_logits.dtype), _ptr(uniforms),
+            _ptr(temperature), _ptr(out_tokens), _ptr(out_n_accepted))
+    t, _ = _tuning(record=True)
+    if t is None:
+        st = lib().spec_verify(*args, _ptr(workspace), ws_bytes, _stream(dev, stream))
+    else:
+        st = lib().spec_verify_tuned(ctypes.byref(t), *args, None, None, None, None, _ptr(workspace), ws_bytes,
+                                     _stream(dev, stream))
     check(st, "spec_verify")
     return out_tokens, out_n_accepted
 
@@ -125,12 +181,13 @@ def spec_verify_probs(target_logits, draft_logits, draft_tokens, offsets, unifor
     row_max = torch.full((2 * total + B,), float("nan"), device=dev)
     row_sum = torch.full((2 * total + B,), float("nan"), device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().spec_verify_probs(
-        _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(offsets),
-        int(k_uniform), total, B, V, _dtype_code(target_logits.dtype), _ptr(uniforms),
-        _ptr(temperature), _ptr(out_tokens), _ptr(out_n), _ptr(out_p) if total else None,
-        _ptr(out_q) if total else None, _ptr(row_max), _ptr(row_sum), _ptr(workspace),
-        ws_bytes, _stream(dev, stream))
+    args = (_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(offsets),
+            int(k_uniform), total, B, V, _dtype_code(target_logits.dtype), _ptr(uniforms),
+            _ptr(temperature), _ptr(out_tokens), _ptr(out_n), _ptr(out_p) if total else None,
+            _ptr(out_q) if total else None, _ptr(row_max), _ptr(row_sum), _ptr(workspace),
+            ws_bytes, _stream(dev, stream))
+    t, _ = _tuning(record=True)
+    st = lib().spec_verify_probs(*args) if t is None else lib().spec_verify_tuned(ctypes.byref(t), *args)
     check(st, "spec_verify_probs")
     return dict(tokens=out_tokens, n=out_n, p=out_p, q=out_q, row_max=row_max, row_sumexp=row_sum)
 
@@ -154,11 +211,13 @@ def spec_verify_gathered(target_logits, draft_logits, draft_tokens, draft_probs,
     if out_emit_prob.numel() != B:
         raise ValueError(f"out_emit_prob must have {B} entries")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().spec_verify_gathered(
-        _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(draft_probs),
-        _ptr(offsets), int(k_uniform), total, B, V, _dtype_code(target_logits.dtype),
-        _ptr(uniforms), _ptr(temperature), _ptr(out_tokens), _ptr(out_n_accepted),
-        _ptr(out_emit_prob), _ptr(workspace), ws_bytes, _stream(dev, stream))
+    args = (_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(draft_probs),
+            _ptr(offsets), int(k_uniform), total, B, V, _dtype_code(target_logits.dtype),
+            _ptr(uniforms), _ptr(temperature), _ptr(out_tokens), _ptr(out_n_accepted),
+            _ptr(out_emit_prob), _ptr(workspace), ws_bytes, _stream(dev, stream))
+    t, _ = _tuning(record=True)
+    st = lib().spec_verify_gathered(*args) if t is None else lib().spec_verify_gathered_tuned(ctypes.byref(t),
+                                                                                              *args)
     check(st, "spec_verify_gathered")
     return out_tokens, out_n_accepted, out_emit_prob
 
@@ -185,9 +244,10 @@ def spec_draft_sample(logits, temperature, uniforms, *, out_tokens=None, out_pro
     if out_tokens.numel() != rows or out_probs.numel() != rows:
         raise ValueError("out_tokens / out_probs have the wrong size")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().spec_draft_sample(_ptr(logits), rows, V, _dtype_code(logits.dtype), _ptr(temperature),
-                                 _ptr(uniforms), _ptr(out_tokens), _ptr(out_probs), _ptr(workspace),
-                                 ws_bytes, _stream(dev, stream))
+    args = (_ptr(logits), rows, V, _dtype_code(logits.dtype), _ptr(temperature), _ptr(uniforms),
+            _ptr(out_tokens), _ptr(out_probs), _ptr(workspace), ws_bytes, _stream(dev, stream))
+    t, _ = _tuning(record=True)
+    st = lib().spec_draft_sample(*args) if t is None else lib().spec_draft_sample_tuned(ctypes.byref(t), *args)
     check(st, "spec_draft_sample")
     return out_tokens, out_probs
 
@@ -276,39 +336,51 @@ def spec_ngram_draft(seq_tokens, seq_len, *, ngram_max: int = 3, ngram_min: int 
 
 
 def spec_verify_workspace_size(B: int, total_draft: int, V: int, dtype) -> int:
+    """Workspace bytes of a call of these sizes under the options currently
+    set in this binding (the library's default size when none is set)."""
     code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
-    return int(lib().spec_verify_workspace_size(B, total_draft, V, code))
+    if not _options_set():
+        return int(lib().spec_verify_workspace_size(B, total_draft, V, code))
+    t = Tuning(**_OPTS)
+    return int(lib().spec_verify_workspace_size_tuned(ctypes.byref(t), B, total_draft, V, code))
 
 
 def spec_verify_release() -> None:
     lib().spec_verify_release()
 
 
+def _set(**kw) -> None:
+    new = dict(_OPTS, **kw)
+    t = Tuning(**new)
+    # the library validates the fields: a tuned size query of 0 for a tiny
+    # valid problem means a field is out of range
+    if lib().spec_verify_workspace_size_tuned(ctypes.byref(t), 1, 0, 8, SV_F32) == 0:
+        raise SpecVerifyError(-2, f"options {kw}")
+    _OPTS.update(kw)
+
+
 def set_geometry(seg_elems: int = 0, chunk_elems: int = 0) -> None:
-    check(lib().spec_verify_set_geometry(seg_elems, chunk_elems), "spec_verify_set_geometry")
+    """Approximate logits per row-pass segment and per draw chunk (0 =
+    automatic) for this process's later calls."""
+    _set(seg_elems=int(seg_elems), chunk_elems=int(chunk_elems))
 
 
 def set_early_exit(lead_positions: int = -1) -> None:
     """Leading positions every sequence reads before the rest (0 = off,
     -1 = automatic by batch size)."""
-    check(lib().spec_verify_set_early_exit(int(lead_positions)), "spec_verify_set_early_exit")
+    _set(lead=int(lead_positions))
 
 
 def set_queue(mode: int = SV_QUEUE_OVERLAP, lag_accept: int = 0, lag_draw: int = 0) -> None:
     """Where early exit's second-round accept scans and draw chunks run, and
     their lags in sequences (0 = automatic); outputs do not change."""
-    check(lib().spec_verify_set_queue(int(mode), int(lag_accept), int(lag_draw)), "spec_verify_set_queue")
+    _set(queue_mode=int(mode), lag_accept=int(lag_accept), lag_draw=int(lag_draw))
 
 
 def set_draw(mode: int = SV_DRAW_AUTO) -> None:
     """One-pass draw as one launch (SV_DRAW_ONE), three (SV_DRAW_THREE) or
     chosen by size (SV_DRAW_AUTO); outputs do not change."""
-    check(lib().spec_verify_set_draw(int(mode)), "spec_verify_set_draw")
-
-
-def set_mode(mode: int = SV_MODE_AUTO, fused_lag: int = 0) -> None:
-    """Staged (four kernels), fused (one persistent kernel) or auto."""
-    check(lib().spec_verify_set_mode(int(mode), int(fused_lag)), "spec_verify_set_mode")
+    _set(draw_mode=int(mode))
 
 
 def stream_probe(data, seg_bytes: int = 163840, out=None, stream=None):
@@ -328,35 +400,48 @@ def stream_probe(data, seg_bytes: int = 163840, out=None, stream=None):
     return out
 
 
+def kernel_names() -> list:
+    return [lib().spec_verify_kernel_name(i).decode() for i in range(SV_NUM_KERNELS)]
+
+
 def timing(enable=True, every: int = 1) -> None:
-    """Turns the kernel timing probe on for every kernel (True), for the named
-    kernels (an iterable of names from kernel_times()), or off (False);
-    one call in `every` is recorded."""
+    """Records HIP events around every kernel (True), the named kernels (an
+    iterable of names from kernel_names()), or none (False) of one verify
+    call in `every`; kernel_times() reports them.  Turning it on or off
+    clears what was recorded."""
+    names = kernel_names()
     if enable is True:
-        mask = SV_TIME_ALL
+        mask = (1 << SV_NUM_KERNELS) - 1
     elif not enable:
         mask = 0
     else:
-        names = list(enable)
-        mask = 0
-        for i in range(16):
-            nm = lib().spec_verify_kernel_name(i)
-            if nm is None:
-                break
-            if nm.decode() in names:
-                mask |= 1 << i
-                names.remove(nm.decode())
-        if names:
-            raise ValueError(f"unknown kernels {names}")
-    check(lib().spec_verify_timing(mask, int(every)), "spec_verify_timing")
+        want = list(enable)
+        unknown = [n for n in want if n not in names]
+        if unknown:
+            raise ValueError(f"unknown kernels {unknown}")
+        mask = sum(1 << names.index(n) for n in set(want))
+    if int(every) < 1:
+        raise ValueError("every must be >= 1")
+    _TIMING["free"].extend(r["events"] for r in _TIMING["records"])
+    _TIMING.update(mask=mask, every=int(every), seen=0, records=[])
 
 
 def kernel_times() -> dict:
-    """Per-kernel milliseconds of the most recent call made with timing on
-    (waits for that call's events)."""
-    buf = (ctypes.c_float * 16)()
-    n = lib().spec_verify_kernel_times(buf, 16)
-    if n < 0:
-        raise RuntimeError("no timed spec_verify call to report")
-    return {lib().spec_verify_kernel_name(i).decode(): float(buf[i]) for i in range(n)
-            if buf[i] == buf[i]}
+    """Mean milliseconds per call of every timed kernel over the recorded
+    calls that launched it (waits for their events); kernels a call did not
+    launch are absent."""
+    recs = _TIMING["records"]
+    if not recs:
+        raise RuntimeError("no timed call to report")
+    names = kernel_names()
+    sums, counts = {}, {}
+    ms = ctypes.c_float(0.0)
+    for rec in recs:
+        done = rec["launched"].value & rec["mask"]
+        for i in range(SV_NUM_KERNELS):
+            if (done >> i) & 1:
+                check(lib().spec_timing_elapsed(rec["events"][2 * i], rec["events"][2 * i + 1], ctypes.byref(ms)),
+                      "spec_timing_elapsed")
+                sums[names[i]] = sums.get(names[i], 0.0) + ms.value
+                counts[names[i]] = counts.get(names[i], 0) + 1
+    return {k: sums[k] / counts[k] for k in sums}

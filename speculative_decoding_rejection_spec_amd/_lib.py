@@ -1,8 +1,9 @@
 """ctypes binding of libspecverify (argument marshalling only).
 
 Every step of the verify path runs in the HIP kernels behind the C ABI
-declared in include/specverify.h; this module only loads the library and
-passes pointers, sizes and the stream.  There is no fallback: if the library
+declared in include/specverify.h (plus the test and benchmark hooks of
+csrc/sv_tuning.h); this module only loads the library and passes pointers,
+sizes and the stream.  There is no fallback: if the library
 is not built, loading it raises.
 """
 from __future__ import annotations
@@ -15,15 +16,24 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 
 SV_F32, SV_BF16 = 0, 1
 SV_K_MAX = 63
-SV_TIME_ALL = 0x1FFF
-SV_MODE_AUTO, SV_MODE_STAGED, SV_MODE_FUSED = 0, 1, 2
+SV_NUM_KERNELS = 11
 SV_QUEUE_OVERLAP, SV_QUEUE_FINAL, SV_QUEUE_HANDOFF = 0, 1, 2
 SV_DRAW_AUTO, SV_DRAW_ONE, SV_DRAW_THREE = 0, 1, 2
 STATUS = {0: "SV_OK", -1: "SV_ERR_NULL", -2: "SV_ERR_SHAPE", -3: "SV_ERR_DTYPE",
           -4: "SV_ERR_ALIGN", -5: "SV_ERR_WORKSPACE", -6: "SV_ERR_HIP"}
 
-# Every symbol include/specverify.h declares, with its ctypes signature.
-_P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_P, _I32, _I64, _SZ, _U32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_uint32
+
+
+class Tuning(ctypes.Structure):
+    """sv_tuning_t of csrc/sv_tuning.h (per-call test and benchmark options)."""
+    _fields_ = [("seg_elems", _I64), ("chunk_elems", _I64), ("lead", _I32), ("queue_mode", _I32),
+                ("lag_accept", _I32), ("lag_draw", _I32), ("draw_mode", _I32), ("timed", _U32),
+                ("events", _P), ("launched", _P)]
+
+
+# Every symbol include/specverify.h declares (the product interface), with its
+# ctypes signature.
 SIGNATURES = {
     "spec_verify_workspace_size": (_SZ, [_I32, _I64, _I64, _I32]),
     "spec_verify": (_I32, [_P, _P, _P, _P, _I32, _I64, _I32, _I64, _I32, _P, _P, _P, _P,
@@ -39,15 +49,24 @@ SIGNATURES = {
     "spec_ngram_draft": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "spec_verify_status_string": (ctypes.c_char_p, [_I32]),
     "spec_verify_release": (None, []),
-    "spec_verify_timing": (_I32, [_I32, _I32]),
-    "spec_verify_kernel_times": (_I32, [_P, _I32]),
+}
+
+# The test and benchmark hooks of csrc/sv_tuning.h (exported, not part of
+# the product interface).
+_TP = ctypes.POINTER(Tuning)
+TUNING_SIGNATURES = {
+    "spec_tuning_defaults": (None, [_TP]),
+    "spec_verify_workspace_size_tuned": (_SZ, [_TP, _I32, _I64, _I64, _I32]),
+    "spec_verify_tuned": (_I32, [_TP, _P, _P, _P, _P, _I32, _I64, _I32, _I64, _I32, _P, _P, _P, _P,
+                                 _P, _P, _P, _P, _P, _SZ, _P]),
+    "spec_verify_gathered_tuned": (_I32, [_TP, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I64, _I32, _P, _P,
+                                          _P, _P, _P, _P, _SZ, _P]),
+    "spec_draft_sample_tuned": (_I32, [_TP, _P, _I32, _I64, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "spec_verify_kernel_name": (ctypes.c_char_p, [_I32]),
-    "spec_verify_set_geometry": (_I32, [_I64, _I64]),
-    "spec_verify_set_queue": (_I32, [_I32, _I32, _I32]),
-    "spec_verify_set_draw": (_I32, [_I32]),
+    "spec_timing_events_create": (_I32, [_I32, _P]),
+    "spec_timing_elapsed": (_I32, [_P, _P, ctypes.POINTER(ctypes.c_float)]),
+    "spec_timing_events_destroy": (_I32, [_I32, _P]),
     "spec_stream_probe": (_I32, [_P, _I64, _I64, _P, _P]),
-    "spec_verify_set_mode": (_I32, [_I32, _I32]),
-    "spec_verify_set_early_exit": (_I32, [_I32]),
 }
 
 _lib = None
@@ -73,7 +92,7 @@ def lib() -> ctypes.CDLL:
         # would launch onto streams its runtime does not know.
         import torch  # noqa: F401
         handle = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in SIGNATURES.items():
+        for name, (res, args) in {**SIGNATURES, **TUNING_SIGNATURES}.items():
             fn = getattr(handle, name)
             fn.restype = res
             fn.argtypes = args

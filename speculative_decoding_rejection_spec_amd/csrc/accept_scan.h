@@ -1,5 +1,5 @@
 // accept_scan.h -- the accept scan of one sequence, run by one wave64;
-// shared by the staged accept kernel and the fused kernel.
+// shared by the accept kernels, the second round and the one-launch draw.
 //
 // Lane i (i <= k_b) owns position i of its sequence.  It merges the segment
 // statistics of target row i (and draft row i) into the row maximum and the
@@ -316,7 +316,7 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
     if (!emit) return !greedy;
 
     // Slot n of a sampling sequence is written by the draw alone: in the
-    // fused form the draw runs in another workgroup, possibly on another XCD,
+    // one-launch forms the draw runs in another workgroup, possibly on another XCD,
     // and two plain stores to one slot from different L2s would land in the
     // order the caches happen to write back.
     if (lane <= k && (lane != n || greedy)) p.out_tokens[trow] = lane < n ? x : (lane == n ? rt.arg : -1);

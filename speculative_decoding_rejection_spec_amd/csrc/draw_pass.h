@@ -1,5 +1,5 @@
 // draw_pass.h -- the emitted token of every sampling sequence, in fp64;
-// shared by the staged draw kernels and the fused kernel.
+// shared by the staged draw kernels, the second round and the one-launch draw.
 //
 // After the first rejection at position n the token is drawn from
 // r = max(0, p_n - q_n) / Z, Z = sum_v max(0, p_n(v) - q_n(v)) (page "投机解码",
@@ -52,7 +52,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr double kLog2e = 0x1.71547652b82fep+0;
 constexpr double kDegenerateZ = 1e-9;            // residual mass treated as empty
 constexpr double kBand = 3e-5;                   // classification band (log2 units)
-constexpr double kMinY = -1021.0 * 256.0;        // weights stay normal doubles (>= 2^-1021)
+// Lower clamp of Y.  At exactly -1023 * 256 the table trick below yields +0.0
+// (high word 0x3ff00000 - (1023 << 20) = 0, low word 0, r = 0), so a masked
+// logit (z = -inf, Y = -inf) and any weight below 2^-1023 get exactly zero
+// mass; Y in (-1023, -1022) * 256 gives a value below 2^-1022 (no weight
+// that small can move a fp64 sum that holds the reference's weight 1).
+constexpr double kMinY = -1023.0 * 256.0;
 constexpr int kSlots = kWaves * kWaveCap;        // band entries per chunk (32)
 constexpr int kBufferDword3 = 0x00020000;        // raw buffer descriptor word 3 (gfx9 family)
 
@@ -138,7 +143,7 @@ __device__ __forceinline__ void load_table(TabEntry* tbl, int nthreads) {
     }
 }
 
-// 2^(Y/256) in fp64 for Y <= 0 (Y is clamped at kMinY).  Y = n + r with
+// 2^(Y/256) in fp64 for Y <= 0 (Y is clamped at kMinY, where it is 0).  Y = n + r with
 // n = round(Y) (the 1.5 * 2^52 shifter: after the add the low 32 bits of the
 // double hold n in two's complement) and |r| <= 1/2, so
 // 2^(Y/256) = 2^(n>>8) 2^((n&255)/256) e^x with x = r ln2/256, |x| <= ln2/512;
@@ -452,6 +457,9 @@ __device__ __forceinline__ void draw_chunk(const Problem& p, const Plan& plan, c
                 st_co<kCo>(&dst[1], lds.wlist[wv][e][1]);
             }
         }
+        // A caller that sums another chunk next would otherwise let waves
+        // 1-3 refill their lists while wave 0 still copies them out.
+        __syncthreads();
     }
 }
 

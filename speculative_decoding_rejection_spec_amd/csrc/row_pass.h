@@ -1,6 +1,5 @@
 // row_pass.h -- the streaming read of one segment of one logit row (pass 1 of
-// the verify step), shared by the staged row_stats kernel and the fused
-// kernel.
+// the verify step), shared by the row-pass kernels and the second round.
 //
 // The accept tests and the bonus draw need the tempered softmax
 // p = softmax(z / T) of each target row and q of each draft row (page

@@ -190,6 +190,15 @@ __global__ __launch_bounds__(kThreads) void rest_draws_kernel(Problem p, Plan pl
 
 }  // namespace
 
+hipError_t rest_blocks_per_cu(int32_t dtype, int32_t* blocks) {
+    int n = 0;
+    const hipError_t e = dtype == SV_BF16
+        ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rest_draws_kernel<SV_BF16>, kThreads, 0)
+        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rest_draws_kernel<SV_F32>, kThreads, 0);
+    *blocks = n;
+    return e;
+}
+
 hipError_t launch_rest_draws(const Problem& p, const Plan& plan, hipStream_t s) {
     const int64_t blocks = (2 * p.total + p.B) * static_cast<int64_t>(plan.nseg) +
                            static_cast<int64_t>(p.B) * (1 + plan.nchunk);

@@ -1,11 +1,13 @@
 // specverify.hip -- host side of the libspecverify C ABI: argument checks,
-// work geometry, workspace, kernel launches and the benchmark timing probe.
-// The operation and every argument are documented in include/specverify.h.
+// work geometry, workspace, kernel launches, and the per-call tuning hooks
+// of sv_tuning.h.  The operation and every argument are documented in
+// include/specverify.h.
 #include <stdlib.h>
 
 #include <mutex>
 
 #include "sv_internal.h"
+#include "sv_tuning.h"
 
 namespace {
 using namespace sv;
@@ -23,18 +25,45 @@ constexpr int64_t kDefaultChunkElems = 8192;  // draw chunk length before roundi
 constexpr int32_t kAutoLead = -1;
 constexpr int64_t kAutoLeadBytes = 512ll << 20;
 constexpr int kMaxDevices = 64;
-constexpr int kNumKernels = 13;
-enum { kKRowStats, kKAccept, kKDrawSums, kKDrawPick, kKFusedReset, kKFused, kKRowLead, kKAcceptLead,
-       kKRowDraft, kKRest, kKDrawAll, kKSampleSums, kKSamplePick };
+enum { kKRowStats, kKAccept, kKDrawSums, kKDrawPick, kKRowLead, kKAcceptLead, kKRowDraft, kKRest, kKDrawAll,
+       kKSampleSums, kKSamplePick, kNumKernels };
+static_assert(kNumKernels == SV_NUM_KERNELS, "kernel count");
 
-const char* const kKernelNames[kNumKernels] = {"row_stats", "accept",      "draw_sums",   "draw_pick",
-                                               "fused_reset", "fused",     "row_lead",    "accept_lead",
-                                               "row_draft", "rest",        "draw_all",    "sample_sums",
-                                               "sample_pick"};
+const char* const kKernelNames[kNumKernels] = {"row_stats", "accept",   "draw_sums", "draw_pick",
+                                               "row_lead",  "accept_lead", "row_draft", "rest",
+                                               "draw_all",  "sample_sums", "sample_pick"};
 
-std::mutex g_mutex;
-int64_t g_seg_elems = 0;                     // 0: automatic (auto_lengths)
-int64_t g_chunk_elems = 0;
+// One call's tuning (sv_tuning.h), resolved: every field in range.
+struct Tuning {
+    int64_t seg_elems = 0, chunk_elems = 0;   // 0: automatic (auto_lengths)
+    int32_t lead = kAutoLead;
+    int32_t queue_mode = SV_QUEUE_OVERLAP;
+    int32_t lag_a = 0, lag_c = 0;             // 0: chosen from the resident grid
+    int32_t draw_mode = SV_DRAW_AUTO;
+    uint32_t timed = 0;                       // kernels whose events are recorded
+    hipEvent_t* events = nullptr;
+    uint32_t* launched = nullptr;
+};
+
+bool resolve(const sv_tuning_t* t, Tuning& r) {
+    r = Tuning{};
+    if (!t) return true;
+    if (t->seg_elems < 0 || t->chunk_elems < 0 || t->lead < kAutoLead || t->lead > SV_K_MAX + 1 ||
+        t->queue_mode < SV_QUEUE_OVERLAP || t->queue_mode > SV_QUEUE_HANDOFF || t->lag_accept < 0 ||
+        t->lag_draw < 0 || t->draw_mode < SV_DRAW_AUTO || t->draw_mode > SV_DRAW_THREE)
+        return false;
+    r.seg_elems = t->seg_elems;
+    r.chunk_elems = t->chunk_elems;
+    r.lead = t->lead;
+    r.queue_mode = t->queue_mode;
+    r.lag_a = t->lag_accept;
+    r.lag_c = t->lag_draw;
+    r.draw_mode = t->draw_mode;
+    r.timed = t->timed;
+    r.events = t->events;
+    r.launched = t->launched;
+    return true;
+}
 
 // Automatic segment and chunk lengths: the defaults suit batches that fill
 // the GPU many times over (256 sequences of k = 8, V = 152064: 8704 row
@@ -44,20 +73,14 @@ int64_t g_chunk_elems = 0;
 // kMinChunk logits).
 constexpr int64_t kRowBlocks = 2048, kDrawBlocks = 1024;
 constexpr int64_t kMinSeg = 8192, kMinChunk = 1024;
-void auto_lengths(int32_t B, int64_t total, int64_t V, int64_t* seg, int64_t* chunk) {
+void auto_lengths(int32_t B, int64_t total, int64_t V, const Tuning& tu, int64_t* seg, int64_t* chunk) {
     const int64_t rows = 2 * total + B;
     int64_t s = rows * V / kRowBlocks, c = static_cast<int64_t>(B) * V / kDrawBlocks;
     s = s < kMinSeg ? kMinSeg : (s > kDefaultSegElems ? kDefaultSegElems : s);
     c = c < kMinChunk ? kMinChunk : (c > kDefaultChunkElems ? kDefaultChunkElems : c);
-    *seg = g_seg_elems ? g_seg_elems : s;
-    *chunk = g_chunk_elems ? g_chunk_elems : c;
+    *seg = tu.seg_elems ? tu.seg_elems : s;
+    *chunk = tu.chunk_elems ? tu.chunk_elems : c;
 }
-int32_t g_mode = SV_MODE_AUTO;
-int32_t g_fused_lag = 0;                     // 0: chosen from the resident grid
-int32_t g_lead = kAutoLead;                  // early exit: leading positions read first (0: off)
-int32_t g_queue_mode = SV_QUEUE_OVERLAP;
-int32_t g_lag_a = 0, g_lag_c = 0;            // 0: chosen from the resident grid
-int32_t g_draw_mode = SV_DRAW_AUTO;
 // One pass: the draw runs as one launch (draw_all) while its workgroups
 // (sequences x chunks) fit one round on the CUs, counted at this many per
 // CU; a larger draw takes three launches (accept, draw_sums, draw_pick),
@@ -65,44 +88,49 @@ int32_t g_draw_mode = SV_DRAW_AUTO;
 // a sequence last do its pick, and with several rounds in flight those
 // land on whichever XCD already lags, which then lags further.
 constexpr int kDrawAllWgsPerCu = 4;
-constexpr int kRestWgsPerCu = 5;             // resident second-round workgroups per CU (its register count)
 
-hipError_t device_cus(int* cus) {
-    static int cached[kMaxDevices] = {};
+// Per-device facts, queried once: compute units, and second-round
+// workgroups a compute unit holds at once (its register count decides).
+std::mutex g_mutex;                          // guards the caches and the owned workspace
+struct DeviceInfo {
+    int cus = 0;
+    int rest_per_cu[2] = {0, 0};             // by dtype
+};
+DeviceInfo g_dev[kMaxDevices];
+
+hipError_t device_info(int32_t dtype, int* cus, int* rest_per_cu) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    if (!cached[dev]) {
-        e = hipDeviceGetAttribute(&cached[dev], hipDeviceAttributeMultiprocessorCount, dev);
+    std::lock_guard<std::mutex> lock(g_mutex);
+    DeviceInfo& d = g_dev[dev];
+    if (!d.cus) {
+        e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
     }
-    *cus = cached[dev];
+    const int di = dtype == SV_BF16 ? 1 : 0;
+    if (!d.rest_per_cu[di]) {
+        int32_t n = 0;
+        e = rest_blocks_per_cu(dtype, &n);
+        if (e != hipSuccess) return e;
+        d.rest_per_cu[di] = n > 0 ? n : 1;
+    }
+    *cus = d.cus;
+    *rest_per_cu = d.rest_per_cu[di];
     return hipSuccess;
 }
 
-int32_t effective_lead(int64_t B, int64_t total, int64_t V, sv_dtype_t dtype) {
-    if (g_mode == SV_MODE_FUSED) return 0;      // the fused form reads every row
-    if (g_lead != kAutoLead) return g_lead;
+int32_t effective_lead(int64_t B, int64_t total, int64_t V, sv_dtype_t dtype, const Tuning& tu) {
+    if (tu.lead != kAutoLead) return tu.lead;
     if (total == 0) return 0;                    // only bonus rows: nothing to skip
     const int64_t bytes = (2 * total + B) * V * (dtype == SV_BF16 ? 2 : 4);
     return bytes >= kAutoLeadBytes ? 1 : 0;
 }
-constexpr double kLagFactor = 1.5;           // resident grids of items between rows and draw
 
 // Library-owned workspace, one grow-only buffer per device.
 void* g_ws[kMaxDevices] = {};
 size_t g_ws_bytes[kMaxDevices] = {};
-
-// Timing probe state: a ring of event pairs for the last kTimedCalls calls.
-constexpr int kTimedCalls = 256;
-uint32_t g_timing = 0;                // bit i: time kernel i
-int32_t g_timing_every = 1;           // record one call in this many
-int64_t g_timing_seen = 0;            // calls made since the probe was enabled
-int64_t g_timed_calls = 0;            // calls recorded since the probe was enabled
-int g_timing_device = -1;
-hipEvent_t g_ev[kTimedCalls][2 * kNumKernels] = {};
-uint32_t g_ev_mask[kTimedCalls] = {};        // kernels recorded in each call
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -110,7 +138,7 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 struct Geometry {
     int32_t nseg, nchunk;
     int64_t seg_len, chunk_len;
-    size_t off_seg, off_task, off_csum, off_band_n, off_band_w, off_xlogit, off_ctr, off_done, off_sched,
+    size_t off_seg, off_task, off_csum, off_band_n, off_band_w, off_xlogit, off_done, off_sched,
         off_blk_ctr, off_blk_seq, off_dlist, off_dlist_n, off_nbuf, off_early, off_early_n, off_aband, off_picked, bytes;
 };
 
@@ -148,8 +176,6 @@ bool make_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dtype, int64_
     off = align256(off + sizeof(double) * 2 * kWaves * kWaveCap * static_cast<size_t>(B) * g.nchunk);
     g.off_xlogit = off;
     off = align256(off + sizeof(float) * static_cast<size_t>(rows));
-    g.off_ctr = off;
-    off = align256(off + sizeof(uint32_t) * static_cast<size_t>(fused_counter_words(B)));
     g.off_done = off;
     off = align256(off + sizeof(int32_t) * static_cast<size_t>(B));
     g.off_sched = off;
@@ -206,6 +232,7 @@ sv_status_t check_args(const void* target, const void* draft, const int32_t* tok
 sv_status_t owned_workspace(size_t bytes, void** out) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SV_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_mutex);
     if (g_ws_bytes[dev] < bytes) {
         if (g_ws[dev]) {
             if (hipFree(g_ws[dev]) != hipSuccess) return SV_ERR_HIP;   // waits for the device
@@ -220,15 +247,25 @@ sv_status_t owned_workspace(size_t bytes, void** out) {
     return SV_OK;
 }
 
+size_t workspace_bytes_for(int32_t B, int64_t total, int64_t V, sv_dtype_t dtype, const Tuning& tu) {
+    if (B < 0 || total < 0 || V < 1 || V > 0x7FFFFFFFll) return 0;
+    if (dtype != SV_F32 && dtype != SV_BF16) return 0;
+    Geometry g;
+    int64_t seg_elems, chunk_elems;
+    auto_lengths(B, total, V, tu, &seg_elems, &chunk_elems);
+    if (!make_geometry(B, total, V, dtype, seg_elems, chunk_elems, g)) return 0;
+    return g.bytes;
+}
+
 // sample: the drafter's sampling step (spec_draft_sample), k = 0 for every
 // row: two launches of its own (sample.hip) instead of the verify's.
 sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipStream_t stream,
-                bool sample = false) {
+                const Tuning& tu, bool sample = false) {
+    if (tu.launched) *tu.launched = 0u;
     if (p.B == 0) return SV_OK;
-    std::lock_guard<std::mutex> lock(g_mutex);
     Geometry g;
     int64_t seg_elems, chunk_elems;
-    auto_lengths(p.B, p.total, p.V, &seg_elems, &chunk_elems);
+    auto_lengths(p.B, p.total, p.V, tu, &seg_elems, &chunk_elems);
     if (!make_geometry(p.B, p.total, p.V, static_cast<sv_dtype_t>(p.dtype), seg_elems, chunk_elems, g))
         return SV_ERR_SHAPE;
     if (workspace) {
@@ -250,7 +287,6 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     plan.band_n = reinterpret_cast<int32_t*>(ws + g.off_band_n);
     plan.band_w = reinterpret_cast<double*>(ws + g.off_band_w);
     plan.xlogit = reinterpret_cast<float*>(ws + g.off_xlogit);
-    plan.ctr = reinterpret_cast<uint32_t*>(ws + g.off_ctr);
     plan.done = reinterpret_cast<int32_t*>(ws + g.off_done);
     plan.sched = reinterpret_cast<RestItem*>(ws + g.off_sched);
     plan.blk_ctr = reinterpret_cast<uint64_t*>(ws + g.off_blk_ctr);
@@ -261,166 +297,98 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     plan.early_n = reinterpret_cast<uint32_t*>(ws + g.off_early_n);
     plan.aband = reinterpret_cast<int32_t*>(ws + g.off_aband);
     plan.picked = reinterpret_cast<uint32_t*>(ws + g.off_picked);
-    plan.queue_mode = g_queue_mode;
+    plan.queue_mode = tu.queue_mode;
     Problem pr = p;
     if (!pr.out_n) pr.out_n = reinterpret_cast<int32_t*>(ws + g.off_nbuf);
 
-    // The fused form needs the schedule prefix and the pick's chunk masses
-    // in LDS, and an item count below 2^31.
-    const int64_t max_items = (2 * p.total + p.B) * static_cast<int64_t>(g.nseg) +
-                              static_cast<int64_t>(p.B) * g.nchunk;
-    const bool fused_fits = p.B <= kFusedMaxB && g.nchunk <= kFusedMaxChunks && max_items < (1ll << 31);
-    // The fused form measured slower than the staged one on MI355X (see
-    // fused.hip), so it runs only when asked for.
-    // The gathered form reads draft rows after the accept scans, which only
-    // the staged form does.
-    const bool fused = g_mode == SV_MODE_FUSED && !p.draft_probs && !sample;
-    if (fused && !fused_fits) return SV_ERR_SHAPE;
-    plan.lead = fused ? 0 : effective_lead(p.B, p.total, p.V, static_cast<sv_dtype_t>(p.dtype));
-    if (device_cus(&plan.cus) != hipSuccess) return SV_ERR_HIP;
+    plan.lead = sample ? 0 : effective_lead(p.B, p.total, p.V, static_cast<sv_dtype_t>(p.dtype), tu);
+    int rest_per_cu = 1;
+    if (device_info(p.dtype, &plan.cus, &rest_per_cu) != hipSuccess) return SV_ERR_HIP;
     plan.lag_a = plan.lag_c = 1 << 30;             // no accept or draw items in the schedule
     plan.queued = plan.lead > 0 && !p.draft_probs;
     if (plan.queued) {
-        if (g_lag_a > 0) {
-            plan.lag_a = g_lag_a;
-            plan.lag_c = g_lag_c > g_lag_a ? g_lag_c : g_lag_a;
+        if (tu.lag_a > 0) {
+            plan.lag_a = tu.lag_a;
+            plan.lag_c = tu.lag_c > tu.lag_a ? tu.lag_c : tu.lag_a;
         } else {
             // An item waiting for what it needs holds its CU slot, so items
             // start well after their rows: the accept item about 1.4 resident
             // grids of row segments later, the draw items about 2.3 (measured
             // on MI355X; shorter lags wait more than they overlap).
-            const double window = static_cast<double>(plan.cus) * kRestWgsPerCu;
+            const double window = static_cast<double>(plan.cus) * rest_per_cu;
             double per_block = (2.0 * static_cast<double>(p.total) / p.B - 2.0 * plan.lead + 1.0) * g.nseg;
             if (per_block < g.nseg) per_block = g.nseg;
             plan.lag_a = static_cast<int32_t>(1.4 * window / per_block) + 1;
             plan.lag_c = static_cast<int32_t>(2.3 * window / per_block) + 2;
         }
     }
-    Fused f{};
-    if (fused) {
-        if (fused_grid(p.dtype, &f.blocks) != hipSuccess) return SV_ERR_HIP;
-        if (g_fused_lag > 0) {
-            f.lag = g_fused_lag;
-        } else {
-            const double per_step = g.nseg * (2.0 * p.total / p.B + 1.0) + g.nchunk;
-            f.lag = static_cast<int32_t>(kLagFactor * f.blocks / per_step + 1.0);
-        }
-        if (f.lag > p.B) f.lag = p.B;
-        if (f.lag < 1) f.lag = 1;
-    }
 
-    hipEvent_t* ev = nullptr;
-    if (g_timing && (g_timing_seen++ % g_timing_every) == 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess) return SV_ERR_HIP;
-        if (g_timing_device != dev) {
-            for (auto& call : g_ev)
-                for (auto& e : call) {
-                    if (e) (void)hipEventDestroy(e);
-                    e = nullptr;
-                }
-            for (auto& call : g_ev)
-                for (auto& e : call)
-                    if (hipEventCreate(&e) != hipSuccess) return SV_ERR_HIP;
-            g_timing_device = dev;
-            g_timed_calls = 0;
-        }
-        ev = g_ev[g_timed_calls % kTimedCalls];
-    }
     uint32_t recorded = 0;
     auto launch = [&](int i, auto&& fn) -> bool {
-        const bool timed = ev && ((g_timing >> i) & 1u);
-        if (timed && hipEventRecord(ev[2 * i], stream) != hipSuccess) return false;
+        hipEvent_t* ev = ((tu.timed >> i) & 1u) ? tu.events : nullptr;
+        if (ev && hipEventRecord(ev[2 * i], stream) != hipSuccess) return false;
         if (fn() != hipSuccess) return false;
-        if (timed && hipEventRecord(ev[2 * i + 1], stream) != hipSuccess) return false;
-        if (timed) recorded |= 1u << i;
+        if (ev && hipEventRecord(ev[2 * i + 1], stream) != hipSuccess) return false;
+        recorded |= 1u << i;
         return true;
+    };
+    auto finish = [&](bool ok) {
+        if (tu.launched) *tu.launched = recorded;
+        return ok ? SV_OK : SV_ERR_HIP;
     };
     bool ok;
     if (sample) {
         ok = launch(kKSampleSums, [&] { return launch_sample_sums(pr, plan, stream); }) &&
              launch(kKSamplePick, [&] { return launch_sample_pick(pr, plan, stream); });
-    } else if (fused) {
-        ok = launch(kKFusedReset, [&] { return launch_fused_reset(pr, plan, stream); }) &&
-             launch(kKFused, [&] { return launch_fused(pr, plan, f, stream); });
-    } else {
-        // Row pass: one pass over every needed row, or (early exit) the
-        // leading positions, their accept scan, then the listed remainder.
-        // Early exit outside the gathered form ends in two launches: the
-        // remaining rows with the draws beside them, and the picks (with the
-        // redo of anything that round left over, usually nothing).
-        const bool queued = plan.queued != 0;
-        if (plan.lead > 0)
-            ok = launch(kKRowLead, [&] { return launch_row_lead(pr, plan, stream); }) &&
-                 launch(kKAcceptLead, [&] { return launch_accept_lead(pr, plan, stream); });
-        else
-            ok = launch(kKRowStats, [&] { return launch_row_stats(pr, plan, stream); });
-        if (queued) {
-            ok = ok && launch(kKRest, [&] { return launch_rest_draws(pr, plan, stream); }) &&
-                 launch(kKDrawPick, [&] { return launch_draw_pick(pr, plan, stream); });
-            if (ev) {
-                g_ev_mask[g_timed_calls % kTimedCalls] = recorded;
-                ++g_timed_calls;
-            }
-            return ok ? SV_OK : SV_ERR_HIP;
-        }
-        if (plan.lead > 0)   // gathered form: a settled sequence has no early draw
-            ok = ok && launch(kKRowStats, [&] {
-                return launch_row_list(pr, plan, plan.sched, reinterpret_cast<const uint32_t*>(plan.blk_ctr),
-                                       (2 * p.total + p.B) * static_cast<int64_t>(g.nseg), stream);
-            });
-        // One pass, outside the gathered form: a draw that fits one round of
-        // workgroups runs as one launch with the accept scans and the picks.
-        const bool draw_all = !pr.draft_probs && plan.lead == 0 &&
-                              (g_draw_mode == SV_DRAW_ONE ||
-                               (g_draw_mode == SV_DRAW_AUTO &&
-                                static_cast<int64_t>(p.B) * g.nchunk <= static_cast<int64_t>(kDrawAllWgsPerCu) * plan.cus));
-        if (draw_all) {
-            ok = ok && launch(kKDrawAll, [&] { return launch_draw_all(pr, plan, stream); });
-            if (ev) {
-                g_ev_mask[g_timed_calls % kTimedCalls] = recorded;
-                ++g_timed_calls;
-            }
-            return ok ? SV_OK : SV_ERR_HIP;
-        }
-        ok = ok && launch(kKAccept, [&] { return launch_accept(pr, plan, stream); });
-        // Gathered form: the draft rows at the rejections.
-        if (ok && pr.draft_probs)
-            ok = launch(kKRowDraft, [&] {
-                return launch_row_list(pr, plan, plan.dlist, plan.dlist_n, static_cast<int64_t>(p.B) * g.nseg, stream);
-            });
-        ok = ok && launch(kKDrawSums, [&] { return launch_draw_sums(pr, plan, stream); }) &&
+        return finish(ok);
+    }
+    // Row pass: one pass over every needed row, or (early exit) the leading
+    // positions, their accept scan, then the listed remainder.  Early exit
+    // outside the gathered form ends in two launches: the remaining rows
+    // with the draws beside them, and the picks (with the redo of anything
+    // that round left over, usually nothing).
+    if (plan.lead > 0)
+        ok = launch(kKRowLead, [&] { return launch_row_lead(pr, plan, stream); }) &&
+             launch(kKAcceptLead, [&] { return launch_accept_lead(pr, plan, stream); });
+    else
+        ok = launch(kKRowStats, [&] { return launch_row_stats(pr, plan, stream); });
+    if (plan.queued) {
+        ok = ok && launch(kKRest, [&] { return launch_rest_draws(pr, plan, stream); }) &&
              launch(kKDrawPick, [&] { return launch_draw_pick(pr, plan, stream); });
+        return finish(ok);
     }
-    if (ev) {
-        g_ev_mask[g_timed_calls % kTimedCalls] = recorded;
-        ++g_timed_calls;
+    if (plan.lead > 0)   // gathered form: a settled sequence has no early draw
+        ok = ok && launch(kKRowStats, [&] {
+            return launch_row_list(pr, plan, plan.sched, reinterpret_cast<const uint32_t*>(plan.blk_ctr),
+                                   (2 * p.total + p.B) * static_cast<int64_t>(g.nseg), stream);
+        });
+    // One pass, outside the gathered form: a draw that fits one round of
+    // workgroups runs as one launch with the accept scans and the picks.
+    const bool draw_all = !pr.draft_probs && plan.lead == 0 &&
+                          (tu.draw_mode == SV_DRAW_ONE ||
+                           (tu.draw_mode == SV_DRAW_AUTO &&
+                            static_cast<int64_t>(p.B) * g.nchunk <= static_cast<int64_t>(kDrawAllWgsPerCu) * plan.cus));
+    if (draw_all) {
+        ok = ok && launch(kKDrawAll, [&] { return launch_draw_all(pr, plan, stream); });
+        return finish(ok);
     }
-    return ok ? SV_OK : SV_ERR_HIP;
+    ok = ok && launch(kKAccept, [&] { return launch_accept(pr, plan, stream); });
+    // Gathered form: the draft rows at the rejections.
+    if (ok && pr.draft_probs)
+        ok = launch(kKRowDraft, [&] {
+            return launch_row_list(pr, plan, plan.dlist, plan.dlist_n, static_cast<int64_t>(p.B) * g.nseg, stream);
+        });
+    ok = ok && launch(kKDrawSums, [&] { return launch_draw_sums(pr, plan, stream); }) &&
+         launch(kKDrawPick, [&] { return launch_draw_pick(pr, plan, stream); });
+    return finish(ok);
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t spec_verify_workspace_size(int32_t B, int64_t total_draft, int64_t V, sv_dtype_t dtype) {
-    if (B < 0 || total_draft < 0 || V < 1 || V > 0x7FFFFFFFll) return 0;
-    if (dtype != SV_F32 && dtype != SV_BF16) return 0;
-    std::lock_guard<std::mutex> lock(g_mutex);
-    Geometry g;
-    int64_t seg_elems, chunk_elems;
-    auto_lengths(B, total_draft, V, &seg_elems, &chunk_elems);
-    if (!make_geometry(B, total_draft, V, dtype, seg_elems, chunk_elems, g)) return 0;
-    return g.bytes;
-}
-
-sv_status_t spec_verify_probs(const void* target_logits, const void* draft_logits,
-                              const int32_t* draft_tokens, const int32_t* offsets,
-                              int32_t k_uniform, int64_t total_draft, int32_t B, int64_t V,
-                              sv_dtype_t dtype, const float* uniforms, const float* temperature,
-                              int32_t* out_tokens, int32_t* out_n_accepted, float* out_p,
-                              float* out_q, float* out_row_max, float* out_row_sumexp,
-                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+sv_status_t verify_probs(const Tuning& tu, const void* target_logits, const void* draft_logits,
+                         const int32_t* draft_tokens, const int32_t* offsets, int32_t k_uniform,
+                         int64_t total_draft, int32_t B, int64_t V, sv_dtype_t dtype, const float* uniforms,
+                         const float* temperature, int32_t* out_tokens, int32_t* out_n_accepted, float* out_p,
+                         float* out_q, float* out_row_max, float* out_row_sumexp, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
     sv_status_t st = check_args(target_logits, draft_logits, draft_tokens, offsets, k_uniform,
                                 total_draft, B, V, dtype, uniforms, temperature, out_tokens,
                                 out_n_accepted);
@@ -431,7 +399,7 @@ sv_status_t spec_verify_probs(const void* target_logits, const void* draft_logit
     if (!aligned(out_p, 4) || !aligned(out_q, 4) || !aligned(out_row_max, 4) ||
         !aligned(out_row_sumexp, 4))
         return SV_ERR_ALIGN;
-    Problem p;
+    Problem p{};
     p.target = target_logits;
     p.draft = draft_logits;
     p.tokens = draft_tokens;
@@ -451,28 +419,15 @@ sv_status_t spec_verify_probs(const void* target_logits, const void* draft_logit
     p.B = B;
     p.k_uniform = offsets ? 0 : k_uniform;
     p.dtype = dtype;
-    return run(p, workspace, workspace_bytes, stream);
+    return run(p, workspace, workspace_bytes, stream, tu);
 }
 
-sv_status_t spec_verify(const void* target_logits, const void* draft_logits,
-                        const int32_t* draft_tokens, const int32_t* offsets, int32_t k_uniform,
-                        int64_t total_draft, int32_t B, int64_t V, sv_dtype_t dtype,
-                        const float* uniforms, const float* temperature, int32_t* out_tokens,
-                        int32_t* out_n_accepted, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream) {
-    return spec_verify_probs(target_logits, draft_logits, draft_tokens, offsets, k_uniform,
-                             total_draft, B, V, dtype, uniforms, temperature, out_tokens,
-                             out_n_accepted, nullptr, nullptr, nullptr, nullptr, workspace,
-                             workspace_bytes, stream);
-}
-
-sv_status_t spec_verify_gathered(const void* target_logits, const void* draft_logits,
-                                 const int32_t* draft_tokens, const float* draft_probs,
-                                 const int32_t* offsets, int32_t k_uniform, int64_t total_draft,
-                                 int32_t B, int64_t V, sv_dtype_t dtype, const float* uniforms,
-                                 const float* temperature, int32_t* out_tokens,
-                                 int32_t* out_n_accepted, float* out_emit_prob, void* workspace,
-                                 size_t workspace_bytes, hipStream_t stream) {
+sv_status_t verify_gathered(const Tuning& tu, const void* target_logits, const void* draft_logits,
+                            const int32_t* draft_tokens, const float* draft_probs, const int32_t* offsets,
+                            int32_t k_uniform, int64_t total_draft, int32_t B, int64_t V, sv_dtype_t dtype,
+                            const float* uniforms, const float* temperature, int32_t* out_tokens,
+                            int32_t* out_n_accepted, float* out_emit_prob, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
     sv_status_t st = check_args(target_logits, draft_logits, draft_tokens, offsets, k_uniform,
                                 total_draft, B, V, dtype, uniforms, temperature, out_tokens,
                                 out_n_accepted);
@@ -495,13 +450,12 @@ sv_status_t spec_verify_gathered(const void* target_logits, const void* draft_lo
     p.B = B;
     p.k_uniform = offsets ? 0 : k_uniform;
     p.dtype = dtype;
-    return run(p, workspace, workspace_bytes, stream);
+    return run(p, workspace, workspace_bytes, stream, tu);
 }
 
-sv_status_t spec_draft_sample(const void* logits, int32_t rows, int64_t V, sv_dtype_t dtype,
-                              const float* temperature, const float* uniforms, int32_t* out_tokens,
-                              float* out_probs, void* workspace, size_t workspace_bytes,
-                              hipStream_t stream) {
+sv_status_t draft_sample(const Tuning& tu, const void* logits, int32_t rows, int64_t V, sv_dtype_t dtype,
+                         const float* temperature, const float* uniforms, int32_t* out_tokens, float* out_probs,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
     // A verify of `rows` sequences with no drafted tokens: each row is the
     // bonus row of its sequence, so its token is drawn from softmax(z / T)
     // by the verify's inverse CDF (or is the argmax at T = 0).
@@ -525,7 +479,58 @@ sv_status_t spec_draft_sample(const void* logits, int32_t rows, int64_t V, sv_dt
     p.B = rows;
     p.k_uniform = 0;
     p.dtype = dtype;
-    return run(p, workspace, workspace_bytes, stream, /*sample=*/true);
+    return run(p, workspace, workspace_bytes, stream, tu, /*sample=*/true);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t spec_verify_workspace_size(int32_t B, int64_t total_draft, int64_t V, sv_dtype_t dtype) {
+    return workspace_bytes_for(B, total_draft, V, dtype, Tuning{});
+}
+
+sv_status_t spec_verify_probs(const void* target_logits, const void* draft_logits,
+                              const int32_t* draft_tokens, const int32_t* offsets,
+                              int32_t k_uniform, int64_t total_draft, int32_t B, int64_t V,
+                              sv_dtype_t dtype, const float* uniforms, const float* temperature,
+                              int32_t* out_tokens, int32_t* out_n_accepted, float* out_p,
+                              float* out_q, float* out_row_max, float* out_row_sumexp,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return verify_probs(Tuning{}, target_logits, draft_logits, draft_tokens, offsets, k_uniform, total_draft, B,
+                        V, dtype, uniforms, temperature, out_tokens, out_n_accepted, out_p, out_q, out_row_max,
+                        out_row_sumexp, workspace, workspace_bytes, stream);
+}
+
+sv_status_t spec_verify(const void* target_logits, const void* draft_logits,
+                        const int32_t* draft_tokens, const int32_t* offsets, int32_t k_uniform,
+                        int64_t total_draft, int32_t B, int64_t V, sv_dtype_t dtype,
+                        const float* uniforms, const float* temperature, int32_t* out_tokens,
+                        int32_t* out_n_accepted, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+    return verify_probs(Tuning{}, target_logits, draft_logits, draft_tokens, offsets, k_uniform, total_draft, B,
+                        V, dtype, uniforms, temperature, out_tokens, out_n_accepted, nullptr, nullptr, nullptr,
+                        nullptr, workspace, workspace_bytes, stream);
+}
+
+sv_status_t spec_verify_gathered(const void* target_logits, const void* draft_logits,
+                                 const int32_t* draft_tokens, const float* draft_probs,
+                                 const int32_t* offsets, int32_t k_uniform, int64_t total_draft,
+                                 int32_t B, int64_t V, sv_dtype_t dtype, const float* uniforms,
+                                 const float* temperature, int32_t* out_tokens,
+                                 int32_t* out_n_accepted, float* out_emit_prob, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+    return verify_gathered(Tuning{}, target_logits, draft_logits, draft_tokens, draft_probs, offsets, k_uniform,
+                           total_draft, B, V, dtype, uniforms, temperature, out_tokens, out_n_accepted,
+                           out_emit_prob, workspace, workspace_bytes, stream);
+}
+
+sv_status_t spec_draft_sample(const void* logits, int32_t rows, int64_t V, sv_dtype_t dtype,
+                              const float* temperature, const float* uniforms, int32_t* out_tokens,
+                              float* out_probs, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+    return draft_sample(Tuning{}, logits, rows, V, dtype, temperature, uniforms, out_tokens, out_probs, workspace,
+                        workspace_bytes, stream);
 }
 
 sv_status_t spec_commit(const int32_t* out_tokens, const int32_t* out_n_accepted, const int32_t* offsets,
@@ -555,15 +560,6 @@ sv_status_t spec_adapt_k(const int32_t* out_n_accepted, const int32_t* offsets, 
                    hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
-sv_status_t spec_stream_probe(const void* data, int64_t bytes, int64_t seg_bytes, uint32_t* out,
-                              hipStream_t stream) {
-    if (bytes < 0 || seg_bytes < 4096 || seg_bytes % 16 != 0 || seg_bytes > (1ll << 30)) return SV_ERR_SHAPE;
-    if ((bytes + seg_bytes - 1) / seg_bytes > 0x7FFFFFFFll) return SV_ERR_SHAPE;
-    if (bytes > 0 && (!data || !out)) return SV_ERR_NULL;
-    if (!aligned(data, 16) || !aligned(out, 4)) return SV_ERR_ALIGN;
-    return launch_stream_probe(data, bytes, seg_bytes, out, stream) == hipSuccess ? SV_OK : SV_ERR_HIP;
-}
-
 size_t spec_ngram_workspace_size(int32_t B) {
     return B < 0 ? 0 : align256(sizeof(int32_t) * (static_cast<size_t>(B) + 1));
 }
@@ -584,7 +580,6 @@ sv_status_t spec_ngram_draft(const int32_t* seq_tokens, const int32_t* seq_len, 
         if (workspace_bytes < need) return SV_ERR_WORKSPACE;
         if (!aligned(workspace, 4)) return SV_ERR_ALIGN;
     } else {
-        std::lock_guard<std::mutex> lock(g_mutex);
         const sv_status_t st = owned_workspace(need, &workspace);
         if (st != SV_OK) return st;
     }
@@ -606,6 +601,7 @@ const char* spec_verify_status_string(sv_status_t status) {
     return "unknown status";
 }
 
+
 void spec_verify_release(void) {
     std::lock_guard<std::mutex> lock(g_mutex);
     int cur = 0;
@@ -619,82 +615,100 @@ void spec_verify_release(void) {
     if (have_cur) (void)hipSetDevice(cur);
 }
 
-sv_status_t spec_verify_timing(int32_t kernels, int32_t every) {
-    std::lock_guard<std::mutex> lock(g_mutex);
-    if (every < 1) return SV_ERR_SHAPE;
-    g_timing = static_cast<uint32_t>(kernels) & ((1u << kNumKernels) - 1u);
-    g_timing_every = every;
-    g_timing_seen = 0;
-    g_timed_calls = 0;
-    return SV_OK;
+
+// ---- sv_tuning.h: test and benchmark hooks --------------------------------
+
+void spec_tuning_defaults(sv_tuning_t* t) {
+    if (!t) return;
+    *t = sv_tuning_t{};
+    t->lead = kAutoLead;
+    t->queue_mode = SV_QUEUE_OVERLAP;
+    t->draw_mode = SV_DRAW_AUTO;
 }
 
-int32_t spec_verify_kernel_times(float* ms, int32_t max_kernels) {
-    std::lock_guard<std::mutex> lock(g_mutex);
-    if (g_timed_calls == 0 || !ms || !g_timing) return -1;
-    const int64_t ncalls = g_timed_calls < kTimedCalls ? g_timed_calls : kTimedCalls;
-    const int64_t last = (g_timed_calls - 1) % kTimedCalls;
-    const uint32_t last_mask = g_ev_mask[last];
-    if (last_mask == 0) return -1;
-    const int last_kernel = 31 - __builtin_clz(last_mask);
-    if (hipEventSynchronize(g_ev[last][2 * last_kernel + 1]) != hipSuccess) return -1;
-    const int n = max_kernels < kNumKernels ? max_kernels : kNumKernels;
-    for (int i = 0; i < n; ++i) {
-        double sum = 0.0;
-        int64_t cnt = 0;
-        for (int64_t c = 0; c < ncalls; ++c) {
-            if (!((g_ev_mask[c] >> i) & 1u)) continue;
-            float t = 0.f;
-            if (hipEventElapsedTime(&t, g_ev[c][2 * i], g_ev[c][2 * i + 1]) != hipSuccess) return -1;
-            sum += t;
-            ++cnt;
-        }
-        ms[i] = cnt ? static_cast<float>(sum / cnt) : __builtin_nanf("");
-    }
-    return kNumKernels;
+size_t spec_verify_workspace_size_tuned(const sv_tuning_t* t, int32_t B, int64_t total_draft, int64_t V,
+                                        sv_dtype_t dtype) {
+    Tuning tu;
+    if (!resolve(t, tu)) return 0;
+    return workspace_bytes_for(B, total_draft, V, dtype, tu);
+}
+
+sv_status_t spec_verify_tuned(const sv_tuning_t* t, const void* target_logits, const void* draft_logits,
+                              const int32_t* draft_tokens, const int32_t* offsets, int32_t k_uniform,
+                              int64_t total_draft, int32_t B, int64_t V, sv_dtype_t dtype,
+                              const float* uniforms, const float* temperature, int32_t* out_tokens,
+                              int32_t* out_n_accepted, float* out_p, float* out_q, float* out_row_max,
+                              float* out_row_sumexp, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+    Tuning tu;
+    if (!resolve(t, tu)) return SV_ERR_SHAPE;
+    return verify_probs(tu, target_logits, draft_logits, draft_tokens, offsets, k_uniform, total_draft, B, V,
+                        dtype, uniforms, temperature, out_tokens, out_n_accepted, out_p, out_q, out_row_max,
+                        out_row_sumexp, workspace, workspace_bytes, stream);
+}
+
+sv_status_t spec_verify_gathered_tuned(const sv_tuning_t* t, const void* target_logits,
+                                       const void* draft_logits, const int32_t* draft_tokens,
+                                       const float* draft_probs, const int32_t* offsets, int32_t k_uniform,
+                                       int64_t total_draft, int32_t B, int64_t V, sv_dtype_t dtype,
+                                       const float* uniforms, const float* temperature, int32_t* out_tokens,
+                                       int32_t* out_n_accepted, float* out_emit_prob, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+    Tuning tu;
+    if (!resolve(t, tu)) return SV_ERR_SHAPE;
+    return verify_gathered(tu, target_logits, draft_logits, draft_tokens, draft_probs, offsets, k_uniform,
+                           total_draft, B, V, dtype, uniforms, temperature, out_tokens, out_n_accepted,
+                           out_emit_prob, workspace, workspace_bytes, stream);
+}
+
+sv_status_t spec_draft_sample_tuned(const sv_tuning_t* t, const void* logits, int32_t rows, int64_t V,
+                                    sv_dtype_t dtype, const float* temperature, const float* uniforms,
+                                    int32_t* out_tokens, float* out_probs, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+    Tuning tu;
+    if (!resolve(t, tu)) return SV_ERR_SHAPE;
+    return draft_sample(tu, logits, rows, V, dtype, temperature, uniforms, out_tokens, out_probs, workspace,
+                        workspace_bytes, stream);
 }
 
 const char* spec_verify_kernel_name(int32_t i) {
     return (i >= 0 && i < kNumKernels) ? kKernelNames[i] : nullptr;
 }
 
-sv_status_t spec_verify_set_mode(int32_t mode, int32_t fused_lag) {
-    if (mode < SV_MODE_AUTO || mode > SV_MODE_FUSED || fused_lag < 0) return SV_ERR_SHAPE;
-    std::lock_guard<std::mutex> lock(g_mutex);
-    g_mode = mode;
-    g_fused_lag = fused_lag;
+sv_status_t spec_timing_events_create(int32_t n, hipEvent_t* ev) {
+    if (n < 0) return SV_ERR_SHAPE;
+    if (n > 0 && !ev) return SV_ERR_NULL;
+    for (int32_t i = 0; i < n; ++i) {
+        if (hipEventCreate(&ev[i]) != hipSuccess) {
+            for (int32_t j = 0; j < i; ++j) (void)hipEventDestroy(ev[j]);
+            return SV_ERR_HIP;
+        }
+    }
     return SV_OK;
 }
 
-sv_status_t spec_verify_set_early_exit(int32_t lead_positions) {
-    if (lead_positions < kAutoLead || lead_positions > SV_K_MAX + 1) return SV_ERR_SHAPE;
-    std::lock_guard<std::mutex> lock(g_mutex);
-    g_lead = lead_positions;
-    return SV_OK;
+sv_status_t spec_timing_elapsed(hipEvent_t start, hipEvent_t stop, float* ms) {
+    if (!start || !stop || !ms) return SV_ERR_NULL;
+    if (hipEventSynchronize(stop) != hipSuccess) return SV_ERR_HIP;
+    return hipEventElapsedTime(ms, start, stop) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
-sv_status_t spec_verify_set_queue(int32_t mode, int32_t lag_accept, int32_t lag_draw) {
-    if (mode < SV_QUEUE_OVERLAP || mode > SV_QUEUE_HANDOFF || lag_accept < 0 || lag_draw < 0) return SV_ERR_SHAPE;
-    std::lock_guard<std::mutex> lock(g_mutex);
-    g_queue_mode = mode;
-    g_lag_a = lag_accept;
-    g_lag_c = lag_draw;
-    return SV_OK;
+sv_status_t spec_timing_events_destroy(int32_t n, hipEvent_t* ev) {
+    if (n < 0) return SV_ERR_SHAPE;
+    if (n > 0 && !ev) return SV_ERR_NULL;
+    sv_status_t st = SV_OK;
+    for (int32_t i = 0; i < n; ++i)
+        if (ev[i] && hipEventDestroy(ev[i]) != hipSuccess) st = SV_ERR_HIP;
+    return st;
 }
 
-sv_status_t spec_verify_set_draw(int32_t mode) {
-    if (mode < SV_DRAW_AUTO || mode > SV_DRAW_THREE) return SV_ERR_SHAPE;
-    std::lock_guard<std::mutex> lock(g_mutex);
-    g_draw_mode = mode;
-    return SV_OK;
-}
-
-sv_status_t spec_verify_set_geometry(int64_t seg_elems, int64_t chunk_elems) {
-    if (seg_elems < 0 || chunk_elems < 0) return SV_ERR_SHAPE;
-    std::lock_guard<std::mutex> lock(g_mutex);
-    g_seg_elems = seg_elems;
-    g_chunk_elems = chunk_elems;
-    return SV_OK;
+sv_status_t spec_stream_probe(const void* data, int64_t bytes, int64_t seg_bytes, uint32_t* out,
+                              hipStream_t stream) {
+    if (bytes < 0 || seg_bytes < 4096 || seg_bytes % 16 != 0 || seg_bytes > (1ll << 30)) return SV_ERR_SHAPE;
+    if ((bytes + seg_bytes - 1) / seg_bytes > 0x7FFFFFFFll) return SV_ERR_SHAPE;
+    if (bytes > 0 && (!data || !out)) return SV_ERR_NULL;
+    if (!aligned(data, 16) || !aligned(out, 4)) return SV_ERR_ALIGN;
+    return launch_stream_probe(data, bytes, seg_bytes, out, stream) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
 }  // extern "C"

@@ -21,16 +21,13 @@
 // accept scans and every draw chunk beside them, and draw_pick picks.  The
 // gathered form instead streams the listed rows (row_list), then runs steps
 // 2-4 with the draft rows at rejections read in between.
-// Fused form (fused.hip): one persistent launch runs the four steps as work
-// items taken from a device-side queue; the last workgroup to finish a
-// sequence's rows runs its accept scan and the last to finish its chunks
-// runs its pick.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "../../include/specverify.h"
+#include "sv_tuning.h"
 
 namespace sv {
 
@@ -148,7 +145,6 @@ struct Plan {
     int32_t* band_n;     // [B * nchunk * kWaves]: band tokens seen per sub-chunk (wave) of a chunk
     double* band_w;      // [B * nchunk * kWaves * kWaveCap * 2]: their (w_t, w_d)
     float* xlogit;       // [2 * total + B]: logit of the drafted token of each row
-    uint32_t* ctr;       // fused form only: kCtrHeader words, then rows_done[B], ready[B], chunks_done[B]
     int32_t lead;        // early exit: positions every sequence reads first (0: one pass over all rows)
     int32_t* done;       // early exit: [B], kUndecided / kDecided / kDecidedEarlyDraw after the lead scan
     RestItem* sched;     // early exit: [(2 * total + B) * nseg + B * (1 + nchunk)], the second round's items
@@ -170,21 +166,6 @@ struct Plan {
 // Plan::done values (early exit).
 enum : int32_t { kUndecided = 0, kDecided = 1, kDecidedEarlyDraw = 2 };
 
-// Layout of Plan::ctr (fused form), zeroed before every launch.  The queue
-// word also carries the abandon bit kQueueAbandoned.
-enum : int32_t { kCtrQueue = 0, kCtrHeader = 4 };
-constexpr uint32_t kQueueAbandoned = 0x80000000u;
-
-// Limits of the fused form (larger calls use the staged form).
-constexpr int kFusedMaxB = 2048;        // sequences (the schedule prefix lives in LDS)
-constexpr int kFusedMaxChunks = 256;    // draw chunks per row (the pick's LDS)
-
-// Launch parameters of the fused form.
-struct Fused {
-    int32_t lag;       // super-steps between a sequence's rows and its draw chunks
-    int32_t blocks;    // resident workgroups
-};
-
 // Host-side launchers (one per kernel).
 hipError_t launch_row_stats(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_row_list(const Problem& p, const Plan& plan, const RestItem* list, const uint32_t* count,
@@ -198,9 +179,8 @@ hipError_t launch_draw_pick(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_draw_all(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_sample_sums(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_sample_pick(const Problem& p, const Plan& plan, hipStream_t s);
-hipError_t launch_fused_reset(const Problem& p, const Plan& plan, hipStream_t s);
-hipError_t launch_fused(const Problem& p, const Plan& plan, const Fused& f, hipStream_t s);
-hipError_t fused_grid(int32_t dtype, int32_t* blocks);   // resident workgroups on this device
+// Second-round workgroups one compute unit holds at once (occupancy query).
+hipError_t rest_blocks_per_cu(int32_t dtype, int32_t* blocks);
 hipError_t launch_commit(const int32_t* out_tokens, const int32_t* out_n, const int32_t* offsets,
                          int32_t k_uniform, int32_t B, int32_t* seq_tokens, int32_t* seq_len,
                          int32_t max_len, int32_t* committed, int32_t* committed_offsets, hipStream_t s);
@@ -210,7 +190,6 @@ hipError_t launch_adapt_k(const int32_t* out_n, const int32_t* offsets, int32_t 
 hipError_t launch_ngram_draft(const int32_t* seq_tokens, const int32_t* seq_len, int32_t B, int32_t max_len,
                               int32_t ngram_max, int32_t ngram_min, int32_t k_max, int32_t* cont_start,
                               int32_t* draft_tokens, int32_t* draft_offsets, hipStream_t s);
-int64_t fused_counter_words(int32_t B);
 hipError_t launch_stream_probe(const void* data, int64_t bytes, int64_t seg_bytes, uint32_t* out,
                                hipStream_t s);
 
@@ -222,12 +201,12 @@ __device__ __forceinline__ float load_logit(const void* base, int32_t dtype, int
     return static_cast<const float*>(base)[idx];
 }
 
-// Data handed between workgroups of ONE launch (the fused form).  The L2 of
-// each XCD is not coherent with the others for ordinary accesses, so such
-// data is stored and loaded with agent-scope relaxed atomics (global_store /
-// global_load with sc1: written through to, and read from, the point where
-// all XCDs agree).  kCo = false gives ordinary accesses for the staged form,
-// where kernel boundaries publish everything.
+// Data handed between workgroups of ONE launch (early exit's second round,
+// the one-launch draw).  The L2 of each XCD is not coherent with the others
+// for ordinary accesses, so such data is stored and loaded with agent-scope
+// relaxed atomics (global_store / global_load with sc1: written through to,
+// and read from, the point where all XCDs agree).  kCo = false gives
+// ordinary accesses where a kernel boundary publishes the data.
 template <bool kCo, class T>
 __device__ __forceinline__ T ld_co(const T* ptr) {
     if constexpr (kCo) return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -1,5 +1,6 @@
 """C-ABI checks that need no GPU: the library loads, exports every function
-include/specverify.h declares, and rejects bad arguments on the host before
+include/specverify.h (the product interface) and csrc/sv_tuning.h (test and
+benchmark hooks) declare, and rejects bad arguments on the host before
 anything is enqueued (every call here fails validation, so no kernel and no
 HIP runtime call is ever made)."""
 import ctypes
@@ -12,6 +13,7 @@ from speculative_decoding_rejection_spec_amd import _lib as svlib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "specverify.h")
+TUNING_HEADER = os.path.join(ROOT, "speculative_decoding_rejection_spec_amd", "csrc", "sv_tuning.h")
 
 OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE = 0, -1, -2, -3, -4, -5
 
@@ -24,8 +26,8 @@ def lib():
     return svlib.lib()
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(path=HEADER):
+    text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(spec_\w+)\s*\(", text)))
 
@@ -36,6 +38,20 @@ def test_every_declared_symbol_is_exported(lib):
     for n in names:
         assert hasattr(lib, n), f"{n} declared in specverify.h but not exported"
     assert sorted(svlib.SIGNATURES) == names, "binding signatures out of sync with the header"
+    hooks = declared_functions(TUNING_HEADER)
+    assert len(hooks) >= 9 and not set(hooks) & set(names)
+    for n in hooks:
+        assert hasattr(lib, n), f"{n} declared in sv_tuning.h but not exported"
+    assert sorted(svlib.TUNING_SIGNATURES) == hooks, "hook signatures out of sync with sv_tuning.h"
+
+
+def test_public_header_holds_no_tuning_hooks():
+    """The product header declares the operation's calls only: no process-wide
+    knobs, timing probes or benchmark references."""
+    text = open(HEADER).read()
+    for word in ("set_geometry", "set_mode", "set_early_exit", "set_queue", "set_draw", "timing",
+                 "kernel_times", "stream_probe", "fused"):
+        assert word not in text, word
 
 
 def test_status_strings(lib):
@@ -45,18 +61,23 @@ def test_status_strings(lib):
     assert lib.spec_verify_status_string(-99).decode() == "unknown status"
     assert lib.spec_verify_kernel_name(0).decode() == "row_stats"
     assert lib.spec_verify_kernel_name(3).decode() == "draw_pick"
-    assert lib.spec_verify_kernel_name(99) is None
+    assert lib.spec_verify_kernel_name(svlib.SV_NUM_KERNELS - 1).decode() == "sample_pick"
+    assert lib.spec_verify_kernel_name(svlib.SV_NUM_KERNELS) is None
+    assert lib.spec_verify_kernel_name(-1) is None
 
 
 def test_workspace_size(lib):
     ws = lib.spec_verify_workspace_size
-    assert ws(256, 2048, 152064, 1) > 0
-    assert ws(512, 2816, 128256, 1) > ws(256, 2048, 152064, 1) * 0 + 1
-    assert ws(256, 2048, 152064, 1) < ws(512, 4096, 152064, 1)
+    c4 = ws(256, 2048, 152064, 1)
+    # at least the per-segment statistics (two segments of 16 bytes per row)
+    assert c4 >= (2 * 2048 + 256) * 2 * 16
+    assert ws(512, 2816, 128256, 1) > ws(64, 256, 128256, 1)
+    assert c4 < ws(512, 4096, 152064, 1)
+    assert ws(256, 2048, 152064, 0) >= c4            # fp32 rows: shorter segments, more of them
     assert ws(-1, 0, 10, 0) == 0
     assert ws(1, 0, 0, 0) == 0
     assert ws(1, 0, 10, 7) == 0
-    assert ws(0, 0, 10, 0) > 0 or ws(0, 0, 10, 0) == 0
+    assert ws(1, -1, 10, 0) == 0
 
 
 def _fake(addr):
@@ -113,15 +134,83 @@ def test_probs_requires_pairs(lib):
     assert st == NULL
 
 
-def test_geometry_knob(lib):
+def _tuning(**kw):
+    t = svlib.Tuning()
+    svlib.lib().spec_tuning_defaults(ctypes.byref(t))
+    for k, v in kw.items():
+        setattr(t, k, v)
+    return t
+
+
+def test_tuned_workspace_size_has_no_global_effect(lib):
     base = lib.spec_verify_workspace_size(64, 256, 128256, 1)
-    try:
-        assert lib.spec_verify_set_geometry(-1, 0) == SHAPE
-        assert lib.spec_verify_set_geometry(1024, 512) == OK
-        assert lib.spec_verify_workspace_size(64, 256, 128256, 1) > base
-    finally:
-        assert lib.spec_verify_set_geometry(0, 0) == OK
+    dflt = _tuning()
+    assert dflt.lead == -1 and dflt.seg_elems == 0 and not dflt.events
+    assert lib.spec_verify_workspace_size_tuned(ctypes.byref(dflt), 64, 256, 128256, 1) == base
+    assert lib.spec_verify_workspace_size_tuned(None, 64, 256, 128256, 1) == base
+    fine = _tuning(seg_elems=1024, chunk_elems=512)
+    assert lib.spec_verify_workspace_size_tuned(ctypes.byref(fine), 64, 256, 128256, 1) > base
+    # a tuned query leaves every other caller's size alone
     assert lib.spec_verify_workspace_size(64, 256, 128256, 1) == base
+
+
+@pytest.mark.parametrize("field,value", [("seg_elems", -1), ("chunk_elems", -1), ("lead", -2), ("lead", 65),
+                                         ("queue_mode", 3), ("queue_mode", -1), ("lag_accept", -1),
+                                         ("lag_draw", -1), ("draw_mode", 3), ("draw_mode", -1)])
+def test_tuning_fields_are_validated(lib, field, value):
+    t = _tuning(**{field: value})
+    assert lib.spec_verify_workspace_size_tuned(ctypes.byref(t), 64, 256, 128256, 1) == 0
+    f = _fake
+    st = lib.spec_verify_tuned(ctypes.byref(t), f(0x10000), f(0x20000), f(0x30000), None, 4, 4, 1, 32000, 0,
+                               f(0x40000), f(0x50000), f(0x60000), f(0x70000), None, None, None, None,
+                               f(0x80000), 1 << 30, None)
+    assert st == SHAPE
+    st = lib.spec_draft_sample_tuned(ctypes.byref(t), f(0x10000), 4, 32000, 0, f(0x50000), f(0x40000),
+                                     f(0x60000), None, f(0x80000), 1 << 30, None)
+    assert st == SHAPE
+
+
+def test_tuned_entries_validate_like_the_plain_ones(lib):
+    f = _fake
+    t = _tuning(lead=0)
+    # k = 64 exceeds SV_K_MAX; a NULL target; a misaligned bf16 base
+    assert lib.spec_verify_tuned(ctypes.byref(t), f(0x10000), f(0x20000), f(0x30000), None, 64, 64, 1, 32000, 0,
+                                 f(0x40000), f(0x50000), f(0x60000), f(0x70000), None, None, None, None,
+                                 f(0x80000), 16, None) == SHAPE
+    assert lib.spec_verify_tuned(None, None, f(0x20000), f(0x30000), None, 4, 4, 1, 32000, 0, f(0x40000),
+                                 f(0x50000), f(0x60000), f(0x70000), None, None, None, None, f(0x80000), 16,
+                                 None) == NULL
+    assert lib.spec_verify_gathered_tuned(ctypes.byref(t), f(0x10001), f(0x20000), f(0x30000), f(0x90000), None,
+                                          4, 4, 1, 32000, 1, f(0x40000), f(0x50000), f(0x60000), f(0x70000),
+                                          None, f(0x80000), 16, None) == ALIGN
+
+
+def test_timing_helpers_argument_errors(lib):
+    assert lib.spec_timing_events_create(-1, None) == SHAPE
+    assert lib.spec_timing_events_create(2, None) == NULL
+    assert lib.spec_timing_events_create(0, None) == OK
+    ms = ctypes.c_float()
+    assert lib.spec_timing_elapsed(None, None, ctypes.byref(ms)) == NULL
+    assert lib.spec_timing_events_destroy(-1, None) == SHAPE
+    assert lib.spec_timing_events_destroy(3, None) == NULL
+
+
+def test_binding_options_stay_in_the_process(lib):
+    """The binding's option setters validate through the library and keep
+    the options on the Python side; reset_options restores the defaults."""
+    import speculative_decoding_rejection_spec_amd as sv
+    base = sv.spec_verify_workspace_size(64, 256, 128256, sv.SV_BF16)
+    try:
+        sv.set_geometry(1024, 512)
+        assert sv.spec_verify_workspace_size(64, 256, 128256, sv.SV_BF16) > base
+        assert lib.spec_verify_workspace_size(64, 256, 128256, 1) == base
+        with pytest.raises(sv.SpecVerifyError):
+            sv.set_early_exit(-7)
+        with pytest.raises(sv.SpecVerifyError):
+            sv.set_queue(9)
+    finally:
+        sv.reset_options()
+    assert sv.spec_verify_workspace_size(64, 256, 128256, sv.SV_BF16) == base
 
 
 def test_stream_probe_argument_errors(lib):
@@ -131,36 +220,6 @@ def test_stream_probe_argument_errors(lib):
     assert lib.spec_stream_probe(p, -1, 4096, p, None) == SHAPE
     assert lib.spec_stream_probe(None, 1 << 20, 4096, p, None) == NULL
     assert lib.spec_stream_probe(ctypes.c_void_p(0x100008), 1 << 20, 4096, p, None) == ALIGN
-
-
-def test_queue_knob(lib):
-    assert lib.spec_verify_set_queue(3, 0, 0) == SHAPE
-    assert lib.spec_verify_set_queue(-1, 0, 0) == SHAPE
-    assert lib.spec_verify_set_queue(0, -1, 0) == SHAPE
-    assert lib.spec_verify_set_queue(0, 0, -1) == SHAPE
-    for mode in (2, 1, 0):
-        assert lib.spec_verify_set_queue(mode, 0, 0) == OK
-
-
-def test_draw_knob(lib):
-    assert lib.spec_verify_set_draw(3) == SHAPE
-    assert lib.spec_verify_set_draw(-1) == SHAPE
-    for mode in (2, 1, 0):
-        assert lib.spec_verify_set_draw(mode) == OK
-
-
-def test_kernel_times_without_timed_call(lib):
-    buf = (ctypes.c_float * 8)()
-    assert lib.spec_verify_kernel_times(buf, 8) == -1
-
-
-def test_timing_probe_arguments(lib):
-    assert lib.spec_verify_timing(1, 0) == SHAPE
-    assert lib.spec_verify_timing(0xF, 4) == OK
-    buf = (ctypes.c_float * 8)()
-    assert lib.spec_verify_kernel_times(buf, 8) == -1      # nothing recorded yet
-    assert lib.spec_verify_timing(0, 1) == OK
-    assert lib.spec_verify_kernel_times(buf, 8) == -1
 
 
 def test_bookkeeping_argument_errors(lib):

@@ -18,7 +18,7 @@ from test_oracle_draft import gathered_q
 
 pytestmark = pytest.mark.gpu
 
-FORMS = ["early", "full", "fused"]
+FORMS = ["early", "full"]
 FORM = {"name": None}
 
 
@@ -30,14 +30,12 @@ def sv(cuda, request):
     if not os.path.exists(sv.LIB_PATH):
         import __graft_entry__
         __graft_entry__.build()
-    sv.set_geometry(0, 0)
-    sv.set_mode(sv.SV_MODE_FUSED if request.param == "fused" else sv.SV_MODE_STAGED)
+    sv.reset_options()
     sv.set_early_exit(1 if request.param == "early" else 0)
     FORM["name"] = request.param
     print(f"[form {request.param}]", flush=True)
     yield sv
-    sv.set_mode(sv.SV_MODE_AUTO)
-    sv.set_early_exit(-1)
+    sv.reset_options()
 
 
 def _logits_tensor(rows, dev):

@@ -23,10 +23,7 @@ TOTALS = {}
 @pytest.fixture(scope="module")
 def sv(cuda):
     import speculative_decoding_rejection_spec_amd as sv
-    sv.set_geometry(0, 0)
-    sv.set_mode(sv.SV_MODE_AUTO)
-    sv.set_early_exit(-1)
-    sv.set_draw(sv.SV_DRAW_AUTO)
+    sv.reset_options()
     return sv
 
 

@@ -22,16 +22,15 @@ pytestmark = pytest.mark.gpu
 AMBIGUOUS = oracle.FLAG_A | oracle.FLAG_B | oracle.FLAG_D
 
 
-# Launch forms: staged with early exit after the first position (the
-# default for large batches), staged reading every row in one pass with the
-# draw as one launch ("full") or as three ("full3"), and the fused
-# persistent kernel.  Every test below runs in each.
-MODES = ["early", "full", "full3", "fused"]
+# Launch forms: early exit after the first position (the default for large
+# batches), and every row read in one pass with the draw as one launch
+# ("full") or as three ("full3").  Every test below runs in each.
+MODES = ["early", "full", "full3"]
 CURRENT = {"mode": None}
 
 
 def set_form(sv, form):
-    sv.set_mode(sv.SV_MODE_FUSED if form == "fused" else sv.SV_MODE_STAGED)
+    sv.reset_options()
     sv.set_early_exit(1 if form == "early" else 0)
     sv.set_draw(sv.SV_DRAW_THREE if form == "full3" else sv.SV_DRAW_ONE if form == "full" else sv.SV_DRAW_AUTO)
 
@@ -44,14 +43,11 @@ def sv(cuda, request):
     if not os.path.exists(sv.LIB_PATH):
         import __graft_entry__
         __graft_entry__.build()
-    sv.set_geometry(0, 0)
     set_form(sv, request.param)
     CURRENT["mode"] = request.param
     print(f"[form {request.param}]", flush=True)
     yield sv
-    sv.set_mode(sv.SV_MODE_AUTO)
-    sv.set_early_exit(-1)
-    sv.set_draw(sv.SV_DRAW_AUTO)
+    sv.reset_options()
 
 
 def to_device(w, dev):
@@ -237,13 +233,10 @@ def test_ragged_vocab(sv, cuda, dtype, V):
 
 def test_tiny_geometry_many_segments(sv, cuda):
     """Force many row segments and draw chunks: exercises the segment merge
-    and the chunk search across hundreds of pieces (the fused form holds at
-    most 256 chunks per row)."""
+    and the chunk search across hundreds of pieces."""
     w = workload("c5", 0, 48)
     ref = oracle.verify(w)
     geoms = ((64, 8), (1000, 200), (1 << 20, 1 << 20))
-    if CURRENT["mode"] == "fused":
-        geoms = ((64, 600), (1000, 512), (1 << 20, 1 << 20))
     try:
         for seg, chunk in geoms:
             sv.set_geometry(seg, chunk)
@@ -335,7 +328,7 @@ def nonfinite_workload(V=4096, dtype="bf16"):
 def test_nonfinite_rows_reading(sv, cuda, dtype):
     """A row with a non-finite maximum is a data error exactly when the scan
     reaches it, in every form (one pass reads rows past the rejection, early
-    exit does not, the fused form reads everything)."""
+    exit does not)."""
     w = nonfinite_workload(dtype=dtype)
     ref = oracle.verify(w)
     assert (ref["n"] == -1).sum() > 10 and (ref["n"] >= 0).sum() > 10
@@ -442,24 +435,8 @@ def test_data_errors_are_per_sequence(sv, cuda):
             assert np.array_equal(gpu["tokens"][sl], ref["tokens"][sl])
 
 
-def test_fused_lag_extremes(sv, cuda):
-    """The fused schedule with the draw chunks right behind their rows
-    (lag 1: draw items wait for their sequence) and after all rows (lag B)."""
-    if CURRENT["mode"] != "fused":
-        pytest.skip("fused form only")
-    w = workload("c5", 0, 64)
-    ref = oracle.verify(w)
-    try:
-        for lag in (1, 2, 64):
-            sv.set_mode(sv.SV_MODE_FUSED, lag)
-            compare(w, run_gpu(sv, w, cuda), ref, f"lag {lag}")
-    finally:
-        sv.set_mode(sv.SV_MODE_FUSED)
-
-
 def test_batch_limits(sv, cuda):
-    """B = 2048 (the fused form's largest batch, every prefix entry used) and
-    B = 2049 (auto falls back to the staged form; forcing fused is refused)."""
+    """Large batches of short rows: B = 2048 and B = 2049 sequences."""
     g = np.random.default_rng(2048)
     V = 520
     for B in (2048, 2049):
@@ -472,16 +449,7 @@ def test_batch_limits(sv, cuda):
         w = wl.assemble(zt, zd, g.integers(0, V, size=len(t_of_d)),
                         g.random(len(t_of_d) + B, dtype=np.float32), temps, k, dtype="bf16")
         ref = oracle.verify(w, threads=16)
-        if B > 2048 and CURRENT["mode"] == "fused":
-            with pytest.raises(sv.SpecVerifyError):
-                run_gpu(sv, w, cuda)
-            sv.set_mode(sv.SV_MODE_AUTO)
-            try:
-                compare(w, run_gpu(sv, w, cuda), ref, f"B={B} auto")
-            finally:
-                sv.set_mode(sv.SV_MODE_FUSED)
-        else:
-            compare(w, run_gpu(sv, w, cuda), ref, f"B={B}")
+        compare(w, run_gpu(sv, w, cuda), ref, f"B={B}")
 
 
 def test_early_exit_leads(sv, cuda):
@@ -537,27 +505,6 @@ def test_queue_modes_bitwise(sv, cuda):
         sv.set_early_exit(1)
 
 
-def test_fused_matches_staged_bitwise(sv, cuda):
-    """Both forms run the same row pass, accept scan and chunk sums, so the
-    counts and diagnostics are identical on the full C4 batch; the pick scans
-    its chunk in pieces of a different size, which could change a token only
-    within about 1e-15 of a CDF boundary (no C4 sequence is that close)."""
-    if CURRENT["mode"] != "fused":
-        pytest.skip("run once")
-    w = workload("c4")
-    out = {}
-    try:
-        for mode in (sv.SV_MODE_STAGED, sv.SV_MODE_FUSED):
-            sv.set_mode(mode)
-            sv.set_early_exit(0)
-            out[mode] = run_gpu(sv, w, cuda, probs=True)
-    finally:
-        set_form(sv, "fused")
-    a, b = out[sv.SV_MODE_STAGED], out[sv.SV_MODE_FUSED]
-    for key in a:
-        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
-
-
 def test_library_loaded_before_torch(cuda):
     """Touching the library before torch is imported still leaves one HIP
     runtime in the process (the binding imports torch before loading it):
@@ -569,7 +516,7 @@ def test_library_loaded_before_torch(cuda):
     code = (
         "import sys; sys.path.insert(0, %r)\n"
         "import speculative_decoding_rejection_spec_amd as sv\n"
-        "sv.set_geometry(0, 0)\n"
+        "sv.spec_verify_workspace_size(4, 16, 32000, sv.SV_F32)\n"
         "import numpy as np, torch, workloads as wl\n"
         "w = wl.make_workload('c1', trial=0, B=4)\n"
         "d = torch.device('cuda:0')\n"
