@@ -46,11 +46,15 @@
  *   * Outputs: out_tokens int32 [total_draft + B] (slot offsets[b] + b + i):
  *     the n_b accepted drafts, then the emitted token, then -1;
  *     out_n_accepted int32 [B]: n_b in 0..k_b, or -1 for a per-sequence data
- *     error (k_b out of range, offsets inconsistent, T < 0 or not finite, a
- *     drafted token outside [0, V), or a logit row with a non-finite
- *     maximum that the scan reaches: target and draft rows up to and
- *     including the first rejection -- rows past it are never looked at,
- *     whichever form reads them); that sequence's token slots are all -1.
+ *     error (k_b out of range; offsets out of order: offsets[b+1] below
+ *     offsets[b], an earlier offset above offsets[b] or a later one below
+ *     offsets[b+1], so that the range overlaps another sequence's -- two
+ *     overlapping ranges are both errors; T < 0 or not finite; a drafted
+ *     token outside [0, V); or a logit row with a non-finite maximum that
+ *     the scan reaches: target and draft rows up to and including the
+ *     first rejection -- rows past it are never looked at, whichever form
+ *     reads them); that sequence's token slots, when its range lies inside
+ *     the batch, are all -1.  Every other sequence is verified as usual.
  *     NaN logits are otherwise outside the contract.
  *   * Argument errors are detected on the host before anything is enqueued
  *     and return a negative sv_status_t with no output written.

@@ -48,7 +48,14 @@
  *   R8 greedy ties go to the lowest token id;
  *   R11 if a rejection leaves Z < 1e-9 the draw falls back to p_n (flag D);
  *   R26 a logit row the scan reaches (positions up to the first rejection)
- *      whose maximum is not finite makes the sequence a data error (flag E).
+ *      whose maximum is not finite makes the sequence a data error (flag E);
+ *   R28 the rows, uniforms and output slots of sequence b are its own only
+ *      when its offsets are in order with every other sequence's:
+ *      offsets[b] <= offsets[b+1], no earlier offset above offsets[b] and no
+ *      later one below offsets[b+1].  Otherwise its range overlaps another
+ *      sequence's (or runs backwards) and it is a data error (flag E); two
+ *      overlapping ranges are thus both errors, and every other sequence is
+ *      verified as usual.
  *
  * Two more entry points follow the same pages: oracle_verify_gathered (the
  * accept tests divide by the drafter's gathered q_i(x_i) instead of the draft
@@ -314,6 +321,9 @@ static int orc_verify_range(const void *target, const void *draft, int32_t dtype
         int32_t *out = out_tokens + trow;
         int bad = (k < 0 || k > ORC_K_MAX || !(T >= 0.0) || isinf(T) || o < 0 ||
                    offsets[b + 1] > total);
+        /* Reading R28: the range must be ordered against every other one. */
+        for (int32_t j = 0; !bad && j < b; ++j) bad |= offsets[j] > o;
+        for (int32_t j = b + 2; !bad && j <= B; ++j) bad |= offsets[j] < offsets[b + 1];
         const int32_t *x = tokens + drow;
         for (int i = 0; !bad && i < k; ++i) bad |= (x[i] < 0 || x[i] >= V);
         /* A gathered q(x) must be a probability the drafter could have drawn
@@ -322,7 +332,9 @@ static int orc_verify_range(const void *target, const void *draft, int32_t dtype
         for (int i = 0; !bad && qg && T > 0.0 && i < k; ++i)
             bad |= !(qg[i] > 0.0f && qg[i] <= 1.0f);
         if (bad) {
-            for (int i = 0; k >= 0 && i <= k && i <= ORC_K_MAX; ++i) out[i] = -1;
+            /* The sequence's own slots, when its range lies inside the batch. */
+            if (o >= 0 && k >= 0 && offsets[b + 1] <= total)
+                for (int i = 0; i <= k; ++i) out[i] = -1;
             out_n[b] = -1;
             if (out_flags) out_flags[b] = ORC_FLAG_E;
             continue;

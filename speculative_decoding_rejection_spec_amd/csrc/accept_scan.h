@@ -149,6 +149,35 @@ __device__ __forceinline__ void list_rest(const Problem& p, const Plan& plan, in
     }
 }
 
+// Whether sequence b's offsets are in order with every other sequence's
+// (reading R28): no earlier offset above o = offsets[b] and no later one
+// (past b + 1) below o1 = offsets[b + 1].  Otherwise its range overlaps
+// another sequence's, whose rows, uniforms and slots it would share.  Run
+// by the whole wave (the offsets are read eight per lane at a time, so a
+// batch of up to 511 sequences costs one round trip); the same in every
+// lane.
+__device__ __forceinline__ bool offsets_in_order(const Problem& p, int32_t b, int64_t o, int64_t o1) {
+    if (!p.offsets) return true;
+    constexpr int kU = 8;
+    const int lane = threadIdx.x & 63;
+    bool ok = true;
+    for (int32_t j0 = 0; j0 <= p.B; j0 += 64 * kU) {
+        int32_t v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int32_t j = j0 + u * 64 + lane;
+            v[u] = j <= p.B ? p.offsets[j] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int32_t j = j0 + u * 64 + lane;
+            if (j < b && v[u] > o) ok = false;
+            if (j > b + 1 && j <= p.B && v[u] < o1) ok = false;
+        }
+    }
+    return !__any(!ok);
+}
+
 // Accept scan of sequence b (0 <= b < B), run by every lane of one wave.
 // kCo: the SegStats and captured logits come from other workgroups of the
 // same launch, and the DrawTask goes to others.
@@ -174,11 +203,13 @@ __device__ __forceinline__ void list_rest(const Problem& p, const Plan& plan, in
 // gives the same task).  pre (sampling sequences outside the gathered form,
 // rows of at most kPolledSegs segments, every position read): the rows'
 // statistics already loaded, used instead of loading them again.
+// check_order = false skips offsets_in_order for a sequence an earlier scan
+// of the same call has already found in order (early exit's later scans).
 template <bool kCo>
 __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& plan, int32_t b,
                                                 int32_t limit = kKMax + 1, int32_t* done = nullptr,
                                                 DrawTask* task_out = nullptr, bool emit = true,
-                                                const Polled* pre = nullptr) {
+                                                const Polled* pre = nullptr, bool check_order = true) {
     const int lane = threadIdx.x & 63;
     int64_t o, o1;
     if (p.offsets) { o = p.offsets[b]; o1 = p.offsets[b + 1]; }
@@ -186,7 +217,8 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
     const int64_t k64 = o1 - o;
     const float Tf = p.temperature[b];
     const int64_t ntarget = p.total + p.B;
-    bool ok = o >= 0 && k64 >= 0 && k64 <= kKMax && o1 <= p.total && temperature_ok(Tf);
+    const bool ordered = !check_order || offsets_in_order(p, b, o, o1);
+    bool ok = ordered && o >= 0 && k64 >= 0 && k64 <= kKMax && o1 <= p.total && temperature_ok(Tf);
     const int k = ok ? static_cast<int>(k64) : 0;
     const bool greedy = (Tf == 0.f);
     const bool gathered = p.draft_probs != nullptr;   // q_i(x_i) from the drafter

@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kPickThreads, 4) void draw_pick_kernel(Problem p, P
     if (redo) {
         load_exp2_table(tbl, kPickThreads);
         if (plan.done[b] == kUndecided) {
-            if (threadIdx.x < 64) accept_sequence<true>(p, plan, b);
+            if (threadIdx.x < 64) accept_sequence<true>(p, plan, b, kKMax + 1, nullptr, nullptr, true, nullptr, false);
             wait_stores();
         }
         __syncthreads();

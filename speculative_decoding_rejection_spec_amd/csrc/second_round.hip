@@ -159,8 +159,9 @@ __global__ __launch_bounds__(kThreads) void rest_draws_kernel(Problem p, Plan pl
                 __builtin_amdgcn_s_sleep(8);
             }
             if (ready) {
-                if (keep) accept_sequence<true>(p, plan, b, kKMax + 1, nullptr, nullptr, true, &pre);
-                else accept_sequence<true>(p, plan, b);
+                // (accept_lead found the sequence's offsets in order)
+                if (keep) accept_sequence<true>(p, plan, b, kKMax + 1, nullptr, nullptr, true, &pre, false);
+                else accept_sequence<true>(p, plan, b, kKMax + 1, nullptr, nullptr, true, nullptr, false);
             }
             else if (tid == 0) plan.aband[b] = 1;    // the pick launch redoes the sequence
             return;

@@ -108,6 +108,36 @@ def test_draft_sample_masked_vocabulary(sv, cuda, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_draft_sample_masked_extreme_uniforms(sv, cuda, dtype):
+    """u = 0 picks the first token with mass (never a masked one before
+    it), u = 1 - 2^-24 a token at the end of the unmasked mass (never a
+    masked tail token): the oracle's tokens, every one finite in its row."""
+    V, rows = 40000, 64
+    g = np.random.default_rng(59)
+    z = (g.standard_normal((rows, V)) * 2).astype(np.float32)
+    idx = np.arange(V)
+    for r in range(rows):
+        kind = r % 4
+        if kind == 0:
+            z[r, idx < 2600] = -np.inf
+        elif kind == 1:
+            z[r, idx >= V - 464] = -np.inf
+        elif kind == 2:
+            z[r, (idx < 3000) | (idx >= V - 3000)] = -np.inf
+        else:
+            z[r, g.random(V) < 0.3] = -np.inf
+    stored = wl.bf16_round(z) if dtype == "bf16" else z
+    T = np.where(np.arange(rows) % 8 < 6, 1.0, 0.6).astype(np.float32)
+    u = np.where(np.arange(rows) % 2 == 0, 0.0, 1.0 - 2.0 ** -24).astype(np.float32)
+    tok, prob = run_sample(sv, stored, T, u, cuda)
+    ref = oracle.draft_sample(stored, T, u, threads=16)
+    np.testing.assert_array_equal(tok, ref["tokens"])
+    assert np.all(np.isfinite(z[np.arange(rows), tok]))
+    first = np.argmax(np.isfinite(z), axis=1)
+    np.testing.assert_array_equal(tok[::2], first[::2])      # u = 0: the first unmasked token
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_draft_sample_nonfinite_rows(sv, cuda, dtype):
     """A row whose maximum is not finite (+inf, or every entry -inf) gives
     -1 and NaN, as a data error does in the verify (reading R26); the other

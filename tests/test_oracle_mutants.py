@@ -14,6 +14,7 @@ import pytest
 import oracle
 import test_oracle_bookkeeping as bpins
 import test_oracle_draft as dpins
+import test_oracle_flags as fpins
 import test_oracle_pins as pins
 import test_oracle_rows as rpins
 
@@ -54,6 +55,20 @@ MUTANTS = {
     "ngram_suffix_matches_itself": ("for (int32_t j = L - n - 1; j >= 0; --j) {", "for (int32_t j = L - n; j >= 0; --j) {"),
     "rows_past_rejection_read": ("for (int i = 0; i <= r.n && !row_bad; ++i)", "for (int i = 0; i <= k && !row_bad; ++i)"),
     "greedy_nonfinite_row_ignored": ("if (!isfinite(m)) { row_bad = 1; break; }", "if (0) { row_bad = 1; break; }"),
+    # the degenerate-residual fallback (reading R11) and the ambiguity flags
+    "fallback_from_q": ("        qr = NULL;\n        Zs.s = Zs.c = 0.0;",
+                        "        pr = qr;\n        qr = NULL;\n        Zs.s = Zs.c = 0.0;"),
+    "no_fallback": ("if (qr && Z < ORC_DEGENERATE_Z) {", "if (0 && qr && Z < ORC_DEGENERATE_Z) {"),
+    "fallback_threshold_1e-3": ("#define ORC_DEGENERATE_Z 1e-9", "#define ORC_DEGENERATE_Z 1e-3"),
+    "fallback_threshold_1e-12": ("#define ORC_DEGENERATE_Z 1e-9", "#define ORC_DEGENERATE_Z 1e-12"),
+    "flag_d_never_set": ("if (degenerate) res.flags |= ORC_FLAG_D;", "if (0) res.flags |= ORC_FLAG_D;"),
+    "accept_band_1e-6": ("#define ORC_ACCEPT_BAND 1e-5", "#define ORC_ACCEPT_BAND 1e-6"),
+    "accept_band_1e-4": ("#define ORC_ACCEPT_BAND 1e-5", "#define ORC_ACCEPT_BAND 1e-4"),
+    "cdf_band_1e-14": ("#define ORC_CDF_BAND 1e-12", "#define ORC_CDF_BAND 1e-14"),
+    "cdf_band_1e-10": ("#define ORC_CDF_BAND 1e-12", "#define ORC_CDF_BAND 1e-10"),
+    "offsets_order_ignored": ("        for (int32_t j = 0; !bad && j < b; ++j) bad |= offsets[j] > o;\n"
+                              "        for (int32_t j = b + 2; !bad && j <= B; ++j) bad |= offsets[j] < offsets[b + 1];",
+                              ""),
     "draft_greedy_highest_tie": ("orc_row_argmax(logits, dtype, r, V, &a);\n            out_tokens[r] = (int32_t)a;",
                                  "orc_row_argmax(logits, dtype, r, V, &a);\n            out_tokens[r] = (int32_t)(V - 1 - a);"),
 }
@@ -81,6 +96,16 @@ PINS = [
     lambda: rpins.test_nonfinite_rows_the_scan_reaches(),
     lambda: rpins.test_nonfinite_past_the_rejection_changes_nothing(),
     lambda: rpins.test_greedy_reaches_rows_up_to_the_first_mismatch(),
+    lambda: pins.test_offsets_out_of_order_are_data_errors(),
+    lambda: fpins.test_degenerate_residual_draws_from_the_target_row(),
+    lambda: fpins.test_degenerate_residual_can_emit_the_rejected_token(),
+    lambda: fpins.test_small_but_usable_residual_is_drawn_normally(),
+    lambda: fpins.test_degenerate_threshold_bracket(),
+    lambda: fpins.test_flag_a_inside_the_band(),
+    lambda: fpins.test_flag_a_outside_the_band(),
+    lambda: fpins.test_flag_a_only_on_evaluated_tests(),
+    lambda: fpins.test_flag_b_on_an_exact_boundary(),
+    lambda: fpins.test_flag_b_band_width(),
 ]
 
 

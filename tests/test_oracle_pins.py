@@ -323,6 +323,34 @@ def test_data_errors_flag_rows():
     assert out["n"][0] == -1 and out["flags"][0] & oracle.FLAG_E
 
 
+def test_offsets_out_of_order_are_data_errors():
+    """Reading R28: offsets [0, 4, 8, 6, 12, 15] run backwards at sequence 2
+    (k = -2), and sequences 1 ([4, 8)) and 3 ([6, 12)) overlap, so all three
+    are data errors with every slot of theirs -1; sequences 0 and 4, whose
+    ranges are in order with every other, give exactly what they give when
+    verified in a batch of their own."""
+    g = _rng(28)
+    V = 300
+    offsets = np.array([0, 4, 8, 6, 12, 15], np.int32)
+    B, total = len(offsets) - 1, 15
+    t = (g.standard_normal((total + B, V)) * 2).astype(np.float32)
+    d = (t[:total] + g.standard_normal((total, V)).astype(np.float32)).astype(np.float32)
+    w = wl.Workload(name="order", V=V, B=B, dtype="f32", k=np.diff(offsets).astype(np.int32),
+                    offsets=offsets, target=t, draft=d, tokens=g.integers(0, V, size=total).astype(np.int32),
+                    uniforms=g.random(total + B, dtype=np.float32),
+                    temperature=np.array([1.0, 1.0, 0.7, 0.0, 0.8], np.float32), sigma=np.zeros(B))
+    out = oracle.verify(w)
+    assert list(out["n"][[1, 2, 3]]) == [-1, -1, -1]
+    assert all(out["flags"][[1, 2, 3]] == oracle.FLAG_E)
+    assert np.all(out["tokens"][w.target_row(1, 0):w.target_row(1, 4) + 1] == -1)
+    assert np.all(out["tokens"][w.target_row(3, 0):w.target_row(3, 6) + 1] == -1)
+    alone = w.subset([0, 4])
+    ref = oracle.verify(alone)
+    assert out["n"][0] == ref["n"][0] >= 0 and out["n"][4] == ref["n"][1] >= 0
+    np.testing.assert_array_equal(out["tokens"][0:5], ref["tokens"][0:5])
+    np.testing.assert_array_equal(out["tokens"][16:20], ref["tokens"][5:9])
+
+
 # --------------------------------------------------------------------------
 # cross-check with an independent numpy / scipy composition at real V
 # --------------------------------------------------------------------------
