@@ -89,7 +89,8 @@ typedef enum {
     SV_ERR_DTYPE = -3,     /* dtype is not SV_F32 / SV_BF16 */
     SV_ERR_ALIGN = -4,     /* a pointer is not aligned to its element size */
     SV_ERR_WORKSPACE = -5, /* workspace_bytes smaller than spec_verify_workspace_size() */
-    SV_ERR_HIP = -6        /* a HIP call or kernel launch failed */
+    SV_ERR_HIP = -6,       /* a HIP call or kernel launch failed */
+    SV_ERR_SCRATCH = -7    /* the call needs more than spec_verify_noalloc's static scratch */
 } sv_status_t;
 
 /* Bytes of device workspace one call needs for these sizes (0 on bad sizes). */
@@ -110,6 +111,26 @@ sv_status_t spec_verify(const void *target_logits, const void *draft_logits,
                         sv_dtype_t dtype, const float *uniforms, const float *temperature,
                         int32_t *out_tokens, int32_t *out_n_accepted, void *workspace,
                         size_t workspace_bytes, hipStream_t stream);
+
+/* spec_verify for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same operation, arguments and outputs as spec_verify, without the
+ * workspace: the library uses a static device array of
+ * SV_NOALLOC_SCRATCH_BYTES on each GPU (held until the process ends; its
+ * address is looked up once per GPU, on the first call there) and calls no
+ * allocating routine.  A call whose workspace (spec_verify_workspace_size)
+ * exceeds the array returns SV_ERR_SCRATCH before anything is enqueued
+ * (256 sequences of k = 8 at V = 152064 need 3.4 MiB, 512 of k <= 10 at
+ * V = 128256 6.0 MiB).  Every call on one GPU shares that GPU's array and
+ * finds it holding the previous call's contents (each call re-initialises
+ * what it reads): calls that overlap in time on one GPU, on different
+ * streams, race and give wrong results. */
+#define SV_NOALLOC_SCRATCH_BYTES (16u << 20)
+sv_status_t spec_verify_noalloc(const void *target_logits, const void *draft_logits,
+                                const int32_t *draft_tokens, const int32_t *offsets,
+                                int32_t k_uniform, int64_t total_draft, int32_t B, int64_t V,
+                                sv_dtype_t dtype, const float *uniforms, const float *temperature,
+                                int32_t *out_tokens, int32_t *out_n_accepted, hipStream_t stream);
 
 /* spec_verify plus diagnostics (each may be NULL):
  *   out_p, out_q fp32 [total_draft]: p_i(x_i), q_i(x_i) of the tempered

@@ -15,11 +15,11 @@ from __future__ import annotations
 
 import ctypes
 
-from ._lib import (LIB_PATH, SV_BF16, SV_DRAW_AUTO, SV_DRAW_ONE, SV_DRAW_THREE, SV_F32, SV_K_MAX, SV_NUM_KERNELS,
+from ._lib import (LIB_PATH, SV_NOALLOC_SCRATCH_BYTES, SV_BF16, SV_DRAW_AUTO, SV_DRAW_ONE, SV_DRAW_THREE, SV_F32, SV_K_MAX, SV_NUM_KERNELS,
                    SV_QUEUE_FINAL, SV_QUEUE_HANDOFF, SV_QUEUE_OVERLAP, SpecVerifyError, Tuning, check, lib)
 
 __all__ = [
-    "spec_verify", "spec_verify_probs", "spec_verify_gathered", "spec_draft_sample",
+    "spec_verify", "spec_verify_noalloc", "spec_verify_probs", "spec_verify_gathered", "spec_draft_sample",
     "spec_commit", "spec_adapt_k", "spec_ngram_draft",
     "spec_verify_workspace_size", "spec_verify_release",
     "stream_probe", "timing", "kernel_times", "set_geometry", "set_early_exit", "set_queue", "set_draw",
@@ -165,6 +165,22 @@ def spec_verify(target_logits, draft_logits, draft_tokens, offsets, uniforms, te
         st = lib().spec_verify_tuned(ctypes.byref(t), *args, None, None, None, None, _ptr(workspace), ws_bytes,
                                      _stream(dev, stream))
     check(st, "spec_verify")
+    return out_tokens, out_n_accepted
+
+
+def spec_verify_noalloc(target_logits, draft_logits, draft_tokens, offsets, uniforms, temperature, *,
+                        k_uniform: int = 0, out_tokens=None, out_n_accepted=None, stream=None):
+    """spec_verify without a workspace or any allocation inside the library
+    (its static per-GPU scratch); pass out_tokens and out_n_accepted to keep
+    the call itself allocation-free.  Returns (out_tokens, out_n_accepted)."""
+    dev, V, B, total, out_tokens, out_n_accepted = _prepare(
+        target_logits, draft_logits, draft_tokens, offsets, uniforms, temperature, k_uniform,
+        out_tokens, out_n_accepted)
+    st = lib().spec_verify_noalloc(
+        _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(offsets), int(k_uniform), total, B, V,
+        _dtype_code(target_logits.dtype), _ptr(uniforms), _ptr(temperature), _ptr(out_tokens),
+        _ptr(out_n_accepted), _stream(dev, stream))
+    check(st, "spec_verify_noalloc")
     return out_tokens, out_n_accepted
 
 

@@ -20,7 +20,8 @@ SV_NUM_KERNELS = 11
 SV_QUEUE_OVERLAP, SV_QUEUE_FINAL, SV_QUEUE_HANDOFF = 0, 1, 2
 SV_DRAW_AUTO, SV_DRAW_ONE, SV_DRAW_THREE = 0, 1, 2
 STATUS = {0: "SV_OK", -1: "SV_ERR_NULL", -2: "SV_ERR_SHAPE", -3: "SV_ERR_DTYPE",
-          -4: "SV_ERR_ALIGN", -5: "SV_ERR_WORKSPACE", -6: "SV_ERR_HIP"}
+          -4: "SV_ERR_ALIGN", -5: "SV_ERR_WORKSPACE", -6: "SV_ERR_HIP", -7: "SV_ERR_SCRATCH"}
+SV_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _P, _I32, _I64, _SZ, _U32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_uint32
 
@@ -38,6 +39,7 @@ SIGNATURES = {
     "spec_verify_workspace_size": (_SZ, [_I32, _I64, _I64, _I32]),
     "spec_verify": (_I32, [_P, _P, _P, _P, _I32, _I64, _I32, _I64, _I32, _P, _P, _P, _P,
                            _P, _SZ, _P]),
+    "spec_verify_noalloc": (_I32, [_P, _P, _P, _P, _I32, _I64, _I32, _I64, _I32, _P, _P, _P, _P, _P]),
     "spec_verify_probs": (_I32, [_P, _P, _P, _P, _I32, _I64, _I32, _I64, _I32, _P, _P, _P,
                                  _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "spec_verify_gathered": (_I32, [_P, _P, _P, _P, _P, _I32, _I64, _I32, _I64, _I32, _P, _P, _P,

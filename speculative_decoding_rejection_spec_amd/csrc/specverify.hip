@@ -9,6 +9,11 @@
 #include "sv_internal.h"
 #include "sv_tuning.h"
 
+// The scratch of spec_verify_noalloc: one copy on each GPU the library runs
+// on, for the life of the process.  In host code `scratch` only names the
+// symbol; its device address comes from hipGetSymbolAddress (scratch_address).
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 using namespace sv;
 
@@ -131,6 +136,23 @@ int32_t effective_lead(int64_t B, int64_t total, int64_t V, sv_dtype_t dtype, co
 // Library-owned workspace, one grow-only buffer per device.
 void* g_ws[kMaxDevices] = {};
 size_t g_ws_bytes[kMaxDevices] = {};
+// Device address of `scratch` on each device (looked up on first use).
+void* g_scratch[kMaxDevices] = {};
+
+// The address of this device's copy of `scratch`: hipGetSymbolAddress once
+// per device, with that device current.  Allocates nothing.
+sv_status_t scratch_address(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SV_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_mutex);
+    if (!g_scratch[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SV_ERR_HIP;
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return SV_OK;
+}
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -513,6 +535,26 @@ sv_status_t spec_verify(const void* target_logits, const void* draft_logits,
                         nullptr, workspace, workspace_bytes, stream);
 }
 
+sv_status_t spec_verify_noalloc(const void* target_logits, const void* draft_logits,
+                                const int32_t* draft_tokens, const int32_t* offsets, int32_t k_uniform,
+                                int64_t total_draft, int32_t B, int64_t V, sv_dtype_t dtype,
+                                const float* uniforms, const float* temperature, int32_t* out_tokens,
+                                int32_t* out_n_accepted, hipStream_t stream) {
+    const sv_status_t st = check_args(target_logits, draft_logits, draft_tokens, offsets, k_uniform, total_draft,
+                                      B, V, dtype, uniforms, temperature, out_tokens, out_n_accepted);
+    if (st != SV_OK) return st;
+    if (B == 0) return SV_OK;
+    const size_t need = workspace_bytes_for(B, total_draft, V, dtype, Tuning{});
+    if (need == 0) return SV_ERR_SHAPE;
+    if (need > SV_NOALLOC_SCRATCH_BYTES) return SV_ERR_SCRATCH;
+    void* ws = nullptr;
+    const sv_status_t sa = scratch_address(&ws);
+    if (sa != SV_OK) return sa;
+    return verify_probs(Tuning{}, target_logits, draft_logits, draft_tokens, offsets, k_uniform, total_draft, B,
+                        V, dtype, uniforms, temperature, out_tokens, out_n_accepted, nullptr, nullptr, nullptr,
+                        nullptr, ws, SV_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 sv_status_t spec_verify_gathered(const void* target_logits, const void* draft_logits,
                                  const int32_t* draft_tokens, const float* draft_probs,
                                  const int32_t* offsets, int32_t k_uniform, int64_t total_draft,
@@ -597,6 +639,7 @@ const char* spec_verify_status_string(sv_status_t status) {
         case SV_ERR_ALIGN: return "pointer not aligned to its element size";
         case SV_ERR_WORKSPACE: return "workspace smaller than spec_verify_workspace_size()";
         case SV_ERR_HIP: return "HIP call or kernel launch failed";
+        case SV_ERR_SCRATCH: return "call needs more than spec_verify_noalloc's static scratch";
     }
     return "unknown status";
 }

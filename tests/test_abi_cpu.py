@@ -55,7 +55,7 @@ def test_public_header_holds_no_tuning_hooks():
 
 
 def test_status_strings(lib):
-    for code in (OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, -6):
+    for code in (OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, -6, -7):
         s = lib.spec_verify_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.spec_verify_status_string(-99).decode() == "unknown status"
@@ -119,6 +119,25 @@ def _call(lib, **kw):
 ])
 def test_argument_errors(lib, kw, code):
     assert _call(lib, **kw) == code
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch(lib):
+    """The size check comes before any HIP call: 4096 sequences of k = 8 at
+    V = 152064 need 55 MiB of workspace, more than the 16 MiB scratch."""
+    f = _fake
+    need = lib.spec_verify_workspace_size(4096, 4096 * 8, 152064, 1)
+    assert need > svlib.SV_NOALLOC_SCRATCH_BYTES
+    assert lib.spec_verify_workspace_size(256, 2048, 152064, 1) <= svlib.SV_NOALLOC_SCRATCH_BYTES
+    assert lib.spec_verify_workspace_size(512, 5120, 128256, 1) <= svlib.SV_NOALLOC_SCRATCH_BYTES
+    st = lib.spec_verify_noalloc(f(0x10000), f(0x20000), f(0x30000), None, 8, 4096 * 8, 4096, 152064, 1,
+                                 f(0x40000), f(0x50000), f(0x60000), f(0x70000), None)
+    assert st == -7
+    assert "scratch" in lib.spec_verify_status_string(-7).decode()
+    # argument errors as for spec_verify, and an empty batch does nothing
+    assert lib.spec_verify_noalloc(None, f(0x20000), f(0x30000), None, 4, 4, 1, 32000, 0, f(0x40000),
+                                   f(0x50000), f(0x60000), f(0x70000), None) == NULL
+    assert lib.spec_verify_noalloc(f(0x10000), None, None, None, 0, 0, 0, 32000, 0, f(0x40000), f(0x50000),
+                                   f(0x60000), f(0x70000), None) == OK
 
 
 def test_empty_batch_is_a_no_op(lib):
