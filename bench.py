@@ -244,6 +244,15 @@ def main():
         k1_live = sum(kt[k] for k in roof)
     sv.timing(False)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # Host cost of enqueueing one step (binding, C host code, launches),
+    # timed without waiting for the GPU: below ms_per_step the GPU is the
+    # bound, not the host.
+    torch.cuda.synchronize()
+    te = time.perf_counter()
+    for i in range(8):
+        step(i)
+    host_ms = (time.perf_counter() - te) * 1e3 / 8
+    torch.cuda.synchronize()
     # Per-step distribution: a further pass with an event pair around each step.
     step_ms = []
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(64)]
@@ -319,6 +328,7 @@ def main():
                     "mean_ms": round(k1_live, 5)}
 
     cpu = None
+    check = None
     if not args.no_cpu_baseline:
         import oracle
         threads = min(16, os.cpu_count() or 1)
@@ -336,8 +346,18 @@ def main():
             tc = time.perf_counter()
             ref = oracle.verify(w, threads=threads, draft_probs=qg)
             tc = time.perf_counter() - tc
-            agree = int(np.sum(ref["n"] == n))
-            what = "accept counts"
+            # every token slot and accept count, sequence by sequence
+            gtok = out_tok.cpu().numpy()
+            same = np.array([ref["n"][b] == n[b] and np.array_equal(
+                ref["tokens"][w.target_row(b, 0):w.target_row(b, int(w.k[b])) + 1],
+                gtok[w.target_row(b, 0):w.target_row(b, int(w.k[b])) + 1]) for b in range(w.B)])
+            flagged = (ref["flags"] & (oracle.FLAG_A | oracle.FLAG_B | oracle.FLAG_D)) != 0
+            agree = int(same.sum())
+            what = "accept counts and token slots"
+            check = {"sequences": w.B, "identical": agree, "flagged": int(flagged.sum()),
+                     "flag_rate": round(float(flagged.mean()), 6),
+                     "differing_unflagged": int(np.sum(~same & ~flagged)),
+                     "data_errors": int(np.sum(ref["n"] < 0))}
         cpu = {"value": round(w.B / tc, 2), "unit": "rows/s" if args.entry == "draft" else "sequences/s",
                "cores": threads, "kind": "oracle", "sample": f"the whole batch ({w.B} sequences) once, "
                f"fp64 C oracle split over {threads} threads; {what} agree with the "
@@ -368,8 +388,12 @@ def main():
                    "early_exit_lead": (args.lead if args.lead > 0 else 1) if early else 0},
         "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
         "algorithmic_bytes": total_bytes, "mean_accepted": round(float(n.mean()), 4),
+        "host_ms_per_step": round(host_ms, 5),
         "rows_read": read_rows, "rows_full_pass": full_rows, "rows_minimum": min_rows,
-        "draw_rows": draw_rows,
+        "rows_past_first_rejection": read_rows - min_rows, "draw_rows": draw_rows,
+        "step_roofline": {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                          "frac": round(hbm_gbs / PEAK_HBM_GBS, 4), "bytes": total_bytes},
+        "oracle_check": check,
         "kernels_ms": {k: round(v, 5) for k, v in kern.items()},   # separate pass, all kernels evented
         "roofline": roofline, "cpu_baseline": cpu, "gen_s": round(t_gen, 2),
         "step_ms_events": {"median": round(step_ms[len(step_ms) // 2], 5), "p10": round(step_ms[6], 5),

@@ -33,6 +33,7 @@ _DEFAULTS = dict(seg_elems=0, chunk_elems=0, lead=-1, queue_mode=SV_QUEUE_OVERLA
 _OPTS = dict(_DEFAULTS)
 _TIMING = {"mask": 0, "every": 1, "seen": 0, "records": [], "free": []}
 _MAX_RECORDS = 256
+_POOL = 64          # event sets created when timing is turned on (none inside a timed loop)
 
 
 def _options_set() -> bool:
@@ -57,16 +58,22 @@ def _tuning(record: bool):
     return t, rec
 
 
+def _new_event_set():
+    ev = (ctypes.c_void_p * (2 * SV_NUM_KERNELS))()
+    check(lib().spec_timing_events_create(2 * SV_NUM_KERNELS, ev), "spec_timing_events_create")
+    return ev
+
+
 def _timing_record():
-    ev = _TIMING["free"].pop() if _TIMING["free"] else None
-    if ev is None:
-        ev = (ctypes.c_void_p * (2 * SV_NUM_KERNELS))()
-        check(lib().spec_timing_events_create(2 * SV_NUM_KERNELS, ev), "spec_timing_events_create")
-    rec = {"events": ev, "launched": ctypes.c_uint32(0), "mask": _TIMING["mask"]}
     recs = _TIMING["records"]
+    if _TIMING["free"]:
+        ev = _TIMING["free"].pop()
+    elif len(recs) >= _MAX_RECORDS or len(recs) >= _POOL:
+        ev = recs.pop(0)["events"]          # the oldest record's events are re-recorded
+    else:
+        ev = _new_event_set()
+    rec = {"events": ev, "launched": ctypes.c_uint32(0), "mask": _TIMING["mask"]}
     recs.append(rec)
-    if len(recs) > _MAX_RECORDS:
-        _TIMING["free"].append(recs.pop(0)["events"])
     return rec
 
 
@@ -423,8 +430,9 @@ def kernel_names() -> list:
 def timing(enable=True, every: int = 1) -> None:
     """Records HIP events around every kernel (True), the named kernels (an
     iterable of names from kernel_names()), or none (False) of one verify
-    call in `every`; kernel_times() reports them.  Turning it on or off
-    clears what was recorded."""
+    call in `every`; kernel_times() reports them over the last 64 recorded
+    calls.  Turning it on creates the events; turning it on or off clears
+    what was recorded."""
     names = kernel_names()
     if enable is True:
         mask = (1 << SV_NUM_KERNELS) - 1
@@ -440,6 +448,8 @@ def timing(enable=True, every: int = 1) -> None:
         raise ValueError("every must be >= 1")
     _TIMING["free"].extend(r["events"] for r in _TIMING["records"])
     _TIMING.update(mask=mask, every=int(every), seen=0, records=[])
+    while mask and len(_TIMING["free"]) < _POOL:
+        _TIMING["free"].append(_new_event_set())
 
 
 def kernel_times() -> dict:

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 
 SV_F32, SV_BF16 = 0, 1
 SV_K_MAX = 63
-SV_NUM_KERNELS = 11
+SV_NUM_KERNELS = 10
 SV_QUEUE_OVERLAP, SV_QUEUE_FINAL, SV_QUEUE_HANDOFF = 0, 1, 2
 SV_DRAW_AUTO, SV_DRAW_ONE, SV_DRAW_THREE = 0, 1, 2
 STATUS = {0: "SV_OK", -1: "SV_ERR_NULL", -2: "SV_ERR_SHAPE", -3: "SV_ERR_DTYPE",

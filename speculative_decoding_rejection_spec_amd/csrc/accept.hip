@@ -1,35 +1,23 @@
 // accept.hip -- the staged accept scan: one wave64 per sequence (the scan
-// itself is in accept_scan.h); with early exit also the scan over the
-// leading positions, which settles every sequence they decide.
+// itself is in accept_scan.h).  (Early exit's scan over the leading
+// positions runs inside row_lead.)
 #include "accept_scan.h"
 
 namespace sv {
 namespace {
 
-// One wave per workgroup: the scans spread over B compute units (the lead
-// scan of 256 sequences of k = 8: 9.7 -> 8.6 us against four waves per
-// workgroup).
+// One wave per workgroup: the scans spread over B compute units (256
+// sequences of k = 8: 9.7 -> 8.6 us against four waves per workgroup).
 __global__ __launch_bounds__(64) void accept_kernel(Problem p, Plan plan) {
     const int32_t b = blockIdx.x;
     if (plan.lead > 0 && plan.done[b]) return;     // decided by its leading positions
     accept_sequence<false>(p, plan, b);
 }
 
-// Early exit: the accept scan over the leading positions only.
-__global__ __launch_bounds__(64) void accept_lead_kernel(Problem p, Plan plan) {
-    const int32_t b = blockIdx.x;
-    accept_sequence<false>(p, plan, b, plan.lead, plan.done + b);
-}
-
 }  // namespace
 
 hipError_t launch_accept(const Problem& p, const Plan& plan, hipStream_t s) {
     accept_kernel<<<dim3(static_cast<uint32_t>(p.B)), dim3(64), 0, s>>>(p, plan);
-    return hipGetLastError();
-}
-
-hipError_t launch_accept_lead(const Problem& p, const Plan& plan, hipStream_t s) {
-    accept_lead_kernel<<<dim3(static_cast<uint32_t>(p.B)), dim3(64), 0, s>>>(p, plan);
     return hipGetLastError();
 }
 

@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void rest_draws_kernel(Problem p, Plan pl
                 __builtin_amdgcn_s_sleep(8);
             }
             if (ready) {
-                // (accept_lead found the sequence's offsets in order)
+                // (the lead scan found the sequence's offsets in order)
                 if (keep) accept_sequence<true>(p, plan, b, kKMax + 1, nullptr, nullptr, true, &pre, false);
                 else accept_sequence<true>(p, plan, b, kKMax + 1, nullptr, nullptr, true, nullptr, false);
             }

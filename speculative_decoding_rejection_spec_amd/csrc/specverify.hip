@@ -4,6 +4,8 @@
 // include/specverify.h.
 #include <stdlib.h>
 
+#include <atomic>
+#include <chrono>
 #include <mutex>
 
 #include "sv_internal.h"
@@ -30,13 +32,25 @@ constexpr int64_t kDefaultChunkElems = 8192;  // draw chunk length before roundi
 constexpr int32_t kAutoLead = -1;
 constexpr int64_t kAutoLeadBytes = 512ll << 20;
 constexpr int kMaxDevices = 64;
-enum { kKRowStats, kKAccept, kKDrawSums, kKDrawPick, kKRowLead, kKAcceptLead, kKRowDraft, kKRest, kKDrawAll,
-       kKSampleSums, kKSamplePick, kNumKernels };
+enum { kKRowStats, kKAccept, kKDrawSums, kKDrawPick, kKRowLead, kKRowDraft, kKRest, kKDrawAll, kKSampleSums,
+       kKSamplePick, kNumKernels };
 static_assert(kNumKernels == SV_NUM_KERNELS, "kernel count");
 
 const char* const kKernelNames[kNumKernels] = {"row_stats", "accept",   "draw_sums", "draw_pick",
-                                               "row_lead",  "accept_lead", "row_draft", "rest",
-                                               "draw_all",  "sample_sums", "sample_pick"};
+                                               "row_lead",  "row_draft", "rest",      "draw_all",
+                                               "sample_sums", "sample_pick"};
+
+// Call numbers: a counter word of the workspace that an earlier call (or
+// fresh memory) left carries another epoch and counts as zero.  Started
+// from the clock so a workspace reused by another process is unlikely to
+// hold a matching one; 0 is skipped.
+std::atomic<uint32_t> g_epoch{static_cast<uint32_t>(
+    std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761u)};
+uint32_t next_epoch() {
+    uint32_t e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+    if (e == 0) e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+    return e;
+}
 
 // One call's tuning (sv_tuning.h), resolved: every field in range.
 struct Tuning {
@@ -161,7 +175,8 @@ struct Geometry {
     int32_t nseg, nchunk;
     int64_t seg_len, chunk_len;
     size_t off_seg, off_task, off_csum, off_band_n, off_band_w, off_xlogit, off_done, off_sched,
-        off_blk_ctr, off_blk_seq, off_dlist, off_dlist_n, off_nbuf, off_early, off_early_n, off_aband, off_picked, bytes;
+        off_blk_ctr, off_blk_seq, off_dlist, off_dlist_n, off_nbuf, off_early, off_early_n, off_aband, off_picked,
+        off_lead_ctr, off_lead_clr, bytes;
 };
 
 // Splits a row of V logits into n <= max_pieces pieces of about `target`
@@ -221,6 +236,10 @@ bool make_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dtype, int64_
     off = align256(off + sizeof(int32_t) * static_cast<size_t>(B));
     g.off_picked = off;
     off = align256(off + sizeof(uint32_t) * static_cast<size_t>(B));
+    g.off_lead_ctr = off;
+    off = align256(off + sizeof(uint64_t) * static_cast<size_t>(B));
+    g.off_lead_clr = off;
+    off = align256(off + sizeof(uint32_t));
     g.bytes = off;
     return true;
 }
@@ -319,6 +338,9 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     plan.early_n = reinterpret_cast<uint32_t*>(ws + g.off_early_n);
     plan.aband = reinterpret_cast<int32_t*>(ws + g.off_aband);
     plan.picked = reinterpret_cast<uint32_t*>(ws + g.off_picked);
+    plan.lead_ctr = reinterpret_cast<uint64_t*>(ws + g.off_lead_ctr);
+    plan.lead_clr = reinterpret_cast<uint32_t*>(ws + g.off_lead_clr);
+    plan.epoch = next_epoch();
     plan.queue_mode = tu.queue_mode;
     Problem pr = p;
     if (!pr.out_n) pr.out_n = reinterpret_cast<int32_t*>(ws + g.off_nbuf);
@@ -365,13 +387,12 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
         return finish(ok);
     }
     // Row pass: one pass over every needed row, or (early exit) the leading
-    // positions, their accept scan, then the listed remainder.  Early exit
-    // outside the gathered form ends in two launches: the remaining rows
-    // with the draws beside them, and the picks (with the redo of anything
-    // that round left over, usually nothing).
+    // positions with their accept scans, then the listed remainder.  Early
+    // exit outside the gathered form ends in two launches: the remaining
+    // rows with the draws beside them, and the picks (with the redo of
+    // anything that round left over, usually nothing).
     if (plan.lead > 0)
-        ok = launch(kKRowLead, [&] { return launch_row_lead(pr, plan, stream); }) &&
-             launch(kKAcceptLead, [&] { return launch_accept_lead(pr, plan, stream); });
+        ok = launch(kKRowLead, [&] { return launch_row_lead(pr, plan, stream); });
     else
         ok = launch(kKRowStats, [&] { return launch_row_stats(pr, plan, stream); });
     if (plan.queued) {

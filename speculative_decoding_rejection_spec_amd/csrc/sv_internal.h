@@ -14,9 +14,10 @@
 //                  fp64 chunk sums;
 //   4. draw_pick   (draw.hip, draw_pass.h): one workgroup per sequence
 //                  locates the chunk that holds u * Z and the token inside it.
-// Early exit (Plan::lead > 0): steps 1 and 2 run over the leading positions
-// of every sequence (row_lead, accept_lead), which settles some sequences and
-// lists the remaining rows of the others; then one launch
+// Early exit (Plan::lead > 0): step 1 runs over the leading positions of
+// every sequence (row_lead), and the workgroup that finishes a sequence's
+// last leading segment runs its accept scan, which settles some sequences
+// and lists the remaining rows of the others; then one launch
 // (second_round.hip) streams those rows, runs the undecided sequences'
 // accept scans and every draw chunk beside them, and draw_pick picks.  The
 // gathered form instead streams the listed rows (row_list), then runs steps
@@ -161,6 +162,9 @@ struct Plan {
     int32_t queued;      // early exit with the draws beside the rows (not the gathered form)
     int32_t cus;         // compute units of the device
     int32_t queue_mode;  // SV_QUEUE_*: where the second round's draw chunks are summed
+    uint32_t epoch;      // this call's number (never 0): tags the counters below
+    uint64_t* lead_ctr;  // early exit: [B] epoch << 32 | leading segments of sequence b finished
+    uint32_t* lead_clr;  // early exit: the epoch of the call whose row_lead has cleared the list counters
 };
 
 // Plan::done values (early exit).
@@ -173,7 +177,6 @@ hipError_t launch_row_list(const Problem& p, const Plan& plan, const RestItem* l
 hipError_t launch_rest_draws(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_row_lead(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_accept(const Problem& p, const Plan& plan, hipStream_t s);
-hipError_t launch_accept_lead(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_draw_sums(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_draw_pick(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_draw_all(const Problem& p, const Plan& plan, hipStream_t s);
@@ -229,6 +232,22 @@ __device__ __forceinline__ void wait_stores() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt unchanged
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// One arrival on a counter word that packs a call's epoch (high 32 bits)
+// with the arrivals of that call (low 32 bits): a word an earlier call left
+// counts as none, so the counters need no clearing between calls.  Returns
+// the arrivals including this one.  (A compare-and-swap loop: each retry
+// means another arrival succeeded, so it ends.)
+__device__ __forceinline__ uint32_t arrive(uint64_t* word, uint32_t epoch) {
+    uint64_t old = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (;;) {
+        const uint64_t base = static_cast<uint32_t>(old >> 32) == epoch ? old : static_cast<uint64_t>(epoch) << 32;
+        const uint64_t want = base + 1;
+        if (__hip_atomic_compare_exchange_strong(word, &old, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT))
+            return static_cast<uint32_t>(want);
+    }
 }
 
 // c = log2(e) / T as the row pass uses it (the accept scan must form the same

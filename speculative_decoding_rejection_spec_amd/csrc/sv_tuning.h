@@ -25,7 +25,7 @@ extern "C" {
 
 /* Kernels a call may launch; bit i of sv_tuning_t::launched and events
  * 2i, 2i+1 belong to spec_verify_kernel_name(i). */
-#define SV_NUM_KERNELS 11
+#define SV_NUM_KERNELS 10
 
 /* Early exit's second round (queue_mode): SV_QUEUE_OVERLAP (the default)
  * sums the draw chunks beside the remaining rows, each accept scan lag_accept
