@@ -52,11 +52,17 @@ def using_library(path: str):
 
 
 def _load():
+    """The oracle library: liboracle.so next to oracle.c (built on first
+    use), or the build ORACLE_LIB names (the sanitizer test runs the pins
+    against an address/undefined-behaviour sanitizer build this way)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build()
-        _lib = _open(_LIB)
+        path = os.environ.get("ORACLE_LIB")
+        if not path:
+            path = _LIB
+            if not os.path.exists(path):
+                build()
+        _lib = _open(path)
     return _lib
 
 

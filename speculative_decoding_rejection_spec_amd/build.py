@@ -18,7 +18,8 @@ HIPCC_FLAGS = [
 
 
 def sources() -> list[str]:
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    """The HIP sources and the plain C++ host sources (host_args.cpp)."""
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
 def build(verbose: bool = False) -> str:

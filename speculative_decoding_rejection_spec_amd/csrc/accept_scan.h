@@ -109,7 +109,8 @@ __device__ __forceinline__ double log2_norm(const RowStat& r, float c) {
 // item is dispatched about lag blocks after the rows it needs.  The task
 // of a sampling sequence is marked unset until that accept item writes it.
 __device__ __forceinline__ void list_rest(const Problem& p, const Plan& plan, int32_t b, int64_t o, int32_t k,
-                                          int32_t limit, bool no_draft, bool greedy, bool skip_bonus_row) {
+                                          int32_t limit, bool no_draft, bool greedy, bool skip_bonus_row,
+                                          int32_t xtok) {
     const int lane = threadIdx.x & 63;
     const int64_t ntarget = p.total + p.B;
     const int32_t nseg = plan.nseg;
@@ -123,12 +124,16 @@ __device__ __forceinline__ void list_rest(const Problem& p, const Plan& plan, in
     const int64_t nchunk = plan.nchunk;
     const int64_t at = base + max(static_cast<int64_t>(0), i - plan.lag_a) +
                        nchunk * max(static_cast<int64_t>(0), i - plan.lag_c);
-    for (int32_t e = lane; e < cnt; e += 64) {
+    for (int32_t e0 = 0; e0 < cnt; e0 += 64) {           // (uniform trip count: every lane shuffles)
+        const int32_t e = e0 + lane;
         const int32_t j = e / nseg, sg = e - j * nseg;
         const bool tgt = j < nt;
         const int32_t pos = limit + (tgt ? j : j - nt);          // position in the sequence
+        // the drafted token of position pos, from the lane that holds it
+        const int32_t xs = __shfl(xtok, pos < 64 ? pos : 0, 64);
+        if (e >= cnt) continue;
         const int64_t row = tgt ? o + b + pos : o + pos;
-        const int32_t x = (!greedy && pos < k) ? p.tokens[o + pos] : -1;   // (validated by the scan)
+        const int32_t x = (!greedy && pos < k) ? xs : -1;
         plan.sched[at + e] = rest_item(b, static_cast<int32_t>(row), tgt ? kItemTarget : kItemDraft, sg, x);
         SegStat* st = plan.seg + (tgt ? row : ntarget + row) * nseg + sg;
         st->head = kUnset64;
@@ -164,9 +169,9 @@ __device__ __forceinline__ bool offsets_in_order(const Problem& p, int32_t b, in
     for (int32_t j0 = 0; j0 <= p.B; j0 += 64 * kU) {
         int32_t v[kU];
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
+        for (int u = 0; u < kU; ++u) {             // (clamped: no load under a branch)
             const int32_t j = j0 + u * 64 + lane;
-            v[u] = j <= p.B ? p.offsets[j] : 0;
+            v[u] = p.offsets[j <= p.B ? j : p.B];
         }
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
@@ -217,8 +222,9 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
     const int64_t k64 = o1 - o;
     const float Tf = p.temperature[b];
     const int64_t ntarget = p.total + p.B;
-    const bool ordered = !check_order || offsets_in_order(p, b, o, o1);
-    bool ok = ordered && o >= 0 && k64 >= 0 && k64 <= kKMax && o1 <= p.total && temperature_ok(Tf);
+    // (the order check, reading R28, comes after this lane's loads are
+    // issued; its verdict joins ok before anything depends on it)
+    bool ok = o >= 0 && k64 >= 0 && k64 <= kKMax && o1 <= p.total && temperature_ok(Tf);
     const int k = ok ? static_cast<int>(k64) : 0;
     const bool greedy = (Tf == 0.f);
     const bool gathered = p.draft_probs != nullptr;   // q_i(x_i) from the drafter
@@ -229,13 +235,50 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
     const int64_t trow = o + b + lane;             // this lane's target row
     const int64_t drow = o + lane;                 // this lane's draft row
 
+    // Every load this lane needs, issued together before any is used: the
+    // indices are clamped into their arrays so that no load sits under a
+    // branch (a value of a lane past k_b, or of a sequence found bad, is
+    // never used).  Rows of at most kSegBatch segments have their segment
+    // statistics loaded here too.
+    const bool drafts = p.total > 0;               // (tokens and draft rows may be absent otherwise)
+    const bool dstats = !greedy && !gathered && drafts;   // the draft rows' softmax enters the tests
+    const int64_t trow_c = trow < 0 ? 0 : (trow >= ntarget ? ntarget - 1 : trow);
+    const int64_t drow_c = drow < 0 ? 0 : (drow >= p.total ? p.total - 1 : drow);
+    const int32_t x_ld = drafts ? p.tokens[drow_c] : -1;
+    const float qg_ld = (gathered && drafts) ? p.draft_probs[drow_c] : NAN;
+    const float u_ld = p.uniforms[trow_c];
+    constexpr int kSegBatch = 4;
+    const bool batched = !pre && plan.nseg <= kSegBatch;
+    uint64_t th[kSegBatch] = {}, dh[kSegBatch] = {};
+    double ts[kSegBatch] = {}, ds[kSegBatch] = {};
+    float xt_ld = 0.f, xd_ld = 0.f;
+    // (no draft rows in the call: the draft-side loads read the target row
+    // again, so every address stays inside its array)
+    const int64_t drow_all = drafts ? ntarget + drow_c : trow_c;   // index among all rows
+    if (batched) {
+        const SegStat* st = plan.seg + trow_c * plan.nseg;
+        const SegStat* sd = plan.seg + drow_all * plan.nseg;
+#pragma unroll
+        for (int sg = 0; sg < kSegBatch; ++sg) {   // (segments past nseg reload the last one: unused)
+            const int sgc = sg < plan.nseg ? sg : plan.nseg - 1;
+            th[sg] = ld_co<kCo>(&st[sgc].head);
+            ts[sg] = ld_co<kCo>(&st[sgc].s);
+            dh[sg] = ld_co<kCo>(&sd[sgc].head);
+            ds[sg] = ld_co<kCo>(&sd[sgc].s);
+        }
+    }
+    if (!pre) {
+        xt_ld = ld_co<kCo>(&plan.xlogit[trow_c]);
+        xd_ld = ld_co<kCo>(&plan.xlogit[drow_all]);
+    }
+
     int32_t x = -1;
     float qg = NAN;
     if (ok && lane < k) {
-        x = p.tokens[drow];
+        x = x_ld;
         if (x < 0 || x >= p.V) ok = false;
         if (gathered && !greedy) {
-            qg = p.draft_probs[drow];
+            qg = qg_ld;
             if (!(qg > 0.f && qg <= 1.f)) ok = false;   // not a probability x could be drawn with
         }
     }
@@ -244,27 +287,32 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
     const bool tread = read && !(bonus_unread && lane == k);   // ... and its target row
     bool row_bad = false;                          // a row of this position has a non-finite maximum
     if (ok && lane <= k && tread) {
-        if (pre) {
+        if (pre || batched) {
             rt = RowStat{-INFINITY, INT32_MAX, -INFINITY, 0.0};
 #pragma unroll
-            for (int sg = 0; sg < kPolledSegs; ++sg)
-                if (sg < plan.nseg) merge_seg(rt, pre->th[sg], pre->ts[sg], false);
+            for (int sg = 0; sg < kSegBatch; ++sg) {
+                if (sg >= plan.nseg || (pre && sg >= kPolledSegs)) break;
+                merge_seg(rt, pre ? pre->th[sg] : th[sg], greedy ? 0.0 : (pre ? pre->ts[sg] : ts[sg]), greedy);
+            }
         } else {
             rt = merge_row<kCo>(plan.seg + trow * plan.nseg, plan.nseg, greedy);
         }
         row_bad = !(fabsf(rt.m) <= 3.4e38f);
         if (!greedy && !gathered && lane < k) {
-            if (pre) {
+            if (pre || batched) {
                 rd = RowStat{-INFINITY, INT32_MAX, -INFINITY, 0.0};
 #pragma unroll
-                for (int sg = 0; sg < kPolledSegs; ++sg)
-                    if (sg < plan.nseg) merge_seg(rd, pre->dh[sg], pre->ds[sg], false);
+                for (int sg = 0; sg < kSegBatch; ++sg) {
+                    if (sg >= plan.nseg || (pre && sg >= kPolledSegs)) break;
+                    merge_seg(rd, pre ? pre->dh[sg] : dh[sg], pre ? pre->ds[sg] : ds[sg], false);
+                }
             } else {
                 rd = merge_row<kCo>(plan.seg + (ntarget + drow) * plan.nseg, plan.nseg, false);
             }
             row_bad = row_bad || !(fabsf(rd.m) <= 3.4e38f);
         }
     }
+    if (check_order && !offsets_in_order(p, b, o, o1)) ok = false;
     ok = !__any(!ok);                              // one verdict for the whole sequence
 
     // Data error: the sequence's own token slots (when its offsets describe
@@ -286,22 +334,23 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
         return false;
     }
 
+    const float u_draw = __shfl(u_ld, k, 64);     // slot k_b: the draw uniform (k <= 63)
     bool reject = false;
     double px = NAN, qx = NAN;
     if (lane < k && read) {
         if (greedy) {
             reject = (x != rt.arg);
         } else {
-            const double zt = pre ? pre->xt : ld_co<kCo>(&plan.xlogit[trow]);   // captured by the row pass
+            const double zt = pre ? pre->xt : xt_ld;   // captured by the row pass
             px = exp2(zt * c - rt.R) / rt.S;
             if (gathered) {
                 qx = qg;
             } else {
-                const double zd = pre ? pre->xd : ld_co<kCo>(&plan.xlogit[ntarget + drow]);
+                const double zd = pre ? pre->xd : xd_ld;
                 qx = exp2(zd * c - rd.R) / rd.S;
             }
             const double alpha = fmin(1.0, px / qx);
-            reject = !(static_cast<double>(p.uniforms[trow]) < alpha);
+            reject = !(static_cast<double>(u_ld) < alpha);
         }
     }
     // A row with a non-finite maximum ends the scan where it stands, like a
@@ -312,7 +361,7 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
     if (!mask && (bonus_unread ? k > limit : k >= limit)) {   // undecided: rows past limit are needed
         if (done) {
             if (lane == 0) *done = kUndecided;
-            list_rest(p, plan, b, o, k, limit, greedy || gathered, greedy, bonus_unread);
+            list_rest(p, plan, b, o, k, limit, greedy || gathered, greedy, bonus_unread, x);
         }
         return false;
     }
@@ -341,7 +390,7 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
         t.m_t = __shfl(rt.m, n, 64);
         t.m_d = n < k ? __shfl(rd.m, n, 64) : 0.f;
         t.T = Tf;
-        t.u = p.uniforms[o + b + k];
+        t.u = u_draw;
         const double th = (!greedy && n < k) ? log2_norm(rt, c) - log2_norm(rd, c) : 0.0;
         t.theta = __shfl(th, n, 64);
     }
@@ -371,7 +420,7 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
         st_co<kCo>(&t->m_t, rt.m);
         st_co<kCo>(&t->m_d, n < k ? rd.m : 0.f);
         st_co<kCo>(&t->T, Tf);
-        st_co<kCo>(&t->u, p.uniforms[o + b + k]);
+        st_co<kCo>(&t->u, u_draw);
         st_co<kCo>(&t->theta, (!greedy && n < k) ? log2_norm(rt, c) - (pending ? 0.0 : log2_norm(rd, c)) : 0.0);
         if constexpr (kCo) wait_stores();          // the kind, written last, says the rest is visible
         st_co<kCo>(&t->kind, static_cast<int32_t>(greedy ? kNone : (n < k ? (pending ? kResidualPending : kResidual)

@@ -1,0 +1,92 @@
+// host_args.h -- the host-side checks and work geometry of a call: argument
+// validation, per-call tuning, segment and chunk lengths, and the layout of
+// the workspace.  Plain C++ (no device code), so that it also builds with a
+// host compiler under address and undefined-behaviour sanitizers.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/specverify.h"
+#include "sv_layout.h"
+#include "sv_tuning.h"
+
+namespace sv {
+namespace host {
+
+constexpr int64_t kDefaultSegElems = 65536;   // row-pass segment length before rounding
+// Row-pass segments are whole load windows: 256 lanes x 16 B x the window
+// depth (8 loads for bf16, 4 for fp32), so only a row's last segment can end
+// inside a window.
+inline int64_t row_unit(sv_dtype_t dtype) { return dtype == SV_BF16 ? 256 * 8 * 8 : 256 * 4 * 4; }
+constexpr int64_t kDefaultChunkElems = 8192;  // draw chunk length before rounding
+// Early exit is worth its two extra launches (~15 us) only when the rows
+// it may skip take longer than that to stream: automatic mode (lead -1)
+// uses one leading position when all rows together hold at least
+// kAutoLeadBytes, and one full pass otherwise.
+constexpr int32_t kAutoLead = -1;
+constexpr int64_t kAutoLeadBytes = 512ll << 20;
+
+// One call's tuning (sv_tuning.h), resolved: every field in range.
+struct Tuning {
+    int64_t seg_elems = 0, chunk_elems = 0;   // 0: automatic (auto_lengths)
+    int32_t lead = kAutoLead;
+    int32_t queue_mode = SV_QUEUE_OVERLAP;
+    int32_t lag_a = 0, lag_c = 0;             // 0: chosen from the resident grid
+    int32_t draw_mode = SV_DRAW_AUTO;
+    uint32_t timed = 0;                       // kernels whose events are recorded
+    hipEvent_t* events = nullptr;
+    uint32_t* launched = nullptr;
+};
+
+// Reads a caller's tuning (NULL: the defaults); false if a field is out of range.
+bool resolve(const sv_tuning_t* t, Tuning& r);
+
+// Automatic segment and chunk lengths: the defaults suit batches that fill
+// the GPU many times over (256 sequences of k = 8, V = 152064: 8704 row
+// workgroups, 4864 draw workgroups);
+// a small call is cut finer so its row pass still has about kRowBlocks
+// workgroups and its draw about kDrawBlocks (no finer than kMinSeg /
+// kMinChunk logits).
+constexpr int64_t kRowBlocks = 2048, kDrawBlocks = 1024;
+constexpr int64_t kMinSeg = 8192, kMinChunk = 1024;
+void auto_lengths(int32_t B, int64_t total, int64_t V, const Tuning& tu, int64_t* seg, int64_t* chunk);
+
+// Leading positions read first (early exit): the tuning's, or 1 when the
+// call's rows hold at least kAutoLeadBytes (0 for calls without drafts).
+int32_t effective_lead(int64_t B, int64_t total, int64_t V, sv_dtype_t dtype, const Tuning& tu);
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct Geometry {
+    int32_t nseg, nchunk;
+    int64_t seg_len, chunk_len;
+    size_t off_seg, off_task, off_csum, off_band_n, off_band_w, off_xlogit, off_done, off_sched,
+        off_blk_ctr, off_blk_seq, off_dlist, off_dlist_n, off_nbuf, off_early, off_early_n, off_aband, off_picked,
+        off_lead_ctr, off_lead_clr, bytes;
+};
+
+// Splits a row of V logits into n <= max_pieces pieces of about `target`
+// elements, each a multiple of `unit` long (see host_args.cpp).
+void split(int64_t V, int64_t target, int64_t max_pieces, int64_t unit, int64_t max_len, int32_t& n,
+           int64_t& len);
+
+// The segment and chunk geometry and the workspace layout of a call; false
+// when the second round's grid would not fit 2^31 - 1 workgroups.
+bool make_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dtype, int64_t seg_elems,
+                   int64_t chunk_elems, Geometry& g);
+
+inline bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+// The argument checks of spec_verify and its variants (before anything is enqueued).
+sv_status_t check_args(const void* target, const void* draft, const int32_t* tokens,
+                       const int32_t* offsets, int32_t k_uniform, int64_t total, int32_t B,
+                       int64_t V, sv_dtype_t dtype, const float* uniforms, const float* temperature,
+                       const int32_t* out_tokens, const int32_t* out_n);
+
+// Workspace bytes of a call (0 on bad sizes).
+size_t workspace_bytes_for(int32_t B, int64_t total, int64_t V, sv_dtype_t dtype, const Tuning& tu);
+
+}  // namespace host
+}  // namespace sv

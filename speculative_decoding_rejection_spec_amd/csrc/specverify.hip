@@ -8,6 +8,7 @@
 #include <chrono>
 #include <mutex>
 
+#include "host_args.h"
 #include "sv_internal.h"
 #include "sv_tuning.h"
 
@@ -18,19 +19,8 @@ static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES]
 
 namespace {
 using namespace sv;
+using namespace sv::host;
 
-constexpr int64_t kDefaultSegElems = 65536;   // row-pass segment length before rounding
-// Row-pass segments are whole load windows: 256 lanes x 16 B x the window
-// depth (8 loads for bf16, 4 for fp32), so only a row's last segment can end
-// inside a window.
-int64_t row_unit(sv_dtype_t dtype) { return dtype == SV_BF16 ? 256 * 8 * 8 : 256 * 4 * 4; }
-constexpr int64_t kDefaultChunkElems = 8192;  // draw chunk length before rounding
-// Early exit is worth its two extra launches (~15 us) only when the rows
-// it may skip take longer than that to stream: automatic mode (lead -1)
-// uses one leading position when all rows together hold at least
-// kAutoLeadBytes, and one full pass otherwise.
-constexpr int32_t kAutoLead = -1;
-constexpr int64_t kAutoLeadBytes = 512ll << 20;
 constexpr int kMaxDevices = 64;
 enum { kKRowStats, kKAccept, kKDrawSums, kKDrawPick, kKRowLead, kKRowDraft, kKRest, kKDrawAll, kKSampleSums,
        kKSamplePick, kNumKernels };
@@ -52,54 +42,6 @@ uint32_t next_epoch() {
     return e;
 }
 
-// One call's tuning (sv_tuning.h), resolved: every field in range.
-struct Tuning {
-    int64_t seg_elems = 0, chunk_elems = 0;   // 0: automatic (auto_lengths)
-    int32_t lead = kAutoLead;
-    int32_t queue_mode = SV_QUEUE_OVERLAP;
-    int32_t lag_a = 0, lag_c = 0;             // 0: chosen from the resident grid
-    int32_t draw_mode = SV_DRAW_AUTO;
-    uint32_t timed = 0;                       // kernels whose events are recorded
-    hipEvent_t* events = nullptr;
-    uint32_t* launched = nullptr;
-};
-
-bool resolve(const sv_tuning_t* t, Tuning& r) {
-    r = Tuning{};
-    if (!t) return true;
-    if (t->seg_elems < 0 || t->chunk_elems < 0 || t->lead < kAutoLead || t->lead > SV_K_MAX + 1 ||
-        t->queue_mode < SV_QUEUE_OVERLAP || t->queue_mode > SV_QUEUE_HANDOFF || t->lag_accept < 0 ||
-        t->lag_draw < 0 || t->draw_mode < SV_DRAW_AUTO || t->draw_mode > SV_DRAW_THREE)
-        return false;
-    r.seg_elems = t->seg_elems;
-    r.chunk_elems = t->chunk_elems;
-    r.lead = t->lead;
-    r.queue_mode = t->queue_mode;
-    r.lag_a = t->lag_accept;
-    r.lag_c = t->lag_draw;
-    r.draw_mode = t->draw_mode;
-    r.timed = t->timed;
-    r.events = t->events;
-    r.launched = t->launched;
-    return true;
-}
-
-// Automatic segment and chunk lengths: the defaults suit batches that fill
-// the GPU many times over (256 sequences of k = 8, V = 152064: 8704 row
-// workgroups, 4864 draw workgroups);
-// a small call is cut finer so its row pass still has about kRowBlocks
-// workgroups and its draw about kDrawBlocks (no finer than kMinSeg /
-// kMinChunk logits).
-constexpr int64_t kRowBlocks = 2048, kDrawBlocks = 1024;
-constexpr int64_t kMinSeg = 8192, kMinChunk = 1024;
-void auto_lengths(int32_t B, int64_t total, int64_t V, const Tuning& tu, int64_t* seg, int64_t* chunk) {
-    const int64_t rows = 2 * total + B;
-    int64_t s = rows * V / kRowBlocks, c = static_cast<int64_t>(B) * V / kDrawBlocks;
-    s = s < kMinSeg ? kMinSeg : (s > kDefaultSegElems ? kDefaultSegElems : s);
-    c = c < kMinChunk ? kMinChunk : (c > kDefaultChunkElems ? kDefaultChunkElems : c);
-    *seg = tu.seg_elems ? tu.seg_elems : s;
-    *chunk = tu.chunk_elems ? tu.chunk_elems : c;
-}
 // One pass: the draw runs as one launch (draw_all) while its workgroups
 // (sequences x chunks) fit one round on the CUs, counted at this many per
 // CU; a larger draw takes three launches (accept, draw_sums, draw_pick),
@@ -140,13 +82,6 @@ hipError_t device_info(int32_t dtype, int* cus, int* rest_per_cu) {
     return hipSuccess;
 }
 
-int32_t effective_lead(int64_t B, int64_t total, int64_t V, sv_dtype_t dtype, const Tuning& tu) {
-    if (tu.lead != kAutoLead) return tu.lead;
-    if (total == 0) return 0;                    // only bonus rows: nothing to skip
-    const int64_t bytes = (2 * total + B) * V * (dtype == SV_BF16 ? 2 : 4);
-    return bytes >= kAutoLeadBytes ? 1 : 0;
-}
-
 // Library-owned workspace, one grow-only buffer per device.
 void* g_ws[kMaxDevices] = {};
 size_t g_ws_bytes[kMaxDevices] = {};
@@ -168,107 +103,6 @@ sv_status_t scratch_address(void** out) {
     return SV_OK;
 }
 
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
-
-struct Geometry {
-    int32_t nseg, nchunk;
-    int64_t seg_len, chunk_len;
-    size_t off_seg, off_task, off_csum, off_band_n, off_band_w, off_xlogit, off_done, off_sched,
-        off_blk_ctr, off_blk_seq, off_dlist, off_dlist_n, off_nbuf, off_early, off_early_n, off_aband, off_picked,
-        off_lead_ctr, off_lead_clr, bytes;
-};
-
-// Splits a row of V logits into n <= max_pieces pieces of about `target`
-// elements (at most max_len when that fits max_pieces; max_len a multiple of
-// unit), each a multiple of `unit` elements long, none empty.
-void split(int64_t V, int64_t target, int64_t max_pieces, int64_t unit, int64_t max_len, int32_t& n,
-           int64_t& len) {
-    int64_t pieces = (V + target / 2) / target;
-    if (pieces < ceil_div(V, max_len)) pieces = ceil_div(V, max_len);
-    if (pieces < 1) pieces = 1;
-    if (pieces > max_pieces) pieces = max_pieces;
-    len = ceil_div(ceil_div(V, pieces), unit) * unit;
-    n = static_cast<int32_t>(ceil_div(V, len));
-}
-
-bool make_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dtype, int64_t seg_elems,
-                   int64_t chunk_elems, Geometry& g) {
-    const int64_t unit = row_unit(dtype);
-    split(V, seg_elems, 1 << 20, seg_elems >= unit ? unit : 8, max_seg_elems(dtype), g.nseg, g.seg_len);
-    split(V, chunk_elems, kMaxChunks, 8, V, g.nchunk, g.chunk_len);
-    const int64_t rows = 2 * total + B;
-    // (the second round's grid holds every row segment and every draw chunk)
-    if (rows * g.nseg + static_cast<int64_t>(B) * (1 + g.nchunk) > 0x7FFFFFFFll) return false;
-    size_t off = 0;
-    g.off_seg = off;
-    off = align256(off + sizeof(SegStat) * static_cast<size_t>(rows) * g.nseg);
-    g.off_task = off;
-    off = align256(off + sizeof(DrawTask) * static_cast<size_t>(B));
-    g.off_csum = off;
-    off = align256(off + sizeof(ChunkSums) * kWaves * static_cast<size_t>(B) * g.nchunk);
-    g.off_band_n = off;
-    off = align256(off + sizeof(int32_t) * kWaves * static_cast<size_t>(B) * g.nchunk);
-    g.off_band_w = off;
-    off = align256(off + sizeof(double) * 2 * kWaves * kWaveCap * static_cast<size_t>(B) * g.nchunk);
-    g.off_xlogit = off;
-    off = align256(off + sizeof(float) * static_cast<size_t>(rows));
-    g.off_done = off;
-    off = align256(off + sizeof(int32_t) * static_cast<size_t>(B));
-    g.off_sched = off;
-    off = align256(off + sizeof(RestItem) * (static_cast<size_t>(rows) * g.nseg +
-                                             static_cast<size_t>(B) * (1 + g.nchunk)));
-    g.off_blk_ctr = off;
-    off = align256(off + sizeof(uint64_t));
-    g.off_blk_seq = off;
-    off = align256(off + sizeof(int32_t) * static_cast<size_t>(B));
-    g.off_dlist = off;
-    off = align256(off + sizeof(RestItem) * static_cast<size_t>(B) * g.nseg);
-    g.off_dlist_n = off;
-    off = align256(off + sizeof(uint32_t));
-    g.off_nbuf = off;                                   // accept counts of spec_draft_sample
-    off = align256(off + sizeof(int32_t) * static_cast<size_t>(B));
-    g.off_early = off;
-    off = align256(off + sizeof(int32_t) * static_cast<size_t>(B));
-    g.off_early_n = off;
-    off = align256(off + sizeof(uint32_t));
-    g.off_aband = off;
-    off = align256(off + sizeof(int32_t) * static_cast<size_t>(B));
-    g.off_picked = off;
-    off = align256(off + sizeof(uint32_t) * static_cast<size_t>(B));
-    g.off_lead_ctr = off;
-    off = align256(off + sizeof(uint64_t) * static_cast<size_t>(B));
-    g.off_lead_clr = off;
-    off = align256(off + sizeof(uint32_t));
-    g.bytes = off;
-    return true;
-}
-
-bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
-
-sv_status_t check_args(const void* target, const void* draft, const int32_t* tokens,
-                       const int32_t* offsets, int32_t k_uniform, int64_t total, int32_t B,
-                       int64_t V, sv_dtype_t dtype, const float* uniforms, const float* temperature,
-                       const int32_t* out_tokens, const int32_t* out_n) {
-    if (B < 0 || total < 0) return SV_ERR_SHAPE;
-    if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
-    if (!target || !uniforms || !temperature || !out_tokens || !out_n) return SV_ERR_NULL;
-    if (total > 0 && (!draft || !tokens)) return SV_ERR_NULL;
-    if (V < 1 || V > 0x7FFFFFFFll) return SV_ERR_SHAPE;
-    if (!offsets) {
-        if (k_uniform < 0 || k_uniform > SV_K_MAX || total != static_cast<int64_t>(B) * k_uniform)
-            return SV_ERR_SHAPE;
-    } else if (total > static_cast<int64_t>(B) * SV_K_MAX) {
-        return SV_ERR_SHAPE;
-    }
-    const size_t elt = dtype == SV_BF16 ? 2 : 4;
-    if (!aligned(target, elt) || !aligned(draft, elt) || !aligned(tokens, 4) ||
-        !aligned(offsets, 4) || !aligned(uniforms, 4) || !aligned(temperature, 4) ||
-        !aligned(out_tokens, 4) || !aligned(out_n, 4))
-        return SV_ERR_ALIGN;
-    return SV_OK;
-}
-
 // Returns a workspace of at least `bytes` on the current device.
 sv_status_t owned_workspace(size_t bytes, void** out) {
     int dev = 0;
@@ -286,16 +120,6 @@ sv_status_t owned_workspace(size_t bytes, void** out) {
     }
     *out = g_ws[dev];
     return SV_OK;
-}
-
-size_t workspace_bytes_for(int32_t B, int64_t total, int64_t V, sv_dtype_t dtype, const Tuning& tu) {
-    if (B < 0 || total < 0 || V < 1 || V > 0x7FFFFFFFll) return 0;
-    if (dtype != SV_F32 && dtype != SV_BF16) return 0;
-    Geometry g;
-    int64_t seg_elems, chunk_elems;
-    auto_lengths(B, total, V, tu, &seg_elems, &chunk_elems);
-    if (!make_geometry(B, total, V, dtype, seg_elems, chunk_elems, g)) return 0;
-    return g.bytes;
 }
 
 // sample: the drafter's sampling step (spec_draft_sample), k = 0 for every

@@ -1,0 +1,80 @@
+// sv_layout.h -- sizes and records of the workspace, shared by the kernels
+// and the host code that lays the workspace out (plain C++: the host-side
+// argument checks in host_args.cpp compile with any C++17 compiler).
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/specverify.h"
+
+namespace sv {
+
+constexpr int kThreads = 256;          // workgroup size of every kernel (4 x wave64)
+constexpr int kWaves = kThreads / 64;
+constexpr int kKMax = SV_K_MAX;
+constexpr int kWaveCap = 8;            // band tokens listed per wave of a draw chunk
+constexpr int kMaxChunks = 256;        // draw chunks per row (the pick keeps a mass per sub-chunk in LDS)
+// Row pass: the longest segment, so that each lane's fp32 partial sums
+// take at most 40 vectors (16 bytes: 8 bf16 or 4 fp32 logits) each.
+constexpr int64_t max_seg_elems(int32_t dtype) {
+    return 40 * kThreads * (dtype == SV_BF16 ? 8 : 4);
+}
+
+// Statistics of one segment of one logit row, as two 64-bit words, each
+// written and read whole.  `head` packs the largest logit m of the segment
+// (exact; low 32 bits, fp32) with, for sampling rows, the integer-valued
+// reference exponent R >= max(z) * c - 2, c = log2(e)/T (row_scale below;
+// fp32 bits), and for greedy rows the lowest token id holding m.  `s` is, for
+// sampling rows, the sum over the segment of 2^(z*c - R) (0 for greedy
+// rows), so every rescale is an exact power of two.  kUnset64 in a word
+// marks it not yet written; a captured logit not yet written is kUnset32.
+struct SegStat {
+    uint64_t head;
+    double s;
+};
+constexpr uint64_t kUnset64 = ~0ull;
+constexpr uint32_t kUnset32 = ~0u;
+
+// kResidualPending: a residual draw of the gathered form, whose draft row n
+// is read after the accept scan (its maximum and normaliser come from that
+// row's SegStats; DrawTask::theta holds log2 S_p until then).
+// kTaskUnset: early exit's second round has not yet written the task (its
+// kind is written last, after the other fields are visible).
+// kBonusSelf: a bonus draw whose row the row pass did not read (early exit
+// beside the draws): the draw takes the weights relative to references of
+// its own, and the pick checks the row's maximum (a non-finite one makes the
+// sequence a data error).
+enum : int32_t { kTaskUnset = -1, kNone = 0, kResidual = 1, kBonus = 2, kResidualPending = 3, kBonusSelf = 4 };
+
+// The draw one sequence still needs after the accept scan.
+struct DrawTask {
+    int32_t kind;      // kNone (greedy, error), kResidual (n < k), kBonus or kBonusSelf (n = k)
+    int32_t out_slot;  // index into out_tokens of the emitted token
+    int64_t trow;      // target row at position n
+    int64_t drow;      // draft row at position n (kResidual only)
+    float m_t, m_d;    // exact maxima of those rows
+    float T, u;        // temperature and the draw uniform
+    double theta;      // log2(S_p / S_q) from the row pass: p_v > q_v iff d_v > theta
+};
+
+// Partial sums of the draw over one sub-chunk (fp64).
+struct ChunkSums {
+    double sp;   // sum of w_t = exp((z_t - m_t)/T) over the chunk
+    double sq;   // sum of w_d over the chunk (residual)
+    double a;    // sum of w_t over tokens robustly classified p > q
+    double b;    // sum of w_d over the same tokens
+};
+
+// One work item of the second early-exit round: a row segment (kind
+// kItemDraft / kItemTarget), the accept scan of an undecided sequence
+// (kItemAccept), or one draw chunk of such a sequence (kItemChunk).  The
+// gathered form's row lists use the row-segment kinds.
+enum : int32_t { kItemDraft = 0, kItemTarget = 1, kItemAccept = 2, kItemChunk = 3 };
+struct RestItem {
+    int32_t b;      // row segments: the sequence; accept and draw items: its block (listing order)
+    int32_t row;    // row segments: row index in its array
+    int32_t kseg;   // kind << 28 | segment (row segments) or chunk (draw items)
+    int32_t x;      // row segments: the drafted token whose logit the row's segments capture, or -1
+};
+
+}  // namespace sv
