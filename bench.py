@@ -42,9 +42,10 @@ EVENT_EVERY = 8
 METRIC = "sequences verified/s and achieved HBM GB/s (% of peak), B=256 k=8 V=152064 bf16"
 # Counter summaries per roofline kernel, and the sources each kernel is built from.
 COUNTERS = {"row_stats": os.path.join(ROOT, "profiles", "row_stats_c4_counters.txt"),
-            "rest": os.path.join(ROOT, "profiles", "second_round_c4_counters.txt")}
+            "rounds": os.path.join(ROOT, "profiles", "rounds_c4_counters.txt")}
 KERNEL_SOURCES = {"row_stats": ["row_stats.hip", "row_pass.h", "sv_internal.h"],
-                  "rest": ["second_round.hip", "row_pass.h", "accept_scan.h", "draw_pass.h", "sv_internal.h"]}
+                  "rounds": ["second_round.hip", "lead_pass.h", "row_pass.h", "accept_scan.h", "draw_pass.h",
+                             "sv_internal.h", "sv_layout.h"]}
 
 
 def code_text(src: str) -> str:
@@ -213,16 +214,16 @@ def main():
     step(0)
     torch.cuda.synchronize()
     launched = sv.kernel_times()
-    early = "row_lead" in launched
+    queued = "rounds" in launched
+    early = queued or "row_lead" in launched
     sv.timing(False)
     # The roofline kernel: the row pass (one launch, or the two launches of
-    # early exit in the gathered form), or -- early exit -- the second round,
-    # the dominant launch, which streams the remaining rows and every draw row.
-    queued = "rest" in launched
+    # early exit in the gathered form), or -- early exit -- the two-round
+    # launch, which streams every row the step reads and every draw row.
     if "sample_sums" in launched:                # the draft sampler: one read of each row
         roof = ["sample_sums"]
     elif queued:
-        roof = ["rest"]
+        roof = ["rounds"]
     else:
         roof = ["row_lead", "row_stats"] if early else ["row_stats"]
     if "row_draft" in launched:
@@ -294,7 +295,6 @@ def main():
         decided = (n < L) | (k < L) | (dsamp & (k <= L))
         rest_rows = np.where(decided, 0, (k - L + 1) - dsamp + np.where(dsamp, k - L, 0))
         read_rows = int(np.sum(lead_rows + rest_rows))
-        second_rows = int(np.sum(rest_rows))
     else:
         read_rows = full_rows
     if gathered:                                 # the draft row at each rejection
@@ -317,9 +317,9 @@ def main():
     counters_apply = (args.workload == "c4" and args.entry == "verify" and args.seg == 0 and args.chunk == 0 and
                       args.lead in (-1, 0, 1) and args.queue == 0 and list(args.queue_lag) == [0, 0])
     if k1_live is not None:
-        # The row pass reads every needed row once; the second round also
+        # The row pass reads every needed row once; the two-round launch also
         # reads the draw rows (unless they are all left to the pick launch).
-        kbytes = (second_rows + (draw_rows if args.queue == 0 else 0)) * row_bytes if queued else k1_bytes
+        kbytes = (read_rows + (draw_rows if args.queue == 0 else 0)) * row_bytes if queued else k1_bytes
         achieved = kbytes / (k1_live / 1e3) / 1e9
         roofline = {"bound": "hbm", "kernel": roof_kernel, "achieved": round(achieved, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),

@@ -29,7 +29,7 @@ __all__ = [
 
 # ---- per-call options (csrc/sv_tuning.h), held by this binding ------------
 _DEFAULTS = dict(seg_elems=0, chunk_elems=0, lead=-1, queue_mode=SV_QUEUE_OVERLAP, lag_accept=0, lag_draw=0,
-                 draw_mode=SV_DRAW_AUTO)
+                 draw_mode=SV_DRAW_AUTO, item_polls=0)
 _OPTS = dict(_DEFAULTS)
 _TIMING = {"mask": 0, "every": 1, "seen": 0, "records": [], "free": []}
 _MAX_RECORDS = 256
@@ -394,10 +394,13 @@ def set_early_exit(lead_positions: int = -1) -> None:
     _set(lead=int(lead_positions))
 
 
-def set_queue(mode: int = SV_QUEUE_OVERLAP, lag_accept: int = 0, lag_draw: int = 0) -> None:
+def set_queue(mode: int = SV_QUEUE_OVERLAP, lag_accept: int = 0, lag_draw: int = 0, item_polls: int = 0) -> None:
     """Where early exit's second-round accept scans and draw chunks run, and
-    their lags in sequences (0 = automatic); outputs do not change."""
-    _set(queue_mode=int(mode), lag_accept=int(lag_accept), lag_draw=int(lag_draw))
+    their lags in sequences (0 = automatic); outputs do not change.
+    item_polls: bound of a second-round workgroup's wait for its schedule
+    entry (0 = automatic); a wait that runs out makes every sequence of the
+    call a data error (a test hook for that path)."""
+    _set(queue_mode=int(mode), lag_accept=int(lag_accept), lag_draw=int(lag_draw), item_polls=int(item_polls))
 
 
 def set_draw(mode: int = SV_DRAW_AUTO) -> None:

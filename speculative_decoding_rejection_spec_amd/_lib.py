@@ -29,7 +29,8 @@ _P, _I32, _I64, _SZ, _U32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, cty
 class Tuning(ctypes.Structure):
     """sv_tuning_t of csrc/sv_tuning.h (per-call test and benchmark options)."""
     _fields_ = [("seg_elems", _I64), ("chunk_elems", _I64), ("lead", _I32), ("queue_mode", _I32),
-                ("lag_accept", _I32), ("lag_draw", _I32), ("draw_mode", _I32), ("timed", _U32),
+                ("lag_accept", _I32), ("lag_draw", _I32), ("draw_mode", _I32), ("item_polls", _U32),
+                ("timed", _U32),
                 ("events", _P), ("launched", _P)]
 
 

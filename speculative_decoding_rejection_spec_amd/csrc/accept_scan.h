@@ -99,59 +99,96 @@ __device__ __forceinline__ double log2_norm(const RowStat& r, float c) {
     return log2(r.S) + (static_cast<double>(r.R) - static_cast<double>(r.m) * c);
 }
 
-// Early exit: lists the rows sequence b still needs (target rows limit..k,
-// then draft rows limit..k-1 unless no_draft), nseg segments each, as block
-// i of the second round's schedule, and marks their statistics and
-// captured logits unset.  The schedule is block after block in listing
-// order; after block i come the accept item of block i - lag_a and the
-// nchunk draw items of block i - lag_c (those of the last blocks follow the
-// whole schedule, where the second round finds them by arithmetic), so an
-// item is dispatched about lag blocks after the rows it needs.  The task
-// of a sampling sequence is marked unset until that accept item writes it.
+// Early exit: lists what sequence b needs from the second round.  An
+// undecided sequence becomes block i of the schedule: its remaining rows
+// (target rows limit..k, then draft rows limit..k-1 unless no_draft), nseg
+// segments each, whose statistics and captured logits it marks unset; after
+// block i come the accept item of block i - lag_a and the nchunk draw items
+// of block i - lag_c (those of the last blocks follow the whole schedule,
+// where the second round finds them by arithmetic), so an item is
+// dispatched about lag blocks after the rows it needs.  The task of an
+// undecided sampling sequence is marked unset until its accept item writes
+// it.  A sampling sequence its leading positions settled (settled) lists
+// only its nchunk draw chunks (kItemChunkSeq), at the schedule's current
+// end: its task is already written, so they can run at once, beside the
+// rows of the sequences listed around it.
+//
+// One atomic add on blk_ctr (undecided blocks << 32 | row segments and
+// settled chunks listed) places the listing; what the items need is
+// written through and visible before the entries, which carry the call's
+// epoch (store_entry).
+//
+// The place in the schedule is taken first (list_reserve, lane 0's atomic
+// add); a settled sequence takes it as soon as its scan decides, before its
+// task is written, so that the listings keep the order in which the scans
+// decide.
+__device__ __forceinline__ uint64_t list_reserve(const Plan& plan, bool settled, int32_t cnt) {
+    uint64_t pos = 0;
+    if ((threadIdx.x & 63) == 0)
+        pos = atomicAdd(reinterpret_cast<unsigned long long*>(plan.blk_ctr),
+                        (settled ? 0ull : (1ull << 32)) | static_cast<uint64_t>(cnt));
+    return pos;                                    // (lane 0's; list_rest broadcasts it)
+}
+
 __device__ __forceinline__ void list_rest(const Problem& p, const Plan& plan, int32_t b, int64_t o, int32_t k,
                                           int32_t limit, bool no_draft, bool greedy, bool skip_bonus_row,
-                                          int32_t xtok) {
+                                          int32_t xtok, bool settled, uint64_t reserved = ~0ull) {
     const int lane = threadIdx.x & 63;
     const int64_t ntarget = p.total + p.B;
     const int32_t nseg = plan.nseg;
-    const int32_t nt = k - limit + (skip_bonus_row ? 0 : 1), nd = no_draft ? 0 : k - limit;
-    const int32_t cnt = (nt + nd) * nseg;
-    uint64_t pos = 0;
-    if (lane == 0) pos = atomicAdd(reinterpret_cast<unsigned long long*>(plan.blk_ctr),
-                                   (1ull << 32) | static_cast<uint64_t>(cnt));
+    const int64_t nchunk = plan.nchunk;
+    const int32_t nt = settled ? 0 : k - limit + (skip_bonus_row ? 0 : 1);
+    const int32_t nd = (settled || no_draft) ? 0 : k - limit;
+    const int32_t cnt = settled ? static_cast<int32_t>(nchunk) : (nt + nd) * nseg;
+    uint64_t pos = reserved != ~0ull ? reserved : list_reserve(plan, settled, cnt);
     pos = __shfl(pos, 0, 64);
     const int64_t i = static_cast<int64_t>(pos >> 32), base = static_cast<int64_t>(pos & 0xffffffffu);
-    const int64_t nchunk = plan.nchunk;
     const int64_t at = base + max(static_cast<int64_t>(0), i - plan.lag_a) +
                        nchunk * max(static_cast<int64_t>(0), i - plan.lag_c);
+    if (settled) {
+        wait_stores();                             // (the task, written before the call)
+        for (int32_t c = lane; c < cnt; c += 64)
+            store_entry(plan.sched + at + c, rest_item(b, 0, kItemChunkSeq, c, -1), plan.epoch);
+        return;
+    }
+    // the marks first, visible before any entry that leads to them
+    for (int32_t e = lane; e < cnt; e += 64) {
+        const int32_t j = e / nseg, sg = e - j * nseg;
+        const bool tgt = j < nt;
+        const int32_t ps = limit + (tgt ? j : j - nt);            // position in the sequence
+        const int64_t row = tgt ? o + b + ps : o + ps;
+        SegStat* st = plan.seg + (tgt ? row : ntarget + row) * nseg + sg;
+        st_co<true>(&st->head, kUnset64);
+        st_co<true>(&st->s, __longlong_as_double(static_cast<long long>(kUnset64)));
+        if (sg == 0 && !greedy) st_co<true>(&plan.xlogit[tgt ? row : ntarget + row], __uint_as_float(kUnset32));
+    }
+    if (lane == 0 && !greedy) st_co<true>(&plan.task[b].kind, static_cast<int32_t>(kTaskUnset));
+    wait_stores();
+    if (lane == 0) st_co<true>(plan.blk_seq + i, (static_cast<uint64_t>(plan.epoch) << 32) | static_cast<uint32_t>(b));
     for (int32_t e0 = 0; e0 < cnt; e0 += 64) {           // (uniform trip count: every lane shuffles)
         const int32_t e = e0 + lane;
         const int32_t j = e / nseg, sg = e - j * nseg;
         const bool tgt = j < nt;
-        const int32_t pos = limit + (tgt ? j : j - nt);          // position in the sequence
-        // the drafted token of position pos, from the lane that holds it
-        const int32_t xs = __shfl(xtok, pos < 64 ? pos : 0, 64);
+        const int32_t ps = limit + (tgt ? j : j - nt);
+        // the drafted token of position ps, from the lane that holds it
+        const int32_t xs = __shfl(xtok, ps < 64 ? ps : 0, 64);
         if (e >= cnt) continue;
-        const int64_t row = tgt ? o + b + pos : o + pos;
-        const int32_t x = (!greedy && pos < k) ? xs : -1;
-        plan.sched[at + e] = rest_item(b, static_cast<int32_t>(row), tgt ? kItemTarget : kItemDraft, sg, x);
-        SegStat* st = plan.seg + (tgt ? row : ntarget + row) * nseg + sg;
-        st->head = kUnset64;
-        st->s = __longlong_as_double(static_cast<long long>(kUnset64));
-        if (sg == 0 && !greedy) plan.xlogit[tgt ? row : ntarget + row] = __uint_as_float(kUnset32);
+        const int64_t row = tgt ? o + b + ps : o + ps;
+        const int32_t x = (!greedy && ps < k) ? xs : -1;
+        store_entry(plan.sched + at + e, rest_item(b, static_cast<int32_t>(row), tgt ? kItemTarget : kItemDraft, sg, x),
+                    plan.epoch);
     }
     int64_t q = at + cnt;
     if (i >= plan.lag_a) {
-        if (lane == 0) plan.sched[q] = rest_item(static_cast<int32_t>(i - plan.lag_a), 0, kItemAccept, 0, -1);
+        if (lane == 0)
+            store_entry(plan.sched + q, rest_item(static_cast<int32_t>(i - plan.lag_a), 0, kItemAccept, 0, -1),
+                        plan.epoch);
         ++q;
     }
     if (i >= plan.lag_c)
         for (int32_t c = lane; c < nchunk; c += 64)
-            plan.sched[q + c] = rest_item(static_cast<int32_t>(i - plan.lag_c), 0, kItemChunk, c, -1);
-    if (lane == 0) {
-        plan.blk_seq[i] = b;
-        if (!greedy) plan.task[b].kind = kTaskUnset;
-    }
+            store_entry(plan.sched + q + c, rest_item(static_cast<int32_t>(i - plan.lag_c), 0, kItemChunk, c, -1),
+                        plan.epoch);
 }
 
 // Whether sequence b's offsets are in order with every other sequence's
@@ -190,13 +227,13 @@ __device__ __forceinline__ bool offsets_in_order(const Problem& p, int32_t b, in
 // Early exit: only the rows of positions < limit have been read.  If their
 // tests already decide the outcome (a rejection among them, or every
 // position including the bonus row read) the scan writes everything and
-// sets *done to kDecided, or to kDecidedEarlyDraw (listing b in plan.early)
-// when the draw rows have been read too; otherwise (the first rejection, if
-// any, lies at or past limit) it writes nothing but *done = kUndecided, and
-// runs again once the remaining
-// rows are read; it then lists those rows' segments (list_rest).  The
-// scan stops at the first rejection, like the pages'
-// loop over positions, so rows after it never influence the result.
+// sets *done to kDecided, or to kDecidedEarlyDraw for a sampling sequence,
+// whose draw chunks it then lists for the second round (list_rest);
+// otherwise (the first rejection, if any, lies at or past limit) it writes
+// nothing but *done = kUndecided, lists the rows still needed (list_rest)
+// and runs again once they are read.  The scan stops at the first
+// rejection, like the pages' loop over positions, so rows after it never
+// influence the result.
 // Diagnostics of rows that were not read are NaN.  Returns (the same in
 // every lane) whether the scan settled the sequence with a draw still to
 // make, i.e. wrote a DrawTask other than kNone.
@@ -361,7 +398,7 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
     if (!mask && (bonus_unread ? k > limit : k >= limit)) {   // undecided: rows past limit are needed
         if (done) {
             if (lane == 0) *done = kUndecided;
-            list_rest(p, plan, b, o, k, limit, greedy || gathered, greedy, bonus_unread, x);
+            list_rest(p, plan, b, o, k, limit, greedy || gathered, greedy, bonus_unread, x, false);
         }
         return false;
     }
@@ -370,14 +407,13 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
         data_error();
         return false;
     }
-    if (done && lane == n) {
-        // Settled by its leading positions: a sampling sequence whose draw
-        // rows have been read can draw beside the remaining row pass.
-        // (not in the gathered form, whose second round only streams rows)
-        const bool early_draw = !greedy && !gathered;
-        *done = early_draw ? kDecidedEarlyDraw : kDecided;
-        if (early_draw) plan.early[atomicAdd(plan.early_n, 1u)] = b;
-    }
+    // Settled by its leading positions: a sampling sequence draws in the
+    // second round, beside the remaining rows (not in the gathered form,
+    // whose second round only streams rows); it is listed below, once its
+    // task is written.
+    const bool early_draw = done && !greedy && !gathered;
+    if (done && lane == n) *done = early_draw ? kDecidedEarlyDraw : kDecided;
+    const uint64_t reserved = early_draw ? list_reserve(plan, true, plan.nchunk) : ~0ull;
 
     const int32_t kind = greedy ? kNone : (n < k ? kResidual : (bonus_unread ? kBonusSelf : kBonus));
     if (task_out) {
@@ -426,6 +462,7 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
         st_co<kCo>(&t->kind, static_cast<int32_t>(greedy ? kNone : (n < k ? (pending ? kResidualPending : kResidual)
                                                                           : kind)));
     }
+    if (early_draw) list_rest(p, plan, b, o, k, limit, true, greedy, bonus_unread, x, true, reserved);
     if (p.out_p && lane < k) {
         p.out_p[drow] = static_cast<float>(px);
         p.out_q[drow] = static_cast<float>(qx);

@@ -27,7 +27,9 @@ __global__ __launch_bounds__(kThreads) void draw_sums_kernel(Problem p, Plan pla
 // wait in the second round ran out (or every sequence, SV_QUEUE_FINAL) is
 // redone here first -- its accept scan if its leading positions left it
 // undecided, then every chunk -- with the chunk pass of a 256-thread
-// workgroup (the other threads only take part in its barriers).
+// workgroup (the other threads only take part in its barriers).  A call
+// whose second round could not find an item's work (never expected) makes
+// every sequence a data error.
 // (At 4 waves per SIMD two 512-thread workgroups share a CU: at most 128 VGPRs.)
 template <int DT, int kPickThreads>
 __global__ __launch_bounds__(kPickThreads, 4) void draw_pick_kernel(Problem p, Plan plan) {
@@ -40,8 +42,23 @@ __global__ __launch_bounds__(kPickThreads, 4) void draw_pick_kernel(Problem p, P
     // The loads of the common path are issued together, before anything
     // depends on them: the redo flag, the task, chunk threadIdx.x's sums.
     const int32_t ab = plan.queued ? plan.aband[b] : 0;
+    const uint32_t stall = plan.queued ? *plan.stall : 0u;
     const DrawTask task0 = load_task<false>(p, plan, b);
     const PickPrefetch pf = pick_prefetch<false>(plan, b);
+    auto data_error = [&]() {
+        const int64_t o = p.offsets ? static_cast<int64_t>(p.offsets[b]) : static_cast<int64_t>(b) * p.k_uniform;
+        const int64_t o1 = p.offsets ? static_cast<int64_t>(p.offsets[b + 1]) : o + p.k_uniform;
+        if (o >= 0 && o1 >= o && o1 - o <= kKMax && o1 <= p.total)
+            for (int64_t i = threadIdx.x; i <= o1 - o; i += kPickThreads) p.out_tokens[o + b + i] = -1;
+        if (threadIdx.x == 0) {
+            p.out_n[b] = -1;
+            if (p.out_emit_prob) p.out_emit_prob[b] = NAN;
+        }
+    };
+    if (plan.queued && stall == plan.epoch) {
+        data_error();
+        return;
+    }
     const bool redo = plan.queued && (plan.queue_mode == SV_QUEUE_FINAL || ab != 0);
     if (redo) {
         load_exp2_table(tbl, kPickThreads);
@@ -65,13 +82,7 @@ __global__ __launch_bounds__(kPickThreads, 4) void draw_pick_kernel(Problem p, P
     if (task.kind == kResidual && !(fabsf(task.m_d) <= 3.4e38f)) {
         // The gathered form reads the rejected position's draft row only
         // now: a non-finite maximum there makes the sequence a data error.
-        const int64_t o = p.offsets ? static_cast<int64_t>(p.offsets[b]) : static_cast<int64_t>(b) * p.k_uniform;
-        const int64_t k = p.offsets ? static_cast<int64_t>(p.offsets[b + 1]) - o : p.k_uniform;
-        for (int64_t i = threadIdx.x; i <= k; i += kPickThreads) p.out_tokens[o + b + i] = -1;
-        if (threadIdx.x == 0) {
-            p.out_n[b] = -1;
-            if (p.out_emit_prob) p.out_emit_prob[b] = NAN;
-        }
+        data_error();
         return;
     }
     __syncthreads();

@@ -19,6 +19,7 @@ bool resolve(const sv_tuning_t* t, Tuning& r) {
     r.lag_a = t->lag_accept;
     r.lag_c = t->lag_draw;
     r.draw_mode = t->draw_mode;
+    r.item_polls = t->item_polls ? t->item_polls : kItemPolls;
     r.timed = t->timed;
     r.events = t->events;
     r.launched = t->launched;
@@ -35,6 +36,22 @@ void auto_lengths(int32_t B, int64_t total, int64_t V, const Tuning& tu, int64_t
     c = c < kMinChunk ? kMinChunk : (c > kDefaultChunkElems ? kDefaultChunkElems : c);
     *seg = tu.seg_elems ? tu.seg_elems : s;
     *chunk = tu.chunk_elems ? tu.chunk_elems : c;
+}
+
+int64_t lead_multiplier(int32_t B) {
+    if (B <= 2) return 1;
+    int64_t m = static_cast<int64_t>(0.6180339887498949 * B);
+    if (m < 1) m = 1;
+    auto gcd = [](int64_t a, int64_t b) {
+        while (b) {
+            const int64_t t = a % b;
+            a = b;
+            b = t;
+        }
+        return a;
+    };
+    while (gcd(m, B) != 1) ++m;                  // (ends: B - 1 is coprime with B)
+    return m;
 }
 
 int32_t effective_lead(int64_t B, int64_t total, int64_t V, sv_dtype_t dtype, const Tuning& tu) {
@@ -81,23 +98,19 @@ bool make_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dtype, int64_
     off = align256(off + sizeof(float) * static_cast<size_t>(rows));
     g.off_done = off;
     off = align256(off + sizeof(int32_t) * static_cast<size_t>(B));
+    const size_t entries = static_cast<size_t>(rows) * g.nseg + static_cast<size_t>(B) * (1 + g.nchunk);
     g.off_sched = off;
-    off = align256(off + sizeof(RestItem) * (static_cast<size_t>(rows) * g.nseg +
-                                             static_cast<size_t>(B) * (1 + g.nchunk)));
+    off = align256(off + sizeof(SchedEntry) * entries);
     g.off_blk_ctr = off;
     off = align256(off + sizeof(uint64_t));
     g.off_blk_seq = off;
-    off = align256(off + sizeof(int32_t) * static_cast<size_t>(B));
+    off = align256(off + sizeof(uint64_t) * static_cast<size_t>(B));
     g.off_dlist = off;
     off = align256(off + sizeof(RestItem) * static_cast<size_t>(B) * g.nseg);
     g.off_dlist_n = off;
     off = align256(off + sizeof(uint32_t));
     g.off_nbuf = off;                                   // accept counts of spec_draft_sample
     off = align256(off + sizeof(int32_t) * static_cast<size_t>(B));
-    g.off_early = off;
-    off = align256(off + sizeof(int32_t) * static_cast<size_t>(B));
-    g.off_early_n = off;
-    off = align256(off + sizeof(uint32_t));
     g.off_aband = off;
     off = align256(off + sizeof(int32_t) * static_cast<size_t>(B));
     g.off_picked = off;
@@ -105,6 +118,10 @@ bool make_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dtype, int64_
     g.off_lead_ctr = off;
     off = align256(off + sizeof(uint64_t) * static_cast<size_t>(B));
     g.off_lead_clr = off;
+    off = align256(off + sizeof(uint32_t));
+    g.off_lead_done = off;
+    off = align256(off + sizeof(uint64_t));
+    g.off_stall = off;
     off = align256(off + sizeof(uint32_t));
     g.bytes = off;
     return true;

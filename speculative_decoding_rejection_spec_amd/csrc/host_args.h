@@ -27,6 +27,10 @@ constexpr int64_t kDefaultChunkElems = 8192;  // draw chunk length before roundi
 constexpr int32_t kAutoLead = -1;
 constexpr int64_t kAutoLeadBytes = 512ll << 20;
 
+// Early exit: bound of a second-round workgroup's wait for its item (one
+// poll takes a memory round trip and a short sleep, about a microsecond).
+constexpr uint32_t kItemPolls = 1u << 22;
+
 // One call's tuning (sv_tuning.h), resolved: every field in range.
 struct Tuning {
     int64_t seg_elems = 0, chunk_elems = 0;   // 0: automatic (auto_lengths)
@@ -34,6 +38,7 @@ struct Tuning {
     int32_t queue_mode = SV_QUEUE_OVERLAP;
     int32_t lag_a = 0, lag_c = 0;             // 0: chosen from the resident grid
     int32_t draw_mode = SV_DRAW_AUTO;
+    uint32_t item_polls = kItemPolls;
     uint32_t timed = 0;                       // kernels whose events are recorded
     hipEvent_t* events = nullptr;
     uint32_t* launched = nullptr;
@@ -56,6 +61,12 @@ void auto_lengths(int32_t B, int64_t total, int64_t V, const Tuning& tu, int64_t
 // call's rows hold at least kAutoLeadBytes (0 for calls without drafts).
 int32_t effective_lead(int64_t B, int64_t total, int64_t V, sv_dtype_t dtype, const Tuning& tu);
 
+// The first round visits sequence (j * m) mod B as its j-th: m is coprime
+// with B (so every sequence is visited once) and near 0.618 B, which spreads
+// neighbouring sequences apart, so that the order in which the first round
+// finishes, and lists, does not follow how the caller ordered the batch.
+int64_t lead_multiplier(int32_t B);
+
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -63,8 +74,8 @@ struct Geometry {
     int32_t nseg, nchunk;
     int64_t seg_len, chunk_len;
     size_t off_seg, off_task, off_csum, off_band_n, off_band_w, off_xlogit, off_done, off_sched,
-        off_blk_ctr, off_blk_seq, off_dlist, off_dlist_n, off_nbuf, off_early, off_early_n, off_aband, off_picked,
-        off_lead_ctr, off_lead_clr, bytes;
+        off_blk_ctr, off_blk_seq, off_dlist, off_dlist_n, off_nbuf, off_aband, off_picked,
+        off_lead_ctr, off_lead_clr, off_lead_done, off_stall, bytes;
 };
 
 // Splits a row of V logits into n <= max_pieces pieces of about `target`

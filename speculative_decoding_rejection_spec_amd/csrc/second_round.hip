@@ -1,29 +1,30 @@
-// second_round.hip -- early exit outside the gathered form: the second round,
-// which streams the remaining rows and makes the draws beside them.
+// second_round.hip -- early exit outside the gathered form: both rounds in
+// one launch (rounds_kernel), then the staged pick (draw.hip).
 //
-// Second round (rest_draws_kernel).  The lead accept scan listed, for each
-// undecided sequence (a block), its remaining row segments, followed lag_a
-// blocks later by an accept item for it and lag_c blocks later by its
-// nchunk draw items (list_rest in accept_scan.h); the draw chunks of the
-// sequences the leading positions settled are interleaved evenly.
-// Workgroup w takes item w:
+// First round (lead_pass.h): the rows of the leading positions of every
+// sequence and their accept scans.  Each scan lists in the second round's
+// schedule what its sequence still needs (list_rest in accept_scan.h): an
+// undecided sequence becomes a block of its remaining row segments, whose
+// accept item comes lag_a blocks later and its nchunk draw items lag_c
+// blocks later; a settled sampling sequence lists its nchunk draw chunks at
+// once.  The second round's workgroups follow the first round's in the
+// grid; workgroup nlead + v takes item v:
 //   * a row segment: streams it and writes its statistics (written through,
-//     so workgroups on other XCDs see them); it waits for nothing.
+//     so workgroups on other XCDs see them);
 //   * an accept item: polls until every statistic and captured logit of its
-//     sequence's rows is written (the lead accept scan marked them unset),
-//     then runs the sequence's accept scan, whose draw task is written with
-//     its kind last.
-//   * a draw item: polls until its sequence's task kind is set, then sums
-//     its chunk.
+//     sequence's rows is written (the lister marked them unset), then runs
+//     the sequence's accept scan, whose draw task is written with its kind
+//     last;
+//   * a draw item: polls until its sequence's task kind is set (a settled
+//     sequence's is set before its chunks are listed), then sums its chunk.
 // Items are dispatched in grid order, so by the time an item waits, what it
-// waits for is running or done (the lags put about a resident grid of
-// row segments in between, so it is usually done).  Each wait is bounded; a
-// sequence whose wait runs out is marked and redone by the pick launch.
+// waits for is running or done (the lags put about a resident grid of row
+// segments in between, so it is usually done).
 //
-// Then the staged pick (draw_pick_kernel) redoes any marked sequence and
-// picks every emitted token.
+// Then the staged pick (draw_pick_kernel) redoes any sequence a wait left
+// to it and picks every emitted token.
 #include "draw_pass.h"
-#include "row_pass.h"
+#include "lead_pass.h"
 
 namespace sv {
 namespace {
@@ -94,41 +95,45 @@ __device__ __forceinline__ bool rows_written_polled(const Problem& p, const Plan
     return !__any(!ok);
 }
 
-template <int DT>
-__global__ __launch_bounds__(kThreads) void rest_draws_kernel(Problem p, Plan plan) {
-    __shared__ union {
-        RowLds row;
-        struct {
-            drawpass::TabEntry tbl[256];
-            DrawLds draw;
-        } d;
-    } lds;
-    __shared__ int32_t s_ready;
-    const int tid = threadIdx.x;
-    const int64_t w = blockIdx.x;
-    const int64_t nchunk = plan.nchunk;
-    const uint64_t ctr = *plan.blk_ctr;
-    const int64_t nblk = static_cast<int64_t>(ctr >> 32), nr = static_cast<int64_t>(ctr & 0xffffffffu);
-    const int64_t nvirt = nr + nblk * (1 + nchunk);
-    const int64_t ne = static_cast<int64_t>(*plan.early_n) * nchunk;
-    const int64_t all = nvirt + ne;
-    if (w >= all) return;
-    int32_t b, c;
-    // Even interleave: item w is an early draw chunk iff the count of early
-    // chunks among the first w + 1 items, floor((w + 1) ne / all), steps up at w.
-    const int64_t d0 = (w * ne) / all, d1 = ((w + 1) * ne) / all;
-    if (d1 > d0) {
-        if (plan.queue_mode == SV_QUEUE_FINAL) return;
-        b = plan.early[d0 / nchunk];
-        c = static_cast<int32_t>(d0 % nchunk);
-    } else {
-        const int64_t v = w - d0;
-        const int64_t la = plan.lag_a, lc = plan.lag_c;
+// Thread 0 of a second-round workgroup: item v of the schedule.  Waits
+// until its entry carries this call's epoch, or until every sequence is
+// counted on lead_done: then the whole schedule is written, and an item
+// past the written entries (the accept and draw items of the last blocks)
+// follows from the final counts.  For an accept or kItemChunk item, also the
+// undecided sequence of its block (*seq).  Returns false past the schedule's
+// end, and when a wait runs out (the call is then marked stalled: never
+// expected, see the kernel).
+__device__ __forceinline__ bool find_item(const Problem& p, const Plan& plan, int64_t v, RestItem* out,
+                                          int32_t* seq) {
+    bool listed = false, final_counts = false;
+    RestItem it{};
+    const uint64_t all_done = (static_cast<uint64_t>(plan.epoch) << 32) | static_cast<uint32_t>(p.B);
+    // first an ordinary load: an entry written long ago usually comes back current
+    if (load_entry<false>(plan.sched + v, plan.epoch, &it)) {
+        *out = it;
+        listed = true;
+    }
+    for (uint32_t polls = 0; !listed; ++polls) {
+        // (lead_done, one word every waiting workgroup reads, only on every
+        // fourth poll)
+        const bool count = (polls & 3) == 0;
+        const bool got = load_entry<true>(plan.sched + v, plan.epoch, &it);
+        const uint64_t d = count ? ld_co<true>(plan.lead_done) : 0;
+        if (got) { listed = true; break; }
+        if (d == all_done) { final_counts = true; break; }
+        if (polls >= plan.item_polls) break;
+        __builtin_amdgcn_s_sleep(8);
+    }
+    if (!listed && final_counts) {
+        const uint64_t ctr = ld_co<true>(plan.blk_ctr);
+        const int64_t nblk = static_cast<int64_t>(ctr >> 32), nr = static_cast<int64_t>(ctr & 0xffffffffu);
+        const int64_t la = plan.lag_a, lc = plan.lag_c, nchunk = plan.nchunk;
         const int64_t vend = nr + max(static_cast<int64_t>(0), nblk - la) + nchunk * max(static_cast<int64_t>(0), nblk - lc);
-        RestItem it;
+        if (v >= nr + nblk * (1 + nchunk)) return false;             // past the schedule
         if (v < vend) {
-            it = plan.sched[v];
-        } else {                                       // the items of the last blocks
+            // (written before its lister counted its sequence)
+            listed = load_entry<true>(plan.sched + v, plan.epoch, &it);
+        } else {                                   // the items of the last blocks
             int64_t t = v - vend;
             const int64_t na = min(nblk, la);
             if (t < na) {
@@ -138,50 +143,121 @@ __global__ __launch_bounds__(kThreads) void rest_draws_kernel(Problem p, Plan pl
                 it = rest_item(static_cast<int32_t>(nblk - min(nblk, lc) + t / nchunk), 0, kItemChunk,
                                static_cast<int32_t>(t % nchunk), -1);
             }
+            listed = true;
         }
-        const int32_t kind = item_kind(it);
-        if (kind == kItemTarget || kind == kItemDraft) {
-            row_segment<DT, true>(p, plan, it.b, kind == kItemTarget, it.row, item_seg(it), lds.row, it.x);
-            return;
+    }
+    if (!listed) {
+        st_co<true>(plan.stall, plan.epoch);
+        return false;
+    }
+    *out = it;
+    const int32_t kind = item_kind(it);
+    if (kind == kItemAccept || kind == kItemChunk) {
+        // the block's sequence: written by its lister, which has counted the
+        // block and so is running (an ordinary load first, as for the entry)
+        for (uint32_t polls = 0;; ++polls) {
+            const uint64_t s = polls == 0 ? plan.blk_seq[it.b] : ld_co<true>(plan.blk_seq + it.b);
+            if (static_cast<uint32_t>(s >> 32) == plan.epoch) {
+                *seq = static_cast<int32_t>(static_cast<uint32_t>(s));
+                break;
+            }
+            if (polls >= plan.item_polls) {
+                st_co<true>(plan.stall, plan.epoch);
+                return false;
+            }
+            if (polls > 0) __builtin_amdgcn_s_sleep(8);
         }
-        b = plan.blk_seq[it.b];
-        if (plan.queue_mode == SV_QUEUE_FINAL) return;
-        if (kind == kItemAccept) {
-            if (tid >= 64) return;                     // one wave runs it
-            bool ready = plan.queue_mode != SV_QUEUE_HANDOFF;
-            // (a sampling sequence with short segment lists keeps what its
-            // last poll loaded, saving the scan a round trip to memory)
-            const bool keep = p.temperature[b] != 0.f && plan.nseg <= kPolledSegs;
-            Polled pre;
-            for (uint32_t polls = 0; ready; ++polls) {
-                if (keep ? rows_written_polled(p, plan, b, &pre) : rows_written(p, plan, b)) break;
-                if (polls == kPolls) ready = false;
+    } else if (kind == kItemChunkSeq) {
+        *seq = it.b;
+    }
+    return true;
+}
+
+// Both rounds of early exit in one launch.  Workgroups [0, nlead) run the
+// first round (lead_pass.h); workgroup nlead + v runs item v of the
+// schedule the first round's accept scans list (list_rest).
+//
+// Every wait ends: workgroups are dispatched in order of their index (on
+// each XCD, which receives every eighth one), a first-round workgroup never
+// waits for a second-round one, so every first-round workgroup runs to its
+// end, after which every entry is written.  The waits are bounded all the
+// same: an item wait that runs out marks the call stalled, and the pick
+// launch then reports every sequence as a data error; an accept or draw
+// wait that runs out leaves its sequence to the pick launch, which redoes
+// it.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void rounds_kernel(Problem p, Plan plan, uint32_t nlead) {
+    __shared__ union {
+        RowLds row;
+        struct {
+            drawpass::TabEntry tbl[256];
+            DrawLds draw;
+        } d;
+    } lds;
+    __shared__ int32_t s_flag, s_ready;
+    __shared__ uint32_t s_clr;
+    __shared__ RestItem s_item;
+    __shared__ int32_t s_seq;
+    const int tid = threadIdx.x;
+    if (blockIdx.x < nlead) {
+        lead_workgroup<DT>(p, plan, blockIdx.x, lds.row, s_flag, s_clr);
+        return;
+    }
+    const int64_t v = static_cast<int64_t>(blockIdx.x) - nlead;
+    if (tid == 0) {
+        RestItem it;
+        int32_t seq = 0;
+        const bool found = find_item(p, plan, v, &it, &seq);
+        s_flag = found;
+        s_item = it;
+        s_seq = seq;
+    }
+    __syncthreads();
+    if (!s_flag) return;
+    const RestItem it = s_item;
+    const int32_t kind = item_kind(it);
+    if (kind == kItemTarget || kind == kItemDraft) {
+        row_segment<DT, true>(p, plan, it.b, kind == kItemTarget, it.row, item_seg(it), lds.row, it.x);
+        return;
+    }
+    if (plan.queue_mode == SV_QUEUE_FINAL) return;
+    const int32_t b = s_seq;
+    if (kind == kItemAccept) {
+        if (tid >= 64) return;                     // one wave runs it
+        bool ready = plan.queue_mode != SV_QUEUE_HANDOFF;
+        // (a sampling sequence with short segment lists keeps what its
+        // last poll loaded, saving the scan a round trip to memory)
+        const bool keep = p.temperature[b] != 0.f && plan.nseg <= kPolledSegs;
+        Polled pre;
+        for (uint32_t polls = 0; ready; ++polls) {
+            if (keep ? rows_written_polled(p, plan, b, &pre) : rows_written(p, plan, b)) break;
+            if (polls == kPolls) ready = false;
+            __builtin_amdgcn_s_sleep(8);
+        }
+        if (ready) {
+            // (the lead scan found the sequence's offsets in order)
+            if (keep) accept_sequence<true>(p, plan, b, kKMax + 1, nullptr, nullptr, true, &pre, false);
+            else accept_sequence<true>(p, plan, b, kKMax + 1, nullptr, nullptr, true, nullptr, false);
+        }
+        else if (tid == 0) st_co<true>(plan.aband + b, 1);   // the pick launch redoes the sequence
+        return;
+    }
+    // a draw chunk
+    if (p.temperature[b] == 0.f) return;           // greedy: nothing to draw
+    const int32_t c = item_seg(it);
+    // (a settled sequence's task was written before its chunks were listed)
+    if (kind == kItemChunk && tid == 0) {
+        bool ready = false;
+        if (plan.queue_mode != SV_QUEUE_HANDOFF)
+            for (uint32_t polls = 0; polls < kPolls; ++polls) {
+                if (ld_co<true>(&plan.task[b].kind) != kTaskUnset) { ready = true; break; }
                 __builtin_amdgcn_s_sleep(8);
             }
-            if (ready) {
-                // (the lead scan found the sequence's offsets in order)
-                if (keep) accept_sequence<true>(p, plan, b, kKMax + 1, nullptr, nullptr, true, &pre, false);
-                else accept_sequence<true>(p, plan, b, kKMax + 1, nullptr, nullptr, true, nullptr, false);
-            }
-            else if (tid == 0) plan.aband[b] = 1;    // the pick launch redoes the sequence
-            return;
-        }
-        // a draw chunk of an undecided sequence
-        if (p.temperature[b] == 0.f) return;       // greedy: nothing to draw
-        c = item_seg(it);
-        if (tid == 0) {
-            bool ready = false;
-            if (plan.queue_mode != SV_QUEUE_HANDOFF)
-                for (uint32_t polls = 0; polls < kPolls; ++polls) {
-                    if (ld_co<true>(&plan.task[b].kind) != kTaskUnset) { ready = true; break; }
-                    __builtin_amdgcn_s_sleep(8);
-                }
-            if (!ready) plan.aband[b] = 1;
-            s_ready = ready;
-        }
-        __syncthreads();
-        if (!s_ready) return;
+        if (!ready) st_co<true>(plan.aband + b, 1);
+        s_ready = ready;
     }
+    __syncthreads();
+    if (kind == kItemChunk && !s_ready) return;
     load_exp2_table(lds.d.tbl, kThreads);
     const DrawTask task = load_task<true>(p, plan, b);
     if (task.kind == kNone) return;                // a data error found past the leading positions
@@ -191,22 +267,36 @@ __global__ __launch_bounds__(kThreads) void rest_draws_kernel(Problem p, Plan pl
 
 }  // namespace
 
-hipError_t rest_blocks_per_cu(int32_t dtype, int32_t* blocks) {
+hipError_t rounds_blocks_per_cu(int32_t dtype, int32_t* blocks) {
     int n = 0;
     const hipError_t e = dtype == SV_BF16
-        ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rest_draws_kernel<SV_BF16>, kThreads, 0)
-        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rest_draws_kernel<SV_F32>, kThreads, 0);
+        ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rounds_kernel<SV_BF16>, kThreads, 0)
+        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rounds_kernel<SV_F32>, kThreads, 0);
     *blocks = n;
     return e;
 }
 
-hipError_t launch_rest_draws(const Problem& p, const Plan& plan, hipStream_t s) {
-    const int64_t blocks = (2 * p.total + p.B) * static_cast<int64_t>(plan.nseg) +
-                           static_cast<int64_t>(p.B) * (1 + plan.nchunk);
+int64_t rounds_lead_blocks(const Problem& p, const Plan& plan) {
+    return static_cast<int64_t>(p.B) * plan.lead * 2 * plan.nseg;
+}
+
+// Row segments listed at most: with a uniform k every undecided sequence
+// lists at most 2 (k - lead) + 1 rows (none when lead > k); with offsets,
+// every row bounds it.  Then an accept item and nchunk draw items per block.
+int64_t rounds_rest_blocks(const Problem& p, const Plan& plan) {
+    const int64_t rows = p.offsets ? 2 * p.total + p.B
+                                   : static_cast<int64_t>(p.B) *
+                                         max(static_cast<int64_t>(0), 2 * (static_cast<int64_t>(p.k_uniform) - plan.lead) + 1);
+    return rows * plan.nseg + static_cast<int64_t>(p.B) * (1 + plan.nchunk);
+}
+
+hipError_t launch_rounds(const Problem& p, const Plan& plan, hipStream_t s) {
+    const int64_t nlead = rounds_lead_blocks(p, plan);
+    const dim3 grid(static_cast<uint32_t>(nlead + rounds_rest_blocks(p, plan)));
     if (p.dtype == SV_BF16)
-        rest_draws_kernel<SV_BF16><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s>>>(p, plan);
+        rounds_kernel<SV_BF16><<<grid, dim3(kThreads), 0, s>>>(p, plan, static_cast<uint32_t>(nlead));
     else
-        rest_draws_kernel<SV_F32><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s>>>(p, plan);
+        rounds_kernel<SV_F32><<<grid, dim3(kThreads), 0, s>>>(p, plan, static_cast<uint32_t>(nlead));
     return hipGetLastError();
 }
 

@@ -22,12 +22,12 @@ using namespace sv;
 using namespace sv::host;
 
 constexpr int kMaxDevices = 64;
-enum { kKRowStats, kKAccept, kKDrawSums, kKDrawPick, kKRowLead, kKRowDraft, kKRest, kKDrawAll, kKSampleSums,
+enum { kKRowStats, kKAccept, kKDrawSums, kKDrawPick, kKRowLead, kKRowDraft, kKRounds, kKDrawAll, kKSampleSums,
        kKSamplePick, kNumKernels };
 static_assert(kNumKernels == SV_NUM_KERNELS, "kernel count");
 
 const char* const kKernelNames[kNumKernels] = {"row_stats", "accept",   "draw_sums", "draw_pick",
-                                               "row_lead",  "row_draft", "rest",      "draw_all",
+                                               "row_lead",  "row_draft", "rounds",    "draw_all",
                                                "sample_sums", "sample_pick"};
 
 // Call numbers: a counter word of the workspace that an earlier call (or
@@ -50,8 +50,8 @@ uint32_t next_epoch() {
 // land on whichever XCD already lags, which then lags further.
 constexpr int kDrawAllWgsPerCu = 4;
 
-// Per-device facts, queried once: compute units, and second-round
-// workgroups a compute unit holds at once (its register count decides).
+// Per-device facts, queried once: compute units, and workgroups of the
+// two-round launch a compute unit holds at once (its register count decides).
 std::mutex g_mutex;                          // guards the caches and the owned workspace
 struct DeviceInfo {
     int cus = 0;
@@ -73,7 +73,7 @@ hipError_t device_info(int32_t dtype, int* cus, int* rest_per_cu) {
     const int di = dtype == SV_BF16 ? 1 : 0;
     if (!d.rest_per_cu[di]) {
         int32_t n = 0;
-        e = rest_blocks_per_cu(dtype, &n);
+        e = rounds_blocks_per_cu(dtype, &n);
         if (e != hipSuccess) return e;
         d.rest_per_cu[di] = n > 0 ? n : 1;
     }
@@ -153,27 +153,32 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     plan.band_w = reinterpret_cast<double*>(ws + g.off_band_w);
     plan.xlogit = reinterpret_cast<float*>(ws + g.off_xlogit);
     plan.done = reinterpret_cast<int32_t*>(ws + g.off_done);
-    plan.sched = reinterpret_cast<RestItem*>(ws + g.off_sched);
+    plan.sched = reinterpret_cast<SchedEntry*>(ws + g.off_sched);
     plan.blk_ctr = reinterpret_cast<uint64_t*>(ws + g.off_blk_ctr);
-    plan.blk_seq = reinterpret_cast<int32_t*>(ws + g.off_blk_seq);
+    plan.blk_seq = reinterpret_cast<uint64_t*>(ws + g.off_blk_seq);
     plan.dlist = reinterpret_cast<RestItem*>(ws + g.off_dlist);
     plan.dlist_n = reinterpret_cast<uint32_t*>(ws + g.off_dlist_n);
-    plan.early = reinterpret_cast<int32_t*>(ws + g.off_early);
-    plan.early_n = reinterpret_cast<uint32_t*>(ws + g.off_early_n);
     plan.aband = reinterpret_cast<int32_t*>(ws + g.off_aband);
     plan.picked = reinterpret_cast<uint32_t*>(ws + g.off_picked);
     plan.lead_ctr = reinterpret_cast<uint64_t*>(ws + g.off_lead_ctr);
     plan.lead_clr = reinterpret_cast<uint32_t*>(ws + g.off_lead_clr);
+    plan.lead_done = reinterpret_cast<uint64_t*>(ws + g.off_lead_done);
+    plan.stall = reinterpret_cast<uint32_t*>(ws + g.off_stall);
+    plan.item_polls = tu.item_polls;
     plan.epoch = next_epoch();
     plan.queue_mode = tu.queue_mode;
     Problem pr = p;
     if (!pr.out_n) pr.out_n = reinterpret_cast<int32_t*>(ws + g.off_nbuf);
 
     plan.lead = sample ? 0 : effective_lead(p.B, p.total, p.V, static_cast<sv_dtype_t>(p.dtype), tu);
+    plan.lead_mul = lead_multiplier(p.B);
     int rest_per_cu = 1;
     if (device_info(p.dtype, &plan.cus, &rest_per_cu) != hipSuccess) return SV_ERR_HIP;
     plan.lag_a = plan.lag_c = 1 << 30;             // no accept or draw items in the schedule
     plan.queued = plan.lead > 0 && !p.draft_probs;
+    // (a call whose two-round grid would not fit 2^31 - 1 workgroups runs as one pass)
+    if (plan.queued && rounds_lead_blocks(pr, plan) + rounds_rest_blocks(pr, plan) > 0x7FFFFFFFll)
+        plan.lead = plan.queued = 0;
     if (plan.queued) {
         if (tu.lag_a > 0) {
             plan.lag_a = tu.lag_a;
@@ -210,24 +215,26 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
              launch(kKSamplePick, [&] { return launch_sample_pick(pr, plan, stream); });
         return finish(ok);
     }
-    // Row pass: one pass over every needed row, or (early exit) the leading
-    // positions with their accept scans, then the listed remainder.  Early
-    // exit outside the gathered form ends in two launches: the remaining
-    // rows with the draws beside them, and the picks (with the redo of
-    // anything that round left over, usually nothing).
+    // Early exit outside the gathered form: two launches, both rounds (the
+    // leading positions with their accept scans, then the remaining rows
+    // with the draws beside them), and the picks (with the redo of anything
+    // the rounds left over, usually nothing).
+    if (plan.queued) {
+        ok = launch(kKRounds, [&] { return launch_rounds(pr, plan, stream); }) &&
+             launch(kKDrawPick, [&] { return launch_draw_pick(pr, plan, stream); });
+        return finish(ok);
+    }
+    // Row pass: one pass over every needed row, or (the gathered form's
+    // early exit) the leading positions with their accept scans, then the
+    // listed remainder.
     if (plan.lead > 0)
         ok = launch(kKRowLead, [&] { return launch_row_lead(pr, plan, stream); });
     else
         ok = launch(kKRowStats, [&] { return launch_row_stats(pr, plan, stream); });
-    if (plan.queued) {
-        ok = ok && launch(kKRest, [&] { return launch_rest_draws(pr, plan, stream); }) &&
-             launch(kKDrawPick, [&] { return launch_draw_pick(pr, plan, stream); });
-        return finish(ok);
-    }
     if (plan.lead > 0)   // gathered form: a settled sequence has no early draw
         ok = ok && launch(kKRowStats, [&] {
-            return launch_row_list(pr, plan, plan.sched, reinterpret_cast<const uint32_t*>(plan.blk_ctr),
-                                   (2 * p.total + p.B) * static_cast<int64_t>(g.nseg), stream);
+            return launch_sched_rows(pr, plan, reinterpret_cast<const uint32_t*>(plan.blk_ctr),
+                                     (2 * p.total + p.B) * static_cast<int64_t>(g.nseg), stream);
         });
     // One pass, outside the gathered form: a draw that fits one round of
     // workgroups runs as one launch with the accept scans and the picks.

@@ -14,13 +14,14 @@
 //                  fp64 chunk sums;
 //   4. draw_pick   (draw.hip, draw_pass.h): one workgroup per sequence
 //                  locates the chunk that holds u * Z and the token inside it.
-// Early exit (Plan::lead > 0): step 1 runs over the leading positions of
-// every sequence (row_lead), and the workgroup that finishes a sequence's
-// last leading segment runs its accept scan, which settles some sequences
-// and lists the remaining rows of the others; then one launch
-// (second_round.hip) streams those rows, runs the undecided sequences'
-// accept scans and every draw chunk beside them, and draw_pick picks.  The
-// gathered form instead streams the listed rows (row_list), then runs steps
+// Early exit (Plan::lead > 0): one launch (second_round.hip) runs two
+// rounds.  Its first workgroups read the leading positions of every
+// sequence (lead_pass.h), and the workgroup that finishes a sequence's last
+// leading segment runs its accept scan, which settles the sequence or lists
+// its remaining rows; the later workgroups take the listed items in order:
+// those rows, the undecided sequences' accept scans and every draw chunk.
+// Then draw_pick picks.  The gathered form runs the first round as its own
+// launch (row_lead), streams the listed rows (row_list), then runs steps
 // 2-4 with the draft rows at rejections read in between.
 #pragma once
 
@@ -83,14 +84,13 @@ struct Plan {
     double* band_w;      // [B * nchunk * kWaves * kWaveCap * 2]: their (w_t, w_d)
     float* xlogit;       // [2 * total + B]: logit of the drafted token of each row
     int32_t lead;        // early exit: positions every sequence reads first (0: one pass over all rows)
+    int64_t lead_mul;    // early exit: the first round's j-th sequence is (j * lead_mul) mod B
     int32_t* done;       // early exit: [B], kUndecided / kDecided / kDecidedEarlyDraw after the lead scan
-    RestItem* sched;     // early exit: [(2 * total + B) * nseg + B * (1 + nchunk)], the second round's items
+    SchedEntry* sched;   // early exit: [(2 * total + B) * nseg + B * (1 + nchunk)], the second round's items
     uint64_t* blk_ctr;   // early exit: (undecided sequences listed) << 32 | (row segments listed)
     RestItem* dlist;     // gathered form: [B * nseg], segments of the draft rows at rejections
     uint32_t* dlist_n;   // gathered form: number of entries in dlist
-    int32_t* early;      // early exit: [B], sampling sequences the leading positions settled
-    uint32_t* early_n;   // early exit: number of entries in early
-    int32_t* blk_seq;    // early exit: [B] the sequence listed as block i
+    uint64_t* blk_seq;   // early exit: [B] epoch << 32 | the undecided sequence listed as block i
     int32_t lag_a, lag_c;// early exit: the accept item of block j follows block j + lag_a, its chunks
                          // follow block j + lag_c (huge: none inserted, the gathered form)
     int32_t* aband;      // [B] 1: sequence b is left to the pick launch
@@ -100,17 +100,25 @@ struct Plan {
     int32_t queue_mode;  // SV_QUEUE_*: where the second round's draw chunks are summed
     uint32_t epoch;      // this call's number (never 0): tags the counters below
     uint64_t* lead_ctr;  // early exit: [B] epoch << 32 | leading segments of sequence b finished
-    uint32_t* lead_clr;  // early exit: the epoch of the call whose row_lead has cleared the list counters
+    uint32_t* lead_clr;  // early exit: the epoch of the call whose first round has cleared the list counters
+    uint64_t* lead_done; // early exit: epoch << 32 | sequences whose leading accept scan has finished
+                         // (set to epoch << 32 before lead_clr is published)
+    uint32_t* stall;     // early exit: the epoch of a call whose second round could not find an item's work
+    uint32_t item_polls; // early exit: bound of a second-round workgroup's wait for its item
 };
 
-// Plan::done values (early exit).
+
+// Plan::done values (early exit).  kDecidedEarlyDraw: settled with a draw
+// that the second round makes.
 enum : int32_t { kUndecided = 0, kDecided = 1, kDecidedEarlyDraw = 2 };
 
 // Host-side launchers (one per kernel).
 hipError_t launch_row_stats(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_row_list(const Problem& p, const Plan& plan, const RestItem* list, const uint32_t* count,
                            int64_t max_items, hipStream_t s);
-hipError_t launch_rest_draws(const Problem& p, const Plan& plan, hipStream_t s);
+hipError_t launch_sched_rows(const Problem& p, const Plan& plan, const uint32_t* count, int64_t max_items,
+                             hipStream_t s);
+hipError_t launch_rounds(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_row_lead(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_accept(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_draw_sums(const Problem& p, const Plan& plan, hipStream_t s);
@@ -118,8 +126,12 @@ hipError_t launch_draw_pick(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_draw_all(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_sample_sums(const Problem& p, const Plan& plan, hipStream_t s);
 hipError_t launch_sample_pick(const Problem& p, const Plan& plan, hipStream_t s);
-// Second-round workgroups one compute unit holds at once (occupancy query).
-hipError_t rest_blocks_per_cu(int32_t dtype, int32_t* blocks);
+// Workgroups of the two-round launch one compute unit holds at once
+// (occupancy query).
+hipError_t rounds_blocks_per_cu(int32_t dtype, int32_t* blocks);
+// Workgroups of the two-round launch: the first round's, then the second's.
+int64_t rounds_lead_blocks(const Problem& p, const Plan& plan);
+int64_t rounds_rest_blocks(const Problem& p, const Plan& plan);
 hipError_t launch_commit(const int32_t* out_tokens, const int32_t* out_n, const int32_t* offsets,
                          int32_t k_uniform, int32_t B, int32_t* seq_tokens, int32_t* seq_len,
                          int32_t max_len, int32_t* committed, int32_t* committed_offsets, hipStream_t s);
@@ -175,8 +187,9 @@ __device__ __forceinline__ void wait_stores() {
 // counts as none, so the counters need no clearing between calls.  Returns
 // the arrivals including this one.  (A compare-and-swap loop: each retry
 // means another arrival succeeded, so it ends.)
-__device__ __forceinline__ uint32_t arrive(uint64_t* word, uint32_t epoch) {
-    uint64_t old = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// arrive_from: the same with the word's value already loaded (possibly
+// stale: the first compare-and-swap then fails and returns the current one).
+__device__ __forceinline__ uint32_t arrive_from(uint64_t* word, uint32_t epoch, uint64_t old) {
     for (;;) {
         const uint64_t base = static_cast<uint32_t>(old >> 32) == epoch ? old : static_cast<uint64_t>(epoch) << 32;
         const uint64_t want = base + 1;
@@ -185,11 +198,40 @@ __device__ __forceinline__ uint32_t arrive(uint64_t* word, uint32_t epoch) {
             return static_cast<uint32_t>(want);
     }
 }
+__device__ __forceinline__ uint32_t arrive(uint64_t* word, uint32_t epoch) {
+    return arrive_from(word, epoch, __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Early exit's schedule entries (SchedEntry): written through, one word at a
+// time, by a lister whose earlier stores (what the item needs) are already
+// visible; read with the epoch checked on every word.
+__device__ __forceinline__ void store_entry(SchedEntry* dst, const RestItem& it, uint32_t epoch) {
+    const uint64_t e = static_cast<uint64_t>(epoch) << 32;
+    st_co<true>(&dst->w[0], e | static_cast<uint32_t>(it.b));
+    st_co<true>(&dst->w[1], e | static_cast<uint32_t>(it.row));
+    st_co<true>(&dst->w[2], e | static_cast<uint32_t>(it.kseg));
+    st_co<true>(&dst->w[3], e | static_cast<uint32_t>(it.x));
+}
+// True when every word of the entry carries `epoch`; *it gets the fields.
+template <bool kCo>
+__device__ __forceinline__ bool load_entry(const SchedEntry* src, uint32_t epoch, RestItem* it) {
+    const uint64_t w0 = ld_co<kCo>(&src->w[0]), w1 = ld_co<kCo>(&src->w[1]);
+    const uint64_t w2 = ld_co<kCo>(&src->w[2]), w3 = ld_co<kCo>(&src->w[3]);
+    *it = RestItem{static_cast<int32_t>(static_cast<uint32_t>(w0)), static_cast<int32_t>(static_cast<uint32_t>(w1)),
+                   static_cast<int32_t>(static_cast<uint32_t>(w2)), static_cast<int32_t>(static_cast<uint32_t>(w3))};
+    return static_cast<uint32_t>(w0 >> 32) == epoch && static_cast<uint32_t>(w1 >> 32) == epoch &&
+           static_cast<uint32_t>(w2 >> 32) == epoch && static_cast<uint32_t>(w3 >> 32) == epoch;
+}
 
 // c = log2(e) / T as the row pass uses it (the accept scan must form the same
 // float).  Capped at 2^60: beyond that every non-maximal term underflows.
 __device__ __forceinline__ float row_scale(float T) {
     return static_cast<float>(fmin(1.4426950408889634 / static_cast<double>(T), 0x1p60));
+}
+
+// First drafted slot of sequence b (offsets, or k_uniform per sequence).
+__device__ __forceinline__ int64_t first_slot(const Problem& p, int32_t b) {
+    return p.offsets ? static_cast<int64_t>(p.offsets[b]) : static_cast<int64_t>(b) * p.k_uniform;
 }
 
 // Sequence owning target row r: the largest b with first_draft(b) + b <= r.

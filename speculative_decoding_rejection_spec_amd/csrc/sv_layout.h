@@ -69,12 +69,22 @@ struct ChunkSums {
 // kItemDraft / kItemTarget), the accept scan of an undecided sequence
 // (kItemAccept), or one draw chunk of such a sequence (kItemChunk).  The
 // gathered form's row lists use the row-segment kinds.
-enum : int32_t { kItemDraft = 0, kItemTarget = 1, kItemAccept = 2, kItemChunk = 3 };
+// kItemChunkSeq: a draw chunk of a sampling sequence its leading positions
+// settled (b is the sequence itself; its task is written before the item is
+// listed).
+enum : int32_t { kItemDraft = 0, kItemTarget = 1, kItemAccept = 2, kItemChunk = 3, kItemChunkSeq = 4 };
 struct RestItem {
-    int32_t b;      // row segments: the sequence; accept and draw items: its block (listing order)
+    int32_t b;      // row segments and kItemChunkSeq: the sequence; accept and kItemChunk items: its block
     int32_t row;    // row segments: row index in its array
     int32_t kseg;   // kind << 28 | segment (row segments) or chunk (draw items)
     int32_t x;      // row segments: the drafted token whose logit the row's segments capture, or -1
+};
+
+// An entry of early exit's schedule: the four fields of a RestItem, each in
+// a 64-bit word whose high half is the number (epoch) of the call that wrote
+// it.  A reader takes the entry once all four words carry its call's epoch.
+struct alignas(32) SchedEntry {
+    uint64_t w[4];
 };
 
 }  // namespace sv

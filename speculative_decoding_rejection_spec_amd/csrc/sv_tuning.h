@@ -52,6 +52,9 @@ typedef struct {
     int32_t lag_accept;   /* 0 = chosen from the resident grid */
     int32_t lag_draw;     /* 0 = chosen from the resident grid */
     int32_t draw_mode;    /* SV_DRAW_* */
+    uint32_t item_polls;  /* early exit: bound of a second-round workgroup's wait for its schedule
+                             entry (0 = automatic: several seconds); a wait that runs out makes every
+                             sequence of the call a data error (out_n_accepted -1) */
     uint32_t timed;       /* with events: bit i set = record events around kernel i */
     hipEvent_t *events;   /* NULL, or 2 * SV_NUM_KERNELS events created by the caller: events[2i] is
                              recorded on the call's stream right before kernel i, events[2i+1] right

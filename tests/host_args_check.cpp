@@ -8,6 +8,7 @@
 #include <stdlib.h>
 
 #include <random>
+#include <vector>
 
 #include "host_args.h"
 
@@ -49,10 +50,10 @@ static void check_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dt, c
           (g.nchunk - 1) * g.chunk_len < V);
     CHECK(g.chunk_len % 8 == 0);
     if (V > max_seg_elems(dt) && tu.seg_elems == 0) CHECK(g.seg_len <= max_seg_elems(dt));
-    const size_t offs[] = {g.off_seg,  g.off_task,   g.off_csum,    g.off_band_n, g.off_band_w, g.off_xlogit,
-                           g.off_done, g.off_sched,  g.off_blk_ctr, g.off_blk_seq, g.off_dlist,  g.off_dlist_n,
-                           g.off_nbuf, g.off_early,  g.off_early_n, g.off_aband,   g.off_picked, g.off_lead_ctr,
-                           g.off_lead_clr, g.bytes};
+    const size_t offs[] = {g.off_seg,     g.off_task,     g.off_csum,     g.off_band_n,    g.off_band_w,
+                           g.off_xlogit,  g.off_done,     g.off_sched,    g.off_blk_ctr,   g.off_blk_seq,
+                           g.off_dlist,   g.off_dlist_n,  g.off_nbuf,     g.off_aband,     g.off_picked,
+                           g.off_lead_ctr, g.off_lead_clr, g.off_lead_done, g.off_stall,    g.bytes};
     for (size_t i = 0; i < sizeof(offs) / sizeof(offs[0]); ++i) {
         CHECK(offs[i] % 256 == 0);
         if (i > 0) CHECK(offs[i] >= offs[i - 1]);
@@ -60,8 +61,9 @@ static void check_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dt, c
     // every record the kernels index fits before the next block
     const size_t rows = static_cast<size_t>(2 * total + B);
     CHECK(g.off_task - g.off_seg >= sizeof(SegStat) * rows * static_cast<size_t>(g.nseg));
-    CHECK(g.off_sched + sizeof(RestItem) * (rows * g.nseg + static_cast<size_t>(B) * (1 + g.nchunk)) <=
-          g.off_blk_ctr);
+    const size_t entries = rows * g.nseg + static_cast<size_t>(B) * (1 + g.nchunk);
+    CHECK(g.off_sched + sizeof(SchedEntry) * entries <= g.off_blk_ctr);
+    CHECK(g.off_blk_seq + sizeof(uint64_t) * static_cast<size_t>(B) <= g.off_dlist);
     CHECK(g.bytes == workspace_bytes_for(B, total, V, dt, tu));
 }
 
@@ -103,7 +105,9 @@ int main() {
     raw.draw_mode = -1; CHECK(!resolve(&raw, tu)); raw.draw_mode = 0;
     raw.lag_accept = -1; CHECK(!resolve(&raw, tu)); raw.lag_accept = 0;
     raw.seg_elems = -5; CHECK(!resolve(&raw, tu)); raw.seg_elems = 0;
-    CHECK(resolve(&raw, tu) && tu.lead == 0);
+    CHECK(resolve(&raw, tu) && tu.lead == 0 && tu.item_polls == kItemPolls);
+    raw.item_polls = 3;
+    CHECK(resolve(&raw, tu) && tu.item_polls == 3);
 
     // ---- geometry and workspace layout -------------------------------------
     const Tuning dflt;
@@ -135,6 +139,16 @@ int main() {
     CHECK(workspace_bytes_for(1, 0, 10, static_cast<sv_dtype_t>(7), dflt) == 0);
     check_geometry(1, 0, 0x7FFFFFFF, SV_F32, dflt);
     check_geometry(4096, 4096ll * 8, 152064, SV_BF16, dflt);
+
+    // the first round's order visits every sequence once
+    for (int32_t B = 1; B <= 3000; B += (B < 600 ? 1 : 97)) {
+        const int64_t m = lead_multiplier(B);
+        CHECK(m >= 1);
+        std::vector<char> seen(static_cast<size_t>(B), 0);
+        for (int64_t j = 0; j < B; ++j) seen[static_cast<size_t>(j * m % B)] = 1;
+        for (int32_t b = 0; b < B; ++b) CHECK(seen[static_cast<size_t>(b)]);
+    }
+    CHECK(lead_multiplier(0x7FFFFFFF) >= 1);
 
     if (failures) {
         fprintf(stderr, "%d checks failed\n", failures);

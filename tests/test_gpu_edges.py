@@ -258,3 +258,32 @@ def test_zero_draw_uniform_never_emits_a_masked_token(sv, cuda, dtype):
         n = int(gpu["n"][b])
         t = int(gpu["tokens"][w.target_row(b, n)])
         assert np.isfinite(vals[w.target_row(b, n), t]), (b, n, t)
+
+
+# --------------------------------------------------------------------------
+# a second-round wait that runs out
+# --------------------------------------------------------------------------
+def test_item_wait_that_runs_out_reports_data_errors(sv, cuda):
+    """Early exit: a second-round workgroup whose wait for its schedule
+    entry runs out (forced from the host with a bound of one poll, so that
+    workgroups starting beside the first round give up) makes every sequence
+    of the call a data error, never a hang or a wrong token; the next call,
+    with the automatic bound, is exact again."""
+    if FORM["name"] != "early":
+        pytest.skip("early exit only")
+    w = wl.make_workload("c3", trial=9, B=16, V=128256)
+    ref = oracle.verify(w, threads=16)
+    stalled = 0
+    try:
+        sv.set_queue(item_polls=1)
+        for i in range(3):
+            gpu = run_gpu(sv, w, cuda)
+            if np.all(gpu["n"] == -1):
+                assert np.all(gpu["tokens"] == -1)
+                stalled += 1
+            else:                                  # (every workgroup found its entry in time)
+                compare(w, gpu, ref, f"item_polls 1, call {i}")
+    finally:
+        sv.set_queue()
+    assert stalled >= 1
+    compare(w, run_gpu(sv, w, cuda), ref, "after a stalled call")
