@@ -185,14 +185,17 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
             plan.lag_c = tu.lag_c > tu.lag_a ? tu.lag_c : tu.lag_a;
         } else {
             // An item waiting for what it needs holds its CU slot, so items
-            // start well after their rows: the accept item about 1.4 resident
-            // grids of row segments later, the draw items about 2.3 (measured
-            // on MI355X; shorter lags wait more than they overlap).
+            // start after their rows: the accept item about 0.8 resident grids
+            // of an undecided block's row segments later, the draw items about
+            // 1.3 (measured on MI355X, B=256 k=8 and B=512 ragged k: the
+            // settled sequences' draw chunks listed between the blocks stretch
+            // each block's share of the schedule; lags 1.4 / 2.3 took 2-4 us
+            // longer, much shorter ones wait more than they overlap).
             const double window = static_cast<double>(plan.cus) * rest_per_cu;
             double per_block = (2.0 * static_cast<double>(p.total) / p.B - 2.0 * plan.lead + 1.0) * g.nseg;
             if (per_block < g.nseg) per_block = g.nseg;
-            plan.lag_a = static_cast<int32_t>(1.4 * window / per_block) + 1;
-            plan.lag_c = static_cast<int32_t>(2.3 * window / per_block) + 2;
+            plan.lag_a = static_cast<int32_t>(0.8 * window / per_block) + 1;
+            plan.lag_c = static_cast<int32_t>(1.3 * window / per_block) + 2;
         }
     }
 
