@@ -1,6 +1,6 @@
 // accept.hip -- the staged accept scan: one wave64 per sequence (the scan
 // itself is in accept_scan.h).  (Early exit's scan over the leading
-// positions runs inside row_lead.)
+// positions runs inside the first round, lead_pass.h.)
 #include "accept_scan.h"
 
 namespace sv {

@@ -84,7 +84,9 @@ void split(int64_t V, int64_t target, int64_t max_pieces, int64_t unit, int64_t 
            int64_t& len);
 
 // The segment and chunk geometry and the workspace layout of a call; false
-// when the second round's grid would not fit 2^31 - 1 workgroups.
+// when the second round's grid would not fit 2^31 - 1 workgroups (a call
+// whose two-round launch, the first round's workgroups included, would not
+// fit runs as one pass).
 bool make_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dtype, int64_t seg_elems,
                    int64_t chunk_elems, Geometry& g);
 
