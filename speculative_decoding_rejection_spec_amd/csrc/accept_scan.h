@@ -140,30 +140,33 @@ __device__ __forceinline__ void list_rest(const Problem& p, const Plan& plan, in
     const int32_t nt = settled ? 0 : k - limit + (skip_bonus_row ? 0 : 1);
     const int32_t nd = (settled || no_draft) ? 0 : k - limit;
     const int32_t cnt = settled ? static_cast<int32_t>(nchunk) : (nt + nd) * nseg;
+    if (!settled) {
+        // The marks first, visible before any entry that leads to them.  They
+        // need no place in the schedule, so the reservation below goes out
+        // with them and one store-completion wait covers both.
+        for (int32_t e = lane; e < cnt; e += 64) {
+            const int32_t j = e / nseg, sg = e - j * nseg;
+            const bool tgt = j < nt;
+            const int32_t ps = limit + (tgt ? j : j - nt);            // position in the sequence
+            const int64_t row = tgt ? o + b + ps : o + ps;
+            SegStat* st = plan.seg + (tgt ? row : ntarget + row) * nseg + sg;
+            st_co<true>(&st->head, kUnset64);
+            st_co<true>(&st->s, __longlong_as_double(static_cast<long long>(kUnset64)));
+            if (sg == 0 && !greedy) st_co<true>(&plan.xlogit[tgt ? row : ntarget + row], __uint_as_float(kUnset32));
+        }
+        if (lane == 0 && !greedy) st_co<true>(&plan.task[b].kind, static_cast<int32_t>(kTaskUnset));
+    }
     uint64_t pos = reserved != ~0ull ? reserved : list_reserve(plan, settled, cnt);
+    wait_stores();                                 // (the marks, or a settled sequence's task, and the reply)
     pos = __shfl(pos, 0, 64);
     const int64_t i = static_cast<int64_t>(pos >> 32), base = static_cast<int64_t>(pos & 0xffffffffu);
     const int64_t at = base + max(static_cast<int64_t>(0), i - plan.lag_a) +
                        nchunk * max(static_cast<int64_t>(0), i - plan.lag_c);
     if (settled) {
-        wait_stores();                             // (the task, written before the call)
         for (int32_t c = lane; c < cnt; c += 64)
             store_entry(plan.sched + at + c, rest_item(b, 0, kItemChunkSeq, c, -1), plan.epoch);
         return;
     }
-    // the marks first, visible before any entry that leads to them
-    for (int32_t e = lane; e < cnt; e += 64) {
-        const int32_t j = e / nseg, sg = e - j * nseg;
-        const bool tgt = j < nt;
-        const int32_t ps = limit + (tgt ? j : j - nt);            // position in the sequence
-        const int64_t row = tgt ? o + b + ps : o + ps;
-        SegStat* st = plan.seg + (tgt ? row : ntarget + row) * nseg + sg;
-        st_co<true>(&st->head, kUnset64);
-        st_co<true>(&st->s, __longlong_as_double(static_cast<long long>(kUnset64)));
-        if (sg == 0 && !greedy) st_co<true>(&plan.xlogit[tgt ? row : ntarget + row], __uint_as_float(kUnset32));
-    }
-    if (lane == 0 && !greedy) st_co<true>(&plan.task[b].kind, static_cast<int32_t>(kTaskUnset));
-    wait_stores();
     if (lane == 0) st_co<true>(plan.blk_seq + i, (static_cast<uint64_t>(plan.epoch) << 32) | static_cast<uint32_t>(b));
     for (int32_t e0 = 0; e0 < cnt; e0 += 64) {           // (uniform trip count: every lane shuffles)
         const int32_t e = e0 + lane;
