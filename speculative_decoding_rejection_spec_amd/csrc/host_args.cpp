@@ -54,6 +54,18 @@ int64_t lead_multiplier(int32_t B) {
     return m;
 }
 
+int64_t rounds_lead_blocks(int32_t B, int32_t lead, int32_t nseg) {
+    return static_cast<int64_t>(B) * lead * 2 * nseg;
+}
+
+int64_t rounds_rest_blocks(int32_t B, int64_t total, bool has_offsets, int32_t k_uniform, int32_t lead, int32_t nseg,
+                           int32_t nchunk) {
+    int64_t per = 2 * (static_cast<int64_t>(k_uniform) - lead) + 1;
+    if (per < 0) per = 0;
+    const int64_t rows = has_offsets ? 2 * total + B : static_cast<int64_t>(B) * per;
+    return rows * nseg + static_cast<int64_t>(B) * (1 + nchunk);
+}
+
 int32_t effective_lead(int64_t B, int64_t total, int64_t V, sv_dtype_t dtype, const Tuning& tu) {
     if (tu.lead != kAutoLead) return tu.lead;
     if (total == 0) return 0;                    // only bonus rows: nothing to skip

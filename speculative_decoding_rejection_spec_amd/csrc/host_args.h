@@ -90,6 +90,17 @@ void split(int64_t V, int64_t target, int64_t max_pieces, int64_t unit, int64_t 
 bool make_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dtype, int64_t seg_elems,
                    int64_t chunk_elems, Geometry& g);
 
+// Workgroups of early exit's two-round launch: the first round's (every
+// sequence's leading rows, lead x 2 x nseg each), then enough for every item
+// the first round's scans can list.  An undecided sequence lists its
+// remaining row segments, an accept item and nchunk draw items; a settled
+// sampling sequence nchunk draw items.  With a uniform k an undecided
+// sequence has at most 2 (k - lead) + 1 remaining rows (none when lead > k);
+// with offsets, every row of the call bounds them.
+int64_t rounds_lead_blocks(int32_t B, int32_t lead, int32_t nseg);
+int64_t rounds_rest_blocks(int32_t B, int64_t total, bool has_offsets, int32_t k_uniform, int32_t lead, int32_t nseg,
+                           int32_t nchunk);
+
 inline bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
 // The argument checks of spec_verify and its variants (before anything is enqueued).

@@ -24,6 +24,7 @@
 // Then the staged pick (draw_pick_kernel) redoes any sequence a wait left
 // to it and picks every emitted token.
 #include "draw_pass.h"
+#include "host_args.h"
 #include "lead_pass.h"
 
 namespace sv {
@@ -276,23 +277,11 @@ hipError_t rounds_blocks_per_cu(int32_t dtype, int32_t* blocks) {
     return e;
 }
 
-int64_t rounds_lead_blocks(const Problem& p, const Plan& plan) {
-    return static_cast<int64_t>(p.B) * plan.lead * 2 * plan.nseg;
-}
-
-// Row segments listed at most: with a uniform k every undecided sequence
-// lists at most 2 (k - lead) + 1 rows (none when lead > k); with offsets,
-// every row bounds it.  Then an accept item and nchunk draw items per block.
-int64_t rounds_rest_blocks(const Problem& p, const Plan& plan) {
-    const int64_t rows = p.offsets ? 2 * p.total + p.B
-                                   : static_cast<int64_t>(p.B) *
-                                         max(static_cast<int64_t>(0), 2 * (static_cast<int64_t>(p.k_uniform) - plan.lead) + 1);
-    return rows * plan.nseg + static_cast<int64_t>(p.B) * (1 + plan.nchunk);
-}
-
 hipError_t launch_rounds(const Problem& p, const Plan& plan, hipStream_t s) {
-    const int64_t nlead = rounds_lead_blocks(p, plan);
-    const dim3 grid(static_cast<uint32_t>(nlead + rounds_rest_blocks(p, plan)));
+    const int64_t nlead = host::rounds_lead_blocks(p.B, plan.lead, plan.nseg);
+    const dim3 grid(static_cast<uint32_t>(
+        nlead + host::rounds_rest_blocks(p.B, p.total, p.offsets != nullptr, p.k_uniform, plan.lead, plan.nseg,
+                                         plan.nchunk)));
     if (p.dtype == SV_BF16)
         rounds_kernel<SV_BF16><<<grid, dim3(kThreads), 0, s>>>(p, plan, static_cast<uint32_t>(nlead));
     else

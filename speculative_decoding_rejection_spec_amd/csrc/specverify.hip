@@ -177,7 +177,9 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     plan.lag_a = plan.lag_c = 1 << 30;             // no accept or draw items in the schedule
     plan.queued = plan.lead > 0 && !p.draft_probs;
     // (a call whose two-round grid would not fit 2^31 - 1 workgroups runs as one pass)
-    if (plan.queued && rounds_lead_blocks(pr, plan) + rounds_rest_blocks(pr, plan) > 0x7FFFFFFFll)
+    if (plan.queued && rounds_lead_blocks(p.B, plan.lead, g.nseg) +
+                           rounds_rest_blocks(p.B, p.total, p.offsets != nullptr, p.k_uniform, plan.lead, g.nseg,
+                                              g.nchunk) > 0x7FFFFFFFll)
         plan.lead = plan.queued = 0;
     if (plan.queued) {
         if (tu.lag_a > 0) {

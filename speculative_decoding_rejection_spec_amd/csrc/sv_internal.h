@@ -129,9 +129,7 @@ hipError_t launch_sample_pick(const Problem& p, const Plan& plan, hipStream_t s)
 // Workgroups of the two-round launch one compute unit holds at once
 // (occupancy query).
 hipError_t rounds_blocks_per_cu(int32_t dtype, int32_t* blocks);
-// Workgroups of the two-round launch: the first round's, then the second's.
-int64_t rounds_lead_blocks(const Problem& p, const Plan& plan);
-int64_t rounds_rest_blocks(const Problem& p, const Plan& plan);
+
 hipError_t launch_commit(const int32_t* out_tokens, const int32_t* out_n, const int32_t* offsets,
                          int32_t k_uniform, int32_t B, int32_t* seq_tokens, int32_t* seq_len,
                          int32_t max_len, int32_t* committed, int32_t* committed_offsets, hipStream_t s);

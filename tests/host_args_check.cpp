@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <random>
 #include <vector>
 
@@ -139,6 +140,41 @@ int main() {
     CHECK(workspace_bytes_for(1, 0, 10, static_cast<sv_dtype_t>(7), dflt) == 0);
     check_geometry(1, 0, 0x7FFFFFFF, SV_F32, dflt);
     check_geometry(4096, 4096ll * 8, 152064, SV_BF16, dflt);
+
+    // the two-round grid holds every item the first round's scans can list:
+    // an undecided greedy sequence lists target rows lead..k (when k >= lead),
+    // an undecided sampling sequence target and draft rows lead..k-1 (its bonus
+    // row is read by its draw alone; when k > lead), each nseg segments, plus
+    // an accept item and nchunk draw items; a settled sampling sequence nchunk
+    // draw items
+    auto max_items = [](int64_t k, int64_t lead, int64_t nseg, int64_t nchunk) {
+        int64_t m = nchunk;                                              // settled, sampling
+        if (k >= lead) m = std::max(m, (k - lead + 1) * nseg + 1 + nchunk);        // undecided, greedy
+        if (k > lead) m = std::max(m, 2 * (k - lead) * nseg + 1 + nchunk);         // undecided, sampling
+        return m;
+    };
+    const int32_t nsegs[] = {1, 2, 3, 19}, nchunks[] = {1, 19, 256};
+    for (int32_t k = 0; k <= SV_K_MAX; ++k)
+        for (int32_t lead = 1; lead <= SV_K_MAX + 1; ++lead)
+            for (int32_t ns : nsegs)
+                for (int32_t nc : nchunks) {
+                    const int32_t B = 3;
+                    CHECK(rounds_rest_blocks(B, static_cast<int64_t>(B) * k, false, k, lead, ns, nc) >=
+                          B * max_items(k, lead, ns, nc));
+                    CHECK(rounds_lead_blocks(B, lead, ns) == static_cast<int64_t>(B) * lead * 2 * ns);
+                }
+    for (int i = 0; i < 500; ++i) {              // ragged k with offsets
+        const int32_t B = 1 + static_cast<int32_t>(rng() % 300);
+        const int32_t lead = 1 + static_cast<int32_t>(rng() % 4);
+        const int32_t ns = nsegs[rng() % 4], nc = nchunks[rng() % 3];
+        int64_t total = 0, need = 0;
+        for (int32_t b = 0; b < B; ++b) {
+            const int64_t k = static_cast<int64_t>(rng() % (SV_K_MAX + 1));
+            total += k;
+            need += max_items(k, lead, ns, nc);
+        }
+        CHECK(rounds_rest_blocks(B, total, true, 0, lead, ns, nc) >= need);
+    }
 
     // the first round's order visits every sequence once
     for (int32_t B = 1; B <= 3000; B += (B < 600 ? 1 : 97)) {
