@@ -1,5 +1,5 @@
 // draw.hip -- the staged draw: draw_sums (grid sequence x chunk, 256
-// threads) and draw_pick (one 512-thread workgroup per sequence),
+// threads) and draw_pick (one 256-thread workgroup per sequence),
 // where the kernel boundary publishes the chunk sums; or, for one-pass calls
 // whose draw fits one round of workgroups, draw_all, which also runs the
 // accept scans and the picks.  The work itself is in accept_scan.h and
@@ -30,7 +30,7 @@ __global__ __launch_bounds__(kThreads) void draw_sums_kernel(Problem p, Plan pla
 // workgroup (the other threads only take part in its barriers).  A call
 // whose second round could not find an item's work (never expected) makes
 // every sequence a data error.
-// (At 4 waves per SIMD two 512-thread workgroups share a CU: at most 128 VGPRs.)
+// (At 4 waves per SIMD four 256-thread workgroups share a CU: at most 128 VGPRs.)
 template <int DT, int kPickThreads>
 __global__ __launch_bounds__(kPickThreads, 4) void draw_pick_kernel(Problem p, Plan plan) {
     const int32_t b = blockIdx.x;
@@ -146,16 +146,18 @@ hipError_t launch_draw_sums(const Problem& p, const Plan& plan, hipStream_t s) {
     return hipGetLastError();
 }
 
-// One 512-thread workgroup per sequence (two share a CU once the sequences
-// outnumber the CUs).  1024-thread picks, one per CU, were slower for 256
-// sequences of V = 152064 (13.3 against 11.5 us): twice the waves in every
-// barrier for half the tokens per lane.
+// One 256-thread workgroup per sequence.  The pick is a chain of round
+// trips and workgroup-wide reductions; fewer waves per barrier outweigh the
+// longer per-lane share of its final scan (8 tokens): 256 sequences of
+// V = 152064 took 11.8 against 12.0 us with 512 threads and 13.3 against
+// 11.5 with 1024 (one per CU); 512 ragged sequences of V = 128256 12.1
+// against 12.9 us.
 hipError_t launch_draw_pick(const Problem& p, const Plan& plan, hipStream_t s) {
     const dim3 grid(static_cast<uint32_t>(p.B));
     if (p.dtype == SV_BF16)
-        draw_pick_kernel<SV_BF16, 512><<<grid, dim3(512), 0, s>>>(p, plan);
+        draw_pick_kernel<SV_BF16, 256><<<grid, dim3(256), 0, s>>>(p, plan);
     else
-        draw_pick_kernel<SV_F32, 512><<<grid, dim3(512), 0, s>>>(p, plan);
+        draw_pick_kernel<SV_F32, 256><<<grid, dim3(256), 0, s>>>(p, plan);
     return hipGetLastError();
 }
 
