@@ -89,7 +89,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c4", help="c1 c2 c2g c3 c4 c5")
+    ap.add_argument("--workload", default="c4", help="c1 c2 c2g c3 c4 c4s c5 (c4s: C4 with shuffled halves)")
     ap.add_argument("--copies", type=int, default=4, help="input copies rotated between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true",
@@ -142,7 +142,10 @@ def main():
         return bench_stream(args, sv, torch, np)
 
     t_gen = time.perf_counter()
-    w = wl.make_workload(args.workload)
+    # c4s: C4 with the near-identical and independent drafts on a random half
+    # of the sequences each instead of the first and second half
+    w = (wl.make_workload("c4", shuffle_halves=True) if args.workload == "c4s"
+         else wl.make_workload(args.workload))
     t_gen = time.perf_counter() - t_gen
     if args.entry == "commit":
         return bench_commit(args, sv, torch, np, w)
