@@ -107,16 +107,18 @@ __device__ __forceinline__ double log2_norm(const RowStat& r, float c) {
 // of block i - lag_c (those of the last blocks follow the whole schedule,
 // where the second round finds them by arithmetic), so an item is
 // dispatched about lag blocks after the rows it needs.  The task of an
-// undecided sampling sequence is marked unset until its accept item writes
-// it.  A sampling sequence its leading positions settled (settled) lists
-// only its nchunk draw chunks (kItemChunkSeq), at the schedule's current
-// end: its task is already written, so they can run at once, beside the
-// rows of the sequences listed around it.
+// undecided sampling sequence keeps an earlier call's epoch until its accept
+// item writes it, so its draw items read it as unset (load_task) and wait.
+// A sampling sequence its leading positions settled (settled) lists only its
+// nchunk draw chunks (kItemChunkSeq), at the schedule's current end: its
+// task was written just before, so they can run at once, beside the rows of
+// the sequences listed around it (a chunk that finds its entry before the
+// task's words waits for them like any draw item).
 //
 // One atomic add on blk_ctr (undecided blocks << 32 | row segments and
-// settled chunks listed) places the listing; what the items need is
-// written through and visible before the entries, which carry the call's
-// epoch (store_entry).
+// settled chunks listed) places the listing; the marks an undecided
+// sequence's accept item waits on are written through and visible before
+// the entries, which carry the call's epoch (store_entry).
 //
 // The place in the schedule is taken first (list_reserve, lane 0's atomic
 // add); a settled sequence takes it as soon as its scan decides, before its
@@ -154,10 +156,9 @@ __device__ __forceinline__ void list_rest(const Problem& p, const Plan& plan, in
             st_co<true>(&st->s, __longlong_as_double(static_cast<long long>(kUnset64)));
             if (sg == 0 && !greedy) st_co<true>(&plan.xlogit[tgt ? row : ntarget + row], __uint_as_float(kUnset32));
         }
-        if (lane == 0 && !greedy) st_co<true>(&plan.task[b].kind, static_cast<int32_t>(kTaskUnset));
     }
     uint64_t pos = reserved != ~0ull ? reserved : list_reserve(plan, settled, cnt);
-    wait_stores();                                 // (the marks, or a settled sequence's task, and the reply)
+    if (!settled) wait_stores();                   // (the marks, and the reply)
     pos = __shfl(pos, 0, 64);
     const int64_t i = static_cast<int64_t>(pos >> 32), base = static_cast<int64_t>(pos & 0xffffffffu);
     const int64_t at = base + max(static_cast<int64_t>(0), i - plan.lag_a) +
@@ -365,7 +366,7 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
         if (lane == 0) {
             p.out_n[b] = -1;
             if (p.out_emit_prob) p.out_emit_prob[b] = NAN;
-            st_co<kCo>(&plan.task[b].kind, static_cast<int32_t>(kNone));
+            store_no_task<kCo>(plan, b);
             if (done) *done = kDecided;
         }
     };
@@ -452,18 +453,9 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
                 plan.dlist[base + sg] = rest_item(b, static_cast<int32_t>(drow), kItemDraft, sg, -1);
             }
         }
-        DrawTask* t = plan.task + b;
-        st_co<kCo>(&t->out_slot, static_cast<int32_t>(trow));
-        st_co<kCo>(&t->trow, trow);
-        st_co<kCo>(&t->drow, drow);
-        st_co<kCo>(&t->m_t, rt.m);
-        st_co<kCo>(&t->m_d, n < k ? rd.m : 0.f);
-        st_co<kCo>(&t->T, Tf);
-        st_co<kCo>(&t->u, u_draw);
-        st_co<kCo>(&t->theta, (!greedy && n < k) ? log2_norm(rt, c) - (pending ? 0.0 : log2_norm(rd, c)) : 0.0);
-        if constexpr (kCo) wait_stores();          // the kind, written last, says the rest is visible
-        st_co<kCo>(&t->kind, static_cast<int32_t>(greedy ? kNone : (n < k ? (pending ? kResidualPending : kResidual)
-                                                                          : kind)));
+        store_task<kCo>(plan, b, greedy ? kNone : (n < k ? (pending ? kResidualPending : kResidual) : kind), trow,
+                        drow, rt.m, n < k ? rd.m : 0.f, Tf, u_draw,
+                        (!greedy && n < k) ? log2_norm(rt, c) - (pending ? 0.0 : log2_norm(rd, c)) : 0.0);
     }
     if (early_draw) list_rest(p, plan, b, o, k, limit, true, greedy, bonus_unread, x, true, reserved);
     if (p.out_p && lane < k) {
@@ -482,22 +474,43 @@ __device__ __forceinline__ bool accept_sequence(const Problem& p, const Plan& pl
     return !greedy;
 }
 
-// The DrawTask of sequence b as written by accept_sequence; a pending
-// residual of the gathered form is completed from its draft row's SegStats
-// (read after the accept scan): its maximum, and theta = log2 S_p - log2 S_q.
+// The DrawTask of sequence b as written by accept_sequence (store_task); a
+// pending residual of the gathered form is completed from its draft row's
+// SegStats (read after the accept scan): its maximum, and theta = log2 S_p -
+// log2 S_q.  kind = kTaskUnset when the record is not (yet) this call's: a
+// word still carries another call's epoch.  kCo: the task comes from another
+// workgroup of the same launch; an ordinary load is tried first (a record
+// this XCD has not cached since it was written comes back current) unless
+// kPlainFirst is false, then one written-through load.
 template <bool kCo>
+__device__ __forceinline__ bool fetch_task(const TaskRec* t, uint32_t epoch, uint64_t* w) {
+#pragma unroll
+    for (int i = 0; i < 9; ++i) w[i] = ld_co<kCo>(&t->w[i]);
+    bool cur = true;
+#pragma unroll
+    for (int i = 0; i < 9; ++i) cur = cur && static_cast<uint32_t>(w[i] >> 32) == epoch;
+    return cur;
+}
+template <bool kCo, bool kPlainFirst = true>
 __device__ __forceinline__ DrawTask load_task(const Problem& p, const Plan& plan, int32_t b) {
-    const DrawTask* t = plan.task + b;
+    const TaskRec* t = plan.task + b;
+    uint64_t w[9];
+    bool cur = false;
+    if constexpr (kPlainFirst || !kCo) cur = fetch_task<false>(t, plan.epoch, w);
+    if constexpr (kCo) {
+        if (!cur) cur = fetch_task<true>(t, plan.epoch, w);
+    }
     DrawTask r;
-    r.kind = ld_co<kCo>(&t->kind);
-    r.out_slot = ld_co<kCo>(&t->out_slot);
-    r.trow = ld_co<kCo>(&t->trow);
-    r.drow = ld_co<kCo>(&t->drow);
-    r.m_t = ld_co<kCo>(&t->m_t);
-    r.m_d = ld_co<kCo>(&t->m_d);
-    r.T = ld_co<kCo>(&t->T);
-    r.u = ld_co<kCo>(&t->u);
-    r.theta = ld_co<kCo>(&t->theta);
+    auto lo = [&](int i) { return static_cast<uint32_t>(w[i]); };
+    r.kind = cur ? static_cast<int32_t>(lo(0)) : static_cast<int32_t>(kTaskUnset);
+    r.trow = lo(1);
+    r.out_slot = static_cast<int32_t>(lo(1));
+    r.drow = lo(2);
+    r.m_t = __uint_as_float(lo(3));
+    r.m_d = __uint_as_float(lo(4));
+    r.T = __uint_as_float(lo(5));
+    r.u = __uint_as_float(lo(6));
+    r.theta = __hiloint2double(static_cast<int>(lo(8)), static_cast<int>(lo(7)));
     if (r.kind == kResidualPending) {
         const RowStat rd = merge_row<kCo>(plan.seg + (p.total + p.B + r.drow) * plan.nseg, plan.nseg, false);
         r.m_d = rd.m;

@@ -18,7 +18,9 @@ __global__ __launch_bounds__(kThreads) void draw_sums_kernel(Problem p, Plan pla
     __shared__ DrawLds lds;
     load_exp2_table(tbl, kThreads);            // overlaps the task load
     const DrawTask task = load_task<false>(p, plan, b);
-    if (task.kind == kNone) return;            // the whole workgroup leaves
+    // (the whole workgroup leaves; a task the accept scan did not write is
+    // the pick's data error)
+    if (task.kind == kNone || task.kind == kTaskUnset) return;
     __syncthreads();
     draw_chunk<DT, false>(p, plan, task, b, c, tbl, lds);
 }
@@ -68,6 +70,10 @@ __global__ __launch_bounds__(kPickThreads, 4) void draw_pick_kernel(Problem p, P
         }
         __syncthreads();
         const DrawTask task = load_task<true>(p, plan, b);
+        if (task.kind == kTaskUnset) {         // (not expected: the scan above or the first round wrote it)
+            data_error();
+            return;
+        }
         if (task.kind == kNone) return;
         for (int32_t c = 0; c < plan.nchunk; ++c)
             draw_chunk<DT, true, kPickThreads>(p, plan, task, b, c, tbl, lds.draw);
@@ -78,6 +84,10 @@ __global__ __launch_bounds__(kPickThreads, 4) void draw_pick_kernel(Problem p, P
     }
     const DrawTask task = task0;
     load_exp2_table(tbl, kPickThreads);
+    if (task.kind == kTaskUnset) {             // (not expected: every accept scan writes its task)
+        data_error();
+        return;
+    }
     if (task.kind == kNone) return;
     if (task.kind == kResidual && !(fabsf(task.m_d) <= 3.4e38f)) {
         // The gathered form reads the rejected position's draft row only

@@ -99,7 +99,7 @@ bool make_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dtype, int64_
     g.off_seg = off;
     off = align256(off + sizeof(SegStat) * static_cast<size_t>(rows) * g.nseg);
     g.off_task = off;
-    off = align256(off + sizeof(DrawTask) * static_cast<size_t>(B));
+    off = align256(off + sizeof(TaskRec) * static_cast<size_t>(B));
     g.off_csum = off;
     off = align256(off + sizeof(ChunkSums) * kWaves * static_cast<size_t>(B) * g.nchunk);
     g.off_band_n = off;

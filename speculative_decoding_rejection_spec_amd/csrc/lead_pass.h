@@ -93,7 +93,7 @@ __device__ __forceinline__ void lead_workgroup(const Problem& p, const Plan& pla
             p.out_n[b] = -1;
             if (p.out_emit_prob) p.out_emit_prob[b] = NAN;
             plan.done[b] = kDecided;
-            st_co<true>(&plan.task[b].kind, static_cast<int32_t>(kNone));
+            store_no_task<true>(plan, b);
         }
     }
     if (threadIdx.x == 0) {

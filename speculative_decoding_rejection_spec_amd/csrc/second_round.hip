@@ -195,7 +195,8 @@ __global__ __launch_bounds__(kThreads) void rounds_kernel(Problem p, Plan plan, 
             DrawLds draw;
         } d;
     } lds;
-    __shared__ int32_t s_flag, s_ready;
+    __shared__ int32_t s_flag;
+    __shared__ DrawTask s_task;
     __shared__ uint32_t s_clr;
     __shared__ RestItem s_item;
     __shared__ int32_t s_seq;
@@ -243,26 +244,30 @@ __global__ __launch_bounds__(kThreads) void rounds_kernel(Problem p, Plan plan, 
         else if (tid == 0) st_co<true>(plan.aband + b, 1);   // the pick launch redoes the sequence
         return;
     }
-    // a draw chunk
+    // a draw chunk: thread 0 waits for the sequence's task (a settled
+    // sequence's was written just before its chunks were listed, an
+    // undecided one's comes from its accept item) while the others load the
+    // exp2 table
     if (p.temperature[b] == 0.f) return;           // greedy: nothing to draw
     const int32_t c = item_seg(it);
-    // (a settled sequence's task was written before its chunks were listed)
-    if (kind == kItemChunk && tid == 0) {
-        bool ready = false;
-        if (plan.queue_mode != SV_QUEUE_HANDOFF)
-            for (uint32_t polls = 0; polls < kPolls; ++polls) {
-                if (ld_co<true>(&plan.task[b].kind) != kTaskUnset) { ready = true; break; }
+    if (tid == 0) {
+        DrawTask t{};
+        t.kind = kTaskUnset;
+        if (kind == kItemChunkSeq || plan.queue_mode != SV_QUEUE_HANDOFF) {
+            t = load_task<true>(p, plan, b);
+            for (uint32_t polls = 0; polls < kPolls && t.kind == kTaskUnset; ++polls) {
                 __builtin_amdgcn_s_sleep(8);
+                t = load_task<true, false>(p, plan, b);
             }
-        if (!ready) st_co<true>(plan.aband + b, 1);
-        s_ready = ready;
+        }
+        if (t.kind == kTaskUnset) st_co<true>(plan.aband + b, 1);   // the pick launch redoes the sequence
+        s_task = t;
     }
-    __syncthreads();
-    if (kind == kItemChunk && !s_ready) return;
     load_exp2_table(lds.d.tbl, kThreads);
-    const DrawTask task = load_task<true>(p, plan, b);
-    if (task.kind == kNone) return;                // a data error found past the leading positions
     __syncthreads();
+    const DrawTask task = s_task;
+    // (kNone: a data error found past the leading positions)
+    if (task.kind == kTaskUnset || task.kind == kNone) return;
     draw_chunk<DT, false>(p, plan, task, b, c, lds.d.tbl, lds.d.draw);
 }
 

@@ -147,7 +147,7 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     plan.nchunk = g.nchunk;
     plan.chunk_len = g.chunk_len;
     plan.seg = reinterpret_cast<SegStat*>(ws + g.off_seg);
-    plan.task = reinterpret_cast<DrawTask*>(ws + g.off_task);
+    plan.task = reinterpret_cast<TaskRec*>(ws + g.off_task);
     plan.csum = reinterpret_cast<ChunkSums*>(ws + g.off_csum);
     plan.band_n = reinterpret_cast<int32_t*>(ws + g.off_band_n);
     plan.band_w = reinterpret_cast<double*>(ws + g.off_band_w);

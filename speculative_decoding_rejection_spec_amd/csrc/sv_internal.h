@@ -78,7 +78,7 @@ struct Plan {
     int32_t nchunk;      // chunks per row in the draw
     int64_t chunk_len;   // elements per chunk (multiple of 8)
     SegStat* seg;        // [(2 * total + B) * nseg]; target rows first
-    DrawTask* task;      // [B]
+    TaskRec* task;       // [B]
     ChunkSums* csum;     // [B * nchunk * kWaves]: one per sub-chunk (wave) of each chunk
     int32_t* band_n;     // [B * nchunk * kWaves]: band tokens seen per sub-chunk (wave) of a chunk
     double* band_w;      // [B * nchunk * kWaves * kWaveCap * 2]: their (w_t, w_d)
@@ -219,6 +219,30 @@ __device__ __forceinline__ bool load_entry(const SchedEntry* src, uint32_t epoch
                    static_cast<int32_t>(static_cast<uint32_t>(w2)), static_cast<int32_t>(static_cast<uint32_t>(w3))};
     return static_cast<uint32_t>(w0 >> 32) == epoch && static_cast<uint32_t>(w1 >> 32) == epoch &&
            static_cast<uint32_t>(w2 >> 32) == epoch && static_cast<uint32_t>(w3 >> 32) == epoch;
+}
+
+// Sequence b's DrawTask record (TaskRec): every word carries the call's
+// epoch, so the stores need no order among themselves (kCo: written through,
+// for workgroups of the same launch).
+template <bool kCo>
+__device__ __forceinline__ void store_task(const Plan& plan, int32_t b, int32_t kind, int64_t trow, int64_t drow,
+                                           float m_t, float m_d, float T, float u, double theta) {
+    TaskRec* r = plan.task + b;
+    const uint64_t e = static_cast<uint64_t>(plan.epoch) << 32;
+    st_co<kCo>(&r->w[1], e | static_cast<uint32_t>(trow));
+    st_co<kCo>(&r->w[2], e | static_cast<uint32_t>(drow));
+    st_co<kCo>(&r->w[3], e | __float_as_uint(m_t));
+    st_co<kCo>(&r->w[4], e | __float_as_uint(m_d));
+    st_co<kCo>(&r->w[5], e | __float_as_uint(T));
+    st_co<kCo>(&r->w[6], e | __float_as_uint(u));
+    st_co<kCo>(&r->w[7], e | static_cast<uint32_t>(__double2loint(theta)));
+    st_co<kCo>(&r->w[8], e | static_cast<uint32_t>(__double2hiint(theta)));
+    st_co<kCo>(&r->w[0], e | static_cast<uint32_t>(kind));
+}
+// A task that draws nothing (greedy, or a data error).
+template <bool kCo>
+__device__ __forceinline__ void store_no_task(const Plan& plan, int32_t b) {
+    store_task<kCo>(plan, b, kNone, 0, 0, 0.f, 0.f, 0.f, 0.f, 0.0);
 }
 
 // c = log2(e) / T as the row pass uses it (the accept scan must form the same

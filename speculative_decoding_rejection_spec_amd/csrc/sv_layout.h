@@ -38,15 +38,16 @@ constexpr uint32_t kUnset32 = ~0u;
 // kResidualPending: a residual draw of the gathered form, whose draft row n
 // is read after the accept scan (its maximum and normaliser come from that
 // row's SegStats; DrawTask::theta holds log2 S_p until then).
-// kTaskUnset: early exit's second round has not yet written the task (its
-// kind is written last, after the other fields are visible).
+// kTaskUnset: what a read of a task the call has not (yet) written returns
+// (its record still carries an earlier call's epoch).
 // kBonusSelf: a bonus draw whose row the row pass did not read (early exit
 // beside the draws): the draw takes the weights relative to references of
 // its own, and the pick checks the row's maximum (a non-finite one makes the
 // sequence a data error).
 enum : int32_t { kTaskUnset = -1, kNone = 0, kResidual = 1, kBonus = 2, kResidualPending = 3, kBonusSelf = 4 };
 
-// The draw one sequence still needs after the accept scan.
+// The draw one sequence still needs after the accept scan (as a kernel
+// holds it; TaskRec is its form in the workspace).
 struct DrawTask {
     int32_t kind;      // kNone (greedy, error), kResidual (n < k), kBonus or kBonusSelf (n = k)
     int32_t out_slot;  // index into out_tokens of the emitted token
@@ -55,6 +56,16 @@ struct DrawTask {
     float m_t, m_d;    // exact maxima of those rows
     float T, u;        // temperature and the draw uniform
     double theta;      // log2(S_p / S_q) from the row pass: p_v > q_v iff d_v > theta
+};
+
+// A DrawTask in the workspace: nine 64-bit words, each with the number
+// (epoch) of the call that wrote it in its high half and one 32-bit field in
+// its low half: kind, trow, drow, m_t, m_d, T, u, and theta's low and high
+// words (out_slot is trow).  A reader takes the task once every word carries
+// its call's epoch, so the writer's stores may land in any order and a task
+// of an earlier call reads as not yet written.  One record per 128-byte line.
+struct alignas(128) TaskRec {
+    uint64_t w[9];
 };
 
 // Partial sums of the draw over one sub-chunk (fp64).

@@ -62,6 +62,7 @@ static void check_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dt, c
     // every record the kernels index fits before the next block
     const size_t rows = static_cast<size_t>(2 * total + B);
     CHECK(g.off_task - g.off_seg >= sizeof(SegStat) * rows * static_cast<size_t>(g.nseg));
+    CHECK(g.off_task + sizeof(TaskRec) * static_cast<size_t>(B) <= g.off_csum);
     const size_t entries = rows * g.nseg + static_cast<size_t>(B) * (1 + g.nchunk);
     CHECK(g.off_sched + sizeof(SchedEntry) * entries <= g.off_blk_ctr);
     CHECK(g.off_blk_seq + sizeof(uint64_t) * static_cast<size_t>(B) <= g.off_dlist);
