@@ -87,7 +87,6 @@ __device__ __forceinline__ RowStat merge_row(const SegStat* seg, int32_t nseg, b
 // The statistics a sampling sequence's accept scan reads, loaded by the wave
 // that polled for them (rows of at most kPolledSegs segments): lane i holds
 // position i's target and draft row segments and captured logits.
-constexpr int kPolledSegs = 2;
 struct Polled {
     uint64_t th[kPolledSegs], dh[kPolledSegs];
     double ts[kPolledSegs], ds[kPolledSegs];

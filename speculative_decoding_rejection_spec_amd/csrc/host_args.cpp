@@ -135,6 +135,8 @@ bool make_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dtype, int64_
     off = align256(off + sizeof(uint64_t));
     g.off_stall = off;
     off = align256(off + sizeof(uint32_t));
+    g.off_lead_rec = off;
+    off = align256(off + sizeof(LeadRec) * 2 * kPolledSegs * static_cast<size_t>(B));
     g.bytes = off;
     return true;
 }

@@ -14,11 +14,15 @@
 // sequences that settle early should not come in one run because the
 // caller grouped them.  A workgroup whose row does not exist (position past k_b, a
 // draft row the tests do not use, or a sequence whose offsets describe no
-// usable range) streams nothing.  Every workgroup then counts itself on its
-// sequence's counter, its statistics written through first; the one that
+// usable range) streams nothing.  With one leading position and rows of at
+// most kPolledSegs segments (the usual case), every workgroup writes its
+// statistics as an epoch-tagged record (LeadRec) and leaves; the sequence's
+// last workgroup (highest index) polls the records and runs the accept
+// scan on them.  Otherwise every workgroup counts itself on its sequence's
+// counter, its statistics written through first, and the one that
 // completes the count (all lead x 2 x nseg workgroups of the sequence) runs
-// the accept scan, so the scans run beside the streaming of other
-// sequences' rows.  Finally it counts the sequence on plan.lead_done, after
+// the accept scan.  Either way the scans run beside the streaming of other
+// sequences' rows.  Finally the scan counts the sequence on plan.lead_done, after
 // everything the scan listed is visible: a second-round workgroup that sees
 // every sequence counted knows the whole schedule is written.  (lead_done
 // takes a plain atomic add: the sequences finish their scans at nearly the
@@ -35,6 +39,69 @@ namespace sv {
 // clears them first thing, so the wait is never expected to run out; if it
 // does the sequence becomes a data error rather than a hang).
 constexpr uint32_t kClearPolls = 1u << 22;
+
+// The accept scan of sequence b from the first round's records (LeadRec:
+// one leading position, rows of at most kPolledSegs segments), run by wave
+// 0 of the sequence's last first-round workgroup: each lane polls one word
+// of the sequence's records (an ordinary load first, then written-through
+// loads) until all carry the call's epoch and the list counters are
+// cleared, and lane 0 gets position 0's statistics and captured logits
+// (Polled), so the scan loads no statistics itself.
+__device__ __forceinline__ void lead_scan_polled(const Problem& p, const Plan& plan, int32_t b, bool usable,
+                                                 int64_t o, int64_t k) {
+    const int lane = threadIdx.x & 63;
+    const int32_t nseg = plan.nseg;
+    const int32_t nw = 2 * nseg * 5;                     // (at most 20 words)
+    const uint64_t* words = plan.lead_rec[static_cast<int64_t>(b) * 2 * nseg].w;
+    // the drafted token of position 0 names the segment that captured its logits
+    const int32_t x = (usable && k >= 1) ? p.tokens[o] : -1;
+    uint64_t wv = lane < nw ? words[lane] : 0;
+    bool cur = lane >= nw || static_cast<uint32_t>(wv >> 32) == plan.epoch;
+    uint32_t clr = ld_co<true>(plan.lead_clr);
+    bool ready = false;
+    for (uint32_t polls = 0; polls < kClearPolls; ++polls) {
+        ready = __ballot(!cur) == 0 && __shfl(clr, 0, 64) == plan.epoch;
+        if (ready) break;
+        __builtin_amdgcn_s_sleep(2);
+        if (!cur) {
+            wv = ld_co<true>(words + lane);
+            cur = static_cast<uint32_t>(wv >> 32) == plan.epoch;
+        }
+        if (clr != plan.epoch) clr = ld_co<true>(plan.lead_clr);
+    }
+    if (!ready) {
+        // (not expected: every first-round workgroup writes its record)
+        if (usable)
+            for (int64_t j = lane; j <= k; j += 64) p.out_tokens[o + b + j] = -1;
+        if (lane == 0) {
+            p.out_n[b] = -1;
+            if (p.out_emit_prob) p.out_emit_prob[b] = NAN;
+            plan.done[b] = kDecided;
+            store_no_task<true>(plan, b);
+        }
+        return;
+    }
+    auto word = [&](int rec, int j) {              // (every lane takes part)
+        return static_cast<uint32_t>(__shfl(static_cast<int>(static_cast<uint32_t>(wv)), rec * 5 + j, 64));
+    };
+    Polled pre;
+#pragma unroll
+    for (int sg = 0; sg < kPolledSegs; ++sg) {
+        const int st = sg < nseg ? sg : 0, sd = nseg + st;
+        pre.th[sg] = (static_cast<uint64_t>(word(st, 1)) << 32) | word(st, 0);
+        pre.ts[sg] = __hiloint2double(static_cast<int>(word(st, 3)), static_cast<int>(word(st, 2)));
+        pre.dh[sg] = (static_cast<uint64_t>(word(sd, 1)) << 32) | word(sd, 0);
+        pre.ds[sg] = __hiloint2double(static_cast<int>(word(sd, 3)), static_cast<int>(word(sd, 2)));
+    }
+    int32_t sx = (x >= 0 && x < p.V) ? static_cast<int32_t>(x / plan.seg_len) : 0;
+    if (sx >= nseg) sx = nseg - 1;
+    pre.xt = __uint_as_float(word(sx, 4));
+    pre.xd = __uint_as_float(word(nseg + sx, 4));
+    // (cleared before the sequence is listed: a second-round item marks it
+    // only after a long wait of its own)
+    if (lane == 0) st_co<true>(plan.aband + b, 0);
+    accept_sequence<true>(p, plan, b, 1, plan.done + b, nullptr, true, &pre);
+}
 
 // s_last, s_clr: LDS words of the calling kernel.
 template <int DT>
@@ -58,16 +125,36 @@ __device__ __forceinline__ void lead_workgroup(const Problem& p, const Plan& pla
     q >>= 1;
     const int32_t i = static_cast<int32_t>(q % plan.lead);
     const int32_t b = static_cast<int32_t>((q / plan.lead) * plan.lead_mul % p.B);
+    // One leading position, rows of at most kPolledSegs segments: the
+    // sequence's workgroups hand their statistics over as records (LeadRec)
+    // and the last of them runs the scan, with no count of arrivals.
+    const bool recs = plan.lead == 1 && plan.nseg <= kPolledSegs;
     // (cleared by one of the sequence's own workgroups, before it counts
     // itself: the sequence is listed, and a second-round item can mark it,
     // only after that)
-    if (i == 0 && is_target && seg == 0 && threadIdx.x == 0) st_co<true>(plan.aband + b, 0);
+    if (!recs && i == 0 && is_target && seg == 0 && threadIdx.x == 0) st_co<true>(plan.aband + b, 0);
     const int64_t o = first_slot(p, b);
     const int64_t o1 = p.offsets ? static_cast<int64_t>(p.offsets[b + 1]) : o + p.k_uniform;
     const int64_t k = o1 - o;
     const bool usable = o >= 0 && o1 >= o && k <= kKMax && o1 <= p.total;
     const bool exists = usable && (is_target ? i <= k : (i < k && !p.draft_probs));
-    if (exists) row_segment<DT, true>(p, plan, b, is_target, is_target ? o + b + i : o + i, seg, lds);
+    LeadRec* rec = recs ? plan.lead_rec + (static_cast<int64_t>(b) * 2 + (is_target ? 0 : 1)) * plan.nseg + seg
+                        : nullptr;
+    if (exists)
+        row_segment<DT, true>(p, plan, b, is_target, is_target ? o + b + i : o + i, seg, lds, kXFromOffsets, rec);
+    else if (rec && threadIdx.x == 0)
+        store_lead_rec(rec, plan.epoch, 0, 0.0, 0.f);
+    if (recs) {
+        // The scan: the draft row's last segment, the sequence's highest
+        // index, so it waits only for workgroups dispatched before it.
+        if (is_target || seg != plan.nseg - 1 || threadIdx.x >= 64) return;
+        lead_scan_polled(p, plan, b, usable, o, k);
+        if (threadIdx.x == 0) {
+            wait_stores();                         // (the wave's listing stores, every lane's)
+            __hip_atomic_fetch_add(plan.lead_done, uint64_t{1}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        return;
+    }
     if (threadIdx.x == 0) {
         // (the counter and lead_clr are loaded while the statistics' stores
         // complete: the wait for those covers both round trips)

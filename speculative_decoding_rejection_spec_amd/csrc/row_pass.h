@@ -294,19 +294,24 @@ struct RowLds {
 // are skipped.  kCo selects stores that other workgroups of the same launch
 // may read (see st_co).  kWindow: 16-byte loads in flight per lane (0: the
 // dtype's default, sized for full occupancy).  x_hint: the drafted token of
-// this row (-1: none), when the caller knows it, else kXFromOffsets.
+// this row (-1: none), when the caller knows it, else kXFromOffsets.  rec
+// (first round, see LeadRec): also written, whether or not the row is read.
 constexpr int32_t kXFromOffsets = -2;   // row_segment's x_hint: look the drafted token up
 
 template <int DT, bool kCo, int kWindowArg = 0>
 __device__ __forceinline__ void row_segment(const Problem& p, const Plan& plan, int32_t b, bool is_target,
                                             int64_t r, int64_t seg, RowLds& lds,
-                                            int32_t x_hint = kXFromOffsets) {
+                                            int32_t x_hint = kXFromOffsets, LeadRec* rec = nullptr) {
     using namespace rowpass;
     constexpr int kWindow = kWindowArg > 0 ? kWindowArg : Elem<DT>::kWindow;
     const float T = p.temperature[b];
-    if (!temperature_ok(T)) return;               // reported by the accept scan
     const bool greedy = (T == 0.f);
-    if (greedy && !is_target) return;             // greedy never reads draft rows
+    // (a bad temperature is reported by the accept scan; greedy never reads
+    // draft rows)
+    if (!temperature_ok(T) || (greedy && !is_target)) {
+        if (rec && threadIdx.x == 0) store_lead_rec(rec, plan.epoch, 0, 0.0, 0.f);
+        return;
+    }
 
     using E = typename Elem<DT>::T;
     const int64_t ntarget = p.total + p.B;
@@ -349,6 +354,7 @@ __device__ __forceinline__ void row_segment(const Problem& p, const Plan& plan, 
             for (int i = 1; i < kWaves; ++i) merge_argmax(m, a, lds.m[i], lds.a[i]);
             st_co<kCo>(&plan.seg[w].head, seg_head(m, static_cast<uint32_t>(a)));
             st_co<kCo>(&plan.seg[w].s, 0.0);
+            if (rec) store_lead_rec(rec, plan.epoch, seg_head(m, static_cast<uint32_t>(a)), 0.0, 0.f);
         }
     } else {
         SoftmaxAcc acc;
@@ -366,6 +372,7 @@ __device__ __forceinline__ void row_segment(const Problem& p, const Plan& plan, 
             st_co<kCo>(&plan.seg[w].head, seg_head(m, __float_as_uint(R)));
             st_co<kCo>(&plan.seg[w].s, s);
             if (capture) st_co<kCo>(&plan.xlogit[is_target ? r : ntarget + r], zx);
+            if (rec) store_lead_rec(rec, plan.epoch, seg_head(m, __float_as_uint(R)), s, capture ? zx : 0.f);
         }
     }
 }

@@ -163,6 +163,7 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     plan.lead_ctr = reinterpret_cast<uint64_t*>(ws + g.off_lead_ctr);
     plan.lead_clr = reinterpret_cast<uint32_t*>(ws + g.off_lead_clr);
     plan.lead_done = reinterpret_cast<uint64_t*>(ws + g.off_lead_done);
+    plan.lead_rec = reinterpret_cast<LeadRec*>(ws + g.off_lead_rec);
     plan.stall = reinterpret_cast<uint32_t*>(ws + g.off_stall);
     plan.item_polls = tu.item_polls;
     plan.epoch = next_epoch();

@@ -102,6 +102,7 @@ struct Plan {
     uint64_t* lead_ctr;  // early exit: [B] epoch << 32 | leading segments of sequence b finished
     uint32_t* lead_clr;  // early exit: the epoch of the call whose first round has cleared the list counters
     uint64_t* lead_done; // early exit: epoch << 32 | sequences whose leading accept scan has finished
+    LeadRec* lead_rec;   // early exit, lead 1, nseg <= kPolledSegs: [B][2][nseg] first-round records
                          // (set to epoch << 32 before lead_clr is published)
     uint32_t* stall;     // early exit: the epoch of a call whose second round could not find an item's work
     uint32_t item_polls; // early exit: bound of a second-round workgroup's wait for its item
@@ -240,6 +241,16 @@ __device__ __forceinline__ void store_task(const Plan& plan, int32_t b, int32_t 
     st_co<kCo>(&r->w[0], e | static_cast<uint32_t>(kind));
 }
 // A task that draws nothing (greedy, or a data error).
+// A first-round workgroup's LeadRec (written through).
+__device__ __forceinline__ void store_lead_rec(LeadRec* r, uint32_t epoch, uint64_t head, double s, float x) {
+    const uint64_t e = static_cast<uint64_t>(epoch) << 32;
+    st_co<true>(&r->w[0], e | static_cast<uint32_t>(head));
+    st_co<true>(&r->w[1], e | static_cast<uint32_t>(head >> 32));
+    st_co<true>(&r->w[2], e | static_cast<uint32_t>(__double2loint(s)));
+    st_co<true>(&r->w[3], e | static_cast<uint32_t>(__double2hiint(s)));
+    st_co<true>(&r->w[4], e | __float_as_uint(x));
+}
+
 template <bool kCo>
 __device__ __forceinline__ void store_no_task(const Plan& plan, int32_t b) {
     store_task<kCo>(plan, b, kNone, 0, 0, 0.f, 0.f, 0.f, 0.f, 0.0);

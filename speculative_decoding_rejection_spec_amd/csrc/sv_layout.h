@@ -58,6 +58,23 @@ struct DrawTask {
     double theta;      // log2(S_p / S_q) from the row pass: p_v > q_v iff d_v > theta
 };
 
+// Rows of at most this many segments have their statistics handed to an
+// accept scan by the wave that polled for them (accept_scan.h's Polled;
+// LeadRec below).
+constexpr int kPolledSegs = 2;
+
+// What one first-round workgroup of early exit (one leading position per
+// sequence, rows of at most kPolledSegs segments) hands to its sequence's
+// accept scan: its segment's head (two words: low, high half) and sum (two
+// words), and the logit of the drafted token if its segment holds it (one
+// word, else 0), each word with the call's epoch in its high half.  Every
+// first-round workgroup writes its record, also one whose row is not read
+// (then the words carry the epoch and nothing else), so the scan waits for
+// a fixed set of records.  Indexed [sequence][target, draft][segment].
+struct LeadRec {
+    uint64_t w[5];
+};
+
 // A DrawTask in the workspace: nine 64-bit words, each with the number
 // (epoch) of the call that wrote it in its high half and one 32-bit field in
 // its low half: kind, trow, drow, m_t, m_d, T, u, and theta's low and high

@@ -54,7 +54,8 @@ static void check_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dt, c
     const size_t offs[] = {g.off_seg,     g.off_task,     g.off_csum,     g.off_band_n,    g.off_band_w,
                            g.off_xlogit,  g.off_done,     g.off_sched,    g.off_blk_ctr,   g.off_blk_seq,
                            g.off_dlist,   g.off_dlist_n,  g.off_nbuf,     g.off_aband,     g.off_picked,
-                           g.off_lead_ctr, g.off_lead_clr, g.off_lead_done, g.off_stall,    g.bytes};
+                           g.off_lead_ctr, g.off_lead_clr, g.off_lead_done, g.off_stall,    g.off_lead_rec,
+                           g.bytes};
     for (size_t i = 0; i < sizeof(offs) / sizeof(offs[0]); ++i) {
         CHECK(offs[i] % 256 == 0);
         if (i > 0) CHECK(offs[i] >= offs[i - 1]);
@@ -66,6 +67,7 @@ static void check_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dt, c
     const size_t entries = rows * g.nseg + static_cast<size_t>(B) * (1 + g.nchunk);
     CHECK(g.off_sched + sizeof(SchedEntry) * entries <= g.off_blk_ctr);
     CHECK(g.off_blk_seq + sizeof(uint64_t) * static_cast<size_t>(B) <= g.off_dlist);
+    CHECK(g.off_lead_rec + sizeof(LeadRec) * 2 * kPolledSegs * static_cast<size_t>(B) <= g.bytes);
     CHECK(g.bytes == workspace_bytes_for(B, total, V, dt, tu));
 }
 
