@@ -287,3 +287,28 @@ def test_item_wait_that_runs_out_reports_data_errors(sv, cuda):
         sv.set_queue()
     assert stalled >= 1
     compare(w, run_gpu(sv, w, cuda), ref, "after a stalled call")
+
+
+# --------------------------------------------------------------------------
+# the first round's two hand-overs to the accept scan
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("seg", [0, 32768, 12288])
+def test_first_round_records_and_counts(sv, cuda, seg):
+    """Early exit after one leading position hands each first-round
+    workgroup's statistics to its sequence's scan as epoch-tagged records
+    when a row has at most two segments (V = 50000 bf16: one segment by
+    default, two at 32768 logits per segment), and through a count of
+    arrivals otherwise (five segments at 12288).  Both against the oracle,
+    over several calls (the records of one call must never pass for the
+    next call's)."""
+    if FORM["name"] != "early":
+        pytest.skip("early exit only")
+    w = wl.make_workload("c3", trial=11, B=24, V=50000)
+    ref = oracle.verify(w, threads=16)
+    try:
+        sv.set_geometry(seg_elems=seg)
+        sv.set_early_exit(1)
+        for i in range(3):
+            compare(w, run_gpu(sv, w, cuda), ref, f"seg {seg}, call {i}")
+    finally:
+        sv.set_geometry()
