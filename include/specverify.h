@@ -120,8 +120,8 @@ sv_status_t spec_verify(const void *target_logits, const void *draft_logits,
  * address is looked up once per GPU, on the first call there) and calls no
  * allocating routine.  A call whose workspace (spec_verify_workspace_size)
  * exceeds the array returns SV_ERR_SCRATCH before anything is enqueued
- * (256 sequences of k = 8 at V = 152064 need 3.4 MiB, 512 of k <= 10 at
- * V = 128256 6.0 MiB).  Every call on one GPU shares that GPU's array and
+ * (256 sequences of k = 8 at V = 152064 need 3.7 MiB, 512 of k <= 10 at
+ * V = 128256 6.1 MiB).  Every call on one GPU shares that GPU's array and
  * finds it holding the previous call's contents (each call re-initialises
  * what it reads): calls that overlap in time on one GPU, on different
  * streams, race and give wrong results. */
