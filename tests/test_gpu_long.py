@@ -1,6 +1,7 @@
 """Long parity runs: 10^4 sequences per small configuration (C1, C2, C3) and
-about 1800 at the full sizes (three C4 batches of 256, two C5 batches of
-512, both in the default early-exit form), in batches of fresh seeds,
+about 2300 at the full sizes (three C4 batches of 256, two of C4 with its
+two kinds of drafts on random halves, two C5 batches of 512, all in the
+default early-exit form), in batches of fresh seeds,
 through the default launch form; tokens and accept counts bit-exact on
 every sequence the oracle does not flag, flagged sequences valid, and the
 flagged share under 0.1%.  Generating the synthetic rows dominates the time
@@ -16,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 BATCHES = [("c1", 2500, t) for t in range(100, 104)] + [("c2", 2000, t) for t in range(100, 105)] + \
           [("c3", 2000, t) for t in range(100, 105)] + [("c4", 256, t) for t in range(100, 103)] + \
-          [("c5", 512, t) for t in range(100, 102)]
+          [("c4s", 256, t) for t in range(100, 102)] + [("c5", 512, t) for t in range(100, 102)]
 TOTALS = {}
 
 
@@ -30,7 +31,8 @@ def sv(cuda):
 @pytest.mark.parametrize("name,B,trial", BATCHES, ids=[f"{n}-t{t}" for n, _, t in BATCHES])
 def test_long_parity_batch(sv, cuda, name, B, trial):
     print(f"[{name} trial {trial} B={B}]", flush=True)
-    w = wl.make_workload(name, trial=trial, B=B)
+    w = (wl.make_workload("c4", trial=trial, B=B, shuffle_halves=True) if name == "c4s"
+         else wl.make_workload(name, trial=trial, B=B))
     ref = oracle.verify(w, threads=16)
     n, a = compare(w, run_gpu(sv, w, cuda), ref, f"{name}-t{trial}")
     tot = TOTALS.setdefault(name, [0, 0])
