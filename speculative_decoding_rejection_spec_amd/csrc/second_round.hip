@@ -13,10 +13,11 @@
 //     so workgroups on other XCDs see them);
 //   * an accept item: polls until every statistic and captured logit of its
 //     sequence's rows is written (the lister marked them unset), then runs
-//     the sequence's accept scan, whose draw task is written with its kind
-//     last;
-//   * a draw item: polls until its sequence's task kind is set (a settled
-//     sequence's is set before its chunks are listed), then sums its chunk.
+//     the sequence's accept scan, which writes its draw task as an
+//     epoch-tagged record (TaskRec);
+//   * a draw item: polls until its sequence's task record is this call's (a
+//     settled sequence's is written just before its chunks are listed), then
+//     sums its chunk.
 // Items are dispatched in grid order, so by the time an item waits, what it
 // waits for is running or done (the lags put about a resident grid of row
 // segments in between, so it is usually done).

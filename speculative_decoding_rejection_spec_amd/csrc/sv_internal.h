@@ -16,13 +16,14 @@
 //                  locates the chunk that holds u * Z and the token inside it.
 // Early exit (Plan::lead > 0): one launch (second_round.hip) runs two
 // rounds.  Its first workgroups read the leading positions of every
-// sequence (lead_pass.h), and the workgroup that finishes a sequence's last
-// leading segment runs its accept scan, which settles the sequence or lists
+// sequence (lead_pass.h), and the sequence's last workgroup (or, with more
+// leading positions or segments, the one that completes its count of
+// arrivals) runs its accept scan, which settles the sequence or lists
 // its remaining rows; the later workgroups take the listed items in order:
 // those rows, the undecided sequences' accept scans and every draw chunk.
 // Then draw_pick picks.  The gathered form runs the first round as its own
-// launch (row_lead), streams the listed rows (row_list), then runs steps
-// 2-4 with the draft rows at rejections read in between.
+// launch (row_lead), streams the listed rows (sched_rows), then runs steps
+// 2-4 with the draft rows at rejections read in between (row_list).
 #pragma once
 
 #include <hip/hip_runtime.h>
