@@ -140,6 +140,11 @@ __device__ __forceinline__ void lead_workgroup(const Problem& p, const Plan& pla
     const bool exists = usable && (is_target ? i <= k : (i < k && !p.draft_probs));
     LeadRec* rec = recs ? plan.lead_rec + (static_cast<int64_t>(b) * 2 + (is_target ? 0 : 1)) * plan.nseg + seg
                         : nullptr;
+    // (the second half waits: Plan::lead_pace; s_memrealtime counts at 100 MHz)
+    if (plan.lead_pace != 0 && w >= static_cast<int64_t>(p.B) * plan.lead * plan.nseg) {
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        while (__builtin_amdgcn_s_memrealtime() - t0 < plan.lead_pace) __builtin_amdgcn_s_sleep(10);
+    }
     if (exists)
         row_segment<DT, true>(p, plan, b, is_target, is_target ? o + b + i : o + i, seg, lds, kXFromOffsets, rec);
     else if (rec && threadIdx.x == 0)

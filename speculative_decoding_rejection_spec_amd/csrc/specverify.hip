@@ -164,6 +164,7 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     plan.lead_clr = reinterpret_cast<uint32_t*>(ws + g.off_lead_clr);
     plan.lead_done = reinterpret_cast<uint64_t*>(ws + g.off_lead_done);
     plan.lead_rec = reinterpret_cast<LeadRec*>(ws + g.off_lead_rec);
+    plan.lead_pace = 0;
     plan.stall = reinterpret_cast<uint32_t*>(ws + g.off_stall);
     plan.item_polls = tu.item_polls;
     plan.epoch = next_epoch();
@@ -199,6 +200,19 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
             if (per_block < g.nseg) per_block = g.nseg;
             plan.lag_a = static_cast<int32_t>(0.8 * window / per_block) + 1;
             plan.lag_c = static_cast<int32_t>(1.3 * window / per_block) + 2;
+        }
+        // Pacing of the first round when all of it is resident at once (one
+        // leading position, records): its second half of workgroups waits
+        // about 90% of the time the first half takes to stream its rows at
+        // the read ceiling (~7 TB/s), so that the first half's scans list
+        // second-round work while the second half streams instead of all
+        // scans finishing together (C4: 2-3 us shorter; a first round larger
+        // than the resident grid staggers by itself, and pacing it was slower).
+        const int64_t nlead = rounds_lead_blocks(p.B, plan.lead, g.nseg);
+        if (plan.lead == 1 && g.nseg <= kPolledSegs &&
+            static_cast<double>(nlead) <= static_cast<double>(plan.cus) * rest_per_cu) {
+            const double half_bytes = static_cast<double>(p.B) * p.V * (p.dtype == SV_BF16 ? 2 : 4);
+            plan.lead_pace = static_cast<uint32_t>(0.9 * half_bytes / 7.0e12 * 1e8);
         }
     }
 

@@ -104,6 +104,7 @@ struct Plan {
     uint32_t* lead_clr;  // early exit: the epoch of the call whose first round has cleared the list counters
     uint64_t* lead_done; // early exit: epoch << 32 | sequences whose leading accept scan has finished
     LeadRec* lead_rec;   // early exit, lead 1, nseg <= kPolledSegs: [B][2][nseg] first-round records
+    uint32_t lead_pace;  // early exit: 100 MHz ticks the first round's second half waits before streaming (0: none)
                          // (set to epoch << 32 before lead_clr is published)
     uint32_t* stall;     // early exit: the epoch of a call whose second round could not find an item's work
     uint32_t item_polls; // early exit: bound of a second-round workgroup's wait for its item
