@@ -39,6 +39,7 @@ namespace sv {
 // clears them first thing, so the wait is never expected to run out; if it
 // does the sequence becomes a data error rather than a hang).
 constexpr uint32_t kClearPolls = 1u << 22;
+constexpr uint32_t kPaceSleeps = 4096;   // bound of the first round's pacing wait (Plan::lead_pace)
 
 // The accept scan of sequence b from the first round's records (LeadRec:
 // one leading position, rows of at most kPolledSegs segments), run by wave
@@ -140,10 +141,13 @@ __device__ __forceinline__ void lead_workgroup(const Problem& p, const Plan& pla
     const bool exists = usable && (is_target ? i <= k : (i < k && !p.draft_probs));
     LeadRec* rec = recs ? plan.lead_rec + (static_cast<int64_t>(b) * 2 + (is_target ? 0 : 1)) * plan.nseg + seg
                         : nullptr;
-    // (the second half waits: Plan::lead_pace; s_memrealtime counts at 100 MHz)
+    // (the second half waits: Plan::lead_pace; s_memrealtime counts at 100 MHz.
+    // The wait also ends after kPaceSleeps sleeps of ~640 clocks, ~1 ms, whatever
+    // the counter reads.)
     if (plan.lead_pace != 0 && w >= static_cast<int64_t>(p.B) * plan.lead * plan.nseg) {
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-        while (__builtin_amdgcn_s_memrealtime() - t0 < plan.lead_pace) __builtin_amdgcn_s_sleep(10);
+        for (uint32_t n = 0; n < kPaceSleeps && __builtin_amdgcn_s_memrealtime() - t0 < plan.lead_pace; ++n)
+            __builtin_amdgcn_s_sleep(10);
     }
     if (exists)
         row_segment<DT, true>(p, plan, b, is_target, is_target ? o + b + i : o + i, seg, lds, kXFromOffsets, rec);
