@@ -13,8 +13,8 @@ One step = one spec_verify call (row pass, accept scan, fp64 draw) over the
 whole batch.  Output: one JSON line with sequences/s, the achieved HBM
 bandwidth on algorithmic bytes, the roofline of the dominant kernel and the
 fp64 CPU oracle timed on this host as a baseline.  The dominant kernel is
-early exit's second round (the remaining rows and every draw row) for C4 and
-C5, the one-pass row pass for smaller calls.
+early exit's two-round launch (every row the step reads and every draw row)
+for C4 and C5, the one-pass row pass for smaller calls.
 
 Algorithmic bytes per step: the logit rows the step reads, once each, plus
 one extra read of each draw row (2 rows for a residual draw, 1 for a bonus
