@@ -19,7 +19,8 @@
 // statistics as an epoch-tagged record (LeadRec) and leaves; the sequence's
 // last workgroup (highest index) polls the records and runs the accept
 // scan on them.  Otherwise every workgroup counts itself on its sequence's
-// counter, its statistics written through first, and the one that
+// counter (cleared by workgroup 0 before it publishes lead_clr; a plain
+// atomic add), its statistics written through first, and the one that
 // completes the count (all lead x 2 x nseg workgroups of the sequence) runs
 // the accept scan.  Either way the scans run beside the streaming of other
 // sequences' rows.  Finally the scan counts the sequence on plan.lead_done, after
@@ -104,20 +105,32 @@ __device__ __forceinline__ void lead_scan_polled(const Problem& p, const Plan& p
     accept_sequence<true>(p, plan, b, 1, plan.done + b, nullptr, true, &pre);
 }
 
-// s_last, s_clr: LDS words of the calling kernel.
+// s_last: an LDS word of the calling kernel.
 template <int DT>
 __device__ __forceinline__ void lead_workgroup(const Problem& p, const Plan& plan, int64_t w, RowLds& lds,
-                                               int32_t& s_last, uint32_t& s_clr) {
-    if (w == 0 && threadIdx.x == 0) {
+                                               int32_t& s_last) {
+    const bool recs = plan.lead == 1 && plan.nseg <= kPolledSegs;   // (see below)
+    if (w == 0) {
         // The accept scans below fill these lists and count themselves on
-        // lead_done: cleared (written through) before the epoch that lets a
-        // scan use them.  lead_done keeps the epoch in its high half, so a
-        // reader tells this call's count from an earlier call's.
-        st_co<true>(plan.blk_ctr, uint64_t{0});
-        st_co<true>(plan.dlist_n, 0u);
-        st_co<true>(plan.lead_done, static_cast<uint64_t>(plan.epoch) << 32);
-        wait_stores();
-        st_co<true>(plan.lead_clr, plan.epoch);
+        // lead_done, and without records every workgroup counts itself on
+        // its sequence's lead_ctr: cleared (written through) before the
+        // epoch that lets them be used.  lead_done keeps the epoch in its
+        // high half, so a reader tells this call's count from an earlier
+        // call's.
+        // (with records only thread 0 takes part: the other threads go on
+        // to stream their segment at once)
+        if (!recs) {
+            for (int32_t j = threadIdx.x; j < p.B; j += kThreads) st_co<true>(plan.lead_ctr + j, uint64_t{0});
+            wait_stores();
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) {
+            st_co<true>(plan.blk_ctr, uint64_t{0});
+            st_co<true>(plan.dlist_n, 0u);
+            st_co<true>(plan.lead_done, static_cast<uint64_t>(plan.epoch) << 32);
+            wait_stores();
+            st_co<true>(plan.lead_clr, plan.epoch);
+        }
     }
     int64_t q = w;
     const int64_t seg = q % plan.nseg;
@@ -126,10 +139,9 @@ __device__ __forceinline__ void lead_workgroup(const Problem& p, const Plan& pla
     q >>= 1;
     const int32_t i = static_cast<int32_t>(q % plan.lead);
     const int32_t b = static_cast<int32_t>((q / plan.lead) * plan.lead_mul % p.B);
-    // One leading position, rows of at most kPolledSegs segments: the
+    // One leading position, rows of at most kPolledSegs segments (recs): the
     // sequence's workgroups hand their statistics over as records (LeadRec)
     // and the last of them runs the scan, with no count of arrivals.
-    const bool recs = plan.lead == 1 && plan.nseg <= kPolledSegs;
     // (cleared by one of the sequence's own workgroups, before it counts
     // itself: the sequence is listed, and a second-round item can mark it,
     // only after that)
@@ -165,24 +177,31 @@ __device__ __forceinline__ void lead_workgroup(const Problem& p, const Plan& pla
         return;
     }
     if (threadIdx.x == 0) {
-        // (the counter and lead_clr are loaded while the statistics' stores
-        // complete: the wait for those covers both round trips)
-        const uint64_t old = ld_co<true>(plan.lead_ctr + b);
-        s_clr = ld_co<true>(plan.lead_clr);
+        // One arrival (a plain atomic add: the lead x 2 x nseg workgroups of
+        // a sequence would serialise a compare-and-swap loop into a chain of
+        // round trips) on the counter workgroup 0 has cleared, after this
+        // workgroup's statistics are visible.  (lead_clr is loaded while
+        // those stores complete: the wait for them covers both round trips.)
+        uint32_t clr = ld_co<true>(plan.lead_clr);
         wait_stores();
-        s_last = arrive_from(plan.lead_ctr + b, plan.epoch, old) ==
-                 static_cast<uint32_t>(plan.lead * 2 * plan.nseg);
+        for (uint32_t polls = 0; polls < kClearPolls && clr != plan.epoch; ++polls) {
+            __builtin_amdgcn_s_sleep(2);
+            clr = ld_co<true>(plan.lead_clr);
+        }
+        // (a clear never seen, not expected: no arrival, so the sequence is
+        // never scanned; this workgroup makes it a data error, and the call
+        // stalled, which the pick launch makes every sequence's data error)
+        if (clr != plan.epoch)
+            s_last = -1;
+        else
+            s_last = __hip_atomic_fetch_add(plan.lead_ctr + b, uint64_t{1}, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT) +
+                             1 ==
+                         static_cast<uint64_t>(plan.lead * 2 * plan.nseg);
     }
     __syncthreads();
-    if (!s_last || threadIdx.x >= 64) return;
-    bool cleared = s_clr == plan.epoch;
-    for (uint32_t polls = 0; polls < kClearPolls && !cleared; ++polls) {
-        cleared = ld_co<true>(plan.lead_clr) == plan.epoch;
-        if (!cleared) __builtin_amdgcn_s_sleep(2);
-    }
-    if (cleared) {
-        accept_sequence<true>(p, plan, b, plan.lead, plan.done + b);
-    } else {
+    if (s_last == 0 || threadIdx.x >= 64) return;
+    if (s_last < 0) {
         if (usable)
             for (int64_t j = threadIdx.x; j <= k; j += 64) p.out_tokens[o + b + j] = -1;
         if (threadIdx.x == 0) {
@@ -190,8 +209,11 @@ __device__ __forceinline__ void lead_workgroup(const Problem& p, const Plan& pla
             if (p.out_emit_prob) p.out_emit_prob[b] = NAN;
             plan.done[b] = kDecided;
             store_no_task<true>(plan, b);
+            st_co<true>(plan.stall, plan.epoch);
         }
+        return;
     }
+    accept_sequence<true>(p, plan, b, plan.lead, plan.done + b);
     if (threadIdx.x == 0) {
         wait_stores();                             // (the wave's listing stores, every lane's)
         __hip_atomic_fetch_add(plan.lead_done, uint64_t{1}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -68,8 +68,7 @@ template <int DT>
 __global__ __launch_bounds__(kThreads) void row_lead_kernel(Problem p, Plan plan) {
     __shared__ RowLds lds;
     __shared__ int32_t s_last;
-    __shared__ uint32_t s_clr;
-    lead_workgroup<DT>(p, plan, blockIdx.x, lds, s_last, s_clr);
+    lead_workgroup<DT>(p, plan, blockIdx.x, lds, s_last);
 }
 
 }  // namespace

@@ -198,12 +198,11 @@ __global__ __launch_bounds__(kThreads) void rounds_kernel(Problem p, Plan plan, 
     } lds;
     __shared__ int32_t s_flag;
     __shared__ DrawTask s_task;
-    __shared__ uint32_t s_clr;
     __shared__ RestItem s_item;
     __shared__ int32_t s_seq;
     const int tid = threadIdx.x;
     if (blockIdx.x < nlead) {
-        lead_workgroup<DT>(p, plan, blockIdx.x, lds.row, s_flag, s_clr);
+        lead_workgroup<DT>(p, plan, blockIdx.x, lds.row, s_flag);
         return;
     }
     const int64_t v = static_cast<int64_t>(blockIdx.x) - nlead;

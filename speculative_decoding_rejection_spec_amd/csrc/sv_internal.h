@@ -100,12 +100,13 @@ struct Plan {
     int32_t cus;         // compute units of the device
     int32_t queue_mode;  // SV_QUEUE_*: where the second round's draw chunks are summed
     uint32_t epoch;      // this call's number (never 0): tags the counters below
-    uint64_t* lead_ctr;  // early exit: [B] epoch << 32 | leading segments of sequence b finished
+    uint64_t* lead_ctr;  // early exit without records: [B] leading segments of sequence b finished
+                         // (cleared before lead_clr is published)
     uint32_t* lead_clr;  // early exit: the epoch of the call whose first round has cleared the list counters
     uint64_t* lead_done; // early exit: epoch << 32 | sequences whose leading accept scan has finished
+                         // (set to epoch << 32 before lead_clr is published)
     LeadRec* lead_rec;   // early exit, lead 1, nseg <= kPolledSegs: [B][2][nseg] first-round records
     uint32_t lead_pace;  // early exit: 100 MHz ticks the first round's second half waits before streaming (0: none)
-                         // (set to epoch << 32 before lead_clr is published)
     uint32_t* stall;     // early exit: the epoch of a call whose second round could not find an item's work
     uint32_t item_polls; // early exit: bound of a second-round workgroup's wait for its item
 };
@@ -181,26 +182,6 @@ __device__ __forceinline__ void wait_stores() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt unchanged
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// One arrival on a counter word that packs a call's epoch (high 32 bits)
-// with the arrivals of that call (low 32 bits): a word an earlier call left
-// counts as none, so the counters need no clearing between calls.  Returns
-// the arrivals including this one.  (A compare-and-swap loop: each retry
-// means another arrival succeeded, so it ends.)
-// arrive_from: the same with the word's value already loaded (possibly
-// stale: the first compare-and-swap then fails and returns the current one).
-__device__ __forceinline__ uint32_t arrive_from(uint64_t* word, uint32_t epoch, uint64_t old) {
-    for (;;) {
-        const uint64_t base = static_cast<uint32_t>(old >> 32) == epoch ? old : static_cast<uint64_t>(epoch) << 32;
-        const uint64_t want = base + 1;
-        if (__hip_atomic_compare_exchange_strong(word, &old, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT))
-            return static_cast<uint32_t>(want);
-    }
-}
-__device__ __forceinline__ uint32_t arrive(uint64_t* word, uint32_t epoch) {
-    return arrive_from(word, epoch, __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
 // Early exit's schedule entries (SchedEntry): written through, one word at a
