@@ -312,3 +312,25 @@ def test_first_round_records_and_counts(sv, cuda, seg):
             compare(w, run_gpu(sv, w, cuda), ref, f"seg {seg}, call {i}")
     finally:
         sv.set_geometry()
+
+
+@pytest.mark.parametrize("lead", [2, 5, 64])
+def test_counted_first_round_at_full_size(sv, cuda, lead):
+    """The count of arrivals at the full C3 size (B = 64, k = 4, V = 128256
+    bf16, two segments a row): every first-round workgroup of a sequence,
+    lead x 2 x 2 of them (256 at lead 64, past k + 1 = 5 positions the
+    workgroups have no row to read), counts itself on the sequence's
+    counter, which the round clears; the one that completes the count runs
+    the scan.  Two calls per lead against the oracle (a count left by one
+    call must never complete the next call's)."""
+    if FORM["name"] != "early":
+        pytest.skip("early exit only")
+    print(f"[c3 full size, lead {lead}]", flush=True)
+    w = wl.make_workload("c3", trial=12)
+    ref = oracle.verify(w, threads=16)
+    try:
+        sv.set_early_exit(lead)
+        for i in range(2):
+            compare(w, run_gpu(sv, w, cuda), ref, f"lead {lead}, call {i}")
+    finally:
+        sv.set_early_exit(1)
