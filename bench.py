@@ -101,6 +101,8 @@ def main():
     ap.add_argument("--settle-ms", type=float, default=60.0,
                     help="untimed steps for this long before the warmup (GPU clock settling; 0 = none)")
     ap.add_argument("--workload", default="c4", help="c1 c2 c2g c3 c4 c4s c5 (c4s: C4 with shuffled halves)")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="sequences in the batch (0 = the workload's own; other sizes keep its recipe)")
     ap.add_argument("--copies", type=int, default=4, help="input copies rotated between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true",
@@ -155,8 +157,9 @@ def main():
     t_gen = time.perf_counter()
     # c4s: C4 with the near-identical and independent drafts on a random half
     # of the sequences each instead of the first and second half
-    w = (wl.make_workload("c4", shuffle_halves=True) if args.workload == "c4s"
-         else wl.make_workload(args.workload))
+    bsz = args.batch if args.batch > 0 else None
+    w = (wl.make_workload("c4", B=bsz, shuffle_halves=True) if args.workload == "c4s"
+         else wl.make_workload(args.workload, B=bsz))
     t_gen = time.perf_counter() - t_gen
     if args.entry == "commit":
         return bench_commit(args, sv, torch, np, w)
@@ -329,7 +332,8 @@ def main():
     roofline = None
     # The committed counter summaries were taken on the C4 verify in the
     # default geometry: their traffic applies to no other workload or shape.
-    counters_apply = (args.workload == "c4" and args.entry == "verify" and args.seg == 0 and args.chunk == 0 and
+    counters_apply = (args.workload == "c4" and args.batch in (0, 256) and args.entry == "verify" and
+                      args.seg == 0 and args.chunk == 0 and
                       args.lead in (-1, 0, 1) and args.queue == 0 and list(args.queue_lag) == [0, 0])
     if k1_live is not None:
         # The row pass reads every needed row once; the two-round launch also

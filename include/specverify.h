@@ -101,8 +101,8 @@ size_t spec_verify_workspace_size(int32_t B, int64_t total_draft, int64_t V, sv_
  * greedy rows); one wavefront per sequence then runs the accept tests and
  * finds the first rejection; a last fp64 pass over the one rejected or bonus
  * row pair draws the emitted token by inverse CDF.  Calls whose logit rows
- * hold at least 512 MiB read the rows in position order and stop at each
- * sequence's first rejection (early exit, four launches); smaller calls read
+ * hold at least 192 MiB read the rows in position order and stop at each
+ * sequence's first rejection (early exit, two launches); smaller calls read
  * every needed row in one pass (two to four launches).  The outputs do not
  * depend on the form. */
 sv_status_t spec_verify(const void *target_logits, const void *draft_logits,
@@ -167,7 +167,8 @@ sv_status_t spec_verify_probs(const void *target_logits, const void *draft_logit
  *     for data errors).
  * Every other argument and output is as for spec_verify.  Only target rows
  * and, for each sequence that rejects at position n < k_b, draft row n are
- * read; early exit applies to the target rows. */
+ * read; early exit applies to the target rows (automatically when they
+ * hold at least 320 MiB). */
 sv_status_t spec_verify_gathered(const void *target_logits, const void *draft_logits,
                                  const int32_t *draft_tokens, const float *draft_probs,
                                  const int32_t *offsets, int32_t k_uniform, int64_t total_draft,

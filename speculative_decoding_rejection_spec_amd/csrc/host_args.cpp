@@ -66,11 +66,13 @@ int64_t rounds_rest_blocks(int32_t B, int64_t total, bool has_offsets, int32_t k
     return rows * nseg + static_cast<int64_t>(B) * (1 + nchunk);
 }
 
-int32_t effective_lead(int64_t B, int64_t total, int64_t V, sv_dtype_t dtype, const Tuning& tu) {
+int32_t effective_lead(int64_t B, int64_t total, int64_t V, sv_dtype_t dtype, const Tuning& tu, bool gathered) {
     if (tu.lead != kAutoLead) return tu.lead;
     if (total == 0) return 0;                    // only bonus rows: nothing to skip
-    const int64_t bytes = (2 * total + B) * V * (dtype == SV_BF16 ? 2 : 4);
-    return bytes >= kAutoLeadBytes ? 1 : 0;
+    // (in double: no product of the sizes can overflow)
+    const double rows = static_cast<double>(gathered ? total + B : 2 * total + B);
+    const double bytes = rows * static_cast<double>(V) * (dtype == SV_BF16 ? 2.0 : 4.0);
+    return bytes >= static_cast<double>(gathered ? kAutoLeadBytesGathered : kAutoLeadBytes) ? 1 : 0;
 }
 
 // Splits a row of V logits into n <= max_pieces pieces of about `target`

@@ -20,12 +20,17 @@ constexpr int64_t kDefaultSegElems = 65536;   // row-pass segment length before 
 // inside a window.
 inline int64_t row_unit(sv_dtype_t dtype) { return dtype == SV_BF16 ? 256 * 8 * 8 : 256 * 4 * 4; }
 constexpr int64_t kDefaultChunkElems = 8192;  // draw chunk length before rounding
-// Early exit is worth its two extra launches (~15 us) only when the rows
-// it may skip take longer than that to stream: automatic mode (lead -1)
-// uses one leading position when all rows together hold at least
-// kAutoLeadBytes, and one full pass otherwise.
+// Early exit pays for its first round's scans and its pick launch only when
+// the rows it may skip take longer than those to stream: automatic mode
+// (lead -1) uses one leading position when the rows a full pass reads hold
+// at least kAutoLeadBytes (target and draft rows) or, in the gathered form
+// (target rows only, with its own launches), kAutoLeadBytesGathered, and
+// one full pass otherwise.  Both are the sizes where the two forms took
+// equally long on an MI355X (bf16, V = 128256 and 152064, one full pass
+// against one leading position over a range of batch sizes).
 constexpr int32_t kAutoLead = -1;
-constexpr int64_t kAutoLeadBytes = 512ll << 20;
+constexpr int64_t kAutoLeadBytes = 192ll << 20;
+constexpr int64_t kAutoLeadBytesGathered = 320ll << 20;
 
 // Early exit: bound of a second-round workgroup's wait for its item (one
 // poll takes a memory round trip and a short sleep, about a microsecond).
@@ -58,8 +63,10 @@ constexpr int64_t kMinSeg = 8192, kMinChunk = 1024;
 void auto_lengths(int32_t B, int64_t total, int64_t V, const Tuning& tu, int64_t* seg, int64_t* chunk);
 
 // Leading positions read first (early exit): the tuning's, or 1 when the
-// call's rows hold at least kAutoLeadBytes (0 for calls without drafts).
-int32_t effective_lead(int64_t B, int64_t total, int64_t V, sv_dtype_t dtype, const Tuning& tu);
+// rows a full pass reads hold at least kAutoLeadBytes (kAutoLeadBytesGathered
+// in the gathered form), 0 for calls without drafts.
+int32_t effective_lead(int64_t B, int64_t total, int64_t V, sv_dtype_t dtype, const Tuning& tu,
+                       bool gathered = false);
 
 // The first round visits sequence (j * m) mod B as its j-th: m is coprime
 // with B (so every sequence is visited once) and near 0.618 B, which spreads

@@ -172,7 +172,9 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     Problem pr = p;
     if (!pr.out_n) pr.out_n = reinterpret_cast<int32_t*>(ws + g.off_nbuf);
 
-    plan.lead = sample ? 0 : effective_lead(p.B, p.total, p.V, static_cast<sv_dtype_t>(p.dtype), tu);
+    plan.lead = sample ? 0
+                       : effective_lead(p.B, p.total, p.V, static_cast<sv_dtype_t>(p.dtype), tu,
+                                        p.draft_probs != nullptr);
     plan.lead_mul = lead_multiplier(p.B);
     int rest_per_cu = 1;
     if (device_info(p.dtype, &plan.cus, &rest_per_cu) != hipSuccess) return SV_ERR_HIP;

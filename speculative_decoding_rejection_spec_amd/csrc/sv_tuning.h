@@ -47,7 +47,8 @@ typedef struct {
                              that fill the GPU, shorter for small calls) */
     int64_t chunk_elems;  /* approx logits per draw chunk; 0 = automatic (8192, shorter for small calls) */
     int32_t lead;         /* early exit: leading positions read first; -1 = automatic (1 when the
-                             call's rows hold >= 512 MiB, else 0), 0 = one pass, up to SV_K_MAX + 1 */
+                             rows a full pass reads hold >= 192 MiB, 320 MiB in the gathered form,
+                             else 0), 0 = one pass, up to SV_K_MAX + 1 */
     int32_t queue_mode;   /* SV_QUEUE_* */
     int32_t lag_accept;   /* 0 = chosen from the resident grid */
     int32_t lag_draw;     /* 0 = chosen from the resident grid */

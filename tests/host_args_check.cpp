@@ -134,6 +134,7 @@ int main() {
         if (i % 5 == 0) { tt.chunk_elems = 1 + static_cast<int64_t>(rng() % 50000); }
         check_geometry(B, total, V, static_cast<sv_dtype_t>(i & 1), tt);
         CHECK(effective_lead(B, total, V, static_cast<sv_dtype_t>(i & 1), dflt) >= 0);
+        CHECK(effective_lead(B, total, V, static_cast<sv_dtype_t>(i & 1), dflt, true) >= 0);
     }
     // extremes: sizes whose workspace or grid cannot be formed give 0, without overflow
     CHECK(workspace_bytes_for(0x7FFFFFFF, 0x7FFFFFFFll * 63, 0x7FFFFFFF, SV_BF16, dflt) == 0);
