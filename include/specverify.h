@@ -66,6 +66,12 @@
  *     must not overlap in time on one GPU.  Callers that run concurrent
  *     streams pass their own workspace of spec_verify_workspace_size() bytes
  *     per stream.
+ *   * A call with a caller workspace, or through spec_verify_noalloc, may be
+ *     captured in a HIP graph and replayed: each replay is a call of its own
+ *     (its kernels number it from a counter at the workspace's start), and
+ *     replays, like calls, must not overlap in time on one workspace.  The
+ *     library-owned buffer is allocated on a call's first use of a size,
+ *     which capture does not allow.
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H

@@ -9,6 +9,7 @@ namespace {
 // One wave per workgroup: the scans spread over B compute units (256
 // sequences of k = 8: 9.7 -> 8.6 us against four waves per workgroup).
 __global__ __launch_bounds__(64) void accept_kernel(Problem p, Plan plan) {
+    plan.epoch = call_epoch(plan);
     const int32_t b = blockIdx.x;
     if (plan.lead > 0 && plan.done[b]) return;     // decided by its leading positions
     accept_sequence<false>(p, plan, b);

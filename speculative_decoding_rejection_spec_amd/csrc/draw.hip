@@ -11,6 +11,7 @@ namespace {
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void draw_sums_kernel(Problem p, Plan plan) {
+    plan.epoch = call_epoch(plan);
     const int64_t w = blockIdx.x;
     const int32_t b = static_cast<int32_t>(w / plan.nchunk);
     const int32_t c = static_cast<int32_t>(w - static_cast<int64_t>(b) * plan.nchunk);
@@ -35,6 +36,7 @@ __global__ __launch_bounds__(kThreads) void draw_sums_kernel(Problem p, Plan pla
 // (At 4 waves per SIMD four 256-thread workgroups share a CU: at most 128 VGPRs.)
 template <int DT, int kPickThreads>
 __global__ __launch_bounds__(kPickThreads, 4) void draw_pick_kernel(Problem p, Plan plan) {
+    plan.epoch = call_epoch(plan);
     const int32_t b = blockIdx.x;
     __shared__ drawpass::TabEntry tbl[256];
     __shared__ union {
@@ -107,6 +109,7 @@ __global__ __launch_bounds__(kPickThreads, 4) void draw_pick_kernel(Problem p, P
 // sums written through before the count) picks the token.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void draw_all_kernel(Problem p, Plan plan) {
+    plan.epoch = call_epoch(plan);
     const int64_t w = blockIdx.x;
     const int32_t b = static_cast<int32_t>(w / plan.nchunk);
     const int32_t c = static_cast<int32_t>(w - static_cast<int64_t>(b) * plan.nchunk);

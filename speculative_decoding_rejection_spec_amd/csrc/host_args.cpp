@@ -97,7 +97,9 @@ bool make_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dtype, int64_
     // (the second round's grid holds every row segment and every draw chunk)
     if (rows > 0x7FFFFFFFll / g.nseg) return false;   // (checked first: rows * nseg may not fit 64 bits)
     if (rows * g.nseg + static_cast<int64_t>(B) * (1 + g.nchunk) > 0x7FFFFFFFll) return false;
-    size_t off = 0;
+    // (the epoch counter first, at the same place for every geometry)
+    g.off_epoch = 0;
+    size_t off = align256(2 * sizeof(uint32_t));
     g.off_seg = off;
     off = align256(off + sizeof(SegStat) * static_cast<size_t>(rows) * g.nseg);
     g.off_task = off;

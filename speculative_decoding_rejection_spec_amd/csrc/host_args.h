@@ -82,7 +82,7 @@ struct Geometry {
     int64_t seg_len, chunk_len;
     size_t off_seg, off_task, off_csum, off_band_n, off_band_w, off_xlogit, off_done, off_sched,
         off_blk_ctr, off_blk_seq, off_dlist, off_dlist_n, off_nbuf, off_aband, off_picked,
-        off_lead_ctr, off_lead_clr, off_lead_done, off_stall, off_lead_rec, bytes;
+        off_lead_ctr, off_lead_clr, off_lead_done, off_stall, off_lead_rec, off_epoch, bytes;
 };
 
 // Splits a row of V logits into n <= max_pieces pieces of about `target`

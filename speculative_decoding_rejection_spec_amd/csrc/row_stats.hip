@@ -23,6 +23,7 @@ namespace {
 // their softmax, i.e. not in the gathered form).
 template <int DT>
 __global__ __launch_bounds__(kThreads) void row_stats_kernel(Problem p, Plan plan) {
+    plan.epoch = begin_epoch(plan);                // (the call's first kernel)
     const int64_t w = blockIdx.x;
     if (w == 0 && threadIdx.x == 0) *plan.dlist_n = 0;   // the accept scan fills the draft list
     if (w < p.B && threadIdx.x == 0) plan.picked[w] = 0u;   // (the grid has at least B blocks)
@@ -43,6 +44,7 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(Problem p, Plan pla
 template <int DT>
 __global__ __launch_bounds__(kThreads) void row_list_kernel(Problem p, Plan plan, const RestItem* list,
                                                             const uint32_t* count) {
+    plan.epoch = call_epoch(plan);
     const int64_t w = blockIdx.x;
     if (w >= *count) return;
     const RestItem it = list[w];
@@ -54,6 +56,7 @@ __global__ __launch_bounds__(kThreads) void row_list_kernel(Problem p, Plan plan
 // gathered form, whose schedule holds row segments only).
 template <int DT>
 __global__ __launch_bounds__(kThreads) void sched_rows_kernel(Problem p, Plan plan, const uint32_t* count) {
+    plan.epoch = call_epoch(plan);
     const int64_t w = blockIdx.x;
     if (w >= *count) return;
     RestItem it;
@@ -66,6 +69,7 @@ __global__ __launch_bounds__(kThreads) void sched_rows_kernel(Problem p, Plan pl
 // other forms run it inside the second round's launch): lead_pass.h.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void row_lead_kernel(Problem p, Plan plan) {
+    plan.epoch = begin_epoch(plan);                // (the call's first kernel)
     __shared__ RowLds lds;
     __shared__ int32_t s_last;
     lead_workgroup<DT>(p, plan, blockIdx.x, lds, s_last);

@@ -189,6 +189,7 @@ __device__ __forceinline__ bool find_item(const Problem& p, const Plan& plan, in
 // it.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void rounds_kernel(Problem p, Plan plan, uint32_t nlead) {
+    plan.epoch = begin_epoch(plan);                // (the call's first kernel)
     __shared__ union {
         RowLds row;
         struct {

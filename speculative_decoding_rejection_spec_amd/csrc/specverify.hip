@@ -4,8 +4,6 @@
 // include/specverify.h.
 #include <stdlib.h>
 
-#include <atomic>
-#include <chrono>
 #include <mutex>
 
 #include "host_args.h"
@@ -29,18 +27,6 @@ static_assert(kNumKernels == SV_NUM_KERNELS, "kernel count");
 const char* const kKernelNames[kNumKernels] = {"row_stats", "accept",   "draw_sums", "draw_pick",
                                                "row_lead",  "row_draft", "rounds",    "draw_all",
                                                "sample_sums", "sample_pick"};
-
-// Call numbers: a counter word of the workspace that an earlier call (or
-// fresh memory) left carries another epoch and counts as zero.  Started
-// from the clock so a workspace reused by another process is unlikely to
-// hold a matching one; 0 is skipped.
-std::atomic<uint32_t> g_epoch{static_cast<uint32_t>(
-    std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761u)};
-uint32_t next_epoch() {
-    uint32_t e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
-    if (e == 0) e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
-    return e;
-}
 
 // One pass: the draw runs as one launch (draw_all) while its workgroups
 // (sequences x chunks) fit one round on the CUs, counted at this many per
@@ -167,7 +153,8 @@ sv_status_t run(const Problem& p, void* workspace, size_t workspace_bytes, hipSt
     plan.lead_pace = 0;
     plan.stall = reinterpret_cast<uint32_t*>(ws + g.off_stall);
     plan.item_polls = tu.item_polls;
-    plan.epoch = next_epoch();
+    plan.epoch = 0;                                // (each kernel takes the call's epoch on the device)
+    plan.epoch_ctr = reinterpret_cast<uint32_t*>(ws + g.off_epoch);
     plan.queue_mode = tu.queue_mode;
     Problem pr = p;
     if (!pr.out_n) pr.out_n = reinterpret_cast<int32_t*>(ws + g.off_nbuf);

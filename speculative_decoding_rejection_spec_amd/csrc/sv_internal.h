@@ -99,7 +99,9 @@ struct Plan {
     int32_t queued;      // early exit with the draws beside the rows (not the gathered form)
     int32_t cus;         // compute units of the device
     int32_t queue_mode;  // SV_QUEUE_*: where the second round's draw chunks are summed
-    uint32_t epoch;      // this call's number (never 0): tags the counters below
+    uint32_t epoch;      // this call's number (never 0): tags the counters below; set on the
+                         // device by each kernel (begin_epoch / call_epoch), not by the host
+    uint32_t* epoch_ctr; // [2] at the workspace's start: the calls counter, this call's epoch
     uint64_t* lead_ctr;  // early exit without records: [B] leading segments of sequence b finished
                          // (cleared before lead_clr is published)
     uint32_t* lead_clr;  // early exit: the epoch of the call whose first round has cleared the list counters
@@ -182,6 +184,26 @@ __device__ __forceinline__ void wait_stores() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt unchanged
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// The call's epoch comes from device memory, so that a call replayed from a
+// captured graph (the same kernel arguments every time) still gets a number
+// of its own.  The call's first kernel takes the workspace's counter plus
+// one (never 0) in every workgroup -- no kernel of the call writes the
+// counter while the first one runs -- and workgroup 0 publishes it in
+// epoch_ctr[1]; the call's later kernels read it back there, and their
+// workgroup 0 advances the counter to it for the next call.  Kept at the
+// workspace's start, the counter survives calls of other sizes.
+__device__ __forceinline__ uint32_t begin_epoch(const Plan& plan) {
+    uint32_t e = plan.epoch_ctr[0] + 1u;
+    if (e == 0u) e = 1u;
+    if (blockIdx.x == 0 && threadIdx.x == 0) plan.epoch_ctr[1] = e;
+    return e;
+}
+__device__ __forceinline__ uint32_t call_epoch(const Plan& plan) {
+    const uint32_t e = plan.epoch_ctr[1];
+    if (blockIdx.x == 0 && threadIdx.x == 0) plan.epoch_ctr[0] = e;
+    return e;
 }
 
 // Early exit's schedule entries (SchedEntry): written through, one word at a

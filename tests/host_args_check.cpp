@@ -51,7 +51,7 @@ static void check_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dt, c
           (g.nchunk - 1) * g.chunk_len < V);
     CHECK(g.chunk_len % 8 == 0);
     if (V > max_seg_elems(dt) && tu.seg_elems == 0) CHECK(g.seg_len <= max_seg_elems(dt));
-    const size_t offs[] = {g.off_seg,     g.off_task,     g.off_csum,     g.off_band_n,    g.off_band_w,
+    const size_t offs[] = {g.off_epoch,   g.off_seg,     g.off_task,     g.off_csum,     g.off_band_n,    g.off_band_w,
                            g.off_xlogit,  g.off_done,     g.off_sched,    g.off_blk_ctr,   g.off_blk_seq,
                            g.off_dlist,   g.off_dlist_n,  g.off_nbuf,     g.off_aband,     g.off_picked,
                            g.off_lead_ctr, g.off_lead_clr, g.off_lead_done, g.off_stall,    g.off_lead_rec,
@@ -60,7 +60,9 @@ static void check_geometry(int32_t B, int64_t total, int64_t V, sv_dtype_t dt, c
         CHECK(offs[i] % 256 == 0);
         if (i > 0) CHECK(offs[i] >= offs[i - 1]);
     }
-    // every record the kernels index fits before the next block
+    // every record the kernels index fits before the next block; the epoch
+    // counter (two words) first, at the same offset for every geometry
+    CHECK(g.off_epoch == 0 && g.off_seg >= 2 * sizeof(uint32_t));
     const size_t rows = static_cast<size_t>(2 * total + B);
     CHECK(g.off_task - g.off_seg >= sizeof(SegStat) * rows * static_cast<size_t>(g.nseg));
     CHECK(g.off_task + sizeof(TaskRec) * static_cast<size_t>(B) <= g.off_csum);
