@@ -7,14 +7,16 @@ the workspace's start.  Every replay below gets new inputs copied into the
 captured tensors and must match the fp64 oracle on those inputs, with eager
 calls on the same workspace between the replays (their epochs come from
 the same counter); in each launch form through spec_verify with a caller
-workspace, and through spec_verify_noalloc in the early-exit form (chosen
-by size) and in one pass.  The bar is that of tests/test_gpu_parity.py.
+workspace, through spec_verify_noalloc in the early-exit form (chosen by
+size) and in one pass, and through spec_verify_gathered in both.  The bar
+is that of tests/test_gpu_parity.py.
 """
 import pytest
 
 import oracle
 import workloads as wl
 from test_gpu_parity import compare, set_form, to_device
+from test_oracle_draft import gathered_q
 
 pytestmark = pytest.mark.gpu
 
@@ -33,14 +35,19 @@ def sv(cuda):
     sv.reset_options()
 
 
-def _replays(sv, dev, works, call, eager):
+def _replays(sv, dev, works, call, eager, qgs=None):
     """Captures call(static inputs) once and replays it in ORDER, each time
     after copying that workload's inputs in; eager(j) runs an eager call
     on workload j between replays.  Every output is compared with the
-    oracle."""
+    oracle.  qgs: the drafter's gathered q_i(x_i) of each workload (input
+    "qg"), for the gathered form."""
     import torch
-    refs = [oracle.verify(w, threads=16) for w in works]
+    refs = [oracle.verify(w, threads=16, **({} if qgs is None else {"draft_probs": qgs[i]}))
+            for i, w in enumerate(works)]
     inputs = [to_device(w, dev) for w in works]
+    if qgs is not None:
+        for d, q in zip(inputs, qgs):
+            d["qg"] = torch.from_numpy(q).to(dev)
     static = {k: v.clone() for k, v in inputs[0].items()}
     B, total = works[0].B, int(works[0].k.sum())
     out_tok = torch.empty(total + B, dtype=torch.int32, device=dev)
@@ -112,3 +119,31 @@ def test_graph_replays_without_allocation(sv, cuda, case):
                                       d["temperature"])
 
     _replays(sv, cuda, works, call, eager)
+
+
+@pytest.mark.parametrize("lead", [1, 0], ids=["early-exit", "one-pass"])
+def test_graph_replays_gathered(sv, cuda, lead):
+    """spec_verify_gathered (the drafter's q_i(x_i) handed over), its first
+    round and listed remainder or its one pass, with a caller workspace."""
+    import torch
+    sv.reset_options()
+    sv.set_early_exit(lead)
+    try:
+        works = [wl.make_workload("c3", trial=t, B=24, V=50000) for t in (41, 42, 43)]
+        qgs = [gathered_q(w) for w in works]
+        w = works[0]
+        ws = torch.empty(sv.spec_verify_workspace_size(w.B, int(w.k.sum()), w.V, torch.bfloat16),
+                         dtype=torch.uint8, device=cuda)
+
+        def call(d, out_tok, out_n):
+            sv.spec_verify_gathered(d["target"], d["draft"], d["tokens"], d["qg"], d["offsets"], d["uniforms"],
+                                    d["temperature"], out_tokens=out_tok, out_n_accepted=out_n, workspace=ws)
+
+        def eager(d):
+            tok, n, _ = sv.spec_verify_gathered(d["target"], d["draft"], d["tokens"], d["qg"], d["offsets"],
+                                                d["uniforms"], d["temperature"], workspace=ws)
+            return tok, n
+
+        _replays(sv, cuda, works, call, eager, qgs)
+    finally:
+        sv.reset_options()
