@@ -147,3 +147,31 @@ def test_graph_replays_gathered(sv, cuda, lead):
         _replays(sv, cuda, works, call, eager, qgs)
     finally:
         sv.reset_options()
+
+
+def test_epoch_counter_skips_zero(sv, cuda):
+    """The epoch counter at the workspace's start wraps past 0 (the number
+    no call takes): set to 2^32 - 2, two early-exit calls take 2^32 - 1 and
+    then 1, both against the oracle, and leave 1 in both words."""
+    import numpy as np
+    import torch
+    sv.reset_options()
+    sv.set_early_exit(1)
+    try:
+        works = [wl.make_workload("c3", trial=t, B=24, V=50000) for t in (51, 52)]
+        w = works[0]
+        ws = torch.zeros(sv.spec_verify_workspace_size(w.B, int(w.k.sum()), w.V, torch.bfloat16),
+                         dtype=torch.uint8, device=cuda)
+        ws[:4].copy_(torch.tensor([0xFE, 0xFF, 0xFF, 0xFF], dtype=torch.uint8))
+        seen = []
+        for i, wk in enumerate(works):
+            d = to_device(wk, cuda)
+            tok, n = sv.spec_verify(d["target"], d["draft"], d["tokens"], d["offsets"], d["uniforms"],
+                                    d["temperature"], workspace=ws)
+            torch.cuda.synchronize()
+            compare(wk, dict(tokens=tok.cpu().numpy(), n=n.cpu().numpy()), oracle.verify(wk, threads=16),
+                    f"call {i}")
+            seen.append(ws[:8].cpu().numpy().view(np.uint32).tolist())
+        assert seen == [[0xFFFFFFFF, 0xFFFFFFFF], [1, 1]], seen
+    finally:
+        sv.reset_options()
