@@ -1,0 +1,87 @@
+"""Randomized parity: calls of random shape against the fp64 oracle.
+
+Each case draws a workload recipe (C1-C5's value distributions), a batch
+size, a vocabulary (the workloads' own, 4099, or any size from 64 up), the
+drafts per sequence, a launch form (automatic by size, early exit after one
+or two leading positions, one pass with the draw in one launch or in three)
+and an entry point (spec_verify, spec_verify_gathered with the drafter's
+q_i(x_i), or spec_verify_noalloc), from a fixed seed, so a failure names a
+case that reproduces on the CPU side exactly.  The bar is that of
+tests/test_gpu_parity.py; inputs are capped at 1.5 GB of logits.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from test_gpu_parity import compare, set_form, to_device
+from test_oracle_draft import gathered_q
+
+pytestmark = pytest.mark.gpu
+
+
+def _cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        name = str(rng.choice(["c1", "c2", "c3", "c4", "c5"]))
+        V = int(rng.choice([4099, 32000, 50000, 128256, 152064, int(rng.integers(64, 200000))]))
+        k = int(rng.integers(1, 13)) if name != "c5" else None
+        B = int(rng.integers(1, 300))
+        elt = 4 if name == "c1" else 2
+        if (2 * (k or 10) + 1) * B * V * elt > 1.5e9:
+            B = max(1, int(1.5e9 / ((2 * (k or 10) + 1) * V * elt)))
+        form = str(rng.choice(["auto", "early1", "early2", "full", "full3"]))
+        entry = str(rng.choice(["verify", "verify", "gathered", "noalloc"]))
+        out.append((i, name, B, V, k, "auto" if entry == "noalloc" else form, entry))
+    return out
+
+
+CASES = _cases(32, 7)
+
+
+@pytest.fixture(scope="module")
+def sv(cuda):
+    import os
+
+    import speculative_decoding_rejection_spec_amd as sv
+    if not os.path.exists(sv.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    yield sv
+    sv.reset_options()
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-{c[1]}-B{c[2]}-V{c[3]}-{c[5]}-{c[6]}" for c in CASES])
+def test_random_call(sv, cuda, case):
+    import torch
+    i, name, B, V, k, form, entry = case
+    print(f"[case {i}: {name} B={B} V={V} k={k} form={form} entry={entry}]", flush=True)
+    w = wl.make_workload(name, trial=2000 + i, B=B, V=V, k=k)
+    sv.reset_options()
+    try:
+        if form == "early1":
+            sv.set_early_exit(1)
+        elif form == "early2":
+            sv.set_early_exit(2)
+        elif form in ("full", "full3"):
+            set_form(sv, form)
+        d = to_device(w, cuda)
+        if entry == "gathered":
+            qg = gathered_q(w)
+            ref = oracle.verify(w, threads=16, draft_probs=qg)
+            tok, n, _ = sv.spec_verify_gathered(d["target"], d["draft"], d["tokens"], torch.from_numpy(qg).to(cuda),
+                                                d["offsets"], d["uniforms"], d["temperature"])
+        else:
+            ref = oracle.verify(w, threads=16)
+            call = sv.spec_verify_noalloc if entry == "noalloc" else sv.spec_verify
+            try:
+                tok, n = call(d["target"], d["draft"], d["tokens"], d["offsets"], d["uniforms"], d["temperature"])
+            except sv.SpecVerifyError as e:
+                # (only the no-alloc scratch may refuse a valid call: too large for it)
+                assert entry == "noalloc" and "scratch" in str(e), e
+                pytest.skip(f"larger than the no-alloc scratch: {e}")
+        torch.cuda.synchronize()
+        compare(w, dict(tokens=tok.cpu().numpy(), n=n.cpu().numpy()), ref, f"case {i}")
+    finally:
+        sv.reset_options()
