@@ -85,3 +85,41 @@ def test_random_call(sv, cuda, case):
         compare(w, dict(tokens=tok.cpu().numpy(), n=n.cpu().numpy()), ref, f"case {i}")
     finally:
         sv.reset_options()
+
+
+def _sample_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dtype = str(rng.choice(["f32", "bf16"]))
+        V = int(rng.choice([4099, 32000, 152064, int(rng.integers(16, 200000))]))
+        rows = int(rng.integers(1, 600))
+        rows = max(1, min(rows, int(5e8 // (V * 4))))
+        shape = str(rng.choice(["normal", "spiky", "flat"]))
+        out.append((i, dtype, V, rows, shape))
+    return out
+
+
+SAMPLE_CASES = _sample_cases(12, 11)
+
+
+@pytest.mark.parametrize("case", SAMPLE_CASES, ids=[f"{c[0]}-{c[1]}-V{c[2]}-R{c[3]}-{c[4]}" for c in SAMPLE_CASES])
+def test_random_draft_sample(sv, cuda, case):
+    """spec_draft_sample on random rows: logits normal (scale 2), spiky (a
+    few tokens 8-20 above the rest) or flat (scale 0.05), temperatures from
+    0 to 2, against the oracle's sampler (the bar of
+    tests/test_gpu_drafting.py)."""
+    from test_gpu_drafting import check_sample, run_sample
+    i, dtype, V, rows, shape = case
+    print(f"[sample case {i}: {dtype} V={V} rows={rows} {shape}]", flush=True)
+    g = np.random.default_rng(3000 + i)
+    z = (g.standard_normal((rows, V)) * (0.05 if shape == "flat" else 2.0)).astype(np.float32)
+    if shape == "spiky":
+        for r in range(rows):
+            z[r, g.integers(0, V, size=3)] += g.uniform(8.0, 20.0, size=3).astype(np.float32)
+    stored = wl.bf16_round(z) if dtype == "bf16" else z
+    T = g.choice(np.array([0.0, 0.3, 0.7, 1.0, 2.0], np.float32), size=rows)
+    u = g.random(rows, dtype=np.float32)
+    tok, prob = run_sample(sv, stored, T, u, cuda)
+    nflag = check_sample(stored, T, u, tok, prob, f"sample case {i}")
+    assert nflag <= max(1, rows // 100)
