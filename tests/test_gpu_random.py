@@ -123,3 +123,43 @@ def test_random_draft_sample(sv, cuda, case):
     tok, prob = run_sample(sv, stored, T, u, cuda)
     nflag = check_sample(stored, T, u, tok, prob, f"sample case {i}")
     assert nflag <= max(1, rows // 100)
+
+
+def _book_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    return [(i, int(rng.integers(1, 3000)), int(rng.integers(16, 3000)), int(rng.integers(2, 50000)),
+             int(rng.integers(1, 7)), int(rng.integers(0, 64))) for i in range(n)]
+
+
+BOOK_CASES = _book_cases(10, 13)
+
+
+@pytest.mark.parametrize("case", BOOK_CASES, ids=[f"{c[0]}-B{c[1]}-L{c[2]}-a{c[3]}" for c in BOOK_CASES])
+def test_random_commit_and_ngram(sv, cuda, case):
+    """spec_commit of a random round (k_b up to the case's k_max, n_b from -1
+    to k_b, sequences from empty to full) and spec_ngram_draft over random
+    token streams with repeats (n from the case's n_max down to a random
+    n_min), both bit-exact against the oracle."""
+    import torch
+    from test_gpu_bookkeeping import T, random_round, random_text
+    i, B, max_len, alphabet, nmax, kmax = case
+    print(f"[bookkeeping case {i}: B={B} max_len={max_len} alphabet={alphabet} n_max={nmax} k_max={kmax}]",
+          flush=True)
+    g = np.random.default_rng(4000 + i)
+    k, offsets, out_tokens, out_n, seq, L = random_round(g, B, max_len, kmax=kmax)
+    want = oracle.commit(out_tokens, out_n, offsets, seq, L)
+    dseq, dL = T(seq, cuda), T(L, cuda)
+    com, coff = sv.spec_commit(T(out_tokens, cuda), T(out_n, cuda), T(offsets, cuda), dseq, dL)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dseq.cpu().numpy(), want[0])
+    np.testing.assert_array_equal(dL.cpu().numpy(), want[1])
+    np.testing.assert_array_equal(coff.cpu().numpy(), want[3])
+    np.testing.assert_array_equal(com.cpu().numpy()[:want[3][-1]], want[2])
+
+    nmin = int(g.integers(1, nmax + 1))
+    seq, L = random_text(g, min(B, 400), max_len, alphabet)
+    want_t, want_o = oracle.ngram_draft(seq, L, nmax, nmin, kmax)
+    dt, do = sv.spec_ngram_draft(T(seq, cuda), T(L, cuda), ngram_max=nmax, ngram_min=nmin, k_max=kmax)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(do.cpu().numpy(), want_o)
+    np.testing.assert_array_equal(dt.cpu().numpy()[:want_o[-1]], want_t)
