@@ -189,8 +189,10 @@ __device__ __forceinline__ void lead_workgroup(const Problem& p, const Plan& pla
             clr = ld_co<true>(plan.lead_clr);
         }
         // (a clear never seen, not expected: no arrival, so the sequence is
-        // never scanned; this workgroup makes it a data error, and the call
-        // stalled, which the pick launch makes every sequence's data error)
+        // never scanned; this workgroup makes it a data error and marks the
+        // call stalled -- after the two-round launch the pick launch then
+        // makes every sequence a data error, since the second round's waits
+        // for the uncounted sequence run out)
         if (clr != plan.epoch)
             s_last = -1;
         else
