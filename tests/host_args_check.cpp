@@ -138,6 +138,24 @@ int main() {
         CHECK(effective_lead(B, total, V, static_cast<sv_dtype_t>(i & 1), dflt) >= 0);
         CHECK(effective_lead(B, total, V, static_cast<sv_dtype_t>(i & 1), dflt, true) >= 0);
     }
+    // the automatic form at the measured crossovers: one pass below 192 MiB
+    // of rows (target and draft), early exit above; the gathered form counts
+    // target rows against 320 MiB; calls without drafts take one pass; a
+    // lead set in the tuning wins
+    CHECK(effective_lead(64, 64 * 4, 128256, SV_BF16, dflt) == 0);          // C3: 148 MB
+    CHECK(effective_lead(32, 32 * 8, 152064, SV_BF16, dflt) == 0);          // 165 MB
+    CHECK(effective_lead(48, 48 * 8, 152064, SV_BF16, dflt) == 1);          // 248 MB
+    CHECK(effective_lead(256, 256 * 8, 152064, SV_BF16, dflt) == 1);        // C4
+    CHECK(effective_lead(96, 96 * 8, 152064, SV_BF16, dflt, true) == 0);    // gathered: 280 MB of target rows
+    CHECK(effective_lead(128, 128 * 8, 152064, SV_BF16, dflt, true) == 1);  // gathered: 373 MB
+    CHECK(effective_lead(4096, 0, 152064, SV_BF16, dflt) == 0);             // bonus rows only
+    {
+        Tuning t0;
+        t0.lead = 0;
+        CHECK(effective_lead(256, 256 * 8, 152064, SV_BF16, t0) == 0);
+        t0.lead = 3;
+        CHECK(effective_lead(1, 1, 100, SV_F32, t0) == 3);
+    }
     // extremes: sizes whose workspace or grid cannot be formed give 0, without overflow
     CHECK(workspace_bytes_for(0x7FFFFFFF, 0x7FFFFFFFll * 63, 0x7FFFFFFF, SV_BF16, dflt) == 0);
     CHECK(workspace_bytes_for(-1, 0, 10, SV_F32, dflt) == 0);
