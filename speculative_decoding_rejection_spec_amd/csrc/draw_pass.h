@@ -251,8 +251,15 @@ __device__ __forceinline__ Rows<DT> rows_of(const Problem& p, const DrawTask& ta
                     c, -static_cast<double>(task.m_t) * c, -static_cast<double>(task.m_d) * c, tbl};
 }
 
+// Cache policy of the draw's row loads: non-temporal.  Each draw chunk reads
+// its piece of a row once; letting those lines allocate in the caches only
+// evicts others (512 ragged sequences of V = 128256: the two-round launch
+// 162.7-163.0 against 166.3-166.5 us; 256 of V = 152064: 157.2-157.6
+// against 157.6-158.5).
+constexpr int kDrawLoadPolicy = 2;
+
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int32_t byte_off) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kDrawLoadPolicy));
 }
 
 // Calls f(z_t, z_d) for this lane's tokens of [v0, v1), run by one whole
